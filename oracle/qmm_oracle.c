@@ -1,0 +1,409 @@
+/*
+ * CPU oracle for the quantized-weight matmul  out[t][r] = sum_i W[r][i] * x[t][i]
+ * with W in GGUF-style Q4_K / Q6_K super-blocks and x quantized to int8 blocks
+ * of 32 (an f32 scale d and the f32 product s = d * sum(q) per block).
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's CPU
+ * baseline leg may load or run this code.  It shares nothing with the HIP path:
+ * no headers, helpers, tables or constants.  Plain, slow and written to be read
+ * against the pages; f64 wherever a value is combined.
+ *
+ * Pages cited (by title; section in brackets):
+ *   [GEMM]  "The quantized GEMM" (mojo-dllm kernels page)
+ *   [MMQ]   "llama.cpp MMQ -- quantized-weight int8 tensor-core matmul: structure,
+ *            numerics, SASS census, and minfer contrast"
+ *   [CH04]  "04 - Reading minfer's kernels II -- from GEMV to tiled GEMM"
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes of the repository):
+ *   R1  Q6_K element-to-bit map inside the low-nibble / high-2-bit planes: the
+ *       pages name the planes and their order only; the public GGUF arrangement
+ *       is used (two halves of 128; see q6k_decode).  PARITY UNPINNED by the
+ *       pages for that map: pinned only by internal consistency and special cases.
+ *   R2  Activation scale d = amax / 127 (IEEE f32 divide), codes
+ *       q = roundf(x / d) (IEEE f32 divide, ties away from zero), so |q| <= 127.
+ *   R3  All-zero block (d == 0): q = 0, s = 0.
+ *   R4  s = d * (float)sum(q), one f32 multiply, round to nearest even.
+ *   R5  Q6_K group scales are signed int8; Q6_K d sits in the last two bytes.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp (no -ffast-math, no -march).
+ *
+ * OQ_MUTATE (default 0) plants one known mistake, for the tests that show the
+ * pins catch it: 1 swapped nibble halves, 2 Q6_K offset 32 dropped, 3 Q4_K min
+ * term dropped, 4 scale and min swapped, 5 Q6_K scale per 32 instead of per 16.
+ */
+#ifndef OQ_MUTATE
+#define OQ_MUTATE 0
+#endif
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define OQ_TYPE_Q4_K 1
+#define OQ_TYPE_Q6_K 2
+
+/* f16 bits -> f64, exact (normal, subnormal, zero; inf/nan kept as such). */
+static double f16_bits_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int ex = (h >> 10) & 0x1F;
+    int man = h & 0x3FF;
+    double v;
+    if (ex == 0)
+        v = ldexp((double)man, -24);               /* subnormal: man * 2^-24 */
+    else if (ex == 31)
+        v = man ? NAN : INFINITY;
+    else
+        v = ldexp((double)(man | 0x400), ex - 25); /* (1024 + man) * 2^(ex-25) */
+    return sign ? -v : v;
+}
+
+static uint16_t rd_u16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* ---- O1. Q4_K super-block (144 bytes) ------------------------------------
+ * [GEMM, "The GPU path", "Q4_K: packed in shared memory"]: a row's super-block is
+ * a 16-byte header (d, dmin, packed scales) then 128 bytes of codes; in code
+ * chunk p (32 bytes) byte l carries sub-block 2p in its low nibble and sub-block
+ * 2p+1 in its high nibble, at position l.
+ * [MMQ, section 6, get_scale_min_k4 semantics]: the 12 scale bytes decode to a
+ * (scale, min) pair per sub-block of 32; for j < 4 scale = s[j] & 63,
+ * min = s[j+4] & 63; otherwise scale = (s[j+4] & 0xF) | ((s[j-4] >> 6) << 4) and
+ * min = (s[j+4] >> 4) | ((s[j] >> 6) << 4).  A code v in 0..15 stands for
+ * d*scale*v - dmin*min.  Codes are never centred [MMQ, section 11.4]. */
+typedef struct {
+    double d, dmin;
+    int sc[8], m[8];
+    int q[256];
+} q4k_block;
+
+static void q4k_scale_min(const uint8_t* s, int j, int* sc, int* m)
+{
+    if (j < 4) {
+        *sc = s[j] & 63;
+        *m = s[j + 4] & 63;
+    } else {
+        *sc = (s[j + 4] & 0xF) | ((s[j - 4] >> 6) << 4);
+        *m = (s[j + 4] >> 4) | ((s[j] >> 6) << 4);
+    }
+#if OQ_MUTATE == 4
+    int t = *sc;
+    *sc = *m;
+    *m = t;
+#endif
+}
+
+static void q4k_decode(const uint8_t* B, q4k_block* o)
+{
+    o->d = f16_bits_to_f64(rd_u16(B + 0));
+    o->dmin = f16_bits_to_f64(rd_u16(B + 2));
+    const uint8_t* s12 = B + 4;
+    const uint8_t* qs = B + 16;
+    for (int j = 0; j < 8; ++j)
+        q4k_scale_min(s12, j, &o->sc[j], &o->m[j]);
+    for (int j = 0; j < 8; ++j) {
+        int p = j >> 1;
+        for (int l = 0; l < 32; ++l) {
+            uint8_t byte = qs[32 * p + l];
+#if OQ_MUTATE == 1
+            o->q[32 * j + l] = (j & 1) ? (byte & 0x0F) : (byte >> 4);
+#else
+            o->q[32 * j + l] = (j & 1) ? (byte >> 4) : (byte & 0x0F);
+#endif
+        }
+    }
+}
+
+/* ---- O2. Q6_K super-block (210 bytes) ------------------------------------
+ * [GEMM, "Q6_K: the same layout and prefetch"]: low nibbles, high bits, 16 int8
+ * group scales, d -- in that order; [GEMM, "Weights: 8 rows per register"]: the
+ * stored Q6_K code is the value plus 32.  [MMQ, section 4, Q6_K specialization]: the 6-bit
+ * code is (low | high) and the value is d * scale * (code - 32), one int8 scale per
+ * 16 values.  Element-to-bit map: reading R1 (two halves h of 128 elements; half
+ * h uses low bytes 64h.., high bytes 32h.., scales 8h..): for l in 0..31,
+ *   element 128h+l      <- low nibble of ql[64h+l],    bits 0-1 of qh[32h+l]
+ *   element 128h+32+l   <- low nibble of ql[64h+32+l], bits 2-3 of qh[32h+l]
+ *   element 128h+64+l   <- high nibble of ql[64h+l],   bits 4-5 of qh[32h+l]
+ *   element 128h+96+l   <- high nibble of ql[64h+32+l],bits 6-7 of qh[32h+l]. */
+typedef struct {
+    double d;
+    int sc[16];
+    int q6[256]; /* stored code, 0..63 (value uses q6 - 32) */
+} q6k_block;
+
+static void q6k_decode(const uint8_t* B, q6k_block* o)
+{
+    const uint8_t* ql = B;
+    const uint8_t* qh = B + 128;
+    const int8_t* sc = (const int8_t*)(B + 192);
+    o->d = f16_bits_to_f64(rd_u16(B + 208));
+    for (int g = 0; g < 16; ++g)
+        o->sc[g] = sc[g];
+    for (int h = 0; h < 2; ++h) {
+        for (int l = 0; l < 32; ++l) {
+            int hb = qh[32 * h + l];
+            int a = ql[64 * h + l];
+            int b = ql[64 * h + 32 + l];
+            o->q6[128 * h + l] = (a & 0xF) | (((hb >> 0) & 3) << 4);
+            o->q6[128 * h + 32 + l] = (b & 0xF) | (((hb >> 2) & 3) << 4);
+            o->q6[128 * h + 64 + l] = (a >> 4) | (((hb >> 4) & 3) << 4);
+            o->q6[128 * h + 96 + l] = (b >> 4) | (((hb >> 6) & 3) << 4);
+        }
+    }
+}
+
+/* ---- O3. Activation quantizer --------------------------------------------
+ * [GEMM, "The GPU path", "Activations get one scale per 32"]: int8 codes with one
+ * f32 scale per 32 values, with the product of the scale and the code sum stored
+ * beside it.  [CH04, section 2.1]: largest magnitude, then scale, then rounding.
+ * Readings R2, R3, R4.  Per token t, block k of 32:
+ *   amax = max |x|;  d = amax / 127;  q = roundf(x / d);  s = d * sum(q). */
+int oracle_quantize(const float* x, int nt, int id, int8_t* q, float* d, float* s)
+{
+    if (!x || !q || !d || !s || nt < 0 || id < 0 || id % 32)
+        return -1;
+    int nblk = id / 32;
+    for (int t = 0; t < nt; ++t) {
+        for (int k = 0; k < nblk; ++k) {
+            const float* xb = x + (size_t)t * id + 32 * k;
+            int8_t* qb = q + (size_t)t * id + 32 * k;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                float a = fabsf(xb[i]);
+                if (a > amax)
+                    amax = a;
+            }
+            float dk = amax / 127.0f;
+            int sum = 0;
+            if (dk == 0.0f) {
+                for (int i = 0; i < 32; ++i)
+                    qb[i] = 0;
+            } else {
+                for (int i = 0; i < 32; ++i) {
+                    float r = roundf(xb[i] / dk);
+                    int qi = (int)r;
+                    if (qi > 127 || qi < -127)
+                        return -2; /* cannot happen for finite input; kept as a check */
+                    qb[i] = (int8_t)qi;
+                    sum += qi;
+                }
+            }
+            d[(size_t)t * nblk + k] = dk;
+            s[(size_t)t * nblk + k] = dk * (float)sum;
+        }
+    }
+    return 0;
+}
+
+/* ---- O4. Per-scale-group integer dots --------------------------------------
+ * [GEMM, "The GPU path"]: a 32-weight Q4_K sub-block meets exactly one activation
+ * scale and is reduced as sum(q * qx) in integers; Q6_K reduces per 16-weight
+ * group.  Q4_K: S[t][r][b][j] = sum_{l<32} q(32j+l) * qx[t][256b+32j+l], codes
+ * 0..15 uncentred.  Q6_K: S[t][r][b][g] = sum_{l<16} (q6(16g+l) - 32) *
+ * qx[t][256b+16g+l]. */
+static int32_t dot_q4k_sub(const q4k_block* w, const int8_t* qx, int j)
+{
+    int32_t acc = 0;
+    for (int l = 0; l < 32; ++l)
+        acc += w->q[32 * j + l] * (int32_t)qx[32 * j + l];
+    return acc;
+}
+
+static int32_t dot_q6k_group(const q6k_block* w, const int8_t* qx, int g)
+{
+    int32_t acc = 0;
+    for (int l = 0; l < 16; ++l) {
+#if OQ_MUTATE == 2
+        acc += w->q6[16 * g + l] * (int32_t)qx[16 * g + l];
+#else
+        acc += (w->q6[16 * g + l] - 32) * (int32_t)qx[16 * g + l];
+#endif
+    }
+    return acc;
+}
+
+static size_t blk_bytes(int type) { return type == OQ_TYPE_Q4_K ? 144 : 210; }
+
+int oracle_subblock_dots(int type, const uint8_t* W, const int8_t* q, int nt, int od, int id,
+                         int32_t* S)
+{
+    if (!W || !q || !S || nt < 0 || od < 0 || id < 0 || id % 256)
+        return -1;
+    if (type != OQ_TYPE_Q4_K && type != OQ_TYPE_Q6_K)
+        return -2;
+    int nsb = id / 256;
+    int ng = type == OQ_TYPE_Q4_K ? 8 : 16;
+    size_t bb = blk_bytes(type);
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < od; ++r) {
+        for (int b = 0; b < nsb; ++b) {
+            const uint8_t* B = W + ((size_t)r * nsb + b) * bb;
+            q4k_block w4;
+            q6k_block w6;
+            if (type == OQ_TYPE_Q4_K)
+                q4k_decode(B, &w4);
+            else
+                q6k_decode(B, &w6);
+            for (int t = 0; t < nt; ++t) {
+                const int8_t* qx = q + (size_t)t * id + 256 * b;
+                int32_t* dst = S + (((size_t)t * od + r) * nsb + b) * ng;
+                for (int g = 0; g < ng; ++g)
+                    dst[g] = type == OQ_TYPE_Q4_K ? dot_q4k_sub(&w4, qx, g) : dot_q6k_group(&w6, qx, g);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ---- O5. Combine one output ------------------------------------------------
+ * [GEMM, "The GPU path"]: sum w x = d*sc*dx * sum(q*qx) - dmin*m * (dx*sum(qx)) per
+ * 32-weight sub-block; the second factor of the min term is the stored s.
+ * [GEMM, "Weights: 8 rows per register"]: the mins stay out of the integer
+ * loop.  Q6_K: d*sc_g*dx * sum((q6-32)*qx), dx the scale of the 32-block holding
+ * group g.  Every term in f64, summed in f64, one rounding to f32 at the end.
+ * mag receives sum |term| (used for the comparison tolerance). */
+static void one_output(int type, const uint8_t* Wrow, const int8_t* qx_t, const float* d_t,
+                       const float* s_t, int nsb, float* out, double* mag)
+{
+    double acc = 0.0, am = 0.0;
+    size_t bb = blk_bytes(type);
+    for (int b = 0; b < nsb; ++b) {
+        const uint8_t* B = Wrow + (size_t)b * bb;
+        const int8_t* qx = qx_t + 256 * b;
+        if (type == OQ_TYPE_Q4_K) {
+            q4k_block w;
+            q4k_decode(B, &w);
+            for (int j = 0; j < 8; ++j) {
+                double dx = (double)d_t[8 * b + j];
+                double sx = (double)s_t[8 * b + j];
+                double S = (double)dot_q4k_sub(&w, qx, j);
+                double tmain = (w.d * (double)w.sc[j]) * dx * S;
+#if OQ_MUTATE == 3
+                double tmin = 0.0 * sx;
+#else
+                double tmin = (w.dmin * (double)w.m[j]) * sx;
+#endif
+                acc += tmain - tmin;
+                am += fabs(tmain) + fabs(tmin);
+            }
+        } else {
+            q6k_block w;
+            q6k_decode(B, &w);
+            for (int g = 0; g < 16; ++g) {
+                double dx = (double)d_t[8 * b + g / 2];
+                double S = (double)dot_q6k_group(&w, qx, g);
+#if OQ_MUTATE == 5
+                double tm = (w.d * (double)w.sc[g / 2]) * dx * S;
+#else
+                double tm = (w.d * (double)w.sc[g]) * dx * S;
+#endif
+                acc += tm;
+                am += fabs(tm);
+            }
+        }
+    }
+    *out = (float)acc;
+    if (mag)
+        *mag = am;
+}
+
+int oracle_matmul_q8(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
+                     int nt, int od, int id, float* out, double* mag)
+{
+    if (!W || !q || !d || !s || !out || nt < 0 || od < 0 || id < 0 || id % 256)
+        return -1;
+    if (type != OQ_TYPE_Q4_K && type != OQ_TYPE_Q6_K)
+        return -2;
+    int nsb = id / 256;
+    size_t row_bytes = (size_t)nsb * blk_bytes(type);
+    long total = (long)nt * od;
+#pragma omp parallel for schedule(static)
+    for (long e = 0; e < total; ++e) {
+        int t = (int)(e / od), r = (int)(e % od);
+        one_output(type, W + (size_t)r * row_bytes, q + (size_t)t * id, d + (size_t)t * (id / 32),
+                   s + (size_t)t * (id / 32), nsb, out + (size_t)t * od + r, mag ? mag + (size_t)t * od + r : NULL);
+    }
+    return 0;
+}
+
+/* Selected outputs only: out[k] = output (t_idx[k], r_idx[k]). */
+int oracle_matmul_q8_points(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
+                            int nt, int od, int id, int npts, const int* t_idx, const int* r_idx,
+                            float* out, double* mag)
+{
+    if (!W || !q || !d || !s || !out || !t_idx || !r_idx || id % 256 || npts < 0)
+        return -1;
+    if (type != OQ_TYPE_Q4_K && type != OQ_TYPE_Q6_K)
+        return -2;
+    int nsb = id / 256;
+    size_t row_bytes = (size_t)nsb * blk_bytes(type);
+    for (int k = 0; k < npts; ++k)
+        if (t_idx[k] < 0 || t_idx[k] >= nt || r_idx[k] < 0 || r_idx[k] >= od)
+            return -3;
+#pragma omp parallel for schedule(static)
+    for (int k = 0; k < npts; ++k) {
+        int t = t_idx[k], r = r_idx[k];
+        one_output(type, W + (size_t)r * row_bytes, q + (size_t)t * id, d + (size_t)t * (id / 32),
+                   s + (size_t)t * (id / 32), nsb, out + k, mag ? mag + k : NULL);
+    }
+    return 0;
+}
+
+/* The whole path: quantize the activations, then combine.  q, d, s are scratch
+ * buffers the caller provides (nt*id int8, nt*id/32 floats each). */
+int oracle_matmul(int type, const uint8_t* W, const float* x, int nt, int od, int id, int8_t* q,
+                  float* d, float* s, float* out, double* mag)
+{
+    int rc = oracle_quantize(x, nt, id, q, d, s);
+    if (rc)
+        return rc;
+    return oracle_matmul_q8(type, W, q, d, s, nt, od, id, out, mag);
+}
+
+/* Decoded fields of one super-block, for the pins: Q4_K fills d, dmin, sc[8], m[8],
+ * codes[256]; Q6_K fills d, sc[16], codes[256] (stored 0..63). */
+int oracle_decode_block(int type, const uint8_t* B, double* d, double* dmin, int* sc, int* m, int* codes)
+{
+    if (type == OQ_TYPE_Q4_K) {
+        q4k_block w;
+        q4k_decode(B, &w);
+        *d = w.d;
+        *dmin = w.dmin;
+        memcpy(sc, w.sc, sizeof w.sc);
+        memcpy(m, w.m, sizeof w.m);
+        memcpy(codes, w.q, sizeof w.q);
+        return 0;
+    }
+    if (type == OQ_TYPE_Q6_K) {
+        q6k_block w;
+        q6k_decode(B, &w);
+        *d = w.d;
+        *dmin = 0.0;
+        memcpy(sc, w.sc, sizeof w.sc);
+        memcpy(codes, w.q6, sizeof w.q6);
+        return 0;
+    }
+    return -2;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
