@@ -1,0 +1,151 @@
+/*
+ * qmm.h -- C ABI of libqmm, the quantized-weight matmul for MI355X (gfx950).
+ *
+ *   out[t][r] = sum_i W[r][i] * x[t][i]
+ *
+ * W stays in GGUF-style super-blocks of 256 weights; x is quantized on the
+ * device to int8 blocks of 32 with an f32 scale d and the f32 product
+ * s = d * sum(q); each scale group of W meets one activation block and is
+ * reduced as an integer dot, and the weight min folds out through the identity
+ *   sum w x = d*sc*dx * sum(q*qx) - dmin*m * (dx*sum(qx)).
+ *
+ * Pages cited (by title, section in brackets):
+ *   [GEMM] "The quantized GEMM" (mojo-dllm kernels page)
+ *   [MMQ]  "llama.cpp MMQ -- quantized-weight int8 tensor-core matmul: structure,
+ *          numerics, SASS census, and minfer contrast"
+ *   [CH04] "04 - Reading minfer's kernels II -- from GEMV to tiled GEMM"
+ *
+ * Conventions (all entry points):
+ *  - Pointers named W, x, q, d, s, out, S, workspace are DEVICE pointers owned by
+ *    the caller; the library allocates nothing and keeps no state beyond a
+ *    per-device property cache.  `stream` is a hipStream_t (NULL = default stream).
+ *  - Calls are asynchronous: QMM_OK means "validated and enqueued".  Faults of
+ *    the device surface at the caller's next synchronisation.
+ *  - Validation happens before any device work; on an error nothing is enqueued
+ *    and no output is touched.
+ *  - Layouts: W row-major [od][id/256] super-blocks (row r is id/256 contiguous
+ *    blocks); x token-major [nt][id] f32; q [nt][id] int8; d and s [nt][id/32] f32;
+ *    out [nt][od] f32, fully overwritten.  [CH04, section 3.3]: weights arrive
+ *    row-major [out][in]; [GEMM, "The shape of the problem"].
+ *  - Shape rules: nt >= 1, od >= 1, id >= 256 and id % 256 == 0 (whole
+ *    super-blocks); nt*id and od*(id/256) must fit in 31 bits.
+ *  - Alignment: W, x, q, d, s, out and workspace must be 16-byte aligned.
+ *  - Inputs must be finite (NaN/Inf behaviour is unspecified).
+ *  - Only gfx950 devices are accepted (QMM_ERR_DEVICE otherwise); there is no
+ *    CPU fallback and no second device path.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats.  Own ids (other tables number these types differently). */
+enum {
+    /* [GEMM, "The GPU path"]; [MMQ, sections 4 and 6]: 144 bytes per 256 weights:
+     * f16 d | f16 dmin | 12 bytes packing eight 6-bit (scale, min) pairs | 128
+     * bytes of 4-bit codes (code chunk p: byte l holds sub-block 2p low, 2p+1
+     * high, position l).  w = d*sc*q - dmin*m, q in 0..15. */
+    QMM_TYPE_Q4_K = 1,
+    /* [GEMM, "Q6_K: the same layout and prefetch"]; [MMQ, section 4]: 210 bytes
+     * per 256 weights: 128 bytes low 4-bit fields | 64 bytes high 2-bit fields |
+     * 16 int8 scales (one per 16 weights) | f16 d.  w = d*sc*(q6 - 32).  The
+     * element-to-bit map inside the two planes is the public GGUF arrangement
+     * (two halves of 128 elements), a reading the pages leave open. */
+    QMM_TYPE_Q6_K = 2
+};
+
+/* Status codes. */
+enum {
+    QMM_OK = 0,
+    QMM_ERR_ARG = -1,       /* null pointer, nt/od < 1, bad kind selector */
+    QMM_ERR_TYPE = -2,      /* unknown weight type */
+    QMM_ERR_SHAPE = -3,     /* id not a positive multiple of 256, or sizes too large */
+    QMM_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
+    QMM_ERR_WORKSPACE = -5, /* workspace smaller than qmm_act_bytes(nt, id) */
+    QMM_ERR_DEVICE = -6,    /* current device is not gfx950, or no device */
+    QMM_ERR_LAUNCH = -7     /* a kernel launch reported an error */
+};
+
+/* Dispatch kinds. */
+enum {
+    QMM_KIND_MMVQ = 1, /* nt <= switch: weights streamed once, tokens in registers */
+    QMM_KIND_MMQ = 2   /* nt > switch: tiled int8 MFMA GEMM */
+};
+
+/* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K) or *210
+ * (Q6_K).  0 for an unknown type or a bad shape. */
+size_t qmm_weight_bytes(int type, int od, int id);
+
+/* Workspace bytes qmm_matmul needs for nt tokens of id values: the q8 plane
+ * (nt*id int8, rounded up to 256 B) then d and s (nt*id/32 f32 each, each rounded
+ * up to 256 B).  0 for a bad shape. */
+size_t qmm_act_bytes(int nt, int id);
+
+/* Quantize activations to int8 blocks of 32.
+ * [GEMM, "The GPU path", "Activations get one scale per 32"]; [CH04, section 2.1].
+ * Per token t and block k of 32 values: amax = max|x|, d = amax/127 (IEEE f32
+ * divide), q = round(x/d) with ties away from zero (IEEE divide), s = d*sum(q);
+ * a block of zeros gives d = 0, q = 0, s = 0.  One wave64 handles 8 blocks with
+ * 16-byte loads and cross-lane max / sum reductions.
+ * x: [nt][id] f32 in; q: [nt][id] int8 out; d, s: [nt][id/32] f32 out.
+ * Shape rule here: id % 32 == 0 (any id >= 32). */
+int qmm_quantize_act(const float* x, int nt, int id, int8_t* q, float* d, float* s, void* stream);
+
+/* The whole path: quantize x into `workspace`, then dispatch on nt.
+ * [CH04, section 3.3]: one matmul call takes raw pointers, f32 activations, the
+ * weight type and the shape, and quantizes the activations itself; invalid shapes
+ * are errors, never a silent fallback.  [MMQ, section 12]: every nt has a kernel:
+ * nt <= 8 (QMM_NT_SWITCH) runs MMVQ, larger nt runs MMQ.
+ * workspace: device buffer of at least qmm_act_bytes(nt, id) bytes, used as
+ * scratch (overwritten); ws_bytes its size. */
+int qmm_matmul(int type, const void* W, const float* x, int nt, int od, int id, float* out,
+               void* workspace, size_t ws_bytes, void* stream);
+
+/* The matmul on already quantized activations (reuse one quantized input for
+ * several weight matrices).  q, d, s as produced by qmm_quantize_act. */
+int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, const float* s, int nt,
+                  int od, int id, float* out, void* stream);
+
+/* Same as qmm_matmul_q8 but with the kernel chosen by the caller (kind =
+ * QMM_KIND_MMVQ for nt <= 8 only, or QMM_KIND_MMQ for any nt).  For tests and
+ * measurement of both kernels on one shape. */
+int qmm_matmul_q8_kind(int kind, int type, const void* W, const int8_t* q, const float* d,
+                       const float* s, int nt, int od, int id, float* out, void* stream);
+
+/* Which kernel qmm_matmul would run for this call: QMM_KIND_MMVQ or QMM_KIND_MMQ,
+ * or a negative status for invalid arguments. */
+int qmm_dispatch_kind(int type, int nt, int od, int id);
+
+/* The nt at or below which MMVQ runs (default 8; environment QMM_NT_SWITCH,
+ * clamped to 0..8, read once). */
+int qmm_nt_switch(void);
+
+/* Diagnostic: the integer stage of a kernel alone.  [GEMM, "The GPU path"]: each
+ * scale group (32 weights for Q4_K, 16 for Q6_K) is reduced as an integer dot
+ * with its activation codes.  Writes S[t][r][b][g] = sum over group g of super-
+ * block b of row r of (code * qx) -- codes 0..15 uncentred for Q4_K, (q6 - 32) for
+ * Q6_K -- as int32, computed by the unpack and dot code of the kernel `kind`
+ * (QMM_KIND_MMVQ: v_dot4 path, nt <= 8; QMM_KIND_MMQ: int8 MFMA path).
+ * S: [nt][od][id/256][8 or 16] int32, 16-byte aligned. */
+int qmm_group_dots(int kind, int type, const void* W, const int8_t* q, int nt, int od, int id,
+                   int32_t* S, void* stream);
+
+/* Diagnostic: one 32 x 32 x 32 int8 MFMA tile with the operand and result lane
+ * mapping the MMQ kernel relies on.  A: [32 rows][32 K] int8, B: [32 tokens][32 K]
+ * int8 (both row-major, 16-byte aligned), C: [32 tokens][32 rows] int32 receives
+ * B . A^T when the mapping holds.  For a test that pins the MFMA lane layout. */
+int qmm_mfma_tile_check(const int8_t* A, const int8_t* B, int32_t* C, void* stream);
+
+/* Short text for a status code (static storage). */
+const char* qmm_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMM_H */

@@ -1,0 +1,195 @@
+"""quantized_matmul_amd: Python binding of libqmm (the quantized-weight matmul for
+MI355X / gfx950).
+
+The binding only marshals arguments: tensors become device pointers, the current
+torch stream becomes the hipStream_t, status codes become exceptions.  Every step
+of the computation runs in the library's HIP kernels; there is no CPU path.
+PyTorch provides device memory and streams.
+
+Entry points mirror include/qmm.h (same names).  Weight types: QMM_TYPE_Q4_K,
+QMM_TYPE_Q6_K.  Layouts: W uint8 [od * id/256 * block bytes] row-major super-blocks;
+x f32 [nt, id]; q int8 [nt, id]; d, s f32 [nt, id/32]; out f32 [nt, od].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so libqmm binds to the HIP runtime torch already mapped
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmm.so")
+
+QMM_TYPE_Q4_K = 1
+QMM_TYPE_Q6_K = 2
+QMM_KIND_MMVQ = 1
+QMM_KIND_MMQ = 2
+QMM_OK = 0
+QMM_ERR_ARG = -1
+QMM_ERR_TYPE = -2
+QMM_ERR_SHAPE = -3
+QMM_ERR_ALIGN = -4
+QMM_ERR_WORKSPACE = -5
+QMM_ERR_DEVICE = -6
+QMM_ERR_LAUNCH = -7
+
+BLOCK_BYTES = {QMM_TYPE_Q4_K: 144, QMM_TYPE_Q6_K: 210}
+
+EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8",
+           "qmm_matmul_q8_kind", "qmm_dispatch_kind", "qmm_nt_switch", "qmm_group_dots",
+           "qmm_mfma_tile_check", "qmm_strerror")
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libqmm (ctypes).  Raises if the library was not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                              "(there is no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.qmm_weight_bytes.argtypes = [I, I, I]
+        L.qmm_weight_bytes.restype = Z
+        L.qmm_act_bytes.argtypes = [I, I]
+        L.qmm_act_bytes.restype = Z
+        L.qmm_quantize_act.argtypes = [P, I, I, P, P, P, P]
+        L.qmm_matmul.argtypes = [I, P, P, I, I, I, P, P, Z, P]
+        L.qmm_matmul_q8.argtypes = [I, P, P, P, P, I, I, I, P, P]
+        L.qmm_matmul_q8_kind.argtypes = [I, I, P, P, P, P, I, I, I, P, P]
+        L.qmm_dispatch_kind.argtypes = [I, I, I, I]
+        L.qmm_nt_switch.argtypes = []
+        L.qmm_group_dots.argtypes = [I, I, P, P, I, I, I, P, P]
+        L.qmm_mfma_tile_check.argtypes = [P, P, P, P]
+        L.qmm_strerror.argtypes = [I]
+        L.qmm_strerror.restype = ctypes.c_char_p
+        for f in ("qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8", "qmm_matmul_q8_kind",
+                  "qmm_dispatch_kind", "qmm_nt_switch", "qmm_group_dots", "qmm_mfma_tile_check"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return lib().qmm_strerror(int(status)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != QMM_OK:
+        raise QmmError(rc, what)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> ctypes.c_void_p:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def qmm_weight_bytes(qtype: int, od: int, idim: int) -> int:
+    return int(lib().qmm_weight_bytes(qtype, od, idim))
+
+
+def qmm_act_bytes(nt: int, idim: int) -> int:
+    return int(lib().qmm_act_bytes(nt, idim))
+
+
+def qmm_nt_switch() -> int:
+    return int(lib().qmm_nt_switch())
+
+
+def qmm_dispatch_kind(qtype: int, nt: int, od: int, idim: int) -> int:
+    k = int(lib().qmm_dispatch_kind(qtype, nt, od, idim))
+    if k < 0:
+        raise QmmError(k, "qmm_dispatch_kind")
+    return k
+
+
+def qmm_quantize_act(x: torch.Tensor, q=None, d=None, s=None, stream=None):
+    """x f32 [nt, id] -> (q int8 [nt, id], d f32 [nt, id/32], s f32 [nt, id/32])."""
+    nt, idim = x.shape
+    if q is None:
+        q = torch.empty((nt, idim), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((nt, idim // 32), dtype=torch.float32, device=x.device)
+    if s is None:
+        s = torch.empty((nt, idim // 32), dtype=torch.float32, device=x.device)
+    _check(lib().qmm_quantize_act(_dev(x, torch.float32, "x"), nt, idim, _dev(q, torch.int8, "q"),
+                                  _dev(d, torch.float32, "d"), _dev(s, torch.float32, "s"), _stream(stream)),
+           "qmm_quantize_act")
+    return q, d, s
+
+
+def qmm_matmul(qtype: int, W: torch.Tensor, x: torch.Tensor, od: int, out=None, workspace=None, stream=None):
+    """out f32 [nt, od] = quantize(x) then the nt-dispatched kernel."""
+    nt, idim = x.shape
+    if out is None:
+        out = torch.empty((nt, od), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(qmm_act_bytes(nt, idim), 1), dtype=torch.uint8, device=x.device)
+    _check(lib().qmm_matmul(qtype, _dev(W, torch.uint8, "W"), _dev(x, torch.float32, "x"), nt, od, idim,
+                            _dev(out, torch.float32, "out"), _dev(workspace, torch.uint8, "workspace"),
+                            workspace.numel(), _stream(stream)), "qmm_matmul")
+    return out
+
+
+def qmm_matmul_q8(qtype: int, W: torch.Tensor, q: torch.Tensor, d: torch.Tensor, s: torch.Tensor, od: int,
+                  out=None, stream=None):
+    nt, idim = q.shape
+    if out is None:
+        out = torch.empty((nt, od), dtype=torch.float32, device=q.device)
+    _check(lib().qmm_matmul_q8(qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"),
+                               _dev(d, torch.float32, "d"), _dev(s, torch.float32, "s"), nt, od, idim,
+                               _dev(out, torch.float32, "out"), _stream(stream)), "qmm_matmul_q8")
+    return out
+
+
+def qmm_matmul_q8_kind(kind: int, qtype: int, W, q, d, s, od: int, out=None, stream=None):
+    nt, idim = q.shape
+    if out is None:
+        out = torch.empty((nt, od), dtype=torch.float32, device=q.device)
+    _check(lib().qmm_matmul_q8_kind(kind, qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"),
+                                    _dev(d, torch.float32, "d"), _dev(s, torch.float32, "s"), nt, od, idim,
+                                    _dev(out, torch.float32, "out"), _stream(stream)), "qmm_matmul_q8_kind")
+    return out
+
+
+def qmm_group_dots(kind: int, qtype: int, W: torch.Tensor, q: torch.Tensor, od: int, S=None, stream=None):
+    """int32 [nt, od, id/256, 8 or 16] per-scale-group integer dots from kernel `kind`."""
+    nt, idim = q.shape
+    ng = 8 if qtype == QMM_TYPE_Q4_K else 16
+    if S is None:
+        S = torch.empty((nt, od, idim // 256, ng), dtype=torch.int32, device=q.device)
+    _check(lib().qmm_group_dots(kind, qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"), nt, od,
+                                idim, _dev(S, torch.int32, "S"), _stream(stream)), "qmm_group_dots")
+    return S
+
+
+def qmm_mfma_tile_check(A: torch.Tensor, B: torch.Tensor, C=None, stream=None):
+    if C is None:
+        C = torch.empty((32, 32), dtype=torch.int32, device=A.device)
+    _check(lib().qmm_mfma_tile_check(_dev(A, torch.int8, "A"), _dev(B, torch.int8, "B"), _dev(C, torch.int32, "C"),
+                                     _stream(stream)), "qmm_mfma_tile_check")
+    return C

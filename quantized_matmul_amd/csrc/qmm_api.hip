@@ -1,0 +1,262 @@
+// C ABI of libqmm: argument validation, workspace layout, nt dispatch.
+// Declarations and their contracts are in include/qmm.h.
+//
+// [CH04, section 3.3]: one entry point takes raw pointers, the weight type and the
+// shape and decides the kernel from nt; shapes it cannot serve are errors, never a
+// silent fallback.  [MMQ, section 12.1]: nt <= 8 runs the vector kernel, larger nt
+// the matrix kernel, so every nt has a dedicated kernel.
+#include <stdlib.h>
+#include <string.h>
+
+#include "qmm.h"
+#include "qmm_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+int check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return QMM_ERR_DEVICE;
+    if (dev >= kMaxDevices)
+        return QMM_ERR_DEVICE;
+    int st = __atomic_load_n(&g_dev_state[dev], __ATOMIC_ACQUIRE);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return QMM_ERR_DEVICE;
+        st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+        __atomic_store_n(&g_dev_state[dev], st, __ATOMIC_RELEASE);
+    }
+    return st == 1 ? QMM_OK : QMM_ERR_DEVICE;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+int check_type(int type) { return (type == QMM_TYPE_Q4_K || type == QMM_TYPE_Q6_K) ? QMM_OK : QMM_ERR_TYPE; }
+
+// Shape rule shared by the matmul entry points.
+int check_shape(int nt, int od, int id)
+{
+    if (nt < 1 || od < 1)
+        return QMM_ERR_ARG;
+    if (id < 256 || id % 256 != 0)
+        return QMM_ERR_SHAPE;
+    if ((long long)nt * id > 0x7FFFFFFFLL || (long long)od * (id / 256) > 0x7FFFFFFFLL ||
+        (long long)nt * od > 0x7FFFFFFFLL)
+        return QMM_ERR_SHAPE;
+    return QMM_OK;
+}
+
+int nt_switch_value()
+{
+    static int v = -1;
+    int cur = __atomic_load_n(&v, __ATOMIC_ACQUIRE);
+    if (cur >= 0)
+        return cur;
+    int val = 8;
+    const char* e = getenv("QMM_NT_SWITCH");
+    if (e && *e) {
+        val = atoi(e);
+        if (val < 0)
+            val = 0;
+        if (val > 8)
+            val = 8;
+    }
+    __atomic_store_n(&v, val, __ATOMIC_RELEASE);
+    return val;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH; }
+
+int matmul_q8_checked(int kind, int type, const void* W, const int8_t* q, const float* d,
+                      const float* s, int nt, int od, int id, float* out, int32_t* S, void* stream)
+{
+    const auto st = reinterpret_cast<hipStream_t>(stream);
+    const auto w = reinterpret_cast<const uint8_t*>(W);
+    if (kind == QMM_KIND_MMVQ)
+        return launched(qmm::launch_mmvq(type, w, q, d, s, nt, od, id, out, S, st));
+    return launched(qmm::launch_mmq(type, w, q, d, s, nt, od, id, out, S, st));
+}
+
+int validate_q8(int type, const void* W, const int8_t* q, const float* d, const float* s, int nt,
+                int od, int id, const void* out)
+{
+    if (!W || !q || !d || !s || !out)
+        return QMM_ERR_ARG;
+    int rc = check_type(type);
+    if (rc)
+        return rc;
+    rc = check_shape(nt, od, id);
+    if (rc)
+        return rc;
+    if (!aligned16(W) || !aligned16(q) || !aligned16(d) || !aligned16(s) || !aligned16(out))
+        return QMM_ERR_ALIGN;
+    return QMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qmm_weight_bytes(int type, int od, int id)
+{
+    if (check_type(type) || od < 1 || id < 256 || id % 256)
+        return 0;
+    return (size_t)od * (size_t)(id / 256) * (type == QMM_TYPE_Q4_K ? qmm::kQ4KBytes : qmm::kQ6KBytes);
+}
+
+size_t qmm_act_bytes(int nt, int id)
+{
+    if (nt < 1 || id < 32 || id % 32)
+        return 0;
+    const size_t n = (size_t)nt * (size_t)id;
+    return round256(n) + 2 * round256(n / 32 * sizeof(float));
+}
+
+int qmm_quantize_act(const float* x, int nt, int id, int8_t* q, float* d, float* s, void* stream)
+{
+    if (!x || !q || !d || !s || nt < 1)
+        return QMM_ERR_ARG;
+    if (id < 32 || id % 32 || (long long)nt * id > 0x7FFFFFFFLL)
+        return QMM_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || !aligned16(d) || !aligned16(s))
+        return QMM_ERR_ALIGN;
+    int rc = check_device();
+    if (rc)
+        return rc;
+    return launched(qmm::launch_quantize(x, nt, id, q, d, s, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qmm_nt_switch(void) { return nt_switch_value(); }
+
+int qmm_dispatch_kind(int type, int nt, int od, int id)
+{
+    int rc = check_type(type);
+    if (rc)
+        return rc;
+    rc = check_shape(nt, od, id);
+    if (rc)
+        return rc;
+    return nt <= nt_switch_value() ? QMM_KIND_MMVQ : QMM_KIND_MMQ;
+}
+
+int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, const float* s, int nt,
+                  int od, int id, float* out, void* stream)
+{
+    int rc = validate_q8(type, W, q, d, s, nt, od, id, out);
+    if (rc)
+        return rc;
+    rc = check_device();
+    if (rc)
+        return rc;
+    const int kind = nt <= nt_switch_value() ? QMM_KIND_MMVQ : QMM_KIND_MMQ;
+    return matmul_q8_checked(kind, type, W, q, d, s, nt, od, id, out, nullptr, stream);
+}
+
+int qmm_matmul_q8_kind(int kind, int type, const void* W, const int8_t* q, const float* d,
+                       const float* s, int nt, int od, int id, float* out, void* stream)
+{
+    if (kind != QMM_KIND_MMVQ && kind != QMM_KIND_MMQ)
+        return QMM_ERR_ARG;
+    int rc = validate_q8(type, W, q, d, s, nt, od, id, out);
+    if (rc)
+        return rc;
+    if (kind == QMM_KIND_MMVQ && nt > 8)
+        return QMM_ERR_ARG;
+    rc = check_device();
+    if (rc)
+        return rc;
+    return matmul_q8_checked(kind, type, W, q, d, s, nt, od, id, out, nullptr, stream);
+}
+
+int qmm_matmul(int type, const void* W, const float* x, int nt, int od, int id, float* out,
+               void* workspace, size_t ws_bytes, void* stream)
+{
+    if (!W || !x || !out || !workspace)
+        return QMM_ERR_ARG;
+    int rc = check_type(type);
+    if (rc)
+        return rc;
+    rc = check_shape(nt, od, id);
+    if (rc)
+        return rc;
+    if (!aligned16(W) || !aligned16(x) || !aligned16(out) || !aligned16(workspace))
+        return QMM_ERR_ALIGN;
+    if (ws_bytes < qmm_act_bytes(nt, id))
+        return QMM_ERR_WORKSPACE;
+    rc = check_device();
+    if (rc)
+        return rc;
+    const size_t n = (size_t)nt * (size_t)id;
+    auto* base = static_cast<uint8_t*>(workspace);
+    auto* q = reinterpret_cast<int8_t*>(base);
+    auto* d = reinterpret_cast<float*>(base + round256(n));
+    auto* s = reinterpret_cast<float*>(base + round256(n) + round256(n / 32 * sizeof(float)));
+    const auto st = reinterpret_cast<hipStream_t>(stream);
+    rc = launched(qmm::launch_quantize(x, nt, id, q, d, s, st));
+    if (rc)
+        return rc;
+    const int kind = nt <= nt_switch_value() ? QMM_KIND_MMVQ : QMM_KIND_MMQ;
+    return matmul_q8_checked(kind, type, W, q, d, s, nt, od, id, out, nullptr, stream);
+}
+
+int qmm_group_dots(int kind, int type, const void* W, const int8_t* q, int nt, int od, int id,
+                   int32_t* S, void* stream)
+{
+    if (!W || !q || !S)
+        return QMM_ERR_ARG;
+    if (kind != QMM_KIND_MMVQ && kind != QMM_KIND_MMQ)
+        return QMM_ERR_ARG;
+    int rc = check_type(type);
+    if (rc)
+        return rc;
+    rc = check_shape(nt, od, id);
+    if (rc)
+        return rc;
+    if (kind == QMM_KIND_MMVQ && nt > 8)
+        return QMM_ERR_ARG;
+    if (!aligned16(W) || !aligned16(q) || !aligned16(S))
+        return QMM_ERR_ALIGN;
+    rc = check_device();
+    if (rc)
+        return rc;
+    // the integer stage does not use the activation scales; the code buffer (at
+    // least 8x larger than a scale plane) stands in so any scale read stays in bounds
+    const float* dummy = reinterpret_cast<const float*>(q);
+    return matmul_q8_checked(kind, type, W, q, dummy, dummy, nt, od, id, nullptr, S, stream);
+}
+
+int qmm_mfma_tile_check(const int8_t* A, const int8_t* B, int32_t* C, void* stream)
+{
+    if (!A || !B || !C)
+        return QMM_ERR_ARG;
+    if (!aligned16(A) || !aligned16(B) || !aligned16(C))
+        return QMM_ERR_ALIGN;
+    int rc = check_device();
+    if (rc)
+        return rc;
+    return launched(qmm::launch_mfma_tile_probe(A, B, C, reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char* qmm_strerror(int status)
+{
+    switch (status) {
+    case QMM_OK: return "ok";
+    case QMM_ERR_ARG: return "invalid argument (null pointer, nt or od < 1, or bad kind)";
+    case QMM_ERR_TYPE: return "unknown weight type";
+    case QMM_ERR_SHAPE: return "bad shape (id must be a positive multiple of 256; sizes must fit 31 bits)";
+    case QMM_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case QMM_ERR_WORKSPACE: return "workspace too small (see qmm_act_bytes)";
+    case QMM_ERR_DEVICE: return "current device is not gfx950";
+    case QMM_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,80 @@
+// Internal declarations and device helpers of libqmm (HIP, gfx950 only).
+//
+// Pages cited (by title, section in brackets):
+//   [GEMM] "The quantized GEMM" (mojo-dllm kernels page)
+//   [MMQ]  "llama.cpp MMQ -- quantized-weight int8 tensor-core matmul: structure,
+//          numerics, SASS census, and minfer contrast"
+//   [CH04] "04 - Reading minfer's kernels II -- from GEMV to tiled GEMM"
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmm {
+
+constexpr int kQK = 256;          // weights per super-block
+constexpr int kQ4KBytes = 144;    // Q4_K super-block
+constexpr int kQ6KBytes = 210;    // Q6_K super-block
+constexpr int kActBlock = 32;     // activation values per scale
+
+// Launchers (return hipError_t of the launch).  All pointers are device
+// pointers validated by the C ABI layer; shapes satisfy id % 256 == 0.
+hipError_t launch_quantize(const float* x, int nt, int id, int8_t* q, float* d, float* s,
+                           hipStream_t st);
+hipError_t launch_mmvq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
+                       int nt, int od, int id, float* out, int32_t* S, hipStream_t st);
+hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
+                      int nt, int od, int id, float* out, int32_t* S, hipStream_t st);
+hipError_t launch_mfma_tile_probe(const int8_t* A, const int8_t* B, int32_t* C, hipStream_t st);
+
+// ---------------------------------------------------------------- device helpers
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
+{
+    _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)h);
+    return (float)v;
+}
+
+// DPP lane moves inside one wave64 (all lanes active).
+__device__ __forceinline__ int dpp_quad_xor1(int v) { return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_quad_xor2(int v) { return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_half_mirror(int v) { return __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false); }
+
+__device__ __forceinline__ int sdot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
+
+// Q4_K (scale, min) of sub-block j from header dwords h1 = bytes 4..7, h2 = 8..11,
+// h3 = 12..15.  [MMQ, section 6, get_scale_min_k4 semantics]: j < 4 takes the low
+// six bits of byte j (scale) and of byte j+4 (min); j >= 4 takes a nibble of byte
+// j+4 for the low four bits and the top two bits of byte j-4 (scale) or byte j
+// (min) for the high two.
+__device__ __forceinline__ void q4k_scale_min(uint32_t h1, uint32_t h2, uint32_t h3, int j, int& sc,
+                                              int& m)
+{
+    const int jj = j & 3;
+    const int sh = 8 * jj;
+    const uint32_t b1 = (h1 >> sh) & 0xFF, b2 = (h2 >> sh) & 0xFF, b3 = (h3 >> sh) & 0xFF;
+    if (j < 4) {
+        sc = (int)(b1 & 63);
+        m = (int)(b2 & 63);
+    } else {
+        sc = (int)((b3 & 0xF) | ((b1 >> 6) << 4));
+        m = (int)((b3 >> 4) | ((b2 >> 6) << 4));
+    }
+}
+
+// Q6_K: build four signed codes (q6 - 32) from a dword of low fields and a dword
+// of high 2-bit fields.  [GEMM, "Q6_K: the same layout and prefetch"]: the code is
+// the nibble plus the two high bits, and the offset 32 comes off by flipping the
+// bias into a sign: (q | 0x80) - 0x20 never borrows across bytes, ^ 0x80 then
+// gives q - 32 as int8.
+__device__ __forceinline__ int q6_center4(uint32_t low4, uint32_t high2)
+{
+    const uint32_t q = low4 | (high2 << 4);
+    return (int)(((q | 0x80808080u) - 0x20202020u) ^ 0x80808080u);
+}
+
+}  // namespace qmm

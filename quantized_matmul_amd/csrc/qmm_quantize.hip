@@ -1,0 +1,76 @@
+// Activation quantizer: f32 [nt][id] -> int8 codes, f32 scale d and f32 d*sum(q)
+// per block of 32 values.
+//
+// [GEMM, "The GPU path", "Activations get one scale per 32"]: int8 codes with one
+// f32 scale per 32 values and the scale times the code sum stored beside it; a
+// 32-value block is handled by one group of lanes with cross-lane max and sum
+// reductions so loads and stores stay coalesced.  [CH04, section 2.1]: largest
+// magnitude, scale, round.  Readings (the pages leave them open): d = amax / 127
+// by IEEE division, q = round(x / d) half away from zero by IEEE division, a zero
+// block gives d = q = s = 0, s = d * (float)sum(q) with one rounding.
+//
+// wave64 mapping: each lane loads 16 bytes (four values), eight lanes hold one
+// block, a wave covers eight blocks = 1 KiB of input.  The eight-lane max and sum
+// use DPP (two quad permutes and a half-row mirror) -- no LDS.  Each lane stores
+// its four codes as one dword; the first lane of each block stores d and s.
+#include "qmm_internal.h"
+
+namespace qmm {
+
+__global__ __launch_bounds__(256) void quantize_q8_kernel(const float4* __restrict__ x, int nblk,
+                                                          uint32_t* __restrict__ q,
+                                                          float* __restrict__ d,
+                                                          float* __restrict__ s)
+{
+    const int g = blockIdx.x * 256 + threadIdx.x;  // index of this lane's four values
+    const int blk = g >> 3;
+    const bool valid = blk < nblk;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (valid)
+        v = x[g];
+
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    int ai = __builtin_bit_cast(int, a);  // non-negative floats order like their bits
+    ai = max(ai, dpp_quad_xor1(ai));
+    ai = max(ai, dpp_quad_xor2(ai));
+    ai = max(ai, dpp_half_mirror(ai));
+    const float amax = __builtin_bit_cast(float, ai);
+
+    const float dk = amax / 127.0f;
+    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+    if (dk != 0.0f) {
+        q0 = (int)roundf(v.x / dk);
+        q1 = (int)roundf(v.y / dk);
+        q2 = (int)roundf(v.z / dk);
+        q3 = (int)roundf(v.w / dk);
+    }
+    int sum = q0 + q1 + q2 + q3;
+    sum += dpp_quad_xor1(sum);
+    sum += dpp_quad_xor2(sum);
+    sum += dpp_half_mirror(sum);
+
+    if (valid) {
+        q[g] = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
+               ((uint32_t)(q3 & 0xFF) << 24);
+        if ((threadIdx.x & 7) == 0) {
+            d[blk] = dk;
+            s[blk] = dk * (float)sum;
+        }
+    }
+}
+
+hipError_t launch_quantize(const float* x, int nt, int id, int8_t* q, float* d, float* s,
+                           hipStream_t st)
+{
+    const long nvals = (long)nt * id;
+    const int nblk = (int)(nvals / kActBlock);
+    const long lanes = nvals / 4;
+    const int grid = (int)((lanes + 255) / 256);
+    if (grid == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(quantize_q8_kernel, dim3(grid), dim3(256), 0, st,
+                       reinterpret_cast<const float4*>(x), nblk, reinterpret_cast<uint32_t*>(q), d, s);
+    return hipGetLastError();
+}
+
+}  // namespace qmm

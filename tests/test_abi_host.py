@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+function include/qmm.h declares, sizes follow their closed forms, and argument
+validation answers before any device work."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_matmul_amd as qmm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "qmm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert "qmm_matmul" in names and "qmm_quantize_act" in names
+    L = qmm.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(qmm.EXPORTS)
+
+
+def test_weight_bytes_closed_forms():
+    assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q4_K, 1, 256) == 144
+    assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q6_K, 1, 256) == 210
+    assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q4_K, 1024, 4096) == 2_359_296
+    assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q4_K, 12288, 4096) == 28_311_552
+    assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q6_K, 32000, 4096) == 107_520_000
+    # "The quantized GEMM", Q6_K paragraph: 6,217,728 Q6_K blocks in the output,
+    # 16 attn_v and 16 ffn_down tensors of an 8B model (vocab 126464, hidden 4096,
+    # FFN 12288); 12 more bytes each is 74,612,736 bytes (74.6 MB, 71.2 MiB).
+    nblk = (qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q6_K, 126464, 4096)
+            + 16 * qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q6_K, 4096, 4096)
+            + 16 * qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q6_K, 4096, 12288)) // 210
+    assert nblk == 6_217_728
+    assert nblk * 12 == 74_612_736 and round(nblk * 12 / 2**20, 1) == 71.2
+    assert qmm.qmm_weight_bytes(7, 1, 256) == 0
+    assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q4_K, 1, 300) == 0
+
+
+def test_act_bytes():
+    # q8 plane then d then s, each rounded up to 256 bytes
+    assert qmm.qmm_act_bytes(1, 4096) == 4096 + 2 * 512
+    assert qmm.qmm_act_bytes(3, 256) == 768 + 2 * 256
+    assert qmm.qmm_act_bytes(512, 12288) == 512 * 12288 + 2 * 512 * 384 * 4
+    assert qmm.qmm_act_bytes(0, 256) == 0 and qmm.qmm_act_bytes(1, 33) == 0
+
+
+def test_dispatch_kind_host():
+    assert qmm.qmm_nt_switch() == 8
+    for nt in range(1, 9):
+        assert qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q4_K, nt, 4096, 4096) == qmm.QMM_KIND_MMVQ
+    for nt in (9, 16, 256, 512):
+        assert qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q6_K, nt, 4096, 4096) == qmm.QMM_KIND_MMQ
+    with pytest.raises(qmm.QmmError):
+        qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q4_K, 1, 4096, 4000)
+
+
+def test_validation_before_device_work():
+    L = qmm.lib()
+    p = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced
+    mis = ctypes.c_void_p((1 << 20) + 4)
+    big = 1 << 30
+    assert L.qmm_matmul(5, p, p, 1, 4, 256, p, p, big, None) == qmm.QMM_ERR_TYPE
+    assert L.qmm_matmul(1, None, p, 1, 4, 256, p, p, big, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_matmul(1, p, p, 0, 4, 256, p, p, big, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_matmul(1, p, p, 1, 4, 320, p, p, big, None) == qmm.QMM_ERR_SHAPE
+    assert L.qmm_matmul(1, p, p, 1, 4, 0, p, p, big, None) == qmm.QMM_ERR_SHAPE
+    assert L.qmm_matmul(1, mis, p, 1, 4, 256, p, p, big, None) == qmm.QMM_ERR_ALIGN
+    assert L.qmm_matmul(1, p, p, 1, 4, 256, p, p, 10, None) == qmm.QMM_ERR_WORKSPACE
+    assert L.qmm_matmul_q8(2, p, p, p, mis, 1, 4, 256, p, None) == qmm.QMM_ERR_ALIGN
+    assert L.qmm_matmul_q8_kind(3, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMVQ, 1, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_quantize_act(p, 1, 40, p, p, p, None) == qmm.QMM_ERR_SHAPE
+    assert L.qmm_group_dots(qmm.QMM_KIND_MMVQ, 1, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_matmul(1, p, p, 1 << 20, 4, 4096, p, p, big, None) == qmm.QMM_ERR_SHAPE
+
+
+def test_no_device_is_an_error_not_a_fallback():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = qmm.lib()
+    p = ctypes.c_void_p(1 << 20)
+    assert L.qmm_quantize_act(p, 1, 32, p, p, p, None) == qmm.QMM_ERR_DEVICE
+    assert L.qmm_matmul(1, p, p, 1, 4, 256, p, p, 1 << 20, None) == qmm.QMM_ERR_DEVICE
+
+
+def test_strerror():
+    for code in range(-7, 1):
+        assert qmm.strerror(code) and qmm.strerror(code) != "unknown status"
+    assert qmm.strerror(-99) == "unknown status"
+
+
+def test_product_does_not_import_oracle():
+    import sys
+    import subprocess
+    code = ("import sys; import quantized_matmul_amd; "
+            "assert not any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules), 'oracle imported'")
+    subprocess.run([sys.executable, "-c", code], cwd=ROOT, check=True)
+    src = "".join(open(os.path.join(ROOT, "quantized_matmul_amd", f)).read()
+                  for f in os.listdir(os.path.join(ROOT, "quantized_matmul_amd")) if f.endswith(".py"))
+    assert "oracle" not in src.replace("no CPU path", "")
