@@ -1,0 +1,323 @@
+"""Benchmark of the quantized-weight matmul on one MI355X.
+
+Default workload ("q4k_decode_prefill"): one step is the whole hot path --
+activation quantize, nt dispatch, and the selected kernel -- over
+  * Q4_K decode MMVQ: W 4096x4096 and 12288x4096 at nt = 1, 4 and 8 (six calls),
+  * Q4_K prefill MMQ: W 12288x4096 and 4096x12288 at nt = 512, activations
+    N(0,1) with 1 % of elements x20 (two calls).
+Inputs are seeded synthetic data (see synth/), resident in HBM before timing.
+Weight copies rotate so every weight read of the timed region comes from HBM
+(more than 1 GB of copies per shape, above the 256 MB last-level cache).
+
+Reported (one JSON line): value = HBM GB/s of the MMVQ kernel at nt = 1
+(algorithmic bytes: weights + q8 activations + f32 output, over the kernel's
+average launch time, both nt = 1 shapes together), the int8 TOP/s of the MMQ
+kernel at nt = 512 (2*nt*od*id over its average launch time), each with its
+roofline fraction, and the CPU oracle timed on a bounded sample.
+
+Kernel times come from HIP events on the launch stream inside the timed region.
+The K steps are issued call by call: for each call, a chunk of 20 quantize
+launches and then 20 matmul launches (rotating weight copies) run back to back
+between events, and the per-launch time is the chunk time over 20 (a HIP event
+itself costs about 4 us of GPU time).  A bounded busy-wait kernel
+(torch.cuda._sleep) at the head of each chunk group lets the host queue ahead of
+the GPU.  ms_per_step is wall time per step (gate included); gpu_ms_per_step sums
+the per-launch quantize and matmul times of one step.
+
+Options: --gpus N (1 only), --steps K, --warmup W, --workload
+{q4k_decode_prefill, q6k_head, dllm_step}, --no-cpu-baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+COPY_BYTES = 1 << 30           # weight copies per shape: at least 1 GiB
+CHUNK = 20                     # launches per event-timed chunk
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200, help="multiple of 20")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="q4k_decode_prefill",
+                    choices=["q4k_decode_prefill", "q6k_head", "dllm_step"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Call:
+    """One matmul of the step: weights (rotating copies), activations, buffers."""
+
+    def __init__(self, torch, qmm, qtype, od, idim, nt, seed, outliers, copies=None, label="", x=None):
+        self.qtype, self.od, self.idim, self.nt = qtype, od, idim, nt
+        self.label = label or f"{'Q4_K' if qtype == 1 else 'Q6_K'} {od}x{idim} nt={nt}"
+        dev = torch.device("cuda:0")
+        if copies is None:
+            w = torch.from_numpy(synth.weights(qtype, od, idim, seed=seed)).to(dev)
+            n = max(1, -(-COPY_BYTES // w.numel()))
+            copies = [w] + [w.clone() for _ in range(n - 1)]
+        self.W = copies
+        if x is None:
+            x = torch.from_numpy(synth.activations(nt, idim, seed=seed + 1,
+                                                   outlier_frac=0.01 if outliers else 0.0)).to(dev)
+        self.x = x
+        self.q = torch.empty((nt, idim), dtype=torch.int8, device=dev)
+        self.d = torch.empty((nt, idim // 32), dtype=torch.float32, device=dev)
+        self.s = torch.empty((nt, idim // 32), dtype=torch.float32, device=dev)
+        self.out = torch.empty((nt, od), dtype=torch.float32, device=dev)
+        self.kind = qmm.qmm_dispatch_kind(qtype, nt, od, idim)
+        self.wbytes = qmm.qmm_weight_bytes(qtype, od, idim)
+        # algorithmic bytes of the matmul kernel: weights + q8 activations + output
+        self.kbytes = self.wbytes + nt * idim * (1 + 8 / 32) + nt * od * 4
+        self.ops = 2.0 * nt * od * idim
+        self.k_ms = []   # matmul kernel time per launch, one entry per timed chunk
+        self.q_ms = []   # quantize kernel time per launch, one entry per timed chunk
+        self.i = 0
+        # raw C-ABI arguments, built once so the timed loop only makes the calls
+        P, I = ctypes.c_void_p, ctypes.c_int
+        st = P(torch.cuda.current_stream().cuda_stream)
+        self.L = qmm.lib()
+        self.qargs = (P(self.x.data_ptr()), I(nt), I(idim), P(self.q.data_ptr()), P(self.d.data_ptr()),
+                      P(self.s.data_ptr()), st)
+        self.margs = [(I(qtype), P(w.data_ptr()), P(self.q.data_ptr()), P(self.d.data_ptr()),
+                       P(self.s.data_ptr()), I(nt), I(od), I(idim), P(self.out.data_ptr()), st) for w in self.W]
+
+    def quantize(self):
+        rc = self.L.qmm_quantize_act(*self.qargs)
+        if rc:
+            raise RuntimeError(f"qmm_quantize_act failed: {rc}")
+
+    def matmul(self):
+        rc = self.L.qmm_matmul_q8(*self.margs[self.i % len(self.margs)])
+        self.i += 1
+        if rc:
+            raise RuntimeError(f"qmm_matmul_q8 failed: {rc}")
+
+    def run(self):
+        self.quantize()
+        self.matmul()
+
+
+def build_calls(torch, qmm, workload):
+    Q4, Q6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K
+    calls = []
+    if workload == "q4k_decode_prefill":
+        shared = {}
+        for od, idim in ((4096, 4096), (12288, 4096)):
+            for nt in (1, 4, 8):
+                c = Call(torch, qmm, Q4, od, idim, nt, seed=10 * nt + od, outliers=False,
+                         copies=shared.get((od, idim)))
+                shared[(od, idim)] = c.W
+                calls.append(c)
+        calls.append(Call(torch, qmm, Q4, 12288, 4096, 512, seed=7, outliers=True, copies=shared[(12288, 4096)]))
+        calls.append(Call(torch, qmm, Q4, 4096, 12288, 512, seed=8, outliers=True))
+    elif workload == "q6k_head":
+        calls.append(Call(torch, qmm, Q6, 32000, 4096, 1, seed=3, outliers=False))
+    else:  # dllm_step: 32 layers x (q, k, v, o, gate, up Q4_K; down Q6_K) at L = 256
+        shapes = [(Q4, 4096, 4096)] * 4 + [(Q4, 12288, 4096)] * 2 + [(Q6, 4096, 12288)]
+        # distinct weights per layer (4.34 GB per step): one seeded matrix per
+        # projection, copied to 32 distinct HBM places; one input per projection
+        per_proj = []
+        for p, (qt, od, idim) in enumerate(shapes):
+            w = torch.from_numpy(synth.weights(qt, od, idim, seed=100 + p)).to("cuda:0")
+            x = torch.from_numpy(synth.activations(256, idim, seed=200 + p)).to("cuda:0")
+            per_proj.append(([w] + [w.clone() for _ in range(31)], x))
+        for layer in range(32):
+            for p, (qt, od, idim) in enumerate(shapes):
+                copies, x = per_proj[p]
+                calls.append(Call(torch, qmm, qt, od, idim, 256, seed=0, outliers=False, copies=[copies[layer]],
+                                  label=f"layer{layer} proj{p} {od}x{idim}", x=x))
+    return calls
+
+
+def cpu_baseline(calls):
+    """The CPU oracle as it stands, on a bounded sample of the same workload."""
+    import oracle
+    oracle.build(force=False)
+    res = {"kind": "oracle", "cores": oracle.num_threads()}
+    dec = [c for c in calls if c.nt == 1]
+    big = [c for c in calls if c.nt >= 9]
+    if dec:
+        nbytes, t_total, reps = 0.0, 0.0, 0
+        data = [(c, synth.weights(c.qtype, c.od, c.idim, seed=10 * c.nt + c.od if c.qtype == 1 else 3),
+                 c.x.cpu().numpy()) for c in dec]
+        while t_total < 5.0:
+            for c, W, x in data:
+                t0 = time.perf_counter()
+                oracle.matmul(c.qtype, W, x, c.od)
+                t_total += time.perf_counter() - t0
+                nbytes += c.kbytes
+            reps += 1
+        res.update(value=nbytes / t_total / 1e9, unit="GB/s",
+                   sample=f"quantize + matmul of every nt=1 call ({', '.join(c.label for c in dec)}), "
+                          f"repeated {reps}x, {t_total:.1f} s")
+    if big:
+        c = big[0]
+        rows = 1024 if c.nt >= 512 else 2048
+        bpr = c.wbytes // c.od
+        W = synth.weights(c.qtype, c.od, c.idim, seed=7)[: rows * bpr]
+        x = c.x.cpu().numpy()
+        ops, t_total, reps = 0.0, 0.0, 0
+        while t_total < 5.0:
+            t0 = time.perf_counter()
+            oracle.matmul(c.qtype, W, x, rows)
+            t_total += time.perf_counter() - t0
+            ops += 2.0 * c.nt * rows * c.idim
+            reps += 1
+        res["mmq_value"] = ops / t_total / 1e12
+        res["mmq_unit"] = "TOP/s"
+        res["mmq_sample"] = f"quantize + matmul of {c.label} on its first {rows} rows, repeated {reps}x, {t_total:.1f} s"
+        if "value" not in res:
+            res.update(value=res["mmq_value"], unit="TOP/s", sample=res["mmq_sample"])
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(a row-sharded design is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import quantized_matmul_amd as qmm
+
+    torch.cuda.set_device(0)
+    calls = build_calls(torch, qmm, args.workload)
+    st = torch.cuda.current_stream()
+    chunk = min(CHUNK, args.steps)
+    nchunks = max(1, args.steps // chunk)
+    steps = chunk * nchunks
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in calls] for _ in range(nchunks)]
+
+    for _ in range(args.warmup):
+        for c in calls:
+            c.run()
+    torch.cuda.synchronize()
+
+    # gate: a bounded busy-wait kernel covering the host time to queue the first
+    # chunk, so the GPU then runs the queued launches back to back
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(st)
+    torch.cuda._sleep(1_000_000)
+    g1.record(st)
+    torch.cuda.synchronize()
+    ns_per_cycle = g0.elapsed_time(g1) * 1e6 / 1_000_000
+    h0 = time.perf_counter()
+    for c in calls:
+        for _ in range(chunk):
+            c.run()
+    host_s = time.perf_counter() - h0
+    torch.cuda.synchronize()
+    gate_cycles = int(max(1.5 * host_s, 100e-6) * 1e9 / ns_per_cycle)
+    for c in calls:
+        c.i = 0
+
+    # timed region: K steps, i.e. K launches of every call of the step; launches of
+    # one call are issued back to back in chunks bracketed by HIP events on the
+    # launch stream (an event costs about 4 us of GPU time, so a chunk of CHUNK
+    # launches amortises it)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for ch in range(nchunks):
+        torch.cuda._sleep(gate_cycles)
+        for c, (e0, e1, e2) in zip(calls, evs[ch]):
+            e0.record(st)
+            for _ in range(chunk):
+                c.quantize()
+            e1.record(st)
+            for _ in range(chunk):
+                c.matmul()
+            e2.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for ch in range(nchunks):
+        for c, (e0, e1, e2) in zip(calls, evs[ch]):
+            c.q_ms.append(e0.elapsed_time(e1) / chunk)
+            c.k_ms.append(e1.elapsed_time(e2) / chunk)
+
+    detail = []
+    for c in calls:
+        k = float(np.mean(c.k_ms))
+        qm = float(np.mean(c.q_ms))
+        row = {"call": c.label, "kernel": "mmvq" if c.kind == qmm.QMM_KIND_MMVQ else "mmq",
+               "kernel_us": round(k * 1e3, 2), "quantize_us": round(qm * 1e3, 2),
+               "kernel_us_p10_p90": [round(float(np.percentile(c.k_ms, 10)) * 1e3, 2),
+                                     round(float(np.percentile(c.k_ms, 90)) * 1e3, 2)],
+               "GB_s": round(c.kbytes / (k * 1e-3) / 1e9, 1),
+               "TOP_s": round(c.ops / (k * 1e-3) / 1e12, 2)}
+        row["hbm_frac"] = round(row["GB_s"] / HBM_PEAK_GBS, 4)
+        row["int8_frac"] = round(row["TOP_s"] / INT8_PEAK_TOPS, 4)
+        detail.append(row)
+
+    ms_per_step = wall * 1e3 / steps
+    gpu_ms = sum(float(np.mean(c.k_ms)) + float(np.mean(c.q_ms)) for c in calls)
+    line = {"metric": "Q4_K×q8 matmul: HBM GB/s at nt=1 and int8 TOPS at nt=512 (% of roofline)",
+            "n_gpus": 1, "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "gpu_ms_per_step": round(gpu_ms, 4), "gate_us": round(gate_cycles * ns_per_cycle / 1e3, 1),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+            "data": "synthetic (seeded; no model weights)"}
+
+    dec = [c for c in calls if c.nt == 1]
+    big = [c for c in calls if c.nt >= 9]
+    if args.workload == "q4k_decode_prefill":
+        tb = sum(c.kbytes for c in dec)
+        tt = sum(float(np.mean(c.k_ms)) * 1e-3 for c in dec)
+        line.update(value=round(tb / tt / 1e9, 1), unit="GB/s")
+        head = max(dec, key=lambda c: c.od)
+        kh = float(np.mean(head.k_ms)) * 1e-3
+        line["roofline"] = {"bound": "hbm", "achieved": round(head.kbytes / kh / 1e9, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(head.kbytes / kh / 1e9 / HBM_PEAK_GBS, 4),
+                            "traffic": None, "kernel": "mmvq_q4k_kernel<1,4,false>", "call": head.label,
+                            "bytes_per_launch": int(head.kbytes)}
+        ops = sum(c.ops for c in big)
+        tb2 = sum(float(np.mean(c.k_ms)) * 1e-3 for c in big)
+        m = max(big, key=lambda c: float(np.mean(c.k_ms)))
+        km = float(np.mean(m.k_ms)) * 1e-3
+        line["mmq"] = {"value": round(ops / tb2 / 1e12, 2), "unit": "TOP/s",
+                       "roofline": {"bound": "mfma", "achieved": round(m.ops / km / 1e12, 2),
+                                    "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
+                                    "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4), "traffic": None,
+                                    "kernel": "mmq_q4k_kernel", "call": m.label, "ops_per_launch": int(m.ops)}}
+        line["config"] = {"workload": "q4k_decode_prefill",
+                          "mmvq": "Q4_K 4096x4096 and 12288x4096, nt=1,4,8",
+                          "mmq": "Q4_K 12288x4096 and 4096x12288, nt=512, 1% outliers x20",
+                          "weight_copies_bytes_per_shape": COPY_BYTES}
+    elif args.workload == "q6k_head":
+        c = dec[0]
+        k = float(np.mean(c.k_ms)) * 1e-3
+        line.update(value=round(c.kbytes / k / 1e9, 1), unit="GB/s")
+        line["roofline"] = {"bound": "hbm", "achieved": line["value"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(line["value"] / HBM_PEAK_GBS, 4), "traffic": None,
+                            "kernel": "mmvq_q6k_kernel<1,4,false>", "bytes_per_launch": int(c.kbytes)}
+        line["config"] = {"workload": "q6k_head", "shape": "Q6_K 32000x4096 nt=1"}
+    else:
+        ops = sum(c.ops for c in calls)
+        t = sum(float(np.mean(c.k_ms)) * 1e-3 for c in calls)
+        line.update(value=round(ops / t / 1e12, 2), unit="TOP/s")
+        line["note"] = "value = int8 ops of the 224 matmuls over the sum of their kernel times"
+        line["config"] = {"workload": "dllm_step", "layers": 32, "canvas": 256, "hidden": 4096, "ffn": 12288,
+                          "matmuls_per_step": len(calls)}
+        detail = detail[:7]
+    line["detail"] = detail
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(calls)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

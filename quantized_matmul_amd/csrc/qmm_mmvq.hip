@@ -8,18 +8,23 @@
 // the Q6_K offset stay out of the integer loop.
 //
 // MI355X mapping (wave64):
-//  * A wave owns R output rows (a row group) and all of K.  Its 64 lanes split a
-//    K window of eight super-blocks: lane L takes super-block slot g = L/8 and
-//    16-byte code chunk c = L%8, i.e. 32 weights.  One window load instruction
-//    touches 8 consecutive super-blocks of a row (1152 contiguous bytes).
-//  * Weights are read once with 16-byte loads; the lane's activation codes (two
-//    16-byte pieces per token) and scales are loaded once per window and reused
-//    for all R rows (tokens x rows accumulators in registers).
+//  * K is cut into windows of eight super-blocks (2048 values).  A wave owns one
+//    row group of R rows and one window (or a few, strided) of it; the waves of a
+//    row group sit in one workgroup and add their partial sums through LDS.  So a
+//    wave issues all of its loads at once -- R rows x two 16-byte weight loads plus
+//    the activation loads of its window -- and there is no serial chain of loads.
+//  * Inside a window, lane L takes super-block slot g = L/8 and 16-byte code chunk
+//    c = L%8 (32 weights).  A weight load instruction covers eight consecutive
+//    super-blocks of a row (1152 contiguous bytes for Q4_K).
+//  * The lane's activation codes (two 16-byte pieces per token) and scales are
+//    loaded once and reused for all R rows (tokens x rows accumulators in VGPRs).
 //  * Integer dots use v_dot4_i32_i8 (codes 0..15 are valid int8; Q6_K codes are
 //    centred to -32..31 in registers), scales fold once per group in f32.
-//  * At the end the R*NT partial sums are reduced across the 64 lanes with a
-//    halving exchange (each step halves the values per lane), so lane l ends with
-//    output number l.
+//  * The R*NT partial sums are reduced across the 64 lanes with a halving
+//    exchange (each step halves the values per lane), then across the waves of
+//    the row group in LDS.
+#include <stdlib.h>
+
 #include "qmm_internal.h"
 
 namespace qmm {
@@ -29,8 +34,10 @@ struct pow2_ceil {
     static constexpr int value = N <= 1 ? 1 : N <= 2 ? 2 : N <= 4 ? 4 : N <= 8 ? 8 : N <= 16 ? 16 : N <= 32 ? 32 : 64;
 };
 
-// Reduce V values per lane across the wave.  After the call lane l (l < V) holds in
-// a[0] the wave total of value index l.  V must be a power of two <= 64.
+constexpr int kMaxWaves = 8;   // waves per workgroup
+
+// Reduce V values per lane across the wave.  Afterwards lane l (l < V) holds the
+// wave total of value index l.  V must be a power of two <= 64.
 template <int V>
 __device__ __forceinline__ float wave_reduce_spread(float (&a)[V], int lane)
 {
@@ -52,94 +59,132 @@ __device__ __forceinline__ float wave_reduce_spread(float (&a)[V], int lane)
     return a[0];
 }
 
-// Four dwords starting at byte address p, which is 2-byte aligned: read five
-// aligned dwords (all inside the same 210-byte block) and funnel-shift.
-__device__ __forceinline__ uint4 load16_a2(const uint8_t* p)
+// Sum the per-wave results of a row group in LDS and store them.  Every wave of
+// the workgroup calls this (it holds a barrier).  v: this lane's value after the
+// wave reduction (lane l < V holds value l = r * NTP + t).
+template <int NT, int R, int NTP>
+__device__ __forceinline__ void group_store(float v, int lane, int wave, int grp, int wk, int wpr,
+                                            int row0, int od, float* __restrict__ out)
 {
-    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(a & ~(uintptr_t)3);
-    const uint32_t sh = (uint32_t)(a & 3);
-    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3], w4 = w[4];
-    uint4 r;
-    r.x = __builtin_amdgcn_alignbyte(w1, w0, sh);
-    r.y = __builtin_amdgcn_alignbyte(w2, w1, sh);
-    r.z = __builtin_amdgcn_alignbyte(w3, w2, sh);
-    r.w = __builtin_amdgcn_alignbyte(w4, w3, sh);
-    return r;
+    constexpr int V = R * NTP;
+    __shared__ float red[kMaxWaves][V];
+    if (wpr > 1) {
+        if (lane < V)
+            red[wave][lane] = v;
+        __syncthreads();
+        if (wk != 0)
+            return;
+        if (lane < V)
+            for (int k = 1; k < wpr; ++k)
+                v += red[grp * wpr + k][lane];
+    }
+    if (lane < V) {
+        const int r = lane / NTP, t = lane % NTP;
+        if (t < NT && row0 + r < od)
+            out[(size_t)t * od + row0 + r] = v;
+    }
 }
 
 // ------------------------------------------------------------------ Q4_K
 // Lane chunk c: code chunk p = c/2 (32 bytes: sub-block 2p in low nibbles, 2p+1
 // in high nibbles, same positions), half = c%2 -> positions 16*half .. +15.
+//
+// Scales of sub-blocks 2p and 2p+1 in one pass, as bytes [sc0, sc1, m0, m1] of
+// one dword.  [MMQ, section 6, get_scale_min_k4 semantics]: for p < 2 the six
+// low bits of bytes 2p, 2p+1 of scale dword 1 (scales) and dword 2 (mins); for
+// p >= 2 the nibbles of bytes 2p-4, 2p-3 of dword 3 (low nibble: scale, high
+// nibble: min) below the top two bits of the same bytes of dword 1 (scale) or
+// dword 2 (min).  Both cases use bytes k, k+1 with k = 2*(p%2), gathered with
+// v_perm_b32 (selectors built once per lane).
+__device__ __forceinline__ uint32_t q4k_scale_bytes(uint32_t h1, uint32_t h2, uint32_t h3, uint32_t selx,
+                                                    uint32_t selz, bool plt2)
+{
+    const uint32_t x = __builtin_amdgcn_perm(h2, h1, selx);  // [h1.k, h1.k+1, h2.k, h2.k+1]
+    const uint32_t z = __builtin_amdgcn_perm(h3, h3, selz);  // [h3.k, h3.k+1, h3.k, h3.k+1]
+    const uint32_t lo = x & 0x3F3F3F3Fu;
+    const uint32_t nib = (z & 0x00000F0Fu) | ((z >> 4) & 0x0F0F0000u);
+    const uint32_t hi = ((x >> 2) & 0x30303030u) | nib;
+    return plt2 ? lo : hi;
+}
+
 template <int NT, int R, bool DUMP>
-__global__ __launch_bounds__(256) void mmvq_q4k_kernel(const uint8_t* __restrict__ W,
-                                                       const int8_t* __restrict__ q,
-                                                       const float* __restrict__ dx,
-                                                       const float* __restrict__ sx,
-                                                       float* __restrict__ out, int od, int id,
-                                                       int32_t* __restrict__ S)
+__global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q4k_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ q, const float* __restrict__ dx,
+    const float* __restrict__ sx, float* __restrict__ out, int od, int id, int32_t* __restrict__ S,
+    int wpr, int gpw)
 {
     constexpr int NTP = pow2_ceil<NT>::value;
     constexpr int V = R * NTP;
     const int lane = threadIdx.x & 63;
-    const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
-    if (row0 >= od)
-        return;  // whole wave leaves together
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave / wpr, wk = wave - grp * wpr;
+    const int row0 = (blockIdx.x * gpw + grp) * R;
     const int g = lane >> 3, c = lane & 7;
     const int p = c >> 1, half = c & 1;
+    const uint32_t k = 2u * (uint32_t)(p & 1);
+    const uint32_t selx = k | ((k + 1) << 8) | ((k + 4) << 16) | ((k + 5) << 24);
+    const uint32_t selz = k | ((k + 1) << 8) | (k << 16) | ((k + 1) << 24);
+    const bool plt2 = p < 2;
     const int nsb = id >> 8;
     const int nblk = id >> 5;
     const int nwin = (nsb + 7) >> 3;
+    const size_t row_bytes = (size_t)nsb * kQ4KBytes;
+    const bool live = row0 < od;  // a dead row group still reaches the barrier
 
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i)
         acc[i] = 0.f;
 
-    for (int w = 0; w < nwin; ++w) {
+    for (int w = wk; live && w < nwin; w += wpr) {
         const int b = 8 * w + g;
         const bool bv = b < nsb;
-        // activations of this lane for every token
+        const uint32_t bc = (uint32_t)(bv ? b : nsb - 1);
+        // ---- loads: uniform row / token bases plus a 32-bit lane offset
+        const uint32_t oh = bc * kQ4KBytes, oq = oh + 16 + 32 * p + 16 * half;
+        uint4 hdr[R], qs[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint8_t* rp = W + (size_t)min(row0 + r, od - 1) * row_bytes;
+            hdr[r] = *reinterpret_cast<const uint4*>(rp + oh);
+            qs[r] = *reinterpret_cast<const uint4*>(rp + oq);
+        }
+        const uint32_t ox = 256 * bc + 64 * p + 16 * half, od2 = 8 * bc + 2 * p;
         int4 xa[NT], xb[NT];
+        float2 dd[NT], ss[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int8_t* qt = q + (size_t)t * id;
+            xa[t] = *reinterpret_cast<const int4*>(qt + ox);
+            xb[t] = *reinterpret_cast<const int4*>(qt + ox + 32);
+            dd[t] = *reinterpret_cast<const float2*>(dx + (size_t)t * nblk + od2);
+            ss[t] = *reinterpret_cast<const float2*>(sx + (size_t)t * nblk + od2);
+        }
+        // keep every load above this point: the wave waits once for all of them
+        __builtin_amdgcn_sched_barrier(0);
+        // a lane past the row end adds nothing; the min term of a sub-block is
+        // added by its half-0 lane only
         float da[NT], db[NT], sa[NT], sb[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            if (bv) {
-                const int8_t* qt = q + (size_t)t * id + 256 * b + 64 * p + 16 * half;
-                xa[t] = *reinterpret_cast<const int4*>(qt);
-                xb[t] = *reinterpret_cast<const int4*>(qt + 32);
-                const int ai = t * nblk + 8 * b + 2 * p;
-                da[t] = dx[ai];
-                db[t] = dx[ai + 1];
-                // the min term of a sub-block is added once: by the half-0 lane
-                sa[t] = half ? 0.f : sx[ai];
-                sb[t] = half ? 0.f : sx[ai + 1];
-            } else {
-                xa[t] = make_int4(0, 0, 0, 0);
-                xb[t] = make_int4(0, 0, 0, 0);
-                da[t] = db[t] = sa[t] = sb[t] = 0.f;
-            }
+            da[t] = bv ? dd[t].x : 0.f;
+            db[t] = bv ? dd[t].y : 0.f;
+            sa[t] = (bv && half == 0) ? ss[t].x : 0.f;
+            sb[t] = (bv && half == 0) ? ss[t].y : 0.f;
         }
+        // ---- compute
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = row0 + r;
-            uint4 hdr = make_uint4(0, 0, 0, 0), qs = make_uint4(0, 0, 0, 0);
-            if (bv && row < od) {
-                const uint8_t* blk = W + ((size_t)row * nsb + b) * kQ4KBytes;
-                hdr = *reinterpret_cast<const uint4*>(blk);
-                qs = *reinterpret_cast<const uint4*>(blk + 16 + 16 * c);
-            }
-            const int lo0 = (int)(qs.x & 0x0F0F0F0Fu), lo1 = (int)(qs.y & 0x0F0F0F0Fu);
-            const int lo2 = (int)(qs.z & 0x0F0F0F0Fu), lo3 = (int)(qs.w & 0x0F0F0F0Fu);
-            const int hi0 = (int)((qs.x >> 4) & 0x0F0F0F0Fu), hi1 = (int)((qs.y >> 4) & 0x0F0F0F0Fu);
-            const int hi2 = (int)((qs.z >> 4) & 0x0F0F0F0Fu), hi3 = (int)((qs.w >> 4) & 0x0F0F0F0Fu);
-            int sc0, m0, sc1, m1;
-            q4k_scale_min(hdr.y, hdr.z, hdr.w, 2 * p, sc0, m0);
-            q4k_scale_min(hdr.y, hdr.z, hdr.w, 2 * p + 1, sc1, m1);
-            const float dw = f16_bits_to_f32(hdr.x & 0xFFFF);
-            const float dm = f16_bits_to_f32(hdr.x >> 16);
-            const float W0 = dw * (float)sc0, W1 = dw * (float)sc1;
-            const float M0 = dm * (float)m0, M1 = dm * (float)m1;
+            const uint4 h = hdr[r], w4 = qs[r];
+            const int lo0 = (int)(w4.x & 0x0F0F0F0Fu), lo1 = (int)(w4.y & 0x0F0F0F0Fu);
+            const int lo2 = (int)(w4.z & 0x0F0F0F0Fu), lo3 = (int)(w4.w & 0x0F0F0F0Fu);
+            const int hi0 = (int)((w4.x >> 4) & 0x0F0F0F0Fu), hi1 = (int)((w4.y >> 4) & 0x0F0F0F0Fu);
+            const int hi2 = (int)((w4.z >> 4) & 0x0F0F0F0Fu), hi3 = (int)((w4.w >> 4) & 0x0F0F0F0Fu);
+            const uint32_t sm = q4k_scale_bytes(h.y, h.z, h.w, selx, selz, plt2);
+            const int sc0 = (int)(sm & 0xFF), sc1 = (int)((sm >> 8) & 0xFF);
+            const float m0 = (float)((sm >> 16) & 0xFF), m1 = (float)(sm >> 24);
+            const float dw = f16_bits_to_f32(h.x & 0xFFFF);
+            const float dm = f16_bits_to_f32(h.x >> 16);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 int s0 = sdot4(lo0, xa[t].x, 0);
@@ -153,25 +198,26 @@ __global__ __launch_bounds__(256) void mmvq_q4k_kernel(const uint8_t* __restrict
                 if constexpr (DUMP) {
                     const int f0 = s0 + __shfl_xor(s0, 1, 64);
                     const int f1 = s1 + __shfl_xor(s1, 1, 64);
-                    if (bv && row < od && half == 0) {
-                        int32_t* dst = S + (((size_t)t * od + row) * nsb + b) * 8 + 2 * p;
+                    if (bv && row0 + r < od && half == 0) {
+                        int32_t* dst = S + (((size_t)t * od + row0 + r) * nsb + b) * 8 + 2 * p;
                         dst[0] = f0;
                         dst[1] = f1;
                     }
                 } else {
-                    acc[r * NTP + t] += W0 * (da[t] * (float)s0) + W1 * (db[t] * (float)s1) -
-                                        (M0 * sa[t] + M1 * sb[t]);
+                    // sc * S in integers (|sc * S| < 2^22, exact in f32), then
+                    // acc += d * (dx0 * sc0 S0 + dx1 * sc1 S1) - dmin * (m0 s0 + m1 s1)
+                    const float x0 = (float)__mul24(sc0, s0), x1 = (float)__mul24(sc1, s1);
+                    float a = acc[r * NTP + t];
+                    a = fmaf(dw, fmaf(da[t], x0, db[t] * x1), a);
+                    a = fmaf(-dm, fmaf(m0, sa[t], m1 * sb[t]), a);
+                    acc[r * NTP + t] = a;
                 }
             }
         }
     }
     if constexpr (!DUMP) {
         const float v = wave_reduce_spread<V>(acc, lane);
-        if (lane < V) {
-            const int r = lane / NTP, t = lane % NTP;
-            if (t < NT && row0 + r < od)
-                out[(size_t)t * od + row0 + r] = v;
-        }
+        group_store<NT, R, NTP>(v, lane, wave, grp, wk, wpr, row0, od, out);
     }
 }
 
@@ -181,138 +227,201 @@ __global__ __launch_bounds__(256) void mmvq_q4k_kernel(const uint8_t* __restrict
 // half takes low nibbles (k < 2) or high nibbles (k >= 2) of low bytes 64h+32(k%2)+l
 // and bits 2k..2k+1 of high byte 32h+l.  Lane chunk c: h = c/4, jq = (c/2)%2,
 // half = c%2 -> 16 positions of quarter jq (low nibbles) and of quarter jq+2 (high
-// nibbles) read from one 16-byte low chunk and one 16-byte high chunk.
+// nibbles) read from one 16-byte low chunk and one 16-byte high chunk.  Blocks
+// are 210 bytes, so a block can start 2 bytes off a dword: chunks are read as
+// five aligned dwords inside the block and funnel-shifted.  The raw 6-bit codes
+// (0..63) enter the integer dot and the offset 32 comes off afterwards as
+// 32 * sum(qx) of the group ([GEMM, "Weights: 8 rows per register"]: the offset
+// folds out through the activation sum), the sum being computed once per window.
 template <int NT, int R, bool DUMP>
-__global__ __launch_bounds__(256) void mmvq_q6k_kernel(const uint8_t* __restrict__ W,
-                                                       const int8_t* __restrict__ q,
-                                                       const float* __restrict__ dx,
-                                                       float* __restrict__ out, int od, int id,
-                                                       int32_t* __restrict__ S)
+__global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q6k_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ q, const float* __restrict__ dx,
+    float* __restrict__ out, int od, int id, int32_t* __restrict__ S, int wpr, int gpw)
 {
     constexpr int NTP = pow2_ceil<NT>::value;
     constexpr int V = R * NTP;
     const int lane = threadIdx.x & 63;
-    const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R;
-    if (row0 >= od)
-        return;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave / wpr, wk = wave - grp * wpr;
+    const int row0 = (blockIdx.x * gpw + grp) * R;
     const int g = lane >> 3, c = lane & 7;
     const int h = c >> 2, jq = (c >> 1) & 1, half = c & 1;
     const int g1 = 8 * h + 2 * jq + half;  // scale group of the low-nibble quarter
     const int g2 = g1 + 4;                 // scale group of the high-nibble quarter
+    const uint32_t hs = 2u * (uint32_t)jq;
+    const uint32_t f1 = 64 * h + 32 * jq + 16 * half, f2 = 128 + 32 * h + 16 * half;
     const int nsb = id >> 8;
     const int nblk = id >> 5;
     const int nwin = (nsb + 7) >> 3;
+    const size_t row_bytes = (size_t)nsb * kQ6KBytes;
+    const bool live = row0 < od;
 
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i)
         acc[i] = 0.f;
 
-    for (int w = 0; w < nwin; ++w) {
+    for (int w = wk; live && w < nwin; w += wpr) {
         const int b = 8 * w + g;
         const bool bv = b < nsb;
+        const uint32_t bc = (uint32_t)(bv ? b : nsb - 1);
+        const uint32_t ob = bc * kQ6KBytes;
+        uint4 ql[R], qh[R];
+        int sc1[R], sc2[R];
+        uint32_t dbits[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint8_t* rp = W + (size_t)min(row0 + r, od - 1) * row_bytes;
+            // rp's offset from a dword is uniform; the lane adds its block offset
+            const uint32_t res = (uint32_t)(reinterpret_cast<uintptr_t>(rp) & 3);
+            const uint8_t* rp4 = rp - res;
+            const uint32_t o = ob + res, o4 = o & ~3u, sh = o & 3u;
+            const uint32_t* pl = reinterpret_cast<const uint32_t*>(rp4 + o4 + f1);
+            const uint32_t* ph = reinterpret_cast<const uint32_t*>(rp4 + o4 + f2);
+            const uint32_t l0 = pl[0], l1 = pl[1], l2 = pl[2], l3 = pl[3], l4 = pl[4];
+            const uint32_t m0 = ph[0], m1 = ph[1], m2 = ph[2], m3 = ph[3], m4 = ph[4];
+            ql[r] = make_uint4(__builtin_amdgcn_alignbyte(l1, l0, sh), __builtin_amdgcn_alignbyte(l2, l1, sh),
+                               __builtin_amdgcn_alignbyte(l3, l2, sh), __builtin_amdgcn_alignbyte(l4, l3, sh));
+            qh[r] = make_uint4(__builtin_amdgcn_alignbyte(m1, m0, sh), __builtin_amdgcn_alignbyte(m2, m1, sh),
+                               __builtin_amdgcn_alignbyte(m3, m2, sh), __builtin_amdgcn_alignbyte(m4, m3, sh));
+            sc1[r] = (int)reinterpret_cast<const int8_t*>(rp)[ob + 192 + g1];
+            sc2[r] = (int)reinterpret_cast<const int8_t*>(rp)[ob + 192 + g2];
+            dbits[r] = *reinterpret_cast<const uint16_t*>(rp + ob + 208);
+        }
+        const uint32_t ox = 256 * bc + 128 * h + 32 * jq + 16 * half, od2 = 8 * bc + 4 * h + jq;
         int4 xa[NT], xb[NT];
         float da[NT], db[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            if (bv) {
-                const int8_t* qt = q + (size_t)t * id + 256 * b + 128 * h + 32 * jq + 16 * half;
-                xa[t] = *reinterpret_cast<const int4*>(qt);
-                xb[t] = *reinterpret_cast<const int4*>(qt + 64);
-                const int ai = t * nblk + 8 * b + 4 * h + jq;
-                da[t] = dx[ai];
-                db[t] = dx[ai + 2];
-            } else {
-                xa[t] = make_int4(0, 0, 0, 0);
-                xb[t] = make_int4(0, 0, 0, 0);
-                da[t] = db[t] = 0.f;
-            }
+            const int8_t* qt = q + (size_t)t * id;
+            xa[t] = *reinterpret_cast<const int4*>(qt + ox);
+            xb[t] = *reinterpret_cast<const int4*>(qt + ox + 64);
+            da[t] = dx[(size_t)t * nblk + od2];
+            db[t] = dx[(size_t)t * nblk + od2 + 2];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // 32 * sum of the activation codes of each of the lane's two groups
+        int ca[NT], cb[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            da[t] = bv ? da[t] : 0.f;
+            db[t] = bv ? db[t] : 0.f;
+            int u = sdot4(0x01010101, xa[t].x, 0);
+            u = sdot4(0x01010101, xa[t].y, u);
+            u = sdot4(0x01010101, xa[t].z, u);
+            ca[t] = 32 * sdot4(0x01010101, xa[t].w, u);
+            int v = sdot4(0x01010101, xb[t].x, 0);
+            v = sdot4(0x01010101, xb[t].y, v);
+            v = sdot4(0x01010101, xb[t].z, v);
+            cb[t] = 32 * sdot4(0x01010101, xb[t].w, v);
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            const int row = row0 + r;
-            uint4 ql = make_uint4(0, 0, 0, 0), qh = make_uint4(0, 0, 0, 0);
-            int scl1 = 0, scl2 = 0;
-            uint32_t dbits = 0;
-            if (bv && row < od) {
-                const uint8_t* blk = W + ((size_t)row * nsb + b) * kQ6KBytes;
-                ql = load16_a2(blk + 64 * h + 32 * jq + 16 * half);
-                qh = load16_a2(blk + 128 + 32 * h + 16 * half);
-                scl1 = (int)reinterpret_cast<const int8_t*>(blk)[192 + g1];
-                scl2 = (int)reinterpret_cast<const int8_t*>(blk)[192 + g2];
-                dbits = *reinterpret_cast<const uint16_t*>(blk + 208);
-            }
-            const int hs1 = 2 * jq, hs2 = 2 * jq + 4;
-            const int a0 = q6_center4(ql.x & 0x0F0F0F0Fu, (qh.x >> hs1) & 0x03030303u);
-            const int a1 = q6_center4(ql.y & 0x0F0F0F0Fu, (qh.y >> hs1) & 0x03030303u);
-            const int a2 = q6_center4(ql.z & 0x0F0F0F0Fu, (qh.z >> hs1) & 0x03030303u);
-            const int a3 = q6_center4(ql.w & 0x0F0F0F0Fu, (qh.w >> hs1) & 0x03030303u);
-            const int b0 = q6_center4((ql.x >> 4) & 0x0F0F0F0Fu, (qh.x >> hs2) & 0x03030303u);
-            const int b1 = q6_center4((ql.y >> 4) & 0x0F0F0F0Fu, (qh.y >> hs2) & 0x03030303u);
-            const int b2 = q6_center4((ql.z >> 4) & 0x0F0F0F0Fu, (qh.z >> hs2) & 0x03030303u);
-            const int b3 = q6_center4((ql.w >> 4) & 0x0F0F0F0Fu, (qh.w >> hs2) & 0x03030303u);
-            const float dw = f16_bits_to_f32(dbits);
-            const float W1 = dw * (float)scl1, W2 = dw * (float)scl2;
+            const uint4 L = ql[r], H = qh[r];
+            // quarter jq: low nibbles with bits hs..hs+1 of the high bytes above them;
+            // quarter jq+2: high nibbles with bits hs+4..hs+5
+            const uint32_t h0 = H.x >> hs, h1 = H.y >> hs, h2 = H.z >> hs, h3 = H.w >> hs;
+            const int a0 = (int)(((h0 << 4) & 0x30303030u) | (L.x & 0x0F0F0F0Fu));
+            const int a1 = (int)(((h1 << 4) & 0x30303030u) | (L.y & 0x0F0F0F0Fu));
+            const int a2 = (int)(((h2 << 4) & 0x30303030u) | (L.z & 0x0F0F0F0Fu));
+            const int a3 = (int)(((h3 << 4) & 0x30303030u) | (L.w & 0x0F0F0F0Fu));
+            const int b0 = (int)((h0 & 0x30303030u) | ((L.x >> 4) & 0x0F0F0F0Fu));
+            const int b1 = (int)((h1 & 0x30303030u) | ((L.y >> 4) & 0x0F0F0F0Fu));
+            const int b2 = (int)((h2 & 0x30303030u) | ((L.z >> 4) & 0x0F0F0F0Fu));
+            const int b3 = (int)((h3 & 0x30303030u) | ((L.w >> 4) & 0x0F0F0F0Fu));
+            const float dw = f16_bits_to_f32(dbits[r]);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 int s1 = sdot4(a0, xa[t].x, 0);
                 s1 = sdot4(a1, xa[t].y, s1);
                 s1 = sdot4(a2, xa[t].z, s1);
-                s1 = sdot4(a3, xa[t].w, s1);
+                s1 = sdot4(a3, xa[t].w, s1) - ca[t];
                 int s2 = sdot4(b0, xb[t].x, 0);
                 s2 = sdot4(b1, xb[t].y, s2);
                 s2 = sdot4(b2, xb[t].z, s2);
-                s2 = sdot4(b3, xb[t].w, s2);
+                s2 = sdot4(b3, xb[t].w, s2) - cb[t];
                 if constexpr (DUMP) {
-                    if (bv && row < od) {
-                        int32_t* dst = S + (((size_t)t * od + row) * nsb + b) * 16;
+                    if (bv && row0 + r < od) {
+                        int32_t* dst = S + (((size_t)t * od + row0 + r) * nsb + b) * 16;
                         dst[g1] = s1;
                         dst[g2] = s2;
                     }
                 } else {
-                    acc[r * NTP + t] += W1 * (da[t] * (float)s1) + W2 * (db[t] * (float)s2);
+                    // sc * S in integers (|sc * S| < 2^22, exact in f32)
+                    const float x1 = (float)__mul24(sc1[r], s1), x2 = (float)__mul24(sc2[r], s2);
+                    acc[r * NTP + t] = fmaf(dw, fmaf(da[t], x1, db[t] * x2), acc[r * NTP + t]);
                 }
             }
         }
     }
     if constexpr (!DUMP) {
         const float v = wave_reduce_spread<V>(acc, lane);
-        if (lane < V) {
-            const int r = lane / NTP, t = lane % NTP;
-            if (t < NT && row0 + r < od)
-                out[(size_t)t * od + row0 + r] = v;
-        }
+        group_store<NT, R, NTP>(v, lane, wave, grp, wk, wpr, row0, od, out);
     }
 }
 
 // ------------------------------------------------------------------ launch
 
+// Waves per row group: one per K window up to kMaxWaves (more windows are
+// strided over the waves); row groups per workgroup fill up to four waves.
 template <int NT, int R, bool DUMP>
 static hipError_t launch_one(int type, const uint8_t* W, const int8_t* q, const float* d,
                              const float* s, int od, int id, float* out, int32_t* S, hipStream_t st)
 {
-    const int waves = (od + R - 1) / R;
-    const int grid = (waves + 3) / 4;
+    const int nwin = (id / 256 + 7) / 8;
+    const int wpr = nwin < kMaxWaves ? nwin : kMaxWaves;
+    const int gpw = wpr >= 4 ? 1 : 4 / wpr;
+    const int groups = (od + R - 1) / R;
+    const int grid = (groups + gpw - 1) / gpw;
+    const dim3 block(64 * wpr * gpw);
     if (type == 1)
-        hipLaunchKernelGGL((mmvq_q4k_kernel<NT, R, DUMP>), dim3(grid), dim3(256), 0, st, W, q, d, s,
-                           out, od, id, S);
+        hipLaunchKernelGGL((mmvq_q4k_kernel<NT, R, DUMP>), dim3(grid), block, 0, st, W, q, d, s, out, od, id,
+                           S, wpr, gpw);
     else
-        hipLaunchKernelGGL((mmvq_q6k_kernel<NT, R, DUMP>), dim3(grid), dim3(256), 0, st, W, q, d, out,
-                           od, id, S);
+        hipLaunchKernelGGL((mmvq_q6k_kernel<NT, R, DUMP>), dim3(grid), block, 0, st, W, q, d, out, od, id, S,
+                           wpr, gpw);
     return hipGetLastError();
 }
 
-// Rows per wave: enough waves to give every CU several (256 CUs), then fewer,
-// larger row groups to reuse the activation registers.
+// Rows per row group R: the largest of 4, 2, 1 that leaves at least 2048 row
+// groups (eight per CU on 256 CUs), capped by the register budget of NT tokens.
+// QMM_MMVQ_ROWS (1, 2, 4, or 8 for nt <= 2) overrides it, read once, for tuning
+// sweeps.
+static int rows_override()
+{
+    static int v = -1;
+    int cur = __atomic_load_n(&v, __ATOMIC_ACQUIRE);
+    if (cur >= 0)
+        return cur;
+    const char* e = getenv("QMM_MMVQ_ROWS");
+    int val = e ? atoi(e) : 0;
+    if (val != 1 && val != 2 && val != 4 && val != 8)
+        val = 0;
+    __atomic_store_n(&v, val, __ATOMIC_RELEASE);
+    return val;
+}
+
 template <int NT>
 static hipError_t launch_nt(int type, const uint8_t* W, const int8_t* q, const float* d,
                             const float* s, int od, int id, float* out, int32_t* S, hipStream_t st)
 {
     if (S)
         return launch_one<NT, 1, true>(type, W, q, d, s, od, id, out, S, st);
-    if (od >= 4 * 2048)
+    int R = rows_override();
+    if (R == 0) {
+        const int rmax = NT <= 4 ? 4 : 2;
+        R = od >= 4 * 2048 ? 4 : od >= 2 * 2048 ? 2 : 1;
+        R = R < rmax ? R : rmax;
+    }
+    if constexpr (NT <= 2) {
+        if (R == 8)
+            return launch_one<NT, 8, false>(type, W, q, d, s, od, id, out, S, st);
+    } else if (R == 8) {
+        R = 4;
+    }
+    if (R == 4)
         return launch_one<NT, 4, false>(type, W, q, d, s, od, id, out, S, st);
-    if (od >= 2 * 2048)
+    if (R == 2)
         return launch_one<NT, 2, false>(type, W, q, d, s, od, id, out, S, st);
     return launch_one<NT, 1, false>(type, W, q, d, s, od, id, out, S, st);
 }
