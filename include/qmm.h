@@ -135,11 +135,14 @@ int qmm_nt_switch(void);
 int qmm_group_dots(int kind, int type, const void* W, const int8_t* q, int nt, int od, int id,
                    int32_t* S, void* stream);
 
-/* Diagnostic: one 32 x 32 x 32 int8 MFMA tile with the operand and result lane
- * mapping the MMQ kernel relies on.  A: [32 rows][32 K] int8, B: [32 tokens][32 K]
- * int8 (both row-major, 16-byte aligned), C: [32 tokens][32 rows] int32 receives
- * B . A^T when the mapping holds.  For a test that pins the MFMA lane layout. */
-int qmm_mfma_tile_check(const int8_t* A, const int8_t* B, int32_t* C, void* stream);
+/* Diagnostic: one MFMA tile with the operand and result lane mapping the MMQ
+ * kernels rely on, written out as C[.][token][row], for a test that pins the
+ * layouts.  kind 1: int8 32x32x32; A [32 rows][32 K] int8, B [32 tokens][32 K] int8,
+ * C [32 tokens][32 rows] int32 = B . A^T.  kind 2: f32 pair of 32 x 32 outer
+ * products; A [2][32 rows] f32, B [2][32 tokens] f32, C [2][32 tokens][32 rows] f32.
+ * kind 3: f32 32x32x2; A [2 K][32 rows], B [2 K][32 tokens] f32, C [32 tokens][32
+ * rows] f32 = sum over K.  All buffers device, 16-byte aligned. */
+int qmm_mfma_tile_check(int kind, const void* A, const void* B, void* C, void* stream);
 
 /* Short text for a status code (static storage). */
 const char* qmm_strerror(int status);

@@ -69,7 +69,7 @@ def lib():
         L.qmm_dispatch_kind.argtypes = [I, I, I, I]
         L.qmm_nt_switch.argtypes = []
         L.qmm_group_dots.argtypes = [I, I, P, P, I, I, I, P, P]
-        L.qmm_mfma_tile_check.argtypes = [P, P, P, P]
+        L.qmm_mfma_tile_check.argtypes = [I, P, P, P, P]
         L.qmm_strerror.argtypes = [I]
         L.qmm_strerror.restype = ctypes.c_char_p
         for f in ("qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8", "qmm_matmul_q8_kind",
@@ -187,9 +187,17 @@ def qmm_group_dots(kind: int, qtype: int, W: torch.Tensor, q: torch.Tensor, od: 
     return S
 
 
-def qmm_mfma_tile_check(A: torch.Tensor, B: torch.Tensor, C=None, stream=None):
+def qmm_mfma_tile_check(kind: int, A: torch.Tensor, B: torch.Tensor, C=None, stream=None):
+    """One MFMA tile in the MMQ kernels' lane mapping (see include/qmm.h)."""
     if C is None:
-        C = torch.empty((32, 32), dtype=torch.int32, device=A.device)
-    _check(lib().qmm_mfma_tile_check(_dev(A, torch.int8, "A"), _dev(B, torch.int8, "B"), _dev(C, torch.int32, "C"),
+        if kind == 1:
+            C = torch.empty((32, 32), dtype=torch.int32, device=A.device)
+        elif kind == 2:
+            C = torch.empty((2, 32, 32), dtype=torch.float32, device=A.device)
+        else:
+            C = torch.empty((32, 32), dtype=torch.float32, device=A.device)
+    dt = torch.int8 if kind == 1 else torch.float32
+    ct = torch.int32 if kind == 1 else torch.float32
+    _check(lib().qmm_mfma_tile_check(int(kind), _dev(A, dt, "A"), _dev(B, dt, "B"), _dev(C, ct, "C"),
                                      _stream(stream)), "qmm_mfma_tile_check")
     return C

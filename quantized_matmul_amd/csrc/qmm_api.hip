@@ -232,16 +232,16 @@ int qmm_group_dots(int kind, int type, const void* W, const int8_t* q, int nt, i
     return matmul_q8_checked(kind, type, W, q, dummy, dummy, nt, od, id, nullptr, S, stream);
 }
 
-int qmm_mfma_tile_check(const int8_t* A, const int8_t* B, int32_t* C, void* stream)
+int qmm_mfma_tile_check(int kind, const void* A, const void* B, void* C, void* stream)
 {
-    if (!A || !B || !C)
+    if (!A || !B || !C || kind < 1 || kind > 3)
         return QMM_ERR_ARG;
     if (!aligned16(A) || !aligned16(B) || !aligned16(C))
         return QMM_ERR_ALIGN;
     int rc = check_device();
     if (rc)
         return rc;
-    return launched(qmm::launch_mfma_tile_probe(A, B, C, reinterpret_cast<hipStream_t>(stream)));
+    return launched(qmm::launch_mfma_tile_probe(kind, A, B, C, reinterpret_cast<hipStream_t>(stream)));
 }
 
 const char* qmm_strerror(int status)

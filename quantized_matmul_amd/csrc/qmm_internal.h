@@ -26,7 +26,7 @@ hipError_t launch_mmvq(int type, const uint8_t* W, const int8_t* q, const float*
                        int nt, int od, int id, float* out, int32_t* S, hipStream_t st);
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
                       int nt, int od, int id, float* out, int32_t* S, hipStream_t st);
-hipError_t launch_mfma_tile_probe(const int8_t* A, const int8_t* B, int32_t* C, hipStream_t st);
+hipError_t launch_mfma_tile_probe(int kind, const void* A, const void* B, void* C, hipStream_t st);
 
 // ---------------------------------------------------------------- device helpers
 

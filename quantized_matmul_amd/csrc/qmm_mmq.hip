@@ -8,24 +8,74 @@
 // f32 accumulation and a plain f32 store; [MMQ, section 11.4]: codes 0..15 enter
 // the integer op uncentred.  [GEMM, "Q4_K: packed in shared memory"]: one LDS
 // read of a 16-byte code piece feeds two sub-blocks (low and high nibbles).
+// [GEMM, "Prefetching the next super-block"]: the next super-block is read into
+// registers while the current one computes, and stored to LDS after the barrier.
 //
 // MI355X mapping:
-//  * Workgroup tile BM rows x BN tokens, 256 threads = 4 waves in a 2 x 2 grid,
-//    each wave (BM/2) x (BN/2) in 32 x 32 MFMA blocks.
+//  * Workgroup tile BM = 32*WR rows x BN = 32*WC tokens, one wave per 32 x 32
+//    output block.  Workgroups are numbered so that the tiles of one row block
+//    land on one XCD (workgroups go round-robin over the 8 XCDs), which keeps a
+//    weight tile in one L2.
 //  * v_mfma_i32_32x32x32_i8: K = 32 is exactly one Q4_K sub-block.  Operand A =
 //    32 weight rows x 32 codes, B = 32 codes x 32 tokens; lane l supplies row/token
 //    l%32 and K positions 16*(l/32) .. +15 for both operands (any common K order
 //    gives the same dot).  Result lane l: token l%32, rows 8*(i/4)+4*(l/32)+i%4 for
 //    accumulator i.  Q6_K groups of 16 use v_mfma_i32_32x32x16_i8 (8 K bytes per lane).
-//  * Per super-block: stage raw code bytes (rows padded to keep 16-byte LDS reads
+//  * The f32 epilogue is the bottleneck on this chip (one rescale per 32 int8
+//    MACs; MFMA does 1024 MACs per clock per SIMD, VALU 16 lanes).  So only the
+//    per-element work stays on VALU: cvt(C) and one fma with the scale product.
+//    The scale product P = (d*sc)[row] x dx[token] of two sub-blocks comes from
+//    one v_mfma_f32_32x32x1_2b_f32 (two outer products), and the min term
+//    sum_j (-dmin*m_j)[row] * s_j[token] accumulates on v_mfma_f32_32x32x2_f32 in
+//    its own accumulator, both on the otherwise idle part of the MFMA pipe.
+//  * Per super-block: raw code bytes (rows padded so 16-byte LDS reads are
 //    conflict-free), decoded per-(row, group) f32 scales, activation codes and
-//    activation scales into LDS with 16-byte global loads; barrier; MFMA + f32
-//    epilogue; barrier.
+//    activation scales are staged in LDS; the next super-block's global loads are
+//    issued before the compute of the current one.
 #include "qmm_internal.h"
 
 namespace qmm {
 
-typedef long v1l;
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v32f __attribute__((ext_vector_type(32)));
+
+__device__ __forceinline__ v16i mfma_i8_k32(v4i a, v4i b)
+{
+    const v16i z = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, z, 0, 0, 0);
+}
+
+__device__ __forceinline__ v16i mfma_i8_k16(long a, long b)
+{
+    const v16i z = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_i32_32x32x16_i8(a, b, z, 0, 0, 0);
+}
+
+// Two 32 x 32 outer products: lane l gives a[row l%32] and b[col l%32] of block
+// l/32; result registers 16*k .. 16*k+15 hold block k in the 32 x 32 layout.
+__device__ __forceinline__ v32f mfma_outer2(float a, float b)
+{
+    const v32f z = {};
+    return __builtin_amdgcn_mfma_f32_32x32x1f32(a, b, z, 0, 0, 0);
+}
+
+// acc += A (32 x 2) . B (2 x 32): lane l gives A[row l%32][k = l/32] and
+// B[k = l/32][col l%32].
+__device__ __forceinline__ v16f mfma_k2(float a, float b, v16f acc)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+}
+
+// Tile index of this workgroup: consecutive tiles (same row block, successive
+// token blocks) go to the same XCD.  Returns -1 for a padding workgroup.
+__device__ __forceinline__ int xcd_tile(int ntiles)
+{
+    const int per = (ntiles + 7) >> 3;
+    const int t = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+    return t < ntiles ? t : -1;
+}
+
+// ------------------------------------------------------------------ Q4_K
 
 template <int BM, int BN>
 struct __attribute__((aligned(16))) Q4Smem {
@@ -33,178 +83,212 @@ struct __attribute__((aligned(16))) Q4Smem {
     static constexpr int X_STRIDE = 272;    // 256 activation codes + 16 pad
     uint8_t qs[BM * QS_STRIDE];
     float wsc[8 * BM];                      // d * sc_j, [j][row]
-    float wmn[8 * BM];                      // dmin * m_j, [j][row]
+    float wmn[8 * BM];                      // -dmin * m_j, [j][row]
     uint8_t xq[BN * X_STRIDE];
     float xd[8 * BN];                       // activation d, [j][token]
     float xs[8 * BN];                       // activation s, [j][token]
 };
 
-template <int BM, int BN, bool DUMP>
-__global__ __launch_bounds__(256) void mmq_q4k_kernel(const uint8_t* __restrict__ W,
-                                                      const int8_t* __restrict__ q,
-                                                      const float* __restrict__ dx,
-                                                      const float* __restrict__ sx,
-                                                      float* __restrict__ out, int nt, int od,
-                                                      int id, int32_t* __restrict__ S)
+template <int BM, int BN, int NTH, int QC, int HC, int XC, int SC>
+__device__ __forceinline__ void q4_prefetch(v4i (&pq)[QC], v4i (&ph)[HC], v4i (&px)[XC], v4i (&ps)[SC],
+                                            const uint8_t* __restrict__ W, const int8_t* __restrict__ q,
+                                            const float* __restrict__ dx, const float* __restrict__ sx, int sb,
+                                            int tid, int row0, int tok0, int nt, int od, int id, int nblk,
+                                            size_t row_bytes)
+{
+#pragma unroll
+    for (int k = 0; k < QC; ++k) {
+        const int e = tid + k * NTH;
+        if (e < BM * 8) {
+            const int r = e >> 3, ch = e & 7;
+            const uint8_t* blk = W + (size_t)min(row0 + r, od - 1) * row_bytes + (size_t)sb * kQ4KBytes;
+            pq[k] = *reinterpret_cast<const v4i*>(blk + 16 + 16 * ch);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < HC; ++k) {
+        const int e = tid + k * NTH;
+        if (e < BM * 4) {
+            const int r = e >> 2;
+            const uint8_t* blk = W + (size_t)min(row0 + r, od - 1) * row_bytes + (size_t)sb * kQ4KBytes;
+            ph[k] = *reinterpret_cast<const v4i*>(blk);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < XC; ++k) {
+        const int e = tid + k * NTH;
+        px[k] = v4i{0, 0, 0, 0};
+        if (e < BN * 16) {
+            const int t = e >> 4, ch = e & 15;
+            if (tok0 + t < nt)
+                px[k] = *reinterpret_cast<const v4i*>(q + (size_t)(tok0 + t) * id + 256 * sb + 16 * ch);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < SC; ++k) {
+        const int e = tid + k * NTH;
+        ps[k] = v4i{0, 0, 0, 0};
+        if (e < BN * 4) {
+            const int t = (e >> 1) % BN, hf = e & 1;
+            const float* src = e < BN * 2 ? dx : sx;
+            if (tok0 + t < nt)
+                ps[k] = *reinterpret_cast<const v4i*>(src + (size_t)(tok0 + t) * nblk + 8 * sb + 4 * hf);
+        }
+    }
+
+}
+
+template <int BM, int BN, int NTH, int QC, int HC, int XC, int SC>
+__device__ __forceinline__ void q4_stage(Q4Smem<BM, BN>& sm, const v4i (&pq)[QC], const v4i (&ph)[HC],
+                                         const v4i (&px)[XC], const v4i (&ps)[SC], int tid)
 {
     using SM = Q4Smem<BM, BN>;
-    __shared__ SM sm;
-    constexpr int MR = BM / 64;   // 32-row blocks per wave
-    constexpr int NC = BN / 64;   // 32-token blocks per wave
-    static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wr = wave >> 1, wc = wave & 1;
-    const int li = lane & 31, lh = lane >> 5;
-    const int row0 = blockIdx.y * BM;
-    const int tok0 = blockIdx.x * BN;
-    const int nsb = id >> 8;
-    const int nblk = id >> 5;
-
-    float acc[MR][NC][16];
 #pragma unroll
-    for (int a = 0; a < MR; ++a)
+    for (int k = 0; k < QC; ++k) {
+        const int e = tid + k * NTH;
+        if (e < BM * 8)
+            *reinterpret_cast<v4i*>(&sm.qs[(e >> 3) * SM::QS_STRIDE + 16 * (e & 7)]) = pq[k];
+    }
 #pragma unroll
-        for (int b = 0; b < NC; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                acc[a][b][i] = 0.f;
-
-    for (int sb = 0; sb < nsb; ++sb) {
-        // ---- stage weights: BM rows, 4 threads per row per pass
-        for (int e = tid; e < BM * 4; e += 256) {
+    for (int k = 0; k < HC; ++k) {
+        const int e = tid + k * NTH;
+        if (e < BM * 4) {
             const int r = e >> 2, part = e & 3;
-            const int rg = min(row0 + r, od - 1);
-            const uint8_t* blk = W + ((size_t)rg * nsb + sb) * kQ4KBytes;
-            const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
-            const uint4 c0 = *reinterpret_cast<const uint4*>(blk + 16 + 16 * part);
-            const uint4 c1 = *reinterpret_cast<const uint4*>(blk + 16 + 16 * (part + 4));
-            *reinterpret_cast<uint4*>(&sm.qs[r * SM::QS_STRIDE + 16 * part]) = c0;
-            *reinterpret_cast<uint4*>(&sm.qs[r * SM::QS_STRIDE + 16 * (part + 4)]) = c1;
-            const float dw = f16_bits_to_f32(hdr.x & 0xFFFF);
-            const float dm = f16_bits_to_f32(hdr.x >> 16);
+            const v4i h = ph[k];
+            const float dw = f16_bits_to_f32((uint32_t)h.x & 0xFFFF);
+            const float dm = f16_bits_to_f32((uint32_t)h.x >> 16);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int j = 2 * part + u;
                 int sc, m;
-                q4k_scale_min(hdr.y, hdr.z, hdr.w, j, sc, m);
+                q4k_scale_min((uint32_t)h.y, (uint32_t)h.z, (uint32_t)h.w, j, sc, m);
                 sm.wsc[j * BM + r] = dw * (float)sc;
-                sm.wmn[j * BM + r] = dm * (float)m;
+                sm.wmn[j * BM + r] = -(dm * (float)m);
             }
         }
-        // ---- stage activations: BN tokens x 16 pieces of 16 bytes
-        for (int e = tid; e < BN * 16; e += 256) {
-            const int t = e >> 4, part = e & 15;
-            const int tg = tok0 + t;
-            int4 v = make_int4(0, 0, 0, 0);
-            if (tg < nt)
-                v = *reinterpret_cast<const int4*>(q + (size_t)tg * id + 256 * sb + 16 * part);
-            *reinterpret_cast<int4*>(&sm.xq[t * SM::X_STRIDE + 16 * part]) = v;
+    }
+#pragma unroll
+    for (int k = 0; k < XC; ++k) {
+        const int e = tid + k * NTH;
+        if (e < BN * 16)
+            *reinterpret_cast<v4i*>(&sm.xq[(e >> 4) * SM::X_STRIDE + 16 * (e & 15)]) = px[k];
+    }
+#pragma unroll
+    for (int k = 0; k < SC; ++k) {
+        const int e = tid + k * NTH;
+        if (e < BN * 4) {
+            const int t = (e >> 1) % BN, hf = e & 1;
+            float* dst = e < BN * 2 ? sm.xd : sm.xs;
+            // __int_as_float per element: __builtin_bit_cast of an ext-vector
+            // element is lowered as a cast of element 0 by this compiler.
+            dst[(4 * hf + 0) * BN + t] = __int_as_float(ps[k].x);
+            dst[(4 * hf + 1) * BN + t] = __int_as_float(ps[k].y);
+            dst[(4 * hf + 2) * BN + t] = __int_as_float(ps[k].z);
+            dst[(4 * hf + 3) * BN + t] = __int_as_float(ps[k].w);
         }
-        for (int e = tid; e < BN * 2; e += 256) {
-            const int t = e >> 1, hf = e & 1;
-            const int tg = tok0 + t;
-            float4 vd = make_float4(0.f, 0.f, 0.f, 0.f), vs = vd;
-            if (tg < nt) {
-                vd = *reinterpret_cast<const float4*>(dx + (size_t)tg * nblk + 8 * sb + 4 * hf);
-                vs = *reinterpret_cast<const float4*>(sx + (size_t)tg * nblk + 8 * sb + 4 * hf);
-            }
-            sm.xd[(4 * hf + 0) * BN + t] = vd.x;
-            sm.xd[(4 * hf + 1) * BN + t] = vd.y;
-            sm.xd[(4 * hf + 2) * BN + t] = vd.z;
-            sm.xd[(4 * hf + 3) * BN + t] = vd.w;
-            sm.xs[(4 * hf + 0) * BN + t] = vs.x;
-            sm.xs[(4 * hf + 1) * BN + t] = vs.y;
-            sm.xs[(4 * hf + 2) * BN + t] = vs.z;
-            sm.xs[(4 * hf + 3) * BN + t] = vs.w;
-        }
-        __syncthreads();
+    }
 
-        // ---- compute
+}
+
+template <int WR, int WC, bool DUMP>
+__global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_kernel(const uint8_t* __restrict__ W,
+                                                               const int8_t* __restrict__ q,
+                                                               const float* __restrict__ dx,
+                                                               const float* __restrict__ sx,
+                                                               float* __restrict__ out, int nt, int od,
+                                                               int id, int32_t* __restrict__ S)
+{
+    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;
+    constexpr int QC = (BM * 8 + NTH - 1) / NTH;   // code chunks per thread
+    constexpr int HC = (BM * 4 + NTH - 1) / NTH;   // header tasks per thread
+    constexpr int XC = (BN * 16 + NTH - 1) / NTH;  // activation chunks per thread
+    constexpr int SC = (BN * 4 + NTH - 1) / NTH;   // activation scale float4s per thread
+    using SM = Q4Smem<BM, BN>;
+    __shared__ SM sm;
+
+    const int ntb = (nt + BN - 1) / BN;
+    const int tile = xcd_tile(ntb * ((od + BM - 1) / BM));
+    if (tile < 0)
+        return;  // whole workgroup
+    const int row0 = (tile / ntb) * BM, tok0 = (tile % ntb) * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / WC, wc = wave % WC;
+    const int li = lane & 31, lh = lane >> 5;
+    const int nsb = id >> 8;
+    const int nblk = id >> 5;
+    const size_t row_bytes = (size_t)nsb * kQ4KBytes;
+
+    // ---- prefetch registers (one super-block)
+    v4i pq[QC], ph[HC], px[XC], ps[SC];
+    v16f accv = {}, accm = {};
+    const int arow = wr * 32 + li;   // this lane's row as an A operand
+    const int btok = wc * 32 + li;   // this lane's token as a B operand
+
+    q4_prefetch<BM, BN, NTH, QC, HC, XC, SC>(pq, ph, px, ps, W, q, dx, sx, 0, tid, row0, tok0, nt, od, id, nblk, row_bytes);
+    for (int sb = 0; sb < nsb; ++sb) {
+        if (sb > 0)
+            __syncthreads();  // the previous super-block is no longer read
+        q4_stage<BM, BN, NTH, QC, HC, XC, SC>(sm, pq, ph, px, ps, tid);
+        __syncthreads();
+        if (sb + 1 < nsb)
+            q4_prefetch<BM, BN, NTH, QC, HC, XC, SC>(pq, ph, px, ps, W, q, dx, sx, sb + 1, tid, row0, tok0, nt, od, id,
+                                                     nblk, row_bytes);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            uint4 A16[MR];
+            const uint4 A16 = *reinterpret_cast<const uint4*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
+            const int4 b0 = *reinterpret_cast<const int4*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
+            const int4 b1 = *reinterpret_cast<const int4*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
+            const v4i a0 = v4i{(int)(A16.x & 0x0F0F0F0Fu), (int)(A16.y & 0x0F0F0F0Fu), (int)(A16.z & 0x0F0F0F0Fu),
+                               (int)(A16.w & 0x0F0F0F0Fu)};
+            const v4i a1 = v4i{(int)((A16.x >> 4) & 0x0F0F0F0Fu), (int)((A16.y >> 4) & 0x0F0F0F0Fu),
+                               (int)((A16.z >> 4) & 0x0F0F0F0Fu), (int)((A16.w >> 4) & 0x0F0F0F0Fu)};
+            const v16i C0 = mfma_i8_k32(a0, v4i{b0.x, b0.y, b0.z, b0.w});
+            const v16i C1 = mfma_i8_k32(a1, v4i{b1.x, b1.y, b1.z, b1.w});
+            if constexpr (DUMP) {
+                const int tg = tok0 + btok;
 #pragma unroll
-            for (int a = 0; a < MR; ++a) {
-                const int r = wr * (BM / 2) + 32 * a + li;
-                A16[a] = *reinterpret_cast<const uint4*>(&sm.qs[r * SM::QS_STRIDE + 32 * p + 16 * lh]);
-            }
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int j = 2 * p + u;
-                v4i Bv[NC];
-#pragma unroll
-                for (int b = 0; b < NC; ++b) {
-                    const int t = wc * (BN / 2) + 32 * b + li;
-                    const int4 bq = *reinterpret_cast<const int4*>(&sm.xq[t * SM::X_STRIDE + 32 * j + 16 * lh]);
-                    Bv[b] = v4i{bq.x, bq.y, bq.z, bq.w};
+                for (int i = 0; i < 16; ++i) {
+                    const int rg = row0 + wr * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+                    if (tg < nt && rg < od) {
+                        int32_t* dst = S + (((size_t)tg * od + rg) * nsb + sb) * 8 + 2 * p;
+                        dst[0] = C0[i];
+                        dst[1] = C1[i];
+                    }
                 }
+            } else {
+                // sub-block 2p + lh from this lane: scale product and min term
+                const int j = 2 * p + lh;
+                const v32f P = mfma_outer2(sm.wsc[j * BM + arow], sm.xd[j * BN + btok]);
+                accm = mfma_k2(sm.wmn[j * BM + arow], sm.xs[j * BN + btok], accm);
 #pragma unroll
-                for (int a = 0; a < MR; ++a) {
-                    const uint32_t sh = 4 * u;
-                    const v4i Av = v4i{(int)((A16[a].x >> sh) & 0x0F0F0F0Fu), (int)((A16[a].y >> sh) & 0x0F0F0F0Fu),
-                                       (int)((A16[a].z >> sh) & 0x0F0F0F0Fu), (int)((A16[a].w >> sh) & 0x0F0F0F0Fu)};
-                    // weight scales of this lane's 16 rows
-                    const int rbase = wr * (BM / 2) + 32 * a + 4 * lh;
-                    float ws[16], wm[16];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const float4 w4 = *reinterpret_cast<const float4*>(&sm.wsc[j * BM + rbase + 8 * k]);
-                        const float4 m4 = *reinterpret_cast<const float4*>(&sm.wmn[j * BM + rbase + 8 * k]);
-                        ws[4 * k + 0] = w4.x; ws[4 * k + 1] = w4.y; ws[4 * k + 2] = w4.z; ws[4 * k + 3] = w4.w;
-                        wm[4 * k + 0] = m4.x; wm[4 * k + 1] = m4.y; wm[4 * k + 2] = m4.z; wm[4 * k + 3] = m4.w;
-                    }
-#pragma unroll
-                    for (int b = 0; b < NC; ++b) {
-                        const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-                        const v16i C = __builtin_amdgcn_mfma_i32_32x32x32_i8(Av, Bv[b], zero, 0, 0, 0);
-                        const int t = wc * (BN / 2) + 32 * b + li;
-                        if constexpr (DUMP) {
-                            const int tg = tok0 + t;
-#pragma unroll
-                            for (int i = 0; i < 16; ++i) {
-                                const int rg = row0 + rbase + 8 * (i >> 2) + (i & 3);
-                                if (tg < nt && rg < od)
-                                    S[(((size_t)tg * od + rg) * nsb + sb) * 8 + j] = C[i];
-                            }
-                        } else {
-                            const float dxv = sm.xd[j * BN + t];
-                            const float sxv = sm.xs[j * BN + t];
-#pragma unroll
-                            for (int i = 0; i < 16; ++i)
-                                acc[a][b][i] += ws[i] * (dxv * (float)C[i]) - wm[i] * sxv;
-                        }
-                    }
+                for (int i = 0; i < 16; ++i) {
+                    accv[i] = fmaf((float)C0[i], P[i], accv[i]);
+                    accv[i] = fmaf((float)C1[i], P[16 + i], accv[i]);
                 }
             }
         }
-        __syncthreads();
     }
 
     if constexpr (!DUMP) {
+        const int tg = tok0 + btok;
+        if (tg < nt) {
 #pragma unroll
-        for (int a = 0; a < MR; ++a)
-#pragma unroll
-            for (int b = 0; b < NC; ++b) {
-                const int tg = tok0 + wc * (BN / 2) + 32 * b + li;
-                if (tg >= nt)
-                    continue;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int rg = row0 + wr * (BM / 2) + 32 * a + 4 * lh + 8 * k;
-                    float* o = out + (size_t)tg * od + rg;
-                    if (rg + 3 < od && ((od & 3) == 0)) {
-                        *reinterpret_cast<float4*>(o) =
-                            make_float4(acc[a][b][4 * k], acc[a][b][4 * k + 1], acc[a][b][4 * k + 2], acc[a][b][4 * k + 3]);
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (rg + i < od)
-                                o[i] = acc[a][b][4 * k + i];
-                    }
+            for (int k = 0; k < 4; ++k) {
+                const int rg = row0 + wr * 32 + 8 * k + 4 * lh;
+                float* o = out + (size_t)tg * od + rg;
+                const float v0 = accv[4 * k] + accm[4 * k], v1 = accv[4 * k + 1] + accm[4 * k + 1];
+                const float v2 = accv[4 * k + 2] + accm[4 * k + 2], v3 = accv[4 * k + 3] + accm[4 * k + 3];
+                if (rg + 3 < od && (od & 3) == 0) {
+                    *reinterpret_cast<float4*>(o) = make_float4(v0, v1, v2, v3);
+                } else {
+                    if (rg < od) o[0] = v0;
+                    if (rg + 1 < od) o[1] = v1;
+                    if (rg + 2 < od) o[2] = v2;
+                    if (rg + 3 < od) o[3] = v3;
                 }
             }
+        }
     }
 }
 
@@ -213,7 +297,8 @@ __global__ __launch_bounds__(256) void mmq_q4k_kernel(const uint8_t* __restrict_
 // 8*(l/32) .. +7).  Codes are rebuilt and centred at staging time into signed
 // bytes in LDS ([MMQ, section 4, Q6_K specialization]: centre at load), so the
 // MFMA operands are plain 8-byte LDS reads.  Rescale per group:
-// acc += (d*sc_g) * dx * C, dx the scale of the 32-block holding group g.
+// acc += (d*sc_g) * dx * C, dx the scale of the 32-block holding group g; the two
+// groups of a 32-block share dx, so one outer-product MFMA gives both products.
 template <int BM, int BN>
 struct __attribute__((aligned(16))) Q6Smem {
     static constexpr int W_STRIDE = 272;    // 256 centred codes + 16 pad
@@ -224,62 +309,80 @@ struct __attribute__((aligned(16))) Q6Smem {
     float xd[8 * BN];
 };
 
-template <int BM, int BN, bool DUMP>
-__global__ __launch_bounds__(256) void mmq_q6k_kernel(const uint8_t* __restrict__ W,
-                                                      const int8_t* __restrict__ q,
-                                                      const float* __restrict__ dx,
-                                                      float* __restrict__ out, int nt, int od,
-                                                      int id, int32_t* __restrict__ S)
+template <int BM, int BN, int NTH, int WC8, int XC, int SC>
+__device__ __forceinline__ void q6_prefetch(uint32_t (&pl)[WC8][5], uint32_t (&phh)[WC8][5], uint32_t (&pshift)[WC8],
+                                            v4i (&px)[XC], v4i (&ps)[SC], v4i (&psc)[WC8], uint32_t (&pd)[WC8],
+                                            const uint8_t* __restrict__ W, const int8_t* __restrict__ q,
+                                            const float* __restrict__ dx, int sb, int tid, int row0, int tok0, int nt,
+                                            int od, int id, int nblk, size_t row_bytes)
 {
-    using SM = Q6Smem<BM, BN>;
-    __shared__ SM sm;
-    constexpr int MR = BM / 64;
-    constexpr int NC = BN / 64;
-    static_assert(BM % 64 == 0 && BN % 64 == 0, "tile");
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wr = wave >> 1, wc = wave & 1;
-    const int li = lane & 31, lh = lane >> 5;
-    const int row0 = blockIdx.y * BM;
-    const int tok0 = blockIdx.x * BN;
-    const int nsb = id >> 8;
-    const int nblk = id >> 5;
-
-    float acc[MR][NC][16];
 #pragma unroll
-    for (int a = 0; a < MR; ++a)
-#pragma unroll
-        for (int b = 0; b < NC; ++b)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                acc[a][b][i] = 0.f;
-
-    for (int sb = 0; sb < nsb; ++sb) {
-        // ---- stage weights: 8 threads per row, thread c rebuilds 32 codes
-        for (int e = tid; e < BM * 8; e += 256) {
+    for (int k = 0; k < WC8; ++k) {
+        const int e = tid + k * NTH;
+        if (e < BM * 8) {
             const int r = e >> 3, c = e & 7;
             const int h = c >> 2, jq = (c >> 1) & 1, half = c & 1;
-            const int rg = min(row0 + r, od - 1);
-            const uint8_t* blk = W + ((size_t)rg * nsb + sb) * kQ6KBytes;
-            // low bytes 64h+32jq+16half.., high bytes 32h+16half.. (2-byte aligned block)
+            const uint8_t* blk = W + (size_t)min(row0 + r, od - 1) * row_bytes + (size_t)sb * kQ6KBytes;
             const uintptr_t al = reinterpret_cast<uintptr_t>(blk + 64 * h + 32 * jq + 16 * half);
             const uintptr_t ah = reinterpret_cast<uintptr_t>(blk + 128 + 32 * h + 16 * half);
-            const uint32_t* pl = reinterpret_cast<const uint32_t*>(al & ~(uintptr_t)3);
-            const uint32_t* ph = reinterpret_cast<const uint32_t*>(ah & ~(uintptr_t)3);
-            const uint32_t shl = (uint32_t)(al & 3), shh = (uint32_t)(ah & 3);
+            const uint32_t* wl = reinterpret_cast<const uint32_t*>(al & ~(uintptr_t)3);
+            const uint32_t* wh = reinterpret_cast<const uint32_t*>(ah & ~(uintptr_t)3);
+            pshift[k] = (uint32_t)(al & 3);  // same for both chunks
+#pragma unroll
+            for (int i = 0; i < 5; ++i) {
+                pl[k][i] = wl[i];
+                phh[k][i] = wh[i];
+            }
+            if (c < 2) {
+                // scales: c = 0 takes groups 0..7, c = 1 groups 8..15 (2 bytes each
+                // read as one 2-byte aligned piece), plus d
+                const uint16_t* sp = reinterpret_cast<const uint16_t*>(blk + 192 + 8 * c);
+                psc[k] = v4i{(int)(sp[0] | ((uint32_t)sp[1] << 16)), (int)(sp[2] | ((uint32_t)sp[3] << 16)), 0, 0};
+                pd[k] = *reinterpret_cast<const uint16_t*>(blk + 208);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < XC; ++k) {
+        const int e = tid + k * NTH;
+        px[k] = v4i{0, 0, 0, 0};
+        if (e < BN * 16) {
+            const int t = e >> 4, ch = e & 15;
+            if (tok0 + t < nt)
+                px[k] = *reinterpret_cast<const v4i*>(q + (size_t)(tok0 + t) * id + 256 * sb + 16 * ch);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < SC; ++k) {
+        const int e = tid + k * NTH;
+        ps[k] = v4i{0, 0, 0, 0};
+        if (e < BN * 2) {
+            const int t = e >> 1, hf = e & 1;
+            if (tok0 + t < nt)
+                ps[k] = *reinterpret_cast<const v4i*>(dx + (size_t)(tok0 + t) * nblk + 8 * sb + 4 * hf);
+        }
+    }
+
+}
+
+template <int BM, int BN, int NTH, int WC8, int XC, int SC>
+__device__ __forceinline__ void q6_stage(Q6Smem<BM, BN>& sm, const uint32_t (&pl)[WC8][5], const uint32_t (&phh)[WC8][5],
+                                         const uint32_t (&pshift)[WC8], const v4i (&px)[XC], const v4i (&ps)[SC],
+                                         const v4i (&psc)[WC8], const uint32_t (&pd)[WC8], int tid)
+{
+    using SM = Q6Smem<BM, BN>;
+#pragma unroll
+    for (int k = 0; k < WC8; ++k) {
+        const int e = tid + k * NTH;
+        if (e < BM * 8) {
+            const int r = e >> 3, c = e & 7;
+            const int h = c >> 2, jq = (c >> 1) & 1, half = c & 1;
+            const uint32_t sh = pshift[k];
             uint32_t L[4], H[4];
-            {
-                const uint32_t l0 = pl[0], l1 = pl[1], l2 = pl[2], l3 = pl[3], l4 = pl[4];
-                L[0] = __builtin_amdgcn_alignbyte(l1, l0, shl);
-                L[1] = __builtin_amdgcn_alignbyte(l2, l1, shl);
-                L[2] = __builtin_amdgcn_alignbyte(l3, l2, shl);
-                L[3] = __builtin_amdgcn_alignbyte(l4, l3, shl);
-                const uint32_t h0 = ph[0], h1 = ph[1], h2 = ph[2], h3 = ph[3], h4 = ph[4];
-                H[0] = __builtin_amdgcn_alignbyte(h1, h0, shh);
-                H[1] = __builtin_amdgcn_alignbyte(h2, h1, shh);
-                H[2] = __builtin_amdgcn_alignbyte(h3, h2, shh);
-                H[3] = __builtin_amdgcn_alignbyte(h4, h3, shh);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                L[i] = __builtin_amdgcn_alignbyte(pl[k][i + 1], pl[k][i], sh);
+                H[i] = __builtin_amdgcn_alignbyte(phh[k][i + 1], phh[k][i], sh);
             }
             const int hs1 = 2 * jq, hs2 = 2 * jq + 4;
             int4 ca, cb;
@@ -296,154 +399,211 @@ __global__ __launch_bounds__(256) void mmq_q6k_kernel(const uint8_t* __restrict_
             *reinterpret_cast<int4*>(&sm.wq[r * SM::W_STRIDE + e1]) = ca;
             *reinterpret_cast<int4*>(&sm.wq[r * SM::W_STRIDE + e1 + 64]) = cb;
             if (c < 2) {
-                // scales: thread c = 0 takes groups 0..7, c = 1 groups 8..15
-                const float dw = f16_bits_to_f32(*reinterpret_cast<const uint16_t*>(blk + 208));
-                const int8_t* scp = reinterpret_cast<const int8_t*>(blk + 192 + 8 * c);
+                const float dw = f16_bits_to_f32(pd[k]);
+                const uint32_t s0 = (uint32_t)psc[k].x, s1 = (uint32_t)psc[k].y;
 #pragma unroll
-                for (int gg = 0; gg < 8; ++gg)
-                    sm.wsc[(8 * c + gg) * BM + r] = dw * (float)scp[gg];
-            }
-        }
-        for (int e = tid; e < BN * 16; e += 256) {
-            const int t = e >> 4, part = e & 15;
-            const int tg = tok0 + t;
-            int4 v = make_int4(0, 0, 0, 0);
-            if (tg < nt)
-                v = *reinterpret_cast<const int4*>(q + (size_t)tg * id + 256 * sb + 16 * part);
-            *reinterpret_cast<int4*>(&sm.xq[t * SM::X_STRIDE + 16 * part]) = v;
-        }
-        for (int e = tid; e < BN * 2; e += 256) {
-            const int t = e >> 1, hf = e & 1;
-            const int tg = tok0 + t;
-            float4 vd = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (tg < nt)
-                vd = *reinterpret_cast<const float4*>(dx + (size_t)tg * nblk + 8 * sb + 4 * hf);
-            sm.xd[(4 * hf + 0) * BN + t] = vd.x;
-            sm.xd[(4 * hf + 1) * BN + t] = vd.y;
-            sm.xd[(4 * hf + 2) * BN + t] = vd.z;
-            sm.xd[(4 * hf + 3) * BN + t] = vd.w;
-        }
-        __syncthreads();
-
-#pragma unroll 4
-        for (int gq = 0; gq < 16; ++gq) {
-            long Bv[NC];
-#pragma unroll
-            for (int b = 0; b < NC; ++b) {
-                const int t = wc * (BN / 2) + 32 * b + li;
-                Bv[b] = *reinterpret_cast<const long*>(&sm.xq[t * SM::X_STRIDE + 16 * gq + 8 * lh]);
-            }
-#pragma unroll
-            for (int a = 0; a < MR; ++a) {
-                const int r = wr * (BM / 2) + 32 * a + li;
-                const long Av = *reinterpret_cast<const long*>(&sm.wq[r * SM::W_STRIDE + 16 * gq + 8 * lh]);
-                const int rbase = wr * (BM / 2) + 32 * a + 4 * lh;
-                float ws[16];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const float4 w4 = *reinterpret_cast<const float4*>(&sm.wsc[gq * BM + rbase + 8 * k]);
-                    ws[4 * k + 0] = w4.x; ws[4 * k + 1] = w4.y; ws[4 * k + 2] = w4.z; ws[4 * k + 3] = w4.w;
+                for (int gg = 0; gg < 4; ++gg) {
+                    sm.wsc[(8 * c + gg) * BM + r] = dw * (float)(int8_t)(s0 >> (8 * gg));
+                    sm.wsc[(8 * c + 4 + gg) * BM + r] = dw * (float)(int8_t)(s1 >> (8 * gg));
                 }
+            }
+        }
+    }
 #pragma unroll
-                for (int b = 0; b < NC; ++b) {
-                    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-                    const v16i C = __builtin_amdgcn_mfma_i32_32x32x16_i8(Av, Bv[b], zero, 0, 0, 0);
-                    const int t = wc * (BN / 2) + 32 * b + li;
-                    if constexpr (DUMP) {
-                        const int tg = tok0 + t;
+    for (int k = 0; k < XC; ++k) {
+        const int e = tid + k * NTH;
+        if (e < BN * 16)
+            *reinterpret_cast<v4i*>(&sm.xq[(e >> 4) * SM::X_STRIDE + 16 * (e & 15)]) = px[k];
+    }
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int rg = row0 + rbase + 8 * (i >> 2) + (i & 3);
-                            if (tg < nt && rg < od)
-                                S[(((size_t)tg * od + rg) * nsb + sb) * 16 + gq] = C[i];
-                        }
-                    } else {
-                        const float dxv = sm.xd[(gq >> 1) * BN + t];
+    for (int k = 0; k < SC; ++k) {
+        const int e = tid + k * NTH;
+        if (e < BN * 2) {
+            const int t = e >> 1, hf = e & 1;
+            sm.xd[(4 * hf + 0) * BN + t] = __int_as_float(ps[k].x);
+            sm.xd[(4 * hf + 1) * BN + t] = __int_as_float(ps[k].y);
+            sm.xd[(4 * hf + 2) * BN + t] = __int_as_float(ps[k].z);
+            sm.xd[(4 * hf + 3) * BN + t] = __int_as_float(ps[k].w);
+        }
+    }
+
+}
+
+template <int WR, int WC, bool DUMP>
+__global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q6k_kernel(const uint8_t* __restrict__ W,
+                                                               const int8_t* __restrict__ q,
+                                                               const float* __restrict__ dx,
+                                                               float* __restrict__ out, int nt, int od,
+                                                               int id, int32_t* __restrict__ S)
+{
+    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;
+    constexpr int WC8 = (BM * 8 + NTH - 1) / NTH;  // (row, 32-code piece) tasks per thread
+    constexpr int XC = (BN * 16 + NTH - 1) / NTH;
+    constexpr int SC = (BN * 2 + NTH - 1) / NTH;
+    using SM = Q6Smem<BM, BN>;
+    __shared__ SM sm;
+
+    const int ntb = (nt + BN - 1) / BN;
+    const int tile = xcd_tile(ntb * ((od + BM - 1) / BM));
+    if (tile < 0)
+        return;
+    const int row0 = (tile / ntb) * BM, tok0 = (tile % ntb) * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / WC, wc = wave % WC;
+    const int li = lane & 31, lh = lane >> 5;
+    const int nsb = id >> 8;
+    const int nblk = id >> 5;
+    const size_t row_bytes = (size_t)nsb * kQ6KBytes;
+
+    // prefetch registers: per task the five-dword windows of a low and a high
+    // chunk (2-byte aligned blocks), the two scale dwords and d
+    uint32_t pl[WC8][5], phh[WC8][5];
+    uint32_t pshift[WC8];
+    v4i px[XC], ps[SC], psc[WC8];
+    uint32_t pd[WC8];
+    v16f accv = {};
+    const int arow = wr * 32 + li;
+    const int btok = wc * 32 + li;
+
+    q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psc, pd, W, q, dx, 0, tid, row0, tok0, nt, od, id,
+                                          nblk, row_bytes);
+    for (int sb = 0; sb < nsb; ++sb) {
+        if (sb > 0)
+            __syncthreads();
+        q6_stage<BM, BN, NTH, WC8, XC, SC>(sm, pl, phh, pshift, px, ps, psc, pd, tid);
+        __syncthreads();
+        if (sb + 1 < nsb)
+            q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psc, pd, W, q, dx, sb + 1, tid, row0, tok0,
+                                                  nt, od, id, nblk, row_bytes);
+#pragma unroll 2
+        for (int m = 0; m < 8; ++m) {
+            // groups 2m and 2m+1 share activation block m
+            const long a0 = *reinterpret_cast<const long*>(&sm.wq[arow * SM::W_STRIDE + 32 * m + 8 * lh]);
+            const long a1 = *reinterpret_cast<const long*>(&sm.wq[arow * SM::W_STRIDE + 32 * m + 16 + 8 * lh]);
+            const long b0 = *reinterpret_cast<const long*>(&sm.xq[btok * SM::X_STRIDE + 32 * m + 8 * lh]);
+            const long b1 = *reinterpret_cast<const long*>(&sm.xq[btok * SM::X_STRIDE + 32 * m + 16 + 8 * lh]);
+            const v16i C0 = mfma_i8_k16(a0, b0);
+            const v16i C1 = mfma_i8_k16(a1, b1);
+            if constexpr (DUMP) {
+                const int tg = tok0 + btok;
 #pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            acc[a][b][i] += ws[i] * (dxv * (float)C[i]);
+                for (int i = 0; i < 16; ++i) {
+                    const int rg = row0 + wr * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+                    if (tg < nt && rg < od) {
+                        int32_t* dst = S + (((size_t)tg * od + rg) * nsb + sb) * 16 + 2 * m;
+                        dst[0] = C0[i];
+                        dst[1] = C1[i];
                     }
                 }
+            } else {
+                const v32f P = mfma_outer2(sm.wsc[(2 * m + lh) * BM + arow], sm.xd[m * BN + btok]);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    accv[i] = fmaf((float)C0[i], P[i], accv[i]);
+                    accv[i] = fmaf((float)C1[i], P[16 + i], accv[i]);
+                }
             }
         }
-        __syncthreads();
     }
 
     if constexpr (!DUMP) {
+        const int tg = tok0 + btok;
+        if (tg < nt) {
 #pragma unroll
-        for (int a = 0; a < MR; ++a)
-#pragma unroll
-            for (int b = 0; b < NC; ++b) {
-                const int tg = tok0 + wc * (BN / 2) + 32 * b + li;
-                if (tg >= nt)
-                    continue;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int rg = row0 + wr * (BM / 2) + 32 * a + 4 * lh + 8 * k;
-                    float* o = out + (size_t)tg * od + rg;
-                    if (rg + 3 < od && ((od & 3) == 0)) {
-                        *reinterpret_cast<float4*>(o) =
-                            make_float4(acc[a][b][4 * k], acc[a][b][4 * k + 1], acc[a][b][4 * k + 2], acc[a][b][4 * k + 3]);
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (rg + i < od)
-                                o[i] = acc[a][b][4 * k + i];
-                    }
+            for (int k = 0; k < 4; ++k) {
+                const int rg = row0 + wr * 32 + 8 * k + 4 * lh;
+                float* o = out + (size_t)tg * od + rg;
+                if (rg + 3 < od && (od & 3) == 0) {
+                    *reinterpret_cast<float4*>(o) = make_float4(accv[4 * k], accv[4 * k + 1], accv[4 * k + 2], accv[4 * k + 3]);
+                } else {
+                    if (rg < od) o[0] = accv[4 * k];
+                    if (rg + 1 < od) o[1] = accv[4 * k + 1];
+                    if (rg + 2 < od) o[2] = accv[4 * k + 2];
+                    if (rg + 3 < od) o[3] = accv[4 * k + 3];
                 }
             }
+        }
     }
 }
 
-// ------------------------------------------------------------------ probe
-// One 32 x 32 x 32 int8 MFMA with the operand and result mapping the MMQ kernel
-// assumes: A [32 rows][32 K] and B [32 tokens][32 K] row-major int8, C [32 tokens]
-// [32 rows] int32 = B . A^T.  Used by a test to pin the lane layout.
-__global__ __launch_bounds__(64) void mfma_tile_probe_kernel(const int8_t* __restrict__ A,
-                                                             const int8_t* __restrict__ B,
-                                                             int32_t* __restrict__ C)
+// ------------------------------------------------------------------ probes
+// One MFMA tile with the operand and result mapping the MMQ kernels rely on,
+// written out in a fixed layout (C[.][token][row]) for a test:
+//  kind 1: v_mfma_i32_32x32x32_i8; A [32 rows][32 K] int8, B [32 tokens][32 K]
+//          int8 -> C [32 tokens][32 rows] int32 = B . A^T
+//  kind 2: v_mfma_f32_32x32x1_2b_f32; A [2][32 rows], B [2][32 tokens] f32 ->
+//          C [2][32 tokens][32 rows] f32 = outer products per block
+//  kind 3: v_mfma_f32_32x32x2_f32; A [2 K][32 rows], B [2 K][32 tokens] f32 ->
+//          C [32 tokens][32 rows] f32 = sum over K
+__global__ __launch_bounds__(64) void mfma_tile_probe_kernel(int kind, const void* __restrict__ A,
+                                                             const void* __restrict__ B,
+                                                             void* __restrict__ C)
 {
     const int lane = threadIdx.x, li = lane & 31, lh = lane >> 5;
-    const int4 a = *reinterpret_cast<const int4*>(A + 32 * li + 16 * lh);
-    const int4 b = *reinterpret_cast<const int4*>(B + 32 * li + 16 * lh);
-    const v16i zero = {0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
-    const v16i r = __builtin_amdgcn_mfma_i32_32x32x32_i8(v4i{a.x, a.y, a.z, a.w}, v4i{b.x, b.y, b.z, b.w}, zero, 0, 0, 0);
+    if (kind == 1) {
+        const int8_t* a8 = static_cast<const int8_t*>(A);
+        const int8_t* b8 = static_cast<const int8_t*>(B);
+        const int4 a = *reinterpret_cast<const int4*>(a8 + 32 * li + 16 * lh);
+        const int4 b = *reinterpret_cast<const int4*>(b8 + 32 * li + 16 * lh);
+        const v16i r = mfma_i8_k32(v4i{a.x, a.y, a.z, a.w}, v4i{b.x, b.y, b.z, b.w});
+        int32_t* c = static_cast<int32_t*>(C);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * lh + (i & 3);
-        C[32 * li + row] = r[i];
+        for (int i = 0; i < 16; ++i)
+            c[32 * li + 8 * (i >> 2) + 4 * lh + (i & 3)] = r[i];
+    } else if (kind == 2) {
+        const v32f r = mfma_outer2(static_cast<const float*>(A)[lane], static_cast<const float*>(B)[lane]);
+        float* c = static_cast<float*>(C);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                c[1024 * k + 32 * li + 8 * (i >> 2) + 4 * lh + (i & 3)] = r[16 * k + i];
+    } else {
+        const v16f z = {};
+        const v16f r = mfma_k2(static_cast<const float*>(A)[lane], static_cast<const float*>(B)[lane], z);
+        float* c = static_cast<float*>(C);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            c[32 * li + 8 * (i >> 2) + 4 * lh + (i & 3)] = r[i];
     }
 }
 
-hipError_t launch_mfma_tile_probe(const int8_t* A, const int8_t* B, int32_t* C, hipStream_t st)
+hipError_t launch_mfma_tile_probe(int kind, const void* A, const void* B, void* C, hipStream_t st)
 {
-    hipLaunchKernelGGL(mfma_tile_probe_kernel, dim3(1), dim3(64), 0, st, A, B, C);
+    hipLaunchKernelGGL(mfma_tile_probe_kernel, dim3(1), dim3(64), 0, st, kind, A, B, C);
     return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ launch
 
-template <int BM, int BN, bool DUMP>
+template <int WR, int WC, bool DUMP>
 static hipError_t launch_tile(int type, const uint8_t* W, const int8_t* q, const float* d,
                               const float* s, int nt, int od, int id, float* out, int32_t* S,
                               hipStream_t st)
 {
-    const dim3 grid((nt + BN - 1) / BN, (od + BM - 1) / BM);
+    const int ntiles = ((nt + 32 * WC - 1) / (32 * WC)) * ((od + 32 * WR - 1) / (32 * WR));
+    const int grid = 8 * ((ntiles + 7) / 8);
     if (type == 1)
-        hipLaunchKernelGGL((mmq_q4k_kernel<BM, BN, DUMP>), grid, dim3(256), 0, st, W, q, d, s, out, nt,
-                           od, id, S);
+        hipLaunchKernelGGL((mmq_q4k_kernel<WR, WC, DUMP>), dim3(grid), dim3(64 * WR * WC), 0, st, W, q, d, s,
+                           out, nt, od, id, S);
     else
-        hipLaunchKernelGGL((mmq_q6k_kernel<BM, BN, DUMP>), grid, dim3(256), 0, st, W, q, d, out, nt, od,
-                           id, S);
+        hipLaunchKernelGGL((mmq_q6k_kernel<WR, WC, DUMP>), dim3(grid), dim3(64 * WR * WC), 0, st, W, q, d, out,
+                           nt, od, id, S);
     return hipGetLastError();
 }
 
+// Tile shape: 128 rows x 64 tokens (8 waves) when that still gives every CU a
+// tile, else 64 x 64 (4 waves).
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
                       int nt, int od, int id, float* out, int32_t* S, hipStream_t st)
 {
     if (S)
-        return launch_tile<64, 64, true>(type, W, q, d, s, nt, od, id, out, S, st);
-    return launch_tile<64, 64, false>(type, W, q, d, s, nt, od, id, out, S, st);
+        return launch_tile<2, 2, true>(type, W, q, d, s, nt, od, id, out, S, st);
+    const long big = (long)((nt + 63) / 64) * ((od + 127) / 128);
+    if (big >= 256)
+        return launch_tile<4, 2, false>(type, W, q, d, s, nt, od, id, out, S, st);
+    return launch_tile<2, 2, false>(type, W, q, d, s, nt, od, id, out, S, st);
 }
 
 }  // namespace qmm

@@ -30,7 +30,8 @@ def _say(*a):
 
 
 def test_mfma_tile_layout():
-    """Pins the int8 MFMA operand/result lane mapping the MMQ kernel assumes."""
+    """Pins the MFMA operand/result lane mappings the MMQ kernels assume: the int8
+    32x32x32 tile, the f32 pair of outer products and the f32 K=2 product."""
     rng = np.random.default_rng(0)
     for trial in range(3):
         A = rng.integers(-128, 128, (32, 32), dtype=np.int8)
@@ -38,10 +39,20 @@ def test_mfma_tile_layout():
         if trial == 2:
             A[:] = 0
             A[np.arange(32), np.arange(32)] = 1   # identity: C = B exactly
-        C = qmm.qmm_mfma_tile_check(_up(A), _up(B))
+        C = qmm.qmm_mfma_tile_check(1, _up(A), _up(B))
         torch.cuda.synchronize()
         want = B.astype(np.int64) @ A.astype(np.int64).T
         assert np.array_equal(C.cpu().numpy().astype(np.int64), want)
+    # small integers keep every f32 product and sum exact
+    a = rng.integers(-50, 50, (2, 32)).astype(np.float32)
+    b = rng.integers(-50, 50, (2, 32)).astype(np.float32)
+    C2 = qmm.qmm_mfma_tile_check(2, _up(a), _up(b))
+    C3 = qmm.qmm_mfma_tile_check(3, _up(a), _up(b))
+    torch.cuda.synchronize()
+    want2 = np.stack([np.outer(b[k], a[k]) for k in range(2)])      # [k][token][row]
+    want3 = b.T @ a                                                # [token][row]
+    assert np.array_equal(C2.cpu().numpy(), want2)
+    assert np.array_equal(C3.cpu().numpy(), want3)
 
 
 QUANT_CASES = [(1, 32, 0), (1, 96, 1), (3, 256, 2), (7, 4096, 3), (64, 768, 4), (129, 2048, 5), (512, 4096, 6)]
