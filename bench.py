@@ -24,8 +24,15 @@ itself costs about 4 us of GPU time).  A bounded busy-wait kernel
 the GPU.  ms_per_step is wall time per step (gate included); gpu_ms_per_step sums
 the per-launch quantize and matmul times of one step.
 
+roofline.traffic is the HBM bytes per launch of the roofline kernel as measured by
+the rocprofv3 FETCH_SIZE / WRITE_SIZE runs summarised in profiles/ (scaled by a
+plain copy of known size), or null when that summary is missing or was taken from
+kernel sources other than the ones built here.
+
 Options: --gpus N (1 only), --steps K, --warmup W, --workload
-{q4k_decode_prefill, q6k_head, dllm_step}, --no-cpu-baseline.
+{q4k_decode_prefill, q6k_head, dllm_step}, --no-cpu-baseline, --copy-calibration
+MIB (before warm-up, run five plain device copies of MIB MiB between two spin-kernel
+markers, for scaling the HBM counters of a profiled run).
 """
 from __future__ import annotations
 
@@ -47,6 +54,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
 COPY_BYTES = 1 << 30           # weight copies per shape: at least 1 GiB
 CHUNK = 20                     # launches per event-timed chunk
+COUNTERS = os.path.join(ROOT, "profiles", "q4k_decode_prefill_hbm_counters.md")
 
 
 def parse():
@@ -57,7 +65,30 @@ def parse():
     ap.add_argument("--workload", default="q4k_decode_prefill",
                     choices=["q4k_decode_prefill", "q6k_head", "dllm_step"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     return ap.parse_args()
+
+
+def copy_calibration(torch, mib):
+    """Five plain device-to-device copies of `mib` MiB between two spin-kernel markers."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(1)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda._sleep(1)
+    torch.cuda.synchronize()
+    del src, dst
+    return {"bytes": n, "reps": 5}
+
+
+def mmq_grid_threads(nt, od):
+    """Launch shape of the MMQ kernel at a wide tile (128 rows x 64 tokens, 512
+    threads), workgroup count padded to a multiple of the 8 XCDs."""
+    tiles = -(-nt // 64) * -(-od // 128)
+    return 8 * -(-tiles // 8) * 512
 
 
 class Call:
@@ -196,8 +227,11 @@ def main():
     import torch
     import quantized_matmul_amd as qmm
 
+    from quantized_matmul_amd.profile_summary import read_traffic
+
     torch.cuda.set_device(0)
     calls = build_calls(torch, qmm, args.workload)
+    cal = copy_calibration(torch, args.copy_calibration) if args.copy_calibration > 0 else None
     st = torch.cuda.current_stream()
     chunk = min(CHUNK, args.steps)
     nchunks = max(1, args.steps // chunk)
@@ -282,7 +316,8 @@ def main():
         kh = float(np.mean(head.k_ms)) * 1e-3
         line["roofline"] = {"bound": "hbm", "achieved": round(head.kbytes / kh / 1e9, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(head.kbytes / kh / 1e9 / HBM_PEAK_GBS, 4),
-                            "traffic": None, "kernel": "mmvq_q4k_kernel<1,4,false>", "call": head.label,
+                            "traffic": read_traffic(COUNTERS, "qmm::mmvq_q4k_kernel<1, 4, false>", None),
+                            "kernel": "mmvq_q4k_kernel<1,4,false>", "call": head.label,
                             "bytes_per_launch": int(head.kbytes)}
         ops = sum(c.ops for c in big)
         tb2 = sum(float(np.mean(c.k_ms)) * 1e-3 for c in big)
@@ -291,8 +326,11 @@ def main():
         line["mmq"] = {"value": round(ops / tb2 / 1e12, 2), "unit": "TOP/s",
                        "roofline": {"bound": "mfma", "achieved": round(m.ops / km / 1e12, 2),
                                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                                    "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4), "traffic": None,
-                                    "kernel": "mmq_q4k_kernel", "call": m.label, "ops_per_launch": int(m.ops)}}
+                                    "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4),
+                                    "traffic": read_traffic(COUNTERS, "qmm::mmq_q4k_kernel<4, 2, false>",
+                                                            mmq_grid_threads(m.nt, m.od)),
+                                    "kernel": "mmq_q4k_kernel<4,2,false>", "call": m.label,
+                                    "ops_per_launch": int(m.ops)}}
         line["config"] = {"workload": "q4k_decode_prefill",
                           "mmvq": "Q4_K 4096x4096 and 12288x4096, nt=1,4,8",
                           "mmq": "Q4_K 12288x4096 and 4096x12288, nt=512, 1% outliers x20",
@@ -314,6 +352,8 @@ def main():
                           "matmuls_per_step": len(calls)}
         detail = detail[:7]
     line["detail"] = detail
+    if cal:
+        line["copy_calibration"] = cal
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(calls)
     print(json.dumps(line), flush=True)
