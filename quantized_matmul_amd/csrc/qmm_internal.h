@@ -66,6 +66,19 @@ __device__ __forceinline__ void q4k_scale_min(uint32_t h1, uint32_t h2, uint32_t
     }
 }
 
+// The same for the pair of sub-blocks jj and jj + 4 (jj < 4), which share their
+// three source bytes; no data-dependent branch.
+__device__ __forceinline__ void q4k_scale_min_pair(uint32_t h1, uint32_t h2, uint32_t h3, int jj, int& sc_lo,
+                                                   int& m_lo, int& sc_hi, int& m_hi)
+{
+    const int sh = 8 * jj;
+    const uint32_t b1 = (h1 >> sh) & 0xFF, b2 = (h2 >> sh) & 0xFF, b3 = (h3 >> sh) & 0xFF;
+    sc_lo = (int)(b1 & 63);
+    m_lo = (int)(b2 & 63);
+    sc_hi = (int)((b3 & 0xF) | ((b1 >> 6) << 4));
+    m_hi = (int)((b3 >> 4) | ((b2 >> 6) << 4));
+}
+
 // Q6_K: build four signed codes (q6 - 32) from a dword of low fields and a dword
 // of high 2-bit fields.  [GEMM, "Q6_K: the same layout and prefetch"]: the code is
 // the nibble plus the two high bits, and the offset 32 comes off by flipping the

@@ -89,6 +89,20 @@ struct __attribute__((aligned(16))) Q4Smem {
     float xs[8 * BN];                       // activation s, [j][token]
 };
 
+// Task index e of a thread clamped into [0, n): threads past the end repeat the
+// last task -- the same loads and the same LDS stores of the same values -- so
+// the prefetch and staging code has no branches (a load under a branch makes the
+// compiler wait for it at once; a branch in the loop body lets it move compute
+// work past the staging and keep every MFMA result live).
+template <int N, int NTH, int CNT>
+__device__ __forceinline__ int task(int e)
+{
+    if constexpr (N % NTH == 0 && CNT * NTH == N)
+        return e;
+    else
+        return min(e, N - 1);
+}
+
 template <int BM, int BN, int NTH, int QC, int HC, int XC, int SC>
 __device__ __forceinline__ void q4_prefetch(v4i (&pq)[QC], v4i (&ph)[HC], v4i (&px)[XC], v4i (&ps)[SC],
                                             const uint8_t* __restrict__ W, const int8_t* __restrict__ q,
@@ -96,46 +110,34 @@ __device__ __forceinline__ void q4_prefetch(v4i (&pq)[QC], v4i (&ph)[HC], v4i (&
                                             int tid, int row0, int tok0, int nt, int od, int id, int nblk,
                                             size_t row_bytes)
 {
+    // rows past od and tokens past nt read the last valid row / token: their
+    // results are never stored
 #pragma unroll
     for (int k = 0; k < QC; ++k) {
-        const int e = tid + k * NTH;
-        if (e < BM * 8) {
-            const int r = e >> 3, ch = e & 7;
-            const uint8_t* blk = W + (size_t)min(row0 + r, od - 1) * row_bytes + (size_t)sb * kQ4KBytes;
-            pq[k] = *reinterpret_cast<const v4i*>(blk + 16 + 16 * ch);
-        }
+        const int e = task<BM * 8, NTH, QC>(tid + k * NTH);
+        const int r = e >> 3, ch = e & 7;
+        const uint8_t* blk = W + (size_t)min(row0 + r, od - 1) * row_bytes + (size_t)sb * kQ4KBytes;
+        pq[k] = *reinterpret_cast<const v4i*>(blk + 16 + 16 * ch);
     }
 #pragma unroll
     for (int k = 0; k < HC; ++k) {
-        const int e = tid + k * NTH;
-        if (e < BM * 4) {
-            const int r = e >> 2;
-            const uint8_t* blk = W + (size_t)min(row0 + r, od - 1) * row_bytes + (size_t)sb * kQ4KBytes;
-            ph[k] = *reinterpret_cast<const v4i*>(blk);
-        }
+        const int e = task<BM * 4, NTH, HC>(tid + k * NTH);
+        const uint8_t* blk = W + (size_t)min(row0 + (e >> 2), od - 1) * row_bytes + (size_t)sb * kQ4KBytes;
+        ph[k] = *reinterpret_cast<const v4i*>(blk);
     }
 #pragma unroll
     for (int k = 0; k < XC; ++k) {
-        const int e = tid + k * NTH;
-        px[k] = v4i{0, 0, 0, 0};
-        if (e < BN * 16) {
-            const int t = e >> 4, ch = e & 15;
-            if (tok0 + t < nt)
-                px[k] = *reinterpret_cast<const v4i*>(q + (size_t)(tok0 + t) * id + 256 * sb + 16 * ch);
-        }
+        const int e = task<BN * 16, NTH, XC>(tid + k * NTH);
+        const int t = min(tok0 + (e >> 4), nt - 1), ch = e & 15;
+        px[k] = *reinterpret_cast<const v4i*>(q + (size_t)t * id + 256 * sb + 16 * ch);
     }
 #pragma unroll
     for (int k = 0; k < SC; ++k) {
-        const int e = tid + k * NTH;
-        ps[k] = v4i{0, 0, 0, 0};
-        if (e < BN * 4) {
-            const int t = (e >> 1) % BN, hf = e & 1;
-            const float* src = e < BN * 2 ? dx : sx;
-            if (tok0 + t < nt)
-                ps[k] = *reinterpret_cast<const v4i*>(src + (size_t)(tok0 + t) * nblk + 8 * sb + 4 * hf);
-        }
+        const int e = task<BN * 4, NTH, SC>(tid + k * NTH);
+        const int t = min(tok0 + ((e >> 1) % BN), nt - 1), hf = e & 1;
+        const float* src = e < BN * 2 ? dx : sx;
+        ps[k] = *reinterpret_cast<const v4i*>(src + (size_t)t * nblk + 8 * sb + 4 * hf);
     }
-
 }
 
 template <int BM, int BN, int NTH, int QC, int HC, int XC, int SC>
@@ -145,49 +147,66 @@ __device__ __forceinline__ void q4_stage(Q4Smem<BM, BN>& sm, const v4i (&pq)[QC]
     using SM = Q4Smem<BM, BN>;
 #pragma unroll
     for (int k = 0; k < QC; ++k) {
-        const int e = tid + k * NTH;
-        if (e < BM * 8)
-            *reinterpret_cast<v4i*>(&sm.qs[(e >> 3) * SM::QS_STRIDE + 16 * (e & 7)]) = pq[k];
+        const int e = task<BM * 8, NTH, QC>(tid + k * NTH);
+        *reinterpret_cast<v4i*>(&sm.qs[(e >> 3) * SM::QS_STRIDE + 16 * (e & 7)]) = pq[k];
     }
 #pragma unroll
     for (int k = 0; k < HC; ++k) {
-        const int e = tid + k * NTH;
-        if (e < BM * 4) {
-            const int r = e >> 2, part = e & 3;
-            const v4i h = ph[k];
-            const float dw = f16_bits_to_f32((uint32_t)h.x & 0xFFFF);
-            const float dm = f16_bits_to_f32((uint32_t)h.x >> 16);
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int j = 2 * part + u;
-                int sc, m;
-                q4k_scale_min((uint32_t)h.y, (uint32_t)h.z, (uint32_t)h.w, j, sc, m);
-                sm.wsc[j * BM + r] = dw * (float)sc;
-                sm.wmn[j * BM + r] = -(dm * (float)m);
-            }
-        }
+        const int e = task<BM * 4, NTH, HC>(tid + k * NTH);
+        // task (r, jj) decodes sub-blocks jj and jj + 4 of row r
+        const int r = e >> 2, jj = e & 3;
+        const v4i h = ph[k];
+        const float dw = f16_bits_to_f32((uint32_t)h.x & 0xFFFF);
+        const float dm = f16_bits_to_f32((uint32_t)h.x >> 16);
+        int sc0, m0, sc1, m1;
+        q4k_scale_min_pair((uint32_t)h.y, (uint32_t)h.z, (uint32_t)h.w, jj, sc0, m0, sc1, m1);
+        sm.wsc[jj * BM + r] = dw * (float)sc0;
+        sm.wmn[jj * BM + r] = -(dm * (float)m0);
+        sm.wsc[(jj + 4) * BM + r] = dw * (float)sc1;
+        sm.wmn[(jj + 4) * BM + r] = -(dm * (float)m1);
     }
 #pragma unroll
     for (int k = 0; k < XC; ++k) {
-        const int e = tid + k * NTH;
-        if (e < BN * 16)
-            *reinterpret_cast<v4i*>(&sm.xq[(e >> 4) * SM::X_STRIDE + 16 * (e & 15)]) = px[k];
+        const int e = task<BN * 16, NTH, XC>(tid + k * NTH);
+        *reinterpret_cast<v4i*>(&sm.xq[(e >> 4) * SM::X_STRIDE + 16 * (e & 15)]) = px[k];
     }
 #pragma unroll
     for (int k = 0; k < SC; ++k) {
-        const int e = tid + k * NTH;
-        if (e < BN * 4) {
-            const int t = (e >> 1) % BN, hf = e & 1;
-            float* dst = e < BN * 2 ? sm.xd : sm.xs;
-            // __int_as_float per element: __builtin_bit_cast of an ext-vector
-            // element is lowered as a cast of element 0 by this compiler.
-            dst[(4 * hf + 0) * BN + t] = __int_as_float(ps[k].x);
-            dst[(4 * hf + 1) * BN + t] = __int_as_float(ps[k].y);
-            dst[(4 * hf + 2) * BN + t] = __int_as_float(ps[k].z);
-            dst[(4 * hf + 3) * BN + t] = __int_as_float(ps[k].w);
-        }
+        const int e = task<BN * 4, NTH, SC>(tid + k * NTH);
+        const int t = (e >> 1) % BN, hf = e & 1;
+        float* dst = e < BN * 2 ? sm.xd : sm.xs;
+        // __int_as_float per element: __builtin_bit_cast of an ext-vector
+        // element is lowered as a cast of element 0 by this compiler.
+        dst[(4 * hf + 0) * BN + t] = __int_as_float(ps[k].x);
+        dst[(4 * hf + 1) * BN + t] = __int_as_float(ps[k].y);
+        dst[(4 * hf + 2) * BN + t] = __int_as_float(ps[k].z);
+        dst[(4 * hf + 3) * BN + t] = __int_as_float(ps[k].w);
     }
 
+}
+
+// One compute step of the Q4_K kernel: sub-blocks 2p and 2p + 1 of the staged
+// super-block.  C0 / C1: the two int8 tile products; P: their scale products
+// (d*sc)[row] x dx[token] from one outer-product pair; the min term of the same
+// two sub-blocks is added into accm.
+template <int BM, int BN>
+__device__ __forceinline__ void q4_step(const Q4Smem<BM, BN>& sm, int p, int arow, int btok, int lh, v16i& C0,
+                                        v16i& C1, v32f& P, v16f& accm)
+{
+    using SM = Q4Smem<BM, BN>;
+    const uint4 A16 = *reinterpret_cast<const uint4*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
+    const int4 b0 = *reinterpret_cast<const int4*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
+    const int4 b1 = *reinterpret_cast<const int4*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
+    const v4i a0 = v4i{(int)(A16.x & 0x0F0F0F0Fu), (int)(A16.y & 0x0F0F0F0Fu), (int)(A16.z & 0x0F0F0F0Fu),
+                       (int)(A16.w & 0x0F0F0F0Fu)};
+    const v4i a1 = v4i{(int)((A16.x >> 4) & 0x0F0F0F0Fu), (int)((A16.y >> 4) & 0x0F0F0F0Fu),
+                       (int)((A16.z >> 4) & 0x0F0F0F0Fu), (int)((A16.w >> 4) & 0x0F0F0F0Fu)};
+    C0 = mfma_i8_k32(a0, v4i{b0.x, b0.y, b0.z, b0.w});
+    C1 = mfma_i8_k32(a1, v4i{b1.x, b1.y, b1.z, b1.w});
+    // sub-block 2p + lh from this lane
+    const int j = 2 * p + lh;
+    P = mfma_outer2(sm.wsc[j * BM + arow], sm.xd[j * BN + btok]);
+    accm = mfma_k2(sm.wmn[j * BM + arow], sm.xs[j * BN + btok], accm);
 }
 
 template <int WR, int WC, bool DUMP>
@@ -204,7 +223,7 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_kernel(const uint8_t*
     constexpr int XC = (BN * 16 + NTH - 1) / NTH;  // activation chunks per thread
     constexpr int SC = (BN * 4 + NTH - 1) / NTH;   // activation scale float4s per thread
     using SM = Q4Smem<BM, BN>;
-    __shared__ SM sm;
+    __shared__ SM smb[2];
 
     const int ntb = (nt + BN - 1) / BN;
     const int tile = xcd_tile(ntb * ((od + BM - 1) / BM));
@@ -225,27 +244,32 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_kernel(const uint8_t*
     const int arow = wr * 32 + li;   // this lane's row as an A operand
     const int btok = wc * 32 + li;   // this lane's token as a B operand
 
+    // Two LDS buffers: super-block sb computes from smb[sb & 1] while the next one,
+    // already in registers, is stored into the other buffer and the loads of the
+    // one after are issued; one barrier per super-block.
     q4_prefetch<BM, BN, NTH, QC, HC, XC, SC>(pq, ph, px, ps, W, q, dx, sx, 0, tid, row0, tok0, nt, od, id, nblk, row_bytes);
+    q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[0], pq, ph, px, ps, tid);
+    // prefetches are unconditional (index clamped to the last super-block, an L2
+    // re-read at the end): a prefetch under a branch merges register values and
+    // costs spills
+    q4_prefetch<BM, BN, NTH, QC, HC, XC, SC>(pq, ph, px, ps, W, q, dx, sx, min(1, nsb - 1), tid, row0, tok0, nt, od,
+                                             id, nblk, row_bytes);
+    __syncthreads();
     for (int sb = 0; sb < nsb; ++sb) {
-        if (sb > 0)
-            __syncthreads();  // the previous super-block is no longer read
-        q4_stage<BM, BN, NTH, QC, HC, XC, SC>(sm, pq, ph, px, ps, tid);
-        __syncthreads();
-        if (sb + 1 < nsb)
-            q4_prefetch<BM, BN, NTH, QC, HC, XC, SC>(pq, ph, px, ps, W, q, dx, sx, sb + 1, tid, row0, tok0, nt, od, id,
-                                                     nblk, row_bytes);
+        const SM& sm = smb[sb & 1];
+        if constexpr (DUMP) {
+            // integer products only, written out per sub-block
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint4 A16 = *reinterpret_cast<const uint4*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
-            const int4 b0 = *reinterpret_cast<const int4*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
-            const int4 b1 = *reinterpret_cast<const int4*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
-            const v4i a0 = v4i{(int)(A16.x & 0x0F0F0F0Fu), (int)(A16.y & 0x0F0F0F0Fu), (int)(A16.z & 0x0F0F0F0Fu),
-                               (int)(A16.w & 0x0F0F0F0Fu)};
-            const v4i a1 = v4i{(int)((A16.x >> 4) & 0x0F0F0F0Fu), (int)((A16.y >> 4) & 0x0F0F0F0Fu),
-                               (int)((A16.z >> 4) & 0x0F0F0F0Fu), (int)((A16.w >> 4) & 0x0F0F0F0Fu)};
-            const v16i C0 = mfma_i8_k32(a0, v4i{b0.x, b0.y, b0.z, b0.w});
-            const v16i C1 = mfma_i8_k32(a1, v4i{b1.x, b1.y, b1.z, b1.w});
-            if constexpr (DUMP) {
+            for (int p = 0; p < 4; ++p) {
+                const uint4 A16 = *reinterpret_cast<const uint4*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
+                const int4 b0 = *reinterpret_cast<const int4*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
+                const int4 b1 = *reinterpret_cast<const int4*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
+                const v4i a0 = v4i{(int)(A16.x & 0x0F0F0F0Fu), (int)(A16.y & 0x0F0F0F0Fu), (int)(A16.z & 0x0F0F0F0Fu),
+                                   (int)(A16.w & 0x0F0F0F0Fu)};
+                const v4i a1 = v4i{(int)((A16.x >> 4) & 0x0F0F0F0Fu), (int)((A16.y >> 4) & 0x0F0F0F0Fu),
+                                   (int)((A16.z >> 4) & 0x0F0F0F0Fu), (int)((A16.w >> 4) & 0x0F0F0F0Fu)};
+                const v16i C0 = mfma_i8_k32(a0, v4i{b0.x, b0.y, b0.z, b0.w});
+                const v16i C1 = mfma_i8_k32(a1, v4i{b1.x, b1.y, b1.z, b1.w});
                 const int tg = tok0 + btok;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -256,18 +280,45 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_kernel(const uint8_t*
                         dst[1] = C1[i];
                     }
                 }
-            } else {
-                // sub-block 2p + lh from this lane: scale product and min term
-                const int j = 2 * p + lh;
-                const v32f P = mfma_outer2(sm.wsc[j * BM + arow], sm.xd[j * BN + btok]);
-                accm = mfma_k2(sm.wmn[j * BM + arow], sm.xs[j * BN + btok], accm);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+            // Software pipelined over the four steps: the MFMAs of step p + 1 are
+            // issued before the epilogue of step p, one step of results in flight.
+            v16i Ca0, Ca1;
+            v32f Pa;
+            q4_step<BM, BN>(sm, 0, arow, btok, lh, Ca0, Ca1, Pa, accm);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                v16i Cb0, Cb1;
+                v32f Pb;
+                if (p < 3)
+                    q4_step<BM, BN>(sm, p + 1, arow, btok, lh, Cb0, Cb1, Pb, accm);
+                __builtin_amdgcn_sched_barrier(0);
+                // sub-blocks 2p (registers 0..15 of P) and 2p + 1 (16..31)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    accv[i] = fmaf((float)C0[i], P[i], accv[i]);
-                    accv[i] = fmaf((float)C1[i], P[16 + i], accv[i]);
+                    accv[i] = fmaf((float)Ca0[i], Pa[i], accv[i]);
+                    accv[i] = fmaf((float)Ca1[i], Pa[16 + i], accv[i]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (p < 3) {
+                    Ca0 = Cb0;
+                    Ca1 = Cb1;
+                    Pa = Pb;
                 }
             }
         }
+        // keep the staging of the next super-block after the compute (moved into
+        // it, its values would be live across the whole compute phase)
+        __builtin_amdgcn_sched_barrier(0);
+        // smb[(sb + 1) & 1] was last read in super-block sb - 1, before the barrier;
+        // after the last super-block this fills a buffer nobody reads
+        q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[(sb + 1) & 1], pq, ph, px, ps, tid);
+        q4_prefetch<BM, BN, NTH, QC, HC, XC, SC>(pq, ph, px, ps, W, q, dx, sx, min(sb + 2, nsb - 1), tid, row0, tok0,
+                                                 nt, od, id, nblk, row_bytes);
+        __syncthreads();
     }
 
     if constexpr (!DUMP) {
@@ -311,122 +362,99 @@ struct __attribute__((aligned(16))) Q6Smem {
 
 template <int BM, int BN, int NTH, int WC8, int XC, int SC>
 __device__ __forceinline__ void q6_prefetch(uint32_t (&pl)[WC8][5], uint32_t (&phh)[WC8][5], uint32_t (&pshift)[WC8],
-                                            v4i (&px)[XC], v4i (&ps)[SC], v4i (&psc)[WC8], uint32_t (&pd)[WC8],
+                                            v4i (&px)[XC], v4i (&ps)[SC], uint32_t (&psd)[WC8],
                                             const uint8_t* __restrict__ W, const int8_t* __restrict__ q,
                                             const float* __restrict__ dx, int sb, int tid, int row0, int tok0, int nt,
                                             int od, int id, int nblk, size_t row_bytes)
 {
+    // unconditional loads, as for Q4_K: clamped task, row and token indices
 #pragma unroll
     for (int k = 0; k < WC8; ++k) {
-        const int e = tid + k * NTH;
-        if (e < BM * 8) {
-            const int r = e >> 3, c = e & 7;
-            const int h = c >> 2, jq = (c >> 1) & 1, half = c & 1;
-            const uint8_t* blk = W + (size_t)min(row0 + r, od - 1) * row_bytes + (size_t)sb * kQ6KBytes;
-            const uintptr_t al = reinterpret_cast<uintptr_t>(blk + 64 * h + 32 * jq + 16 * half);
-            const uintptr_t ah = reinterpret_cast<uintptr_t>(blk + 128 + 32 * h + 16 * half);
-            const uint32_t* wl = reinterpret_cast<const uint32_t*>(al & ~(uintptr_t)3);
-            const uint32_t* wh = reinterpret_cast<const uint32_t*>(ah & ~(uintptr_t)3);
-            pshift[k] = (uint32_t)(al & 3);  // same for both chunks
+        const int e = task<BM * 8, NTH, WC8>(tid + k * NTH);
+        const int r = e >> 3, c = e & 7;
+        const int h = c >> 2, jq = (c >> 1) & 1, half = c & 1;
+        const uint8_t* blk = W + (size_t)min(row0 + r, od - 1) * row_bytes + (size_t)sb * kQ6KBytes;
+        const uintptr_t al = reinterpret_cast<uintptr_t>(blk + 64 * h + 32 * jq + 16 * half);
+        const uintptr_t ah = reinterpret_cast<uintptr_t>(blk + 128 + 32 * h + 16 * half);
+        const uint32_t* wl = reinterpret_cast<const uint32_t*>(al & ~(uintptr_t)3);
+        const uint32_t* wh = reinterpret_cast<const uint32_t*>(ah & ~(uintptr_t)3);
+        pshift[k] = (uint32_t)(al & 3);  // same for both chunks
 #pragma unroll
-            for (int i = 0; i < 5; ++i) {
-                pl[k][i] = wl[i];
-                phh[k][i] = wh[i];
-            }
-            if (c < 2) {
-                // scales: c = 0 takes groups 0..7, c = 1 groups 8..15 (2 bytes each
-                // read as one 2-byte aligned piece), plus d
-                const uint16_t* sp = reinterpret_cast<const uint16_t*>(blk + 192 + 8 * c);
-                psc[k] = v4i{(int)(sp[0] | ((uint32_t)sp[1] << 16)), (int)(sp[2] | ((uint32_t)sp[3] << 16)), 0, 0};
-                pd[k] = *reinterpret_cast<const uint16_t*>(blk + 208);
-            }
+        for (int i = 0; i < 5; ++i) {
+            pl[k][i] = wl[i];
+            phh[k][i] = wh[i];
         }
+        // task c also stages group scales 2c and 2c+1 (two bytes, 2-byte aligned)
+        // and reads d: low half the two int8 scales, high half the f16 d
+        const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(blk + 192 + 2 * c);
+        const uint32_t d16 = *reinterpret_cast<const uint16_t*>(blk + 208);
+        psd[k] = sc2 | (d16 << 16);
     }
 #pragma unroll
     for (int k = 0; k < XC; ++k) {
-        const int e = tid + k * NTH;
-        px[k] = v4i{0, 0, 0, 0};
-        if (e < BN * 16) {
-            const int t = e >> 4, ch = e & 15;
-            if (tok0 + t < nt)
-                px[k] = *reinterpret_cast<const v4i*>(q + (size_t)(tok0 + t) * id + 256 * sb + 16 * ch);
-        }
+        const int e = task<BN * 16, NTH, XC>(tid + k * NTH);
+        const int t = min(tok0 + (e >> 4), nt - 1), ch = e & 15;
+        px[k] = *reinterpret_cast<const v4i*>(q + (size_t)t * id + 256 * sb + 16 * ch);
     }
 #pragma unroll
     for (int k = 0; k < SC; ++k) {
-        const int e = tid + k * NTH;
-        ps[k] = v4i{0, 0, 0, 0};
-        if (e < BN * 2) {
-            const int t = e >> 1, hf = e & 1;
-            if (tok0 + t < nt)
-                ps[k] = *reinterpret_cast<const v4i*>(dx + (size_t)(tok0 + t) * nblk + 8 * sb + 4 * hf);
-        }
+        const int e = task<BN * 2, NTH, SC>(tid + k * NTH);
+        const int t = min(tok0 + (e >> 1), nt - 1), hf = e & 1;
+        ps[k] = *reinterpret_cast<const v4i*>(dx + (size_t)t * nblk + 8 * sb + 4 * hf);
     }
-
 }
 
 template <int BM, int BN, int NTH, int WC8, int XC, int SC>
 __device__ __forceinline__ void q6_stage(Q6Smem<BM, BN>& sm, const uint32_t (&pl)[WC8][5], const uint32_t (&phh)[WC8][5],
                                          const uint32_t (&pshift)[WC8], const v4i (&px)[XC], const v4i (&ps)[SC],
-                                         const v4i (&psc)[WC8], const uint32_t (&pd)[WC8], int tid)
+                                         const uint32_t (&psd)[WC8], int tid)
 {
     using SM = Q6Smem<BM, BN>;
 #pragma unroll
     for (int k = 0; k < WC8; ++k) {
-        const int e = tid + k * NTH;
-        if (e < BM * 8) {
-            const int r = e >> 3, c = e & 7;
-            const int h = c >> 2, jq = (c >> 1) & 1, half = c & 1;
-            const uint32_t sh = pshift[k];
-            uint32_t L[4], H[4];
+        const int e = task<BM * 8, NTH, WC8>(tid + k * NTH);
+        const int r = e >> 3, c = e & 7;
+        const int h = c >> 2, jq = (c >> 1) & 1, half = c & 1;
+        const uint32_t sh = pshift[k];
+        uint32_t L[4], H[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                L[i] = __builtin_amdgcn_alignbyte(pl[k][i + 1], pl[k][i], sh);
-                H[i] = __builtin_amdgcn_alignbyte(phh[k][i + 1], phh[k][i], sh);
-            }
-            const int hs1 = 2 * jq, hs2 = 2 * jq + 4;
-            int4 ca, cb;
-            ca.x = q6_center4(L[0] & 0x0F0F0F0Fu, (H[0] >> hs1) & 0x03030303u);
-            ca.y = q6_center4(L[1] & 0x0F0F0F0Fu, (H[1] >> hs1) & 0x03030303u);
-            ca.z = q6_center4(L[2] & 0x0F0F0F0Fu, (H[2] >> hs1) & 0x03030303u);
-            ca.w = q6_center4(L[3] & 0x0F0F0F0Fu, (H[3] >> hs1) & 0x03030303u);
-            cb.x = q6_center4((L[0] >> 4) & 0x0F0F0F0Fu, (H[0] >> hs2) & 0x03030303u);
-            cb.y = q6_center4((L[1] >> 4) & 0x0F0F0F0Fu, (H[1] >> hs2) & 0x03030303u);
-            cb.z = q6_center4((L[2] >> 4) & 0x0F0F0F0Fu, (H[2] >> hs2) & 0x03030303u);
-            cb.w = q6_center4((L[3] >> 4) & 0x0F0F0F0Fu, (H[3] >> hs2) & 0x03030303u);
-            // element index of the low-nibble piece: 128h + 32jq + 16half; high: +64
-            const int e1 = 128 * h + 32 * jq + 16 * half;
-            *reinterpret_cast<int4*>(&sm.wq[r * SM::W_STRIDE + e1]) = ca;
-            *reinterpret_cast<int4*>(&sm.wq[r * SM::W_STRIDE + e1 + 64]) = cb;
-            if (c < 2) {
-                const float dw = f16_bits_to_f32(pd[k]);
-                const uint32_t s0 = (uint32_t)psc[k].x, s1 = (uint32_t)psc[k].y;
-#pragma unroll
-                for (int gg = 0; gg < 4; ++gg) {
-                    sm.wsc[(8 * c + gg) * BM + r] = dw * (float)(int8_t)(s0 >> (8 * gg));
-                    sm.wsc[(8 * c + 4 + gg) * BM + r] = dw * (float)(int8_t)(s1 >> (8 * gg));
-                }
-            }
+        for (int i = 0; i < 4; ++i) {
+            L[i] = __builtin_amdgcn_alignbyte(pl[k][i + 1], pl[k][i], sh);
+            H[i] = __builtin_amdgcn_alignbyte(phh[k][i + 1], phh[k][i], sh);
         }
+        const int hs1 = 2 * jq, hs2 = 2 * jq + 4;
+        int4 ca, cb;
+        ca.x = q6_center4(L[0] & 0x0F0F0F0Fu, (H[0] >> hs1) & 0x03030303u);
+        ca.y = q6_center4(L[1] & 0x0F0F0F0Fu, (H[1] >> hs1) & 0x03030303u);
+        ca.z = q6_center4(L[2] & 0x0F0F0F0Fu, (H[2] >> hs1) & 0x03030303u);
+        ca.w = q6_center4(L[3] & 0x0F0F0F0Fu, (H[3] >> hs1) & 0x03030303u);
+        cb.x = q6_center4((L[0] >> 4) & 0x0F0F0F0Fu, (H[0] >> hs2) & 0x03030303u);
+        cb.y = q6_center4((L[1] >> 4) & 0x0F0F0F0Fu, (H[1] >> hs2) & 0x03030303u);
+        cb.z = q6_center4((L[2] >> 4) & 0x0F0F0F0Fu, (H[2] >> hs2) & 0x03030303u);
+        cb.w = q6_center4((L[3] >> 4) & 0x0F0F0F0Fu, (H[3] >> hs2) & 0x03030303u);
+        // element index of the low-nibble piece: 128h + 32jq + 16half; high: +64
+        const int e1 = 128 * h + 32 * jq + 16 * half;
+        *reinterpret_cast<int4*>(&sm.wq[r * SM::W_STRIDE + e1]) = ca;
+        *reinterpret_cast<int4*>(&sm.wq[r * SM::W_STRIDE + e1 + 64]) = cb;
+        // group scales 2c and 2c+1
+        const float dw = f16_bits_to_f32(psd[k] >> 16);
+        sm.wsc[(2 * c) * BM + r] = dw * (float)(int8_t)(psd[k] & 0xFF);
+        sm.wsc[(2 * c + 1) * BM + r] = dw * (float)(int8_t)((psd[k] >> 8) & 0xFF);
     }
 #pragma unroll
     for (int k = 0; k < XC; ++k) {
-        const int e = tid + k * NTH;
-        if (e < BN * 16)
-            *reinterpret_cast<v4i*>(&sm.xq[(e >> 4) * SM::X_STRIDE + 16 * (e & 15)]) = px[k];
+        const int e = task<BN * 16, NTH, XC>(tid + k * NTH);
+        *reinterpret_cast<v4i*>(&sm.xq[(e >> 4) * SM::X_STRIDE + 16 * (e & 15)]) = px[k];
     }
 #pragma unroll
     for (int k = 0; k < SC; ++k) {
-        const int e = tid + k * NTH;
-        if (e < BN * 2) {
-            const int t = e >> 1, hf = e & 1;
-            sm.xd[(4 * hf + 0) * BN + t] = __int_as_float(ps[k].x);
-            sm.xd[(4 * hf + 1) * BN + t] = __int_as_float(ps[k].y);
-            sm.xd[(4 * hf + 2) * BN + t] = __int_as_float(ps[k].z);
-            sm.xd[(4 * hf + 3) * BN + t] = __int_as_float(ps[k].w);
-        }
+        const int e = task<BN * 2, NTH, SC>(tid + k * NTH);
+        const int t = e >> 1, hf = e & 1;
+        sm.xd[(4 * hf + 0) * BN + t] = __int_as_float(ps[k].x);
+        sm.xd[(4 * hf + 1) * BN + t] = __int_as_float(ps[k].y);
+        sm.xd[(4 * hf + 2) * BN + t] = __int_as_float(ps[k].z);
+        sm.xd[(4 * hf + 3) * BN + t] = __int_as_float(ps[k].w);
     }
-
 }
 
 template <int WR, int WC, bool DUMP>
@@ -441,7 +469,7 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q6k_kernel(const uint8_t*
     constexpr int XC = (BN * 16 + NTH - 1) / NTH;
     constexpr int SC = (BN * 2 + NTH - 1) / NTH;
     using SM = Q6Smem<BM, BN>;
-    __shared__ SM sm;
+    __shared__ SM smb[2];
 
     const int ntb = (nt + BN - 1) / BN;
     const int tile = xcd_tile(ntb * ((od + BM - 1) / BM));
@@ -460,22 +488,21 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q6k_kernel(const uint8_t*
     // chunk (2-byte aligned blocks), the two scale dwords and d
     uint32_t pl[WC8][5], phh[WC8][5];
     uint32_t pshift[WC8];
-    v4i px[XC], ps[SC], psc[WC8];
-    uint32_t pd[WC8];
+    v4i px[XC], ps[SC];
+    uint32_t psd[WC8];
     v16f accv = {};
     const int arow = wr * 32 + li;
     const int btok = wc * 32 + li;
 
-    q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psc, pd, W, q, dx, 0, tid, row0, tok0, nt, od, id,
+    // double-buffered LDS, one barrier per super-block (as in the Q4_K kernel)
+    q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psd, W, q, dx, 0, tid, row0, tok0, nt, od, id,
                                           nblk, row_bytes);
+    q6_stage<BM, BN, NTH, WC8, XC, SC>(smb[0], pl, phh, pshift, px, ps, psd, tid);
+    q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psd, W, q, dx, min(1, nsb - 1), tid, row0,
+                                          tok0, nt, od, id, nblk, row_bytes);
+    __syncthreads();
     for (int sb = 0; sb < nsb; ++sb) {
-        if (sb > 0)
-            __syncthreads();
-        q6_stage<BM, BN, NTH, WC8, XC, SC>(sm, pl, phh, pshift, px, ps, psc, pd, tid);
-        __syncthreads();
-        if (sb + 1 < nsb)
-            q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psc, pd, W, q, dx, sb + 1, tid, row0, tok0,
-                                                  nt, od, id, nblk, row_bytes);
+        const SM& sm = smb[sb & 1];
 #pragma unroll 2
         for (int m = 0; m < 8; ++m) {
             // groups 2m and 2m+1 share activation block m
@@ -504,7 +531,15 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q6k_kernel(const uint8_t*
                     accv[i] = fmaf((float)C1[i], P[16 + i], accv[i]);
                 }
             }
+            // one step's MFMA results at a time: hoisting every MFMA of the
+            // super-block keeps all their results live (register spills)
+            __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        q6_stage<BM, BN, NTH, WC8, XC, SC>(smb[(sb + 1) & 1], pl, phh, pshift, px, ps, psd, tid);
+        q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psd, W, q, dx, min(sb + 2, nsb - 1), tid,
+                                              row0, tok0, nt, od, id, nblk, row_bytes);
+        __syncthreads();
     }
 
     if constexpr (!DUMP) {
