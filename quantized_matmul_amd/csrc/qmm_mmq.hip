@@ -103,46 +103,88 @@ __device__ __forceinline__ int task(int e)
         return min(e, N - 1);
 }
 
-template <int BM, int BN, int NTH, int QC, int HC, int XC, int SC>
-__device__ __forceinline__ void q4_prefetch(v4i (&pq)[QC], v4i (&ph)[HC], v4i (&px)[XC], v4i (&ps)[SC],
-                                            const uint8_t* __restrict__ W, const int8_t* __restrict__ q,
-                                            const float* __restrict__ dx, const float* __restrict__ sx, int sb,
-                                            int tid, int row0, int tok0, int nt, int od, int id, int nblk,
-                                            size_t row_bytes)
+// Prefetch loads are buffer loads: a wave-uniform resource (base address in
+// scalar registers) per operand, a per-thread byte offset fixed for the whole
+// kernel, and the super-block step as the scalar offset -- so the loop spends no
+// vector instructions on addresses.  The resource's range is the rest of the
+// operand from the tile's first row / token; rows past od and tokens past nt read
+// the last valid row / token (their results are never stored).
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, size_t bytes)
 {
-    // rows past od and tokens past nt read the last valid row / token: their
-    // results are never stored
+    // third descriptor word 0x00020000: raw 32-bit data, the gfx9-family setting
+    const int n = (int)(bytes < 0xFFFFFFF0u ? bytes : 0xFFFFFFF0u);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+
+__device__ __forceinline__ v4i bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+template <int QC, int HC, int XC, int SC>
+struct Q4Offs {
+    uint32_t q[QC], h[HC], x[XC], s[SC];
+};
+
+template <int BM, int BN, int NTH, int QC, int HC, int XC, int SC>
+__device__ __forceinline__ void q4_offsets(Q4Offs<QC, HC, XC, SC>& o, int tid, int row0, int tok0, int nt, int od,
+                                           int id, int nblk, uint32_t row_bytes)
+{
 #pragma unroll
     for (int k = 0; k < QC; ++k) {
         const int e = task<BM * 8, NTH, QC>(tid + k * NTH);
-        const int r = e >> 3, ch = e & 7;
-        const uint8_t* blk = W + (size_t)min(row0 + r, od - 1) * row_bytes + (size_t)sb * kQ4KBytes;
-        pq[k] = *reinterpret_cast<const v4i*>(blk + 16 + 16 * ch);
+        const uint32_t r = (uint32_t)(min(row0 + (e >> 3), od - 1) - row0);
+        o.q[k] = r * row_bytes + 16 + 16 * (e & 7);
     }
 #pragma unroll
     for (int k = 0; k < HC; ++k) {
         const int e = task<BM * 4, NTH, HC>(tid + k * NTH);
-        const uint8_t* blk = W + (size_t)min(row0 + (e >> 2), od - 1) * row_bytes + (size_t)sb * kQ4KBytes;
-        ph[k] = *reinterpret_cast<const v4i*>(blk);
+        o.h[k] = (uint32_t)(min(row0 + (e >> 2), od - 1) - row0) * row_bytes;
     }
 #pragma unroll
     for (int k = 0; k < XC; ++k) {
         const int e = task<BN * 16, NTH, XC>(tid + k * NTH);
-        const int t = min(tok0 + (e >> 4), nt - 1), ch = e & 15;
-        px[k] = *reinterpret_cast<const v4i*>(q + (size_t)t * id + 256 * sb + 16 * ch);
+        o.x[k] = (uint32_t)(min(tok0 + (e >> 4), nt - 1) - tok0) * (uint32_t)id + 16 * (e & 15);
     }
 #pragma unroll
     for (int k = 0; k < SC; ++k) {
-        const int e = task<BN * 4, NTH, SC>(tid + k * NTH);
-        const int t = min(tok0 + ((e >> 1) % BN), nt - 1), hf = e & 1;
-        const float* src = e < BN * 2 ? dx : sx;
-        ps[k] = *reinterpret_cast<const v4i*>(src + (size_t)t * nblk + 8 * sb + 4 * hf);
+        const int e = task<BN * 2, NTH, SC>(tid + k * NTH);
+        const uint32_t t = (uint32_t)(min(tok0 + (e >> 1), nt - 1) - tok0);
+        o.s[k] = (t * (uint32_t)nblk + 4 * (e & 1)) * 4;
+    }
+}
+
+// Resources of one tile: weights from row0, activation codes / d / s from tok0.
+struct Q4Rsrc {
+    __amdgpu_buffer_rsrc_t w, x, d, s;
+};
+
+template <int QC, int HC, int XC, int SC>
+__device__ __forceinline__ void q4_prefetch(v4i (&pq)[QC], v4i (&ph)[HC], v4i (&px)[XC], v4i (&pd)[SC], v4i (&ps)[SC],
+                                            const Q4Offs<QC, HC, XC, SC>& o, const Q4Rsrc& rs, int sb)
+{
+    const uint32_t ow = (uint32_t)sb * kQ4KBytes, ox = 256u * (uint32_t)sb, os = 32u * (uint32_t)sb;
+#pragma unroll
+    for (int k = 0; k < QC; ++k)
+        pq[k] = bload16(rs.w, o.q[k], ow);
+#pragma unroll
+    for (int k = 0; k < HC; ++k)
+        ph[k] = bload16(rs.w, o.h[k], ow);
+#pragma unroll
+    for (int k = 0; k < XC; ++k)
+        px[k] = bload16(rs.x, o.x[k], ox);
+#pragma unroll
+    for (int k = 0; k < SC; ++k) {
+        pd[k] = bload16(rs.d, o.s[k], os);
+        ps[k] = bload16(rs.s, o.s[k], os);
     }
 }
 
 template <int BM, int BN, int NTH, int QC, int HC, int XC, int SC>
 __device__ __forceinline__ void q4_stage(Q4Smem<BM, BN>& sm, const v4i (&pq)[QC], const v4i (&ph)[HC],
-                                         const v4i (&px)[XC], const v4i (&ps)[SC], int tid)
+                                         const v4i (&px)[XC], const v4i (&pd)[SC], const v4i (&ps)[SC], int tid)
 {
     using SM = Q4Smem<BM, BN>;
 #pragma unroll
@@ -172,15 +214,18 @@ __device__ __forceinline__ void q4_stage(Q4Smem<BM, BN>& sm, const v4i (&pq)[QC]
     }
 #pragma unroll
     for (int k = 0; k < SC; ++k) {
-        const int e = task<BN * 4, NTH, SC>(tid + k * NTH);
-        const int t = (e >> 1) % BN, hf = e & 1;
-        float* dst = e < BN * 2 ? sm.xd : sm.xs;
+        const int e = task<BN * 2, NTH, SC>(tid + k * NTH);
+        const int t = e >> 1, hf = e & 1;
         // __int_as_float per element: __builtin_bit_cast of an ext-vector
         // element is lowered as a cast of element 0 by this compiler.
-        dst[(4 * hf + 0) * BN + t] = __int_as_float(ps[k].x);
-        dst[(4 * hf + 1) * BN + t] = __int_as_float(ps[k].y);
-        dst[(4 * hf + 2) * BN + t] = __int_as_float(ps[k].z);
-        dst[(4 * hf + 3) * BN + t] = __int_as_float(ps[k].w);
+        sm.xd[(4 * hf + 0) * BN + t] = __int_as_float(pd[k].x);
+        sm.xd[(4 * hf + 1) * BN + t] = __int_as_float(pd[k].y);
+        sm.xd[(4 * hf + 2) * BN + t] = __int_as_float(pd[k].z);
+        sm.xd[(4 * hf + 3) * BN + t] = __int_as_float(pd[k].w);
+        sm.xs[(4 * hf + 0) * BN + t] = __int_as_float(ps[k].x);
+        sm.xs[(4 * hf + 1) * BN + t] = __int_as_float(ps[k].y);
+        sm.xs[(4 * hf + 2) * BN + t] = __int_as_float(ps[k].z);
+        sm.xs[(4 * hf + 3) * BN + t] = __int_as_float(ps[k].w);
     }
 
 }
@@ -194,15 +239,13 @@ __device__ __forceinline__ void q4_step(const Q4Smem<BM, BN>& sm, int p, int aro
                                         v16i& C1, v32f& P, v16f& accm)
 {
     using SM = Q4Smem<BM, BN>;
-    const uint4 A16 = *reinterpret_cast<const uint4*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
-    const int4 b0 = *reinterpret_cast<const int4*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
-    const int4 b1 = *reinterpret_cast<const int4*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
-    const v4i a0 = v4i{(int)(A16.x & 0x0F0F0F0Fu), (int)(A16.y & 0x0F0F0F0Fu), (int)(A16.z & 0x0F0F0F0Fu),
-                       (int)(A16.w & 0x0F0F0F0Fu)};
-    const v4i a1 = v4i{(int)((A16.x >> 4) & 0x0F0F0F0Fu), (int)((A16.y >> 4) & 0x0F0F0F0Fu),
-                       (int)((A16.z >> 4) & 0x0F0F0F0Fu), (int)((A16.w >> 4) & 0x0F0F0F0Fu)};
-    C0 = mfma_i8_k32(a0, v4i{b0.x, b0.y, b0.z, b0.w});
-    C1 = mfma_i8_k32(a1, v4i{b1.x, b1.y, b1.z, b1.w});
+    // one 16-byte read gives sub-block 2p (low nibbles) and 2p + 1 (high nibbles)
+    const v4i a16 = *reinterpret_cast<const v4i*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
+    const v4i a0 = a16 & 0x0F0F0F0F, a1 = (a16 >> 4) & 0x0F0F0F0F;
+    const v4i b0 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
+    const v4i b1 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
+    C0 = mfma_i8_k32(a0, b0);
+    C1 = mfma_i8_k32(a1, b1);
     // sub-block 2p + lh from this lane
     const int j = 2 * p + lh;
     P = mfma_outer2(sm.wsc[j * BM + arow], sm.xd[j * BN + btok]);
@@ -221,7 +264,7 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_kernel(const uint8_t*
     constexpr int QC = (BM * 8 + NTH - 1) / NTH;   // code chunks per thread
     constexpr int HC = (BM * 4 + NTH - 1) / NTH;   // header tasks per thread
     constexpr int XC = (BN * 16 + NTH - 1) / NTH;  // activation chunks per thread
-    constexpr int SC = (BN * 4 + NTH - 1) / NTH;   // activation scale float4s per thread
+    constexpr int SC = (BN * 2 + NTH - 1) / NTH;   // activation (d, s) float4 pairs per thread
     using SM = Q4Smem<BM, BN>;
     __shared__ SM smb[2];
 
@@ -236,10 +279,18 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_kernel(const uint8_t*
     const int li = lane & 31, lh = lane >> 5;
     const int nsb = id >> 8;
     const int nblk = id >> 5;
-    const size_t row_bytes = (size_t)nsb * kQ4KBytes;
+    const uint32_t row_bytes = (uint32_t)nsb * kQ4KBytes;
 
-    // ---- prefetch registers (one super-block)
-    v4i pq[QC], ph[HC], px[XC], ps[SC];
+    // ---- prefetch registers (one super-block), per-thread offsets, resources
+    v4i pq[QC], ph[HC], px[XC], pd[SC], ps[SC];
+    Q4Offs<QC, HC, XC, SC> offs;
+    q4_offsets<BM, BN, NTH, QC, HC, XC, SC>(offs, tid, row0, tok0, nt, od, id, nblk, row_bytes);
+    Q4Rsrc rs;
+    rs.w = buffer_rsrc(W + (size_t)row0 * row_bytes, (size_t)(od - row0) * row_bytes);
+    rs.x = buffer_rsrc(q + (size_t)tok0 * id, (size_t)(nt - tok0) * id);
+    rs.d = buffer_rsrc(dx + (size_t)tok0 * nblk, (size_t)(nt - tok0) * nblk * 4);
+    rs.s = buffer_rsrc(sx + (size_t)tok0 * nblk, (size_t)(nt - tok0) * nblk * 4);
+    auto prefetch = [&](int sbi) { q4_prefetch<QC, HC, XC, SC>(pq, ph, px, pd, ps, offs, rs, sbi); };
     v16f accv = {}, accm = {};
     const int arow = wr * 32 + li;   // this lane's row as an A operand
     const int btok = wc * 32 + li;   // this lane's token as a B operand
@@ -247,13 +298,12 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_kernel(const uint8_t*
     // Two LDS buffers: super-block sb computes from smb[sb & 1] while the next one,
     // already in registers, is stored into the other buffer and the loads of the
     // one after are issued; one barrier per super-block.
-    q4_prefetch<BM, BN, NTH, QC, HC, XC, SC>(pq, ph, px, ps, W, q, dx, sx, 0, tid, row0, tok0, nt, od, id, nblk, row_bytes);
-    q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[0], pq, ph, px, ps, tid);
+    prefetch(0);
+    q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[0], pq, ph, px, pd, ps, tid);
     // prefetches are unconditional (index clamped to the last super-block, an L2
     // re-read at the end): a prefetch under a branch merges register values and
     // costs spills
-    q4_prefetch<BM, BN, NTH, QC, HC, XC, SC>(pq, ph, px, ps, W, q, dx, sx, min(1, nsb - 1), tid, row0, tok0, nt, od,
-                                             id, nblk, row_bytes);
+    prefetch(min(1, nsb - 1));
     __syncthreads();
     for (int sb = 0; sb < nsb; ++sb) {
         const SM& sm = smb[sb & 1];
@@ -261,15 +311,12 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_kernel(const uint8_t*
             // integer products only, written out per sub-block
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const uint4 A16 = *reinterpret_cast<const uint4*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
-                const int4 b0 = *reinterpret_cast<const int4*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
-                const int4 b1 = *reinterpret_cast<const int4*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
-                const v4i a0 = v4i{(int)(A16.x & 0x0F0F0F0Fu), (int)(A16.y & 0x0F0F0F0Fu), (int)(A16.z & 0x0F0F0F0Fu),
-                                   (int)(A16.w & 0x0F0F0F0Fu)};
-                const v4i a1 = v4i{(int)((A16.x >> 4) & 0x0F0F0F0Fu), (int)((A16.y >> 4) & 0x0F0F0F0Fu),
-                                   (int)((A16.z >> 4) & 0x0F0F0F0Fu), (int)((A16.w >> 4) & 0x0F0F0F0Fu)};
-                const v16i C0 = mfma_i8_k32(a0, v4i{b0.x, b0.y, b0.z, b0.w});
-                const v16i C1 = mfma_i8_k32(a1, v4i{b1.x, b1.y, b1.z, b1.w});
+                const v4i a16 = *reinterpret_cast<const v4i*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
+                const v4i a0 = a16 & 0x0F0F0F0F, a1 = (a16 >> 4) & 0x0F0F0F0F;
+                const v4i b0 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
+                const v4i b1 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
+                const v16i C0 = mfma_i8_k32(a0, b0);
+                const v16i C1 = mfma_i8_k32(a1, b1);
                 const int tg = tok0 + btok;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -315,9 +362,8 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_kernel(const uint8_t*
         __builtin_amdgcn_sched_barrier(0);
         // smb[(sb + 1) & 1] was last read in super-block sb - 1, before the barrier;
         // after the last super-block this fills a buffer nobody reads
-        q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[(sb + 1) & 1], pq, ph, px, ps, tid);
-        q4_prefetch<BM, BN, NTH, QC, HC, XC, SC>(pq, ph, px, ps, W, q, dx, sx, min(sb + 2, nsb - 1), tid, row0, tok0,
-                                                 nt, od, id, nblk, row_bytes);
+        q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[(sb + 1) & 1], pq, ph, px, pd, ps, tid);
+        prefetch(min(sb + 2, nsb - 1));
         __syncthreads();
     }
 
