@@ -84,11 +84,16 @@ def copy_calibration(torch, mib):
     return {"bytes": n, "reps": 5}
 
 
-def mmq_grid_threads(nt, od):
-    """Launch shape of the MMQ kernel at a wide tile (128 rows x 64 tokens, 512
-    threads), workgroup count padded to a multiple of the 8 XCDs."""
-    tiles = -(-nt // 64) * -(-od // 128)
-    return 8 * -(-tiles // 8) * 512
+MMQ_TILES = {3: (4, 2, 1), 4: (2, 2, 1), 5: (2, 2, 2)}   # tile kind -> (row waves, token waves, K groups)
+
+
+def mmq_kernel(qmm, nt, od, idim):
+    """(kernel name, launch threads) of the Q4_K MMQ kernel the library runs for this
+    shape: 32*WR rows x 32*WC tokens per workgroup, KS groups splitting K, the
+    workgroup count padded to a multiple of the 8 XCDs."""
+    wr, wc, ks = MMQ_TILES[qmm.qmm_mmq_tile(nt, od, idim)]
+    tiles = -(-nt // (32 * wc)) * -(-od // (32 * wr))
+    return f"qmm::mmq_q4k_kernel<{wr}, {wc}, {ks}, false>", 8 * -(-tiles // 8) * 64 * wr * wc * ks
 
 
 class Call:
@@ -323,13 +328,13 @@ def main():
         tb2 = sum(float(np.mean(c.k_ms)) * 1e-3 for c in big)
         m = max(big, key=lambda c: float(np.mean(c.k_ms)))
         km = float(np.mean(m.k_ms)) * 1e-3
+        mk, mg = mmq_kernel(qmm, m.nt, m.od, m.idim)
         line["mmq"] = {"value": round(ops / tb2 / 1e12, 2), "unit": "TOP/s",
                        "roofline": {"bound": "mfma", "achieved": round(m.ops / km / 1e12, 2),
                                     "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                                     "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4),
-                                    "traffic": read_traffic(COUNTERS, "qmm::mmq_q4k_kernel<4, 2, false>",
-                                                            mmq_grid_threads(m.nt, m.od)),
-                                    "kernel": "mmq_q4k_kernel<4,2,false>", "call": m.label,
+                                    "traffic": read_traffic(COUNTERS, mk, mg),
+                                    "kernel": mk.replace("qmm::", "").replace(" ", ""), "call": m.label,
                                     "ops_per_launch": int(m.ops)}}
         line["config"] = {"workload": "q4k_decode_prefill",
                           "mmvq": "Q4_K 4096x4096 and 12288x4096, nt=1,4,8",

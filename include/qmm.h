@@ -74,7 +74,11 @@ enum {
 /* Dispatch kinds. */
 enum {
     QMM_KIND_MMVQ = 1, /* nt <= switch: weights streamed once, tokens in registers */
-    QMM_KIND_MMQ = 2   /* nt > switch: tiled int8 MFMA GEMM */
+    QMM_KIND_MMQ = 2,  /* nt > switch: tiled int8 MFMA GEMM, tile shape by cost model */
+    /* MMQ with a given tile shape (qmm_matmul_q8_kind and qmm_mmq_tile only): */
+    QMM_KIND_MMQ_128X64 = 3,        /* 128 rows x 64 tokens, 8 waves */
+    QMM_KIND_MMQ_64X64 = 4,         /* 64 rows x 64 tokens, 4 waves */
+    QMM_KIND_MMQ_64X64_SPLITK = 5   /* 64 x 64, 8 waves in two groups splitting K */
 };
 
 /* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K) or *210
@@ -112,10 +116,17 @@ int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, cons
                   int od, int id, float* out, void* stream);
 
 /* Same as qmm_matmul_q8 but with the kernel chosen by the caller (kind =
- * QMM_KIND_MMVQ for nt <= 8 only, or QMM_KIND_MMQ for any nt).  For tests and
- * measurement of both kernels on one shape. */
+ * QMM_KIND_MMVQ for nt <= 8 only, QMM_KIND_MMQ for any nt, or one of the
+ * QMM_KIND_MMQ_* tile shapes for any nt).  For tests and measurement of every
+ * kernel variant on one shape.  Unknown kind: QMM_ERR_ARG. */
 int qmm_matmul_q8_kind(int kind, int type, const void* W, const int8_t* q, const float* d,
                        const float* s, int nt, int od, int id, float* out, void* stream);
+
+/* The MMQ tile shape (QMM_KIND_MMQ_128X64, _64X64 or _64X64_SPLITK) that MMQ uses
+ * for this shape: the one with the fewest (rounds of workgroups over the 256 CUs)
+ * x (super-blocks per wave).  Negative status for invalid shapes.  Environment
+ * QMM_MMQ_TILE = 1, 2 or 3 (read once) forces one, for tuning. */
+int qmm_mmq_tile(int nt, int od, int id);
 
 /* Which kernel qmm_matmul would run for this call: QMM_KIND_MMVQ or QMM_KIND_MMQ,
  * or a negative status for invalid arguments. */

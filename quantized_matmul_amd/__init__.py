@@ -24,6 +24,9 @@ QMM_TYPE_Q4_K = 1
 QMM_TYPE_Q6_K = 2
 QMM_KIND_MMVQ = 1
 QMM_KIND_MMQ = 2
+QMM_KIND_MMQ_128X64 = 3
+QMM_KIND_MMQ_64X64 = 4
+QMM_KIND_MMQ_64X64_SPLITK = 5
 QMM_OK = 0
 QMM_ERR_ARG = -1
 QMM_ERR_TYPE = -2
@@ -36,7 +39,7 @@ QMM_ERR_LAUNCH = -7
 BLOCK_BYTES = {QMM_TYPE_Q4_K: 144, QMM_TYPE_Q6_K: 210}
 
 EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8",
-           "qmm_matmul_q8_kind", "qmm_dispatch_kind", "qmm_nt_switch", "qmm_group_dots",
+           "qmm_matmul_q8_kind", "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots",
            "qmm_mfma_tile_check", "qmm_strerror")
 
 
@@ -67,13 +70,14 @@ def lib():
         L.qmm_matmul_q8.argtypes = [I, P, P, P, P, I, I, I, P, P]
         L.qmm_matmul_q8_kind.argtypes = [I, I, P, P, P, P, I, I, I, P, P]
         L.qmm_dispatch_kind.argtypes = [I, I, I, I]
+        L.qmm_mmq_tile.argtypes = [I, I, I]
         L.qmm_nt_switch.argtypes = []
         L.qmm_group_dots.argtypes = [I, I, P, P, I, I, I, P, P]
         L.qmm_mfma_tile_check.argtypes = [I, P, P, P, P]
         L.qmm_strerror.argtypes = [I]
         L.qmm_strerror.restype = ctypes.c_char_p
         for f in ("qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8", "qmm_matmul_q8_kind",
-                  "qmm_dispatch_kind", "qmm_nt_switch", "qmm_group_dots", "qmm_mfma_tile_check"):
+                  "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots", "qmm_mfma_tile_check"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -124,6 +128,14 @@ def qmm_dispatch_kind(qtype: int, nt: int, od: int, idim: int) -> int:
     k = int(lib().qmm_dispatch_kind(qtype, nt, od, idim))
     if k < 0:
         raise QmmError(k, "qmm_dispatch_kind")
+    return k
+
+
+def qmm_mmq_tile(nt: int, od: int, idim: int) -> int:
+    """The MMQ tile shape (a QMM_KIND_MMQ_* value) used for this shape."""
+    k = int(lib().qmm_mmq_tile(nt, od, idim))
+    if k < 0:
+        raise QmmError(k, "qmm_mmq_tile")
     return k
 
 

@@ -81,7 +81,8 @@ int matmul_q8_checked(int kind, int type, const void* W, const int8_t* q, const 
     const auto w = reinterpret_cast<const uint8_t*>(W);
     if (kind == QMM_KIND_MMVQ)
         return launched(qmm::launch_mmvq(type, w, q, d, s, nt, od, id, out, S, st));
-    return launched(qmm::launch_mmq(type, w, q, d, s, nt, od, id, out, S, st));
+    const int tile = kind >= QMM_KIND_MMQ_128X64 ? kind - QMM_KIND_MMQ_128X64 + 1 : 0;
+    return launched(qmm::launch_mmq(type, w, q, d, s, nt, od, id, out, S, st, tile));
 }
 
 int validate_q8(int type, const void* W, const int8_t* q, const float* d, const float* s, int nt,
@@ -146,6 +147,14 @@ int qmm_dispatch_kind(int type, int nt, int od, int id)
     return nt <= nt_switch_value() ? QMM_KIND_MMVQ : QMM_KIND_MMQ;
 }
 
+int qmm_mmq_tile(int nt, int od, int id)
+{
+    const int rc = check_shape(nt, od, id);
+    if (rc)
+        return rc;
+    return QMM_KIND_MMQ_128X64 - 1 + qmm::mmq_tile_choice(nt, od, id);
+}
+
 int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, const float* s, int nt,
                   int od, int id, float* out, void* stream)
 {
@@ -162,7 +171,7 @@ int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, cons
 int qmm_matmul_q8_kind(int kind, int type, const void* W, const int8_t* q, const float* d,
                        const float* s, int nt, int od, int id, float* out, void* stream)
 {
-    if (kind != QMM_KIND_MMVQ && kind != QMM_KIND_MMQ)
+    if (kind < QMM_KIND_MMVQ || kind > QMM_KIND_MMQ_64X64_SPLITK)
         return QMM_ERR_ARG;
     int rc = validate_q8(type, W, q, d, s, nt, od, id, out);
     if (rc)

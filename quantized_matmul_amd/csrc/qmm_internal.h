@@ -24,8 +24,11 @@ hipError_t launch_quantize(const float* x, int nt, int id, int8_t* q, float* d, 
                            hipStream_t st);
 hipError_t launch_mmvq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
                        int nt, int od, int id, float* out, int32_t* S, hipStream_t st);
+// tile: 0 = by the cost model (mmq_tile_choice), 1 = 128 x 64, 2 = 64 x 64,
+// 3 = 64 x 64 split over K in two groups.  S != null (the debug dump) runs 64 x 64.
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
-                      int nt, int od, int id, float* out, int32_t* S, hipStream_t st);
+                      int nt, int od, int id, float* out, int32_t* S, hipStream_t st, int tile = 0);
+int mmq_tile_choice(int nt, int od, int id);
 hipError_t launch_mfma_tile_probe(int kind, const void* A, const void* B, void* C, hipStream_t st);
 
 // ---------------------------------------------------------------- device helpers

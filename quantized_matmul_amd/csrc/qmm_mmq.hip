@@ -32,6 +32,8 @@
 //    conflict-free), decoded per-(row, group) f32 scales, activation codes and
 //    activation scales are staged in LDS; the next super-block's global loads are
 //    issued before the compute of the current one.
+#include <stdlib.h>
+
 #include "qmm_internal.h"
 
 namespace qmm {
@@ -182,9 +184,12 @@ __device__ __forceinline__ void q4_prefetch(v4i (&pq)[QC], v4i (&ph)[HC], v4i (&
     }
 }
 
+// valid == false (a super-block index past the end, in a split over K) stages
+// zero scales: that super-block then adds nothing, with no branch.
 template <int BM, int BN, int NTH, int QC, int HC, int XC, int SC>
 __device__ __forceinline__ void q4_stage(Q4Smem<BM, BN>& sm, const v4i (&pq)[QC], const v4i (&ph)[HC],
-                                         const v4i (&px)[XC], const v4i (&pd)[SC], const v4i (&ps)[SC], int tid)
+                                         const v4i (&px)[XC], const v4i (&pd)[SC], const v4i (&ps)[SC], int tid,
+                                         bool valid)
 {
     using SM = Q4Smem<BM, BN>;
 #pragma unroll
@@ -202,10 +207,10 @@ __device__ __forceinline__ void q4_stage(Q4Smem<BM, BN>& sm, const v4i (&pq)[QC]
         const float dm = f16_bits_to_f32((uint32_t)h.x >> 16);
         int sc0, m0, sc1, m1;
         q4k_scale_min_pair((uint32_t)h.y, (uint32_t)h.z, (uint32_t)h.w, jj, sc0, m0, sc1, m1);
-        sm.wsc[jj * BM + r] = dw * (float)sc0;
-        sm.wmn[jj * BM + r] = -(dm * (float)m0);
-        sm.wsc[(jj + 4) * BM + r] = dw * (float)sc1;
-        sm.wmn[(jj + 4) * BM + r] = -(dm * (float)m1);
+        sm.wsc[jj * BM + r] = valid ? dw * (float)sc0 : 0.f;
+        sm.wmn[jj * BM + r] = valid ? -(dm * (float)m0) : 0.f;
+        sm.wsc[(jj + 4) * BM + r] = valid ? dw * (float)sc1 : 0.f;
+        sm.wmn[(jj + 4) * BM + r] = valid ? -(dm * (float)m1) : 0.f;
     }
 #pragma unroll
     for (int k = 0; k < XC; ++k) {
@@ -230,6 +235,55 @@ __device__ __forceinline__ void q4_stage(Q4Smem<BM, BN>& sm, const v4i (&pq)[QC]
 
 }
 
+// Split over K: groups 1 .. KS-1 write their partial 32 x 32 tile (v, the
+// lane's 16 values) to LDS; group 0 adds them in group order.  Returns false for
+// the waves that are done (groups past 0).  Called by every wave after the last
+// barrier of the K loop; red is the workgroup's tile memory, free by then.
+template <int NW, int KS>
+__device__ __forceinline__ bool combine_k_groups(v16f& v, float* red, int kg, int gw, int lane)
+{
+    if constexpr (KS == 1) {
+        return true;
+    } else {
+        if (kg > 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                red[((kg - 1) * NW + gw) * 1024 + i * 64 + lane] = v[i];
+        }
+        __syncthreads();
+        if (kg > 0)
+            return false;
+#pragma unroll
+        for (int g = 1; g < KS; ++g)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] += red[((g - 1) * NW + gw) * 1024 + i * 64 + lane];
+        return true;
+    }
+}
+
+// Store one wave's 32 x 32 result tile (lane: token tg, rows r0 + 8k + 4 lh + 0..3
+// from v[4k .. 4k+3]) into out [nt][od], masked at the edges.
+__device__ __forceinline__ void store_tile(const v16f& v, float* __restrict__ out, int nt, int od, int tg, int r0,
+                                           int lh)
+{
+    if (tg >= nt)
+        return;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int rg = r0 + 8 * k + 4 * lh;
+        float* o = out + (size_t)tg * od + rg;
+        if (rg + 3 < od && (od & 3) == 0) {
+            *reinterpret_cast<float4*>(o) = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+        } else {
+            if (rg < od) o[0] = v[4 * k];
+            if (rg + 1 < od) o[1] = v[4 * k + 1];
+            if (rg + 2 < od) o[2] = v[4 * k + 2];
+            if (rg + 3 < od) o[3] = v[4 * k + 3];
+        }
+    }
+}
+
 // One compute step of the Q4_K kernel: sub-blocks 2p and 2p + 1 of the staged
 // super-block.  C0 / C1: the two int8 tile products; P: their scale products
 // (d*sc)[row] x dx[token] from one outer-product pair; the min term of the same
@@ -252,33 +306,43 @@ __device__ __forceinline__ void q4_step(const Q4Smem<BM, BN>& sm, int p, int aro
     accm = mfma_k2(sm.wmn[j * BM + arow], sm.xs[j * BN + btok], accm);
 }
 
-template <int WR, int WC, bool DUMP>
-__global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_kernel(const uint8_t* __restrict__ W,
-                                                               const int8_t* __restrict__ q,
-                                                               const float* __restrict__ dx,
-                                                               const float* __restrict__ sx,
-                                                               float* __restrict__ out, int nt, int od,
-                                                               int id, int32_t* __restrict__ S)
+// KS > 1 splits K inside the workgroup: KS groups of WR x WC waves, each with its
+// own double-buffered LDS tiles, take super-blocks kg, kg + KS, kg + 2 KS, ...;
+// at the end groups 1 .. KS-1 hand their 32 x 32 partial sums to group 0 through
+// LDS, which adds them in group order (a fixed order: the result does not
+// depend on timing).  It gives a tile grid with few tiles more waves.
+template <int WR, int WC, int KS, bool DUMP>
+__global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q4k_kernel(const uint8_t* __restrict__ W,
+                                                                    const int8_t* __restrict__ q,
+                                                                    const float* __restrict__ dx,
+                                                                    const float* __restrict__ sx,
+                                                                    float* __restrict__ out, int nt, int od,
+                                                                    int id, int32_t* __restrict__ S)
 {
-    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;
+    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;   // NTH: threads of one K group
     constexpr int QC = (BM * 8 + NTH - 1) / NTH;   // code chunks per thread
     constexpr int HC = (BM * 4 + NTH - 1) / NTH;   // header tasks per thread
     constexpr int XC = (BN * 16 + NTH - 1) / NTH;  // activation chunks per thread
     constexpr int SC = (BN * 2 + NTH - 1) / NTH;   // activation (d, s) float4 pairs per thread
     using SM = Q4Smem<BM, BN>;
-    __shared__ SM smb[2];
+    __shared__ SM smb[KS][2];
+    static_assert(!DUMP || KS == 1, "the debug dump runs unsplit");
+    static_assert((KS - 1) * WR * WC * 1024 * sizeof(float) <= sizeof(smb), "reduction scratch fits the tiles");
 
     const int ntb = (nt + BN - 1) / BN;
     const int tile = xcd_tile(ntb * ((od + BM - 1) / BM));
     if (tile < 0)
         return;  // whole workgroup
     const int row0 = (tile / ntb) * BM, tok0 = (tile % ntb) * BN;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wr = wave / WC, wc = wave % WC;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // K group and wave in group (a compile-time 0 without a split)
+    const int kg = KS > 1 ? wave / (WR * WC) : 0, gw = wave - kg * (WR * WC);
+    const int tid = threadIdx.x - kg * NTH;                           // thread in group
+    const int wr = gw / WC, wc = gw % WC;
     const int li = lane & 31, lh = lane >> 5;
     const int nsb = id >> 8;
     const int nblk = id >> 5;
+    const int niter = (nsb + KS - 1) / KS;
     const uint32_t row_bytes = (uint32_t)nsb * kQ4KBytes;
 
     // ---- prefetch registers (one super-block), per-thread offsets, resources
@@ -295,18 +359,19 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_kernel(const uint8_t*
     const int arow = wr * 32 + li;   // this lane's row as an A operand
     const int btok = wc * 32 + li;   // this lane's token as a B operand
 
-    // Two LDS buffers: super-block sb computes from smb[sb & 1] while the next one,
-    // already in registers, is stored into the other buffer and the loads of the
-    // one after are issued; one barrier per super-block.
-    prefetch(0);
-    q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[0], pq, ph, px, pd, ps, tid);
-    // prefetches are unconditional (index clamped to the last super-block, an L2
+    // Two LDS buffers per K group: iteration i computes from smb[kg][i & 1] while
+    // the next super-block, already in registers, is stored into the other buffer
+    // and the loads of the one after are issued; one barrier per iteration.
+    // Prefetches are unconditional (index clamped to the last super-block, an L2
     // re-read at the end): a prefetch under a branch merges register values and
-    // costs spills
-    prefetch(min(1, nsb - 1));
+    // costs spills.
+    prefetch(min(kg, nsb - 1));
+    q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[kg][0], pq, ph, px, pd, ps, tid, kg < nsb);
+    prefetch(min(KS + kg, nsb - 1));
     __syncthreads();
-    for (int sb = 0; sb < nsb; ++sb) {
-        const SM& sm = smb[sb & 1];
+    for (int it = 0; it < niter; ++it) {
+        const SM& sm = smb[kg][it & 1];
+        const int sb = it * KS + kg;
         if constexpr (DUMP) {
             // integer products only, written out per sub-block
 #pragma unroll
@@ -360,32 +425,18 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_kernel(const uint8_t*
         // keep the staging of the next super-block after the compute (moved into
         // it, its values would be live across the whole compute phase)
         __builtin_amdgcn_sched_barrier(0);
-        // smb[(sb + 1) & 1] was last read in super-block sb - 1, before the barrier;
-        // after the last super-block this fills a buffer nobody reads
-        q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[(sb + 1) & 1], pq, ph, px, pd, ps, tid);
-        prefetch(min(sb + 2, nsb - 1));
+        // smb[kg][(it + 1) & 1] was last read in iteration it - 1, before the
+        // barrier; after the last iteration this fills a buffer nobody reads
+        q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[kg][(it + 1) & 1], pq, ph, px, pd, ps, tid, sb + KS < nsb);
+        prefetch(min(sb + 2 * KS, nsb - 1));
         __syncthreads();
     }
 
     if constexpr (!DUMP) {
-        const int tg = tok0 + btok;
-        if (tg < nt) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int rg = row0 + wr * 32 + 8 * k + 4 * lh;
-                float* o = out + (size_t)tg * od + rg;
-                const float v0 = accv[4 * k] + accm[4 * k], v1 = accv[4 * k + 1] + accm[4 * k + 1];
-                const float v2 = accv[4 * k + 2] + accm[4 * k + 2], v3 = accv[4 * k + 3] + accm[4 * k + 3];
-                if (rg + 3 < od && (od & 3) == 0) {
-                    *reinterpret_cast<float4*>(o) = make_float4(v0, v1, v2, v3);
-                } else {
-                    if (rg < od) o[0] = v0;
-                    if (rg + 1 < od) o[1] = v1;
-                    if (rg + 2 < od) o[2] = v2;
-                    if (rg + 3 < od) o[3] = v3;
-                }
-            }
-        }
+        v16f v = accv + accm;
+        if (!combine_k_groups<WR * WC, KS>(v, reinterpret_cast<float*>(&smb[0][0]), kg, gw, lane))
+            return;
+        store_tile(v, out, nt, od, tok0 + btok, row0 + wr * 32, lh);
     }
 }
 
@@ -453,7 +504,7 @@ __device__ __forceinline__ void q6_prefetch(uint32_t (&pl)[WC8][5], uint32_t (&p
 template <int BM, int BN, int NTH, int WC8, int XC, int SC>
 __device__ __forceinline__ void q6_stage(Q6Smem<BM, BN>& sm, const uint32_t (&pl)[WC8][5], const uint32_t (&phh)[WC8][5],
                                          const uint32_t (&pshift)[WC8], const v4i (&px)[XC], const v4i (&ps)[SC],
-                                         const uint32_t (&psd)[WC8], int tid)
+                                         const uint32_t (&psd)[WC8], int tid, bool valid)
 {
     using SM = Q6Smem<BM, BN>;
 #pragma unroll
@@ -483,7 +534,8 @@ __device__ __forceinline__ void q6_stage(Q6Smem<BM, BN>& sm, const uint32_t (&pl
         *reinterpret_cast<int4*>(&sm.wq[r * SM::W_STRIDE + e1]) = ca;
         *reinterpret_cast<int4*>(&sm.wq[r * SM::W_STRIDE + e1 + 64]) = cb;
         // group scales 2c and 2c+1
-        const float dw = f16_bits_to_f32(psd[k] >> 16);
+        // a super-block past the end (split over K) stages zero scales
+        const float dw = valid ? f16_bits_to_f32(psd[k] >> 16) : 0.f;
         sm.wsc[(2 * c) * BM + r] = dw * (float)(int8_t)(psd[k] & 0xFF);
         sm.wsc[(2 * c + 1) * BM + r] = dw * (float)(int8_t)((psd[k] >> 8) & 0xFF);
     }
@@ -503,31 +555,35 @@ __device__ __forceinline__ void q6_stage(Q6Smem<BM, BN>& sm, const uint32_t (&pl
     }
 }
 
-template <int WR, int WC, bool DUMP>
-__global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q6k_kernel(const uint8_t* __restrict__ W,
-                                                               const int8_t* __restrict__ q,
-                                                               const float* __restrict__ dx,
-                                                               float* __restrict__ out, int nt, int od,
-                                                               int id, int32_t* __restrict__ S)
+template <int WR, int WC, int KS, bool DUMP>
+__global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q6k_kernel(const uint8_t* __restrict__ W,
+                                                                    const int8_t* __restrict__ q,
+                                                                    const float* __restrict__ dx,
+                                                                    float* __restrict__ out, int nt, int od,
+                                                                    int id, int32_t* __restrict__ S)
 {
-    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;
+    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;   // NTH: threads of one K group
     constexpr int WC8 = (BM * 8 + NTH - 1) / NTH;  // (row, 32-code piece) tasks per thread
     constexpr int XC = (BN * 16 + NTH - 1) / NTH;
     constexpr int SC = (BN * 2 + NTH - 1) / NTH;
     using SM = Q6Smem<BM, BN>;
-    __shared__ SM smb[2];
+    __shared__ SM smb[KS][2];   // K groups as in the Q4_K kernel
+    static_assert(!DUMP || KS == 1, "the debug dump runs unsplit");
+    static_assert((KS - 1) * WR * WC * 1024 * sizeof(float) <= sizeof(smb), "reduction scratch fits the tiles");
 
     const int ntb = (nt + BN - 1) / BN;
     const int tile = xcd_tile(ntb * ((od + BM - 1) / BM));
     if (tile < 0)
         return;
     const int row0 = (tile / ntb) * BM, tok0 = (tile % ntb) * BN;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wr = wave / WC, wc = wave % WC;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kg = KS > 1 ? wave / (WR * WC) : 0, gw = wave - kg * (WR * WC);
+    const int tid = threadIdx.x - kg * NTH;
+    const int wr = gw / WC, wc = gw % WC;
     const int li = lane & 31, lh = lane >> 5;
     const int nsb = id >> 8;
     const int nblk = id >> 5;
+    const int niter = (nsb + KS - 1) / KS;
     const size_t row_bytes = (size_t)nsb * kQ6KBytes;
 
     // prefetch registers: per task the five-dword windows of a low and a high
@@ -540,15 +596,16 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q6k_kernel(const uint8_t*
     const int arow = wr * 32 + li;
     const int btok = wc * 32 + li;
 
-    // double-buffered LDS, one barrier per super-block (as in the Q4_K kernel)
-    q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psd, W, q, dx, 0, tid, row0, tok0, nt, od, id,
-                                          nblk, row_bytes);
-    q6_stage<BM, BN, NTH, WC8, XC, SC>(smb[0], pl, phh, pshift, px, ps, psd, tid);
-    q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psd, W, q, dx, min(1, nsb - 1), tid, row0,
+    // double-buffered LDS per K group, one barrier per iteration (as in the Q4_K kernel)
+    q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psd, W, q, dx, min(kg, nsb - 1), tid, row0, tok0,
+                                          nt, od, id, nblk, row_bytes);
+    q6_stage<BM, BN, NTH, WC8, XC, SC>(smb[kg][0], pl, phh, pshift, px, ps, psd, tid, kg < nsb);
+    q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psd, W, q, dx, min(KS + kg, nsb - 1), tid, row0,
                                           tok0, nt, od, id, nblk, row_bytes);
     __syncthreads();
-    for (int sb = 0; sb < nsb; ++sb) {
-        const SM& sm = smb[sb & 1];
+    for (int it = 0; it < niter; ++it) {
+        const SM& sm = smb[kg][it & 1];
+        const int sb = it * KS + kg;
 #pragma unroll 2
         for (int m = 0; m < 8; ++m) {
             // groups 2m and 2m+1 share activation block m
@@ -582,29 +639,17 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q6k_kernel(const uint8_t*
             __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        q6_stage<BM, BN, NTH, WC8, XC, SC>(smb[(sb + 1) & 1], pl, phh, pshift, px, ps, psd, tid);
-        q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psd, W, q, dx, min(sb + 2, nsb - 1), tid,
+        q6_stage<BM, BN, NTH, WC8, XC, SC>(smb[kg][(it + 1) & 1], pl, phh, pshift, px, ps, psd, tid, sb + KS < nsb);
+        q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psd, W, q, dx, min(sb + 2 * KS, nsb - 1), tid,
                                               row0, tok0, nt, od, id, nblk, row_bytes);
         __syncthreads();
     }
 
     if constexpr (!DUMP) {
-        const int tg = tok0 + btok;
-        if (tg < nt) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int rg = row0 + wr * 32 + 8 * k + 4 * lh;
-                float* o = out + (size_t)tg * od + rg;
-                if (rg + 3 < od && (od & 3) == 0) {
-                    *reinterpret_cast<float4*>(o) = make_float4(accv[4 * k], accv[4 * k + 1], accv[4 * k + 2], accv[4 * k + 3]);
-                } else {
-                    if (rg < od) o[0] = accv[4 * k];
-                    if (rg + 1 < od) o[1] = accv[4 * k + 1];
-                    if (rg + 2 < od) o[2] = accv[4 * k + 2];
-                    if (rg + 3 < od) o[3] = accv[4 * k + 3];
-                }
-            }
-        }
+        v16f v = accv;
+        if (!combine_k_groups<WR * WC, KS>(v, reinterpret_cast<float*>(&smb[0][0]), kg, gw, lane))
+            return;
+        store_tile(v, out, nt, od, tok0 + btok, row0 + wr * 32, lh);
     }
 }
 
@@ -658,7 +703,7 @@ hipError_t launch_mfma_tile_probe(int kind, const void* A, const void* B, void* 
 
 // ------------------------------------------------------------------ launch
 
-template <int WR, int WC, bool DUMP>
+template <int WR, int WC, int KS, bool DUMP>
 static hipError_t launch_tile(int type, const uint8_t* W, const int8_t* q, const float* d,
                               const float* s, int nt, int od, int id, float* out, int32_t* S,
                               hipStream_t st)
@@ -666,25 +711,62 @@ static hipError_t launch_tile(int type, const uint8_t* W, const int8_t* q, const
     const int ntiles = ((nt + 32 * WC - 1) / (32 * WC)) * ((od + 32 * WR - 1) / (32 * WR));
     const int grid = 8 * ((ntiles + 7) / 8);
     if (type == 1)
-        hipLaunchKernelGGL((mmq_q4k_kernel<WR, WC, DUMP>), dim3(grid), dim3(64 * WR * WC), 0, st, W, q, d, s,
-                           out, nt, od, id, S);
+        hipLaunchKernelGGL((mmq_q4k_kernel<WR, WC, KS, DUMP>), dim3(grid), dim3(64 * WR * WC * KS), 0, st, W, q,
+                           d, s, out, nt, od, id, S);
     else
-        hipLaunchKernelGGL((mmq_q6k_kernel<WR, WC, DUMP>), dim3(grid), dim3(64 * WR * WC), 0, st, W, q, d, out,
-                           nt, od, id, S);
+        hipLaunchKernelGGL((mmq_q6k_kernel<WR, WC, KS, DUMP>), dim3(grid), dim3(64 * WR * WC * KS), 0, st, W, q,
+                           d, out, nt, od, id, S);
     return hipGetLastError();
 }
 
-// Tile shape: 128 rows x 64 tokens (8 waves) when that still gives every CU a
-// tile, else 64 x 64 (4 waves).
+// Shape of the launch, by a cost model: the time of a configuration is taken as
+// (rounds of workgroups over the 256 CUs) x (super-blocks each wave walks), all
+// configurations running two waves per SIMD when the chip is full:
+//   128 x 64 tile, 8 waves, 1 workgroup per CU (LDS);
+//   64 x 64 tile, 4 waves, 2 workgroups per CU;
+//   64 x 64 tile split over K in 2 groups, 8 waves, 1 workgroup per CU.
+// Ties go to the larger tile (fewer re-reads of weights and activations).
+// QMM_MMQ_TILE (1, 2 or 3 for the three shapes above) overrides it, for tuning.
+static int tile_override()
+{
+    static int v = -1;
+    int cur = __atomic_load_n(&v, __ATOMIC_ACQUIRE);
+    if (cur >= 0)
+        return cur;
+    const char* e = getenv("QMM_MMQ_TILE");
+    int val = e ? atoi(e) : 0;
+    if (val < 1 || val > 3)
+        val = 0;
+    __atomic_store_n(&v, val, __ATOMIC_RELEASE);
+    return val;
+}
+
+int mmq_tile_choice(int nt, int od, int id)
+{
+    const int o = tile_override();
+    if (o)
+        return o;
+    const long nsb = id / 256;
+    const long t42 = (long)((nt + 63) / 64) * ((od + 127) / 128);
+    const long t22 = (long)((nt + 63) / 64) * ((od + 63) / 64);
+    const long c1 = ((t42 + 255) / 256) * nsb;
+    const long c2 = ((t22 + 511) / 512) * nsb;
+    const long c3 = ((t22 + 255) / 256) * ((nsb + 1) / 2);
+    if (c1 <= c2 && c1 <= c3)
+        return 1;
+    return c2 <= c3 ? 2 : 3;
+}
+
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
-                      int nt, int od, int id, float* out, int32_t* S, hipStream_t st)
+                      int nt, int od, int id, float* out, int32_t* S, hipStream_t st, int tile)
 {
     if (S)
-        return launch_tile<2, 2, true>(type, W, q, d, s, nt, od, id, out, S, st);
-    const long big = (long)((nt + 63) / 64) * ((od + 127) / 128);
-    if (big >= 256)
-        return launch_tile<4, 2, false>(type, W, q, d, s, nt, od, id, out, S, st);
-    return launch_tile<2, 2, false>(type, W, q, d, s, nt, od, id, out, S, st);
+        return launch_tile<2, 2, 1, true>(type, W, q, d, s, nt, od, id, out, S, st);
+    switch (tile ? tile : mmq_tile_choice(nt, od, id)) {
+    case 1: return launch_tile<4, 2, 1, false>(type, W, q, d, s, nt, od, id, out, S, st);
+    case 2: return launch_tile<2, 2, 1, false>(type, W, q, d, s, nt, od, id, out, S, st);
+    default: return launch_tile<2, 2, 2, false>(type, W, q, d, s, nt, od, id, out, S, st);
+    }
 }
 
 }  // namespace qmm

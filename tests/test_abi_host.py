@@ -78,7 +78,11 @@ def test_validation_before_device_work():
     assert L.qmm_matmul(1, mis, p, 1, 4, 256, p, p, big, None) == qmm.QMM_ERR_ALIGN
     assert L.qmm_matmul(1, p, p, 1, 4, 256, p, p, 10, None) == qmm.QMM_ERR_WORKSPACE
     assert L.qmm_matmul_q8(2, p, p, p, mis, 1, 4, 256, p, None) == qmm.QMM_ERR_ALIGN
-    assert L.qmm_matmul_q8_kind(3, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_matmul_q8_kind(0, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_matmul_q8_kind(6, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    # the MMQ tile kinds pass validation; without a GPU the device check answers
+    assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_64X64_SPLITK, 1, p, p, p, p, 1, 4, 256, p, None) == \
+        qmm.QMM_ERR_DEVICE
     assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMVQ, 1, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_ARG
     assert L.qmm_quantize_act(p, 1, 40, p, p, p, None) == qmm.QMM_ERR_SHAPE
     assert L.qmm_group_dots(qmm.QMM_KIND_MMVQ, 1, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_ARG
@@ -110,3 +114,21 @@ def test_product_does_not_import_oracle():
     src = "".join(open(os.path.join(ROOT, "quantized_matmul_amd", f)).read()
                   for f in os.listdir(os.path.join(ROOT, "quantized_matmul_amd")) if f.endswith(".py"))
     assert "oracle" not in src.replace("no CPU path", "")
+
+
+def test_mmq_tile_choice():
+    """The MMQ tile shape by the cost model (rounds of workgroups x super-blocks per
+    wave), on the benchmark shapes and a few small ones; invalid shapes are errors."""
+    qmm = pytest.importorskip("quantized_matmul_amd")
+    T128, T64, TSPLIT = qmm.QMM_KIND_MMQ_128X64, qmm.QMM_KIND_MMQ_64X64, qmm.QMM_KIND_MMQ_64X64_SPLITK
+    # nt = 512: 768 / 256 tiles of 128 x 64 fill the CUs in whole rounds; ties keep the big tile
+    assert qmm.qmm_mmq_tile(512, 12288, 4096) == T128
+    assert qmm.qmm_mmq_tile(512, 4096, 12288) == T128
+    # 256 tokens: too few 128 x 64 tiles; the split over K halves each wave's walk
+    assert qmm.qmm_mmq_tile(256, 4096, 4096) == TSPLIT
+    assert qmm.qmm_mmq_tile(256, 12288, 4096) == TSPLIT
+    assert qmm.qmm_mmq_tile(9, 65, 512) == TSPLIT
+    # one super-block: splitting K gains nothing; many tiles: the big tile
+    assert qmm.qmm_mmq_tile(33, 131072, 256) == T128
+    with pytest.raises(qmm.QmmError):
+        qmm.qmm_mmq_tile(9, 65, 300)

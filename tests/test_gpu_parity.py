@@ -135,6 +135,31 @@ def test_matmul_parity(qtype, nt, od, idim):
             assert_close(o2.cpu().numpy(), ref, mag, qtype, idim, f"kind {kind}")
 
 
+TILE_CASES = [(qt, nt, od, idim) for qt in (Q4, Q6)
+              for nt, od, idim in ((9, 65, 256), (40, 130, 768), (100, 257, 2304), (64, 128, 512), (70, 33, 4608))]
+
+
+@pytest.mark.parametrize("qtype,nt,od,idim", TILE_CASES)
+def test_mmq_every_tile_shape(qtype, nt, od, idim):
+    """Each MMQ tile shape, forced, on ragged tiles and odd super-block counts (1,
+    3, 9, 2, 18: the split over K then has a group with nothing left to add)."""
+    _say(f"mmq tiles type={qtype} nt={nt} od={od} id={idim}")
+    W = synth.weights(qtype, od, idim, seed=3000 + nt)
+    x = synth.activations(nt, idim, seed=4000 + od, outlier_frac=0.01)
+    rq, rd, rs = oracle.quantize(x)
+    ref, mag = oracle.matmul_q8(qtype, W, rq, rd, rs, od)
+    args = (_up(W), _up(rq), _up(rd), _up(rs), od)
+    for kind in (qmm.QMM_KIND_MMQ_128X64, qmm.QMM_KIND_MMQ_64X64, qmm.QMM_KIND_MMQ_64X64_SPLITK):
+        o = qmm.qmm_matmul_q8_kind(kind, qtype, *args)
+        torch.cuda.synchronize()
+        assert_close(o.cpu().numpy(), ref, mag, qtype, idim, f"kind {kind}")
+    # the split adds its partial sums in a fixed order: the same bits every run
+    o1 = qmm.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_64X64_SPLITK, qtype, *args)
+    o2 = qmm.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_64X64_SPLITK, qtype, *args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+
+
 def test_dispatch_boundary():
     """nt = 8 runs MMVQ and nt = 9 runs MMQ; both match the oracle."""
     assert qmm.qmm_dispatch_kind(Q4, 8, 64, 512) == qmm.QMM_KIND_MMVQ
