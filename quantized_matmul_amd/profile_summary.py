@@ -4,6 +4,9 @@
       Per (kernel, grid): dispatch count, mean / median / min / max duration.  With
       --bench, the bench line's per-call kernel times are listed beside the trace.
 
+  python -m quantized_matmul_amd.profile_summary counters DB... --cmd "..." [--cmd "..."] --out FILE
+      Every counter of every library kernel in the databases (mean per dispatch).
+
   python -m quantized_matmul_amd.profile_summary pmc FETCH_DB WRITE_DB --cmd-fetch "..."
       --cmd-write "..." --copy-bytes N --out FILE
       Per (kernel, grid): mean FETCH_SIZE and WRITE_SIZE (KiB per dispatch).  The two
@@ -166,6 +169,42 @@ def cmd_pmc(a):
     print("\n".join(lines))
 
 
+def counter_means(db: str):
+    """{(short kernel, grid): {counter: mean per dispatch}} over all dispatches of a
+    rocpd database (a counter's instances summed within each dispatch)."""
+    con = sqlite3.connect(db)
+    rows = list(con.execute(
+        "select dispatch_id, kernel_name, grid_size, counter_name, sum(value) from counters_collection "
+        "group by dispatch_id, counter_name"))
+    con.close()
+    acc = {}
+    for _, name, grid, counter, v in rows:
+        acc.setdefault((short_name(name), grid), {}).setdefault(counter, []).append(v)
+    return {k: {c: statistics.fmean(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def cmd_counters(a):
+    merged = {}
+    for db in a.dbs:
+        for k, cs in counter_means(db).items():
+            merged.setdefault(k, {}).update(cs)
+    keys = [k for k in merged if any(k[0].startswith(p) for p in KERNEL_SOURCES)]
+    keys.sort(key=lambda k: (k[0], -k[1]))
+    counters = sorted({c for k in keys for c in merged[k]})
+    lines = [f"# rocprofv3 counters: {a.title}", "", "Commands (from the repository root):", "", "```"] + a.cmd + \
+            ["```", "", "Mean per dispatch (each counter's instances summed over the chip).", "",
+             "| kernel | grid (threads) | " + " | ".join(counters) + " |",
+             "|---|---|" + "---|" * len(counters)]
+    for k in keys:
+        lines.append(f"| `{k[0]}` | {k[1]} | " + " | ".join(f"{merged[k].get(c, float('nan')):.4g}" for c in counters)
+                     + " |")
+    if a.notes:
+        lines += ["", a.notes]
+    with open(a.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 _TRAFFIC = re.compile(r"traffic: kernel=(\S+) grid=(\d+) bytes_per_launch=(\d+) sources_sha256=([0-9a-f]+)")
 
 
@@ -202,8 +241,14 @@ def main():
     p.add_argument("--copy-bytes", type=int, required=True)
     p.add_argument("--title", default="")
     p.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dbs", nargs="+")
+    c.add_argument("--cmd", action="append", required=True)
+    c.add_argument("--title", default="")
+    c.add_argument("--notes", default="")
+    c.add_argument("--out", required=True)
     a = ap.parse_args()
-    cmd_trace(a) if a.what == "trace" else cmd_pmc(a)
+    {"trace": cmd_trace, "pmc": cmd_pmc, "counters": cmd_counters}[a.what](a)
 
 
 if __name__ == "__main__":
