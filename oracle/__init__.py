@@ -46,10 +46,15 @@ def _bind(path: str):
     L.oracle_matmul_q8_points.argtypes = [I, P, P, P, P, I, I, I, I, P, P, P, P]
     L.oracle_matmul.argtypes = [I, P, P, I, I, I, P, P, P, P, P]
     L.oracle_decode_block.argtypes = [I, P, P, P, P, P, P]
+    F = ctypes.c_float
+    L.oracle_rmsnorm.argtypes = [P, P, F, I, I, P]
+    L.oracle_add_rmsnorm.argtypes = [P, P, P, F, I, I, P, P]
+    L.oracle_silu_mul.argtypes = [P, P, ctypes.c_size_t, P]
     L.oracle_num_threads.restype = I
     L.oracle_set_num_threads.argtypes = [I]
     for f in ("oracle_quantize", "oracle_subblock_dots", "oracle_matmul_q8",
-              "oracle_matmul_q8_points", "oracle_matmul", "oracle_decode_block"):
+              "oracle_matmul_q8_points", "oracle_matmul", "oracle_decode_block",
+              "oracle_rmsnorm", "oracle_add_rmsnorm", "oracle_silu_mul"):
         getattr(L, f).restype = I
     return L
 
@@ -179,6 +184,41 @@ def decode_block(qtype: int, block: np.ndarray):
     if qtype == TYPE_Q4_K:
         return dict(d=float(d[0]), dmin=float(dmin[0]), sc=sc[:8].copy(), m=m[:8].copy(), codes=codes)
     return dict(d=float(d[0]), sc=sc.copy(), codes=codes)
+
+
+def rmsnorm(x: np.ndarray, w: np.ndarray, eps: float):
+    """y = (x * r) * w per row, r = 1 / sqrt(mean(x^2) + eps) in the fixed f32 order."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    nt, idim = x.shape
+    assert w.shape == (idim,)
+    y = np.empty_like(x)
+    _check(lib().oracle_rmsnorm(_p(x), _p(w), float(eps), nt, idim, _p(y)), "oracle_rmsnorm")
+    return y
+
+
+def add_rmsnorm(h: np.ndarray, o: np.ndarray, w: np.ndarray, eps: float):
+    """Returns (h + o, rmsnorm(h + o))."""
+    h = np.ascontiguousarray(h, dtype=np.float32)
+    o = np.ascontiguousarray(o, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    nt, idim = h.shape
+    assert o.shape == h.shape and w.shape == (idim,)
+    hn = np.empty_like(h)
+    y = np.empty_like(h)
+    _check(lib().oracle_add_rmsnorm(_p(h), _p(o), _p(w), float(eps), nt, idim, _p(hn), _p(y)),
+           "oracle_add_rmsnorm")
+    return hn, y
+
+
+def silu_mul(g: np.ndarray, u: np.ndarray):
+    """silu(g) * u elementwise (f64 evaluation, one rounding to f32)."""
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    u = np.ascontiguousarray(u, dtype=np.float32)
+    assert g.shape == u.shape
+    y = np.empty_like(g)
+    _check(lib().oracle_silu_mul(_p(g), _p(u), g.size, _p(y)), "oracle_silu_mul")
+    return y
 
 
 def num_threads() -> int:

@@ -25,12 +25,22 @@
  *   R3  All-zero block (d == 0): q = 0, s = 0.
  *   R4  s = d * (float)sum(q), one f32 multiply, round to nearest even.
  *   R5  Q6_K group scales are signed int8; Q6_K d sits in the last two bytes.
+ *   R17 RMS norm in f32 with one fixed order (the pages fix neither formula nor
+ *       order, only that the fused and unfused kernels agree bit for bit): 256
+ *       lane partials, lane t taking the values i with (i / 4) mod 256 == t in
+ *       increasing i, each by one fused multiply-add of the square; the partials
+ *       combined by halving (stride 128, 64, ..., 1); r = 1 / sqrtf(ss / n + eps);
+ *       y = (x * r) * w.  See oracle_rmsnorm.
+ *   R18 silu(g) * u evaluated in f64 as (g / (1 + exp(-g))) * u and rounded once
+ *       to f32 (the value the quantizer then reads).
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp (no -ffast-math, no -march).
  *
  * OQ_MUTATE (default 0) plants one known mistake, for the tests that show the
  * pins catch it: 1 swapped nibble halves, 2 Q6_K offset 32 dropped, 3 Q4_K min
- * term dropped, 4 scale and min swapped, 5 Q6_K scale per 32 instead of per 16.
+ * term dropped, 4 scale and min swapped, 5 Q6_K scale per 32 instead of per 16,
+ * 6 RMS mean over n - 1, 7 eps added after the square root, 8 squares summed in
+ * one running sum, 9 silu with exp(+g).
  */
 #ifndef OQ_MUTATE
 #define OQ_MUTATE 0
@@ -194,6 +204,101 @@ int oracle_quantize(const float* x, int nt, int id, int8_t* q, float* d, float* 
             d[(size_t)t * nblk + k] = dk;
             s[(size_t)t * nblk + k] = dk * (float)sum;
         }
+    }
+    return 0;
+}
+
+/* ---- O6. Producer-side elementwise steps that feed the quantizer -----------
+ * [GEMM, "The GPU path", "Fused elementwise kernels"]: each RMS norm and the FFN
+ * activation ends in the quantizer; one step adds the projection output into the
+ * residual stream and normalizes the sum, one normalizes without the add (first
+ * layer), one forms silu(g) * u.  These functions produce the f32 values that
+ * oracle_quantize then quantizes; the fused products are checked as
+ * oracle_quantize(oracle_rmsnorm(...)) and so on.
+ *
+ * Reading R17 (sum order).  The norm's f32 result depends on the order in which
+ * the squares are added, and the quantized codes depend on its last bit, so the
+ * order is part of the operation: lane t (0..255) accumulates, in increasing i,
+ * fma(x_i, x_i, p_t) over the i whose group of four, i / 4, is congruent to t
+ * modulo 256; the lanes are then combined by halving, p_t += p_{t+s} for
+ * s = 128, 64, ..., 1, and ss = p_0. */
+static float rms_sum_squares(const float* x, int n)
+{
+    float p[256];
+    for (int t = 0; t < 256; ++t)
+        p[t] = 0.0f;
+#if OQ_MUTATE == 8
+    for (int i = 0; i < n; ++i)
+        p[0] = fmaf(x[i], x[i], p[0]);
+#else
+    for (int i = 0; i < n; ++i) {
+        int t = (i / 4) % 256;
+        p[t] = fmaf(x[i], x[i], p[t]);
+    }
+#endif
+    for (int stride = 128; stride >= 1; stride /= 2)
+        for (int t = 0; t < stride; ++t)
+            p[t] = p[t] + p[t + stride];
+    return p[0];
+}
+
+/* r = 1 / sqrt(mean(x^2) + eps), three correctly rounded f32 operations. */
+static float rms_scale(float ss, int n, float eps)
+{
+#if OQ_MUTATE == 6
+    float mean = ss / (float)(n - 1);
+#else
+    float mean = ss / (float)n;
+#endif
+#if OQ_MUTATE == 7
+    return 1.0f / (sqrtf(mean) + eps);
+#else
+    return 1.0f / sqrtf(mean + eps);
+#endif
+}
+
+/* y[t][i] = (x[t][i] * r_t) * w[i] with r_t from row t (reading R17). */
+int oracle_rmsnorm(const float* x, const float* w, float eps, int nt, int id, float* y)
+{
+    if (!x || !w || !y || nt < 0 || id < 1 || !(eps >= 0.0f))
+        return -1;
+    for (int t = 0; t < nt; ++t) {
+        const float* xr = x + (size_t)t * id;
+        float* yr = y + (size_t)t * id;
+        float r = rms_scale(rms_sum_squares(xr, id), id, eps);
+        for (int i = 0; i < id; ++i)
+            yr[i] = (xr[i] * r) * w[i];
+    }
+    return 0;
+}
+
+/* The residual update h_new = h + o (one f32 add per element), written to h_new,
+ * then y = rmsnorm(h_new) as above. */
+int oracle_add_rmsnorm(const float* h, const float* o, const float* w, float eps, int nt, int id,
+                       float* h_new, float* y)
+{
+    if (!h || !o || !h_new)
+        return -1;
+    for (size_t i = 0; i < (size_t)nt * (size_t)(id > 0 ? id : 0); ++i)
+        h_new[i] = h[i] + o[i];
+    return oracle_rmsnorm(h_new, w, eps, nt, id, y);
+}
+
+/* y = silu(g) * u, silu(g) = g / (1 + e^-g) = g * sigmoid(g); reading R18: every
+ * operation in f64 in that order, one rounding to f32 at the end. */
+int oracle_silu_mul(const float* g, const float* u, size_t n, float* y)
+{
+    if (!g || !u || !y)
+        return -1;
+    for (size_t i = 0; i < n; ++i) {
+        double gd = (double)g[i];
+#if OQ_MUTATE == 9
+        double e = exp(gd);
+#else
+        double e = exp(-gd);
+#endif
+        double sg = gd / (1.0 + e);
+        y[i] = (float)(sg * (double)u[i]);
     }
     return 0;
 }
