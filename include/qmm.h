@@ -136,6 +136,54 @@ int qmm_dispatch_kind(int type, int nt, int od, int id);
  * clamped to 0..8, read once). */
 int qmm_nt_switch(void);
 
+/* ---- Producer-side steps fused with the quantizer ---------------------------
+ * [GEMM, "The GPU path", "Fused elementwise kernels"]: each RMS norm and the FFN
+ * activation ends in the quantizer; fusing them removes the HBM write and re-read
+ * of the f32 rows.  The fused calls give bit for bit what the unfused chain gives
+ * (the same float expressions in the same order, the same quantizer code):
+ *   qmm_add_rmsnorm_quantize  = qmm_residual_add, qmm_rmsnorm, qmm_quantize_act
+ *   qmm_rmsnorm_quantize      = qmm_rmsnorm, qmm_quantize_act
+ *   qmm_silu_mul_quantize     = qmm_silu_mul, qmm_quantize_act
+ * One quantized activation serves every projection that reads it (q, k, v from
+ * one norm; gate and up from another) through qmm_matmul_q8.
+ *
+ * Arithmetic (the pages fix only that fused equals unfused):
+ *   RMS norm, f32: lane partials p_t (t = 0..255) accumulate fma(x_i, x_i, p_t) in
+ *   increasing i over the i with (i / 4) mod 256 == t; they are combined by halving,
+ *   p_t += p_{t+s} for s = 128, 64, ..., 1, giving ss; r = 1 / sqrtf(ss / id + eps);
+ *   y_i = (x_i * r) * w_i.
+ *   silu(g) * u: (g / (1 + exp(-g))) * u evaluated in f64, rounded once to f32.
+ *
+ * Common rules: rows are [nt][id] f32, id % 32 == 0 (id >= 32); q [nt][id] int8,
+ * d and s [nt][id/32] f32 as from qmm_quantize_act; w [id] f32; every pointer a
+ * device pointer owned by the caller, 16-byte aligned (QMM_ERR_ALIGN), non-null
+ * (QMM_ERR_ARG); nt < 1: QMM_ERR_ARG; id not a positive multiple of 32, or
+ * nt * id >= 2^31: QMM_ERR_SHAPE; eps negative, infinite or NaN: QMM_ERR_ARG.
+ * eps = 0 with an all-zero row is outside the domain (0 * infinity).  Inputs
+ * must be finite and the results finite.  Asynchronous on `stream`. */
+
+/* h <- h + o (the residual stream, updated in place), then the RMS norm of the
+ * new h times w, quantized into q, d, s.  o may equal h. */
+int qmm_add_rmsnorm_quantize(float* h, const float* o, const float* w, float eps, int nt, int id,
+                             int8_t* q, float* d, float* s, void* stream);
+
+/* The RMS norm of x times w, quantized into q, d, s (a layer whose input needs
+ * no residual add). */
+int qmm_rmsnorm_quantize(const float* x, const float* w, float eps, int nt, int id, int8_t* q,
+                         float* d, float* s, void* stream);
+
+/* silu(g) * u, elementwise over [nt][id], quantized into q, d, s. */
+int qmm_silu_mul_quantize(const float* g, const float* u, int nt, int id, int8_t* q, float* d,
+                          float* s, void* stream);
+
+/* Unfused steps (f32 out), the chain the fused calls are equal to. */
+/* h <- h + o over [nt][id] (id % 32 == 0 as above). */
+int qmm_residual_add(float* h, const float* o, int nt, int id, void* stream);
+/* y = RMS norm of x times w; y may equal x. */
+int qmm_rmsnorm(const float* x, const float* w, float eps, int nt, int id, float* y, void* stream);
+/* y = silu(g) * u. */
+int qmm_silu_mul(const float* g, const float* u, int nt, int id, float* y, void* stream);
+
 /* Diagnostic: the integer stage of a kernel alone.  [GEMM, "The GPU path"]: each
  * scale group (32 weights for Q4_K, 16 for Q6_K) is reduced as an integer dot
  * with its activation codes.  Writes S[t][r][b][g] = sum over group g of super-

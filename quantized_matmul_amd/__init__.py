@@ -40,7 +40,8 @@ BLOCK_BYTES = {QMM_TYPE_Q4_K: 144, QMM_TYPE_Q6_K: 210}
 
 EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8",
            "qmm_matmul_q8_kind", "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots",
-           "qmm_mfma_tile_check", "qmm_strerror")
+           "qmm_mfma_tile_check", "qmm_strerror", "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize",
+           "qmm_silu_mul_quantize", "qmm_residual_add", "qmm_rmsnorm", "qmm_silu_mul")
 
 
 class QmmError(RuntimeError):
@@ -74,10 +75,19 @@ def lib():
         L.qmm_nt_switch.argtypes = []
         L.qmm_group_dots.argtypes = [I, I, P, P, I, I, I, P, P]
         L.qmm_mfma_tile_check.argtypes = [I, P, P, P, P]
+        F = ctypes.c_float
+        L.qmm_add_rmsnorm_quantize.argtypes = [P, P, P, F, I, I, P, P, P, P]
+        L.qmm_rmsnorm_quantize.argtypes = [P, P, F, I, I, P, P, P, P]
+        L.qmm_silu_mul_quantize.argtypes = [P, P, I, I, P, P, P, P]
+        L.qmm_residual_add.argtypes = [P, P, I, I, P]
+        L.qmm_rmsnorm.argtypes = [P, P, F, I, I, P, P]
+        L.qmm_silu_mul.argtypes = [P, P, I, I, P, P]
         L.qmm_strerror.argtypes = [I]
         L.qmm_strerror.restype = ctypes.c_char_p
         for f in ("qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8", "qmm_matmul_q8_kind",
-                  "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots", "qmm_mfma_tile_check"):
+                  "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots", "qmm_mfma_tile_check",
+                  "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize", "qmm_silu_mul_quantize", "qmm_residual_add",
+                  "qmm_rmsnorm", "qmm_silu_mul"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -152,6 +162,93 @@ def qmm_quantize_act(x: torch.Tensor, q=None, d=None, s=None, stream=None):
                                   _dev(d, torch.float32, "d"), _dev(s, torch.float32, "s"), _stream(stream)),
            "qmm_quantize_act")
     return q, d, s
+
+
+def _q8_out(x: torch.Tensor, q, d, s):
+    nt, idim = x.shape
+    if q is None:
+        q = torch.empty((nt, idim), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((nt, idim // 32), dtype=torch.float32, device=x.device)
+    if s is None:
+        s = torch.empty((nt, idim // 32), dtype=torch.float32, device=x.device)
+    return q, d, s
+
+
+def _weight_vec(w: torch.Tensor, idim: int):
+    if w.dim() != 1 or w.numel() != idim:
+        raise ValueError(f"w must have shape [{idim}]")
+
+
+def qmm_add_rmsnorm_quantize(h: torch.Tensor, o: torch.Tensor, w: torch.Tensor, eps: float, q=None, d=None,
+                             s=None, stream=None):
+    """h <- h + o in place, then quantize rmsnorm(h) * w: returns (q, d, s)."""
+    nt, idim = h.shape
+    if o.shape != h.shape:
+        raise ValueError("o must have the shape of h")
+    _weight_vec(w, idim)
+    q, d, s = _q8_out(h, q, d, s)
+    _check(lib().qmm_add_rmsnorm_quantize(_dev(h, torch.float32, "h"), _dev(o, torch.float32, "o"),
+                                          _dev(w, torch.float32, "w"), float(eps), nt, idim,
+                                          _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
+                                          _dev(s, torch.float32, "s"), _stream(stream)), "qmm_add_rmsnorm_quantize")
+    return q, d, s
+
+
+def qmm_rmsnorm_quantize(x: torch.Tensor, w: torch.Tensor, eps: float, q=None, d=None, s=None, stream=None):
+    """Quantize rmsnorm(x) * w: returns (q, d, s)."""
+    nt, idim = x.shape
+    _weight_vec(w, idim)
+    q, d, s = _q8_out(x, q, d, s)
+    _check(lib().qmm_rmsnorm_quantize(_dev(x, torch.float32, "x"), _dev(w, torch.float32, "w"), float(eps), nt,
+                                      idim, _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
+                                      _dev(s, torch.float32, "s"), _stream(stream)), "qmm_rmsnorm_quantize")
+    return q, d, s
+
+
+def qmm_silu_mul_quantize(g: torch.Tensor, u: torch.Tensor, q=None, d=None, s=None, stream=None):
+    """Quantize silu(g) * u: returns (q, d, s)."""
+    nt, idim = g.shape
+    if u.shape != g.shape:
+        raise ValueError("u must have the shape of g")
+    q, d, s = _q8_out(g, q, d, s)
+    _check(lib().qmm_silu_mul_quantize(_dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), nt, idim,
+                                       _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
+                                       _dev(s, torch.float32, "s"), _stream(stream)), "qmm_silu_mul_quantize")
+    return q, d, s
+
+
+def qmm_residual_add(h: torch.Tensor, o: torch.Tensor, stream=None) -> torch.Tensor:
+    """h <- h + o in place; returns h."""
+    nt, idim = h.shape
+    if o.shape != h.shape:
+        raise ValueError("o must have the shape of h")
+    _check(lib().qmm_residual_add(_dev(h, torch.float32, "h"), _dev(o, torch.float32, "o"), nt, idim,
+                                  _stream(stream)), "qmm_residual_add")
+    return h
+
+
+def qmm_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float, y=None, stream=None) -> torch.Tensor:
+    """y = rmsnorm(x) * w (f32); y may be x."""
+    nt, idim = x.shape
+    _weight_vec(w, idim)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(lib().qmm_rmsnorm(_dev(x, torch.float32, "x"), _dev(w, torch.float32, "w"), float(eps), nt, idim,
+                             _dev(y, torch.float32, "y"), _stream(stream)), "qmm_rmsnorm")
+    return y
+
+
+def qmm_silu_mul(g: torch.Tensor, u: torch.Tensor, y=None, stream=None) -> torch.Tensor:
+    """y = silu(g) * u (f32)."""
+    nt, idim = g.shape
+    if u.shape != g.shape:
+        raise ValueError("u must have the shape of g")
+    if y is None:
+        y = torch.empty_like(g)
+    _check(lib().qmm_silu_mul(_dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), nt, idim,
+                              _dev(y, torch.float32, "y"), _stream(stream)), "qmm_silu_mul")
+    return y
 
 
 def qmm_matmul(qtype: int, W: torch.Tensor, x: torch.Tensor, od: int, out=None, workspace=None, stream=None):

@@ -8,6 +8,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <initializer_list>
+
 #include "qmm.h"
 #include "qmm_internal.h"
 
@@ -101,6 +103,26 @@ int validate_q8(int type, const void* W, const int8_t* q, const float* d, const 
     return QMM_OK;
 }
 
+// Shape and argument rules shared by the producer-side steps.
+int check_rows(int nt, int id)
+{
+    if (nt < 1)
+        return QMM_ERR_ARG;
+    if (id < 32 || id % 32 || (long long)nt * id > 0x7FFFFFFFLL)
+        return QMM_ERR_SHAPE;
+    return QMM_OK;
+}
+
+bool eps_ok(float eps) { return eps >= 0.0f && eps <= 3.4028234663852886e38f; }  // rejects NaN, inf
+
+bool all_aligned(std::initializer_list<const void*> ps)
+{
+    for (const void* p : ps)
+        if (!aligned16(p))
+            return false;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -132,6 +154,97 @@ int qmm_quantize_act(const float* x, int nt, int id, int8_t* q, float* d, float*
     if (rc)
         return rc;
     return launched(qmm::launch_quantize(x, nt, id, q, d, s, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qmm_add_rmsnorm_quantize(float* h, const float* o, const float* w, float eps, int nt, int id, int8_t* q,
+                             float* d, float* s, void* stream)
+{
+    if (!h || !o || !w || !q || !d || !s || !eps_ok(eps))
+        return QMM_ERR_ARG;
+    int rc = check_rows(nt, id);
+    if (rc)
+        return rc;
+    if (!all_aligned({h, o, w, q, d, s}))
+        return QMM_ERR_ALIGN;
+    if ((rc = check_device()))
+        return rc;
+    return launched(qmm::launch_rmsnorm(h, o, h, w, eps, nt, id, q, d, s, nullptr,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qmm_rmsnorm_quantize(const float* x, const float* w, float eps, int nt, int id, int8_t* q, float* d, float* s,
+                         void* stream)
+{
+    if (!x || !w || !q || !d || !s || !eps_ok(eps))
+        return QMM_ERR_ARG;
+    int rc = check_rows(nt, id);
+    if (rc)
+        return rc;
+    if (!all_aligned({x, w, q, d, s}))
+        return QMM_ERR_ALIGN;
+    if ((rc = check_device()))
+        return rc;
+    return launched(qmm::launch_rmsnorm(x, nullptr, nullptr, w, eps, nt, id, q, d, s, nullptr,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qmm_silu_mul_quantize(const float* g, const float* u, int nt, int id, int8_t* q, float* d, float* s,
+                          void* stream)
+{
+    if (!g || !u || !q || !d || !s)
+        return QMM_ERR_ARG;
+    int rc = check_rows(nt, id);
+    if (rc)
+        return rc;
+    if (!all_aligned({g, u, q, d, s}))
+        return QMM_ERR_ALIGN;
+    if ((rc = check_device()))
+        return rc;
+    return launched(qmm::launch_silu_mul(g, u, nt, id, q, d, s, nullptr, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qmm_residual_add(float* h, const float* o, int nt, int id, void* stream)
+{
+    if (!h || !o)
+        return QMM_ERR_ARG;
+    int rc = check_rows(nt, id);
+    if (rc)
+        return rc;
+    if (!all_aligned({h, o}))
+        return QMM_ERR_ALIGN;
+    if ((rc = check_device()))
+        return rc;
+    return launched(qmm::launch_residual_add(h, o, (long)nt * id, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qmm_rmsnorm(const float* x, const float* w, float eps, int nt, int id, float* y, void* stream)
+{
+    if (!x || !w || !y || !eps_ok(eps))
+        return QMM_ERR_ARG;
+    int rc = check_rows(nt, id);
+    if (rc)
+        return rc;
+    if (!all_aligned({x, w, y}))
+        return QMM_ERR_ALIGN;
+    if ((rc = check_device()))
+        return rc;
+    return launched(qmm::launch_rmsnorm(x, nullptr, nullptr, w, eps, nt, id, nullptr, nullptr, nullptr, y,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qmm_silu_mul(const float* g, const float* u, int nt, int id, float* y, void* stream)
+{
+    if (!g || !u || !y)
+        return QMM_ERR_ARG;
+    int rc = check_rows(nt, id);
+    if (rc)
+        return rc;
+    if (!all_aligned({g, u, y}))
+        return QMM_ERR_ALIGN;
+    if ((rc = check_device()))
+        return rc;
+    return launched(qmm::launch_silu_mul(g, u, nt, id, nullptr, nullptr, nullptr, y,
+                                         reinterpret_cast<hipStream_t>(stream)));
 }
 
 int qmm_nt_switch(void) { return nt_switch_value(); }

@@ -29,6 +29,15 @@ hipError_t launch_mmvq(int type, const uint8_t* W, const int8_t* q, const float*
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
                       int nt, int od, int id, float* out, int32_t* S, hipStream_t st, int tile = 0);
 int mmq_tile_choice(int nt, int od, int id);
+
+// Producer-side steps that feed the quantizer (qmm_fused.hip).  Rows are [nt][id]
+// f32, id % 32 == 0; q/d/s as for launch_quantize.  With q == null the kernels
+// store the f32 values y instead of quantizing them (the unfused chain's steps).
+hipError_t launch_rmsnorm(const float* x, const float* o, float* h, const float* w, float eps, int nt,
+                          int id, int8_t* q, float* d, float* s, float* y, hipStream_t st);
+hipError_t launch_residual_add(float* h, const float* o, long n, hipStream_t st);
+hipError_t launch_silu_mul(const float* g, const float* u, int nt, int id, int8_t* q, float* d, float* s,
+                           float* y, hipStream_t st);
 hipError_t launch_mfma_tile_probe(int kind, const void* A, const void* B, void* C, hipStream_t st);
 
 // ---------------------------------------------------------------- device helpers
@@ -48,6 +57,41 @@ __device__ __forceinline__ int dpp_quad_xor2(int v) { return __builtin_amdgcn_up
 __device__ __forceinline__ int dpp_half_mirror(int v) { return __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false); }
 
 __device__ __forceinline__ int sdot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
+
+// One lane's share of the activation quantizer.  Eight consecutive lanes (an
+// aligned group of eight) hold one 32-value block, four consecutive values each,
+// and all eight must make the call together.  [GEMM, "The GPU path",
+// "Activations get one scale per 32"]: d = amax / 127 (IEEE division), codes
+// round(v / d) half away from zero, s = d * (float)sum(q); a zero block gives
+// d = q = s = 0.  Returns the four codes packed low byte first; every lane gets
+// the block's d and s.  The plain quantizer and the producer-fused kernels both
+// quantize through this function, so a fused result equals the plain quantizer
+// applied to the same f32 values.
+__device__ __forceinline__ uint32_t quantize_lane4(float4 v, float& dk, float& sk)
+{
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    int ai = __builtin_bit_cast(int, a);  // non-negative floats order like their bits
+    ai = max(ai, dpp_quad_xor1(ai));
+    ai = max(ai, dpp_quad_xor2(ai));
+    ai = max(ai, dpp_half_mirror(ai));
+    const float amax = __builtin_bit_cast(float, ai);
+
+    dk = amax / 127.0f;
+    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+    if (dk != 0.0f) {
+        q0 = (int)roundf(v.x / dk);
+        q1 = (int)roundf(v.y / dk);
+        q2 = (int)roundf(v.z / dk);
+        q3 = (int)roundf(v.w / dk);
+    }
+    int sum = q0 + q1 + q2 + q3;
+    sum += dpp_quad_xor1(sum);
+    sum += dpp_quad_xor2(sum);
+    sum += dpp_half_mirror(sum);
+    sk = dk * (float)sum;
+    return (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
+           ((uint32_t)(q3 & 0xFF) << 24);
+}
 
 // Q4_K (scale, min) of sub-block j from header dwords h1 = bytes 4..7, h2 = 8..11,
 // h3 = 12..15.  [MMQ, section 6, get_scale_min_k4 semantics]: j < 4 takes the low

@@ -11,8 +11,9 @@
 //
 // wave64 mapping: each lane loads 16 bytes (four values), eight lanes hold one
 // block, a wave covers eight blocks = 1 KiB of input.  The eight-lane max and sum
-// use DPP (two quad permutes and a half-row mirror) -- no LDS.  Each lane stores
-// its four codes as one dword; the first lane of each block stores d and s.
+// (quantize_lane4) use DPP (two quad permutes and a half-row mirror) -- no LDS.
+// Each lane stores its four codes as one dword; the first lane of each block
+// stores d and s.
 #include "qmm_internal.h"
 
 namespace qmm {
@@ -29,32 +30,13 @@ __global__ __launch_bounds__(256) void quantize_q8_kernel(const float4* __restri
     if (valid)
         v = x[g];
 
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    int ai = __builtin_bit_cast(int, a);  // non-negative floats order like their bits
-    ai = max(ai, dpp_quad_xor1(ai));
-    ai = max(ai, dpp_quad_xor2(ai));
-    ai = max(ai, dpp_half_mirror(ai));
-    const float amax = __builtin_bit_cast(float, ai);
-
-    const float dk = amax / 127.0f;
-    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-    if (dk != 0.0f) {
-        q0 = (int)roundf(v.x / dk);
-        q1 = (int)roundf(v.y / dk);
-        q2 = (int)roundf(v.z / dk);
-        q3 = (int)roundf(v.w / dk);
-    }
-    int sum = q0 + q1 + q2 + q3;
-    sum += dpp_quad_xor1(sum);
-    sum += dpp_quad_xor2(sum);
-    sum += dpp_half_mirror(sum);
-
+    float dk, sk;
+    const uint32_t codes = quantize_lane4(v, dk, sk);
     if (valid) {
-        q[g] = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
-               ((uint32_t)(q3 & 0xFF) << 24);
+        q[g] = codes;
         if ((threadIdx.x & 7) == 0) {
             d[blk] = dk;
-            s[blk] = dk * (float)sum;
+            s[blk] = sk;
         }
     }
 }

@@ -89,6 +89,38 @@ def test_validation_before_device_work():
     assert L.qmm_matmul(1, p, p, 1 << 20, 4, 4096, p, p, big, None) == qmm.QMM_ERR_SHAPE
 
 
+def test_fused_steps_validation_before_device_work():
+    L = qmm.lib()
+    p = ctypes.c_void_p(1 << 20)
+    mis = ctypes.c_void_p((1 << 20) + 8)
+    E = 1e-5
+    A, S, AL, D = qmm.QMM_ERR_ARG, qmm.QMM_ERR_SHAPE, qmm.QMM_ERR_ALIGN, qmm.QMM_ERR_DEVICE
+    assert L.qmm_add_rmsnorm_quantize(None, p, p, E, 1, 64, p, p, p, None) == A
+    assert L.qmm_add_rmsnorm_quantize(p, p, p, -1.0, 1, 64, p, p, p, None) == A
+    assert L.qmm_add_rmsnorm_quantize(p, p, p, float("nan"), 1, 64, p, p, p, None) == A
+    assert L.qmm_add_rmsnorm_quantize(p, p, p, float("inf"), 1, 64, p, p, p, None) == A
+    assert L.qmm_add_rmsnorm_quantize(p, p, p, E, 0, 64, p, p, p, None) == A
+    assert L.qmm_add_rmsnorm_quantize(p, p, p, E, 1, 48, p, p, p, None) == S
+    assert L.qmm_add_rmsnorm_quantize(p, mis, p, E, 1, 64, p, p, p, None) == AL
+    assert L.qmm_rmsnorm_quantize(p, p, E, 1, 0, p, p, p, None) == S
+    assert L.qmm_rmsnorm_quantize(p, p, E, 1 << 16, 1 << 15, p, p, p, None) == S
+    assert L.qmm_rmsnorm_quantize(p, p, E, 1, 64, p, mis, p, None) == AL
+    assert L.qmm_silu_mul_quantize(p, None, 1, 64, p, p, p, None) == A
+    assert L.qmm_silu_mul_quantize(p, p, 1, 16, p, p, p, None) == S
+    assert L.qmm_residual_add(p, p, 0, 64, None) == A
+    assert L.qmm_rmsnorm(p, p, E, 1, 64, mis, None) == AL
+    assert L.qmm_silu_mul(p, p, 1, 100, p, None) == S
+    # valid arguments reach the device check; eps = 0 is allowed
+    import torch
+    if not torch.cuda.is_available():
+        assert L.qmm_add_rmsnorm_quantize(p, p, p, 0.0, 1, 64, p, p, p, None) == D
+        assert L.qmm_rmsnorm_quantize(p, p, E, 3, 32, p, p, p, None) == D
+        assert L.qmm_silu_mul_quantize(p, p, 1, 64, p, p, p, None) == D
+        assert L.qmm_residual_add(p, p, 1, 64, None) == D
+        assert L.qmm_rmsnorm(p, p, E, 1, 64, p, None) == D
+        assert L.qmm_silu_mul(p, p, 1, 64, p, None) == D
+
+
 def test_no_device_is_an_error_not_a_fallback():
     import torch
     if torch.cuda.is_available():
