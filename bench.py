@@ -29,8 +29,16 @@ the rocprofv3 FETCH_SIZE / WRITE_SIZE runs summarised in profiles/ (scaled by a
 plain copy of known size), or null when that summary is missing or was taken from
 kernel sources other than the ones built here.
 
+Workload "fused_quantize": the producer-side steps fused with the quantizer
+(residual add + RMS norm, RMS norm, silu(g) * u), each against its unfused chain
+(the f32 step, then the plain quantizer), at a decode row (nt = 1) and a prefill
+block (nt = 512) of an 8B model (hidden 4096; FFN 12288 for silu).  One step runs
+every fused call once and every chain once; inputs rotate over copies of more than
+1 GiB per shape.  value = HBM GB/s of the fused kernels at nt = 512 (algorithmic
+bytes over their summed launch times); roofline on silu_mul_quantize 512 x 12288.
+
 Options: --gpus N (1 only), --steps K, --warmup W, --workload
-{q4k_decode_prefill, q6k_head, dllm_step}, --no-cpu-baseline, --copy-calibration
+{q4k_decode_prefill, q6k_head, dllm_step, fused_quantize}, --no-cpu-baseline, --copy-calibration
 MIB (before warm-up, run five plain device copies of MIB MiB between two spin-kernel
 markers, for scaling the HBM counters of a profiled run).
 """
@@ -55,6 +63,7 @@ INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
 COPY_BYTES = 1 << 30           # weight copies per shape: at least 1 GiB
 CHUNK = 20                     # launches per event-timed chunk
 COUNTERS = os.path.join(ROOT, "profiles", "q4k_decode_prefill_hbm_counters.md")
+FUSED_COUNTERS = os.path.join(ROOT, "profiles", "fused_quantize_hbm_counters.md")
 
 
 def parse():
@@ -63,7 +72,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200, help="multiple of 20")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q4k_decode_prefill",
-                    choices=["q4k_decode_prefill", "q6k_head", "dllm_step"])
+                    choices=["q4k_decode_prefill", "q6k_head", "dllm_step", "fused_quantize"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     return ap.parse_args()
@@ -181,6 +190,192 @@ def build_calls(torch, qmm, workload):
     return calls
 
 
+class FusedCall:
+    """One producer-side step at one shape: the fused kernel and its unfused chain,
+    each with inputs rotating over copies of more than COPY_BYTES in total."""
+
+    EPS = 1e-5
+
+    def __init__(self, torch, qmm, op, nt, idim, seed):
+        self.op, self.nt, self.idim = op, nt, idim
+        self.label = f"{op} {nt}x{idim}"
+        dev = torch.device("cuda:0")
+        n = nt * idim
+        a = torch.from_numpy(synth.activations(nt, idim, seed=seed)).to(dev)
+        b = torch.from_numpy(synth.activations(nt, idim, seed=seed + 1)).to(dev) * 0.5
+        self.w = torch.from_numpy(1.0 + 0.25 * synth.activations(1, idim, seed=seed + 2)[0]).to(dev)
+        per_copy = 4 * n * (2 if op != "rmsnorm_quantize" else 1)
+        ncopy = min(256, max(2, -(-COPY_BYTES // per_copy)))  # decode rows: 256 small copies
+        self.a = [a] + [a.clone() for _ in range(ncopy - 1)]
+        self.b = [b] + [b.clone() for _ in range(ncopy - 1)] if op != "rmsnorm_quantize" else [None] * ncopy
+        self.y = torch.empty((nt, idim), dtype=torch.float32, device=dev)
+        self.q = torch.empty((nt, idim), dtype=torch.int8, device=dev)
+        self.d = torch.empty((nt, idim // 32), dtype=torch.float32, device=dev)
+        self.s = torch.empty((nt, idim // 32), dtype=torch.float32, device=dev)
+        # algorithmic HBM bytes per launch: inputs read, outputs written once
+        q8 = n * (1 + 8 / 32)
+        self.fbytes = {"add_rmsnorm_quantize": 12 * n + 4 * idim + q8,
+                       "rmsnorm_quantize": 4 * n + 4 * idim + q8,
+                       "silu_mul_quantize": 8 * n + q8}[op]
+        self.cbytes = {"add_rmsnorm_quantize": 12 * n + (8 * n + 4 * idim) + (4 * n + q8),
+                       "rmsnorm_quantize": (8 * n + 4 * idim) + (4 * n + q8),
+                       "silu_mul_quantize": 12 * n + (4 * n + q8)}[op]
+        self.f_ms, self.c_ms = [], []
+        self.i = 0
+        P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        st = P(torch.cuda.current_stream().cuda_stream)
+        L = self.L = qmm.lib()
+        ptr = lambda t: P(t.data_ptr())  # noqa: E731
+        q8a = (ptr(self.q), ptr(self.d), ptr(self.s), st)
+        W, y = ptr(self.w), ptr(self.y)
+        self.fused_calls, self.chain_calls = [], []
+        for k in range(ncopy):
+            A = ptr(self.a[k])
+            if op == "add_rmsnorm_quantize":
+                B = ptr(self.b[k])
+                self.fused_calls.append([(L.qmm_add_rmsnorm_quantize, (A, B, W, F(self.EPS), I(nt), I(idim)) + q8a)])
+                self.chain_calls.append([(L.qmm_residual_add, (A, B, I(nt), I(idim), st)),
+                                         (L.qmm_rmsnorm, (A, W, F(self.EPS), I(nt), I(idim), y, st)),
+                                         (L.qmm_quantize_act, (y, I(nt), I(idim)) + q8a)])
+            elif op == "rmsnorm_quantize":
+                self.fused_calls.append([(L.qmm_rmsnorm_quantize, (A, W, F(self.EPS), I(nt), I(idim)) + q8a)])
+                self.chain_calls.append([(L.qmm_rmsnorm, (A, W, F(self.EPS), I(nt), I(idim), y, st)),
+                                         (L.qmm_quantize_act, (y, I(nt), I(idim)) + q8a)])
+            else:
+                B = ptr(self.b[k])
+                self.fused_calls.append([(L.qmm_silu_mul_quantize, (A, B, I(nt), I(idim)) + q8a)])
+                self.chain_calls.append([(L.qmm_silu_mul, (A, B, I(nt), I(idim), y, st)),
+                                         (L.qmm_quantize_act, (y, I(nt), I(idim)) + q8a)])
+
+    @staticmethod
+    def _issue(seq):
+        for f, args in seq:
+            rc = f(*args)
+            if rc:
+                raise RuntimeError(f"{f.__name__} failed: {rc}")
+
+    def fused(self):
+        self._issue(self.fused_calls[self.i % len(self.fused_calls)])
+        self.i += 1
+
+    def chain(self):
+        self._issue(self.chain_calls[self.i % len(self.chain_calls)])
+        self.i += 1
+
+
+def fused_kernel_name(op, idim):
+    """(trace name, launch threads per row or per element group) of a fused kernel."""
+    if op == "silu_mul_quantize":
+        return "qmm::{anonymous}::silu_mul_kernel<true>"
+    nch = (idim // 4 + 255) // 256
+    ch = next((c for c in (1, 2, 4, 8, 16) if nch <= c), 0)
+    add = "true" if op == "add_rmsnorm_quantize" else "false"
+    return f"qmm::{{anonymous}}::rmsnorm_kernel<{ch}, {add}, true>"
+
+
+def fused_cpu_baseline(calls):
+    """The oracle's fused steps (f32 step, then the quantizer) on a bounded sample."""
+    import oracle
+    oracle.build(force=False)
+    nbytes, t_total, reps = 0.0, 0.0, 0
+    rows = 64
+    data = []
+    for c in calls:
+        if c.nt < 512:
+            continue
+        a = c.a[0][:rows].cpu().numpy()
+        b = c.b[0][:rows].cpu().numpy() if c.b[0] is not None else None
+        data.append((c, a, b, c.w.cpu().numpy(), c.fbytes * rows / c.nt))
+    while t_total < 10.0:
+        for c, a, b, w, nb in data:
+            t0 = time.perf_counter()
+            if c.op == "add_rmsnorm_quantize":
+                oracle.quantize(oracle.add_rmsnorm(a, b, w, FusedCall.EPS)[1])
+            elif c.op == "rmsnorm_quantize":
+                oracle.quantize(oracle.rmsnorm(a, w, FusedCall.EPS))
+            else:
+                oracle.quantize(oracle.silu_mul(a, b))
+            t_total += time.perf_counter() - t0
+            nbytes += nb
+        reps += 1
+    return {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the three fused steps on the first {rows} rows of each nt=512 call "
+                      f"({', '.join(c.label for c, *_ in data)}), repeated {reps}x, {t_total:.1f} s"}
+
+
+def run_fused(args, torch, qmm):
+    from quantized_matmul_amd.profile_summary import read_traffic
+
+    calls = []
+    for op, idim in (("add_rmsnorm_quantize", 4096), ("rmsnorm_quantize", 4096), ("silu_mul_quantize", 12288)):
+        for nt in (1, 512):
+            calls.append(FusedCall(torch, qmm, op, nt, idim, seed=31 + nt + idim))
+    cal = copy_calibration(torch, args.copy_calibration) if args.copy_calibration > 0 else None
+    st = torch.cuda.current_stream()
+    chunk = min(CHUNK, args.steps)
+    nchunks = max(1, args.steps // chunk)
+    steps = chunk * nchunks
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in calls] for _ in range(nchunks)]
+    for _ in range(args.warmup):
+        for c in calls:
+            c.fused()
+            c.chain()
+    torch.cuda.synchronize()
+    gate_cycles = 2_000_000
+    t0 = time.perf_counter()
+    for ch in range(nchunks):
+        torch.cuda._sleep(gate_cycles)
+        for c, (e0, e1, e2) in zip(calls, evs[ch]):
+            e0.record(st)
+            for _ in range(chunk):
+                c.fused()
+            e1.record(st)
+            for _ in range(chunk):
+                c.chain()
+            e2.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for ch in range(nchunks):
+        for c, (e0, e1, e2) in zip(calls, evs[ch]):
+            c.f_ms.append(e0.elapsed_time(e1) / chunk)
+            c.c_ms.append(e1.elapsed_time(e2) / chunk)
+
+    detail = []
+    for c in calls:
+        f, cm = float(np.mean(c.f_ms)), float(np.mean(c.c_ms))
+        gbs = c.fbytes / (f * 1e-3) / 1e9
+        detail.append({"call": c.label, "fused_us": round(f * 1e3, 2), "chain_us": round(cm * 1e3, 2),
+                       "chain_over_fused": round(cm / f, 2), "fused_bytes": int(c.fbytes),
+                       "chain_bytes": int(c.cbytes), "fused_GB_s": round(gbs, 1),
+                       "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
+    big = [c for c in calls if c.nt == 512]
+    tb = sum(c.fbytes for c in big)
+    tt = sum(float(np.mean(c.f_ms)) * 1e-3 for c in big)
+    head = max(big, key=lambda c: c.fbytes)
+    kh = float(np.mean(head.f_ms)) * 1e-3
+    kname = fused_kernel_name(head.op, head.idim)
+    grid = -(-head.nt * head.idim // 4 // 256) * 256
+    line = {"metric": "producer-fused quantize: HBM GB/s of the fused kernels at nt=512",
+            "value": round(tb / tt / 1e9, 1), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+            "warmup": args.warmup, "ms_per_step": round(wall * 1e3 / steps, 4),
+            "gpu_ms_per_step": round(sum(float(np.mean(c.f_ms)) + float(np.mean(c.c_ms)) for c in calls), 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded; no model weights)",
+            "roofline": {"bound": "hbm", "achieved": round(head.fbytes / kh / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(head.fbytes / kh / 1e9 / HBM_PEAK_GBS, 4),
+                         "traffic": read_traffic(FUSED_COUNTERS, kname, grid),
+                         "kernel": kname.replace("qmm::{anonymous}::", "").replace(" ", ""),
+                         "call": head.label, "bytes_per_launch": int(head.fbytes)},
+            "config": {"workload": "fused_quantize", "hidden": 4096, "ffn": 12288, "nt": [1, 512],
+                       "input_copies_bytes_per_shape": COPY_BYTES},
+            "detail": detail}
+    if cal:
+        line["copy_calibration"] = cal
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = fused_cpu_baseline(calls)
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(calls):
     """The CPU oracle as it stands, on a bounded sample of the same workload."""
     import oracle
@@ -235,6 +430,8 @@ def main():
     from quantized_matmul_amd.profile_summary import read_traffic
 
     torch.cuda.set_device(0)
+    if args.workload == "fused_quantize":
+        return run_fused(args, torch, qmm)
     calls = build_calls(torch, qmm, args.workload)
     cal = copy_calibration(torch, args.copy_calibration) if args.copy_calibration > 0 else None
     st = torch.cuda.current_stream()

@@ -35,6 +35,9 @@ KERNEL_SOURCES = {
     "qmm::mmvq_": ("qmm_mmvq.hip", "qmm_internal.h"),
     "qmm::mmq_": ("qmm_mmq.hip", "qmm_internal.h"),
     "qmm::quantize_": ("qmm_quantize.hip", "qmm_internal.h"),
+    "qmm::{anonymous}::rmsnorm_": ("qmm_fused.hip", "qmm_internal.h"),
+    "qmm::{anonymous}::silu_mul_": ("qmm_fused.hip", "qmm_internal.h"),
+    "qmm::{anonymous}::residual_add_": ("qmm_fused.hip", "qmm_internal.h"),
 }
 
 
@@ -99,7 +102,11 @@ def cmd_trace(a):
                   "launches, per launch; under kernel tracing the launches no longer run back to back):", "",
                   "| call | kernel | event us |", "|---|---|---|"]
         for d in line.get("detail", []):
-            lines.append(f"| {d['call']} | {d['kernel']} | {d['kernel_us']} |")
+            if "fused_us" in d:  # producer-fused workload: the fused kernel and its unfused chain
+                lines.append(f"| {d['call']} | fused | {d['fused_us']} |")
+                lines.append(f"| {d['call']} | unfused chain (all launches) | {d['chain_us']} |")
+            else:
+                lines.append(f"| {d['call']} | {d['kernel']} | {d['kernel_us']} |")
         rf = line.get("roofline")
         if rf:
             lines += ["", f"Roofline kernel `{rf.get('kernel')}` ({rf.get('call')}): achieved {rf['achieved']} "
