@@ -50,11 +50,15 @@ def _bind(path: str):
     L.oracle_rmsnorm.argtypes = [P, P, F, I, I, P]
     L.oracle_add_rmsnorm.argtypes = [P, P, P, F, I, I, P, P]
     L.oracle_silu_mul.argtypes = [P, P, ctypes.c_size_t, P]
+    L.oracle_quantize_q8k.argtypes = [P, I, I, P, P, P]
+    L.oracle_matmul_q8k.argtypes = [I, P, P, P, P, I, I, I, P, P]
+    L.oracle_matmul_q8k_points.argtypes = [I, P, P, P, P, I, I, I, I, P, P, P, P]
     L.oracle_num_threads.restype = I
     L.oracle_set_num_threads.argtypes = [I]
     for f in ("oracle_quantize", "oracle_subblock_dots", "oracle_matmul_q8",
               "oracle_matmul_q8_points", "oracle_matmul", "oracle_decode_block",
-              "oracle_rmsnorm", "oracle_add_rmsnorm", "oracle_silu_mul"):
+              "oracle_rmsnorm", "oracle_add_rmsnorm", "oracle_silu_mul", "oracle_quantize_q8k",
+              "oracle_matmul_q8k", "oracle_matmul_q8k_points"):
         getattr(L, f).restype = I
     return L
 
@@ -219,6 +223,48 @@ def silu_mul(g: np.ndarray, u: np.ndarray):
     y = np.empty_like(g)
     _check(lib().oracle_silu_mul(_p(g), _p(u), g.size, _p(y)), "oracle_silu_mul")
     return y
+
+
+def quantize_q8k(x: np.ndarray):
+    """Q8_K activations: (q [nt][id] int8, d [nt][id/256] f32, bsum [nt][id/16] f32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    nt, idim = x.shape
+    q = np.empty((nt, idim), np.int8)
+    d = np.empty((nt, idim // 256), np.float32)
+    bs = np.empty((nt, idim // 16), np.float32)
+    _check(lib().oracle_quantize_q8k(_p(x), nt, idim, _p(q), _p(d), _p(bs)), "oracle_quantize_q8k")
+    return q, d, bs
+
+
+def matmul_q8k(qtype: int, W: np.ndarray, q, d, bsum, od: int):
+    """out [nt][od] f32 and mag [nt][od] f64 from Q8_K activations."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    d = np.ascontiguousarray(d, dtype=np.float32)
+    bsum = np.ascontiguousarray(bsum, dtype=np.float32)
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    nt, idim = q.shape
+    out = np.empty((nt, od), np.float32)
+    mag = np.empty((nt, od), np.float64)
+    _check(lib().oracle_matmul_q8k(qtype, _p(W), _p(q), _p(d), _p(bsum), nt, od, idim, _p(out), _p(mag)),
+           "oracle_matmul_q8k")
+    return out, mag
+
+
+def matmul_q8k_points(qtype: int, W: np.ndarray, q, d, bsum, od: int, t_idx, r_idx):
+    """Selected outputs (t_idx[k], r_idx[k]) from Q8_K activations: (out [k] f32, mag [k] f64)."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    d = np.ascontiguousarray(d, dtype=np.float32)
+    bsum = np.ascontiguousarray(bsum, dtype=np.float32)
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    t_idx = np.ascontiguousarray(t_idx, dtype=np.int32)
+    r_idx = np.ascontiguousarray(r_idx, dtype=np.int32)
+    nt, idim = q.shape
+    n = int(t_idx.size)
+    out = np.empty(n, np.float32)
+    mag = np.empty(n, np.float64)
+    _check(lib().oracle_matmul_q8k_points(qtype, _p(W), _p(q), _p(d), _p(bsum), nt, od, idim, n, _p(t_idx),
+                                          _p(r_idx), _p(out), _p(mag)), "oracle_matmul_q8k_points")
+    return out, mag
 
 
 def num_threads() -> int:

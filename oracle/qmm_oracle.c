@@ -34,13 +34,18 @@
  *   R18 silu(g) * u evaluated in f64 as (g / (1 + exp(-g))) * u and rounded once
  *       to f32 (the value the quantizer then reads).
  *
+ *   R19 Q8_K activations: the per-32 rules R2/R3 applied to blocks of 256
+ *       (d = amax / 127, q = roundf(x / d), zero block -> 0); the 16-value group
+ *       sums are the exact integer sums of the codes, stored as f32.
+ *
  * Build: gcc -O2 -ffp-contract=off -fopenmp (no -ffast-math, no -march).
  *
  * OQ_MUTATE (default 0) plants one known mistake, for the tests that show the
  * pins catch it: 1 swapped nibble halves, 2 Q6_K offset 32 dropped, 3 Q4_K min
  * term dropped, 4 scale and min swapped, 5 Q6_K scale per 32 instead of per 16,
  * 6 RMS mean over n - 1, 7 eps added after the square root, 8 squares summed in
- * one running sum, 9 silu with exp(+g).
+ * one running sum, 9 silu with exp(+g), 10 Q8_K scale from the first 32 values of
+ * the block only, 11 Q8_K min term from the first 16-value sum of each sub-block.
  */
 #ifndef OQ_MUTATE
 #define OQ_MUTATE 0
@@ -430,6 +435,147 @@ int oracle_matmul_q8(int type, const uint8_t* W, const int8_t* q, const float* d
         int t = (int)(e / od), r = (int)(e % od);
         one_output(type, W + (size_t)r * row_bytes, q + (size_t)t * id, d + (size_t)t * (id / 32),
                    s + (size_t)t * (id / 32), nsb, out + (size_t)t * od + r, mag ? mag + (size_t)t * od + r : NULL);
+    }
+    return 0;
+}
+
+/* ---- O7. Q8_K activations (one scale per 256 values) ----------------------
+ * [GEMM, "Activations: int8 with a scale per 256"]: each activation row is
+ * quantized to int8 with one f32 scale per 256 values, and the sum of every group
+ * of 16 values is kept as a float; [GEMM, "The zero points do not touch the inner
+ * loop"]: the Q4_K min term is dmin * m times the activation sum of the
+ * sub-block, taken from those stored sums.  Reading R19.  Per token t, block b of
+ * 256: amax = max |x|; d = amax / 127; q = roundf(x / d); bsum[g] = sum of the 16
+ * codes of group g (exact integer, stored as f32). */
+int oracle_quantize_q8k(const float* x, int nt, int id, int8_t* q, float* d, float* bsum)
+{
+    if (!x || !q || !d || !bsum || nt < 0 || id < 0 || id % 256)
+        return -1;
+    int nsb = id / 256;
+    for (int t = 0; t < nt; ++t) {
+        for (int b = 0; b < nsb; ++b) {
+            const float* xb = x + (size_t)t * id + 256 * b;
+            int8_t* qb = q + (size_t)t * id + 256 * b;
+            float amax = 0.0f;
+#if OQ_MUTATE == 10
+            for (int i = 0; i < 32; ++i) {
+#else
+            for (int i = 0; i < 256; ++i) {
+#endif
+                float a = fabsf(xb[i]);
+                if (a > amax)
+                    amax = a;
+            }
+            float db = amax / 127.0f;
+            for (int i = 0; i < 256; ++i) {
+                int qi = 0;
+                if (db != 0.0f) {
+                    float r = roundf(xb[i] / db);
+                    if (r > 127.0f || r < -127.0f) {
+                        if (OQ_MUTATE != 10)
+                            return -2; /* cannot happen: |x| <= amax */
+                        r = r > 0 ? 127.0f : -127.0f;
+                    }
+                    qi = (int)r;
+                }
+                qb[i] = (int8_t)qi;
+            }
+            d[(size_t)t * nsb + b] = db;
+            for (int g = 0; g < 16; ++g) {
+                int sum = 0;
+                for (int l = 0; l < 16; ++l)
+                    sum += qb[16 * g + l];
+                bsum[(size_t)t * (id / 16) + 16 * b + g] = (float)sum;
+            }
+        }
+    }
+    return 0;
+}
+
+/* One output from Q8_K activations.  Q4_K, per super-block b and sub-block j:
+ *   d * sc_j * dx_b * sum(q * qx)  -  dmin * m_j * dx_b * (bsum_{2j} + bsum_{2j+1});
+ * Q6_K, per group g: d * sc_g * dx_b * sum((q6 - 32) * qx).  Every term in f64,
+ * summed in f64, one rounding to f32; mag = sum |term|. */
+static void one_output_q8k(int type, const uint8_t* Wrow, const int8_t* qx_t, const float* d_t,
+                           const float* bs_t, int nsb, float* out, double* mag)
+{
+    double acc = 0.0, am = 0.0;
+    size_t bb = blk_bytes(type);
+    for (int b = 0; b < nsb; ++b) {
+        const uint8_t* B = Wrow + (size_t)b * bb;
+        const int8_t* qx = qx_t + 256 * b;
+        double dx = (double)d_t[b];
+        if (type == OQ_TYPE_Q4_K) {
+            q4k_block w;
+            q4k_decode(B, &w);
+            for (int j = 0; j < 8; ++j) {
+#if OQ_MUTATE == 11
+                double bs = 2.0 * (double)bs_t[16 * b + 2 * j];
+#else
+                double bs = (double)bs_t[16 * b + 2 * j] + (double)bs_t[16 * b + 2 * j + 1];
+#endif
+                double tmain = (w.d * (double)w.sc[j]) * dx * (double)dot_q4k_sub(&w, qx, j);
+                double tmin = (w.dmin * (double)w.m[j]) * dx * bs;
+                acc += tmain - tmin;
+                am += fabs(tmain) + fabs(tmin);
+            }
+        } else {
+            q6k_block w;
+            q6k_decode(B, &w);
+            for (int g = 0; g < 16; ++g) {
+                double tm = (w.d * (double)w.sc[g]) * dx * (double)dot_q6k_group(&w, qx, g);
+                acc += tm;
+                am += fabs(tm);
+            }
+        }
+    }
+    *out = (float)acc;
+    if (mag)
+        *mag = am;
+}
+
+int oracle_matmul_q8k(int type, const uint8_t* W, const int8_t* q, const float* d, const float* bsum,
+                      int nt, int od, int id, float* out, double* mag)
+{
+    if (!W || !q || !d || !bsum || !out || nt < 0 || od < 0 || id < 0 || id % 256)
+        return -1;
+    if (type != OQ_TYPE_Q4_K && type != OQ_TYPE_Q6_K)
+        return -2;
+    int nsb = id / 256;
+    size_t row_bytes = (size_t)nsb * blk_bytes(type);
+    long total = (long)nt * od;
+#pragma omp parallel for schedule(static)
+    for (long e = 0; e < total; ++e) {
+        int t = (int)(e / od), r = (int)(e % od);
+        one_output_q8k(type, W + (size_t)r * row_bytes, q + (size_t)t * id, d + (size_t)t * nsb,
+                       bsum + (size_t)t * (id / 16), nsb, out + (size_t)t * od + r,
+                       mag ? mag + (size_t)t * od + r : NULL);
+    }
+    return 0;
+}
+
+/* Selected outputs only, as oracle_matmul_q8_points. */
+int oracle_matmul_q8k_points(int type, const uint8_t* W, const int8_t* q, const float* d, const float* bsum,
+                             int nt, int od, int id, int n, const int* t_idx, const int* r_idx, float* out,
+                             double* mag)
+{
+    if (!W || !q || !d || !bsum || !out || !t_idx || !r_idx || nt < 0 || od < 0 || id < 0 || id % 256 || n < 0)
+        return -1;
+    if (type != OQ_TYPE_Q4_K && type != OQ_TYPE_Q6_K)
+        return -2;
+    int nsb = id / 256;
+    size_t row_bytes = (size_t)nsb * blk_bytes(type);
+#pragma omp parallel for schedule(static)
+    for (int k = 0; k < n; ++k) {
+        int t = t_idx[k], r = r_idx[k];
+        if (t < 0 || t >= nt || r < 0 || r >= od) {
+            out[k] = 0.0f;
+            if (mag)
+                mag[k] = -1.0;
+            continue;
+        }
+        one_output_q8k(type, W + (size_t)r * row_bytes, q + (size_t)t * id, d + (size_t)t * nsb,
+                       bsum + (size_t)t * (id / 16), nsb, out + k, mag ? mag + k : NULL);
     }
     return 0;
 }
