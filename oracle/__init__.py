@@ -53,12 +53,13 @@ def _bind(path: str):
     L.oracle_quantize_q8k.argtypes = [P, I, I, P, P, P]
     L.oracle_matmul_q8k.argtypes = [I, P, P, P, P, I, I, I, P, P]
     L.oracle_matmul_q8k_points.argtypes = [I, P, P, P, P, I, I, I, I, P, P, P, P]
+    L.oracle_q8k_superblock_sums.argtypes = [I, P, P, P, I, I, I, P]
     L.oracle_num_threads.restype = I
     L.oracle_set_num_threads.argtypes = [I]
     for f in ("oracle_quantize", "oracle_subblock_dots", "oracle_matmul_q8",
               "oracle_matmul_q8_points", "oracle_matmul", "oracle_decode_block",
               "oracle_rmsnorm", "oracle_add_rmsnorm", "oracle_silu_mul", "oracle_quantize_q8k",
-              "oracle_matmul_q8k", "oracle_matmul_q8k_points"):
+              "oracle_matmul_q8k", "oracle_matmul_q8k_points", "oracle_q8k_superblock_sums"):
         getattr(L, f).restype = I
     return L
 
@@ -265,6 +266,18 @@ def matmul_q8k_points(qtype: int, W: np.ndarray, q, d, bsum, od: int, t_idx, r_i
     _check(lib().oracle_matmul_q8k_points(qtype, _p(W), _p(q), _p(d), _p(bsum), nt, od, idim, n, _p(t_idx),
                                           _p(r_idx), _p(out), _p(mag)), "oracle_matmul_q8k_points")
     return out, mag
+
+
+def q8k_superblock_sums(qtype: int, W: np.ndarray, q, bsum, od: int):
+    """Integer stage of the Q8_K matmul: [nt][od][id/256][2] int32 (scaled dot sum, min sum)."""
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    bsum = np.ascontiguousarray(bsum, dtype=np.float32)
+    W = np.ascontiguousarray(W, dtype=np.uint8)
+    nt, idim = q.shape
+    S = np.empty((nt, od, idim // 256, 2), np.int32)
+    _check(lib().oracle_q8k_superblock_sums(qtype, _p(W), _p(q), _p(bsum), nt, od, idim, _p(S)),
+           "oracle_q8k_superblock_sums")
+    return S
 
 
 def num_threads() -> int:

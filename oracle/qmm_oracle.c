@@ -554,6 +554,52 @@ int oracle_matmul_q8k(int type, const uint8_t* W, const int8_t* q, const float* 
     return 0;
 }
 
+/* The integer stage of the Q8_K matmul: per token t, row r, super-block b,
+ *   S[..][0] = sum_j sc_j * sum(q * qx)                     (Q4_K; Q6_K: sum_g sc_g *
+ *              sum((q6 - 32) * qx)),
+ *   S[..][1] = sum_j m_j * (bsum_{2j} + bsum_{2j+1})         (Q4_K; Q6_K: 0),
+ * exact integers (the group sums are integers stored as f32).  S: [nt][od][id/256][2]. */
+int oracle_q8k_superblock_sums(int type, const uint8_t* W, const int8_t* q, const float* bsum, int nt, int od,
+                               int id, int32_t* S)
+{
+    if (!W || !q || !bsum || !S || nt < 0 || od < 0 || id < 0 || id % 256)
+        return -1;
+    if (type != OQ_TYPE_Q4_K && type != OQ_TYPE_Q6_K)
+        return -2;
+    int nsb = id / 256;
+    size_t bb = blk_bytes(type);
+#pragma omp parallel for schedule(static)
+    for (int r = 0; r < od; ++r) {
+        for (int b = 0; b < nsb; ++b) {
+            const uint8_t* B = W + ((size_t)r * nsb + b) * bb;
+            q4k_block w4;
+            q6k_block w6;
+            if (type == OQ_TYPE_Q4_K)
+                q4k_decode(B, &w4);
+            else
+                q6k_decode(B, &w6);
+            for (int t = 0; t < nt; ++t) {
+                const int8_t* qx = q + (size_t)t * id + 256 * b;
+                const float* bs = bsum + (size_t)t * (id / 16) + 16 * b;
+                long s1 = 0, s2 = 0;
+                if (type == OQ_TYPE_Q4_K) {
+                    for (int j = 0; j < 8; ++j) {
+                        s1 += (long)w4.sc[j] * dot_q4k_sub(&w4, qx, j);
+                        s2 += (long)w4.m[j] * ((long)bs[2 * j] + (long)bs[2 * j + 1]);
+                    }
+                } else {
+                    for (int g = 0; g < 16; ++g)
+                        s1 += (long)w6.sc[g] * dot_q6k_group(&w6, qx, g);
+                }
+                int32_t* dst = S + (((size_t)t * od + r) * nsb + b) * 2;
+                dst[0] = (int32_t)s1;
+                dst[1] = (int32_t)s2;
+            }
+        }
+    }
+    return 0;
+}
+
 /* Selected outputs only, as oracle_matmul_q8_points. */
 int oracle_matmul_q8k_points(int type, const uint8_t* W, const int8_t* q, const float* d, const float* bsum,
                              int nt, int od, int id, int n, const int* t_idx, const int* r_idx, float* out,

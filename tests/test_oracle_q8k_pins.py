@@ -135,6 +135,34 @@ def test_q8k_points_match_full():
         assert np.array_equal(po, out[t, r]) and np.array_equal(pm, mag[t, r])
 
 
+@pytest.mark.parametrize("qtype", [Q4, Q6])
+def test_q8k_superblock_sums_brute_force(qtype):
+    """The integer stage from the element-indexed decoder and plain Python sums."""
+    od, idim, nt = 3, 512, 2
+    W, _, (q, d, bs), *_ = _fold_case(qtype, od, idim, nt, 50)
+    S = oracle.q8k_superblock_sums(qtype, W, q, bs, od)
+    bb = 144 if qtype == Q4 else 210
+    Wb = W.reshape(od, idim // 256, bb)
+    for t in range(nt):
+        for r in range(od):
+            for b in range(idim // 256):
+                blk = Wb[r, b]
+                qx = q[t, 256 * b: 256 * b + 256].astype(np.int64)
+                if qtype == Q4:
+                    codes = np.array([bf.q4k_code(blk, e) for e in range(256)], np.int64)
+                    scm = [bf.q4k_field(blk, j) for j in range(8)]
+                    s1 = sum(scm[j][0] * int(np.dot(codes[32 * j: 32 * j + 32], qx[32 * j: 32 * j + 32]))
+                             for j in range(8))
+                    s2 = sum(scm[j][1] * int(bs[t, 16 * b + 2 * j] + bs[t, 16 * b + 2 * j + 1]) for j in range(8))
+                else:
+                    codes = np.array([bf.q6k_code(blk, e) for e in range(256)], np.int64)
+                    sc = blk[192:208].view(np.int8).astype(np.int64)
+                    s1 = sum(int(sc[g]) * int(np.dot(codes[16 * g: 16 * g + 16] - 32, qx[16 * g: 16 * g + 16]))
+                             for g in range(16))
+                    s2 = 0
+                assert (S[t, r, b, 0], S[t, r, b, 1]) == (s1, s2), (t, r, b)
+
+
 @pytest.mark.parametrize("mutation", [10, 11])
 def test_planted_q8k_mistakes_are_caught(mutation, tmp_path):
     path = oracle.build(out=str(tmp_path / f"liboracle_m{mutation}.so"), mutate=mutation)
