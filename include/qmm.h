@@ -136,6 +136,36 @@ int qmm_dispatch_kind(int type, int nt, int od, int id);
  * clamped to 0..8, read once). */
 int qmm_nt_switch(void);
 
+/* ---- Q8_K activations: one scale per 256 values ------------------------------
+ * [GEMM, "Activations: int8 with a scale per 256"]: each activation row quantized
+ * to int8 with one f32 scale per 256 values and the sum of every 16-value group of
+ * codes kept as a float; [GEMM, "The zero points do not touch the inner loop"]:
+ * the Q4_K min term is dmin * m times the sub-block's activation sum, read from
+ * those stored sums.  Rules as qmm_quantize_act over 256 values: d = amax / 127
+ * (IEEE division), q = round(x / d) half away from zero, a zero block gives
+ * d = q = 0; bsum = exact sum of 16 codes (|bsum| <= 2032).  Numerics differ from
+ * the per-32 path (a coarser activation scale); the results are their own. */
+
+/* x [nt][id] f32 -> q [nt][id] int8, d [nt][id/256] f32, bsum [nt][id/16] f32.
+ * id a positive multiple of 256 (QMM_ERR_SHAPE), nt >= 1 (QMM_ERR_ARG), pointers
+ * device, 16-byte aligned (QMM_ERR_ALIGN), non-null (QMM_ERR_ARG). */
+int qmm_quantize_act_q8k(const float* x, int nt, int id, int8_t* q, float* d, float* bsum, void* stream);
+
+/* out [nt][od] = W x on Q8_K activations (q, d, bsum from qmm_quantize_act_q8k).
+ * Per super-block b of row r and token t:
+ *   d_r * dx_tb * sum_j sc_j * sum(q * qx) - dmin_r * dx_tb * sum_j m_j * (bsum_2j + bsum_2j+1),
+ * the two inner sums exact integers, the f32 terms accumulated in f32.  Runs the
+ * int8-MFMA matrix kernel for every nt (no vector kernel on this path).  Weight
+ * type Q4_K only (QMM_ERR_TYPE otherwise); shapes and alignment as qmm_matmul_q8. */
+int qmm_matmul_q8k(int type, const void* W, const int8_t* q, const float* d, const float* bsum, int nt,
+                   int od, int id, float* out, void* stream);
+
+/* Diagnostic: the integer stage of qmm_matmul_q8k alone.  S [nt][od][id/256][2]
+ * int32: S[..][0] = sum_j sc_j * sum(q * qx), S[..][1] = sum_j m_j * (bsum_2j +
+ * bsum_2j+1), computed by the kernel's code.  Arguments as qmm_matmul_q8k. */
+int qmm_q8k_superblock_sums(int type, const void* W, const int8_t* q, const float* d, const float* bsum,
+                            int nt, int od, int id, int32_t* S, void* stream);
+
 /* ---- Producer-side steps fused with the quantizer ---------------------------
  * [GEMM, "The GPU path", "Fused elementwise kernels"]: each RMS norm and the FFN
  * activation ends in the quantizer; fusing them removes the HBM write and re-read

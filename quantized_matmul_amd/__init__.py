@@ -41,7 +41,8 @@ BLOCK_BYTES = {QMM_TYPE_Q4_K: 144, QMM_TYPE_Q6_K: 210}
 EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8",
            "qmm_matmul_q8_kind", "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots",
            "qmm_mfma_tile_check", "qmm_strerror", "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize",
-           "qmm_silu_mul_quantize", "qmm_residual_add", "qmm_rmsnorm", "qmm_silu_mul")
+           "qmm_silu_mul_quantize", "qmm_residual_add", "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k",
+           "qmm_matmul_q8k", "qmm_q8k_superblock_sums")
 
 
 class QmmError(RuntimeError):
@@ -82,12 +83,16 @@ def lib():
         L.qmm_residual_add.argtypes = [P, P, I, I, P]
         L.qmm_rmsnorm.argtypes = [P, P, F, I, I, P, P]
         L.qmm_silu_mul.argtypes = [P, P, I, I, P, P]
+        L.qmm_quantize_act_q8k.argtypes = [P, I, I, P, P, P, P]
+        L.qmm_matmul_q8k.argtypes = [I, P, P, P, P, I, I, I, P, P]
+        L.qmm_q8k_superblock_sums.argtypes = [I, P, P, P, P, I, I, I, P, P]
         L.qmm_strerror.argtypes = [I]
         L.qmm_strerror.restype = ctypes.c_char_p
         for f in ("qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8", "qmm_matmul_q8_kind",
                   "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots", "qmm_mfma_tile_check",
                   "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize", "qmm_silu_mul_quantize", "qmm_residual_add",
-                  "qmm_rmsnorm", "qmm_silu_mul"):
+                  "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k", "qmm_matmul_q8k",
+                  "qmm_q8k_superblock_sums"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -162,6 +167,45 @@ def qmm_quantize_act(x: torch.Tensor, q=None, d=None, s=None, stream=None):
                                   _dev(d, torch.float32, "d"), _dev(s, torch.float32, "s"), _stream(stream)),
            "qmm_quantize_act")
     return q, d, s
+
+
+def qmm_quantize_act_q8k(x: torch.Tensor, q=None, d=None, bsum=None, stream=None):
+    """Q8_K activations: x f32 [nt, id] -> (q int8 [nt, id], d f32 [nt, id/256], bsum f32 [nt, id/16])."""
+    nt, idim = x.shape
+    if q is None:
+        q = torch.empty((nt, idim), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((nt, idim // 256), dtype=torch.float32, device=x.device)
+    if bsum is None:
+        bsum = torch.empty((nt, idim // 16), dtype=torch.float32, device=x.device)
+    _check(lib().qmm_quantize_act_q8k(_dev(x, torch.float32, "x"), nt, idim, _dev(q, torch.int8, "q"),
+                                      _dev(d, torch.float32, "d"), _dev(bsum, torch.float32, "bsum"),
+                                      _stream(stream)), "qmm_quantize_act_q8k")
+    return q, d, bsum
+
+
+def qmm_matmul_q8k(qtype: int, W: torch.Tensor, q: torch.Tensor, d: torch.Tensor, bsum: torch.Tensor, od: int,
+                   out=None, stream=None):
+    """out f32 [nt, od] from Q8_K activations (Q4_K weights)."""
+    nt, idim = q.shape
+    if out is None:
+        out = torch.empty((nt, od), dtype=torch.float32, device=q.device)
+    _check(lib().qmm_matmul_q8k(qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"),
+                                _dev(d, torch.float32, "d"), _dev(bsum, torch.float32, "bsum"), nt, od, idim,
+                                _dev(out, torch.float32, "out"), _stream(stream)), "qmm_matmul_q8k")
+    return out
+
+
+def qmm_q8k_superblock_sums(qtype: int, W: torch.Tensor, q: torch.Tensor, d: torch.Tensor, bsum: torch.Tensor,
+                            od: int, S=None, stream=None):
+    """Integer stage of qmm_matmul_q8k: S int32 [nt, od, id/256, 2]."""
+    nt, idim = q.shape
+    if S is None:
+        S = torch.empty((nt, od, idim // 256, 2), dtype=torch.int32, device=q.device)
+    _check(lib().qmm_q8k_superblock_sums(qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"),
+                                         _dev(d, torch.float32, "d"), _dev(bsum, torch.float32, "bsum"), nt, od,
+                                         idim, _dev(S, torch.int32, "S"), _stream(stream)), "qmm_q8k_superblock_sums")
+    return S
 
 
 def _q8_out(x: torch.Tensor, q, d, s):

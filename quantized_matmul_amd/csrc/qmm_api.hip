@@ -247,6 +247,58 @@ int qmm_silu_mul(const float* g, const float* u, int nt, int id, float* y, void*
                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
+int qmm_quantize_act_q8k(const float* x, int nt, int id, int8_t* q, float* d, float* bsum, void* stream)
+{
+    if (!x || !q || !d || !bsum || nt < 1)
+        return QMM_ERR_ARG;
+    if (id < 256 || id % 256 || (long long)nt * id > 0x7FFFFFFFLL)
+        return QMM_ERR_SHAPE;
+    if (!all_aligned({x, q, d, bsum}))
+        return QMM_ERR_ALIGN;
+    int rc = check_device();
+    if (rc)
+        return rc;
+    return launched(qmm::launch_quantize_q8k(x, nt, id, q, d, bsum, reinterpret_cast<hipStream_t>(stream)));
+}
+
+static int q8k_checked(int type, const void* W, const int8_t* q, const float* d, const float* bsum, int nt, int od,
+                       int id, float* out, int32_t* S, void* stream)
+{
+    if (!W || !q || !d || !bsum || (!out && !S))
+        return QMM_ERR_ARG;
+    int rc = check_type(type);
+    if (rc)
+        return rc;
+    if (type != QMM_TYPE_Q4_K)
+        return QMM_ERR_TYPE;
+    if ((rc = check_shape(nt, od, id)))
+        return rc;
+    if (S && (long long)nt * od * (id / 256) * 2 > 0x7FFFFFFFLL)
+        return QMM_ERR_SHAPE;
+    if (!all_aligned({W, q, d, bsum, out ? (const void*)out : (const void*)S}))
+        return QMM_ERR_ALIGN;
+    if ((rc = check_device()))
+        return rc;
+    return launched(qmm::launch_mmq_q8k(type, reinterpret_cast<const uint8_t*>(W), q, d, bsum, nt, od, id, out, S,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+int qmm_matmul_q8k(int type, const void* W, const int8_t* q, const float* d, const float* bsum, int nt, int od,
+                   int id, float* out, void* stream)
+{
+    if (!out)
+        return QMM_ERR_ARG;
+    return q8k_checked(type, W, q, d, bsum, nt, od, id, out, nullptr, stream);
+}
+
+int qmm_q8k_superblock_sums(int type, const void* W, const int8_t* q, const float* d, const float* bsum, int nt,
+                            int od, int id, int32_t* S, void* stream)
+{
+    if (!S)
+        return QMM_ERR_ARG;
+    return q8k_checked(type, W, q, d, bsum, nt, od, id, nullptr, S, stream);
+}
+
 int qmm_nt_switch(void) { return nt_switch_value(); }
 
 int qmm_dispatch_kind(int type, int nt, int od, int id)

@@ -30,6 +30,13 @@ hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* 
                       int nt, int od, int id, float* out, int32_t* S, hipStream_t st, int tile = 0);
 int mmq_tile_choice(int nt, int od, int id);
 
+// Q8_K activations: q [nt][id] int8, d [nt][id/256] f32, bsum [nt][id/16] f32
+// (id % 256 == 0), and the Q4_K matmul on them (qmm_mmq_q8k.hip).  S != null: the
+// integer stage only, S [nt][od][id/256][2] int32.
+hipError_t launch_quantize_q8k(const float* x, int nt, int id, int8_t* q, float* d, float* bsum, hipStream_t st);
+hipError_t launch_mmq_q8k(int type, const uint8_t* W, const int8_t* q, const float* d, const float* bsum, int nt,
+                          int od, int id, float* out, int32_t* S, hipStream_t st);
+
 // Producer-side steps that feed the quantizer (qmm_fused.hip).  Rows are [nt][id]
 // f32, id % 32 == 0; q/d/s as for launch_quantize.  With q == null the kernels
 // store the f32 values y instead of quantizing them (the unfused chain's steps).
@@ -55,6 +62,7 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h)
 __device__ __forceinline__ int dpp_quad_xor1(int v) { return __builtin_amdgcn_update_dpp(v, v, 0xB1, 0xF, 0xF, false); }
 __device__ __forceinline__ int dpp_quad_xor2(int v) { return __builtin_amdgcn_update_dpp(v, v, 0x4E, 0xF, 0xF, false); }
 __device__ __forceinline__ int dpp_half_mirror(int v) { return __builtin_amdgcn_update_dpp(v, v, 0x141, 0xF, 0xF, false); }
+__device__ __forceinline__ int dpp_row_mirror(int v) { return __builtin_amdgcn_update_dpp(v, v, 0x140, 0xF, 0xF, false); }
 
 __device__ __forceinline__ int sdot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
 

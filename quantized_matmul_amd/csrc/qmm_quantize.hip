@@ -41,6 +41,63 @@ __global__ __launch_bounds__(256) void quantize_q8_kernel(const float4* __restri
     }
 }
 
+// Q8_K activations ([GEMM, "Activations: int8 with a scale per 256"]): one f32
+// scale per 256 values and the sum of each 16-value group of codes, stored as
+// f32.  Same rules as above over 256 values.  One wave per 256-value block: lane l
+// holds values 4l .. 4l+3, the max runs over the whole wave (DPP inside rows of 16,
+// then two cross-row swaps), a 16-value group is one quad of lanes.
+__global__ __launch_bounds__(256) void quantize_q8k_kernel(const float4* __restrict__ x, int nblk,
+                                                           uint32_t* __restrict__ q, float* __restrict__ d,
+                                                           float* __restrict__ bsum)
+{
+    const int blk = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const bool valid = blk < nblk;
+    const long g = (long)min(blk, nblk - 1) * 64 + lane;  // in bounds for every lane
+    float4 v = x[g];
+    if (!valid)
+        v = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    int ai = __builtin_bit_cast(int, a);
+    ai = max(ai, dpp_quad_xor1(ai));
+    ai = max(ai, dpp_quad_xor2(ai));
+    ai = max(ai, dpp_half_mirror(ai));
+    ai = max(ai, dpp_row_mirror(ai));
+    ai = max(ai, __shfl_xor(ai, 16));
+    ai = max(ai, __shfl_xor(ai, 32));
+    const float dk = __builtin_bit_cast(float, ai) / 127.0f;
+    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+    if (dk != 0.0f) {
+        q0 = (int)roundf(v.x / dk);
+        q1 = (int)roundf(v.y / dk);
+        q2 = (int)roundf(v.z / dk);
+        q3 = (int)roundf(v.w / dk);
+    }
+    int sum = q0 + q1 + q2 + q3;
+    sum += dpp_quad_xor1(sum);
+    sum += dpp_quad_xor2(sum);
+    if (valid) {
+        q[g] = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
+               ((uint32_t)(q3 & 0xFF) << 24);
+        if (lane == 0)
+            d[blk] = dk;
+        if ((lane & 3) == 0)
+            bsum[(long)blk * 16 + (lane >> 2)] = (float)sum;
+    }
+}
+
+hipError_t launch_quantize_q8k(const float* x, int nt, int id, int8_t* q, float* d, float* bsum, hipStream_t st)
+{
+    const long nblk = (long)nt * id / kQK;
+    const int grid = (int)((nblk + 3) / 4);
+    if (grid == 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(quantize_q8k_kernel, dim3(grid), dim3(256), 0, st, reinterpret_cast<const float4*>(x),
+                       (int)nblk, reinterpret_cast<uint32_t*>(q), d, bsum);
+    return hipGetLastError();
+}
+
 hipError_t launch_quantize(const float* x, int nt, int id, int8_t* q, float* d, float* s,
                            hipStream_t st)
 {

@@ -1,0 +1,145 @@
+"""GPU parity of the Q8_K path (activations with one scale per 256 values), through
+the C ABI.
+
+Page: "The quantized GEMM" (mojo-dllm kernels page), "Activations: int8 with a
+scale per 256" and "The zero points do not touch the inner loop".
+
+* qmm_quantize_act_q8k: q, d and the 16-value group sums bit-exact against the
+  oracle (crafted blocks, ragged token counts, zero / subnormal / huge blocks, the
+  full prefill plane);
+* qmm_q8k_superblock_sums: the integer stage (sum_j sc_j * sum(q*qx) and
+  sum_j m_j * (bsum_2j + bsum_2j+1)) bit-exact against the oracle;
+* qmm_matmul_q8k: f32 outputs within |g - o| <= 1e-5 * max(|o|, A / sqrt(n))
+  of the oracle's f64 combine, over several tiles and ragged tails in every
+  dimension, one token, one super-block, long rows, and the benchmark's prefill
+  shapes on a sampled set of outputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests._parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+qmm = pytest.importorskip("quantized_matmul_amd")
+Q4 = qmm.QMM_TYPE_Q4_K
+DEV = "cuda:0"
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _up(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _same(a, b, what):
+    a, b = np.asarray(a), np.asarray(b)
+    assert a.shape == b.shape and a.dtype == b.dtype, what
+    if not np.array_equal(a.view(np.uint8), b.view(np.uint8)):
+        bad = np.argwhere(a.view(np.uint8).reshape(a.shape + (-1,)) != b.view(np.uint8).reshape(b.shape + (-1,)))
+        k = tuple(bad[0][:-1])
+        raise AssertionError(f"{what}: differs at {k}: {a[k]!r} vs {b[k]!r}")
+
+
+def _quant(x):
+    q, d, bs = qmm.qmm_quantize_act_q8k(_up(x))
+    torch.cuda.synchronize()
+    return q, d, bs
+
+
+QSHAPES = [(1, 256), (3, 1024), (7, 4096), (33, 2304), (512, 4096), (512, 12288)]
+
+
+@pytest.mark.parametrize("nt,idim", QSHAPES, ids=[f"{a}x{b}" for a, b in QSHAPES])
+def test_quantize_q8k_bit_exact(nt, idim):
+    _say(f"quantize_q8k nt={nt} id={idim}")
+    x = synth.activations(nt, idim, seed=1000 + nt + idim, outlier_frac=0.01)
+    ref = oracle.quantize_q8k(x)
+    got = [t.cpu().numpy() for t in _quant(x)]
+    for name, g, r in zip(("q", "d", "bsum"), got, ref):
+        _same(g, r, f"{nt}x{idim} {name}")
+
+
+def test_quantize_q8k_edge_blocks():
+    """Whole 256-blocks zero, with subnormal scale, near 1e30; and hand-made ties."""
+    nt, idim = 4, 2048
+    x = synth.activations(nt, idim, seed=1100).reshape(nt, idim // 256, 256)
+    x[:, 0] = 0.0
+    x[:, 1] *= np.float32(1e-39)
+    x[:, 2] *= np.float32(1e-3)
+    x[:, 3] *= np.float32(1e30)
+    x[0, 4] = np.where(np.arange(256) % 2 == 0, 2.5, -2.5)
+    x[0, 4, 0] = 127.0
+    x = np.ascontiguousarray(x.reshape(nt, idim), dtype=np.float32)
+    ref = oracle.quantize_q8k(x)
+    got = [t.cpu().numpy() for t in _quant(x)]
+    for name, g, r in zip(("q", "d", "bsum"), got, ref):
+        _same(g, r, f"edge {name}")
+    assert np.all(got[1][:, 0] == 0) and np.all(got[2][:, :16] == 0)
+    assert got[2][0, 64] == 124.0
+
+
+SHAPES = [(1, 1, 256), (5, 7, 512), (9, 100, 768), (64, 128, 1024), (70, 257, 2304), (130, 96, 4096),
+          (3, 4096, 4096), (200, 300, 256)]
+
+
+@pytest.mark.parametrize("nt,od,idim", SHAPES, ids=[f"{a}x{b}x{c}" for a, b, c in SHAPES])
+def test_q8k_superblock_sums_bit_exact(nt, od, idim):
+    _say(f"q8k integer stage nt={nt} od={od} id={idim}")
+    W = synth.weights(Q4, od, idim, seed=1200 + od)
+    x = synth.activations(nt, idim, seed=1300 + nt, outlier_frac=0.01)
+    q, d, bs = _quant(x)
+    S = qmm.qmm_q8k_superblock_sums(Q4, _up(W), q, d, bs, od)
+    torch.cuda.synchronize()
+    ref = oracle.q8k_superblock_sums(Q4, W, q.cpu().numpy(), bs.cpu().numpy(), od)
+    _same(S.cpu().numpy(), ref, "integer stage")
+
+
+@pytest.mark.parametrize("nt,od,idim", SHAPES, ids=[f"{a}x{b}x{c}" for a, b, c in SHAPES])
+def test_matmul_q8k_against_oracle(nt, od, idim):
+    _say(f"matmul_q8k nt={nt} od={od} id={idim}")
+    W = synth.weights(Q4, od, idim, seed=1400 + od)
+    x = synth.activations(nt, idim, seed=1500 + nt, outlier_frac=0.01)
+    q, d, bs = _quant(x)
+    out = qmm.qmm_matmul_q8k(Q4, _up(W), q, d, bs, od)
+    torch.cuda.synchronize()
+    ref, mag = oracle.matmul_q8k(Q4, W, q.cpu().numpy(), d.cpu().numpy(), bs.cpu().numpy(), od)
+    worst, rel = assert_close(out.cpu().numpy(), ref, mag, Q4, idim, f"{nt}x{od}x{idim}")
+    _say(f"  worst err/tol {worst:.3f}, max rel {rel:.2e}")
+
+
+@pytest.mark.parametrize("od,idim,nt", [(12288, 4096, 512), (4096, 12288, 512), (12288, 4096, 256),
+                                        (40, 65536, 17)])
+def test_matmul_q8k_full_size_sampled(od, idim, nt):
+    _say(f"matmul_q8k full size od={od} id={idim} nt={nt}")
+    W = synth.weights(Q4, od, idim, seed=1600 + od)
+    x = synth.activations(nt, idim, seed=1700 + nt, outlier_frac=0.01)
+    q, d, bs = _quant(x)
+    qn, dn, bn = q.cpu().numpy(), d.cpu().numpy(), bs.cpu().numpy()
+    ref_q = oracle.quantize_q8k(x)
+    for name, g, r in zip(("q", "d", "bsum"), (qn, dn, bn), ref_q):
+        _same(g, r, f"full-size quantize {name}")
+    out = qmm.qmm_matmul_q8k(Q4, _up(W), q, d, bs, od).cpu().numpy()
+    rng = np.random.default_rng(od + nt)
+    ts = np.unique(np.concatenate([rng.choice(nt, size=min(nt, 24), replace=False), [0, nt - 1]]))
+    rs = np.unique(np.concatenate([rng.choice(od, size=min(od, 160), replace=False), [0, od - 1]]))
+    tt, rr = np.meshgrid(ts, rs, indexing="ij")
+    tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
+    ref, mag = oracle.matmul_q8k_points(Q4, W, qn, dn, bn, od, tt, rr)
+    worst, rel = assert_close(out[tt, rr], ref, mag, Q4, idim, f"full size {od}x{idim} nt={nt}")
+    _say(f"  worst err/tol {worst:.3f}, max rel {rel:.2e}")
+
+
+def test_q8k_rejects_q6k():
+    W = torch.zeros(210, dtype=torch.uint8, device=DEV)
+    q, d, bs = _quant(synth.activations(1, 256, seed=1800))
+    with pytest.raises(qmm.QmmError) as e:
+        qmm.qmm_matmul_q8k(qmm.QMM_TYPE_Q6_K, W, q, d, bs, 1)
+    assert e.value.status == qmm.QMM_ERR_TYPE
