@@ -37,8 +37,13 @@ every fused call once and every chain once; inputs rotate over copies of more th
 1 GiB per shape.  value = HBM GB/s of the fused kernels at nt = 512 (algorithmic
 bytes over their summed launch times); roofline on silu_mul_quantize 512 x 12288.
 
+Workload "q8k_prefill": the two prefill shapes above on Q8_K activations (one scale
+per 256 values, 16-value code sums; its own numerics) and, on the same weights and
+inputs, on the per-32 activations.  value = int8 TOP/s of the Q8_K matmul kernel;
+per32_same_shapes gives the per-32 kernel's rate from the same process.
+
 Options: --gpus N (1 only), --steps K, --warmup W, --workload
-{q4k_decode_prefill, q6k_head, dllm_step, fused_quantize}, --no-cpu-baseline, --copy-calibration
+{q4k_decode_prefill, q6k_head, dllm_step, fused_quantize, q8k_prefill}, --no-cpu-baseline, --copy-calibration
 MIB (before warm-up, run five plain device copies of MIB MiB between two spin-kernel
 markers, for scaling the HBM counters of a profiled run).
 """
@@ -64,6 +69,7 @@ COPY_BYTES = 1 << 30           # weight copies per shape: at least 1 GiB
 CHUNK = 20                     # launches per event-timed chunk
 COUNTERS = os.path.join(ROOT, "profiles", "q4k_decode_prefill_hbm_counters.md")
 FUSED_COUNTERS = os.path.join(ROOT, "profiles", "fused_quantize_hbm_counters.md")
+Q8K_COUNTERS = os.path.join(ROOT, "profiles", "q8k_prefill_hbm_counters.md")
 
 
 def parse():
@@ -72,7 +78,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200, help="multiple of 20")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q4k_decode_prefill",
-                    choices=["q4k_decode_prefill", "q6k_head", "dllm_step", "fused_quantize"])
+                    choices=["q4k_decode_prefill", "q6k_head", "dllm_step", "fused_quantize", "q8k_prefill"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     return ap.parse_args()
@@ -96,6 +102,13 @@ def copy_calibration(torch, mib):
 MMQ_TILES = {3: (4, 2, 1), 4: (2, 2, 1), 5: (2, 2, 2)}   # tile kind -> (row waves, token waves, K groups)
 
 
+def q8k_tile(nt, od):
+    """1 for the 128 x 64 tile of the Q8_K kernel, 2 for 64 x 64 (the library's rule)."""
+    t42 = -(-nt // 64) * -(-od // 128)
+    t22 = -(-nt // 64) * -(-od // 64)
+    return 1 if -(-t42 // 256) <= -(-t22 // 512) else 2
+
+
 def mmq_kernel(qmm, nt, od, idim):
     """(kernel name, launch threads) of the Q4_K MMQ kernel the library runs for this
     shape: 32*WR rows x 32*WC tokens per workgroup, KS groups splitting K, the
@@ -108,9 +121,9 @@ def mmq_kernel(qmm, nt, od, idim):
 class Call:
     """One matmul of the step: weights (rotating copies), activations, buffers."""
 
-    def __init__(self, torch, qmm, qtype, od, idim, nt, seed, outliers, copies=None, label="", x=None):
-        self.qtype, self.od, self.idim, self.nt = qtype, od, idim, nt
-        self.label = label or f"{'Q4_K' if qtype == 1 else 'Q6_K'} {od}x{idim} nt={nt}"
+    def __init__(self, torch, qmm, qtype, od, idim, nt, seed, outliers, copies=None, label="", x=None, q8k=False):
+        self.qtype, self.od, self.idim, self.nt, self.q8k = qtype, od, idim, nt, q8k
+        self.label = label or f"{'Q4_K' if qtype == 1 else 'Q6_K'} {od}x{idim} nt={nt}" + (" Q8_K" if q8k else "")
         dev = torch.device("cuda:0")
         if copies is None:
             w = torch.from_numpy(synth.weights(qtype, od, idim, seed=seed)).to(dev)
@@ -125,10 +138,11 @@ class Call:
         self.d = torch.empty((nt, idim // 32), dtype=torch.float32, device=dev)
         self.s = torch.empty((nt, idim // 32), dtype=torch.float32, device=dev)
         self.out = torch.empty((nt, od), dtype=torch.float32, device=dev)
-        self.kind = qmm.qmm_dispatch_kind(qtype, nt, od, idim)
+        self.kind = qmm.QMM_KIND_MMQ if q8k else qmm.qmm_dispatch_kind(qtype, nt, od, idim)
         self.wbytes = qmm.qmm_weight_bytes(qtype, od, idim)
-        # algorithmic bytes of the matmul kernel: weights + q8 activations + output
-        self.kbytes = self.wbytes + nt * idim * (1 + 8 / 32) + nt * od * 4
+        # algorithmic bytes of the matmul kernel: weights + quantized activations + output
+        act = nt * idim * ((1 + 4 / 256 + 4 / 16) if q8k else (1 + 8 / 32))
+        self.kbytes = self.wbytes + act + nt * od * 4
         self.ops = 2.0 * nt * od * idim
         self.k_ms = []   # matmul kernel time per launch, one entry per timed chunk
         self.q_ms = []   # quantize kernel time per launch, one entry per timed chunk
@@ -137,21 +151,26 @@ class Call:
         P, I = ctypes.c_void_p, ctypes.c_int
         st = P(torch.cuda.current_stream().cuda_stream)
         self.L = qmm.lib()
+        if q8k:  # Q8_K activations: d per 256 values, group sums per 16 (in self.s)
+            self.d = torch.empty((nt, idim // 256), dtype=torch.float32, device=dev)
+            self.s = torch.empty((nt, idim // 16), dtype=torch.float32, device=dev)
+        self.qfn = self.L.qmm_quantize_act_q8k if q8k else self.L.qmm_quantize_act
+        self.mfn = self.L.qmm_matmul_q8k if q8k else self.L.qmm_matmul_q8
         self.qargs = (P(self.x.data_ptr()), I(nt), I(idim), P(self.q.data_ptr()), P(self.d.data_ptr()),
                       P(self.s.data_ptr()), st)
         self.margs = [(I(qtype), P(w.data_ptr()), P(self.q.data_ptr()), P(self.d.data_ptr()),
                        P(self.s.data_ptr()), I(nt), I(od), I(idim), P(self.out.data_ptr()), st) for w in self.W]
 
     def quantize(self):
-        rc = self.L.qmm_quantize_act(*self.qargs)
+        rc = self.qfn(*self.qargs)
         if rc:
-            raise RuntimeError(f"qmm_quantize_act failed: {rc}")
+            raise RuntimeError(f"quantize failed: {rc}")
 
     def matmul(self):
-        rc = self.L.qmm_matmul_q8(*self.margs[self.i % len(self.margs)])
+        rc = self.mfn(*self.margs[self.i % len(self.margs)])
         self.i += 1
         if rc:
-            raise RuntimeError(f"qmm_matmul_q8 failed: {rc}")
+            raise RuntimeError(f"matmul failed: {rc}")
 
     def run(self):
         self.quantize()
@@ -171,6 +190,13 @@ def build_calls(torch, qmm, workload):
                 calls.append(c)
         calls.append(Call(torch, qmm, Q4, 12288, 4096, 512, seed=7, outliers=True, copies=shared[(12288, 4096)]))
         calls.append(Call(torch, qmm, Q4, 4096, 12288, 512, seed=8, outliers=True))
+    elif workload == "q8k_prefill":
+        # the prefill shapes on both activation schemes, same weights and inputs
+        for od, idim, seed in ((12288, 4096, 7), (4096, 12288, 8)):
+            per32 = Call(torch, qmm, Q4, od, idim, 512, seed=seed, outliers=True)
+            calls.append(per32)
+            calls.append(Call(torch, qmm, Q4, od, idim, 512, seed=seed, outliers=True, copies=per32.W, x=per32.x,
+                              q8k=True))
     elif workload == "q6k_head":
         calls.append(Call(torch, qmm, Q6, 32000, 4096, 1, seed=3, outliers=False))
     else:  # dllm_step: 32 layers x (q, k, v, o, gate, up Q4_K; down Q6_K) at L = 256
@@ -398,7 +424,7 @@ def cpu_baseline(calls):
                    sample=f"quantize + matmul of every nt=1 call ({', '.join(c.label for c in dec)}), "
                           f"repeated {reps}x, {t_total:.1f} s")
     if big:
-        c = big[0]
+        c = next((b for b in big if b.q8k), big[0])  # the Q8_K oracle where the workload runs Q8_K
         rows = 1024 if c.nt >= 512 else 2048
         bpr = c.wbytes // c.od
         W = synth.weights(c.qtype, c.od, c.idim, seed=7)[: rows * bpr]
@@ -406,7 +432,10 @@ def cpu_baseline(calls):
         ops, t_total, reps = 0.0, 0.0, 0
         while t_total < 5.0:
             t0 = time.perf_counter()
-            oracle.matmul(c.qtype, W, x, rows)
+            if c.q8k:
+                oracle.matmul_q8k(c.qtype, W, *oracle.quantize_q8k(x), rows)
+            else:
+                oracle.matmul(c.qtype, W, x, rows)
             t_total += time.perf_counter() - t0
             ops += 2.0 * c.nt * rows * c.idim
             reps += 1
@@ -537,6 +566,28 @@ def main():
                           "mmvq": "Q4_K 4096x4096 and 12288x4096, nt=1,4,8",
                           "mmq": "Q4_K 12288x4096 and 4096x12288, nt=512, 1% outliers x20",
                           "weight_copies_bytes_per_shape": COPY_BYTES}
+    elif args.workload == "q8k_prefill":
+        q8 = [c for c in calls if c.q8k]
+        p32 = [c for c in calls if not c.q8k]
+        ops = sum(c.ops for c in q8)
+        t8 = sum(float(np.mean(c.k_ms)) * 1e-3 for c in q8)
+        t32 = sum(float(np.mean(c.k_ms)) * 1e-3 for c in p32)
+        line.update(metric="Q4_K x Q8_K activations matmul: int8 TOP/s at nt=512 (% of roofline)",
+                    value=round(ops / t8 / 1e12, 2), unit="TOP/s")
+        m = max(q8, key=lambda c: float(np.mean(c.k_ms)))
+        km = float(np.mean(m.k_ms)) * 1e-3
+        wr, wc = (4, 2) if q8k_tile(m.nt, m.od) == 1 else (2, 2)
+        kname = f"qmm::mmq_q4k_q8k_kernel<{wr}, {wc}, false>"
+        tiles = -(-m.nt // (32 * wc)) * -(-m.od // (32 * wr))
+        line["roofline"] = {"bound": "mfma", "achieved": round(m.ops / km / 1e12, 2), "peak": INT8_PEAK_TOPS,
+                            "unit": "TFLOP/s", "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4),
+                            "traffic": read_traffic(Q8K_COUNTERS, kname, 8 * -(-tiles // 8) * 64 * wr * wc),
+                            "kernel": kname.replace("qmm::", "").replace(" ", ""), "call": m.label,
+                            "ops_per_launch": int(m.ops)}
+        line["per32_same_shapes"] = {"value": round(sum(c.ops for c in p32) / t32 / 1e12, 2), "unit": "TOP/s",
+                                     "speedup_q8k": round(t32 / t8, 3)}
+        line["config"] = {"workload": "q8k_prefill", "shapes": "Q4_K 12288x4096 and 4096x12288, nt=512, "
+                          "1% outliers x20", "activations": "Q8_K (one scale per 256) vs per-32"}
     elif args.workload == "q6k_head":
         c = dec[0]
         k = float(np.mean(c.k_ms)) * 1e-3

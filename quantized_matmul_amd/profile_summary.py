@@ -33,7 +33,8 @@ _CSRC = os.path.join(_HERE, "csrc")
 # library kernel (name prefix) -> sources it is compiled from
 KERNEL_SOURCES = {
     "qmm::mmvq_": ("qmm_mmvq.hip", "qmm_internal.h"),
-    "qmm::mmq_": ("qmm_mmq.hip", "qmm_internal.h"),
+    "qmm::mmq_": ("qmm_mmq.hip", "qmm_mmq_common.h", "qmm_internal.h"),
+    "qmm::mmq_q4k_q8k_": ("qmm_mmq_q8k.hip", "qmm_mmq_common.h", "qmm_internal.h"),
     "qmm::quantize_": ("qmm_quantize.hip", "qmm_internal.h"),
     "qmm::{anonymous}::rmsnorm_": ("qmm_fused.hip", "qmm_internal.h"),
     "qmm::{anonymous}::silu_mul_": ("qmm_fused.hip", "qmm_internal.h"),
@@ -44,14 +45,14 @@ KERNEL_SOURCES = {
 def sources_sha256(kernel_name: str):
     """SHA-256 over the source files of a library kernel, or None for other kernels."""
     short = kernel_name.replace("void ", "")
-    for prefix, files in KERNEL_SOURCES.items():
-        if short.startswith(prefix):
-            h = hashlib.sha256()
-            for f in files:
-                with open(os.path.join(_CSRC, f), "rb") as fh:
-                    h.update(fh.read())
-            return h.hexdigest()
-    return None
+    match = [p for p in KERNEL_SOURCES if short.startswith(p)]
+    if not match:
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[max(match, key=len)]:  # the most specific prefix
+        with open(os.path.join(_CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def short_name(name: str) -> str:
