@@ -18,6 +18,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 TYPE_Q4_K = 1
 TYPE_Q6_K = 2
+TYPE_Q6_K_P224 = 3   # Q6_K blocks padded to 224 bytes
 
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-std=c11"]
 

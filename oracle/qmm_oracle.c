@@ -60,6 +60,10 @@
 
 #define OQ_TYPE_Q4_K 1
 #define OQ_TYPE_Q6_K 2
+/* Q6_K stored with each 210-byte block padded to 224 bytes ([GEMM, "The GPU path",
+ * "Weights stay in GGUF blocks"]: the upload pads each Q6_K block so every 16-byte
+ * piece is aligned).  The first 210 bytes are the block; the pad is ignored. */
+#define OQ_TYPE_Q6_K_P224 3
 
 /* f16 bits -> f64, exact (normal, subnormal, zero; inf/nan kept as such). */
 static double f16_bits_to_f64(uint16_t h)
@@ -335,14 +339,18 @@ static int32_t dot_q6k_group(const q6k_block* w, const int8_t* qx, int g)
     return acc;
 }
 
-static size_t blk_bytes(int type) { return type == OQ_TYPE_Q4_K ? 144 : 210; }
+static size_t blk_bytes(int type) { return type == OQ_TYPE_Q4_K ? 144 : type == OQ_TYPE_Q6_K ? 210 : 224; }
+static int known_type(int type)
+{
+    return type == OQ_TYPE_Q4_K || type == OQ_TYPE_Q6_K || type == OQ_TYPE_Q6_K_P224;
+}
 
 int oracle_subblock_dots(int type, const uint8_t* W, const int8_t* q, int nt, int od, int id,
                          int32_t* S)
 {
     if (!W || !q || !S || nt < 0 || od < 0 || id < 0 || id % 256)
         return -1;
-    if (type != OQ_TYPE_Q4_K && type != OQ_TYPE_Q6_K)
+    if (!known_type(type))
         return -2;
     int nsb = id / 256;
     int ng = type == OQ_TYPE_Q4_K ? 8 : 16;
@@ -425,7 +433,7 @@ int oracle_matmul_q8(int type, const uint8_t* W, const int8_t* q, const float* d
 {
     if (!W || !q || !d || !s || !out || nt < 0 || od < 0 || id < 0 || id % 256)
         return -1;
-    if (type != OQ_TYPE_Q4_K && type != OQ_TYPE_Q6_K)
+    if (!known_type(type))
         return -2;
     int nsb = id / 256;
     size_t row_bytes = (size_t)nsb * blk_bytes(type);
@@ -539,7 +547,7 @@ int oracle_matmul_q8k(int type, const uint8_t* W, const int8_t* q, const float* 
 {
     if (!W || !q || !d || !bsum || !out || nt < 0 || od < 0 || id < 0 || id % 256)
         return -1;
-    if (type != OQ_TYPE_Q4_K && type != OQ_TYPE_Q6_K)
+    if (!known_type(type))
         return -2;
     int nsb = id / 256;
     size_t row_bytes = (size_t)nsb * blk_bytes(type);
@@ -564,7 +572,7 @@ int oracle_q8k_superblock_sums(int type, const uint8_t* W, const int8_t* q, cons
 {
     if (!W || !q || !bsum || !S || nt < 0 || od < 0 || id < 0 || id % 256)
         return -1;
-    if (type != OQ_TYPE_Q4_K && type != OQ_TYPE_Q6_K)
+    if (!known_type(type))
         return -2;
     int nsb = id / 256;
     size_t bb = blk_bytes(type);
@@ -607,7 +615,7 @@ int oracle_matmul_q8k_points(int type, const uint8_t* W, const int8_t* q, const 
 {
     if (!W || !q || !d || !bsum || !out || !t_idx || !r_idx || nt < 0 || od < 0 || id < 0 || id % 256 || n < 0)
         return -1;
-    if (type != OQ_TYPE_Q4_K && type != OQ_TYPE_Q6_K)
+    if (!known_type(type))
         return -2;
     int nsb = id / 256;
     size_t row_bytes = (size_t)nsb * blk_bytes(type);
@@ -633,7 +641,7 @@ int oracle_matmul_q8_points(int type, const uint8_t* W, const int8_t* q, const f
 {
     if (!W || !q || !d || !s || !out || !t_idx || !r_idx || id % 256 || npts < 0)
         return -1;
-    if (type != OQ_TYPE_Q4_K && type != OQ_TYPE_Q6_K)
+    if (!known_type(type))
         return -2;
     int nsb = id / 256;
     size_t row_bytes = (size_t)nsb * blk_bytes(type);
@@ -674,7 +682,7 @@ int oracle_decode_block(int type, const uint8_t* B, double* d, double* dmin, int
         memcpy(codes, w.q, sizeof w.q);
         return 0;
     }
-    if (type == OQ_TYPE_Q6_K) {
+    if (type == OQ_TYPE_Q6_K || type == OQ_TYPE_Q6_K_P224) {
         q6k_block w;
         q6k_decode(B, &w);
         *d = w.d;

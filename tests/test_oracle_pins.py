@@ -342,3 +342,35 @@ def test_planted_mistakes_are_caught(mutation, tmp_path):
     assert failures, f"mutation {mutation} passed every pin"
     # and the real oracle passes all of them
     assert all(p() is None for p in ALL_PINS)
+
+
+def _pad_q6k(W, fill):
+    """210-byte Q6_K blocks to 224-byte blocks, the 14 pad bytes set to `fill`."""
+    b = np.ascontiguousarray(W, dtype=np.uint8).reshape(-1, 210)
+    out = np.full((b.shape[0], 224), fill, np.uint8)
+    out[:, :210] = b
+    return out.reshape(-1)
+
+
+def test_q6k_padded_blocks_equal_unpadded():
+    """Q6_K with blocks padded to 224 bytes ("The quantized GEMM", The GPU path:
+    the upload pads each Q6_K block so every 16-byte piece is aligned) is the same
+    matrix: every oracle entry point gives identical results, whatever the pad
+    bytes hold (a wrong block stride or a pad read as data changes them)."""
+    od, idim, nt = 5, 768, 3
+    W = synth.weights(Q6, od, idim, seed=61)
+    Wp = _pad_q6k(W, 0xA7)
+    P6 = oracle.TYPE_Q6_K_P224
+    x = synth.activations(nt, idim, seed=62, outlier_frac=0.02)
+    o, m, (q, d, s) = oracle.matmul(Q6, W, x, od)
+    op, mp, _ = oracle.matmul(P6, Wp, x, od)
+    assert np.array_equal(o, op) and np.array_equal(m, mp)
+    assert np.array_equal(oracle.subblock_dots(Q6, W, q, od), oracle.subblock_dots(P6, Wp, q, od))
+    q8, d8, b8 = oracle.quantize_q8k(x)
+    assert np.array_equal(oracle.matmul_q8k(Q6, W, q8, d8, b8, od)[0], oracle.matmul_q8k(P6, Wp, q8, d8, b8, od)[0])
+    t = np.array([0, 2], np.int32)
+    r = np.array([4, 1], np.int32)
+    assert np.array_equal(oracle.matmul_q8_points(P6, Wp, q, d, s, od, t, r)[0], o[t, r])
+    dec = oracle.decode_block(P6, Wp[224:448])
+    ref = oracle.decode_block(Q6, W[210:420])
+    assert dec["d"] == ref["d"] and np.array_equal(dec["codes"], ref["codes"]) and np.array_equal(dec["sc"], ref["sc"])
