@@ -56,7 +56,13 @@ enum {
      * 16 int8 scales (one per 16 weights) | f16 d.  w = d*sc*(q6 - 32).  The
      * element-to-bit map inside the two planes is the public GGUF arrangement
      * (two halves of 128 elements), a reading the pages leave open. */
-    QMM_TYPE_Q6_K = 2
+    QMM_TYPE_Q6_K = 2,
+    /* [GEMM, "The GPU path", "Weights stay in GGUF blocks"]: Q6_K with each
+     * 210-byte block padded to 224 bytes at upload, so every 16-byte piece of a
+     * block is aligned and the kernels read it with 16-byte loads.  Bytes 0..209
+     * of a padded block are the Q6_K block; bytes 210..223 are ignored.
+     * qmm_pad_q6k makes this layout from QMM_TYPE_Q6_K. */
+    QMM_TYPE_Q6_K_P224 = 3
 };
 
 /* Status codes. */
@@ -81,9 +87,15 @@ enum {
     QMM_KIND_MMQ_64X64_SPLITK = 5   /* 64 x 64, 8 waves in two groups splitting K */
 };
 
-/* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K) or *210
- * (Q6_K).  0 for an unknown type or a bad shape. */
+/* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K), *210
+ * (Q6_K) or *224 (Q6_K padded).  0 for an unknown type or a bad shape. */
 size_t qmm_weight_bytes(int type, int od, int id);
+
+/* Upload-time repack: nblocks Q6_K blocks of 210 bytes (src, any alignment) to
+ * the padded layout of QMM_TYPE_Q6_K_P224 (dst, 224 bytes per block, 16-byte
+ * aligned; pad bytes written as zero).  src and dst must not overlap; device
+ * pointers; nblocks >= 1 and nblocks * 224 < 2^40 (else QMM_ERR_SHAPE). */
+int qmm_pad_q6k(const void* src, void* dst, long long nblocks, void* stream);
 
 /* Workspace bytes qmm_matmul needs for nt tokens of id values: the q8 plane
  * (nt*id int8, rounded up to 256 B) then d and s (nt*id/32 f32 each, each rounded

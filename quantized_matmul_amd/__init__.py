@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libqmm.so")
 
 QMM_TYPE_Q4_K = 1
 QMM_TYPE_Q6_K = 2
+QMM_TYPE_Q6_K_P224 = 3   # Q6_K blocks padded to 224 bytes (qmm_pad_q6k)
 QMM_KIND_MMVQ = 1
 QMM_KIND_MMQ = 2
 QMM_KIND_MMQ_128X64 = 3
@@ -36,13 +37,13 @@ QMM_ERR_WORKSPACE = -5
 QMM_ERR_DEVICE = -6
 QMM_ERR_LAUNCH = -7
 
-BLOCK_BYTES = {QMM_TYPE_Q4_K: 144, QMM_TYPE_Q6_K: 210}
+BLOCK_BYTES = {QMM_TYPE_Q4_K: 144, QMM_TYPE_Q6_K: 210, QMM_TYPE_Q6_K_P224: 224}
 
 EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8",
            "qmm_matmul_q8_kind", "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots",
            "qmm_mfma_tile_check", "qmm_strerror", "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize",
            "qmm_silu_mul_quantize", "qmm_residual_add", "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k",
-           "qmm_matmul_q8k", "qmm_q8k_superblock_sums")
+           "qmm_matmul_q8k", "qmm_q8k_superblock_sums", "qmm_pad_q6k")
 
 
 class QmmError(RuntimeError):
@@ -86,13 +87,14 @@ def lib():
         L.qmm_quantize_act_q8k.argtypes = [P, I, I, P, P, P, P]
         L.qmm_matmul_q8k.argtypes = [I, P, P, P, P, I, I, I, P, P]
         L.qmm_q8k_superblock_sums.argtypes = [I, P, P, P, P, I, I, I, P, P]
+        L.qmm_pad_q6k.argtypes = [P, P, ctypes.c_longlong, P]
         L.qmm_strerror.argtypes = [I]
         L.qmm_strerror.restype = ctypes.c_char_p
         for f in ("qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8", "qmm_matmul_q8_kind",
                   "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots", "qmm_mfma_tile_check",
                   "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize", "qmm_silu_mul_quantize", "qmm_residual_add",
                   "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k", "qmm_matmul_q8k",
-                  "qmm_q8k_superblock_sums"):
+                  "qmm_q8k_superblock_sums", "qmm_pad_q6k"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -167,6 +169,19 @@ def qmm_quantize_act(x: torch.Tensor, q=None, d=None, s=None, stream=None):
                                   _dev(d, torch.float32, "d"), _dev(s, torch.float32, "s"), _stream(stream)),
            "qmm_quantize_act")
     return q, d, s
+
+
+def qmm_pad_q6k(W: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """Q6_K weights (uint8, 210 bytes per block) -> the padded layout of
+    QMM_TYPE_Q6_K_P224 (224 bytes per block, pad bytes zero)."""
+    if W.numel() % 210:
+        raise ValueError("W must hold whole 210-byte Q6_K blocks")
+    nb = W.numel() // 210
+    if out is None:
+        out = torch.empty(nb * 224, dtype=torch.uint8, device=W.device)
+    _check(lib().qmm_pad_q6k(_dev(W, torch.uint8, "W"), _dev(out, torch.uint8, "out"), nb, _stream(stream)),
+           "qmm_pad_q6k")
+    return out
 
 
 def qmm_quantize_act_q8k(x: torch.Tensor, q=None, d=None, bsum=None, stream=None):

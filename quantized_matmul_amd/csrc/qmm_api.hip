@@ -40,7 +40,34 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-int check_type(int type) { return (type == QMM_TYPE_Q4_K || type == QMM_TYPE_Q6_K) ? QMM_OK : QMM_ERR_TYPE; }
+int check_type(int type)
+{
+    return (type == QMM_TYPE_Q4_K || type == QMM_TYPE_Q6_K || type == QMM_TYPE_Q6_K_P224) ? QMM_OK : QMM_ERR_TYPE;
+}
+
+size_t block_bytes(int type)
+{
+    return type == QMM_TYPE_Q4_K ? qmm::kQ4KBytes : type == QMM_TYPE_Q6_K ? qmm::kQ6KBytes : qmm::kQ6KP224Bytes;
+}
+
+// One thread per 16-byte piece of a padded block (14 per block): bytes of the
+// 210-byte source block, zero past byte 209.
+__global__ __launch_bounds__(256) void pad_q6k_kernel(const uint8_t* __restrict__ src, uint4* __restrict__ dst,
+                                                      long long npieces)
+{
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= npieces)
+        return;
+    const long long b = i / 14;
+    const int p = (int)(i - b * 14);
+    const uint8_t* s = src + b * qmm::kQ6KBytes + 16 * p;
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        if (16 * p + k < qmm::kQ6KBytes)
+            w[k >> 2] |= (uint32_t)s[k] << (8 * (k & 3));
+    dst[i] = make_uint4(w[0], w[1], w[2], w[3]);
+}
 
 // Shape rule shared by the matmul entry points.
 int check_shape(int nt, int od, int id)
@@ -131,7 +158,7 @@ size_t qmm_weight_bytes(int type, int od, int id)
 {
     if (check_type(type) || od < 1 || id < 256 || id % 256)
         return 0;
-    return (size_t)od * (size_t)(id / 256) * (type == QMM_TYPE_Q4_K ? qmm::kQ4KBytes : qmm::kQ6KBytes);
+    return (size_t)od * (size_t)(id / 256) * block_bytes(type);
 }
 
 size_t qmm_act_bytes(int nt, int id)
@@ -297,6 +324,27 @@ int qmm_q8k_superblock_sums(int type, const void* W, const int8_t* q, const floa
     if (!S)
         return QMM_ERR_ARG;
     return q8k_checked(type, W, q, d, bsum, nt, od, id, nullptr, S, stream);
+}
+
+int qmm_pad_q6k(const void* src, void* dst, long long nblocks, void* stream)
+{
+    if (!src || !dst)
+        return QMM_ERR_ARG;
+    if (nblocks < 1 || nblocks > (1LL << 40) / qmm::kQ6KP224Bytes)
+        return QMM_ERR_SHAPE;
+    if (!aligned16(dst))
+        return QMM_ERR_ALIGN;
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+    if (s0 < d0 + (uintptr_t)nblocks * qmm::kQ6KP224Bytes && d0 < s0 + (uintptr_t)nblocks * qmm::kQ6KBytes)
+        return QMM_ERR_ARG;  // overlap
+    int rc = check_device();
+    if (rc)
+        return rc;
+    const long long np = nblocks * 14;
+    hipLaunchKernelGGL(pad_q6k_kernel, dim3((unsigned)((np + 255) / 256)), dim3(256), 0,
+                       reinterpret_cast<hipStream_t>(stream), reinterpret_cast<const uint8_t*>(src),
+                       reinterpret_cast<uint4*>(dst), np);
+    return launched(hipGetLastError());
 }
 
 int qmm_nt_switch(void) { return nt_switch_value(); }

@@ -16,6 +16,7 @@ namespace qmm {
 constexpr int kQK = 256;          // weights per super-block
 constexpr int kQ4KBytes = 144;    // Q4_K super-block
 constexpr int kQ6KBytes = 210;    // Q6_K super-block
+constexpr int kQ6KP224Bytes = 224;  // Q6_K super-block padded to 16-byte alignment (weight type 3)
 constexpr int kActBlock = 32;     // activation values per scale
 
 // Launchers (return hipError_t of the launch).  All pointers are device

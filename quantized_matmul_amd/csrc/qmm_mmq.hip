@@ -384,7 +384,7 @@ struct __attribute__((aligned(16))) Q6Smem {
     float xd[8 * BN];
 };
 
-template <int BM, int BN, int NTH, int WC8, int XC, int SC>
+template <int BM, int BN, int NTH, int WC8, int XC, int SC, bool PAD>
 __device__ __forceinline__ void q6_prefetch(uint32_t (&pl)[WC8][5], uint32_t (&phh)[WC8][5], uint32_t (&pshift)[WC8],
                                             v4i (&px)[XC], v4i (&ps)[SC], uint32_t (&psd)[WC8],
                                             const uint8_t* __restrict__ W, const int8_t* __restrict__ q,
@@ -397,16 +397,25 @@ __device__ __forceinline__ void q6_prefetch(uint32_t (&pl)[WC8][5], uint32_t (&p
         const int e = task<BM * 8, NTH, WC8>(tid + k * NTH);
         const int r = e >> 3, c = e & 7;
         const int h = c >> 2, jq = (c >> 1) & 1, half = c & 1;
-        const uint8_t* blk = W + (size_t)min(row0 + r, od - 1) * row_bytes + (size_t)sb * kQ6KBytes;
+        const uint8_t* blk =
+            W + (size_t)min(row0 + r, od - 1) * row_bytes + (size_t)sb * (PAD ? kQ6KP224Bytes : kQ6KBytes);
         const uintptr_t al = reinterpret_cast<uintptr_t>(blk + 64 * h + 32 * jq + 16 * half);
         const uintptr_t ah = reinterpret_cast<uintptr_t>(blk + 128 + 32 * h + 16 * half);
-        const uint32_t* wl = reinterpret_cast<const uint32_t*>(al & ~(uintptr_t)3);
-        const uint32_t* wh = reinterpret_cast<const uint32_t*>(ah & ~(uintptr_t)3);
-        pshift[k] = (uint32_t)(al & 3);  // same for both chunks
+        if constexpr (PAD) {
+            // 224-byte blocks: both chunks are 16-byte aligned, one load each
+            const uint4 l4 = *reinterpret_cast<const uint4*>(al), h4 = *reinterpret_cast<const uint4*>(ah);
+            pl[k][0] = l4.x, pl[k][1] = l4.y, pl[k][2] = l4.z, pl[k][3] = l4.w, pl[k][4] = 0;
+            phh[k][0] = h4.x, phh[k][1] = h4.y, phh[k][2] = h4.z, phh[k][3] = h4.w, phh[k][4] = 0;
+            pshift[k] = 0;
+        } else {
+            const uint32_t* wl = reinterpret_cast<const uint32_t*>(al & ~(uintptr_t)3);
+            const uint32_t* wh = reinterpret_cast<const uint32_t*>(ah & ~(uintptr_t)3);
+            pshift[k] = (uint32_t)(al & 3);  // same for both chunks
 #pragma unroll
-        for (int i = 0; i < 5; ++i) {
-            pl[k][i] = wl[i];
-            phh[k][i] = wh[i];
+            for (int i = 0; i < 5; ++i) {
+                pl[k][i] = wl[i];
+                phh[k][i] = wh[i];
+            }
         }
         // task c also stages group scales 2c and 2c+1 (two bytes, 2-byte aligned)
         // and reads d: low half the two int8 scales, high half the f16 d
@@ -482,7 +491,7 @@ __device__ __forceinline__ void q6_stage(Q6Smem<BM, BN>& sm, const uint32_t (&pl
     }
 }
 
-template <int WR, int WC, int KS, bool DUMP>
+template <int WR, int WC, int KS, bool DUMP, bool PAD>
 __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q6k_kernel(const uint8_t* __restrict__ W,
                                                                     const int8_t* __restrict__ q,
                                                                     const float* __restrict__ dx,
@@ -511,7 +520,7 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q6k_kernel(const uin
     const int nsb = id >> 8;
     const int nblk = id >> 5;
     const int niter = (nsb + KS - 1) / KS;
-    const size_t row_bytes = (size_t)nsb * kQ6KBytes;
+    const size_t row_bytes = (size_t)nsb * (PAD ? kQ6KP224Bytes : kQ6KBytes);
 
     // prefetch registers: per task the five-dword windows of a low and a high
     // chunk (2-byte aligned blocks), the two scale dwords and d
@@ -524,10 +533,10 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q6k_kernel(const uin
     const int btok = wc * 32 + li;
 
     // double-buffered LDS per K group, one barrier per iteration (as in the Q4_K kernel)
-    q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psd, W, q, dx, min(kg, nsb - 1), tid, row0, tok0,
+    q6_prefetch<BM, BN, NTH, WC8, XC, SC, PAD>(pl, phh, pshift, px, ps, psd, W, q, dx, min(kg, nsb - 1), tid, row0, tok0,
                                           nt, od, id, nblk, row_bytes);
     q6_stage<BM, BN, NTH, WC8, XC, SC>(smb[kg][0], pl, phh, pshift, px, ps, psd, tid, kg < nsb);
-    q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psd, W, q, dx, min(KS + kg, nsb - 1), tid, row0,
+    q6_prefetch<BM, BN, NTH, WC8, XC, SC, PAD>(pl, phh, pshift, px, ps, psd, W, q, dx, min(KS + kg, nsb - 1), tid, row0,
                                           tok0, nt, od, id, nblk, row_bytes);
     __syncthreads();
     for (int it = 0; it < niter; ++it) {
@@ -567,7 +576,7 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q6k_kernel(const uin
         }
         __builtin_amdgcn_sched_barrier(0);
         q6_stage<BM, BN, NTH, WC8, XC, SC>(smb[kg][(it + 1) & 1], pl, phh, pshift, px, ps, psd, tid, sb + KS < nsb);
-        q6_prefetch<BM, BN, NTH, WC8, XC, SC>(pl, phh, pshift, px, ps, psd, W, q, dx, min(sb + 2 * KS, nsb - 1), tid,
+        q6_prefetch<BM, BN, NTH, WC8, XC, SC, PAD>(pl, phh, pshift, px, ps, psd, W, q, dx, min(sb + 2 * KS, nsb - 1), tid,
                                               row0, tok0, nt, od, id, nblk, row_bytes);
         __syncthreads();
     }
@@ -640,9 +649,12 @@ static hipError_t launch_tile(int type, const uint8_t* W, const int8_t* q, const
     if (type == 1)
         hipLaunchKernelGGL((mmq_q4k_kernel<WR, WC, KS, DUMP>), dim3(grid), dim3(64 * WR * WC * KS), 0, st, W, q,
                            d, s, out, nt, od, id, S);
+    else if (type == 2)
+        hipLaunchKernelGGL((mmq_q6k_kernel<WR, WC, KS, DUMP, false>), dim3(grid), dim3(64 * WR * WC * KS), 0, st,
+                           W, q, d, out, nt, od, id, S);
     else
-        hipLaunchKernelGGL((mmq_q6k_kernel<WR, WC, KS, DUMP>), dim3(grid), dim3(64 * WR * WC * KS), 0, st, W, q,
-                           d, out, nt, od, id, S);
+        hipLaunchKernelGGL((mmq_q6k_kernel<WR, WC, KS, DUMP, true>), dim3(grid), dim3(64 * WR * WC * KS), 0, st,
+                           W, q, d, out, nt, od, id, S);
     return hipGetLastError();
 }
 

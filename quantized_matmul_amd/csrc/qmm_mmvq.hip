@@ -233,7 +233,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q4k_kernel(
 // (0..63) enter the integer dot and the offset 32 comes off afterwards as
 // 32 * sum(qx) of the group ([GEMM, "Weights: 8 rows per register"]: the offset
 // folds out through the activation sum), the sum being computed once per window.
-template <int NT, int R, bool DUMP>
+// PAD: blocks padded to 224 bytes ([GEMM, "The GPU path"]: every 16-byte piece
+// aligned), so each chunk is one 16-byte load.
+template <int NT, int R, bool DUMP, bool PAD>
 __global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q6k_kernel(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ q, const float* __restrict__ dx,
     float* __restrict__ out, int od, int id, int32_t* __restrict__ S, int wpr, int gpw)
@@ -253,7 +255,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q6k_kernel(
     const int nsb = id >> 8;
     const int nblk = id >> 5;
     const int nwin = (nsb + 7) >> 3;
-    const size_t row_bytes = (size_t)nsb * kQ6KBytes;
+    constexpr uint32_t BB = PAD ? kQ6KP224Bytes : kQ6KBytes;
+    const size_t row_bytes = (size_t)nsb * BB;
     const bool live = row0 < od;
 
     float acc[V];
@@ -265,25 +268,30 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q6k_kernel(
         const int b = 8 * w + g;
         const bool bv = b < nsb;
         const uint32_t bc = (uint32_t)(bv ? b : nsb - 1);
-        const uint32_t ob = bc * kQ6KBytes;
+        const uint32_t ob = bc * BB;
         uint4 ql[R], qh[R];
         int sc1[R], sc2[R];
         uint32_t dbits[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint8_t* rp = W + (size_t)min(row0 + r, od - 1) * row_bytes;
-            // rp's offset from a dword is uniform; the lane adds its block offset
-            const uint32_t res = (uint32_t)(reinterpret_cast<uintptr_t>(rp) & 3);
-            const uint8_t* rp4 = rp - res;
-            const uint32_t o = ob + res, o4 = o & ~3u, sh = o & 3u;
-            const uint32_t* pl = reinterpret_cast<const uint32_t*>(rp4 + o4 + f1);
-            const uint32_t* ph = reinterpret_cast<const uint32_t*>(rp4 + o4 + f2);
-            const uint32_t l0 = pl[0], l1 = pl[1], l2 = pl[2], l3 = pl[3], l4 = pl[4];
-            const uint32_t m0 = ph[0], m1 = ph[1], m2 = ph[2], m3 = ph[3], m4 = ph[4];
-            ql[r] = make_uint4(__builtin_amdgcn_alignbyte(l1, l0, sh), __builtin_amdgcn_alignbyte(l2, l1, sh),
-                               __builtin_amdgcn_alignbyte(l3, l2, sh), __builtin_amdgcn_alignbyte(l4, l3, sh));
-            qh[r] = make_uint4(__builtin_amdgcn_alignbyte(m1, m0, sh), __builtin_amdgcn_alignbyte(m2, m1, sh),
-                               __builtin_amdgcn_alignbyte(m3, m2, sh), __builtin_amdgcn_alignbyte(m4, m3, sh));
+            if constexpr (PAD) {
+                ql[r] = *reinterpret_cast<const uint4*>(rp + ob + f1);
+                qh[r] = *reinterpret_cast<const uint4*>(rp + ob + f2);
+            } else {
+                // rp's offset from a dword is uniform; the lane adds its block offset
+                const uint32_t res = (uint32_t)(reinterpret_cast<uintptr_t>(rp) & 3);
+                const uint8_t* rp4 = rp - res;
+                const uint32_t o = ob + res, o4 = o & ~3u, sh = o & 3u;
+                const uint32_t* pl = reinterpret_cast<const uint32_t*>(rp4 + o4 + f1);
+                const uint32_t* ph = reinterpret_cast<const uint32_t*>(rp4 + o4 + f2);
+                const uint32_t l0 = pl[0], l1 = pl[1], l2 = pl[2], l3 = pl[3], l4 = pl[4];
+                const uint32_t m0 = ph[0], m1 = ph[1], m2 = ph[2], m3 = ph[3], m4 = ph[4];
+                ql[r] = make_uint4(__builtin_amdgcn_alignbyte(l1, l0, sh), __builtin_amdgcn_alignbyte(l2, l1, sh),
+                                   __builtin_amdgcn_alignbyte(l3, l2, sh), __builtin_amdgcn_alignbyte(l4, l3, sh));
+                qh[r] = make_uint4(__builtin_amdgcn_alignbyte(m1, m0, sh), __builtin_amdgcn_alignbyte(m2, m1, sh),
+                                   __builtin_amdgcn_alignbyte(m3, m2, sh), __builtin_amdgcn_alignbyte(m4, m3, sh));
+            }
             sc1[r] = (int)reinterpret_cast<const int8_t*>(rp)[ob + 192 + g1];
             sc2[r] = (int)reinterpret_cast<const int8_t*>(rp)[ob + 192 + g2];
             dbits[r] = *reinterpret_cast<const uint16_t*>(rp + ob + 208);
@@ -377,8 +385,11 @@ static hipError_t launch_one(int type, const uint8_t* W, const int8_t* q, const 
     if (type == 1)
         hipLaunchKernelGGL((mmvq_q4k_kernel<NT, R, DUMP>), dim3(grid), block, 0, st, W, q, d, s, out, od, id,
                            S, wpr, gpw);
+    else if (type == 2)
+        hipLaunchKernelGGL((mmvq_q6k_kernel<NT, R, DUMP, false>), dim3(grid), block, 0, st, W, q, d, out, od, id, S,
+                           wpr, gpw);
     else
-        hipLaunchKernelGGL((mmvq_q6k_kernel<NT, R, DUMP>), dim3(grid), block, 0, st, W, q, d, out, od, id, S,
+        hipLaunchKernelGGL((mmvq_q6k_kernel<NT, R, DUMP, true>), dim3(grid), block, 0, st, W, q, d, out, od, id, S,
                            wpr, gpw);
     return hipGetLastError();
 }

@@ -7,7 +7,7 @@ REL_TOL = 1e-5
 
 
 def n_terms(qtype: int, idim: int) -> int:
-    """Scale-group terms per output: id/32 sub-blocks (Q4_K) or id/16 groups (Q6_K)."""
+    """Scale-group terms per output: id/32 sub-blocks (Q4_K) or id/16 groups (Q6_K, padded or not)."""
     return idim // 32 if qtype == 1 else idim // 16
 
 

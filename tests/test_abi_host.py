@@ -43,6 +43,7 @@ def test_weight_bytes_closed_forms():
             + 16 * qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q6_K, 4096, 12288)) // 210
     assert nblk == 6_217_728
     assert nblk * 12 == 74_612_736 and round(nblk * 12 / 2**20, 1) == 71.2
+    assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q6_K_P224, 32000, 4096) == 32000 * 16 * 224
     assert qmm.qmm_weight_bytes(7, 1, 256) == 0
     assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q4_K, 1, 300) == 0
 
@@ -119,6 +120,20 @@ def test_fused_steps_validation_before_device_work():
         assert L.qmm_residual_add(p, p, 1, 64, None) == D
         assert L.qmm_rmsnorm(p, p, E, 1, 64, p, None) == D
         assert L.qmm_silu_mul(p, p, 1, 64, p, None) == D
+
+
+def test_pad_q6k_validation():
+    L = qmm.lib()
+    p = ctypes.c_void_p(1 << 20)
+    far = ctypes.c_void_p(1 << 30)
+    assert L.qmm_pad_q6k(None, p, 1, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_pad_q6k(far, p, 0, None) == qmm.QMM_ERR_SHAPE
+    assert L.qmm_pad_q6k(far, ctypes.c_void_p((1 << 20) + 8), 1, None) == qmm.QMM_ERR_ALIGN
+    assert L.qmm_pad_q6k(ctypes.c_void_p((1 << 20) + 100), p, 4, None) == qmm.QMM_ERR_ARG   # overlap
+    import torch
+    if not torch.cuda.is_available():
+        assert L.qmm_pad_q6k(far, p, 4, None) == qmm.QMM_ERR_DEVICE
+        assert L.qmm_matmul_q8(qmm.QMM_TYPE_Q6_K_P224, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_DEVICE
 
 
 def test_no_device_is_an_error_not_a_fallback():
