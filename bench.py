@@ -603,7 +603,7 @@ def main():
                               "speedup_vs_unpadded": round(k / kp, 3)}
         line["roofline"] = {"bound": "hbm", "achieved": line["value"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(line["value"] / HBM_PEAK_GBS, 4), "traffic": None,
-                            "kernel": "mmvq_q6k_kernel<1,4,false>", "bytes_per_launch": int(c.kbytes)}
+                            "kernel": "mmvq_q6k_kernel<1,4,false,false>", "bytes_per_launch": int(c.kbytes)}
         line["config"] = {"workload": "q6k_head", "shape": "Q6_K 32000x4096 nt=1"}
     else:
         ops = sum(c.ops for c in calls)
