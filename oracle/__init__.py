@@ -19,6 +19,8 @@ LIB = os.path.join(HERE, "liboracle.so")
 TYPE_Q4_K = 1
 TYPE_Q6_K = 2
 TYPE_Q6_K_P224 = 3   # Q6_K blocks padded to 224 bytes
+TYPE_Q4_0 = 4        # 18-byte blocks of 32 weights
+TYPE_Q8_0 = 5        # 34-byte blocks of 32 weights
 
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-std=c11"]
 
@@ -55,12 +57,14 @@ def _bind(path: str):
     L.oracle_matmul_q8k.argtypes = [I, P, P, P, P, I, I, I, P, P]
     L.oracle_matmul_q8k_points.argtypes = [I, P, P, P, P, I, I, I, I, P, P, P, P]
     L.oracle_q8k_superblock_sums.argtypes = [I, P, P, P, I, I, I, P]
+    L.oracle_decode_group32.argtypes = [I, P, P, P]
     L.oracle_num_threads.restype = I
     L.oracle_set_num_threads.argtypes = [I]
     for f in ("oracle_quantize", "oracle_subblock_dots", "oracle_matmul_q8",
               "oracle_matmul_q8_points", "oracle_matmul", "oracle_decode_block",
               "oracle_rmsnorm", "oracle_add_rmsnorm", "oracle_silu_mul", "oracle_quantize_q8k",
-              "oracle_matmul_q8k", "oracle_matmul_q8k_points", "oracle_q8k_superblock_sums"):
+              "oracle_matmul_q8k", "oracle_matmul_q8k_points", "oracle_q8k_superblock_sums",
+              "oracle_decode_group32"):
         getattr(L, f).restype = I
     return L
 
@@ -124,7 +128,7 @@ def subblock_dots(qtype: int, W: np.ndarray, q: np.ndarray, od: int):
     """Integer dot per scale group: [nt][od][id/256][8 (Q4_K) or 16 (Q6_K)] int32."""
     q = np.ascontiguousarray(q, dtype=np.int8)
     nt, idim = q.shape
-    ng = 8 if qtype == TYPE_Q4_K else 16
+    ng = 16 if qtype in (TYPE_Q6_K, TYPE_Q6_K_P224) else 8
     S = np.empty((nt, od, idim // 256, ng), np.int32)
     W = np.ascontiguousarray(W, dtype=np.uint8)
     _check(lib().oracle_subblock_dots(qtype, _p(W), _p(q), nt, od, idim, _p(S)), "oracle_subblock_dots")
@@ -279,6 +283,15 @@ def q8k_superblock_sums(qtype: int, W: np.ndarray, q, bsum, od: int):
     _check(lib().oracle_q8k_superblock_sums(qtype, _p(W), _p(q), _p(bsum), nt, od, idim, _p(S)),
            "oracle_q8k_superblock_sums")
     return S
+
+
+def decode_group32(qtype: int, group: np.ndarray):
+    """Eight 32-weight blocks (Q4_0 or Q8_0): (d [8] f64, centred codes [256] int32)."""
+    g = np.ascontiguousarray(group, dtype=np.uint8)
+    d = np.zeros(8, np.float64)
+    codes = np.zeros(256, np.int32)
+    _check(lib().oracle_decode_group32(qtype, _p(g), _p(d), _p(codes)), "oracle_decode_group32")
+    return d, codes
 
 
 def num_threads() -> int:

@@ -34,6 +34,10 @@
  *   R18 silu(g) * u evaluated in f64 as (g / (1 + exp(-g))) * u and rounded once
  *       to f32 (the value the quantizer then reads).
  *
+ *   R20 Q8_0 block: f16 d then 32 int8 codes, w = d * q (the pages give the
+ *       34-byte size only; the public GGUF layout).
+ *   R21 Q4_0 / Q8_0 rows are read in groups of eight blocks (256 weights); a row
+ *       length must be a multiple of 256 like the K-quants.
  *   R19 Q8_K activations: the per-32 rules R2/R3 applied to blocks of 256
  *       (d = amax / 127, q = roundf(x / d), zero block -> 0); the 16-value group
  *       sums are the exact integer sums of the codes, stored as f32.
@@ -45,7 +49,9 @@
  * term dropped, 4 scale and min swapped, 5 Q6_K scale per 32 instead of per 16,
  * 6 RMS mean over n - 1, 7 eps added after the square root, 8 squares summed in
  * one running sum, 9 silu with exp(+g), 10 Q8_K scale from the first 32 values of
- * the block only, 11 Q8_K min term from the first 16-value sum of each sub-block.
+ * the block only, 11 Q8_K min term from the first 16-value sum of each sub-block,
+ * 12 Q4_0 offset 8 dropped, 13 Q4_0 nibbles read interleaved (element 2l low, 2l+1
+ * high nibble of byte l) instead of element l low, l + 16 high.
  */
 #ifndef OQ_MUTATE
 #define OQ_MUTATE 0
@@ -64,6 +70,10 @@
  * "Weights stay in GGUF blocks"]: the upload pads each Q6_K block so every 16-byte
  * piece is aligned).  The first 210 bytes are the block; the pad is ignored. */
 #define OQ_TYPE_Q6_K_P224 3
+/* 32-weight block formats ([CH03, section 3.2] Q4_0; Q8_0 named there by its
+ * 34-byte block), read in groups of eight consecutive blocks = 256 weights. */
+#define OQ_TYPE_Q4_0 4
+#define OQ_TYPE_Q8_0 5
 
 /* f16 bits -> f64, exact (normal, subnormal, zero; inf/nan kept as such). */
 static double f16_bits_to_f64(uint16_t h)
@@ -339,10 +349,69 @@ static int32_t dot_q6k_group(const q6k_block* w, const int8_t* qx, int g)
     return acc;
 }
 
-static size_t blk_bytes(int type) { return type == OQ_TYPE_Q4_K ? 144 : type == OQ_TYPE_Q6_K ? 210 : 224; }
+/* bytes per 256 weights */
+static size_t blk_bytes(int type)
+{
+    switch (type) {
+    case OQ_TYPE_Q4_K: return 144;
+    case OQ_TYPE_Q6_K: return 210;
+    case OQ_TYPE_Q6_K_P224: return 224;
+    case OQ_TYPE_Q4_0: return 8 * 18;
+    default: return 8 * 34;
+    }
+}
 static int known_type(int type)
 {
-    return type == OQ_TYPE_Q4_K || type == OQ_TYPE_Q6_K || type == OQ_TYPE_Q6_K_P224;
+    return type == OQ_TYPE_Q4_K || type == OQ_TYPE_Q6_K || type == OQ_TYPE_Q6_K_P224 || type == OQ_TYPE_Q4_0 ||
+           type == OQ_TYPE_Q8_0;
+}
+static int is_k6(int type) { return type == OQ_TYPE_Q6_K || type == OQ_TYPE_Q6_K_P224; }
+static int is_b32(int type) { return type == OQ_TYPE_Q4_0 || type == OQ_TYPE_Q8_0; }
+
+/* ---- O8. 32-weight block formats ------------------------------------------
+ * Q4_0 ([CH03, section 3.2]): 18 bytes = f16 d, then 16 bytes in which byte l
+ * holds element l in its low nibble and element l + 16 in its high nibble; the
+ * stored nibble is round(v / d) + 8, so w = d * (nibble - 8).  Q8_0 (R20): 34
+ * bytes = f16 d, then 32 int8 codes, w = d * q.  A group is eight consecutive
+ * blocks (256 weights); codes are returned centred (Q4_0: nibble - 8). */
+typedef struct {
+    double d[8];
+    int q[256];
+} b32_group;
+
+static void b32_decode(int type, const uint8_t* B, b32_group* o)
+{
+    for (int j = 0; j < 8; ++j) {
+        if (type == OQ_TYPE_Q4_0) {
+            const uint8_t* b = B + 18 * j;
+            o->d[j] = f16_bits_to_f64(rd_u16(b));
+            for (int l = 0; l < 16; ++l) {
+#if OQ_MUTATE == 13
+                o->q[32 * j + 2 * l] = (b[2 + l] & 0xF) - 8;
+                o->q[32 * j + 2 * l + 1] = (b[2 + l] >> 4) - 8;
+#elif OQ_MUTATE == 12
+                o->q[32 * j + l] = b[2 + l] & 0xF;
+                o->q[32 * j + 16 + l] = b[2 + l] >> 4;
+#else
+                o->q[32 * j + l] = (b[2 + l] & 0xF) - 8;
+                o->q[32 * j + 16 + l] = (b[2 + l] >> 4) - 8;
+#endif
+            }
+        } else {
+            const uint8_t* b = B + 34 * j;
+            o->d[j] = f16_bits_to_f64(rd_u16(b));
+            for (int l = 0; l < 32; ++l)
+                o->q[32 * j + l] = (int8_t)b[2 + l];
+        }
+    }
+}
+
+static int32_t dot_b32(const b32_group* w, const int8_t* qx, int j)
+{
+    int32_t acc = 0;
+    for (int l = 0; l < 32; ++l)
+        acc += w->q[32 * j + l] * (int32_t)qx[32 * j + l];
+    return acc;
 }
 
 int oracle_subblock_dots(int type, const uint8_t* W, const int8_t* q, int nt, int od, int id,
@@ -353,7 +422,7 @@ int oracle_subblock_dots(int type, const uint8_t* W, const int8_t* q, int nt, in
     if (!known_type(type))
         return -2;
     int nsb = id / 256;
-    int ng = type == OQ_TYPE_Q4_K ? 8 : 16;
+    int ng = is_k6(type) ? 16 : 8;
     size_t bb = blk_bytes(type);
 #pragma omp parallel for schedule(static)
     for (int r = 0; r < od; ++r) {
@@ -361,15 +430,20 @@ int oracle_subblock_dots(int type, const uint8_t* W, const int8_t* q, int nt, in
             const uint8_t* B = W + ((size_t)r * nsb + b) * bb;
             q4k_block w4;
             q6k_block w6;
+            b32_group w3;
             if (type == OQ_TYPE_Q4_K)
                 q4k_decode(B, &w4);
-            else
+            else if (is_k6(type))
                 q6k_decode(B, &w6);
+            else
+                b32_decode(type, B, &w3);
             for (int t = 0; t < nt; ++t) {
                 const int8_t* qx = q + (size_t)t * id + 256 * b;
                 int32_t* dst = S + (((size_t)t * od + r) * nsb + b) * ng;
                 for (int g = 0; g < ng; ++g)
-                    dst[g] = type == OQ_TYPE_Q4_K ? dot_q4k_sub(&w4, qx, g) : dot_q6k_group(&w6, qx, g);
+                    dst[g] = type == OQ_TYPE_Q4_K ? dot_q4k_sub(&w4, qx, g)
+                             : is_k6(type)        ? dot_q6k_group(&w6, qx, g)
+                                                  : dot_b32(&w3, qx, g);
             }
         }
     }
@@ -406,6 +480,16 @@ static void one_output(int type, const uint8_t* Wrow, const int8_t* qx_t, const 
 #endif
                 acc += tmain - tmin;
                 am += fabs(tmain) + fabs(tmin);
+            }
+        } else if (is_b32(type)) {
+            /* 32-weight blocks: d_w * dx * sum(qc * qx), codes centred -- exact, no
+             * stored sum enters */
+            b32_group w;
+            b32_decode(type, B, &w);
+            for (int j = 0; j < 8; ++j) {
+                double tm = w.d[j] * (double)d_t[8 * b + j] * (double)dot_b32(&w, qx, j);
+                acc += tm;
+                am += fabs(tm);
             }
         } else {
             q6k_block w;
@@ -547,7 +631,7 @@ int oracle_matmul_q8k(int type, const uint8_t* W, const int8_t* q, const float* 
 {
     if (!W || !q || !d || !bsum || !out || nt < 0 || od < 0 || id < 0 || id % 256)
         return -1;
-    if (!known_type(type))
+    if (!known_type(type) || is_b32(type))
         return -2;
     int nsb = id / 256;
     size_t row_bytes = (size_t)nsb * blk_bytes(type);
@@ -572,7 +656,7 @@ int oracle_q8k_superblock_sums(int type, const uint8_t* W, const int8_t* q, cons
 {
     if (!W || !q || !bsum || !S || nt < 0 || od < 0 || id < 0 || id % 256)
         return -1;
-    if (!known_type(type))
+    if (!known_type(type) || is_b32(type))
         return -2;
     int nsb = id / 256;
     size_t bb = blk_bytes(type);
@@ -615,7 +699,7 @@ int oracle_matmul_q8k_points(int type, const uint8_t* W, const int8_t* q, const 
 {
     if (!W || !q || !d || !bsum || !out || !t_idx || !r_idx || nt < 0 || od < 0 || id < 0 || id % 256 || n < 0)
         return -1;
-    if (!known_type(type))
+    if (!known_type(type) || is_b32(type))
         return -2;
     int nsb = id / 256;
     size_t row_bytes = (size_t)nsb * blk_bytes(type);
@@ -692,6 +776,18 @@ int oracle_decode_block(int type, const uint8_t* B, double* d, double* dmin, int
         return 0;
     }
     return -2;
+}
+
+/* Decoded group of eight 32-weight blocks (types 4, 5): d[8], centred codes[256]. */
+int oracle_decode_group32(int type, const uint8_t* B, double* d, int* codes)
+{
+    if (!is_b32(type))
+        return -2;
+    b32_group w;
+    b32_decode(type, B, &w);
+    memcpy(d, w.d, sizeof w.d);
+    memcpy(codes, w.q, sizeof w.q);
+    return 0;
 }
 
 int oracle_num_threads(void)

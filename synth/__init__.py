@@ -22,6 +22,10 @@ Block byte layouts follow the GGUF-style super-blocks the matmul consumes:
   high 2-bit fields | 16 int8 group scales | f16 d.  Uniform low/high bytes give
   6-bit codes uniform on {0..63} whatever the element-to-bit map; the group
   scales are drawn uniform on {-32..31}.
+* Q4_0 (18 B per 32 weights: f16 d | 16 bytes of 4-bit codes) and Q8_0 (34 B per
+  32 weights: f16 d | 32 int8 codes), generated in groups of eight blocks (256
+  weights, 144 and 272 bytes): uniform code bytes (Q8_0 codes uniform on
+  {-128..127}).
 * d, dmin: an f32 uniform on [1e-3, 1e-2), rounded to f16 (round to nearest even).
 * Activations: f32 N(0, 1) by Box-Muller in f64, rounded to f32; optionally a
   fraction of elements multiplied by a factor (outliers).
@@ -41,6 +45,10 @@ QK = 256  # weights per super-block
 
 TYPE_Q4_K = 1
 TYPE_Q6_K = 2
+TYPE_Q4_0 = 4
+TYPE_Q8_0 = 5
+Q40_GROUP_BYTES = 8 * 18
+Q80_GROUP_BYTES = 8 * 34
 
 # stream ids inside one seed
 STREAM_W = 0
@@ -124,11 +132,34 @@ def q6k_blocks(n_blocks: int, seed: int = 0, stream: int = STREAM_W, start_block
     return out
 
 
+def b32_groups(qtype: int, n_groups: int, seed: int = 0, stream: int = STREAM_W, start_group: int = 0) -> np.ndarray:
+    """n_groups groups of eight Q4_0 or Q8_0 blocks as a [n_groups, 144 or 272] uint8 array.
+
+    Per group, 8 draws give the eight d, then 16 (Q4_0) or 32 (Q8_0) draws give the
+    code bytes (16 or 32 per block, in block order).
+    """
+    cb = 16 if qtype == TYPE_Q4_0 else 32
+    bb = cb + 2
+    per = 8 + cb
+    z = draws(seed, stream, n_groups * per, start=start_group * per).reshape(n_groups, per)
+    codes = _bytes_of(z[:, 8:]).reshape(n_groups, 8, cb)
+    dbits = _f16_field(z[:, :8].reshape(-1)).reshape(n_groups, 8, 1).view(np.uint8).reshape(n_groups, 8, 2)
+    out = np.empty((n_groups, 8, bb), dtype=np.uint8)
+    out[:, :, 0:2] = dbits
+    out[:, :, 2:] = codes
+    return out.reshape(n_groups, 8 * bb)
+
+
 def block_bytes(qtype: int) -> int:
+    """Bytes per 256 weights."""
     if qtype == TYPE_Q4_K:
         return Q4K_BLOCK_BYTES
     if qtype == TYPE_Q6_K:
         return Q6K_BLOCK_BYTES
+    if qtype == TYPE_Q4_0:
+        return Q40_GROUP_BYTES
+    if qtype == TYPE_Q8_0:
+        return Q80_GROUP_BYTES
     raise ValueError(f"unknown type {qtype}")
 
 
@@ -137,6 +168,8 @@ def weights(qtype: int, od: int, idim: int, seed: int = 0, stream: int = STREAM_
     if idim % QK:
         raise ValueError("idim must be a multiple of 256")
     nb = od * (idim // QK)
+    if qtype in (TYPE_Q4_0, TYPE_Q8_0):
+        return b32_groups(qtype, nb, seed=seed, stream=stream).reshape(-1)
     gen = q4k_blocks if qtype == TYPE_Q4_K else q6k_blocks
     return gen(nb, seed=seed, stream=stream).reshape(-1)
 

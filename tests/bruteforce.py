@@ -108,3 +108,39 @@ def group_dots(qtype: int, W: np.ndarray, q: np.ndarray, od: int, idim: int) -> 
                 prod = codes * q[t, 256 * b:256 * (b + 1)].astype(np.int64)
                 out[t, r, b] = prod.reshape(-1, gs).sum(axis=1)
     return out
+
+
+def b32_code(qtype: int, group: np.ndarray, e: int) -> int:
+    """Centred code of weight e of a group of eight Q4_0 / Q8_0 blocks (nibble - 8, or the int8)."""
+    j, l = divmod(e, 32)
+    if qtype == 4:
+        byte = int(group[18 * j + 2 + (l % 16)])
+        return (byte % 16 if l < 16 else byte // 16) - 8
+    return int(np.int8(np.uint8(group[34 * j + 2 + l])))
+
+
+def b32_weight(qtype: int, group: np.ndarray, e: int) -> float:
+    """Weight e (0..255) of a group of eight Q4_0 / Q8_0 blocks, from the byte rules:
+    Q4_0 block = f16 d, 16 bytes; byte l low nibble = element l, high = element l+16;
+    w = d (nibble - 8).  Q8_0 block = f16 d, 32 int8; w = d q."""
+    j, l = divmod(e, 32)
+    if qtype == 4:
+        b = group[18 * j: 18 * j + 18]
+        d = f16(int(b[0]), int(b[1]))
+        byte = int(b[2 + (l % 16)])
+        nib = byte % 16 if l < 16 else byte // 16
+        return d * (nib - 8)
+    b = group[34 * j: 34 * j + 34]
+    d = f16(int(b[0]), int(b[1]))
+    return d * int(np.int8(np.uint8(b[2 + l])))
+
+
+def b32_dequant(qtype: int, W: np.ndarray, od: int, idim: int) -> np.ndarray:
+    gb = 144 if qtype == 4 else 272
+    G = np.ascontiguousarray(W, dtype=np.uint8).reshape(od, idim // 256, gb)
+    out = np.empty((od, idim), np.float64)
+    for r in range(od):
+        for g in range(idim // 256):
+            for e in range(256):
+                out[r, 256 * g + e] = b32_weight(qtype, G[r, g], e)
+    return out
