@@ -62,7 +62,18 @@ enum {
      * block is aligned and the kernels read it with 16-byte loads.  Bytes 0..209
      * of a padded block are the Q6_K block; bytes 210..223 are ignored.
      * qmm_pad_q6k makes this layout from QMM_TYPE_Q6_K. */
-    QMM_TYPE_Q6_K_P224 = 3
+    QMM_TYPE_Q6_K_P224 = 3,
+    /* [CH03, section 3.2]: 18 bytes per 32 weights: f16 d, then 16 bytes in which
+     * byte l holds element l in its low nibble and element l + 16 in its high
+     * nibble; the stored nibble is round(v/d) + 8, so w = d*(nibble - 8).  [CH04,
+     * section 3.4]: the offset folds out through the activation sum. */
+    QMM_TYPE_Q4_0 = 4,
+    /* 34 bytes per 32 weights: f16 d, then 32 int8 codes, w = d*q (the pages give
+     * the block size; the layout is the public one). */
+    QMM_TYPE_Q8_0 = 5
+    /* Every type: a row is a whole number of 256-weight groups (id % 256 == 0): one
+     * super-block, or eight consecutive 32-weight blocks (144 bytes for Q4_0, 272
+     * for Q8_0), so rows of the 32-weight types stay 16-byte aligned. */
 };
 
 /* Status codes. */
@@ -87,8 +98,8 @@ enum {
     QMM_KIND_MMQ_64X64_SPLITK = 5   /* 64 x 64, 8 waves in two groups splitting K */
 };
 
-/* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K), *210
- * (Q6_K) or *224 (Q6_K padded).  0 for an unknown type or a bad shape. */
+/* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K, Q4_0), *210
+ * (Q6_K), *224 (Q6_K padded) or *272 (Q8_0).  0 for an unknown type or a bad shape. */
 size_t qmm_weight_bytes(int type, int od, int id);
 
 /* Upload-time repack: nblocks Q6_K blocks of 210 bytes (src, any alignment) to
@@ -227,11 +238,12 @@ int qmm_rmsnorm(const float* x, const float* w, float eps, int nt, int id, float
 int qmm_silu_mul(const float* g, const float* u, int nt, int id, float* y, void* stream);
 
 /* Diagnostic: the integer stage of a kernel alone.  [GEMM, "The GPU path"]: each
- * scale group (32 weights for Q4_K, 16 for Q6_K) is reduced as an integer dot
- * with its activation codes.  Writes S[t][r][b][g] = sum over group g of super-
- * block b of row r of (code * qx) -- codes 0..15 uncentred for Q4_K, (q6 - 32) for
- * Q6_K -- as int32, computed by the unpack and dot code of the kernel `kind`
- * (QMM_KIND_MMVQ: v_dot4 path, nt <= 8; QMM_KIND_MMQ: int8 MFMA path).
+ * scale group (32 weights for Q4_K, Q4_0 and Q8_0, 16 for Q6_K) is reduced as an
+ * integer dot with its activation codes.  Writes S[t][r][b][g] = sum over group g
+ * of 256-weight group b of row r of (code * qx) -- codes 0..15 uncentred for Q4_K,
+ * (q6 - 32) for Q6_K, (nibble - 8) for Q4_0, the int8 for Q8_0 -- as int32,
+ * computed by the unpack and dot code of the kernel `kind` (QMM_KIND_MMVQ: v_dot4
+ * path, nt <= 8; QMM_KIND_MMQ: int8 MFMA path).
  * S: [nt][od][id/256][8 or 16] int32, 16-byte aligned. */
 int qmm_group_dots(int kind, int type, const void* W, const int8_t* q, int nt, int od, int id,
                    int32_t* S, void* stream);

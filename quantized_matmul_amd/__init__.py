@@ -23,6 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libqmm.so")
 QMM_TYPE_Q4_K = 1
 QMM_TYPE_Q6_K = 2
 QMM_TYPE_Q6_K_P224 = 3   # Q6_K blocks padded to 224 bytes (qmm_pad_q6k)
+QMM_TYPE_Q4_0 = 4        # 18-byte blocks of 32 weights
+QMM_TYPE_Q8_0 = 5        # 34-byte blocks of 32 weights
 QMM_KIND_MMVQ = 1
 QMM_KIND_MMQ = 2
 QMM_KIND_MMQ_128X64 = 3
@@ -37,7 +39,8 @@ QMM_ERR_WORKSPACE = -5
 QMM_ERR_DEVICE = -6
 QMM_ERR_LAUNCH = -7
 
-BLOCK_BYTES = {QMM_TYPE_Q4_K: 144, QMM_TYPE_Q6_K: 210, QMM_TYPE_Q6_K_P224: 224}
+BLOCK_BYTES = {QMM_TYPE_Q4_K: 144, QMM_TYPE_Q6_K: 210, QMM_TYPE_Q6_K_P224: 224,  # bytes per 256 weights
+               QMM_TYPE_Q4_0: 144, QMM_TYPE_Q8_0: 272}
 
 EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8",
            "qmm_matmul_q8_kind", "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots",
@@ -347,7 +350,7 @@ def qmm_matmul_q8_kind(kind: int, qtype: int, W, q, d, s, od: int, out=None, str
 def qmm_group_dots(kind: int, qtype: int, W: torch.Tensor, q: torch.Tensor, od: int, S=None, stream=None):
     """int32 [nt, od, id/256, 8 or 16] per-scale-group integer dots from kernel `kind`."""
     nt, idim = q.shape
-    ng = 8 if qtype == QMM_TYPE_Q4_K else 16
+    ng = 16 if qtype in (QMM_TYPE_Q6_K, QMM_TYPE_Q6_K_P224) else 8
     if S is None:
         S = torch.empty((nt, od, idim // 256, ng), dtype=torch.int32, device=q.device)
     _check(lib().qmm_group_dots(kind, qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"), nt, od,

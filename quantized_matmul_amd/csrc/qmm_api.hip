@@ -42,12 +42,19 @@ size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 int check_type(int type)
 {
-    return (type == QMM_TYPE_Q4_K || type == QMM_TYPE_Q6_K || type == QMM_TYPE_Q6_K_P224) ? QMM_OK : QMM_ERR_TYPE;
+    return (type >= QMM_TYPE_Q4_K && type <= QMM_TYPE_Q8_0) ? QMM_OK : QMM_ERR_TYPE;
 }
 
+// bytes per 256 weights
 size_t block_bytes(int type)
 {
-    return type == QMM_TYPE_Q4_K ? qmm::kQ4KBytes : type == QMM_TYPE_Q6_K ? qmm::kQ6KBytes : qmm::kQ6KP224Bytes;
+    switch (type) {
+    case QMM_TYPE_Q4_K: return qmm::kQ4KBytes;
+    case QMM_TYPE_Q6_K: return qmm::kQ6KBytes;
+    case QMM_TYPE_Q6_K_P224: return qmm::kQ6KP224Bytes;
+    case QMM_TYPE_Q4_0: return 8 * 18;
+    default: return 8 * 34;
+    }
 }
 
 // One thread per 16-byte piece of a padded block (14 per block): bytes of the

@@ -589,6 +589,213 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q6k_kernel(const uin
     }
 }
 
+// ------------------------------------------------------------------ Q4_0 / Q8_0
+// 32-weight blocks (Q4_0: f16 d, 16 bytes, element l in the low and l + 16 in the
+// high nibble of byte l, w = d (nibble - 8); Q8_0: f16 d, 32 int8, w = d q), read
+// in groups of eight (a super-block step is 256 weights).  [MMQ, section 4]:
+// codes are centred at staging (Q4_0: nibble - 8 as a signed byte) so the int8
+// MFMA gives the centred dot and no min term is needed; one
+// v_mfma_i32_32x32x32_i8 per block, rescale acc += (d_w * dx) * C with the scale
+// products of two blocks from one outer-product pair.  A staging task (row, block)
+// loads the dwords the block covers (blocks start 0 or 2 bytes past a dword; rows
+// are 16-byte aligned) and funnel-shifts them.
+template <int BM, int BN>
+struct __attribute__((aligned(16))) B32Smem {
+    static constexpr int W_STRIDE = 272;    // 256 centred codes + 16 pad
+    static constexpr int X_STRIDE = 272;
+    int8_t wq[BM * W_STRIDE];
+    float wsc[8 * BM];                      // d of block j, [j][row]
+    uint8_t xq[BN * X_STRIDE];
+    float xd[8 * BN];
+};
+
+// byte-wise n - 8 for nibbles n in 0..15 held one per byte: t = n ^ 8 is n - 8
+// when bit 3 of t is clear; when it is set, filling the top four bits gives t - 16
+template <bool Q8>
+__device__ __forceinline__ uint32_t b32_center(uint32_t nib)
+{
+    const uint32_t t = nib ^ 0x08080808u;
+    return t | ((t & 0x08080808u) * 30u);
+}
+
+template <int BM, int BN, int NTH, int WC8, int XC, int SC, bool Q8>
+__device__ __forceinline__ void b32_prefetch(uint32_t (&pw)[WC8][Q8 ? 9 : 5], uint32_t (&psh)[WC8], v4i (&px)[XC],
+                                             v4i (&ps)[SC], const uint8_t* __restrict__ W,
+                                             const int8_t* __restrict__ q, const float* __restrict__ dx, int sb,
+                                             int tid, int row0, int tok0, int nt, int od, int id, int nblk,
+                                             size_t row_bytes)
+{
+    constexpr uint32_t BB = Q8 ? 34 : 18;
+    constexpr int ND = Q8 ? 9 : 5;
+#pragma unroll
+    for (int k = 0; k < WC8; ++k) {
+        const int e = task<BM * 8, NTH, WC8>(tid + k * NTH);
+        const int r = e >> 3, j = e & 7;
+        const uint8_t* rp = W + (size_t)min(row0 + r, od - 1) * row_bytes;
+        const uint32_t off = ((uint32_t)sb * 8 + (uint32_t)j) * BB;
+        const uint32_t* p4 = reinterpret_cast<const uint32_t*>(rp + (off & ~3u));
+        psh[k] = off & 3u;
+#pragma unroll
+        for (int i = 0; i < ND; ++i)
+            pw[k][i] = p4[i];
+    }
+#pragma unroll
+    for (int k = 0; k < XC; ++k) {
+        const int e = task<BN * 16, NTH, XC>(tid + k * NTH);
+        const int t = min(tok0 + (e >> 4), nt - 1), ch = e & 15;
+        px[k] = *reinterpret_cast<const v4i*>(q + (size_t)t * id + 256 * sb + 16 * ch);
+    }
+#pragma unroll
+    for (int k = 0; k < SC; ++k) {
+        const int e = task<BN * 2, NTH, SC>(tid + k * NTH);
+        const int t = min(tok0 + (e >> 1), nt - 1), hf = e & 1;
+        ps[k] = *reinterpret_cast<const v4i*>(dx + (size_t)t * nblk + 8 * sb + 4 * hf);
+    }
+}
+
+template <int BM, int BN, int NTH, int WC8, int XC, int SC, bool Q8>
+__device__ __forceinline__ void b32_stage(B32Smem<BM, BN>& sm, const uint32_t (&pw)[WC8][Q8 ? 9 : 5],
+                                          const uint32_t (&psh)[WC8], const v4i (&px)[XC], const v4i (&ps)[SC],
+                                          int tid, bool valid)
+{
+    using SM = B32Smem<BM, BN>;
+    constexpr int ND = Q8 ? 9 : 5;
+#pragma unroll
+    for (int k = 0; k < WC8; ++k) {
+        const int e = task<BM * 8, NTH, WC8>(tid + k * NTH);
+        const int r = e >> 3, j = e & 7;
+        uint32_t bb[ND];  // block bytes from byte 0
+#pragma unroll
+        for (int i = 0; i + 1 < ND; ++i)
+            bb[i] = __builtin_amdgcn_alignbyte(pw[k][i + 1], pw[k][i], psh[k]);
+        bb[ND - 1] = pw[k][ND - 1] >> (8 * psh[k]);
+        uint32_t cd[ND - 1];  // code bytes from byte 2
+#pragma unroll
+        for (int i = 0; i + 1 < ND; ++i)
+            cd[i] = __builtin_amdgcn_alignbyte(bb[i + 1], bb[i], 2);
+        int8_t* dst = &sm.wq[r * SM::W_STRIDE + 32 * j];
+        if constexpr (Q8) {
+            *reinterpret_cast<uint4*>(dst) = make_uint4(cd[0], cd[1], cd[2], cd[3]);
+            *reinterpret_cast<uint4*>(dst + 16) = make_uint4(cd[4], cd[5], cd[6], cd[7]);
+        } else {
+            *reinterpret_cast<uint4*>(dst) =
+                make_uint4(b32_center<Q8>(cd[0] & 0x0F0F0F0Fu), b32_center<Q8>(cd[1] & 0x0F0F0F0Fu),
+                           b32_center<Q8>(cd[2] & 0x0F0F0F0Fu), b32_center<Q8>(cd[3] & 0x0F0F0F0Fu));
+            *reinterpret_cast<uint4*>(dst + 16) =
+                make_uint4(b32_center<Q8>((cd[0] >> 4) & 0x0F0F0F0Fu), b32_center<Q8>((cd[1] >> 4) & 0x0F0F0F0Fu),
+                           b32_center<Q8>((cd[2] >> 4) & 0x0F0F0F0Fu), b32_center<Q8>((cd[3] >> 4) & 0x0F0F0F0Fu));
+        }
+        sm.wsc[j * BM + r] = valid ? f16_bits_to_f32(bb[0] & 0xFFFF) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < XC; ++k) {
+        const int e = task<BN * 16, NTH, XC>(tid + k * NTH);
+        *reinterpret_cast<v4i*>(&sm.xq[(e >> 4) * SM::X_STRIDE + 16 * (e & 15)]) = px[k];
+    }
+#pragma unroll
+    for (int k = 0; k < SC; ++k) {
+        const int e = task<BN * 2, NTH, SC>(tid + k * NTH);
+        const int t = e >> 1, hf = e & 1;
+        sm.xd[(4 * hf + 0) * BN + t] = __int_as_float(ps[k].x);
+        sm.xd[(4 * hf + 1) * BN + t] = __int_as_float(ps[k].y);
+        sm.xd[(4 * hf + 2) * BN + t] = __int_as_float(ps[k].z);
+        sm.xd[(4 * hf + 3) * BN + t] = __int_as_float(ps[k].w);
+    }
+}
+
+template <int WR, int WC, int KS, bool DUMP, bool Q8>
+__global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_b32_kernel(const uint8_t* __restrict__ W,
+                                                                    const int8_t* __restrict__ q,
+                                                                    const float* __restrict__ dx,
+                                                                    float* __restrict__ out, int nt, int od,
+                                                                    int id, int32_t* __restrict__ S)
+{
+    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;
+    constexpr int WC8 = (BM * 8 + NTH - 1) / NTH;  // (row, block) tasks per thread
+    constexpr int XC = (BN * 16 + NTH - 1) / NTH;
+    constexpr int SC = (BN * 2 + NTH - 1) / NTH;
+    constexpr int ND = Q8 ? 9 : 5;
+    using SM = B32Smem<BM, BN>;
+    __shared__ SM smb[KS][2];
+    static_assert(!DUMP || KS == 1, "the debug dump runs unsplit");
+    static_assert((KS - 1) * WR * WC * 1024 * sizeof(float) <= sizeof(smb), "reduction scratch fits the tiles");
+
+    const int ntb = (nt + BN - 1) / BN;
+    const int tile = xcd_tile(ntb * ((od + BM - 1) / BM));
+    if (tile < 0)
+        return;
+    const int row0 = (tile / ntb) * BM, tok0 = (tile % ntb) * BN;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kg = KS > 1 ? wave / (WR * WC) : 0, gw = wave - kg * (WR * WC);
+    const int tid = threadIdx.x - kg * NTH;
+    const int wr = gw / WC, wc = gw % WC;
+    const int li = lane & 31, lh = lane >> 5;
+    const int nsb = id >> 8;
+    const int nblk = id >> 5;
+    const int niter = (nsb + KS - 1) / KS;
+    const size_t row_bytes = (size_t)nblk * (Q8 ? 34 : 18);
+
+    uint32_t pw[WC8][ND], psh[WC8];
+    v4i px[XC], ps[SC];
+    v16f accv = {};
+    const int arow = wr * 32 + li;
+    const int btok = wc * 32 + li;
+
+    b32_prefetch<BM, BN, NTH, WC8, XC, SC, Q8>(pw, psh, px, ps, W, q, dx, min(kg, nsb - 1), tid, row0, tok0, nt, od,
+                                               id, nblk, row_bytes);
+    b32_stage<BM, BN, NTH, WC8, XC, SC, Q8>(smb[kg][0], pw, psh, px, ps, tid, kg < nsb);
+    b32_prefetch<BM, BN, NTH, WC8, XC, SC, Q8>(pw, psh, px, ps, W, q, dx, min(KS + kg, nsb - 1), tid, row0, tok0,
+                                               nt, od, id, nblk, row_bytes);
+    __syncthreads();
+    for (int it = 0; it < niter; ++it) {
+        const SM& sm = smb[kg][it & 1];
+        const int sb = it * KS + kg;
+#pragma unroll 2
+        for (int p = 0; p < 4; ++p) {
+            // blocks 2p and 2p + 1
+            const v4i a0 = *reinterpret_cast<const v4i*>(&sm.wq[arow * SM::W_STRIDE + 64 * p + 16 * lh]);
+            const v4i a1 = *reinterpret_cast<const v4i*>(&sm.wq[arow * SM::W_STRIDE + 64 * p + 32 + 16 * lh]);
+            const v4i b0 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
+            const v4i b1 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
+            const v16i C0 = mfma_i8_k32(a0, b0);
+            const v16i C1 = mfma_i8_k32(a1, b1);
+            if constexpr (DUMP) {
+                const int tg = tok0 + btok;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int rg = row0 + wr * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+                    if (tg < nt && rg < od) {
+                        int32_t* dst = S + (((size_t)tg * od + rg) * nsb + sb) * 8 + 2 * p;
+                        dst[0] = C0[i];
+                        dst[1] = C1[i];
+                    }
+                }
+            } else {
+                const int j = 2 * p + lh;
+                const v32f P = mfma_outer2(sm.wsc[j * BM + arow], sm.xd[j * BN + btok]);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    accv[i] = fmaf((float)C0[i], P[i], accv[i]);
+                    accv[i] = fmaf((float)C1[i], P[16 + i], accv[i]);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        b32_stage<BM, BN, NTH, WC8, XC, SC, Q8>(smb[kg][(it + 1) & 1], pw, psh, px, ps, tid, sb + KS < nsb);
+        b32_prefetch<BM, BN, NTH, WC8, XC, SC, Q8>(pw, psh, px, ps, W, q, dx, min(sb + 2 * KS, nsb - 1), tid, row0,
+                                                   tok0, nt, od, id, nblk, row_bytes);
+        __syncthreads();
+    }
+
+    if constexpr (!DUMP) {
+        v16f v = accv;
+        if (!combine_k_groups<WR * WC, KS>(v, reinterpret_cast<float*>(&smb[0][0]), kg, gw, lane))
+            return;
+        store_tile(v, out, nt, od, tok0 + btok, row0 + wr * 32, lh);
+    }
+}
+
 // ------------------------------------------------------------------ probes
 // One MFMA tile with the operand and result mapping the MMQ kernels rely on,
 // written out in a fixed layout (C[.][token][row]) for a test:
@@ -652,8 +859,14 @@ static hipError_t launch_tile(int type, const uint8_t* W, const int8_t* q, const
     else if (type == 2)
         hipLaunchKernelGGL((mmq_q6k_kernel<WR, WC, KS, DUMP, false>), dim3(grid), dim3(64 * WR * WC * KS), 0, st,
                            W, q, d, out, nt, od, id, S);
-    else
+    else if (type == 3)
         hipLaunchKernelGGL((mmq_q6k_kernel<WR, WC, KS, DUMP, true>), dim3(grid), dim3(64 * WR * WC * KS), 0, st,
+                           W, q, d, out, nt, od, id, S);
+    else if (type == 4)
+        hipLaunchKernelGGL((mmq_b32_kernel<WR, WC, KS, DUMP, false>), dim3(grid), dim3(64 * WR * WC * KS), 0, st,
+                           W, q, d, out, nt, od, id, S);
+    else
+        hipLaunchKernelGGL((mmq_b32_kernel<WR, WC, KS, DUMP, true>), dim3(grid), dim3(64 * WR * WC * KS), 0, st,
                            W, q, d, out, nt, od, id, S);
     return hipGetLastError();
 }

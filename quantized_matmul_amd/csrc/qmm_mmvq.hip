@@ -368,6 +368,140 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q6k_kernel(
     }
 }
 
+// ------------------------------------------------------------------ Q4_0 / Q8_0
+// 32-weight blocks ([CH03, section 3.2] Q4_0: f16 d, 16 bytes, byte l holding
+// element l in the low and element l + 16 in the high nibble, w = d (nibble - 8);
+// Q8_0: f16 d, 32 int8 codes, w = d q).  [CH04, section 3.4]: one integer 4-way
+// dot per 4 code bytes, both scales folded once per block, the Q4_0 offset taken
+// off through the activation sum: d4 * (dx * dot - 8 * s), s = dx * sum(qx) as
+// stored by the quantizer.  A window is 64 blocks (2048 weights, as for the
+// K-quants); lane L takes block 64 w + L.  Rows are 16-byte aligned (eight blocks
+// are 144 or 272 bytes), so a block starts 0 or 2 bytes past a dword: the lane
+// loads exactly the dwords the block covers (5 or 9) and funnel-shifts them.
+template <int NT, int R, bool DUMP, bool Q8>
+__global__ __launch_bounds__(64 * kMaxWaves) void mmvq_b32_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ q, const float* __restrict__ dx,
+    const float* __restrict__ sx, float* __restrict__ out, int od, int id, int32_t* __restrict__ S,
+    int wpr, int gpw)
+{
+    constexpr int NTP = pow2_ceil<NT>::value;
+    constexpr int V = R * NTP;
+    constexpr uint32_t BB = Q8 ? 34 : 18;  // bytes per block
+    constexpr int ND = Q8 ? 9 : 5;         // dwords covering one block
+    constexpr int NC = Q8 ? 8 : 4;         // code dwords
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = wave / wpr, wk = wave - grp * wpr;
+    const int row0 = (blockIdx.x * gpw + grp) * R;
+    const int nblk = id >> 5;
+    const int nsb = id >> 8;
+    const int nwin = (nblk + 63) >> 6;
+    const size_t row_bytes = (size_t)nblk * BB;
+    const bool live = row0 < od;
+
+    float acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+        acc[i] = 0.f;
+
+    for (int w = wk; live && w < nwin; w += wpr) {
+        const int u = 64 * w + lane;
+        const bool bv = u < nblk;
+        const uint32_t uc = (uint32_t)(bv ? u : nblk - 1);
+        int4 xa[NT], xb[NT];
+        float da[NT], sa[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int8_t* qt = q + (size_t)t * id + 32 * uc;
+            xa[t] = *reinterpret_cast<const int4*>(qt);
+            xb[t] = *reinterpret_cast<const int4*>(qt + 16);
+            // lanes past the row's last block add nothing: both scale terms zero
+            da[t] = bv ? dx[(size_t)t * nblk + uc] : 0.f;
+            sa[t] = (Q8 || !bv) ? 0.f : sx[(size_t)t * nblk + uc];
+        }
+        uint32_t wd[R][ND];
+        uint32_t shf[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint8_t* rp = W + (size_t)min(row0 + r, od - 1) * row_bytes;
+            const uint32_t off = uc * BB;
+            const uint32_t* pw = reinterpret_cast<const uint32_t*>(rp + (off & ~3u));
+            shf[r] = off & 3u;
+#pragma unroll
+            for (int i = 0; i < ND; ++i)
+                wd[r][i] = pw[i];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        int sxi[NT];
+        if constexpr (DUMP && !Q8) {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                int v = sdot4(0x01010101, xa[t].x, 0);
+                v = sdot4(0x01010101, xa[t].y, v);
+                v = sdot4(0x01010101, xa[t].z, v);
+                v = sdot4(0x01010101, xa[t].w, v);
+                v = sdot4(0x01010101, xb[t].x, v);
+                v = sdot4(0x01010101, xb[t].y, v);
+                v = sdot4(0x01010101, xb[t].z, v);
+                sxi[t] = sdot4(0x01010101, xb[t].w, v);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            // block bytes from byte 0: bb[i] = bytes 4i .. 4i+3 of the block
+            uint32_t bb[ND];
+#pragma unroll
+            for (int i = 0; i + 1 < ND; ++i)
+                bb[i] = __builtin_amdgcn_alignbyte(wd[r][i + 1], wd[r][i], shf[r]);
+            bb[ND - 1] = wd[r][ND - 1] >> (8 * shf[r]);
+            const float dw = f16_bits_to_f32(bb[0] & 0xFFFF);
+            uint32_t cd[NC];  // code bytes 2 .. of the block
+#pragma unroll
+            for (int i = 0; i < NC; ++i)
+                cd[i] = __builtin_amdgcn_alignbyte(bb[i + 1], bb[i], 2);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                int dot;
+                if constexpr (Q8) {
+                    dot = sdot4((int)cd[0], xa[t].x, 0);
+                    dot = sdot4((int)cd[1], xa[t].y, dot);
+                    dot = sdot4((int)cd[2], xa[t].z, dot);
+                    dot = sdot4((int)cd[3], xa[t].w, dot);
+                    dot = sdot4((int)cd[4], xb[t].x, dot);
+                    dot = sdot4((int)cd[5], xb[t].y, dot);
+                    dot = sdot4((int)cd[6], xb[t].z, dot);
+                    dot = sdot4((int)cd[7], xb[t].w, dot);
+                } else {
+                    // elements 4i.. in low nibbles (against xa), 16 + 4i.. in high (xb)
+                    dot = sdot4((int)(cd[0] & 0x0F0F0F0Fu), xa[t].x, 0);
+                    dot = sdot4((int)(cd[1] & 0x0F0F0F0Fu), xa[t].y, dot);
+                    dot = sdot4((int)(cd[2] & 0x0F0F0F0Fu), xa[t].z, dot);
+                    dot = sdot4((int)(cd[3] & 0x0F0F0F0Fu), xa[t].w, dot);
+                    dot = sdot4((int)((cd[0] >> 4) & 0x0F0F0F0Fu), xb[t].x, dot);
+                    dot = sdot4((int)((cd[1] >> 4) & 0x0F0F0F0Fu), xb[t].y, dot);
+                    dot = sdot4((int)((cd[2] >> 4) & 0x0F0F0F0Fu), xb[t].z, dot);
+                    dot = sdot4((int)((cd[3] >> 4) & 0x0F0F0F0Fu), xb[t].w, dot);
+                }
+                if constexpr (DUMP) {
+                    if (bv && row0 + r < od) {
+                        // centred integer dot of the block (Q4_0: dot - 8 sum(qx))
+                        const int sc = Q8 ? dot : dot - 8 * sxi[t];
+                        S[(((size_t)t * od + row0 + r) * nsb + (uc >> 3)) * 8 + (uc & 7)] = sc;
+                    }
+                } else if constexpr (Q8) {
+                    acc[r * NTP + t] = fmaf(dw * da[t], (float)dot, acc[r * NTP + t]);
+                } else {
+                    acc[r * NTP + t] = fmaf(dw, fmaf(da[t], (float)dot, -8.0f * sa[t]), acc[r * NTP + t]);
+                }
+            }
+        }
+    }
+    if constexpr (!DUMP) {
+        const float v = wave_reduce_spread<V>(acc, lane);
+        group_store<NT, R, NTP>(v, lane, wave, grp, wk, wpr, row0, od, out);
+    }
+}
+
 // ------------------------------------------------------------------ launch
 
 // Waves per row group: one per K window up to kMaxWaves (more windows are
@@ -388,9 +522,15 @@ static hipError_t launch_one(int type, const uint8_t* W, const int8_t* q, const 
     else if (type == 2)
         hipLaunchKernelGGL((mmvq_q6k_kernel<NT, R, DUMP, false>), dim3(grid), block, 0, st, W, q, d, out, od, id, S,
                            wpr, gpw);
-    else
+    else if (type == 3)
         hipLaunchKernelGGL((mmvq_q6k_kernel<NT, R, DUMP, true>), dim3(grid), block, 0, st, W, q, d, out, od, id, S,
                            wpr, gpw);
+    else if (type == 4)
+        hipLaunchKernelGGL((mmvq_b32_kernel<NT, R, DUMP, false>), dim3(grid), block, 0, st, W, q, d, s, out, od, id,
+                           S, wpr, gpw);
+    else
+        hipLaunchKernelGGL((mmvq_b32_kernel<NT, R, DUMP, true>), dim3(grid), block, 0, st, W, q, d, s, out, od, id,
+                           S, wpr, gpw);
     return hipGetLastError();
 }
 

@@ -7,8 +7,8 @@ REL_TOL = 1e-5
 
 
 def n_terms(qtype: int, idim: int) -> int:
-    """Scale-group terms per output: id/32 sub-blocks (Q4_K) or id/16 groups (Q6_K, padded or not)."""
-    return idim // 32 if qtype == 1 else idim // 16
+    """Scale-group terms per output: id/32 (Q4_K sub-blocks, Q4_0 / Q8_0 blocks) or id/16 (Q6_K groups)."""
+    return idim // 16 if qtype in (2, 3) else idim // 32
 
 
 def assert_close(got, ref, mag, qtype: int, idim: int, what: str = ""):
