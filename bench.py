@@ -42,8 +42,12 @@ per 256 values, 16-value code sums; its own numerics) and, on the same weights a
 inputs, on the per-32 activations.  value = int8 TOP/s of the Q8_K matmul kernel;
 per32_same_shapes gives the per-32 kernel's rate from the same process.
 
+Workload "formats": Q4_0 and Q8_0 (and Q4_K for comparison) at 12288 x 4096, nt = 1
+and nt = 512.  value = HBM GB/s of the Q4_0 vector kernel at nt = 1.
+
 Options: --gpus N (1 only), --steps K, --warmup W, --workload
-{q4k_decode_prefill, q6k_head, dllm_step, fused_quantize, q8k_prefill}, --no-cpu-baseline, --copy-calibration
+{q4k_decode_prefill, q6k_head, dllm_step, fused_quantize, q8k_prefill, formats}, --no-cpu-baseline,
+--copy-calibration
 MIB (before warm-up, run five plain device copies of MIB MiB between two spin-kernel
 markers, for scaling the HBM counters of a profiled run).
 """
@@ -78,7 +82,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200, help="multiple of 20")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q4k_decode_prefill",
-                    choices=["q4k_decode_prefill", "q6k_head", "dllm_step", "fused_quantize", "q8k_prefill"])
+                    choices=["q4k_decode_prefill", "q6k_head", "dllm_step", "fused_quantize", "q8k_prefill",
+                             "formats"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     return ap.parse_args()
@@ -197,6 +202,15 @@ def build_calls(torch, qmm, workload):
             calls.append(per32)
             calls.append(Call(torch, qmm, Q4, od, idim, 512, seed=seed, outliers=True, copies=per32.W, x=per32.x,
                               q8k=True))
+    elif workload == "formats":
+        # Q4_0 and Q8_0 at the 12288 x 4096 shape, decode and prefill, beside Q4_K
+        for qt in (qmm.QMM_TYPE_Q4_0, qmm.QMM_TYPE_Q8_0, Q4):
+            shared = None
+            for nt in (1, 512):
+                c = Call(torch, qmm, qt, 12288, 4096, nt, seed=40 + qt, outliers=nt > 8, copies=shared,
+                         label=f"{ {1: 'Q4_K', 4: 'Q4_0', 5: 'Q8_0'}[qt] } 12288x4096 nt={nt}")
+                shared = c.W
+                calls.append(c)
     elif workload == "q6k_head":
         c6 = Call(torch, qmm, Q6, 32000, 4096, 1, seed=3, outliers=False)
         calls.append(c6)
@@ -593,6 +607,23 @@ def main():
                                      "speedup_q8k": round(t32 / t8, 3)}
         line["config"] = {"workload": "q8k_prefill", "shapes": "Q4_K 12288x4096 and 4096x12288, nt=512, "
                           "1% outliers x20", "activations": "Q8_K (one scale per 256) vs per-32"}
+    elif args.workload == "formats":
+        by = {c.label: c for c in calls}
+        k = lambda lab: float(np.mean(by[lab].k_ms)) * 1e-3  # noqa: E731
+        head = by["Q4_0 12288x4096 nt=1"]
+        line.update(metric="Q4_0 / Q8_0 matmul: HBM GB/s at nt=1 and int8 TOP/s at nt=512",
+                    value=round(head.kbytes / k(head.label) / 1e9, 1), unit="GB/s")
+        line["roofline"] = {"bound": "hbm", "achieved": line["value"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(line["value"] / HBM_PEAK_GBS, 4), "traffic": None,
+                            "kernel": "mmvq_b32_kernel<1,4,false,false>", "call": head.label,
+                            "bytes_per_launch": int(head.kbytes)}
+        line["per_format"] = {lab: ({"GB_s": round(c.kbytes / k(lab) / 1e9, 1),
+                                     "hbm_frac": round(c.kbytes / k(lab) / 1e9 / HBM_PEAK_GBS, 4)} if c.nt == 1 else
+                                    {"TOP_s": round(c.ops / k(lab) / 1e12, 2),
+                                     "int8_frac": round(c.ops / k(lab) / 1e12 / INT8_PEAK_TOPS, 4)})
+                              for lab, c in by.items()}
+        line["config"] = {"workload": "formats", "shape": "12288x4096", "nt": [1, 512],
+                          "types": ["Q4_0", "Q8_0", "Q4_K"]}
     elif args.workload == "q6k_head":
         c, cp = dec[0], dec[1]
         k = float(np.mean(c.k_ms)) * 1e-3
