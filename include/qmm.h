@@ -145,6 +145,19 @@ int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, cons
 int qmm_matmul_q8_kind(int kind, int type, const void* W, const int8_t* q, const float* d,
                        const float* s, int nt, int od, int id, float* out, void* stream);
 
+/* Stream-K matrix kernel (Q4_K weights, any nt): the ntiles x (id/256) units of
+ * (128 x 64 tile, super-block) are cut into 256 equal contiguous ranges, one per
+ * workgroup, so a tile count that does not fill the chip still loads every CU;
+ * tiles split between workgroups are combined by a second kernel that adds the
+ * partials in workgroup order (a fixed order: results do not depend on timing,
+ * and differ from qmm_matmul_q8 by f32 rounding only).  workspace: caller's device
+ * buffer of at least qmm_streamk_ws_bytes() bytes (QMM_ERR_WORKSPACE), 16-byte
+ * aligned, overwritten.  Type Q4_K only (QMM_ERR_TYPE); other rules as
+ * qmm_matmul_q8.  Calls that share a workspace must not overlap in time. */
+size_t qmm_streamk_ws_bytes(void);
+int qmm_matmul_q8_streamk(int type, const void* W, const int8_t* q, const float* d, const float* s, int nt,
+                          int od, int id, float* out, void* workspace, size_t ws_bytes, void* stream);
+
 /* The MMQ tile shape (QMM_KIND_MMQ_128X64, _64X64 or _64X64_SPLITK) that MMQ uses
  * for this shape: the one with the fewest (rounds of workgroups over the 256 CUs)
  * x (super-blocks per wave).  Negative status for invalid shapes.  Environment

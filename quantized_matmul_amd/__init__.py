@@ -46,7 +46,8 @@ EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul"
            "qmm_matmul_q8_kind", "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots",
            "qmm_mfma_tile_check", "qmm_strerror", "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize",
            "qmm_silu_mul_quantize", "qmm_residual_add", "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k",
-           "qmm_matmul_q8k", "qmm_q8k_superblock_sums", "qmm_pad_q6k")
+           "qmm_matmul_q8k", "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_streamk_ws_bytes",
+           "qmm_matmul_q8_streamk")
 
 
 class QmmError(RuntimeError):
@@ -91,13 +92,16 @@ def lib():
         L.qmm_matmul_q8k.argtypes = [I, P, P, P, P, I, I, I, P, P]
         L.qmm_q8k_superblock_sums.argtypes = [I, P, P, P, P, I, I, I, P, P]
         L.qmm_pad_q6k.argtypes = [P, P, ctypes.c_longlong, P]
+        L.qmm_streamk_ws_bytes.argtypes = []
+        L.qmm_streamk_ws_bytes.restype = Z
+        L.qmm_matmul_q8_streamk.argtypes = [I, P, P, P, P, I, I, I, P, P, Z, P]
         L.qmm_strerror.argtypes = [I]
         L.qmm_strerror.restype = ctypes.c_char_p
         for f in ("qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8", "qmm_matmul_q8_kind",
                   "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots", "qmm_mfma_tile_check",
                   "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize", "qmm_silu_mul_quantize", "qmm_residual_add",
                   "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k", "qmm_matmul_q8k",
-                  "qmm_q8k_superblock_sums", "qmm_pad_q6k"):
+                  "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_matmul_q8_streamk"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -172,6 +176,23 @@ def qmm_quantize_act(x: torch.Tensor, q=None, d=None, s=None, stream=None):
                                   _dev(d, torch.float32, "d"), _dev(s, torch.float32, "s"), _stream(stream)),
            "qmm_quantize_act")
     return q, d, s
+
+
+def qmm_streamk_ws_bytes() -> int:
+    return int(lib().qmm_streamk_ws_bytes())
+
+
+def qmm_matmul_q8_streamk(qtype: int, W: torch.Tensor, q: torch.Tensor, d: torch.Tensor, s: torch.Tensor, od: int,
+                          workspace: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """Stream-K matrix kernel (Q4_K): out f32 [nt, od]; workspace uint8 >= qmm_streamk_ws_bytes()."""
+    nt, idim = q.shape
+    if out is None:
+        out = torch.empty((nt, od), dtype=torch.float32, device=q.device)
+    _check(lib().qmm_matmul_q8_streamk(qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"),
+                                       _dev(d, torch.float32, "d"), _dev(s, torch.float32, "s"), nt, od, idim,
+                                       _dev(out, torch.float32, "out"), _dev(workspace, torch.uint8, "workspace"),
+                                       workspace.numel(), _stream(stream)), "qmm_matmul_q8_streamk")
+    return out
 
 
 def qmm_pad_q6k(W: torch.Tensor, out=None, stream=None) -> torch.Tensor:

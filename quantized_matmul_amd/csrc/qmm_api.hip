@@ -354,6 +354,29 @@ int qmm_pad_q6k(const void* src, void* dst, long long nblocks, void* stream)
     return launched(hipGetLastError());
 }
 
+size_t qmm_streamk_ws_bytes(void) { return qmm::mmq_streamk_ws_bytes(); }
+
+int qmm_matmul_q8_streamk(int type, const void* W, const int8_t* q, const float* d, const float* s, int nt, int od,
+                          int id, float* out, void* workspace, size_t ws_bytes, void* stream)
+{
+    int rc = validate_q8(type, W, q, d, s, nt, od, id, out);
+    if (rc)
+        return rc;
+    if (type != QMM_TYPE_Q4_K)
+        return QMM_ERR_TYPE;
+    if (!workspace)
+        return QMM_ERR_ARG;
+    if (!aligned16(workspace))
+        return QMM_ERR_ALIGN;
+    if (ws_bytes < qmm::mmq_streamk_ws_bytes())
+        return QMM_ERR_WORKSPACE;
+    if ((rc = check_device()))
+        return rc;
+    return launched(qmm::launch_mmq_streamk(reinterpret_cast<const uint8_t*>(W), q, d, s, nt, od, id, out,
+                                            reinterpret_cast<float*>(workspace),
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 int qmm_nt_switch(void) { return nt_switch_value(); }
 
 int qmm_dispatch_kind(int type, int nt, int od, int id)

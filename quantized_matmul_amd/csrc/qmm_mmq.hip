@@ -367,6 +367,153 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q4k_kernel(const uin
     }
 }
 
+// ------------------------------------------------------------------ Q4_K stream-K
+// The work of a launch is ntiles x nsb units (one tile, one super-block), numbered
+// tile-major, and cut into G equal contiguous ranges, one per workgroup
+// ([MMQ, section 12.3] on tile counts that do not fill the chip; the pages flag
+// non-deterministic split reductions, so the combine here has a fixed order).  A
+// workgroup walks its range tile segment by tile segment with the per-tile
+// kernel's pipeline; a tile it covers whole is stored directly, a partial tile goes
+// to its slot in the workspace (slot 0: the first tile of its range, 1: the last).
+// The fixup kernel then adds, for every split tile, the partials of the
+// workgroups covering it in workgroup order and stores the sum.  Workgroups are
+// numbered so that those on one XCD take consecutive ranges (one row block's tiles
+// stay in one L2).  G is a multiple of 8.
+__host__ __device__ inline long sk_first_unit(int g, long units, int G) { return (long)g * units / G; }
+
+template <int WR, int WC>
+__global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_streamk_kernel(const uint8_t* __restrict__ W,
+                                                                         const int8_t* __restrict__ q,
+                                                                         const float* __restrict__ dx,
+                                                                         const float* __restrict__ sx,
+                                                                         float* __restrict__ out, int nt, int od,
+                                                                         int id, float* __restrict__ ws, int G)
+{
+    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC, NW = WR * WC;
+    constexpr int QC = (BM * 8 + NTH - 1) / NTH;
+    constexpr int HC = (BM * 4 + NTH - 1) / NTH;
+    constexpr int XC = (BN * 16 + NTH - 1) / NTH;
+    constexpr int SC = (BN * 2 + NTH - 1) / NTH;
+    using SM = Q4Smem<BM, BN>;
+    __shared__ SM smb[2];
+
+    const int ntb = (nt + BN - 1) / BN;
+    const int ntiles = ntb * ((od + BM - 1) / BM);
+    const int nsb = id >> 8, nblk = id >> 5;
+    const long units = (long)ntiles * nsb;
+    const int g = (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
+    const long u0 = sk_first_unit(g, units, G), u1 = sk_first_unit(g + 1, units, G);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / WC, wc = wave % WC;
+    const int li = lane & 31, lh = lane >> 5;
+    const uint32_t row_bytes = (uint32_t)nsb * kQ4KBytes;
+    const int arow = wr * 32 + li, btok = wc * 32 + li;
+    const int first_tile = (int)(u0 / nsb);
+
+    for (long u = u0; u < u1;) {
+        const int tile = (int)(u / nsb);
+        const int k0 = (int)(u - (long)tile * nsb);
+        const int k1 = (int)min((long)nsb, k0 + (u1 - u));
+        const int row0 = (tile / ntb) * BM, tok0 = (tile % ntb) * BN;
+
+        v4i pq[QC], ph[HC], px[XC], pd[SC], ps[SC];
+        Q4Offs<QC, HC, XC, SC> offs;
+        q4_offsets<BM, BN, NTH, QC, HC, XC, SC>(offs, tid, row0, tok0, nt, od, id, nblk, row_bytes);
+        Q4Rsrc rs;
+        rs.w = buffer_rsrc(W + (size_t)row0 * row_bytes, (size_t)(od - row0) * row_bytes);
+        rs.x = buffer_rsrc(q + (size_t)tok0 * id, (size_t)(nt - tok0) * id);
+        rs.d = buffer_rsrc(dx + (size_t)tok0 * nblk, (size_t)(nt - tok0) * nblk * 4);
+        rs.s = buffer_rsrc(sx + (size_t)tok0 * nblk, (size_t)(nt - tok0) * nblk * 4);
+        auto prefetch = [&](int sbi) { q4_prefetch<QC, HC, XC, SC>(pq, ph, px, pd, ps, offs, rs, sbi); };
+        v16f accv = {}, accm = {};
+
+        prefetch(k0);
+        q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[0], pq, ph, px, pd, ps, tid, true);
+        prefetch(min(k0 + 1, k1 - 1));
+        __syncthreads();
+        for (int sb = k0; sb < k1; ++sb) {
+            const SM& sm = smb[(sb - k0) & 1];
+            v16i Ca0, Ca1;
+            v32f Pa;
+            q4_step<BM, BN>(sm, 0, arow, btok, lh, Ca0, Ca1, Pa, accm);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                v16i Cb0, Cb1;
+                v32f Pb;
+                if (p < 3)
+                    q4_step<BM, BN>(sm, p + 1, arow, btok, lh, Cb0, Cb1, Pb, accm);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    accv[i] = fmaf((float)Ca0[i], Pa[i], accv[i]);
+                    accv[i] = fmaf((float)Ca1[i], Pa[16 + i], accv[i]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (p < 3) {
+                    Ca0 = Cb0;
+                    Ca1 = Cb1;
+                    Pa = Pb;
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[(sb - k0 + 1) & 1], pq, ph, px, pd, ps, tid, sb + 1 < k1);
+            prefetch(min(sb + 2, k1 - 1));
+            __syncthreads();
+        }
+        const v16f v = accv + accm;
+        if (k0 == 0 && k1 == nsb) {
+            store_tile(v, out, nt, od, tok0 + btok, row0 + wr * 32, lh);
+        } else {
+            float* slot = ws + ((size_t)(2 * g + (tile == first_tile ? 0 : 1)) * NW + wave) * 1024;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                slot[i * 64 + lane] = v[i];
+        }
+        u += k1 - k0;
+    }
+}
+
+// One workgroup per tile: a tile split over several workgroups gets the sum of
+// their partials, added in workgroup order; a tile one workgroup covered whole
+// was stored by it.
+template <int WR, int WC>
+__global__ __launch_bounds__(64 * WR * WC) void mmq_streamk_fixup_kernel(const float* __restrict__ ws,
+                                                                        float* __restrict__ out, int nt, int od,
+                                                                        int nsb, int G)
+{
+    constexpr int BM = 32 * WR, BN = 32 * WC, NW = WR * WC;
+    const int ntb = (nt + BN - 1) / BN;
+    const int ntiles = ntb * ((od + BM - 1) / BM);
+    const int tile = blockIdx.x;
+    if (tile >= ntiles)
+        return;
+    const long units = (long)ntiles * nsb;
+    const long t0 = (long)tile * nsb, t1 = t0 + nsb;
+    // workgroups whose ranges meet [t0, t1): the last g with first unit <= t0 ...
+    int glo = (int)(t0 * G / units);
+    while (glo + 1 < G && sk_first_unit(glo + 1, units, G) <= t0)
+        ++glo;
+    while (glo > 0 && sk_first_unit(glo, units, G) > t0)
+        --glo;
+    if (sk_first_unit(glo + 1, units, G) >= t1)
+        return;  // one workgroup covered the whole tile
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wr = wave / WC, wc = wave % WC, li = lane & 31, lh = lane >> 5;
+    v16f v = {};
+    for (int gg = glo; gg < G && sk_first_unit(gg, units, G) < t1; ++gg) {
+        if (sk_first_unit(gg + 1, units, G) <= sk_first_unit(gg, units, G))
+            continue;  // an empty range
+        const int slot = (int)(sk_first_unit(gg, units, G) / nsb) == tile ? 0 : 1;
+        const float* src = ws + ((size_t)(2 * gg + slot) * NW + wave) * 1024;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            v[i] += src[i * 64 + lane];
+    }
+    const int row0 = (tile / ntb) * BM, tok0 = (tile % ntb) * BN;
+    store_tile(v, out, nt, od, tok0 + wc * 32 + li, row0 + wr * 32, lh);
+}
+
 // ------------------------------------------------------------------ Q6_K
 // Groups of 16 weights: v_mfma_i32_32x32x16_i8 (lane l: row/token l%32, K bytes
 // 8*(l/32) .. +7).  Codes are rebuilt and centred at staging time into signed
@@ -907,6 +1054,25 @@ int mmq_tile_choice(int nt, int od, int id)
     if (c1 <= c2 && c1 <= c3)
         return 1;
     return c2 <= c3 ? 2 : 3;
+}
+
+// Stream-K launch (Q4_K): 128 x 64 tiles, 256 workgroups (one per CU at this tile's
+// LDS size).  Workspace: 2 partial tiles per workgroup.
+constexpr int kStreamKGroups = 256;
+
+size_t mmq_streamk_ws_bytes() { return (size_t)kStreamKGroups * 2 * 128 * 64 * sizeof(float); }
+
+hipError_t launch_mmq_streamk(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od,
+                              int id, float* out, float* ws, hipStream_t st)
+{
+    const int G = kStreamKGroups;
+    hipLaunchKernelGGL((mmq_q4k_streamk_kernel<4, 2>), dim3(G), dim3(512), 0, st, W, q, d, s, out, nt, od, id, ws, G);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int ntiles = ((nt + 63) / 64) * ((od + 127) / 128);
+    hipLaunchKernelGGL((mmq_streamk_fixup_kernel<4, 2>), dim3(ntiles), dim3(512), 0, st, ws, out, nt, od, id / 256, G);
+    return hipGetLastError();
 }
 
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,

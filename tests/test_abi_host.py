@@ -139,6 +139,19 @@ def test_pad_q6k_validation():
         assert L.qmm_matmul_q8(qmm.QMM_TYPE_Q6_K_P224, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_DEVICE
 
 
+def test_streamk_validation():
+    L = qmm.lib()
+    p = ctypes.c_void_p(1 << 20)
+    n = qmm.qmm_streamk_ws_bytes()
+    assert n == 256 * 2 * 128 * 64 * 4
+    assert L.qmm_matmul_q8_streamk(1, p, p, p, p, 9, 4, 256, p, None, n, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_matmul_q8_streamk(2, p, p, p, p, 9, 4, 256, p, p, n, None) == qmm.QMM_ERR_TYPE
+    assert L.qmm_matmul_q8_streamk(1, p, p, p, p, 9, 4, 256, p, p, n - 1, None) == qmm.QMM_ERR_WORKSPACE
+    assert L.qmm_matmul_q8_streamk(1, p, p, p, p, 9, 4, 256, p, ctypes.c_void_p((1 << 20) + 4), n, None) == \
+        qmm.QMM_ERR_ALIGN
+    assert L.qmm_matmul_q8_streamk(1, p, p, p, p, 9, 4, 300, p, p, n, None) == qmm.QMM_ERR_SHAPE
+
+
 def test_no_device_is_an_error_not_a_fallback():
     import torch
     if torch.cuda.is_available():
