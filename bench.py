@@ -45,8 +45,12 @@ per32_same_shapes gives the per-32 kernel's rate from the same process.
 Workload "formats": Q4_0 and Q8_0 (and Q4_K for comparison) at 12288 x 4096, nt = 1
 and nt = 512.  value = HBM GB/s of the Q4_0 vector kernel at nt = 1.
 
+Workload "streamk": the Q4_K matrix shapes of the diffusion-LM step (4096x4096 and
+12288x4096 at nt = 256) and of prefill (nt = 512), on the per-tile dispatch and on
+the stream-K kernel (two launches: the kernel and its fixup), same inputs.
+
 Options: --gpus N (1 only), --steps K, --warmup W, --workload
-{q4k_decode_prefill, q6k_head, dllm_step, fused_quantize, q8k_prefill, formats}, --no-cpu-baseline,
+{q4k_decode_prefill, q6k_head, dllm_step, fused_quantize, q8k_prefill, formats, streamk}, --no-cpu-baseline,
 --copy-calibration
 MIB (before warm-up, run five plain device copies of MIB MiB between two spin-kernel
 markers, for scaling the HBM counters of a profiled run).
@@ -83,7 +87,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q4k_decode_prefill",
                     choices=["q4k_decode_prefill", "q6k_head", "dllm_step", "fused_quantize", "q8k_prefill",
-                             "formats"])
+                             "formats", "streamk"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     return ap.parse_args()
@@ -126,7 +130,8 @@ def mmq_kernel(qmm, nt, od, idim):
 class Call:
     """One matmul of the step: weights (rotating copies), activations, buffers."""
 
-    def __init__(self, torch, qmm, qtype, od, idim, nt, seed, outliers, copies=None, label="", x=None, q8k=False):
+    def __init__(self, torch, qmm, qtype, od, idim, nt, seed, outliers, copies=None, label="", x=None, q8k=False,
+                 streamk=None):
         self.qtype, self.od, self.idim, self.nt, self.q8k = qtype, od, idim, nt, q8k
         self.label = label or f"{'Q4_K' if qtype == 1 else 'Q6_K'} {od}x{idim} nt={nt}" + (" Q8_K" if q8k else "")
         dev = torch.device("cuda:0")
@@ -165,6 +170,10 @@ class Call:
                       P(self.s.data_ptr()), st)
         self.margs = [(I(qtype), P(w.data_ptr()), P(self.q.data_ptr()), P(self.d.data_ptr()),
                        P(self.s.data_ptr()), I(nt), I(od), I(idim), P(self.out.data_ptr()), st) for w in self.W]
+        if streamk is not None:  # the stream-K kernel, with its workspace
+            self.mfn = self.L.qmm_matmul_q8_streamk
+            self.margs = [a[:9] + (P(streamk.data_ptr()), ctypes.c_size_t(streamk.numel()), st) for a in self.margs]
+            self.label += " stream-K"
 
     def quantize(self):
         rc = self.qfn(*self.qargs)
@@ -202,6 +211,16 @@ def build_calls(torch, qmm, workload):
             calls.append(per32)
             calls.append(Call(torch, qmm, Q4, od, idim, 512, seed=seed, outliers=True, copies=per32.W, x=per32.x,
                               q8k=True))
+    elif workload == "streamk":
+        # the Q4_K matrix shapes of the diffusion-LM step (L = 256) and of prefill
+        # (nt = 512), per-tile dispatch and stream-K on the same weights and inputs
+        ws = torch.empty(qmm.qmm_streamk_ws_bytes(), dtype=torch.uint8, device="cuda:0")
+        for od, idim, nt, seed in ((4096, 4096, 256, 50), (12288, 4096, 256, 51), (12288, 4096, 512, 52),
+                                   (4096, 12288, 512, 53)):
+            base = Call(torch, qmm, Q4, od, idim, nt, seed=seed, outliers=nt == 512)
+            calls.append(base)
+            calls.append(Call(torch, qmm, Q4, od, idim, nt, seed=seed, outliers=nt == 512, copies=base.W,
+                              x=base.x, streamk=ws))
     elif workload == "formats":
         # Q4_0 and Q8_0 at the 12288 x 4096 shape, decode and prefill, beside Q4_K
         for qt in (qmm.QMM_TYPE_Q4_0, qmm.QMM_TYPE_Q8_0, Q4):
@@ -607,6 +626,22 @@ def main():
                                      "speedup_q8k": round(t32 / t8, 3)}
         line["config"] = {"workload": "q8k_prefill", "shapes": "Q4_K 12288x4096 and 4096x12288, nt=512, "
                           "1% outliers x20", "activations": "Q8_K (one scale per 256) vs per-32"}
+    elif args.workload == "streamk":
+        sk = [c for c in calls if c.label.endswith("stream-K")]
+        tiles = [c for c in calls if not c.label.endswith("stream-K")]
+        ksum = lambda cs: sum(float(np.mean(c.k_ms)) * 1e-3 for c in cs)  # noqa: E731
+        line.update(metric="Q4_K matmul, stream-K: int8 TOP/s over the diffusion-LM and prefill shapes",
+                    value=round(sum(c.ops for c in sk) / ksum(sk) / 1e12, 2), unit="TOP/s")
+        m = max(sk, key=lambda c: c.ops / float(np.mean(c.k_ms)))
+        km = float(np.mean(m.k_ms)) * 1e-3
+        line["roofline"] = {"bound": "mfma", "achieved": round(m.ops / km / 1e12, 2), "peak": INT8_PEAK_TOPS,
+                            "unit": "TFLOP/s", "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4), "traffic": None,
+                            "kernel": "mmq_q4k_streamk_kernel<4,2> + fixup", "call": m.label,
+                            "ops_per_launch": int(m.ops)}
+        line["per_tile_dispatch"] = {"value": round(sum(c.ops for c in tiles) / ksum(tiles) / 1e12, 2),
+                                     "unit": "TOP/s", "speedup_streamk": round(ksum(tiles) / ksum(sk), 3)}
+        line["config"] = {"workload": "streamk", "shapes": "Q4_K 4096x4096 and 12288x4096 at nt=256; "
+                          "12288x4096 and 4096x12288 at nt=512"}
     elif args.workload == "formats":
         by = {c.label: c for c in calls}
         k = lambda lab: float(np.mean(by[lab].k_ms)) * 1e-3  # noqa: E731
