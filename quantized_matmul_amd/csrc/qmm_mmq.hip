@@ -474,9 +474,10 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_streamk_kernel(const 
     }
 }
 
-// One workgroup per tile: a tile split over several workgroups gets the sum of
-// their partials, added in workgroup order; a tile one workgroup covered whole
-// was stored by it.
+// One workgroup per range boundary g = 1 .. G-1: a boundary inside a tile splits it;
+// the first boundary inside a tile adds the partials of the workgroups covering the
+// tile, in workgroup order, and stores the sum (a tile one workgroup covered whole
+// was stored by that workgroup).
 template <int WR, int WC>
 __global__ __launch_bounds__(64 * WR * WC) void mmq_streamk_fixup_kernel(const float* __restrict__ ws,
                                                                         float* __restrict__ out, int nt, int od,
@@ -485,23 +486,20 @@ __global__ __launch_bounds__(64 * WR * WC) void mmq_streamk_fixup_kernel(const f
     constexpr int BM = 32 * WR, BN = 32 * WC, NW = WR * WC;
     const int ntb = (nt + BN - 1) / BN;
     const int ntiles = ntb * ((od + BM - 1) / BM);
-    const int tile = blockIdx.x;
-    if (tile >= ntiles)
-        return;
     const long units = (long)ntiles * nsb;
+    const int b = blockIdx.x + 1;
+    const long ub = sk_first_unit(b, units, G);
+    if (b >= G || ub >= units || ub % nsb == 0)
+        return;  // not a boundary inside a tile
+    const int tile = (int)(ub / nsb);
     const long t0 = (long)tile * nsb, t1 = t0 + nsb;
-    // workgroups whose ranges meet [t0, t1): the last g with first unit <= t0 ...
-    int glo = (int)(t0 * G / units);
-    while (glo + 1 < G && sk_first_unit(glo + 1, units, G) <= t0)
-        ++glo;
-    while (glo > 0 && sk_first_unit(glo, units, G) > t0)
-        --glo;
-    if (sk_first_unit(glo + 1, units, G) >= t1)
-        return;  // one workgroup covered the whole tile
+    if (sk_first_unit(b - 1, units, G) > t0)
+        return;  // an earlier boundary inside this tile does the sum
+    // workgroups b-1, b, ... cover the tile (b-1 holds its first unit)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int wr = wave / WC, wc = wave % WC, li = lane & 31, lh = lane >> 5;
     v16f v = {};
-    for (int gg = glo; gg < G && sk_first_unit(gg, units, G) < t1; ++gg) {
+    for (int gg = b - 1; gg < G && sk_first_unit(gg, units, G) < t1; ++gg) {
         if (sk_first_unit(gg + 1, units, G) <= sk_first_unit(gg, units, G))
             continue;  // an empty range
         const int slot = (int)(sk_first_unit(gg, units, G) / nsb) == tile ? 0 : 1;
@@ -1070,8 +1068,16 @@ hipError_t launch_mmq_streamk(const uint8_t* W, const int8_t* q, const float* d,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const int ntiles = ((nt + 63) / 64) * ((od + 127) / 128);
-    hipLaunchKernelGGL((mmq_streamk_fixup_kernel<4, 2>), dim3(ntiles), dim3(512), 0, st, ws, out, nt, od, id / 256, G);
+    // the fixup only where a range boundary falls inside a tile
+    const long nsb = id / 256, units = (long)((nt + 63) / 64) * ((od + 127) / 128) * nsb;
+    bool split = false;
+    for (int g = 1; g < G && !split; ++g) {
+        const long u = sk_first_unit(g, units, G);
+        split = u < units && u % nsb != 0;
+    }
+    if (!split)
+        return hipSuccess;
+    hipLaunchKernelGGL((mmq_streamk_fixup_kernel<4, 2>), dim3(G - 1), dim3(512), 0, st, ws, out, nt, od, (int)nsb, G);
     return hipGetLastError();
 }
 
