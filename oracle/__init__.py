@@ -21,6 +21,7 @@ TYPE_Q6_K = 2
 TYPE_Q6_K_P224 = 3   # Q6_K blocks padded to 224 bytes
 TYPE_Q4_0 = 4        # 18-byte blocks of 32 weights
 TYPE_Q8_0 = 5        # 34-byte blocks of 32 weights
+TYPE_Q5_K = 6        # 176-byte super-blocks (5-bit codes)
 
 CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-std=c11"]
 
@@ -191,7 +192,7 @@ def decode_block(qtype: int, block: np.ndarray):
     codes = np.zeros(256, np.int32)
     _check(lib().oracle_decode_block(qtype, _p(b), _p(d), _p(dmin), _p(sc), _p(m), _p(codes)),
            "oracle_decode_block")
-    if qtype == TYPE_Q4_K:
+    if qtype in (TYPE_Q4_K, TYPE_Q5_K):
         return dict(d=float(d[0]), dmin=float(dmin[0]), sc=sc[:8].copy(), m=m[:8].copy(), codes=codes)
     return dict(d=float(d[0]), sc=sc.copy(), codes=codes)
 

@@ -38,6 +38,10 @@
  *       34-byte size only; the public GGUF layout).
  *   R21 Q4_0 / Q8_0 rows are read in groups of eight blocks (256 weights); a row
  *       length must be a multiple of 256 like the K-quants.
+ *   R22 Q5_K block (the pages name the type only): the public GGUF layout -- d,
+ *       dmin, the 12 scale bytes of Q4_K, 32 bytes qh, 128 bytes qs; element
+ *       32j + l has low nibble as Q4_K's code and high bit = bit j of qh[l];
+ *       code = nibble | 16 * bit (0..31), w = d * sc_j * code - dmin * m_j.
  *   R19 Q8_K activations: the per-32 rules R2/R3 applied to blocks of 256
  *       (d = amax / 127, q = roundf(x / d), zero block -> 0); the 16-value group
  *       sums are the exact integer sums of the codes, stored as f32.
@@ -51,7 +55,8 @@
  * one running sum, 9 silu with exp(+g), 10 Q8_K scale from the first 32 values of
  * the block only, 11 Q8_K min term from the first 16-value sum of each sub-block,
  * 12 Q4_0 offset 8 dropped, 13 Q4_0 nibbles read interleaved (element 2l low, 2l+1
- * high nibble of byte l) instead of element l low, l + 16 high.
+ * high nibble of byte l) instead of element l low, l + 16 high, 14 Q5_K high bit
+ * dropped.
  */
 #ifndef OQ_MUTATE
 #define OQ_MUTATE 0
@@ -74,6 +79,9 @@
  * 34-byte block), read in groups of eight consecutive blocks = 256 weights. */
 #define OQ_TYPE_Q4_0 4
 #define OQ_TYPE_Q8_0 5
+/* Q5_K (R22): 176 bytes = f16 d | f16 dmin | 12 scale bytes packed as Q4_K's | 32
+ * bytes of high bits | 128 bytes of low nibbles arranged as Q4_K's codes. */
+#define OQ_TYPE_Q5_K 6
 
 /* f16 bits -> f64, exact (normal, subnormal, zero; inf/nan kept as such). */
 static double f16_bits_to_f64(uint16_t h)
@@ -144,6 +152,38 @@ static void q4k_decode(const uint8_t* B, q4k_block* o)
 #endif
         }
     }
+}
+
+static void q5k_decode(const uint8_t* B, q4k_block* o)
+{
+    o->d = f16_bits_to_f64(rd_u16(B + 0));
+    o->dmin = f16_bits_to_f64(rd_u16(B + 2));
+    const uint8_t* s12 = B + 4;
+    const uint8_t* qh = B + 16;
+    const uint8_t* qs = B + 48;
+    for (int j = 0; j < 8; ++j)
+        q4k_scale_min(s12, j, &o->sc[j], &o->m[j]);
+    for (int j = 0; j < 8; ++j) {
+        int p = j >> 1;
+        for (int l = 0; l < 32; ++l) {
+            uint8_t byte = qs[32 * p + l];
+            int lo = (j & 1) ? (byte >> 4) : (byte & 0x0F);
+#if OQ_MUTATE == 14
+            int hi = 0;
+#else
+            int hi = (qh[l] >> j) & 1;
+#endif
+            o->q[32 * j + l] = lo | (hi << 4);
+        }
+    }
+}
+
+static void k4_decode(int type, const uint8_t* B, q4k_block* o)
+{
+    if (type == OQ_TYPE_Q5_K)
+        q5k_decode(B, o);
+    else
+        q4k_decode(B, o);
 }
 
 /* ---- O2. Q6_K super-block (210 bytes) ------------------------------------
@@ -357,14 +397,17 @@ static size_t blk_bytes(int type)
     case OQ_TYPE_Q6_K: return 210;
     case OQ_TYPE_Q6_K_P224: return 224;
     case OQ_TYPE_Q4_0: return 8 * 18;
+    case OQ_TYPE_Q5_K: return 176;
     default: return 8 * 34;
     }
 }
 static int known_type(int type)
 {
     return type == OQ_TYPE_Q4_K || type == OQ_TYPE_Q6_K || type == OQ_TYPE_Q6_K_P224 || type == OQ_TYPE_Q4_0 ||
-           type == OQ_TYPE_Q8_0;
+           type == OQ_TYPE_Q8_0 || type == OQ_TYPE_Q5_K;
 }
+/* Q4_K and Q5_K: sub-blocks of 32 with a 6-bit scale and min, uncentred codes */
+static int is_k4(int type) { return type == OQ_TYPE_Q4_K || type == OQ_TYPE_Q5_K; }
 static int is_k6(int type) { return type == OQ_TYPE_Q6_K || type == OQ_TYPE_Q6_K_P224; }
 static int is_b32(int type) { return type == OQ_TYPE_Q4_0 || type == OQ_TYPE_Q8_0; }
 
@@ -431,8 +474,8 @@ int oracle_subblock_dots(int type, const uint8_t* W, const int8_t* q, int nt, in
             q4k_block w4;
             q6k_block w6;
             b32_group w3;
-            if (type == OQ_TYPE_Q4_K)
-                q4k_decode(B, &w4);
+            if (is_k4(type))
+                k4_decode(type, B, &w4);
             else if (is_k6(type))
                 q6k_decode(B, &w6);
             else
@@ -441,7 +484,7 @@ int oracle_subblock_dots(int type, const uint8_t* W, const int8_t* q, int nt, in
                 const int8_t* qx = q + (size_t)t * id + 256 * b;
                 int32_t* dst = S + (((size_t)t * od + r) * nsb + b) * ng;
                 for (int g = 0; g < ng; ++g)
-                    dst[g] = type == OQ_TYPE_Q4_K ? dot_q4k_sub(&w4, qx, g)
+                    dst[g] = is_k4(type) ? dot_q4k_sub(&w4, qx, g)
                              : is_k6(type)        ? dot_q6k_group(&w6, qx, g)
                                                   : dot_b32(&w3, qx, g);
             }
@@ -465,9 +508,9 @@ static void one_output(int type, const uint8_t* Wrow, const int8_t* qx_t, const 
     for (int b = 0; b < nsb; ++b) {
         const uint8_t* B = Wrow + (size_t)b * bb;
         const int8_t* qx = qx_t + 256 * b;
-        if (type == OQ_TYPE_Q4_K) {
+        if (is_k4(type)) {
             q4k_block w;
-            q4k_decode(B, &w);
+            k4_decode(type, B, &w);
             for (int j = 0; j < 8; ++j) {
                 double dx = (double)d_t[8 * b + j];
                 double sx = (double)s_t[8 * b + j];
@@ -597,9 +640,9 @@ static void one_output_q8k(int type, const uint8_t* Wrow, const int8_t* qx_t, co
         const uint8_t* B = Wrow + (size_t)b * bb;
         const int8_t* qx = qx_t + 256 * b;
         double dx = (double)d_t[b];
-        if (type == OQ_TYPE_Q4_K) {
+        if (is_k4(type)) {
             q4k_block w;
-            q4k_decode(B, &w);
+            k4_decode(type, B, &w);
             for (int j = 0; j < 8; ++j) {
 #if OQ_MUTATE == 11
                 double bs = 2.0 * (double)bs_t[16 * b + 2 * j];
@@ -666,15 +709,15 @@ int oracle_q8k_superblock_sums(int type, const uint8_t* W, const int8_t* q, cons
             const uint8_t* B = W + ((size_t)r * nsb + b) * bb;
             q4k_block w4;
             q6k_block w6;
-            if (type == OQ_TYPE_Q4_K)
-                q4k_decode(B, &w4);
+            if (is_k4(type))
+                k4_decode(type, B, &w4);
             else
                 q6k_decode(B, &w6);
             for (int t = 0; t < nt; ++t) {
                 const int8_t* qx = q + (size_t)t * id + 256 * b;
                 const float* bs = bsum + (size_t)t * (id / 16) + 16 * b;
                 long s1 = 0, s2 = 0;
-                if (type == OQ_TYPE_Q4_K) {
+                if (is_k4(type)) {
                     for (int j = 0; j < 8; ++j) {
                         s1 += (long)w4.sc[j] * dot_q4k_sub(&w4, qx, j);
                         s2 += (long)w4.m[j] * ((long)bs[2 * j] + (long)bs[2 * j + 1]);
@@ -756,9 +799,9 @@ int oracle_matmul(int type, const uint8_t* W, const float* x, int nt, int od, in
  * codes[256]; Q6_K fills d, sc[16], codes[256] (stored 0..63). */
 int oracle_decode_block(int type, const uint8_t* B, double* d, double* dmin, int* sc, int* m, int* codes)
 {
-    if (type == OQ_TYPE_Q4_K) {
+    if (is_k4(type)) {
         q4k_block w;
-        q4k_decode(B, &w);
+        k4_decode(type, B, &w);
         *d = w.d;
         *dmin = w.dmin;
         memcpy(sc, w.sc, sizeof w.sc);

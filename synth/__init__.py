@@ -22,6 +22,9 @@ Block byte layouts follow the GGUF-style super-blocks the matmul consumes:
   high 2-bit fields | 16 int8 group scales | f16 d.  Uniform low/high bytes give
   6-bit codes uniform on {0..63} whatever the element-to-bit map; the group
   scales are drawn uniform on {-32..31}.
+* Q5_K (176 B per 256 weights): f16 d | f16 dmin | 12 scale bytes as Q4_K | 32
+  bytes of high bits | 128 bytes of low nibbles, all but d and dmin uniform bytes
+  (codes uniform on {0..31}).
 * Q4_0 (18 B per 32 weights: f16 d | 16 bytes of 4-bit codes) and Q8_0 (34 B per
   32 weights: f16 d | 32 int8 codes), generated in groups of eight blocks (256
   weights, 144 and 272 bytes): uniform code bytes (Q8_0 codes uniform on
@@ -47,6 +50,8 @@ TYPE_Q4_K = 1
 TYPE_Q6_K = 2
 TYPE_Q4_0 = 4
 TYPE_Q8_0 = 5
+TYPE_Q5_K = 6
+Q5K_BLOCK_BYTES = 176
 Q40_GROUP_BYTES = 8 * 18
 Q80_GROUP_BYTES = 8 * 34
 
@@ -132,6 +137,21 @@ def q6k_blocks(n_blocks: int, seed: int = 0, stream: int = STREAM_W, start_block
     return out
 
 
+def q5k_blocks(n_blocks: int, seed: int = 0, stream: int = STREAM_W, start_block: int = 0) -> np.ndarray:
+    """n_blocks Q5_K super-blocks as a [n_blocks, 176] uint8 array.
+
+    Per block, 24 draws: draw 0 gives d, draw 1 gives dmin, draws 2..23 give 176
+    random bytes of which bytes 4..175 (scales, high bits, codes) are kept.
+    """
+    per = 24
+    z = draws(seed, stream, n_blocks * per, start=start_block * per).reshape(n_blocks, per)
+    out = np.empty((n_blocks, Q5K_BLOCK_BYTES), dtype=np.uint8)
+    out[:, 4:] = _bytes_of(z[:, 2:])[:, 4:Q5K_BLOCK_BYTES]
+    out[:, 0:2] = _f16_field(z[:, 0]).reshape(-1, 1).view(np.uint8).reshape(n_blocks, 2)
+    out[:, 2:4] = _f16_field(z[:, 1]).reshape(-1, 1).view(np.uint8).reshape(n_blocks, 2)
+    return out
+
+
 def b32_groups(qtype: int, n_groups: int, seed: int = 0, stream: int = STREAM_W, start_group: int = 0) -> np.ndarray:
     """n_groups groups of eight Q4_0 or Q8_0 blocks as a [n_groups, 144 or 272] uint8 array.
 
@@ -156,6 +176,8 @@ def block_bytes(qtype: int) -> int:
         return Q4K_BLOCK_BYTES
     if qtype == TYPE_Q6_K:
         return Q6K_BLOCK_BYTES
+    if qtype == TYPE_Q5_K:
+        return Q5K_BLOCK_BYTES
     if qtype == TYPE_Q4_0:
         return Q40_GROUP_BYTES
     if qtype == TYPE_Q8_0:
@@ -170,6 +192,8 @@ def weights(qtype: int, od: int, idim: int, seed: int = 0, stream: int = STREAM_
     nb = od * (idim // QK)
     if qtype in (TYPE_Q4_0, TYPE_Q8_0):
         return b32_groups(qtype, nb, seed=seed, stream=stream).reshape(-1)
+    if qtype == TYPE_Q5_K:
+        return q5k_blocks(nb, seed=seed, stream=stream).reshape(-1)
     gen = q4k_blocks if qtype == TYPE_Q4_K else q6k_blocks
     return gen(nb, seed=seed, stream=stream).reshape(-1)
 

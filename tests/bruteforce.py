@@ -63,10 +63,10 @@ def q6k_weight(block: np.ndarray, e: int) -> float:
 
 def dequant(qtype: int, W: np.ndarray, od: int, idim: int) -> np.ndarray:
     """[od][idim] f64 dequantized weights."""
-    bb = 144 if qtype == 1 else 210
+    bb = {1: 144, 2: 210, 6: 176}[qtype]
     nsb = idim // 256
     blocks = W.reshape(od, nsb, bb)
-    f = q4k_weight if qtype == 1 else q6k_weight
+    f = {1: q4k_weight, 2: q6k_weight, 6: q5k_weight}[qtype]
     out = np.empty((od, idim), np.float64)
     for r in range(od):
         for b in range(nsb):
@@ -144,3 +144,19 @@ def b32_dequant(qtype: int, W: np.ndarray, od: int, idim: int) -> np.ndarray:
             for e in range(256):
                 out[r, 256 * g + e] = b32_weight(qtype, G[r, g], e)
     return out
+
+
+def q5k_code(block: np.ndarray, e: int) -> int:
+    """Q5_K code of element e: the Q4_K-arranged low nibble of bytes 48.. plus 16 *
+    bit j of high-bit byte 16 + l (e = 32 j + l)."""
+    j, l = divmod(e, 32)
+    byte = int(block[48 + 32 * (j // 2) + l])
+    lo = byte % 16 if j % 2 == 0 else byte // 16
+    return lo + 16 * ((int(block[16 + l]) >> j) & 1)
+
+
+def q5k_weight(block: np.ndarray, e: int) -> float:
+    d = f16(int(block[0]), int(block[1]))
+    dmin = f16(int(block[2]), int(block[3]))
+    sc, m = q4k_field(block, e // 32)
+    return d * sc * q5k_code(block, e) - dmin * m
