@@ -70,7 +70,13 @@ enum {
     QMM_TYPE_Q4_0 = 4,
     /* 34 bytes per 32 weights: f16 d, then 32 int8 codes, w = d*q (the pages give
      * the block size; the layout is the public one). */
-    QMM_TYPE_Q8_0 = 5
+    QMM_TYPE_Q8_0 = 5,
+    /* 176 bytes per 256 weights: f16 d | f16 dmin | the 12 scale bytes of Q4_K | 32
+     * bytes of high bits (bit j of byte l: fifth bit of element l of sub-block j) |
+     * 128 bytes of low nibbles arranged as Q4_K's.  code = nibble + 16*bit (0..31),
+     * w = d*sc*code - dmin*m.  The pages name the type only; this is the public
+     * layout. */
+    QMM_TYPE_Q5_K = 6
     /* Every type: a row is a whole number of 256-weight groups (id % 256 == 0): one
      * super-block, or eight consecutive 32-weight blocks (144 bytes for Q4_0, 272
      * for Q8_0), so rows of the 32-weight types stay 16-byte aligned. */
@@ -98,8 +104,9 @@ enum {
     QMM_KIND_MMQ_64X64_SPLITK = 5   /* 64 x 64, 8 waves in two groups splitting K */
 };
 
-/* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K, Q4_0), *210
- * (Q6_K), *224 (Q6_K padded) or *272 (Q8_0).  0 for an unknown type or a bad shape. */
+/* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K, Q4_0), *176
+ * (Q5_K), *210 (Q6_K), *224 (Q6_K padded) or *272 (Q8_0).  0 for an unknown type or
+ * a bad shape. */
 size_t qmm_weight_bytes(int type, int od, int id);
 
 /* Upload-time repack: nblocks Q6_K blocks of 210 bytes (src, any alignment) to
@@ -251,9 +258,10 @@ int qmm_rmsnorm(const float* x, const float* w, float eps, int nt, int id, float
 int qmm_silu_mul(const float* g, const float* u, int nt, int id, float* y, void* stream);
 
 /* Diagnostic: the integer stage of a kernel alone.  [GEMM, "The GPU path"]: each
- * scale group (32 weights for Q4_K, Q4_0 and Q8_0, 16 for Q6_K) is reduced as an
- * integer dot with its activation codes.  Writes S[t][r][b][g] = sum over group g
- * of 256-weight group b of row r of (code * qx) -- codes 0..15 uncentred for Q4_K,
+ * scale group (32 weights for Q4_K, Q5_K, Q4_0 and Q8_0, 16 for Q6_K) is reduced as
+ * an integer dot with its activation codes.  Writes S[t][r][b][g] = sum over group g
+ * of 256-weight group b of row r of (code * qx) -- codes 0..15 (0..31) uncentred for
+ * Q4_K (Q5_K),
  * (q6 - 32) for Q6_K, (nibble - 8) for Q4_0, the int8 for Q8_0 -- as int32,
  * computed by the unpack and dot code of the kernel `kind` (QMM_KIND_MMVQ: v_dot4
  * path, nt <= 8; QMM_KIND_MMQ: int8 MFMA path).

@@ -25,6 +25,7 @@ QMM_TYPE_Q6_K = 2
 QMM_TYPE_Q6_K_P224 = 3   # Q6_K blocks padded to 224 bytes (qmm_pad_q6k)
 QMM_TYPE_Q4_0 = 4        # 18-byte blocks of 32 weights
 QMM_TYPE_Q8_0 = 5        # 34-byte blocks of 32 weights
+QMM_TYPE_Q5_K = 6        # 176-byte super-blocks (5-bit codes)
 QMM_KIND_MMVQ = 1
 QMM_KIND_MMQ = 2
 QMM_KIND_MMQ_128X64 = 3
@@ -40,7 +41,7 @@ QMM_ERR_DEVICE = -6
 QMM_ERR_LAUNCH = -7
 
 BLOCK_BYTES = {QMM_TYPE_Q4_K: 144, QMM_TYPE_Q6_K: 210, QMM_TYPE_Q6_K_P224: 224,  # bytes per 256 weights
-               QMM_TYPE_Q4_0: 144, QMM_TYPE_Q8_0: 272}
+               QMM_TYPE_Q4_0: 144, QMM_TYPE_Q8_0: 272, QMM_TYPE_Q5_K: 176}
 
 EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8",
            "qmm_matmul_q8_kind", "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots",

@@ -42,7 +42,7 @@ size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 int check_type(int type)
 {
-    return (type >= QMM_TYPE_Q4_K && type <= QMM_TYPE_Q8_0) ? QMM_OK : QMM_ERR_TYPE;
+    return (type >= QMM_TYPE_Q4_K && type <= QMM_TYPE_Q5_K) ? QMM_OK : QMM_ERR_TYPE;
 }
 
 // bytes per 256 weights
@@ -53,6 +53,7 @@ size_t block_bytes(int type)
     case QMM_TYPE_Q6_K: return qmm::kQ6KBytes;
     case QMM_TYPE_Q6_K_P224: return qmm::kQ6KP224Bytes;
     case QMM_TYPE_Q4_0: return 8 * 18;
+    case QMM_TYPE_Q5_K: return qmm::kQ5KBytes;
     default: return 8 * 34;
     }
 }

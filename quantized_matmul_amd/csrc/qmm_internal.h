@@ -17,6 +17,7 @@ constexpr int kQK = 256;          // weights per super-block
 constexpr int kQ4KBytes = 144;    // Q4_K super-block
 constexpr int kQ6KBytes = 210;    // Q6_K super-block
 constexpr int kQ6KP224Bytes = 224;  // Q6_K super-block padded to 16-byte alignment (weight type 3)
+constexpr int kQ5KBytes = 176;    // Q5_K super-block (weight type 6)
 constexpr int kActBlock = 32;     // activation values per scale
 
 // Launchers (return hipError_t of the launch).  All pointers are device

@@ -40,32 +40,43 @@ namespace qmm {
 
 // ------------------------------------------------------------------ Q4_K
 
-template <int BM, int BN>
+// Q5 (Q5_K): also the 32 high-bit bytes of each row (stride 48).
+template <int BM, int BN, bool Q5 = false>
 struct __attribute__((aligned(16))) Q4Smem {
     static constexpr int QS_STRIDE = 144;   // 128 code bytes + 16 pad
     static constexpr int X_STRIDE = 272;    // 256 activation codes + 16 pad
+    static constexpr int H_STRIDE = 48;     // 32 high-bit bytes + 16 pad
     uint8_t qs[BM * QS_STRIDE];
     float wsc[8 * BM];                      // d * sc_j, [j][row]
     float wmn[8 * BM];                      // -dmin * m_j, [j][row]
     uint8_t xq[BN * X_STRIDE];
     float xd[8 * BN];                       // activation d, [j][token]
     float xs[8 * BN];                       // activation s, [j][token]
+    uint8_t qh[Q5 ? BM * H_STRIDE : 0];  // empty without Q5 (a clang extension): the Q4_K layout is unchanged
 };
 
-template <int QC, int HC, int XC, int SC>
+template <int QC, int HC, int XC, int SC, int BC = 1>
 struct Q4Offs {
-    uint32_t q[QC], h[HC], x[XC], s[SC];
+    uint32_t q[QC], h[HC], x[XC], s[SC], b5[BC];
 };
 
-template <int BM, int BN, int NTH, int QC, int HC, int XC, int SC>
-__device__ __forceinline__ void q4_offsets(Q4Offs<QC, HC, XC, SC>& o, int tid, int row0, int tok0, int nt, int od,
-                                           int id, int nblk, uint32_t row_bytes)
+// BC: high-bit chunk tasks (Q5_K only; two 16-byte chunks per row)
+template <int BM, int BN, int NTH, int QC, int HC, int XC, int SC, bool Q5 = false, int BC = 1>
+__device__ __forceinline__ void q4_offsets(Q4Offs<QC, HC, XC, SC, BC>& o, int tid, int row0, int tok0, int nt,
+                                           int od, int id, int nblk, uint32_t row_bytes)
 {
 #pragma unroll
     for (int k = 0; k < QC; ++k) {
         const int e = task<BM * 8, NTH, QC>(tid + k * NTH);
         const uint32_t r = (uint32_t)(min(row0 + (e >> 3), od - 1) - row0);
-        o.q[k] = r * row_bytes + 16 + 16 * (e & 7);
+        o.q[k] = r * row_bytes + (Q5 ? 48 : 16) + 16 * (e & 7);
+    }
+    if constexpr (Q5) {
+#pragma unroll
+        for (int k = 0; k < BC; ++k) {
+            const int e = task<BM * 2, NTH, BC>(tid + k * NTH);
+            o.b5[k] = (uint32_t)(min(row0 + (e >> 1), od - 1) - row0) * row_bytes + 16 + 16 * (e & 1);
+        }
     }
 #pragma unroll
     for (int k = 0; k < HC; ++k) {
@@ -90,11 +101,18 @@ struct Q4Rsrc {
     __amdgpu_buffer_rsrc_t w, x, d, s;
 };
 
-template <int QC, int HC, int XC, int SC>
+template <int QC, int HC, int XC, int SC, bool Q5 = false, int BC = 1>
 __device__ __forceinline__ void q4_prefetch(v4i (&pq)[QC], v4i (&ph)[HC], v4i (&px)[XC], v4i (&pd)[SC], v4i (&ps)[SC],
-                                            const Q4Offs<QC, HC, XC, SC>& o, const Q4Rsrc& rs, int sb)
+                                            const Q4Offs<QC, HC, XC, SC, BC>& o, const Q4Rsrc& rs, int sb,
+                                            v4i* pb5 = nullptr)
 {
-    const uint32_t ow = (uint32_t)sb * kQ4KBytes, ox = 256u * (uint32_t)sb, os = 32u * (uint32_t)sb;
+    const uint32_t ow = (uint32_t)sb * (Q5 ? kQ5KBytes : kQ4KBytes), ox = 256u * (uint32_t)sb,
+                   os = 32u * (uint32_t)sb;
+    if constexpr (Q5) {
+#pragma unroll
+        for (int k = 0; k < BC; ++k)
+            pb5[k] = bload16(rs.w, o.b5[k], ow);
+    }
 #pragma unroll
     for (int k = 0; k < QC; ++k)
         pq[k] = bload16(rs.w, o.q[k], ow);
@@ -113,12 +131,19 @@ __device__ __forceinline__ void q4_prefetch(v4i (&pq)[QC], v4i (&ph)[HC], v4i (&
 
 // valid == false (a super-block index past the end, in a split over K) stages
 // zero scales: that super-block then adds nothing, with no branch.
-template <int BM, int BN, int NTH, int QC, int HC, int XC, int SC>
-__device__ __forceinline__ void q4_stage(Q4Smem<BM, BN>& sm, const v4i (&pq)[QC], const v4i (&ph)[HC],
+template <int BM, int BN, int NTH, int QC, int HC, int XC, int SC, bool Q5 = false, int BC = 1>
+__device__ __forceinline__ void q4_stage(Q4Smem<BM, BN, Q5>& sm, const v4i (&pq)[QC], const v4i (&ph)[HC],
                                          const v4i (&px)[XC], const v4i (&pd)[SC], const v4i (&ps)[SC], int tid,
-                                         bool valid)
+                                         bool valid, const v4i* pb5 = nullptr)
 {
-    using SM = Q4Smem<BM, BN>;
+    using SM = Q4Smem<BM, BN, Q5>;
+    if constexpr (Q5) {
+#pragma unroll
+        for (int k = 0; k < BC; ++k) {
+            const int e = task<BM * 2, NTH, BC>(tid + k * NTH);
+            *reinterpret_cast<v4i*>(&sm.qh[(e >> 1) * SM::H_STRIDE + 16 * (e & 1)]) = pb5[k];
+        }
+    }
 #pragma unroll
     for (int k = 0; k < QC; ++k) {
         const int e = task<BM * 8, NTH, QC>(tid + k * NTH);
@@ -215,14 +240,30 @@ __device__ __forceinline__ void store_tile(const v16f& v, float* __restrict__ ou
 // super-block.  C0 / C1: the two int8 tile products; P: their scale products
 // (d*sc)[row] x dx[token] from one outer-product pair; the min term of the same
 // two sub-blocks is added into accm.
-template <int BM, int BN>
-__device__ __forceinline__ void q4_step(const Q4Smem<BM, BN>& sm, int p, int arow, int btok, int lh, v16i& C0,
+// The A operands of sub-blocks 2p and 2p + 1 for this lane (row arow, positions
+// 16 lh .. 16 lh + 15): one 16-byte read gives both (low and high nibbles); Q5_K adds
+// bit 2p / 2p + 1 of the row's high-bit bytes as the fifth code bit.
+template <int BM, int BN, bool Q5>
+__device__ __forceinline__ void q4_codes(const Q4Smem<BM, BN, Q5>& sm, int p, int arow, int lh, v4i& a0, v4i& a1)
+{
+    using SM = Q4Smem<BM, BN, Q5>;
+    const v4i a16 = *reinterpret_cast<const v4i*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
+    a0 = a16 & 0x0F0F0F0F;
+    a1 = (a16 >> 4) & 0x0F0F0F0F;
+    if constexpr (Q5) {
+        const v4i h16 = *reinterpret_cast<const v4i*>(&sm.qh[arow * SM::H_STRIDE + 16 * lh]);
+        a0 |= ((h16 >> (2 * p)) & 0x01010101) << 4;
+        a1 |= ((h16 >> (2 * p + 1)) & 0x01010101) << 4;
+    }
+}
+
+template <int BM, int BN, bool Q5 = false>
+__device__ __forceinline__ void q4_step(const Q4Smem<BM, BN, Q5>& sm, int p, int arow, int btok, int lh, v16i& C0,
                                         v16i& C1, v32f& P, v16f& accm)
 {
-    using SM = Q4Smem<BM, BN>;
-    // one 16-byte read gives sub-block 2p (low nibbles) and 2p + 1 (high nibbles)
-    const v4i a16 = *reinterpret_cast<const v4i*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
-    const v4i a0 = a16 & 0x0F0F0F0F, a1 = (a16 >> 4) & 0x0F0F0F0F;
+    using SM = Q4Smem<BM, BN, Q5>;
+    v4i a0, a1;
+    q4_codes<BM, BN, Q5>(sm, p, arow, lh, a0, a1);
     const v4i b0 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
     const v4i b1 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
     C0 = mfma_i8_k32(a0, b0);
@@ -238,20 +279,19 @@ __device__ __forceinline__ void q4_step(const Q4Smem<BM, BN>& sm, int p, int aro
 // at the end groups 1 .. KS-1 hand their 32 x 32 partial sums to group 0 through
 // LDS, which adds them in group order (a fixed order: the result does not
 // depend on timing).  It gives a tile grid with few tiles more waves.
-template <int WR, int WC, int KS, bool DUMP>
-__global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q4k_kernel(const uint8_t* __restrict__ W,
-                                                                    const int8_t* __restrict__ q,
-                                                                    const float* __restrict__ dx,
-                                                                    const float* __restrict__ sx,
-                                                                    float* __restrict__ out, int nt, int od,
-                                                                    int id, int32_t* __restrict__ S)
+template <int WR, int WC, int KS, bool DUMP, bool Q5>
+__device__ __forceinline__ void mmq_k4_body(const uint8_t* __restrict__ W, const int8_t* __restrict__ q,
+                                            const float* __restrict__ dx, const float* __restrict__ sx,
+                                            float* __restrict__ out, int nt, int od, int id,
+                                            int32_t* __restrict__ S)
 {
     constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;   // NTH: threads of one K group
     constexpr int QC = (BM * 8 + NTH - 1) / NTH;   // code chunks per thread
     constexpr int HC = (BM * 4 + NTH - 1) / NTH;   // header tasks per thread
     constexpr int XC = (BN * 16 + NTH - 1) / NTH;  // activation chunks per thread
     constexpr int SC = (BN * 2 + NTH - 1) / NTH;   // activation (d, s) float4 pairs per thread
-    using SM = Q4Smem<BM, BN>;
+    constexpr int BC = (BM * 2 + NTH - 1) / NTH;   // high-bit chunks per thread (Q5_K)
+    using SM = Q4Smem<BM, BN, Q5>;
     __shared__ SM smb[KS][2];
     static_assert(!DUMP || KS == 1, "the debug dump runs unsplit");
     static_assert((KS - 1) * WR * WC * 1024 * sizeof(float) <= sizeof(smb), "reduction scratch fits the tiles");
@@ -270,18 +310,18 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q4k_kernel(const uin
     const int nsb = id >> 8;
     const int nblk = id >> 5;
     const int niter = (nsb + KS - 1) / KS;
-    const uint32_t row_bytes = (uint32_t)nsb * kQ4KBytes;
+    const uint32_t row_bytes = (uint32_t)nsb * (Q5 ? kQ5KBytes : kQ4KBytes);
 
     // ---- prefetch registers (one super-block), per-thread offsets, resources
-    v4i pq[QC], ph[HC], px[XC], pd[SC], ps[SC];
-    Q4Offs<QC, HC, XC, SC> offs;
-    q4_offsets<BM, BN, NTH, QC, HC, XC, SC>(offs, tid, row0, tok0, nt, od, id, nblk, row_bytes);
+    v4i pq[QC], ph[HC], px[XC], pd[SC], ps[SC], pb5[BC];
+    Q4Offs<QC, HC, XC, SC, BC> offs;
+    q4_offsets<BM, BN, NTH, QC, HC, XC, SC, Q5, BC>(offs, tid, row0, tok0, nt, od, id, nblk, row_bytes);
     Q4Rsrc rs;
     rs.w = buffer_rsrc(W + (size_t)row0 * row_bytes, (size_t)(od - row0) * row_bytes);
     rs.x = buffer_rsrc(q + (size_t)tok0 * id, (size_t)(nt - tok0) * id);
     rs.d = buffer_rsrc(dx + (size_t)tok0 * nblk, (size_t)(nt - tok0) * nblk * 4);
     rs.s = buffer_rsrc(sx + (size_t)tok0 * nblk, (size_t)(nt - tok0) * nblk * 4);
-    auto prefetch = [&](int sbi) { q4_prefetch<QC, HC, XC, SC>(pq, ph, px, pd, ps, offs, rs, sbi); };
+    auto prefetch = [&](int sbi) { q4_prefetch<QC, HC, XC, SC, Q5, BC>(pq, ph, px, pd, ps, offs, rs, sbi, pb5); };
     v16f accv = {}, accm = {};
     const int arow = wr * 32 + li;   // this lane's row as an A operand
     const int btok = wc * 32 + li;   // this lane's token as a B operand
@@ -293,7 +333,7 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q4k_kernel(const uin
     // re-read at the end): a prefetch under a branch merges register values and
     // costs spills.
     prefetch(min(kg, nsb - 1));
-    q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[kg][0], pq, ph, px, pd, ps, tid, kg < nsb);
+    q4_stage<BM, BN, NTH, QC, HC, XC, SC, Q5, BC>(smb[kg][0], pq, ph, px, pd, ps, tid, kg < nsb, pb5);
     prefetch(min(KS + kg, nsb - 1));
     __syncthreads();
     for (int it = 0; it < niter; ++it) {
@@ -303,8 +343,8 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q4k_kernel(const uin
             // integer products only, written out per sub-block
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-                const v4i a16 = *reinterpret_cast<const v4i*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
-                const v4i a0 = a16 & 0x0F0F0F0F, a1 = (a16 >> 4) & 0x0F0F0F0F;
+                v4i a0, a1;
+                q4_codes<BM, BN, Q5>(sm, p, arow, lh, a0, a1);
                 const v4i b0 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
                 const v4i b1 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
                 const v16i C0 = mfma_i8_k32(a0, b0);
@@ -326,14 +366,14 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q4k_kernel(const uin
             // issued before the epilogue of step p, one step of results in flight.
             v16i Ca0, Ca1;
             v32f Pa;
-            q4_step<BM, BN>(sm, 0, arow, btok, lh, Ca0, Ca1, Pa, accm);
+            q4_step<BM, BN, Q5>(sm, 0, arow, btok, lh, Ca0, Ca1, Pa, accm);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 v16i Cb0, Cb1;
                 v32f Pb;
                 if (p < 3)
-                    q4_step<BM, BN>(sm, p + 1, arow, btok, lh, Cb0, Cb1, Pb, accm);
+                    q4_step<BM, BN, Q5>(sm, p + 1, arow, btok, lh, Cb0, Cb1, Pb, accm);
                 __builtin_amdgcn_sched_barrier(0);
                 // sub-blocks 2p (registers 0..15 of P) and 2p + 1 (16..31)
 #pragma unroll
@@ -354,7 +394,8 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q4k_kernel(const uin
         __builtin_amdgcn_sched_barrier(0);
         // smb[kg][(it + 1) & 1] was last read in iteration it - 1, before the
         // barrier; after the last iteration this fills a buffer nobody reads
-        q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[kg][(it + 1) & 1], pq, ph, px, pd, ps, tid, sb + KS < nsb);
+        q4_stage<BM, BN, NTH, QC, HC, XC, SC, Q5, BC>(smb[kg][(it + 1) & 1], pq, ph, px, pd, ps, tid, sb + KS < nsb,
+                                                      pb5);
         prefetch(min(sb + 2 * KS, nsb - 1));
         __syncthreads();
     }
@@ -365,6 +406,30 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q4k_kernel(const uin
             return;
         store_tile(v, out, nt, od, tok0 + btok, row0 + wr * 32, lh);
     }
+}
+
+template <int WR, int WC, int KS, bool DUMP>
+__global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q4k_kernel(const uint8_t* __restrict__ W,
+                                                                    const int8_t* __restrict__ q,
+                                                                    const float* __restrict__ dx,
+                                                                    const float* __restrict__ sx,
+                                                                    float* __restrict__ out, int nt, int od,
+                                                                    int id, int32_t* __restrict__ S)
+{
+    mmq_k4_body<WR, WC, KS, DUMP, false>(W, q, dx, sx, out, nt, od, id, S);
+}
+
+// Q5_K (176-byte blocks): the Q4_K kernel with the fifth code bit from the staged
+// high-bit bytes.
+template <int WR, int WC, int KS, bool DUMP>
+__global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q5k_kernel(const uint8_t* __restrict__ W,
+                                                                    const int8_t* __restrict__ q,
+                                                                    const float* __restrict__ dx,
+                                                                    const float* __restrict__ sx,
+                                                                    float* __restrict__ out, int nt, int od,
+                                                                    int id, int32_t* __restrict__ S)
+{
+    mmq_k4_body<WR, WC, KS, DUMP, true>(W, q, dx, sx, out, nt, od, id, S);
 }
 
 // ------------------------------------------------------------------ Q4_K stream-K
@@ -1010,9 +1075,12 @@ static hipError_t launch_tile(int type, const uint8_t* W, const int8_t* q, const
     else if (type == 4)
         hipLaunchKernelGGL((mmq_b32_kernel<WR, WC, KS, DUMP, false>), dim3(grid), dim3(64 * WR * WC * KS), 0, st,
                            W, q, d, out, nt, od, id, S);
-    else
+    else if (type == 5)
         hipLaunchKernelGGL((mmq_b32_kernel<WR, WC, KS, DUMP, true>), dim3(grid), dim3(64 * WR * WC * KS), 0, st,
                            W, q, d, out, nt, od, id, S);
+    else
+        hipLaunchKernelGGL((mmq_q5k_kernel<WR, WC, KS, DUMP>), dim3(grid), dim3(64 * WR * WC * KS), 0, st, W, q,
+                           d, s, out, nt, od, id, S);
     return hipGetLastError();
 }
 

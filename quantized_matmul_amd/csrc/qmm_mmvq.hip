@@ -107,8 +107,12 @@ __device__ __forceinline__ uint32_t q4k_scale_bytes(uint32_t h1, uint32_t h2, ui
     return plt2 ? lo : hi;
 }
 
-template <int NT, int R, bool DUMP>
-__global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q4k_kernel(
+// Q5 (Q5_K, 176-byte blocks): the same sub-block structure with a fifth code bit --
+// 32 bytes of high bits after the header (bit j of byte l: element l of sub-block
+// j), then the 128 code bytes; the lane's 16 high-bit bytes (positions 16 half ..)
+// supply bits 2p and 2p + 1.
+template <int NT, int R, bool DUMP, bool Q5>
+__device__ __forceinline__ void mmvq_k4_body(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ q, const float* __restrict__ dx,
     const float* __restrict__ sx, float* __restrict__ out, int od, int id, int32_t* __restrict__ S,
     int wpr, int gpw)
@@ -128,7 +132,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q4k_kernel(
     const int nsb = id >> 8;
     const int nblk = id >> 5;
     const int nwin = (nsb + 7) >> 3;
-    const size_t row_bytes = (size_t)nsb * kQ4KBytes;
+    constexpr uint32_t BB = Q5 ? kQ5KBytes : kQ4KBytes;
+    const size_t row_bytes = (size_t)nsb * BB;
     const bool live = row0 < od;  // a dead row group still reaches the barrier
 
     float acc[V];
@@ -141,13 +146,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q4k_kernel(
         const bool bv = b < nsb;
         const uint32_t bc = (uint32_t)(bv ? b : nsb - 1);
         // ---- loads: uniform row / token bases plus a 32-bit lane offset
-        const uint32_t oh = bc * kQ4KBytes, oq = oh + 16 + 32 * p + 16 * half;
-        uint4 hdr[R], qs[R];
+        const uint32_t oh = bc * BB, oq = oh + (Q5 ? 48 : 16) + 32 * p + 16 * half, o5 = oh + 16 + 16 * half;
+        uint4 hdr[R], qs[R], qh[Q5 ? R : 1];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint8_t* rp = W + (size_t)min(row0 + r, od - 1) * row_bytes;
             hdr[r] = *reinterpret_cast<const uint4*>(rp + oh);
             qs[r] = *reinterpret_cast<const uint4*>(rp + oq);
+            if constexpr (Q5)
+                qh[r] = *reinterpret_cast<const uint4*>(rp + o5);
         }
         const uint32_t ox = 256 * bc + 64 * p + 16 * half, od2 = 8 * bc + 2 * p;
         int4 xa[NT], xb[NT];
@@ -176,10 +183,21 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q4k_kernel(
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint4 h = hdr[r], w4 = qs[r];
-            const int lo0 = (int)(w4.x & 0x0F0F0F0Fu), lo1 = (int)(w4.y & 0x0F0F0F0Fu);
-            const int lo2 = (int)(w4.z & 0x0F0F0F0Fu), lo3 = (int)(w4.w & 0x0F0F0F0Fu);
-            const int hi0 = (int)((w4.x >> 4) & 0x0F0F0F0Fu), hi1 = (int)((w4.y >> 4) & 0x0F0F0F0Fu);
-            const int hi2 = (int)((w4.z >> 4) & 0x0F0F0F0Fu), hi3 = (int)((w4.w >> 4) & 0x0F0F0F0Fu);
+            int lo0 = (int)(w4.x & 0x0F0F0F0Fu), lo1 = (int)(w4.y & 0x0F0F0F0Fu);
+            int lo2 = (int)(w4.z & 0x0F0F0F0Fu), lo3 = (int)(w4.w & 0x0F0F0F0Fu);
+            int hi0 = (int)((w4.x >> 4) & 0x0F0F0F0Fu), hi1 = (int)((w4.y >> 4) & 0x0F0F0F0Fu);
+            int hi2 = (int)((w4.z >> 4) & 0x0F0F0F0Fu), hi3 = (int)((w4.w >> 4) & 0x0F0F0F0Fu);
+            if constexpr (Q5) {
+                // fifth bits: bit 2p of each high-bit byte for sub-block 2p, 2p + 1 for 2p + 1
+                const uint4 b5 = qh[r];
+                const uint32_t s0 = 2u * (uint32_t)p;
+                lo0 |= (int)(((b5.x >> s0) & 0x01010101u) << 4), lo1 |= (int)(((b5.y >> s0) & 0x01010101u) << 4);
+                lo2 |= (int)(((b5.z >> s0) & 0x01010101u) << 4), lo3 |= (int)(((b5.w >> s0) & 0x01010101u) << 4);
+                hi0 |= (int)(((b5.x >> (s0 + 1)) & 0x01010101u) << 4);
+                hi1 |= (int)(((b5.y >> (s0 + 1)) & 0x01010101u) << 4);
+                hi2 |= (int)(((b5.z >> (s0 + 1)) & 0x01010101u) << 4);
+                hi3 |= (int)(((b5.w >> (s0 + 1)) & 0x01010101u) << 4);
+            }
             const uint32_t sm = q4k_scale_bytes(h.y, h.z, h.w, selx, selz, plt2);
             const int sc0 = (int)(sm & 0xFF), sc1 = (int)((sm >> 8) & 0xFF);
             const float m0 = (float)((sm >> 16) & 0xFF), m1 = (float)(sm >> 24);
@@ -204,7 +222,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q4k_kernel(
                         dst[1] = f1;
                     }
                 } else {
-                    // sc * S in integers (|sc * S| < 2^22, exact in f32), then
+                    // sc * S in integers (|sc * S| < 2^23, exact in f32), then
                     // acc += d * (dx0 * sc0 S0 + dx1 * sc1 S1) - dmin * (m0 s0 + m1 s1)
                     const float x0 = (float)__mul24(sc0, s0), x1 = (float)__mul24(sc1, s1);
                     float a = acc[r * NTP + t];
@@ -219,6 +237,24 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q4k_kernel(
         const float v = wave_reduce_spread<V>(acc, lane);
         group_store<NT, R, NTP>(v, lane, wave, grp, wk, wpr, row0, od, out);
     }
+}
+
+template <int NT, int R, bool DUMP>
+__global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q4k_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ q, const float* __restrict__ dx,
+    const float* __restrict__ sx, float* __restrict__ out, int od, int id, int32_t* __restrict__ S,
+    int wpr, int gpw)
+{
+    mmvq_k4_body<NT, R, DUMP, false>(W, q, dx, sx, out, od, id, S, wpr, gpw);
+}
+
+template <int NT, int R, bool DUMP>
+__global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q5k_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ q, const float* __restrict__ dx,
+    const float* __restrict__ sx, float* __restrict__ out, int od, int id, int32_t* __restrict__ S,
+    int wpr, int gpw)
+{
+    mmvq_k4_body<NT, R, DUMP, true>(W, q, dx, sx, out, od, id, S, wpr, gpw);
 }
 
 // ------------------------------------------------------------------ Q6_K
@@ -528,9 +564,12 @@ static hipError_t launch_one(int type, const uint8_t* W, const int8_t* q, const 
     else if (type == 4)
         hipLaunchKernelGGL((mmvq_b32_kernel<NT, R, DUMP, false>), dim3(grid), block, 0, st, W, q, d, s, out, od, id,
                            S, wpr, gpw);
-    else
+    else if (type == 5)
         hipLaunchKernelGGL((mmvq_b32_kernel<NT, R, DUMP, true>), dim3(grid), block, 0, st, W, q, d, s, out, od, id,
                            S, wpr, gpw);
+    else
+        hipLaunchKernelGGL((mmvq_q5k_kernel<NT, R, DUMP>), dim3(grid), block, 0, st, W, q, d, s, out, od, id, S, wpr,
+                           gpw);
     return hipGetLastError();
 }
 

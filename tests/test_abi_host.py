@@ -46,6 +46,7 @@ def test_weight_bytes_closed_forms():
     assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q6_K_P224, 32000, 4096) == 32000 * 16 * 224
     assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q4_0, 12288, 4096) == 12288 * 16 * 144
     assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q8_0, 12288, 4096) == 12288 * 16 * 272
+    assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q5_K, 4096, 4096) == 4096 * 16 * 176
     assert qmm.qmm_weight_bytes(7, 1, 256) == 0
     assert qmm.qmm_weight_bytes(qmm.QMM_TYPE_Q4_K, 1, 300) == 0
 
@@ -73,7 +74,7 @@ def test_validation_before_device_work():
     p = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced
     mis = ctypes.c_void_p((1 << 20) + 4)
     big = 1 << 30
-    assert L.qmm_matmul(6, p, p, 1, 4, 256, p, p, big, None) == qmm.QMM_ERR_TYPE
+    assert L.qmm_matmul(7, p, p, 1, 4, 256, p, p, big, None) == qmm.QMM_ERR_TYPE
     assert L.qmm_matmul(0, p, p, 1, 4, 256, p, p, big, None) == qmm.QMM_ERR_TYPE
     assert L.qmm_matmul(1, None, p, 1, 4, 256, p, p, big, None) == qmm.QMM_ERR_ARG
     assert L.qmm_matmul(1, p, p, 0, 4, 256, p, p, big, None) == qmm.QMM_ERR_ARG

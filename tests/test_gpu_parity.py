@@ -204,7 +204,7 @@ def test_error_codes_leave_output_untouched():
     import ctypes
     st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     P = lambda t, off=0: ctypes.c_void_p(t.data_ptr() + off)
-    assert L.qmm_matmul(9, P(W), P(x), nt, od, idim, P(out), P(ws), ws.numel(), st) == qmm.QMM_ERR_TYPE
+    assert L.qmm_matmul(99, P(W), P(x), nt, od, idim, P(out), P(ws), ws.numel(), st) == qmm.QMM_ERR_TYPE
     assert L.qmm_matmul(Q4, P(W), P(x), nt, od, 300, P(out), P(ws), ws.numel(), st) == qmm.QMM_ERR_SHAPE
     assert L.qmm_matmul(Q4, P(W), P(x), 0, od, idim, P(out), P(ws), ws.numel(), st) == qmm.QMM_ERR_ARG
     assert L.qmm_matmul(Q4, P(W, 4), P(x), nt, od, idim, P(out), P(ws), ws.numel(), st) == qmm.QMM_ERR_ALIGN
