@@ -42,7 +42,7 @@ per 256 values, 16-value code sums; its own numerics) and, on the same weights a
 inputs, on the per-32 activations.  value = int8 TOP/s of the Q8_K matmul kernel;
 per32_same_shapes gives the per-32 kernel's rate from the same process.
 
-Workload "formats": Q4_0 and Q8_0 (and Q4_K for comparison) at 12288 x 4096, nt = 1
+Workload "formats": Q4_0, Q8_0 and Q5_K (and Q4_K for comparison) at 12288 x 4096, nt = 1
 and nt = 512.  value = HBM GB/s of the Q4_0 vector kernel at nt = 1.
 
 Workload "streamk": the Q4_K matrix shapes of the diffusion-LM step (4096x4096 and
@@ -223,11 +223,11 @@ def build_calls(torch, qmm, workload):
                               x=base.x, streamk=ws))
     elif workload == "formats":
         # Q4_0 and Q8_0 at the 12288 x 4096 shape, decode and prefill, beside Q4_K
-        for qt in (qmm.QMM_TYPE_Q4_0, qmm.QMM_TYPE_Q8_0, Q4):
+        for qt in (qmm.QMM_TYPE_Q4_0, qmm.QMM_TYPE_Q8_0, qmm.QMM_TYPE_Q5_K, Q4):
             shared = None
             for nt in (1, 512):
                 c = Call(torch, qmm, qt, 12288, 4096, nt, seed=40 + qt, outliers=nt > 8, copies=shared,
-                         label=f"{ {1: 'Q4_K', 4: 'Q4_0', 5: 'Q8_0'}[qt] } 12288x4096 nt={nt}")
+                         label=f"{ {1: 'Q4_K', 4: 'Q4_0', 5: 'Q8_0', 6: 'Q5_K'}[qt] } 12288x4096 nt={nt}")
                 shared = c.W
                 calls.append(c)
     elif workload == "q6k_head":
@@ -658,7 +658,7 @@ def main():
                                      "int8_frac": round(c.ops / k(lab) / 1e12 / INT8_PEAK_TOPS, 4)})
                               for lab, c in by.items()}
         line["config"] = {"workload": "formats", "shape": "12288x4096", "nt": [1, 512],
-                          "types": ["Q4_0", "Q8_0", "Q4_K"]}
+                          "types": ["Q4_0", "Q8_0", "Q5_K", "Q4_K"]}
     elif args.workload == "q6k_head":
         c, cp = dec[0], dec[1]
         k = float(np.mean(c.k_ms)) * 1e-3
