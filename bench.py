@@ -238,12 +238,17 @@ def build_calls(torch, qmm, workload):
         calls.append(Call(torch, qmm, qmm.QMM_TYPE_Q6_K_P224, 32000, 4096, 1, seed=3, outliers=False,
                           copies=padded, x=c6.x, label="Q6_K padded 32000x4096 nt=1"))
     else:  # dllm_step: 32 layers x (q, k, v, o, gate, up Q4_K; down Q6_K) at L = 256
-        shapes = [(Q4, 4096, 4096)] * 4 + [(Q4, 12288, 4096)] * 2 + [(Q6, 4096, 12288)]
-        # distinct weights per layer (4.34 GB per step): one seeded matrix per
-        # projection, copied to 32 distinct HBM places; one input per projection
+        # the down projections in the padded Q6_K layout, as the upload pads Q6_K
+        P6 = qmm.QMM_TYPE_Q6_K_P224
+        shapes = [(Q4, 4096, 4096)] * 4 + [(Q4, 12288, 4096)] * 2 + [(P6, 4096, 12288)]
+        # distinct weights per layer (4.34 GB per step, 4.46 GB with the padding): one
+        # seeded matrix per projection, copied to 32 distinct HBM places; one input
+        # per projection
         per_proj = []
         for p, (qt, od, idim) in enumerate(shapes):
-            w = torch.from_numpy(synth.weights(qt, od, idim, seed=100 + p)).to("cuda:0")
+            w = torch.from_numpy(synth.weights(Q6 if qt == P6 else qt, od, idim, seed=100 + p)).to("cuda:0")
+            if qt == P6:
+                w = qmm.qmm_pad_q6k(w)
             x = torch.from_numpy(synth.activations(256, idim, seed=200 + p)).to("cuda:0")
             per_proj.append(([w] + [w.clone() for _ in range(31)], x))
         for layer in range(32):
@@ -677,7 +682,7 @@ def main():
         line.update(value=round(ops / t / 1e12, 2), unit="TOP/s")
         line["note"] = "value = int8 ops of the 224 matmuls over the sum of their kernel times"
         line["config"] = {"workload": "dllm_step", "layers": 32, "canvas": 256, "hidden": 4096, "ffn": 12288,
-                          "matmuls_per_step": len(calls)}
+                          "matmuls_per_step": len(calls), "down_projection": "Q6_K padded to 224-byte blocks"}
         detail = detail[:7]
     line["detail"] = detail
     if cal:
