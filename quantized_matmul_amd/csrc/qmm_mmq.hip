@@ -821,7 +821,6 @@ struct __attribute__((aligned(16))) B32Smem {
 
 // byte-wise n - 8 for nibbles n in 0..15 held one per byte: t = n ^ 8 is n - 8
 // when bit 3 of t is clear; when it is set, filling the top four bits gives t - 16
-template <bool Q8>
 __device__ __forceinline__ uint32_t b32_center(uint32_t nib)
 {
     const uint32_t t = nib ^ 0x08080808u;
@@ -889,11 +888,11 @@ __device__ __forceinline__ void b32_stage(B32Smem<BM, BN>& sm, const uint32_t (&
             *reinterpret_cast<uint4*>(dst + 16) = make_uint4(cd[4], cd[5], cd[6], cd[7]);
         } else {
             *reinterpret_cast<uint4*>(dst) =
-                make_uint4(b32_center<Q8>(cd[0] & 0x0F0F0F0Fu), b32_center<Q8>(cd[1] & 0x0F0F0F0Fu),
-                           b32_center<Q8>(cd[2] & 0x0F0F0F0Fu), b32_center<Q8>(cd[3] & 0x0F0F0F0Fu));
+                make_uint4(b32_center(cd[0] & 0x0F0F0F0Fu), b32_center(cd[1] & 0x0F0F0F0Fu),
+                           b32_center(cd[2] & 0x0F0F0F0Fu), b32_center(cd[3] & 0x0F0F0F0Fu));
             *reinterpret_cast<uint4*>(dst + 16) =
-                make_uint4(b32_center<Q8>((cd[0] >> 4) & 0x0F0F0F0Fu), b32_center<Q8>((cd[1] >> 4) & 0x0F0F0F0Fu),
-                           b32_center<Q8>((cd[2] >> 4) & 0x0F0F0F0Fu), b32_center<Q8>((cd[3] >> 4) & 0x0F0F0F0Fu));
+                make_uint4(b32_center((cd[0] >> 4) & 0x0F0F0F0Fu), b32_center((cd[1] >> 4) & 0x0F0F0F0Fu),
+                           b32_center((cd[2] >> 4) & 0x0F0F0F0Fu), b32_center((cd[3] >> 4) & 0x0F0F0F0Fu));
         }
         sm.wsc[j * BM + r] = valid ? f16_bits_to_f32(bb[0] & 0xFFFF) : 0.f;
     }
