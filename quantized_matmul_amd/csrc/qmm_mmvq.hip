@@ -111,7 +111,96 @@ __device__ __forceinline__ uint32_t q4k_scale_bytes(uint32_t h1, uint32_t h2, ui
 // 32 bytes of high bits after the header (bit j of byte l: element l of sub-block
 // j), then the 128 code bytes; the lane's 16 high-bit bytes (positions 16 half ..)
 // supply bits 2p and 2p + 1.
-template <int NT, int R, bool DUMP, bool Q5>
+// Tokens T0 .. T0 + TN - 1 of one window: the activation loads, then the products
+// with each of the R rows' blocks (hdr, qs, qh already loaded), added into acc.
+template <int TN, int T0, int NTP, int R, bool DUMP, bool Q5>
+__device__ __forceinline__ void k4_tokens(
+    const int8_t* __restrict__ q, const float* __restrict__ dx, const float* __restrict__ sx, int id, int nblk,
+    uint32_t ox, uint32_t od2, bool bv, int half, int p, uint32_t selx, uint32_t selz, bool plt2,
+    const uint4 (&hdr)[R], const uint4 (&qs)[R], const uint4 (&qh)[Q5 ? R : 1], float (&acc)[R * NTP],
+    int32_t* __restrict__ S, int row0, int od, int nsb, int b)
+{
+    int4 xa[TN], xb[TN];
+    float2 dd[TN], ss[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+        const int8_t* qt = q + (size_t)(T0 + t) * id;
+        xa[t] = *reinterpret_cast<const int4*>(qt + ox);
+        xb[t] = *reinterpret_cast<const int4*>(qt + ox + 32);
+        dd[t] = *reinterpret_cast<const float2*>(dx + (size_t)(T0 + t) * nblk + od2);
+        ss[t] = *reinterpret_cast<const float2*>(sx + (size_t)(T0 + t) * nblk + od2);
+    }
+    // keep every load above this point: the wave waits once for all of them
+    __builtin_amdgcn_sched_barrier(0);
+    // a lane past the row end adds nothing; the min term of a sub-block is
+    // added by its half-0 lane only
+    float da[TN], db[TN], sa[TN], sb[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+        da[t] = bv ? dd[t].x : 0.f;
+        db[t] = bv ? dd[t].y : 0.f;
+        sa[t] = (bv && half == 0) ? ss[t].x : 0.f;
+        sb[t] = (bv && half == 0) ? ss[t].y : 0.f;
+    }
+    // ---- compute
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint4 h = hdr[r], w4 = qs[r];
+        int lo0 = (int)(w4.x & 0x0F0F0F0Fu), lo1 = (int)(w4.y & 0x0F0F0F0Fu);
+        int lo2 = (int)(w4.z & 0x0F0F0F0Fu), lo3 = (int)(w4.w & 0x0F0F0F0Fu);
+        int hi0 = (int)((w4.x >> 4) & 0x0F0F0F0Fu), hi1 = (int)((w4.y >> 4) & 0x0F0F0F0Fu);
+        int hi2 = (int)((w4.z >> 4) & 0x0F0F0F0Fu), hi3 = (int)((w4.w >> 4) & 0x0F0F0F0Fu);
+        if constexpr (Q5) {
+            // fifth bits: bit 2p of each high-bit byte for sub-block 2p, 2p + 1 for 2p + 1
+            const uint4 b5 = qh[r];
+            const uint32_t s0 = 2u * (uint32_t)p;
+            lo0 |= (int)(((b5.x >> s0) & 0x01010101u) << 4), lo1 |= (int)(((b5.y >> s0) & 0x01010101u) << 4);
+            lo2 |= (int)(((b5.z >> s0) & 0x01010101u) << 4), lo3 |= (int)(((b5.w >> s0) & 0x01010101u) << 4);
+            hi0 |= (int)(((b5.x >> (s0 + 1)) & 0x01010101u) << 4);
+            hi1 |= (int)(((b5.y >> (s0 + 1)) & 0x01010101u) << 4);
+            hi2 |= (int)(((b5.z >> (s0 + 1)) & 0x01010101u) << 4);
+            hi3 |= (int)(((b5.w >> (s0 + 1)) & 0x01010101u) << 4);
+        }
+        const uint32_t sm = q4k_scale_bytes(h.y, h.z, h.w, selx, selz, plt2);
+        const int sc0 = (int)(sm & 0xFF), sc1 = (int)((sm >> 8) & 0xFF);
+        const float m0 = (float)((sm >> 16) & 0xFF), m1 = (float)(sm >> 24);
+        const float dw = f16_bits_to_f32(h.x & 0xFFFF);
+        const float dm = f16_bits_to_f32(h.x >> 16);
+#pragma unroll
+        for (int t = 0; t < TN; ++t) {
+            int s0 = sdot4(lo0, xa[t].x, 0);
+            s0 = sdot4(lo1, xa[t].y, s0);
+            s0 = sdot4(lo2, xa[t].z, s0);
+            s0 = sdot4(lo3, xa[t].w, s0);
+            int s1 = sdot4(hi0, xb[t].x, 0);
+            s1 = sdot4(hi1, xb[t].y, s1);
+            s1 = sdot4(hi2, xb[t].z, s1);
+            s1 = sdot4(hi3, xb[t].w, s1);
+            if constexpr (DUMP) {
+                const int f0 = s0 + __shfl_xor(s0, 1, 64);
+                const int f1 = s1 + __shfl_xor(s1, 1, 64);
+                if (bv && row0 + r < od && half == 0) {
+                    int32_t* dst = S + (((size_t)(T0 + t) * od + row0 + r) * nsb + b) * 8 + 2 * p;
+                    dst[0] = f0;
+                    dst[1] = f1;
+                }
+            } else {
+                // sc * S in integers (|sc * S| < 2^23, exact in f32), then
+                // acc += d * (dx0 * sc0 S0 + dx1 * sc1 S1) - dmin * (m0 s0 + m1 s1)
+                const float x0 = (float)__mul24(sc0, s0), x1 = (float)__mul24(sc1, s1);
+                float a = acc[r * NTP + T0 + t];
+                a = fmaf(dw, fmaf(da[t], x0, db[t] * x1), a);
+                a = fmaf(-dm, fmaf(m0, sa[t], m1 * sb[t]), a);
+                acc[r * NTP + T0 + t] = a;
+            }
+        }
+    }
+}
+
+// TB < NT: the activations of tokens 0 .. TB - 1 are loaded and used before those
+// of the rest -- fewer registers (more resident waves) for a second round of load
+// latency per window.
+template <int NT, int R, bool DUMP, bool Q5, int TB = NT>
 __device__ __forceinline__ void mmvq_k4_body(
     const uint8_t* __restrict__ W, const int8_t* __restrict__ q, const float* __restrict__ dx,
     const float* __restrict__ sx, float* __restrict__ out, int od, int id, int32_t* __restrict__ S,
@@ -157,81 +246,11 @@ __device__ __forceinline__ void mmvq_k4_body(
                 qh[r] = *reinterpret_cast<const uint4*>(rp + o5);
         }
         const uint32_t ox = 256 * bc + 64 * p + 16 * half, od2 = 8 * bc + 2 * p;
-        int4 xa[NT], xb[NT];
-        float2 dd[NT], ss[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int8_t* qt = q + (size_t)t * id;
-            xa[t] = *reinterpret_cast<const int4*>(qt + ox);
-            xb[t] = *reinterpret_cast<const int4*>(qt + ox + 32);
-            dd[t] = *reinterpret_cast<const float2*>(dx + (size_t)t * nblk + od2);
-            ss[t] = *reinterpret_cast<const float2*>(sx + (size_t)t * nblk + od2);
-        }
-        // keep every load above this point: the wave waits once for all of them
-        __builtin_amdgcn_sched_barrier(0);
-        // a lane past the row end adds nothing; the min term of a sub-block is
-        // added by its half-0 lane only
-        float da[NT], db[NT], sa[NT], sb[NT];
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            da[t] = bv ? dd[t].x : 0.f;
-            db[t] = bv ? dd[t].y : 0.f;
-            sa[t] = (bv && half == 0) ? ss[t].x : 0.f;
-            sb[t] = (bv && half == 0) ? ss[t].y : 0.f;
-        }
-        // ---- compute
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint4 h = hdr[r], w4 = qs[r];
-            int lo0 = (int)(w4.x & 0x0F0F0F0Fu), lo1 = (int)(w4.y & 0x0F0F0F0Fu);
-            int lo2 = (int)(w4.z & 0x0F0F0F0Fu), lo3 = (int)(w4.w & 0x0F0F0F0Fu);
-            int hi0 = (int)((w4.x >> 4) & 0x0F0F0F0Fu), hi1 = (int)((w4.y >> 4) & 0x0F0F0F0Fu);
-            int hi2 = (int)((w4.z >> 4) & 0x0F0F0F0Fu), hi3 = (int)((w4.w >> 4) & 0x0F0F0F0Fu);
-            if constexpr (Q5) {
-                // fifth bits: bit 2p of each high-bit byte for sub-block 2p, 2p + 1 for 2p + 1
-                const uint4 b5 = qh[r];
-                const uint32_t s0 = 2u * (uint32_t)p;
-                lo0 |= (int)(((b5.x >> s0) & 0x01010101u) << 4), lo1 |= (int)(((b5.y >> s0) & 0x01010101u) << 4);
-                lo2 |= (int)(((b5.z >> s0) & 0x01010101u) << 4), lo3 |= (int)(((b5.w >> s0) & 0x01010101u) << 4);
-                hi0 |= (int)(((b5.x >> (s0 + 1)) & 0x01010101u) << 4);
-                hi1 |= (int)(((b5.y >> (s0 + 1)) & 0x01010101u) << 4);
-                hi2 |= (int)(((b5.z >> (s0 + 1)) & 0x01010101u) << 4);
-                hi3 |= (int)(((b5.w >> (s0 + 1)) & 0x01010101u) << 4);
-            }
-            const uint32_t sm = q4k_scale_bytes(h.y, h.z, h.w, selx, selz, plt2);
-            const int sc0 = (int)(sm & 0xFF), sc1 = (int)((sm >> 8) & 0xFF);
-            const float m0 = (float)((sm >> 16) & 0xFF), m1 = (float)(sm >> 24);
-            const float dw = f16_bits_to_f32(h.x & 0xFFFF);
-            const float dm = f16_bits_to_f32(h.x >> 16);
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                int s0 = sdot4(lo0, xa[t].x, 0);
-                s0 = sdot4(lo1, xa[t].y, s0);
-                s0 = sdot4(lo2, xa[t].z, s0);
-                s0 = sdot4(lo3, xa[t].w, s0);
-                int s1 = sdot4(hi0, xb[t].x, 0);
-                s1 = sdot4(hi1, xb[t].y, s1);
-                s1 = sdot4(hi2, xb[t].z, s1);
-                s1 = sdot4(hi3, xb[t].w, s1);
-                if constexpr (DUMP) {
-                    const int f0 = s0 + __shfl_xor(s0, 1, 64);
-                    const int f1 = s1 + __shfl_xor(s1, 1, 64);
-                    if (bv && row0 + r < od && half == 0) {
-                        int32_t* dst = S + (((size_t)t * od + row0 + r) * nsb + b) * 8 + 2 * p;
-                        dst[0] = f0;
-                        dst[1] = f1;
-                    }
-                } else {
-                    // sc * S in integers (|sc * S| < 2^23, exact in f32), then
-                    // acc += d * (dx0 * sc0 S0 + dx1 * sc1 S1) - dmin * (m0 s0 + m1 s1)
-                    const float x0 = (float)__mul24(sc0, s0), x1 = (float)__mul24(sc1, s1);
-                    float a = acc[r * NTP + t];
-                    a = fmaf(dw, fmaf(da[t], x0, db[t] * x1), a);
-                    a = fmaf(-dm, fmaf(m0, sa[t], m1 * sb[t]), a);
-                    acc[r * NTP + t] = a;
-                }
-            }
-        }
+        k4_tokens<TB, 0, NTP, R, DUMP, Q5>(q, dx, sx, id, nblk, ox, od2, bv, half, p, selx, selz, plt2, hdr, qs,
+                                            qh, acc, S, row0, od, nsb, b);
+        if constexpr (TB < NT)
+            k4_tokens<NT - TB, TB, NTP, R, DUMP, Q5>(q, dx, sx, id, nblk, ox, od2, bv, half, p, selx, selz, plt2,
+                                                     hdr, qs, qh, acc, S, row0, od, nsb, b);
     }
     if constexpr (!DUMP) {
         const float v = wave_reduce_spread<V>(acc, lane);
@@ -246,6 +265,29 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q4k_kernel(
     int wpr, int gpw)
 {
     mmvq_k4_body<NT, R, DUMP, false>(W, q, dx, sx, out, od, id, S, wpr, gpw);
+}
+
+// Token batches of the 4-row Q4_K / Q5_K kernels: loading the activations of TB
+// tokens at a time frees registers for more resident waves (Q5_K at 8 tokens: 166
+// instead of 256 registers plus a spill; Q5_K at 4 tokens: 123 instead of 171, four
+// waves per SIMD instead of two) and costs a round of load latency per batch.  The
+// table is measured on 4096-, 8192- and 12288-row matrices of 4096 and 12288 columns
+// (Q5_K at 8 tokens: 30.5 -> 18.0 us at 12288 x 4096; Q4_K at 7 tokens: 16.9 -> 14.9
+// us); k4_batch_many marks a batch that pays only when the launch holds at least four
+// waves per SIMD (4096 waves), i.e. when occupancy rather than latency is the limit.
+constexpr int k4_batch(int nt, bool q5)
+{
+    return q5 ? (nt == 3 || nt == 4 ? 2 : nt >= 6 ? 4 : nt) : (nt == 3 || nt == 5 || nt == 7 ? 2 : nt == 8 ? 4 : nt);
+}
+constexpr bool k4_batch_many(int nt, bool q5) { return q5 ? nt == 4 : nt == 8; }
+
+template <int NT, int R, bool Q5, int TB>
+__global__ __launch_bounds__(64 * kMaxWaves) void mmvq_k4_tb_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ q, const float* __restrict__ dx,
+    const float* __restrict__ sx, float* __restrict__ out, int od, int id, int32_t* __restrict__ S,
+    int wpr, int gpw)
+{
+    mmvq_k4_body<NT, R, false, Q5, TB>(W, q, dx, sx, out, od, id, S, wpr, gpw);
 }
 
 template <int NT, int R, bool DUMP>
@@ -552,6 +594,23 @@ static hipError_t launch_one(int type, const uint8_t* W, const int8_t* q, const 
     const int groups = (od + R - 1) / R;
     const int grid = (groups + gpw - 1) / gpw;
     const dim3 block(64 * wpr * gpw);
+    if constexpr (!DUMP && R == 4) {
+        const bool many = (int64_t)grid * wpr * gpw >= 4096;
+        if constexpr (k4_batch(NT, false) < NT) {
+            if (type == 1 && (many || !k4_batch_many(NT, false))) {
+                hipLaunchKernelGGL((mmvq_k4_tb_kernel<NT, R, false, k4_batch(NT, false)>), dim3(grid), block, 0, st,
+                                   W, q, d, s, out, od, id, S, wpr, gpw);
+                return hipGetLastError();
+            }
+        }
+        if constexpr (k4_batch(NT, true) < NT) {
+            if (type == 6 && (many || !k4_batch_many(NT, true))) {
+                hipLaunchKernelGGL((mmvq_k4_tb_kernel<NT, R, true, k4_batch(NT, true)>), dim3(grid), block, 0, st,
+                                   W, q, d, s, out, od, id, S, wpr, gpw);
+                return hipGetLastError();
+            }
+        }
+    }
     if (type == 1)
         hipLaunchKernelGGL((mmvq_q4k_kernel<NT, R, DUMP>), dim3(grid), block, 0, st, W, q, d, s, out, od, id,
                            S, wpr, gpw);

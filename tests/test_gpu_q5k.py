@@ -8,7 +8,8 @@ header and codes with a fifth code bit from 32 bytes of high bits.
   at nt = 1..8 and every matrix-kernel tile shape, several tiles and ragged tails;
 * with all high bits zero the Q5_K outputs equal the Q4_K kernel's on the same
   header and nibbles bit for bit (same arithmetic, same order);
-* full size: 12288 x 4096 at nt = 1 and nt = 512 (sampled outputs).
+* full size: 12288 x 4096 at nt = 1, 3, 4, 6, 8 (the vector kernel, with the tokens'
+  activations loaded in batches from nt = 3) and nt = 512 (sampled outputs).
 """
 from __future__ import annotations
 
@@ -65,7 +66,7 @@ def test_q5k_parity(nt, od, idim):
         assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32)), f"kind {kind}"
 
 
-@pytest.mark.parametrize("nt", [1, 512])
+@pytest.mark.parametrize("nt", [1, 3, 4, 6, 8, 512])
 def test_q5k_full_size(nt):
     od, idim = 12288, 4096
     W = synth.weights(Q5, od, idim, seed=5200)
