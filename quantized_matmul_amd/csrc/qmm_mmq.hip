@@ -22,12 +22,17 @@
 //    gives the same dot).  Result lane l: token l%32, rows 8*(i/4)+4*(l/32)+i%4 for
 //    accumulator i.  Q6_K groups of 16 use v_mfma_i32_32x32x16_i8 (8 K bytes per lane).
 //  * The f32 epilogue is the bottleneck on this chip (one rescale per 32 int8
-//    MACs; MFMA does 1024 MACs per clock per SIMD, VALU 16 lanes).  So only the
-//    per-element work stays on VALU: cvt(C) and one fma with the scale product.
-//    The scale product P = (d*sc)[row] x dx[token] of two sub-blocks comes from
-//    one v_mfma_f32_32x32x1_2b_f32 (two outer products), and the min term
-//    sum_j (-dmin*m_j)[row] * s_j[token] accumulates on v_mfma_f32_32x32x2_f32 in
-//    its own accumulator, both on the otherwise idle part of the MFMA pipe.
+//    MACs).  Only the per-element work stays on VALU: cvt(C) and one fma with the
+//    scale product.  The scale product P = (d*sc)[row] x dx[token] of two
+//    sub-blocks comes from one v_mfma_f32_32x32x1_2b_f32 (two outer products), and
+//    the min term sum_j (-dmin*m_j)[row] * s_j[token] accumulates on
+//    v_mfma_f32_32x32x2_f32 in its own accumulator.  Measured on this GPU, MFMA
+//    and VALU time of the waves on one SIMD add up rather than overlap (a
+//    register-only probe: 4 int8 MFMAs ~130 clocks, 64 independent f32 FMAs
+//    ~160, both ~260-285), so these f32 MFMAs (64 clocks each) are not free: they
+//    are cheaper than the 16 VALU multiplies per lane and sub-block they replace.
+//    The compute steps are software pipelined (MFMAs, and where registers allow
+//    LDS reads, issued a step ahead of the epilogue).
 //  * Per super-block: raw code bytes (rows padded so 16-byte LDS reads are
 //    conflict-free), decoded per-(row, group) f32 scales, activation codes and
 //    activation scales are staged in LDS; the next super-block's global loads are
@@ -240,38 +245,148 @@ __device__ __forceinline__ void store_tile(const v16f& v, float* __restrict__ ou
 // super-block.  C0 / C1: the two int8 tile products; P: their scale products
 // (d*sc)[row] x dx[token] from one outer-product pair; the min term of the same
 // two sub-blocks is added into accm.
-// The A operands of sub-blocks 2p and 2p + 1 for this lane (row arow, positions
-// 16 lh .. 16 lh + 15): one 16-byte read gives both (low and high nibbles); Q5_K adds
-// bit 2p / 2p + 1 of the row's high-bit bytes as the fifth code bit.
+// The LDS operands of one compute step (sub-blocks 2p and 2p + 1): this lane's 16
+// code bytes (row arow), its two 16-byte activation pieces (token btok), and the
+// scale and min factors of sub-block 2p + lh for the two outer products.
+struct Q4Ops {
+    v4i a16, b0, b1;
+    float wsc, xd, wmn, xs;
+};
+
+// The same for the kernels whose two steps' codes come as separate pieces (Q6_K:
+// 8 bytes per lane and group; Q4_0 / Q8_0: 16 bytes) with one scale product.
+template <typename T>
+struct StepOps {
+    T a0, a1, b0, b1;
+    float ws, xd;
+};
+using Ops8 = StepOps<long>;
+using Ops16 = StepOps<v4i>;
+
 template <int BM, int BN, bool Q5>
-__device__ __forceinline__ void q4_codes(const Q4Smem<BM, BN, Q5>& sm, int p, int arow, int lh, v4i& a0, v4i& a1)
+__device__ __forceinline__ Q4Ops q4_load(const Q4Smem<BM, BN, Q5>& sm, int p, int arow, int btok, int lh)
 {
     using SM = Q4Smem<BM, BN, Q5>;
-    const v4i a16 = *reinterpret_cast<const v4i*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
+    Q4Ops o;
+    o.a16 = *reinterpret_cast<const v4i*>(&sm.qs[arow * SM::QS_STRIDE + 32 * p + 16 * lh]);
+    o.b0 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
+    o.b1 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
+    const int j = 2 * p + lh;
+    o.wsc = sm.wsc[j * BM + arow];
+    o.xd = sm.xd[j * BN + btok];
+    o.wmn = sm.wmn[j * BM + arow];
+    o.xs = sm.xs[j * BN + btok];
+    return o;
+}
+
+// One compute step from loaded operands: C0 / C1 the two int8 tile products, P
+// their scale products (d*sc)[row] x dx[token] from one outer-product pair; the
+// min term of the two sub-blocks is added into accm.  h16: the row's high-bit
+// bytes (Q5_K), bit 2p / 2p + 1 the fifth code bit.
+// The A operands of sub-blocks 2p and 2p + 1 from one 16-byte code piece (low and
+// high nibbles); Q5_K adds bit 2p / 2p + 1 of the row's high-bit bytes h16 as the
+// fifth code bit.
+template <bool Q5>
+__device__ __forceinline__ void q4_unpack(const v4i& a16, const v4i& h16, int p, v4i& a0, v4i& a1)
+{
     a0 = a16 & 0x0F0F0F0F;
     a1 = (a16 >> 4) & 0x0F0F0F0F;
     if constexpr (Q5) {
-        const v4i h16 = *reinterpret_cast<const v4i*>(&sm.qh[arow * SM::H_STRIDE + 16 * lh]);
         a0 |= ((h16 >> (2 * p)) & 0x01010101) << 4;
         a1 |= ((h16 >> (2 * p + 1)) & 0x01010101) << 4;
     }
 }
 
-template <int BM, int BN, bool Q5 = false>
-__device__ __forceinline__ void q4_step(const Q4Smem<BM, BN, Q5>& sm, int p, int arow, int btok, int lh, v16i& C0,
-                                        v16i& C1, v32f& P, v16f& accm)
+template <bool Q5>
+__device__ __forceinline__ void q4_mma(const Q4Ops& o, int p, const v4i& h16, v16i& C0, v16i& C1, v32f& P,
+                                       v16f& accm)
+{
+    v4i a0, a1;
+    q4_unpack<Q5>(o.a16, h16, p, a0, a1);
+    C0 = mfma_i8_k32(a0, o.b0);
+    C1 = mfma_i8_k32(a1, o.b1);
+    P = mfma_outer2(o.wsc, o.xd);
+    accm = mfma_k2(o.wmn, o.xs, accm);
+}
+
+// NS compute steps of one staged super-block: load(p) reads a step's operands from
+// LDS, mma(ops, p, C0, C1, P) issues its MFMAs, and the f32 epilogue adds
+// cvt(C) * P into accv (two scale groups per step: P registers 0..15 and 16..31).
+// PIPE 0: each step in turn.  PIPE 1: the MFMAs of step p + 1 are issued before the
+// epilogue of step p (one more step of results, 64 registers).  PIPE 2: the LDS
+// reads of step p + 2 are issued there too, so their latency is covered by a step
+// of work instead of stalling the next MFMA (one more step of operands; measured
+// 4-6 % faster than PIPE 1 on 512-token Q4_K shapes).  Each kernel takes the
+// highest mode that does not spill.
+enum { kPipeNone = 0, kPipeMfma = 1, kPipeLds = 2 };
+
+template <int NS, int PIPE, typename Ops, typename Load, typename Mma>
+__device__ __forceinline__ void pipelined_steps(const Load& load, const Mma& mma, v16f& accv)
+{
+    const auto epilogue = [&](const v16i& C0, const v16i& C1, const v32f& P) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            accv[i] = fmaf((float)C0[i], P[i], accv[i]);
+            accv[i] = fmaf((float)C1[i], P[16 + i], accv[i]);
+        }
+    };
+    if constexpr (PIPE == kPipeNone) {
+#pragma unroll 2
+        for (int p = 0; p < NS; ++p) {
+            v16i C0, C1;
+            v32f P;
+            mma(load(p), p, C0, C1, P);
+            epilogue(C0, C1, P);
+            // one step's results at a time
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        constexpr bool AHEAD = PIPE == kPipeLds;
+        Ops o2 = load(0);
+        v16i Ca0, Ca1;
+        v32f Pa;
+        mma(o2, 0, Ca0, Ca1, Pa);
+        if constexpr (AHEAD)
+            o2 = load(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p < NS; ++p) {
+            // with AHEAD, o2 holds step p + 1's operands and step p + 2's are loaded here
+            Ops o3 = o2;
+            if (AHEAD && p + 2 < NS)
+                o3 = load(p + 2);
+            if (!AHEAD && p + 1 < NS)
+                o2 = load(p + 1);
+            v16i Cb0, Cb1;
+            v32f Pb;
+            if (p + 1 < NS)
+                mma(o2, p + 1, Cb0, Cb1, Pb);
+            __builtin_amdgcn_sched_barrier(0);
+            epilogue(Ca0, Ca1, Pa);
+            __builtin_amdgcn_sched_barrier(0);
+            if (p + 1 < NS) {
+                Ca0 = Cb0;
+                Ca1 = Cb1;
+                Pa = Pb;
+                if constexpr (AHEAD)
+                    o2 = o3;
+            }
+        }
+    }
+}
+
+// The four steps (sub-blocks 2p, 2p + 1) of one staged Q4_K / Q5_K super-block.
+template <int BM, int BN, bool Q5, int PIPE>
+__device__ __forceinline__ void q4_superblock(const Q4Smem<BM, BN, Q5>& sm, int arow, int btok, int lh, v16f& accv,
+                                              v16f& accm)
 {
     using SM = Q4Smem<BM, BN, Q5>;
-    v4i a0, a1;
-    q4_codes<BM, BN, Q5>(sm, p, arow, lh, a0, a1);
-    const v4i b0 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
-    const v4i b1 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
-    C0 = mfma_i8_k32(a0, b0);
-    C1 = mfma_i8_k32(a1, b1);
-    // sub-block 2p + lh from this lane
-    const int j = 2 * p + lh;
-    P = mfma_outer2(sm.wsc[j * BM + arow], sm.xd[j * BN + btok]);
-    accm = mfma_k2(sm.wmn[j * BM + arow], sm.xs[j * BN + btok], accm);
+    v4i h16 = {};
+    if constexpr (Q5)
+        h16 = *reinterpret_cast<const v4i*>(&sm.qh[arow * SM::H_STRIDE + 16 * lh]);
+    pipelined_steps<4, PIPE, Q4Ops>(
+        [&](int p) { return q4_load<BM, BN, Q5>(sm, p, arow, btok, lh); },
+        [&](const Q4Ops& o, int p, v16i& C0, v16i& C1, v32f& P) { q4_mma<Q5>(o, p, h16, C0, C1, P, accm); }, accv);
 }
 
 // KS > 1 splits K inside the workgroup: KS groups of WR x WC waves, each with its
@@ -341,14 +456,16 @@ __device__ __forceinline__ void mmq_k4_body(const uint8_t* __restrict__ W, const
         const int sb = it * KS + kg;
         if constexpr (DUMP) {
             // integer products only, written out per sub-block
+            v4i h16 = {};
+            if constexpr (Q5)
+                h16 = *reinterpret_cast<const v4i*>(&sm.qh[arow * SM::H_STRIDE + 16 * lh]);
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
+                const Q4Ops o = q4_load<BM, BN, Q5>(sm, p, arow, btok, lh);
                 v4i a0, a1;
-                q4_codes<BM, BN, Q5>(sm, p, arow, lh, a0, a1);
-                const v4i b0 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
-                const v4i b1 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
-                const v16i C0 = mfma_i8_k32(a0, b0);
-                const v16i C1 = mfma_i8_k32(a1, b1);
+                q4_unpack<Q5>(o.a16, h16, p, a0, a1);
+                const v16i C0 = mfma_i8_k32(a0, o.b0);
+                const v16i C1 = mfma_i8_k32(a1, o.b1);
                 const int tg = tok0 + btok;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -362,32 +479,7 @@ __device__ __forceinline__ void mmq_k4_body(const uint8_t* __restrict__ W, const
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
-            // Software pipelined over the four steps: the MFMAs of step p + 1 are
-            // issued before the epilogue of step p, one step of results in flight.
-            v16i Ca0, Ca1;
-            v32f Pa;
-            q4_step<BM, BN, Q5>(sm, 0, arow, btok, lh, Ca0, Ca1, Pa, accm);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                v16i Cb0, Cb1;
-                v32f Pb;
-                if (p < 3)
-                    q4_step<BM, BN, Q5>(sm, p + 1, arow, btok, lh, Cb0, Cb1, Pb, accm);
-                __builtin_amdgcn_sched_barrier(0);
-                // sub-blocks 2p (registers 0..15 of P) and 2p + 1 (16..31)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    accv[i] = fmaf((float)Ca0[i], Pa[i], accv[i]);
-                    accv[i] = fmaf((float)Ca1[i], Pa[16 + i], accv[i]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                if (p < 3) {
-                    Ca0 = Cb0;
-                    Ca1 = Cb1;
-                    Pa = Pb;
-                }
-            }
+            q4_superblock<BM, BN, Q5, (Q5 && KS > 1) ? kPipeMfma : kPipeLds>(sm, arow, btok, lh, accv, accm);
         }
         // keep the staging of the next super-block after the compute (moved into
         // it, its values would be live across the whole compute phase)
@@ -498,29 +590,7 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_streamk_kernel(const 
         __syncthreads();
         for (int sb = k0; sb < k1; ++sb) {
             const SM& sm = smb[(sb - k0) & 1];
-            v16i Ca0, Ca1;
-            v32f Pa;
-            q4_step<BM, BN>(sm, 0, arow, btok, lh, Ca0, Ca1, Pa, accm);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int p = 0; p < 4; ++p) {
-                v16i Cb0, Cb1;
-                v32f Pb;
-                if (p < 3)
-                    q4_step<BM, BN>(sm, p + 1, arow, btok, lh, Cb0, Cb1, Pb, accm);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    accv[i] = fmaf((float)Ca0[i], Pa[i], accv[i]);
-                    accv[i] = fmaf((float)Ca1[i], Pa[16 + i], accv[i]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                if (p < 3) {
-                    Ca0 = Cb0;
-                    Ca1 = Cb1;
-                    Pa = Pb;
-                }
-            }
+            q4_superblock<BM, BN, false, kPipeMfma>(sm, arow, btok, lh, accv, accm);
             __builtin_amdgcn_sched_barrier(0);
             q4_stage<BM, BN, NTH, QC, HC, XC, SC>(smb[(sb - k0 + 1) & 1], pq, ph, px, pd, ps, tid, sb + 1 < k1);
             prefetch(min(sb + 2, k1 - 1));
@@ -752,16 +822,23 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q6k_kernel(const uin
     for (int it = 0; it < niter; ++it) {
         const SM& sm = smb[kg][it & 1];
         const int sb = it * KS + kg;
+        // step m: groups 2m and 2m+1 (they share activation block m)
+        const auto load = [&](int m) {
+            Ops8 o;
+            o.a0 = *reinterpret_cast<const long*>(&sm.wq[arow * SM::W_STRIDE + 32 * m + 8 * lh]);
+            o.a1 = *reinterpret_cast<const long*>(&sm.wq[arow * SM::W_STRIDE + 32 * m + 16 + 8 * lh]);
+            o.b0 = *reinterpret_cast<const long*>(&sm.xq[btok * SM::X_STRIDE + 32 * m + 8 * lh]);
+            o.b1 = *reinterpret_cast<const long*>(&sm.xq[btok * SM::X_STRIDE + 32 * m + 16 + 8 * lh]);
+            o.ws = sm.wsc[(2 * m + lh) * BM + arow];
+            o.xd = sm.xd[m * BN + btok];
+            return o;
+        };
+        if constexpr (DUMP) {
 #pragma unroll 2
-        for (int m = 0; m < 8; ++m) {
-            // groups 2m and 2m+1 share activation block m
-            const long a0 = *reinterpret_cast<const long*>(&sm.wq[arow * SM::W_STRIDE + 32 * m + 8 * lh]);
-            const long a1 = *reinterpret_cast<const long*>(&sm.wq[arow * SM::W_STRIDE + 32 * m + 16 + 8 * lh]);
-            const long b0 = *reinterpret_cast<const long*>(&sm.xq[btok * SM::X_STRIDE + 32 * m + 8 * lh]);
-            const long b1 = *reinterpret_cast<const long*>(&sm.xq[btok * SM::X_STRIDE + 32 * m + 16 + 8 * lh]);
-            const v16i C0 = mfma_i8_k16(a0, b0);
-            const v16i C1 = mfma_i8_k16(a1, b1);
-            if constexpr (DUMP) {
+            for (int m = 0; m < 8; ++m) {
+                const Ops8 o = load(m);
+                const v16i C0 = mfma_i8_k16(o.a0, o.b0);
+                const v16i C1 = mfma_i8_k16(o.a1, o.b1);
                 const int tg = tok0 + btok;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -772,17 +849,14 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q6k_kernel(const uin
                         dst[1] = C1[i];
                     }
                 }
-            } else {
-                const v32f P = mfma_outer2(sm.wsc[(2 * m + lh) * BM + arow], sm.xd[m * BN + btok]);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    accv[i] = fmaf((float)C0[i], P[i], accv[i]);
-                    accv[i] = fmaf((float)C1[i], P[16 + i], accv[i]);
-                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            // one step's MFMA results at a time: hoisting every MFMA of the
-            // super-block keeps all their results live (register spills)
-            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            pipelined_steps<8, (KS == 1 ? kPipeLds : PAD ? kPipeMfma : kPipeNone), Ops8>(load, [&](const Ops8& o, int, v16i& C0, v16i& C1, v32f& P) {
+                C0 = mfma_i8_k16(o.a0, o.b0);
+                C1 = mfma_i8_k16(o.a1, o.b1);
+                P = mfma_outer2(o.ws, o.xd);
+            }, accv);
         }
         __builtin_amdgcn_sched_barrier(0);
         q6_stage<BM, BN, NTH, WC8, XC, SC>(smb[kg][(it + 1) & 1], pl, phh, pshift, px, ps, psd, tid, sb + KS < nsb);
@@ -959,16 +1033,23 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_b32_kernel(const uin
     for (int it = 0; it < niter; ++it) {
         const SM& sm = smb[kg][it & 1];
         const int sb = it * KS + kg;
+        // step p: blocks 2p and 2p + 1
+        const auto load = [&](int p) {
+            Ops16 o;
+            o.a0 = *reinterpret_cast<const v4i*>(&sm.wq[arow * SM::W_STRIDE + 64 * p + 16 * lh]);
+            o.a1 = *reinterpret_cast<const v4i*>(&sm.wq[arow * SM::W_STRIDE + 64 * p + 32 + 16 * lh]);
+            o.b0 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
+            o.b1 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
+            o.ws = sm.wsc[(2 * p + lh) * BM + arow];
+            o.xd = sm.xd[(2 * p + lh) * BN + btok];
+            return o;
+        };
+        if constexpr (DUMP) {
 #pragma unroll 2
-        for (int p = 0; p < 4; ++p) {
-            // blocks 2p and 2p + 1
-            const v4i a0 = *reinterpret_cast<const v4i*>(&sm.wq[arow * SM::W_STRIDE + 64 * p + 16 * lh]);
-            const v4i a1 = *reinterpret_cast<const v4i*>(&sm.wq[arow * SM::W_STRIDE + 64 * p + 32 + 16 * lh]);
-            const v4i b0 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 16 * lh]);
-            const v4i b1 = *reinterpret_cast<const v4i*>(&sm.xq[btok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
-            const v16i C0 = mfma_i8_k32(a0, b0);
-            const v16i C1 = mfma_i8_k32(a1, b1);
-            if constexpr (DUMP) {
+            for (int p = 0; p < 4; ++p) {
+                const Ops16 o = load(p);
+                const v16i C0 = mfma_i8_k32(o.a0, o.b0);
+                const v16i C1 = mfma_i8_k32(o.a1, o.b1);
                 const int tg = tok0 + btok;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -979,16 +1060,14 @@ __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_b32_kernel(const uin
                         dst[1] = C1[i];
                     }
                 }
-            } else {
-                const int j = 2 * p + lh;
-                const v32f P = mfma_outer2(sm.wsc[j * BM + arow], sm.xd[j * BN + btok]);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    accv[i] = fmaf((float)C0[i], P[i], accv[i]);
-                    accv[i] = fmaf((float)C1[i], P[16 + i], accv[i]);
-                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            pipelined_steps<4, kPipeLds, Ops16>(load, [&](const Ops16& o, int, v16i& C0, v16i& C1, v32f& P) {
+                C0 = mfma_i8_k32(o.a0, o.b0);
+                C1 = mfma_i8_k32(o.a1, o.b1);
+                P = mfma_outer2(o.ws, o.xd);
+            }, accv);
         }
         __builtin_amdgcn_sched_barrier(0);
         b32_stage<BM, BN, NTH, WC8, XC, SC, Q8>(smb[kg][(it + 1) & 1], pw, psh, px, ps, tid, sb + KS < nsb);
