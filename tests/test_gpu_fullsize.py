@@ -99,12 +99,13 @@ def test_full_size_parity(label, qtype, od, idim, nt, outl, seed, full):
 
 
 @pytest.mark.parametrize("qtype,od,idim", [(Q4, 12288, 4096), (Q4, 4096, 4096), (Q4, 4096, 12288),
-                                           (Q6, 32000, 4096), (Q4, 100, 2304), (Q6, 257, 1024),
+                                           (Q6, 32000, 4096), (Q6, 12288, 4096), (Q6, 4096, 4096),
+                                           (Q4, 100, 2304), (Q6, 257, 1024),
                                            (Q5, 12288, 4096), (Q5, 4096, 4096), (Q5, 8192, 4096)])
 def test_mmvq_rows_equal_single_token_calls(qtype, od, idim):
     """Each token row of an nt = 2..8 MMVQ call is bit-identical to that token alone
-    (also where the tokens' activations are loaded in batches: Q4_K and Q5_K with 4
-    rows per group, with and without the launch-size condition)."""
+    (also where the tokens' activations are loaded in batches: Q4_K, Q5_K and Q6_K
+    with 4 rows per group, with and without the launch-size condition)."""
     _say(f"batch invariance type={qtype} od={od} id={idim}")
     W = _up(synth.weights(qtype, od, idim, seed=31))
     x = synth.activations(8, idim, seed=32)

@@ -9,8 +9,9 @@ GGUF blocks": the upload pads each 210-byte Q6_K block to 224 bytes so every
   so every output is bit-identical to QMM_TYPE_Q6_K's, for the vector kernel
   (nt = 1..8) and every matrix-kernel tile shape; the per-group integer dots are
   bit-exact against the oracle; outputs are within tolerance of the oracle;
-* full size: the 32000 x 4096 output head at nt = 1 and the diffusion-LM down
-  projection 4096 x 12288 at L = 256.
+* full size: the 32000 x 4096 output head at nt = 1, 5 and 8, 12288 x 4096 at nt = 7
+  and 4096 x 4096 at nt = 8 (the vector kernel with and without token batches),
+  and the diffusion-LM down projection 4096 x 12288 at L = 256.
 """
 from __future__ import annotations
 
@@ -84,7 +85,8 @@ def test_padded_equals_unpadded(nt, od, idim):
         assert np.array_equal(S.cpu().numpy(), ref_S), f"kind {kind}: group dots"
 
 
-@pytest.mark.parametrize("od,idim,nt", [(32000, 4096, 1), (4096, 12288, 256), (32000, 4096, 5)])
+@pytest.mark.parametrize("od,idim,nt", [(32000, 4096, 1), (4096, 12288, 256), (32000, 4096, 5), (32000, 4096, 8),
+                                        (12288, 4096, 7), (4096, 4096, 8)])
 def test_padded_full_size(od, idim, nt):
     _say(f"padded Q6_K full size od={od} id={idim} nt={nt}")
     W = synth.weights(Q6, od, idim, seed=2300 + nt)
