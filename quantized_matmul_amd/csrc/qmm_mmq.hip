@@ -25,12 +25,14 @@
 //    MACs).  Only the per-element work stays on VALU: cvt(C) and one fma with the
 //    scale product.  The scale product P = (d*sc)[row] x dx[token] of two
 //    sub-blocks comes from one v_mfma_f32_32x32x1_2b_f32 (two outer products), and
-//    the min term sum_j (-dmin*m_j)[row] * s_j[token] accumulates on
-//    v_mfma_f32_32x32x2_f32 in its own accumulator.  Measured on this GPU, MFMA
+//    the min term sum_j (-dmin*m_j)[row] * s_j[token] accumulates in its own
+//    accumulator, once per super-block on three bf16 MFMAs over exact three-part
+//    splits of both factors (q4_min_term).  Measured on this GPU, MFMA
 //    and VALU time of the waves on one SIMD add up rather than overlap (a
 //    register-only probe: 4 int8 MFMAs ~130 clocks, 64 independent f32 FMAs
-//    ~160, both ~260-285), so these f32 MFMAs (64 clocks each) are not free: they
-//    are cheaper than the 16 VALU multiplies per lane and sub-block they replace.
+//    ~160, both ~260-285), so the f32 outer products (64 clocks each) are not
+//    free: they are cheaper than the 16 VALU multiplies per lane and sub-block
+//    they replace.
 //    The compute steps are software pipelined (MFMAs, and where registers allow
 //    LDS reads, issued a step ahead of the epilogue).
 //  * Per super-block: raw code bytes (rows padded so 16-byte LDS reads are
@@ -45,6 +47,22 @@ namespace qmm {
 
 // ------------------------------------------------------------------ Q4_K
 
+// v as three bf16 parts p[0] + p[1] + p[2] (bit patterns): each part is the next 8
+// significant bits, cut by truncation, and both subtractions are exact, so the sum
+// is v exactly for a normal v (a remainder below the normal range loses its bits).
+struct Bf16x3 {
+    uint16_t p[3];
+};
+
+__device__ __forceinline__ Bf16x3 split3_bf16(float v)
+{
+    const uint32_t u0 = __float_as_uint(v);
+    const float r1 = v - __uint_as_float(u0 & 0xFFFF0000u);
+    const uint32_t u1 = __float_as_uint(r1);
+    const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);
+    return {{(uint16_t)(u0 >> 16), (uint16_t)(u1 >> 16), (uint16_t)(__float_as_uint(r2) >> 16)}};
+}
+
 // Q5 (Q5_K): also the 32 high-bit bytes of each row (stride 48).
 template <int BM, int BN, bool Q5 = false>
 struct __attribute__((aligned(16))) Q4Smem {
@@ -53,10 +71,10 @@ struct __attribute__((aligned(16))) Q4Smem {
     static constexpr int H_STRIDE = 48;     // 32 high-bit bytes + 16 pad
     uint8_t qs[BM * QS_STRIDE];
     float wsc[8 * BM];                      // d * sc_j, [j][row]
-    float wmn[8 * BM];                      // -dmin * m_j, [j][row]
+    uint16_t wmn3[3 * BM * 8];              // -dmin * m_j as three bf16 parts, [part][row][j]
     uint8_t xq[BN * X_STRIDE];
     float xd[8 * BN];                       // activation d, [j][token]
-    float xs[8 * BN];                       // activation s, [j][token]
+    uint16_t xs3[3 * BN * 8];               // activation s as three bf16 parts, [part][token][j]
     uint8_t qh[Q5 ? BM * H_STRIDE : 0];  // empty without Q5 (a clang extension): the Q4_K layout is unchanged
 };
 
@@ -165,9 +183,14 @@ __device__ __forceinline__ void q4_stage(Q4Smem<BM, BN, Q5>& sm, const v4i (&pq)
         int sc0, m0, sc1, m1;
         q4k_scale_min_pair((uint32_t)h.y, (uint32_t)h.z, (uint32_t)h.w, jj, sc0, m0, sc1, m1);
         sm.wsc[jj * BM + r] = valid ? dw * (float)sc0 : 0.f;
-        sm.wmn[jj * BM + r] = valid ? -(dm * (float)m0) : 0.f;
         sm.wsc[(jj + 4) * BM + r] = valid ? dw * (float)sc1 : 0.f;
-        sm.wmn[(jj + 4) * BM + r] = valid ? -(dm * (float)m1) : 0.f;
+        const Bf16x3 mn0 = split3_bf16(valid ? -(dm * (float)m0) : 0.f);
+        const Bf16x3 mn1 = split3_bf16(valid ? -(dm * (float)m1) : 0.f);
+#pragma unroll
+        for (int pt = 0; pt < 3; ++pt) {
+            sm.wmn3[(pt * BM + r) * 8 + jj] = mn0.p[pt];
+            sm.wmn3[(pt * BM + r) * 8 + jj + 4] = mn1.p[pt];
+        }
     }
 #pragma unroll
     for (int k = 0; k < XC; ++k) {
@@ -184,10 +207,15 @@ __device__ __forceinline__ void q4_stage(Q4Smem<BM, BN, Q5>& sm, const v4i (&pq)
         sm.xd[(4 * hf + 1) * BN + t] = __int_as_float(pd[k].y);
         sm.xd[(4 * hf + 2) * BN + t] = __int_as_float(pd[k].z);
         sm.xd[(4 * hf + 3) * BN + t] = __int_as_float(pd[k].w);
-        sm.xs[(4 * hf + 0) * BN + t] = __int_as_float(ps[k].x);
-        sm.xs[(4 * hf + 1) * BN + t] = __int_as_float(ps[k].y);
-        sm.xs[(4 * hf + 2) * BN + t] = __int_as_float(ps[k].z);
-        sm.xs[(4 * hf + 3) * BN + t] = __int_as_float(ps[k].w);
+        const Bf16x3 s0 = split3_bf16(__int_as_float(ps[k].x)), s1 = split3_bf16(__int_as_float(ps[k].y));
+        const Bf16x3 s2 = split3_bf16(__int_as_float(ps[k].z)), s3 = split3_bf16(__int_as_float(ps[k].w));
+#pragma unroll
+        for (int pt = 0; pt < 3; ++pt) {
+            // sub-blocks 4 hf .. 4 hf + 3 of token t: 8 contiguous bytes per part
+            const uint2 v = make_uint2((uint32_t)s0.p[pt] | ((uint32_t)s1.p[pt] << 16),
+                                       (uint32_t)s2.p[pt] | ((uint32_t)s3.p[pt] << 16));
+            *reinterpret_cast<uint2*>(&sm.xs3[(pt * BN + t) * 8 + 4 * hf]) = v;
+        }
     }
 
 }
@@ -241,16 +269,12 @@ __device__ __forceinline__ void store_tile(const v16f& v, float* __restrict__ ou
     }
 }
 
-// One compute step of the Q4_K kernel: sub-blocks 2p and 2p + 1 of the staged
-// super-block.  C0 / C1: the two int8 tile products; P: their scale products
-// (d*sc)[row] x dx[token] from one outer-product pair; the min term of the same
-// two sub-blocks is added into accm.
 // The LDS operands of one compute step (sub-blocks 2p and 2p + 1): this lane's 16
 // code bytes (row arow), its two 16-byte activation pieces (token btok), and the
-// scale and min factors of sub-block 2p + lh for the two outer products.
+// scale factors of sub-block 2p + lh for the outer products.
 struct Q4Ops {
     v4i a16, b0, b1;
-    float wsc, xd, wmn, xs;
+    float wsc, xd;
 };
 
 // The same for the kernels whose two steps' codes come as separate pieces (Q6_K:
@@ -274,15 +298,9 @@ __device__ __forceinline__ Q4Ops q4_load(const Q4Smem<BM, BN, Q5>& sm, int p, in
     const int j = 2 * p + lh;
     o.wsc = sm.wsc[j * BM + arow];
     o.xd = sm.xd[j * BN + btok];
-    o.wmn = sm.wmn[j * BM + arow];
-    o.xs = sm.xs[j * BN + btok];
     return o;
 }
 
-// One compute step from loaded operands: C0 / C1 the two int8 tile products, P
-// their scale products (d*sc)[row] x dx[token] from one outer-product pair; the
-// min term of the two sub-blocks is added into accm.  h16: the row's high-bit
-// bytes (Q5_K), bit 2p / 2p + 1 the fifth code bit.
 // The A operands of sub-blocks 2p and 2p + 1 from one 16-byte code piece (low and
 // high nibbles); Q5_K adds bit 2p / 2p + 1 of the row's high-bit bytes h16 as the
 // fifth code bit.
@@ -297,16 +315,17 @@ __device__ __forceinline__ void q4_unpack(const v4i& a16, const v4i& h16, int p,
     }
 }
 
+// One compute step from loaded operands: C0 / C1 the two int8 tile products, P
+// their scale products (d*sc)[row] x dx[token] from one outer-product pair.  h16:
+// the row's high-bit bytes (Q5_K).
 template <bool Q5>
-__device__ __forceinline__ void q4_mma(const Q4Ops& o, int p, const v4i& h16, v16i& C0, v16i& C1, v32f& P,
-                                       v16f& accm)
+__device__ __forceinline__ void q4_mma(const Q4Ops& o, int p, const v4i& h16, v16i& C0, v16i& C1, v32f& P)
 {
     v4i a0, a1;
     q4_unpack<Q5>(o.a16, h16, p, a0, a1);
     C0 = mfma_i8_k32(a0, o.b0);
     C1 = mfma_i8_k32(a1, o.b1);
     P = mfma_outer2(o.wsc, o.xd);
-    accm = mfma_k2(o.wmn, o.xs, accm);
 }
 
 // NS compute steps of one staged super-block: load(p) reads a step's operands from
@@ -375,6 +394,30 @@ __device__ __forceinline__ void pipelined_steps(const Load& load, const Mma& mma
     }
 }
 
+// The min term of one staged super-block, sum_j (-dmin*m_j)[row] * s_j[token] over
+// its 8 sub-blocks, added into accm on the bf16 MFMA: both factors are staged as
+// three bf16 parts (a = a1 + a2 + a3 exactly), and the six part products whose
+// size is above 2^-24 of a*s, (1,1) (1,2) (2,1) (1,3) (2,2) (3,1), are the K = 48
+// entries of three v_mfma_f32_32x32x16_bf16 (K index 8 q + j for part pair q and
+// sub-block j; a lane's 8 entries are one part of one row or token across the 8
+// sub-blocks: one 16-byte LDS read).  Each part product is exact in f32; the f32
+// MFMA it replaces cost 64 clocks per two sub-blocks, these three about 100 per
+// eight.
+template <int BM, int BN, bool Q5>
+__device__ __forceinline__ void q4_min_term(const Q4Smem<BM, BN, Q5>& sm, int arow, int btok, int lh, v16f& accm)
+{
+    // part of the row / token factor for part pair q = 2 m + lh
+    constexpr int kRowPart[6] = {0, 0, 1, 0, 1, 2};
+    constexpr int kTokPart[6] = {0, 1, 0, 2, 1, 0};
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        const int q = 2 * m + lh;
+        const v8bf a = *reinterpret_cast<const v8bf*>(&sm.wmn3[(kRowPart[q] * BM + arow) * 8]);
+        const v8bf b = *reinterpret_cast<const v8bf*>(&sm.xs3[(kTokPart[q] * BN + btok) * 8]);
+        accm = mfma_bf16_k16(a, b, accm);
+    }
+}
+
 // The four steps (sub-blocks 2p, 2p + 1) of one staged Q4_K / Q5_K super-block.
 template <int BM, int BN, bool Q5, int PIPE>
 __device__ __forceinline__ void q4_superblock(const Q4Smem<BM, BN, Q5>& sm, int arow, int btok, int lh, v16f& accv,
@@ -384,9 +427,10 @@ __device__ __forceinline__ void q4_superblock(const Q4Smem<BM, BN, Q5>& sm, int 
     v4i h16 = {};
     if constexpr (Q5)
         h16 = *reinterpret_cast<const v4i*>(&sm.qh[arow * SM::H_STRIDE + 16 * lh]);
+    q4_min_term<BM, BN, Q5>(sm, arow, btok, lh, accm);
     pipelined_steps<4, PIPE, Q4Ops>(
         [&](int p) { return q4_load<BM, BN, Q5>(sm, p, arow, btok, lh); },
-        [&](const Q4Ops& o, int p, v16i& C0, v16i& C1, v32f& P) { q4_mma<Q5>(o, p, h16, C0, C1, P, accm); }, accv);
+        [&](const Q4Ops& o, int p, v16i& C0, v16i& C1, v32f& P) { q4_mma<Q5>(o, p, h16, C0, C1, P); }, accv);
 }
 
 // KS > 1 splits K inside the workgroup: KS groups of WR x WC waves, each with its

@@ -29,6 +29,14 @@ __device__ __forceinline__ v32f mfma_outer2(float a, float b)
     return __builtin_amdgcn_mfma_f32_32x32x1f32(a, b, z, 0, 0, 0);
 }
 
+// acc += A (32 x 16) . B (16 x 32) in bf16: lane l gives A[row l%32][k = 8 (l/32) ..
+// + 7] and B[k = 8 (l/32) .. + 7][col l%32].
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ v16f mfma_bf16_k16(v8bf a, v8bf b, v16f acc)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
 // acc += A (32 x 2) . B (2 x 32): lane l gives A[row l%32][k = l/32] and
 // B[k = l/32][col l%32].
 __device__ __forceinline__ v16f mfma_k2(float a, float b, v16f acc)
