@@ -96,7 +96,8 @@ enum {
 
 /* Dispatch kinds. */
 enum {
-    QMM_KIND_MMVQ = 1, /* nt <= switch: weights streamed once, tokens in registers */
+    QMM_KIND_MMVQ = 1, /* nt <= switch (and 9..16 tokens on od <= 4096, see qmm_dispatch_kind):
+                          weights streamed once per 8 tokens, tokens in registers */
     QMM_KIND_MMQ = 2,  /* nt > switch: tiled int8 MFMA GEMM, tile shape by cost model */
     /* MMQ with a given tile shape (qmm_matmul_q8_kind and qmm_mmq_tile only): */
     QMM_KIND_MMQ_128X64 = 3,        /* 128 rows x 64 tokens, 8 waves */
@@ -146,9 +147,10 @@ int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, cons
                   int od, int id, float* out, void* stream);
 
 /* Same as qmm_matmul_q8 but with the kernel chosen by the caller (kind =
- * QMM_KIND_MMVQ for nt <= 8 only, QMM_KIND_MMQ for any nt, or one of the
- * QMM_KIND_MMQ_* tile shapes for any nt).  For tests and measurement of every
- * kernel variant on one shape.  Unknown kind: QMM_ERR_ARG. */
+ * QMM_KIND_MMVQ, QMM_KIND_MMQ, or one of the QMM_KIND_MMQ_* tile shapes; any nt:
+ * above 8 tokens MMVQ runs one launch per slice of 8 tokens, each slice giving
+ * the same bits as that slice alone).  For tests and measurement of every kernel
+ * variant on one shape.  Unknown kind: QMM_ERR_ARG. */
 int qmm_matmul_q8_kind(int kind, int type, const void* W, const int8_t* q, const float* d,
                        const float* s, int nt, int od, int id, float* out, void* stream);
 
@@ -171,12 +173,16 @@ int qmm_matmul_q8_streamk(int type, const void* W, const int8_t* q, const float*
  * QMM_MMQ_TILE = 1, 2 or 3 (read once) forces one, for tuning. */
 int qmm_mmq_tile(int nt, int od, int id);
 
-/* Which kernel qmm_matmul would run for this call: QMM_KIND_MMVQ or QMM_KIND_MMQ,
- * or a negative status for invalid arguments. */
+/* Which kernel qmm_matmul would run for this call: QMM_KIND_MMVQ for nt <= the
+ * switch, and with the default switch (8) also for 9..16 tokens on od <= 4096
+ * rows, as launches on slices of 8 tokens (the MMQ tile grid of such a matrix
+ * fills at most a quarter of the GPU); QMM_KIND_MMQ otherwise.  A negative status
+ * for invalid arguments. */
 int qmm_dispatch_kind(int type, int nt, int od, int id);
 
-/* The nt at or below which MMVQ runs (default 8; environment QMM_NT_SWITCH,
- * clamped to 0..8, read once). */
+/* The nt at or below which MMVQ runs on every shape (default 8; environment
+ * QMM_NT_SWITCH, clamped to 0..8, read once; a value other than 8 also turns off
+ * the 9..16-token rule of qmm_dispatch_kind). */
 int qmm_nt_switch(void);
 
 /* ---- Q8_K activations: one scale per 256 values ------------------------------

@@ -111,13 +111,42 @@ int nt_switch_value()
 
 int launched(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH; }
 
+// The kernel a call runs: MMVQ up to the switch; with the default switch also for
+// 9..16 tokens on matrices of at most 4096 rows, as launches on token slices of 8.
+// Such a matrix gives MMQ at most 64 tiles of 64 rows, a quarter of the 256 CUs,
+// and MMQ then costs about the same for any nt up to 128 (4096 x 4096: 22 us; two
+// MMVQ launches: 13.7-14.7 us; 4096 x 12288: 57 us against 32-47 us).  On 12288
+// rows the MMQ grid is large enough and two MMVQ launches lose from nt = 12.
+int dispatch_kind(int nt, int od)
+{
+    const int sw = nt_switch_value();
+    if (nt <= sw || (sw == 8 && nt <= 16 && od <= 4096))
+        return QMM_KIND_MMVQ;
+    return QMM_KIND_MMQ;
+}
+
 int matmul_q8_checked(int kind, int type, const void* W, const int8_t* q, const float* d,
                       const float* s, int nt, int od, int id, float* out, int32_t* S, void* stream)
 {
     const auto st = reinterpret_cast<hipStream_t>(stream);
     const auto w = reinterpret_cast<const uint8_t*>(W);
-    if (kind == QMM_KIND_MMVQ)
-        return launched(qmm::launch_mmvq(type, w, q, d, s, nt, od, id, out, S, st));
+    if (kind == QMM_KIND_MMVQ) {
+        if (nt <= 8)
+            return launched(qmm::launch_mmvq(type, w, q, d, s, nt, od, id, out, S, st));
+        if (S)
+            return QMM_ERR_ARG;  // the integer dump runs on up to 8 tokens
+        // tokens t0 .. t0 + 7 are rows t0.. of q, d, s and out: each slice is a
+        // complete call on its own (a token's outputs do not depend on the others)
+        const size_t nblk = (size_t)id / 32;
+        for (int t0 = 0; t0 < nt; t0 += 8) {
+            const int rc = launched(qmm::launch_mmvq(type, w, q + (size_t)t0 * id, d + (size_t)t0 * nblk,
+                                                     s + (size_t)t0 * nblk, min(8, nt - t0), od, id,
+                                                     out + (size_t)t0 * od, nullptr, st));
+            if (rc)
+                return rc;
+        }
+        return QMM_OK;
+    }
     const int tile = kind >= QMM_KIND_MMQ_128X64 ? kind - QMM_KIND_MMQ_128X64 + 1 : 0;
     return launched(qmm::launch_mmq(type, w, q, d, s, nt, od, id, out, S, st, tile));
 }
@@ -388,7 +417,7 @@ int qmm_dispatch_kind(int type, int nt, int od, int id)
     rc = check_shape(nt, od, id);
     if (rc)
         return rc;
-    return nt <= nt_switch_value() ? QMM_KIND_MMVQ : QMM_KIND_MMQ;
+    return dispatch_kind(nt, od);
 }
 
 int qmm_mmq_tile(int nt, int od, int id)
@@ -408,7 +437,7 @@ int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, cons
     rc = check_device();
     if (rc)
         return rc;
-    const int kind = nt <= nt_switch_value() ? QMM_KIND_MMVQ : QMM_KIND_MMQ;
+    const int kind = dispatch_kind(nt, od);
     return matmul_q8_checked(kind, type, W, q, d, s, nt, od, id, out, nullptr, stream);
 }
 
@@ -420,8 +449,6 @@ int qmm_matmul_q8_kind(int kind, int type, const void* W, const int8_t* q, const
     int rc = validate_q8(type, W, q, d, s, nt, od, id, out);
     if (rc)
         return rc;
-    if (kind == QMM_KIND_MMVQ && nt > 8)
-        return QMM_ERR_ARG;
     rc = check_device();
     if (rc)
         return rc;
@@ -455,7 +482,7 @@ int qmm_matmul(int type, const void* W, const float* x, int nt, int od, int id, 
     rc = launched(qmm::launch_quantize(x, nt, id, q, d, s, st));
     if (rc)
         return rc;
-    const int kind = nt <= nt_switch_value() ? QMM_KIND_MMVQ : QMM_KIND_MMQ;
+    const int kind = dispatch_kind(nt, od);
     return matmul_q8_checked(kind, type, W, q, d, s, nt, od, id, out, nullptr, stream);
 }
 

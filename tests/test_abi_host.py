@@ -62,8 +62,15 @@ def test_act_bytes():
 def test_dispatch_kind_host():
     assert qmm.qmm_nt_switch() == 8
     for nt in range(1, 9):
-        assert qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q4_K, nt, 4096, 4096) == qmm.QMM_KIND_MMVQ
-    for nt in (9, 16, 256, 512):
+        for od in (4096, 12288):
+            assert qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q4_K, nt, od, 4096) == qmm.QMM_KIND_MMVQ
+    # 9..16 tokens: MMVQ on token slices of 8 up to 4096 rows, MMQ above
+    for nt in (9, 12, 16):
+        for qt in (qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K):
+            assert qmm.qmm_dispatch_kind(qt, nt, 4096, 4096) == qmm.QMM_KIND_MMVQ
+            assert qmm.qmm_dispatch_kind(qt, nt, 64, 12288) == qmm.QMM_KIND_MMVQ
+            assert qmm.qmm_dispatch_kind(qt, nt, 4097, 4096) == qmm.QMM_KIND_MMQ
+    for nt in (17, 256, 512):
         assert qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q6_K, nt, 4096, 4096) == qmm.QMM_KIND_MMQ
     with pytest.raises(qmm.QmmError):
         qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q4_K, 1, 4096, 4000)
@@ -88,7 +95,8 @@ def test_validation_before_device_work():
     # the MMQ tile kinds pass validation; without a GPU the device check answers
     assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_64X64_SPLITK, 1, p, p, p, p, 1, 4, 256, p, None) == \
         qmm.QMM_ERR_DEVICE
-    assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMVQ, 1, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    # MMVQ takes any nt (slices of 8 tokens above 8): validation passes
+    assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMVQ, 1, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_DEVICE
     assert L.qmm_quantize_act(p, 1, 40, p, p, p, None) == qmm.QMM_ERR_SHAPE
     assert L.qmm_group_dots(qmm.QMM_KIND_MMVQ, 1, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_ARG
     assert L.qmm_matmul(1, p, p, 1 << 20, 4, 4096, p, p, big, None) == qmm.QMM_ERR_SHAPE

@@ -103,21 +103,28 @@ def test_full_size_parity(label, qtype, od, idim, nt, outl, seed, full):
                                            (Q4, 100, 2304), (Q6, 257, 1024),
                                            (Q5, 12288, 4096), (Q5, 4096, 4096), (Q5, 8192, 4096)])
 def test_mmvq_rows_equal_single_token_calls(qtype, od, idim):
-    """Each token row of an nt = 2..8 MMVQ call is bit-identical to that token alone
+    """Each token row of an nt = 2..16 MMVQ call is bit-identical to that token alone
     (also where the tokens' activations are loaded in batches: Q4_K, Q5_K and Q6_K
     with 4 rows per group, with and without the launch-size condition)."""
     _say(f"batch invariance type={qtype} od={od} id={idim}")
     W = _up(synth.weights(qtype, od, idim, seed=31))
-    x = synth.activations(8, idim, seed=32)
+    x = synth.activations(16, idim, seed=32)
     q, d, s = qmm.qmm_quantize_act(_up(x))
     singles = [qmm.qmm_matmul_q8(qtype, W, q[t:t + 1].contiguous(), d[t:t + 1].contiguous(),
-                                 s[t:t + 1].contiguous(), od) for t in range(8)]
+                                 s[t:t + 1].contiguous(), od) for t in range(16)]
     ref = torch.cat(singles).cpu().numpy()
-    for nt in range(2, 9):
-        assert qmm.qmm_dispatch_kind(qtype, nt, od, idim) == qmm.QMM_KIND_MMVQ
-        o = qmm.qmm_matmul_q8(qtype, W, q[:nt].contiguous(), d[:nt].contiguous(), s[:nt].contiguous(), od)
+    for nt in range(2, 17):
+        args = (q[:nt].contiguous(), d[:nt].contiguous(), s[:nt].contiguous(), od)
+        # MMVQ forced for nt > 8 too: one launch per slice of 8 tokens
+        o = qmm.qmm_matmul_q8_kind(qmm.QMM_KIND_MMVQ, qtype, W, *args)
         torch.cuda.synchronize()
-        assert np.array_equal(o.cpu().numpy().view(np.uint32), ref[:nt].view(np.uint32)), f"nt={nt}"
+        assert np.array_equal(o.cpu().numpy().view(np.uint32), ref[:nt].view(np.uint32)), f"MMVQ nt={nt}"
+        kind = qmm.qmm_dispatch_kind(qtype, nt, od, idim)
+        assert kind == (qmm.QMM_KIND_MMVQ if nt <= 8 or od <= 4096 else qmm.QMM_KIND_MMQ)
+        if kind == qmm.QMM_KIND_MMVQ:
+            o = qmm.qmm_matmul_q8(qtype, W, *args)
+            torch.cuda.synchronize()
+            assert np.array_equal(o.cpu().numpy().view(np.uint32), ref[:nt].view(np.uint32)), f"nt={nt}"
 
 
 EDGE = [

@@ -161,20 +161,29 @@ def test_mmq_every_tile_shape(qtype, nt, od, idim):
 
 
 def test_dispatch_boundary():
-    """nt = 8 runs MMVQ and nt = 9 runs MMQ; both match the oracle."""
+    """nt = 8 runs MMVQ; on a matrix of at most 4096 rows nt = 9..16 run MMVQ on
+    token slices of 8 and nt = 17 runs MMQ; every call matches the oracle, and the
+    sliced call gives the same bits as its slices called alone."""
     assert qmm.qmm_dispatch_kind(Q4, 8, 64, 512) == qmm.QMM_KIND_MMVQ
-    assert qmm.qmm_dispatch_kind(Q4, 9, 64, 512) == qmm.QMM_KIND_MMQ
+    assert qmm.qmm_dispatch_kind(Q4, 9, 64, 512) == qmm.QMM_KIND_MMVQ
+    assert qmm.qmm_dispatch_kind(Q4, 16, 64, 512) == qmm.QMM_KIND_MMVQ
+    assert qmm.qmm_dispatch_kind(Q4, 17, 64, 512) == qmm.QMM_KIND_MMQ
     od, idim = 96, 1024
     for qtype in (Q4, Q6):
         W = synth.weights(qtype, od, idim, seed=5)
-        x = synth.activations(9, idim, seed=5)
+        x = synth.activations(17, idim, seed=5)
         ref, mag, _ = oracle.matmul(qtype, W, x, od)
         Wt = _up(W)
-        o8 = qmm.qmm_matmul(qtype, Wt, _up(x[:8]), od)
-        o9 = qmm.qmm_matmul(qtype, Wt, _up(x), od)
+        for nt in (8, 9, 13, 16, 17):
+            o = qmm.qmm_matmul(qtype, Wt, _up(x[:nt]), od)
+            torch.cuda.synchronize()
+            assert_close(o.cpu().numpy(), ref[:nt], mag[:nt], qtype, idim, f"nt={nt}")
+        q, d, s = qmm.qmm_quantize_act(_up(x[:13]))
+        whole = qmm.qmm_matmul_q8(qtype, Wt, q, d, s, od)
+        a = qmm.qmm_matmul_q8(qtype, Wt, q[:8].contiguous(), d[:8].contiguous(), s[:8].contiguous(), od)
+        b = qmm.qmm_matmul_q8(qtype, Wt, q[8:].contiguous(), d[8:].contiguous(), s[8:].contiguous(), od)
         torch.cuda.synchronize()
-        assert_close(o8.cpu().numpy(), ref[:8], mag[:8], qtype, idim, "nt=8")
-        assert_close(o9.cpu().numpy(), ref, mag, qtype, idim, "nt=9")
+        assert torch.equal(whole.view(torch.int32), torch.cat([a, b]).view(torch.int32))
 
 
 def test_special_inputs():
