@@ -42,6 +42,11 @@ per 256 values, 16-value code sums; its own numerics) and, on the same weights a
 inputs, on the per-32 activations.  value = int8 TOP/s of the Q8_K matmul kernel;
 per32_same_shapes gives the per-32 kernel's rate from the same process.
 
+Workload "dllm_step": the 224 matmuls of one diffusion-LM step at L = 256 (32 layers x
+q, k, v, o, gate, up Q4_K and down Q6_K in the padded layout; distinct weights per
+layer).  value = int8 ops over the summed kernel times; graph = the whole step
+(quantize + matmul per call) captured into one HIP graph and replayed.
+
 Workload "formats": Q4_0, Q8_0 and Q5_K (and Q4_K for comparison) at 12288 x 4096, nt = 1
 and nt = 512.  value = HBM GB/s of the Q4_0 vector kernel at nt = 1.
 
@@ -189,6 +194,39 @@ class Call:
     def run(self):
         self.quantize()
         self.matmul()
+
+
+def graph_replay_ms(torch, calls, replays=5):
+    """One step (every call's quantize and matmul, its first weight copy) captured
+    into a HIP graph on a side stream; mean replay time in ms (HIP events on that
+    stream), replays back to back after one untimed replay."""
+    P = ctypes.c_void_p
+    side = torch.cuda.Stream()
+    sp = P(side.cuda_stream)
+    qa = [c.qargs[:-1] + (sp,) for c in calls]
+    ma = [c.margs[0][:-1] + (sp,) for c in calls]
+
+    def issue():
+        for c, a, b in zip(calls, qa, ma):
+            if c.qfn(*a) or c.mfn(*b):
+                raise RuntimeError(f"{c.label}: launch failed while capturing")
+
+    side.wait_stream(torch.cuda.current_stream())
+    issue()  # warm-up on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side, capture_error_mode="relaxed"):
+        issue()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(side)
+        for _ in range(replays):
+            g.replay()
+        e1.record(side)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / replays
 
 
 def build_calls(torch, qmm, workload):
@@ -681,6 +719,10 @@ def main():
         t = sum(float(np.mean(c.k_ms)) * 1e-3 for c in calls)
         line.update(value=round(ops / t / 1e12, 2), unit="TOP/s")
         line["note"] = "value = int8 ops of the 224 matmuls over the sum of their kernel times"
+        # the whole step (224 quantize + 224 matmul launches) as one HIP graph
+        gms = graph_replay_ms(torch, calls)
+        line["graph"] = {"ms_per_step": round(gms, 4), "replays": 5,
+                         "TOP_s_incl_quantize": round(ops / (gms * 1e-3) / 1e12, 2)}
         line["config"] = {"workload": "dllm_step", "layers": 32, "canvas": 256, "hidden": 4096, "ffn": 12288,
                           "matmuls_per_step": len(calls), "down_projection": "Q6_K padded to 224-byte blocks"}
         detail = detail[:7]
