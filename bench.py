@@ -124,9 +124,13 @@ def q8k_tile(nt, od):
 
 
 def mmq_kernel(qmm, nt, od, idim):
-    """(kernel name, launch threads) of the Q4_K MMQ kernel the library runs for this
-    shape: 32*WR rows x 32*WC tokens per workgroup, KS groups splitting K, the
-    workgroup count padded to a multiple of the 8 XCDs."""
+    """(kernel name, launch threads) of the Q4_K matrix kernel qmm_matmul runs for this
+    shape with a full workspace: stream-K (256 workgroups of 8 waves) where
+    qmm_streamk_preferred, else the per-tile kernel: 32*WR rows x 32*WC tokens per
+    workgroup, KS groups splitting K, the workgroup count padded to a multiple of the
+    8 XCDs."""
+    if qmm.qmm_streamk_preferred(qmm.QMM_TYPE_Q4_K, nt, od, idim):
+        return "qmm::mmq_q4k_streamk_kernel<4, 2>", 256 * 512
     wr, wc, ks = MMQ_TILES[qmm.qmm_mmq_tile(nt, od, idim)]
     tiles = -(-nt // (32 * wc)) * -(-od // (32 * wr))
     return f"qmm::mmq_q4k_kernel<{wr}, {wc}, {ks}, false>", 8 * -(-tiles // 8) * 64 * wr * wc * ks
@@ -232,6 +236,17 @@ def graph_replay_ms(torch, calls, replays=5):
 def build_calls(torch, qmm, workload):
     Q4, Q6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K
     calls = []
+    sk_ws = []
+
+    def path_ws(qt, nt, od, idim):
+        """The stream-K workspace where qmm_matmul (with a full workspace) runs the
+        stream-K kernel, else None: matrix calls run what qmm_matmul runs."""
+        if not qmm.qmm_streamk_preferred(qt, nt, od, idim):
+            return None
+        if not sk_ws:  # one workspace: the calls run one after another on one stream
+            sk_ws.append(torch.empty(qmm.qmm_streamk_ws_bytes(), dtype=torch.uint8, device="cuda:0"))
+        return sk_ws[0]
+
     if workload == "q4k_decode_prefill":
         shared = {}
         for od, idim in ((4096, 4096), (12288, 4096)):
@@ -240,8 +255,10 @@ def build_calls(torch, qmm, workload):
                          copies=shared.get((od, idim)))
                 shared[(od, idim)] = c.W
                 calls.append(c)
-        calls.append(Call(torch, qmm, Q4, 12288, 4096, 512, seed=7, outliers=True, copies=shared[(12288, 4096)]))
-        calls.append(Call(torch, qmm, Q4, 4096, 12288, 512, seed=8, outliers=True))
+        calls.append(Call(torch, qmm, Q4, 12288, 4096, 512, seed=7, outliers=True, copies=shared[(12288, 4096)],
+                          streamk=path_ws(Q4, 512, 12288, 4096)))
+        calls.append(Call(torch, qmm, Q4, 4096, 12288, 512, seed=8, outliers=True,
+                          streamk=path_ws(Q4, 512, 4096, 12288)))
     elif workload == "q8k_prefill":
         # the prefill shapes on both activation schemes, same weights and inputs
         for od, idim, seed in ((12288, 4096, 7), (4096, 12288, 8)):
@@ -293,7 +310,8 @@ def build_calls(torch, qmm, workload):
             for p, (qt, od, idim) in enumerate(shapes):
                 copies, x = per_proj[p]
                 calls.append(Call(torch, qmm, qt, od, idim, 256, seed=0, outliers=False, copies=[copies[layer]],
-                                  label=f"layer{layer} proj{p} {od}x{idim}", x=x))
+                                  label=f"layer{layer} proj{p} {od}x{idim}", x=x,
+                                  streamk=path_ws(qt, 256, od, idim)))
     return calls
 
 
@@ -643,6 +661,9 @@ def main():
                                     "traffic": read_traffic(COUNTERS, mk, mg),
                                     "kernel": mk.replace("qmm::", "").replace(" ", ""), "call": m.label,
                                     "ops_per_launch": int(m.ops)}}
+        if "streamk" in mk:
+            # one kernel and one grid for both prefill shapes: the counters give their mean
+            line["mmq"]["roofline"]["traffic_note"] = "HBM bytes per launch, mean over both nt=512 shapes"
         line["config"] = {"workload": "q4k_decode_prefill",
                           "mmvq": "Q4_K 4096x4096 and 12288x4096, nt=1,4,8",
                           "mmq": "Q4_K 12288x4096 and 4096x12288, nt=512, 1% outliers x20",

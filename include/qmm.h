@@ -135,9 +135,13 @@ int qmm_quantize_act(const float* x, int nt, int id, int8_t* q, float* d, float*
  * [CH04, section 3.3]: one matmul call takes raw pointers, f32 activations, the
  * weight type and the shape, and quantizes the activations itself; invalid shapes
  * are errors, never a silent fallback.  [MMQ, section 12]: every nt has a kernel:
- * nt <= 8 (QMM_NT_SWITCH) runs MMVQ, larger nt runs MMQ.
+ * nt <= 8 (QMM_NT_SWITCH) runs MMVQ, larger nt runs MMQ (qmm_dispatch_kind).
  * workspace: device buffer of at least qmm_act_bytes(nt, id) bytes, used as
- * scratch (overwritten); ws_bytes its size. */
+ * scratch (overwritten); ws_bytes its size.  With at least qmm_act_bytes(nt, id) +
+ * qmm_streamk_ws_bytes() bytes, a call for which qmm_streamk_preferred() is 1 runs
+ * the stream-K kernel (its partial tiles after the q8 plane) instead of the
+ * per-tile MMQ; results then differ from the per-tile kernel's by f32 rounding
+ * only, and calls sharing a workspace must not overlap in time. */
 int qmm_matmul(int type, const void* W, const float* x, int nt, int od, int id, float* out,
                void* workspace, size_t ws_bytes, void* stream);
 
@@ -179,6 +183,14 @@ int qmm_mmq_tile(int nt, int od, int id);
  * fills at most a quarter of the GPU); QMM_KIND_MMQ otherwise.  A negative status
  * for invalid arguments. */
 int qmm_dispatch_kind(int type, int nt, int od, int id);
+
+/* 1 if the stream-K kernel is expected to be faster than the per-tile MMQ for this
+ * call (Q4_K, an MMQ call, a tile count (128 x 64 tiles) that is not a whole number
+ * of rounds of 256, and K of at least 32 super-blocks or more than 256 tiles:
+ * measured on Q4_K matrices of 1024..14336 rows and 4096..14336 columns at
+ * 17..512 tokens), else 0; a negative status for invalid arguments.  qmm_matmul
+ * follows it when its workspace is large enough. */
+int qmm_streamk_preferred(int type, int nt, int od, int id);
 
 /* The nt at or below which MMVQ runs on every shape (default 8; environment
  * QMM_NT_SWITCH, clamped to 0..8, read once; a value other than 8 also turns off

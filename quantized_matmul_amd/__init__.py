@@ -48,7 +48,7 @@ EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul"
            "qmm_mfma_tile_check", "qmm_strerror", "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize",
            "qmm_silu_mul_quantize", "qmm_residual_add", "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k",
            "qmm_matmul_q8k", "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_streamk_ws_bytes",
-           "qmm_matmul_q8_streamk")
+           "qmm_matmul_q8_streamk", "qmm_streamk_preferred")
 
 
 class QmmError(RuntimeError):
@@ -78,6 +78,7 @@ def lib():
         L.qmm_matmul_q8.argtypes = [I, P, P, P, P, I, I, I, P, P]
         L.qmm_matmul_q8_kind.argtypes = [I, I, P, P, P, P, I, I, I, P, P]
         L.qmm_dispatch_kind.argtypes = [I, I, I, I]
+        L.qmm_streamk_preferred.argtypes = [I, I, I, I]
         L.qmm_mmq_tile.argtypes = [I, I, I]
         L.qmm_nt_switch.argtypes = []
         L.qmm_group_dots.argtypes = [I, I, P, P, I, I, I, P, P]
@@ -102,7 +103,7 @@ def lib():
                   "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots", "qmm_mfma_tile_check",
                   "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize", "qmm_silu_mul_quantize", "qmm_residual_add",
                   "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k", "qmm_matmul_q8k",
-                  "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_matmul_q8_streamk"):
+                  "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_matmul_q8_streamk", "qmm_streamk_preferred"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -154,6 +155,22 @@ def qmm_dispatch_kind(qtype: int, nt: int, od: int, idim: int) -> int:
     if k < 0:
         raise QmmError(k, "qmm_dispatch_kind")
     return k
+
+
+def qmm_streamk_preferred(qtype: int, nt: int, od: int, idim: int) -> bool:
+    """Whether qmm_matmul runs the stream-K kernel for this call, given a workspace of
+    qmm_matmul_ws_bytes()."""
+    k = int(lib().qmm_streamk_preferred(qtype, nt, od, idim))
+    if k < 0:
+        raise QmmError(k, "qmm_streamk_preferred")
+    return k == 1
+
+
+def qmm_matmul_ws_bytes(qtype: int, nt: int, od: int, idim: int) -> int:
+    """Workspace bytes for qmm_matmul: the q8 plane, plus the stream-K partial tiles
+    where qmm_streamk_preferred."""
+    n = qmm_act_bytes(nt, idim)
+    return n + (qmm_streamk_ws_bytes() if qmm_streamk_preferred(qtype, nt, od, idim) else 0)
 
 
 def qmm_mmq_tile(nt: int, od: int, idim: int) -> int:
@@ -341,7 +358,8 @@ def qmm_matmul(qtype: int, W: torch.Tensor, x: torch.Tensor, od: int, out=None, 
     if out is None:
         out = torch.empty((nt, od), dtype=torch.float32, device=x.device)
     if workspace is None:
-        workspace = torch.empty(max(qmm_act_bytes(nt, idim), 1), dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(max(qmm_matmul_ws_bytes(qtype, nt, od, idim), 1), dtype=torch.uint8,
+                                device=x.device)
     _check(lib().qmm_matmul(qtype, _dev(W, torch.uint8, "W"), _dev(x, torch.float32, "x"), nt, od, idim,
                             _dev(out, torch.float32, "out"), _dev(workspace, torch.uint8, "workspace"),
                             workspace.numel(), _stream(stream)), "qmm_matmul")

@@ -125,6 +125,22 @@ int dispatch_kind(int nt, int od)
     return QMM_KIND_MMQ;
 }
 
+// Whether the stream-K kernel (Q4_K) is expected to beat the per-tile MMQ on this
+// call (measured over 1024..14336-row, 4096..14336-column matrices at 17..512
+// tokens): a long K (>= 32 super-blocks: the few tiles of such a matrix each walk
+// a long chain, up to 2x faster split over all CUs) or more 128 x 64 tiles than one
+// round of the 256 CUs (a fractional last round: 6-20 % faster).  Short-K grids
+// within one round stay per tile (there stream-K loses up to 25 %), and so does a
+// whole number of rounds (256, 512, 768 tiles: no tail to balance; measured equal
+// within 1 %, with more HBM re-reads for stream-K).
+bool streamk_preferred(int type, int nt, int od, int id)
+{
+    if (type != QMM_TYPE_Q4_K || dispatch_kind(nt, od) != QMM_KIND_MMQ)
+        return false;
+    const long tiles = (long)((nt + 63) / 64) * ((od + 127) / 128);
+    return tiles % 256 != 0 && (id / 256 >= 32 || tiles > 256);
+}
+
 int matmul_q8_checked(int kind, int type, const void* W, const int8_t* q, const float* d,
                       const float* s, int nt, int od, int id, float* out, int32_t* S, void* stream)
 {
@@ -409,6 +425,17 @@ int qmm_matmul_q8_streamk(int type, const void* W, const int8_t* q, const float*
 
 int qmm_nt_switch(void) { return nt_switch_value(); }
 
+int qmm_streamk_preferred(int type, int nt, int od, int id)
+{
+    int rc = check_type(type);
+    if (rc)
+        return rc;
+    rc = check_shape(nt, od, id);
+    if (rc)
+        return rc;
+    return streamk_preferred(type, nt, od, id) ? 1 : 0;
+}
+
 int qmm_dispatch_kind(int type, int nt, int od, int id)
 {
     int rc = check_type(type);
@@ -482,6 +509,12 @@ int qmm_matmul(int type, const void* W, const float* x, int nt, int od, int id, 
     rc = launched(qmm::launch_quantize(x, nt, id, q, d, s, st));
     if (rc)
         return rc;
+    // the stream-K kernel where it is faster and the workspace also holds its
+    // partial tiles (after the q8 plane, at a 256-byte boundary)
+    const size_t act = qmm_act_bytes(nt, id);
+    if (streamk_preferred(type, nt, od, id) && ws_bytes >= act + qmm::mmq_streamk_ws_bytes())
+        return launched(qmm::launch_mmq_streamk(static_cast<const uint8_t*>(W), q, d, s, nt, od, id, out,
+                                                reinterpret_cast<float*>(base + act), st));
     const int kind = dispatch_kind(nt, od);
     return matmul_q8_checked(kind, type, W, q, d, s, nt, od, id, out, nullptr, stream);
 }

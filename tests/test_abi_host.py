@@ -72,6 +72,31 @@ def test_dispatch_kind_host():
             assert qmm.qmm_dispatch_kind(qt, nt, 4097, 4096) == qmm.QMM_KIND_MMQ
     for nt in (17, 256, 512):
         assert qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q6_K, nt, 4096, 4096) == qmm.QMM_KIND_MMQ
+
+
+def test_streamk_preferred_host():
+    """Stream-K for Q4_K MMQ calls whose 128 x 64 tile count is not a whole number of
+    rounds of 256, with K of at least 32 super-blocks or more than 256 tiles; never
+    for vector-kernel calls or other types."""
+    Q4, Q6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K
+    assert qmm.qmm_streamk_preferred(Q4, 17, 4096, 12288)      # 48 super-blocks, 32 tiles
+    assert qmm.qmm_streamk_preferred(Q4, 448, 4096, 8192)       # 32 super-blocks, 224 tiles
+    assert not qmm.qmm_streamk_preferred(Q4, 448, 4096, 7936)   # 31 super-blocks
+    assert not qmm.qmm_streamk_preferred(Q4, 512, 4096, 12288)  # 256 tiles: one whole round
+    assert not qmm.qmm_streamk_preferred(Q4, 512, 12288, 4096)  # 768 tiles: three rounds
+    assert qmm.qmm_streamk_preferred(Q4, 384, 12288, 4096)      # 576 tiles
+    assert qmm.qmm_streamk_preferred(Q4, 192, 12288, 4096)      # 288 tiles
+    assert not qmm.qmm_streamk_preferred(Q4, 128, 12288, 4096)  # 192 tiles
+    assert not qmm.qmm_streamk_preferred(Q4, 256, 4096, 4096)   # 128 tiles
+    assert not qmm.qmm_streamk_preferred(Q4, 8, 4096, 65536)    # vector kernel
+    assert not qmm.qmm_streamk_preferred(Q4, 12, 4096, 65536)   # vector kernel on slices
+    assert qmm.qmm_streamk_preferred(Q4, 12, 4097, 65536)       # MMQ above 4096 rows
+    assert not qmm.qmm_streamk_preferred(Q6, 512, 4096, 12288)
+    n = qmm.qmm_act_bytes(384, 12288)
+    assert qmm.qmm_matmul_ws_bytes(Q4, 384, 4096, 12288) == n + qmm.qmm_streamk_ws_bytes()
+    assert qmm.qmm_matmul_ws_bytes(Q6, 384, 4096, 12288) == n
+    with pytest.raises(qmm.QmmError):
+        qmm.qmm_streamk_preferred(Q4, 512, 4096, 4000)
     with pytest.raises(qmm.QmmError):
         qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q4_K, 1, 4096, 4000)
 

@@ -62,3 +62,47 @@ def test_streamk(nt, od, idim):
         tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
         ref, mag = oracle.matmul_q8_points(Q4, W, qn, dn, sn, od, tt, rr)
         assert_close(an[tt, rr], ref, mag, Q4, idim, "stream-K vs oracle (sampled)")
+
+
+PATH_CASES = [(20, 96, 8192), (9, 40, 65536), (300, 1000, 2304), (384, 4096, 12288), (512, 4096, 12288),
+              (384, 12288, 4096), (512, 12288, 4096), (128, 12288, 4096)]
+
+
+@pytest.mark.parametrize("nt,od,idim", PATH_CASES, ids=[f"{a}x{b}x{c}" for a, b, c in PATH_CASES])
+def test_qmm_matmul_takes_streamk_where_preferred(nt, od, idim):
+    """qmm_matmul with a workspace of qmm_matmul_ws_bytes runs the stream-K kernel
+    exactly where qmm_streamk_preferred says so (same bits as the stream-K entry
+    point on the same quantized input), the per-tile kernel elsewhere and with a
+    workspace of only the q8 plane (same bits as qmm_matmul_q8); outputs within the
+    tolerance of the oracle."""
+    pref = qmm.qmm_streamk_preferred(Q4, nt, od, idim)
+    print(f"qmm_matmul path nt={nt} od={od} id={idim} stream-K preferred={pref}", flush=True)
+    mmq = qmm.qmm_dispatch_kind(Q4, nt, od, idim) == qmm.QMM_KIND_MMQ
+    tiles = -(-nt // 64) * -(-od // 128)
+    assert pref == (mmq and tiles % 256 != 0 and (idim // 256 >= 32 or tiles > 256))
+    W = synth.weights(Q4, od, idim, seed=4200 + od)
+    x = synth.activations(nt, idim, seed=4300 + nt, outlier_frac=0.01)
+    Wt, xt = _up(W), _up(x)
+    full = qmm.qmm_matmul(Q4, Wt, xt, od)   # workspace of qmm_matmul_ws_bytes
+    small = qmm.qmm_matmul(Q4, Wt, xt, od,
+                           workspace=torch.empty(qmm.qmm_act_bytes(nt, idim), dtype=torch.uint8, device=DEV))
+    q, d, s = qmm.qmm_quantize_act(xt)
+    ws = torch.empty(qmm.qmm_streamk_ws_bytes(), dtype=torch.uint8, device=DEV)
+    sk = qmm.qmm_matmul_q8_streamk(Q4, Wt, q, d, s, od, ws)
+    pt = qmm.qmm_matmul_q8(Q4, Wt, q, d, s, od)
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int32)
+    assert torch.equal(bits(full), bits(sk if pref else pt))
+    assert torch.equal(bits(small), bits(pt))
+    qn, dn, sn = q.cpu().numpy(), d.cpu().numpy(), s.cpu().numpy()
+    if nt * od <= 300 * 1000:
+        ref, mag = oracle.matmul_q8(Q4, W, qn, dn, sn, od)
+        assert_close(full.cpu().numpy(), ref, mag, Q4, idim, "qmm_matmul vs oracle")
+    else:
+        rng = np.random.default_rng(od + nt + 1)
+        ts = np.unique(np.concatenate([rng.choice(nt, 16, replace=False), [0, nt - 1]]))
+        rs = np.unique(np.concatenate([rng.choice(od, 128, replace=False), [0, od - 1]]))
+        tt, rr = np.meshgrid(ts, rs, indexing="ij")
+        tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
+        ref, mag = oracle.matmul_q8_points(Q4, W, qn, dn, sn, od, tt, rr)
+        assert_close(full.cpu().numpy()[tt, rr], ref, mag, Q4, idim, "qmm_matmul vs oracle (sampled)")
