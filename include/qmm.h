@@ -158,15 +158,16 @@ int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, cons
 int qmm_matmul_q8_kind(int kind, int type, const void* W, const int8_t* q, const float* d,
                        const float* s, int nt, int od, int id, float* out, void* stream);
 
-/* Stream-K matrix kernel (Q4_K weights, any nt): the ntiles x (id/256) units of
- * (128 x 64 tile, super-block) are cut into 256 equal contiguous ranges, one per
- * workgroup, so a tile count that does not fill the chip still loads every CU;
- * tiles split between workgroups are combined by a second kernel that adds the
- * partials in workgroup order (a fixed order: results do not depend on timing,
- * and differ from qmm_matmul_q8 by f32 rounding only).  workspace: caller's device
- * buffer of at least qmm_streamk_ws_bytes() bytes (QMM_ERR_WORKSPACE), 16-byte
- * aligned, overwritten.  Type Q4_K only (QMM_ERR_TYPE); other rules as
- * qmm_matmul_q8.  Calls that share a workspace must not overlap in time. */
+/* Stream-K matrix kernel (Q4_K and Q6_K weights in both layouts, any nt): the
+ * ntiles x (id/256) units of (128 x 64 tile, super-block) are cut into 256 equal
+ * contiguous ranges, one per workgroup, so a tile count that does not fill the
+ * chip still loads every CU; tiles split between workgroups are combined by a
+ * second kernel that adds the partials in workgroup order (a fixed order: results
+ * do not depend on timing, and differ from qmm_matmul_q8 by f32 rounding only).
+ * workspace: caller's device buffer of at least qmm_streamk_ws_bytes() bytes
+ * (QMM_ERR_WORKSPACE), 16-byte aligned, overwritten.  Types Q4_K, Q6_K and
+ * Q6_K_P224 (others: QMM_ERR_TYPE); other rules as qmm_matmul_q8.  Calls that
+ * share a workspace must not overlap in time. */
 size_t qmm_streamk_ws_bytes(void);
 int qmm_matmul_q8_streamk(int type, const void* W, const int8_t* q, const float* d, const float* s, int nt,
                           int od, int id, float* out, void* workspace, size_t ws_bytes, void* stream);
@@ -185,11 +186,13 @@ int qmm_mmq_tile(int nt, int od, int id);
 int qmm_dispatch_kind(int type, int nt, int od, int id);
 
 /* 1 if the stream-K kernel is expected to be faster than the per-tile MMQ for this
- * call (Q4_K, an MMQ call, a tile count (128 x 64 tiles) that is not a whole number
- * of rounds of 256, and K of at least 32 super-blocks or more than 256 tiles:
- * measured on Q4_K matrices of 1024..14336 rows and 4096..14336 columns at
- * 17..512 tokens), else 0; a negative status for invalid arguments.  qmm_matmul
- * follows it when its workspace is large enough. */
+ * call, else 0; a negative status for invalid arguments.  Q4_K and Q6_K (both
+ * layouts), MMQ calls only.  With T tiles of 128 x 64: never when T is a multiple
+ * of 256; for T > 256 when the last round of 256 workgroups leaves at least 10 %
+ * of all workgroup slots idle; for T < 256 when K has at least 32 super-blocks, or
+ * for Q6_K when T <= 64.  Measured on Q4_K and Q6_K matrices of 1024..32000 rows
+ * and 4096..14336 columns at 17..512 tokens.  qmm_matmul follows it when its
+ * workspace is large enough. */
 int qmm_streamk_preferred(int type, int nt, int od, int id);
 
 /* The nt at or below which MMVQ runs on every shape (default 8; environment

@@ -125,20 +125,30 @@ int dispatch_kind(int nt, int od)
     return QMM_KIND_MMQ;
 }
 
-// Whether the stream-K kernel (Q4_K) is expected to beat the per-tile MMQ on this
-// call (measured over 1024..14336-row, 4096..14336-column matrices at 17..512
-// tokens): a long K (>= 32 super-blocks: the few tiles of such a matrix each walk
-// a long chain, up to 2x faster split over all CUs) or more 128 x 64 tiles than one
-// round of the 256 CUs (a fractional last round: 6-20 % faster).  Short-K grids
-// within one round stay per tile (there stream-K loses up to 25 %), and so does a
-// whole number of rounds (256, 512, 768 tiles: no tail to balance; measured equal
-// within 1 %, with more HBM re-reads for stream-K).
+// Whether the stream-K kernel is expected to beat the per-tile MMQ on this call
+// (Q4_K and Q6_K, measured over 1024..32000-row, 4096..14336-column matrices at
+// 17..512 tokens).  With T tiles of 128 x 64 and R = ceil(T / 256) rounds of the
+// 256 CUs:
+//  * T a whole number of rounds: no tail to balance; per tile (within 5 % either
+//    way, and stream-K re-reads more from HBM);
+//  * T > 256: stream-K when the last round leaves at least 10 % of the R * 256
+//    workgroup slots idle (6-22 % faster there; equal below);
+//  * T < 256: stream-K for a long K (>= 32 super-blocks: the few tiles each walk a
+//    long chain; up to 2x faster for Q4_K, 2.5x for Q6_K), and for Q6_K grids of at
+//    most 64 tiles (1.2-1.4x); otherwise per tile (stream-K up to 25 % slower).
 bool streamk_preferred(int type, int nt, int od, int id)
 {
-    if (type != QMM_TYPE_Q4_K || dispatch_kind(nt, od) != QMM_KIND_MMQ)
+    const bool q6 = type == QMM_TYPE_Q6_K || type == QMM_TYPE_Q6_K_P224;
+    if ((type != QMM_TYPE_Q4_K && !q6) || dispatch_kind(nt, od) != QMM_KIND_MMQ)
         return false;
     const long tiles = (long)((nt + 63) / 64) * ((od + 127) / 128);
-    return tiles % 256 != 0 && (id / 256 >= 32 || tiles > 256);
+    if (tiles % 256 == 0)
+        return false;
+    if (tiles > 256) {
+        const long slots = 256 * ((tiles + 255) / 256);
+        return (slots - tiles) * 10 >= slots;
+    }
+    return id / 256 >= 32 || (q6 && tiles <= 64);
 }
 
 int matmul_q8_checked(int kind, int type, const void* W, const int8_t* q, const float* d,
@@ -408,7 +418,7 @@ int qmm_matmul_q8_streamk(int type, const void* W, const int8_t* q, const float*
     int rc = validate_q8(type, W, q, d, s, nt, od, id, out);
     if (rc)
         return rc;
-    if (type != QMM_TYPE_Q4_K)
+    if (type != QMM_TYPE_Q4_K && type != QMM_TYPE_Q6_K && type != QMM_TYPE_Q6_K_P224)
         return QMM_ERR_TYPE;
     if (!workspace)
         return QMM_ERR_ARG;
@@ -418,7 +428,7 @@ int qmm_matmul_q8_streamk(int type, const void* W, const int8_t* q, const float*
         return QMM_ERR_WORKSPACE;
     if ((rc = check_device()))
         return rc;
-    return launched(qmm::launch_mmq_streamk(reinterpret_cast<const uint8_t*>(W), q, d, s, nt, od, id, out,
+    return launched(qmm::launch_mmq_streamk(type, reinterpret_cast<const uint8_t*>(W), q, d, s, nt, od, id, out,
                                             reinterpret_cast<float*>(workspace),
                                             reinterpret_cast<hipStream_t>(stream)));
 }
@@ -513,7 +523,7 @@ int qmm_matmul(int type, const void* W, const float* x, int nt, int od, int id, 
     // partial tiles (after the q8 plane, at a 256-byte boundary)
     const size_t act = qmm_act_bytes(nt, id);
     if (streamk_preferred(type, nt, od, id) && ws_bytes >= act + qmm::mmq_streamk_ws_bytes())
-        return launched(qmm::launch_mmq_streamk(static_cast<const uint8_t*>(W), q, d, s, nt, od, id, out,
+        return launched(qmm::launch_mmq_streamk(type, static_cast<const uint8_t*>(W), q, d, s, nt, od, id, out,
                                                 reinterpret_cast<float*>(base + act), st));
     const int kind = dispatch_kind(nt, od);
     return matmul_q8_checked(kind, type, W, q, d, s, nt, od, id, out, nullptr, stream);

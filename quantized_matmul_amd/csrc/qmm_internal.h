@@ -31,10 +31,10 @@ hipError_t launch_mmvq(int type, const uint8_t* W, const int8_t* q, const float*
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
                       int nt, int od, int id, float* out, int32_t* S, hipStream_t st, int tile = 0);
 int mmq_tile_choice(int nt, int od, int id);
-// Stream-K (Q4_K only): workspace of mmq_streamk_ws_bytes() bytes, 16-byte aligned.
+// Stream-K (Q4_K and Q6_K in both layouts): workspace of mmq_streamk_ws_bytes() bytes, 16-byte aligned.
 size_t mmq_streamk_ws_bytes();
-hipError_t launch_mmq_streamk(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od,
-                              int id, float* out, float* ws, hipStream_t st);
+hipError_t launch_mmq_streamk(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt,
+                              int od, int id, float* out, float* ws, hipStream_t st);
 
 // Q8_K activations: q [nt][id] int8, d [nt][id/256] f32, bsum [nt][id/16] f32
 // (id % 256 == 0), and the Q4_K matmul on them (qmm_mmq_q8k.hip).  S != null: the

@@ -815,6 +815,39 @@ __device__ __forceinline__ void q6_stage(Q6Smem<BM, BN>& sm, const uint32_t (&pl
     }
 }
 
+// Step m of a staged Q6_K super-block: groups 2m and 2m + 1 (they share activation
+// block m): this lane's 8 code bytes of each group (row arow), the matching 8
+// activation bytes (token btok), and the scale factors of group 2m + lh.
+template <int BM, int BN>
+__device__ __forceinline__ Ops8 q6_load(const Q6Smem<BM, BN>& sm, int m, int arow, int btok, int lh)
+{
+    using SM = Q6Smem<BM, BN>;
+    Ops8 o;
+    o.a0 = *reinterpret_cast<const long*>(&sm.wq[arow * SM::W_STRIDE + 32 * m + 8 * lh]);
+    o.a1 = *reinterpret_cast<const long*>(&sm.wq[arow * SM::W_STRIDE + 32 * m + 16 + 8 * lh]);
+    o.b0 = *reinterpret_cast<const long*>(&sm.xq[btok * SM::X_STRIDE + 32 * m + 8 * lh]);
+    o.b1 = *reinterpret_cast<const long*>(&sm.xq[btok * SM::X_STRIDE + 32 * m + 16 + 8 * lh]);
+    o.ws = sm.wsc[(2 * m + lh) * BM + arow];
+    o.xd = sm.xd[m * BN + btok];
+    return o;
+}
+
+// The eight steps of one staged Q6_K super-block, added into accv (the stream-K
+// kernel; the per-tile kernel keeps its own copy of the step code, which the
+// compiler fits in registers without spilling at 128 x 64).
+template <int BM, int BN, int PIPE>
+__device__ __forceinline__ void q6_superblock(const Q6Smem<BM, BN>& sm, int arow, int btok, int lh, v16f& accv)
+{
+    pipelined_steps<8, PIPE, Ops8>(
+        [&](int m) { return q6_load<BM, BN>(sm, m, arow, btok, lh); },
+        [&](const Ops8& o, int, v16i& C0, v16i& C1, v32f& P) {
+            C0 = mfma_i8_k16(o.a0, o.b0);
+            C1 = mfma_i8_k16(o.a1, o.b1);
+            P = mfma_outer2(o.ws, o.xd);
+        },
+        accv);
+}
+
 template <int WR, int WC, int KS, bool DUMP, bool PAD>
 __global__ __launch_bounds__(64 * WR * WC * KS, 2) void mmq_q6k_kernel(const uint8_t* __restrict__ W,
                                                                     const int8_t* __restrict__ q,
@@ -1244,17 +1277,95 @@ int mmq_tile_choice(int nt, int od, int id)
     return c2 <= c3 ? 2 : 3;
 }
 
-// Stream-K launch (Q4_K): 128 x 64 tiles, 256 workgroups (one per CU at this tile's
-// LDS size).  Workspace: 2 partial tiles per workgroup.
+// Q6_K stream-K: the Q4_K stream-K walk (unit ranges, direct stores of whole tiles,
+// workspace slots for partial ones) over the Q6_K staging and steps.
+template <int WR, int WC, bool PAD>
+__global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q6k_streamk_kernel(const uint8_t* __restrict__ W,
+                                                                         const int8_t* __restrict__ q,
+                                                                         const float* __restrict__ dx,
+                                                                         float* __restrict__ out, int nt, int od,
+                                                                         int id, float* __restrict__ ws, int G)
+{
+    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC, NW = WR * WC;
+    constexpr int WC8 = (BM * 8 + NTH - 1) / NTH;
+    constexpr int XC = (BN * 16 + NTH - 1) / NTH;
+    constexpr int SC = (BN * 2 + NTH - 1) / NTH;
+    using SM = Q6Smem<BM, BN>;
+    __shared__ SM smb[2];
+
+    const int ntb = (nt + BN - 1) / BN;
+    const int ntiles = ntb * ((od + BM - 1) / BM);
+    const int nsb = id >> 8, nblk = id >> 5;
+    const long units = (long)ntiles * nsb;
+    const int g = (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
+    const long u0 = sk_first_unit(g, units, G), u1 = sk_first_unit(g + 1, units, G);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / WC, wc = wave % WC;
+    const int li = lane & 31, lh = lane >> 5;
+    const size_t row_bytes = (size_t)nsb * (PAD ? kQ6KP224Bytes : kQ6KBytes);
+    const int arow = wr * 32 + li, btok = wc * 32 + li;
+    const int first_tile = (int)(u0 / nsb);
+
+    for (long u = u0; u < u1;) {
+        const int tile = (int)(u / nsb);
+        const int k0 = (int)(u - (long)tile * nsb);
+        const int k1 = (int)min((long)nsb, k0 + (u1 - u));
+        const int row0 = (tile / ntb) * BM, tok0 = (tile % ntb) * BN;
+
+        uint32_t pl[WC8][5], phh[WC8][5];
+        uint32_t pshift[WC8];
+        v4i px[XC], ps[SC];
+        uint32_t psd[WC8];
+        v16f accv = {};
+        q6_prefetch<BM, BN, NTH, WC8, XC, SC, PAD>(pl, phh, pshift, px, ps, psd, W, q, dx, k0, tid, row0, tok0, nt, od,
+                                                  id, nblk, row_bytes);
+        q6_stage<BM, BN, NTH, WC8, XC, SC>(smb[0], pl, phh, pshift, px, ps, psd, tid, true);
+        q6_prefetch<BM, BN, NTH, WC8, XC, SC, PAD>(pl, phh, pshift, px, ps, psd, W, q, dx, min(k0 + 1, k1 - 1), tid,
+                                                  row0, tok0, nt, od, id, nblk, row_bytes);
+        __syncthreads();
+        for (int sb = k0; sb < k1; ++sb) {
+            const SM& sm = smb[(sb - k0) & 1];
+            // the unpadded layout's five-dword prefetch windows leave no room for a step of results
+            q6_superblock<BM, BN, PAD ? kPipeMfma : kPipeNone>(sm, arow, btok, lh, accv);
+            __builtin_amdgcn_sched_barrier(0);
+            q6_stage<BM, BN, NTH, WC8, XC, SC>(smb[(sb - k0 + 1) & 1], pl, phh, pshift, px, ps, psd, tid, sb + 1 < k1);
+            q6_prefetch<BM, BN, NTH, WC8, XC, SC, PAD>(pl, phh, pshift, px, ps, psd, W, q, dx, min(sb + 2, k1 - 1), tid,
+                                                      row0, tok0, nt, od, id, nblk, row_bytes);
+            __syncthreads();
+        }
+        if (k0 == 0 && k1 == nsb) {
+            store_tile(accv, out, nt, od, tok0 + btok, row0 + wr * 32, lh);
+        } else {
+            float* slot = ws + ((size_t)(2 * g + (tile == first_tile ? 0 : 1)) * NW + wave) * 1024;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                slot[i * 64 + lane] = accv[i];
+        }
+        u += k1 - k0;
+    }
+}
+
+// Stream-K launch (Q4_K, Q6_K in both layouts): 128 x 64 tiles, 256 workgroups (one
+// per CU at this tile's LDS size).  Workspace: 2 partial tiles per workgroup.
 constexpr int kStreamKGroups = 256;
 
 size_t mmq_streamk_ws_bytes() { return (size_t)kStreamKGroups * 2 * 128 * 64 * sizeof(float); }
 
-hipError_t launch_mmq_streamk(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od,
-                              int id, float* out, float* ws, hipStream_t st)
+hipError_t launch_mmq_streamk(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt,
+                              int od, int id, float* out, float* ws, hipStream_t st)
 {
     const int G = kStreamKGroups;
-    hipLaunchKernelGGL((mmq_q4k_streamk_kernel<4, 2>), dim3(G), dim3(512), 0, st, W, q, d, s, out, nt, od, id, ws, G);
+    if (type == 1)
+        hipLaunchKernelGGL((mmq_q4k_streamk_kernel<4, 2>), dim3(G), dim3(512), 0, st, W, q, d, s, out, nt, od, id, ws,
+                           G);
+    else if (type == 2)
+        hipLaunchKernelGGL((mmq_q6k_streamk_kernel<4, 2, false>), dim3(G), dim3(512), 0, st, W, q, d, out, nt, od, id,
+                           ws, G);
+    else if (type == 3)
+        hipLaunchKernelGGL((mmq_q6k_streamk_kernel<4, 2, true>), dim3(G), dim3(512), 0, st, W, q, d, out, nt, od, id,
+                           ws, G);
+    else
+        return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

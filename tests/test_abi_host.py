@@ -75,26 +75,34 @@ def test_dispatch_kind_host():
 
 
 def test_streamk_preferred_host():
-    """Stream-K for Q4_K MMQ calls whose 128 x 64 tile count is not a whole number of
-    rounds of 256, with K of at least 32 super-blocks or more than 256 tiles; never
-    for vector-kernel calls or other types."""
-    Q4, Q6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K
-    assert qmm.qmm_streamk_preferred(Q4, 17, 4096, 12288)      # 48 super-blocks, 32 tiles
-    assert qmm.qmm_streamk_preferred(Q4, 448, 4096, 8192)       # 32 super-blocks, 224 tiles
-    assert not qmm.qmm_streamk_preferred(Q4, 448, 4096, 7936)   # 31 super-blocks
-    assert not qmm.qmm_streamk_preferred(Q4, 512, 4096, 12288)  # 256 tiles: one whole round
-    assert not qmm.qmm_streamk_preferred(Q4, 512, 12288, 4096)  # 768 tiles: three rounds
-    assert qmm.qmm_streamk_preferred(Q4, 384, 12288, 4096)      # 576 tiles
-    assert qmm.qmm_streamk_preferred(Q4, 192, 12288, 4096)      # 288 tiles
-    assert not qmm.qmm_streamk_preferred(Q4, 128, 12288, 4096)  # 192 tiles
-    assert not qmm.qmm_streamk_preferred(Q4, 256, 4096, 4096)   # 128 tiles
-    assert not qmm.qmm_streamk_preferred(Q4, 8, 4096, 65536)    # vector kernel
-    assert not qmm.qmm_streamk_preferred(Q4, 12, 4096, 65536)   # vector kernel on slices
-    assert qmm.qmm_streamk_preferred(Q4, 12, 4097, 65536)       # MMQ above 4096 rows
-    assert not qmm.qmm_streamk_preferred(Q6, 512, 4096, 12288)
+    """Stream-K for Q4_K and Q6_K MMQ calls: never for a whole number of rounds of 256
+    tiles (128 x 64); above 256 tiles when the last round leaves >= 10 % of the
+    workgroup slots idle; within one round for K of >= 32 super-blocks, or Q6_K grids
+    of at most 64 tiles.  Never for vector-kernel calls or other types."""
+    Q4, Q6, P6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K, qmm.QMM_TYPE_Q6_K_P224
+    sp = qmm.qmm_streamk_preferred
+    for qt in (Q4, Q6, P6):
+        assert sp(qt, 17, 4096, 12288)               # 48 super-blocks, 32 tiles
+        assert sp(qt, 448, 4096, 8192)                # 32 super-blocks, 224 tiles
+        assert not sp(qt, 512, 4096, 12288)           # 256 tiles: one whole round
+        assert not sp(qt, 512, 12288, 4096)           # 768 tiles: three rounds
+        assert sp(qt, 192, 12288, 4096)               # 288 tiles: 44 % of 512 slots idle
+        assert sp(qt, 384, 14336, 4096)               # 672 tiles: 12.5 % of 768 idle
+        assert not sp(qt, 128, 32000, 4096)           # 500 tiles: 2.3 % of 512 idle
+        assert not sp(qt, 128, 12288, 4096)           # 192 tiles, short K
+        assert not sp(qt, 8, 4096, 65536)             # vector kernel
+        assert not sp(qt, 12, 4096, 65536)            # vector kernel on slices
+        assert sp(qt, 12, 4097, 65536)                # MMQ above 4096 rows
+    assert not sp(Q4, 448, 4096, 7936)                # 31 super-blocks, 224 tiles
+    # short K within one round: only Q6_K grids of at most 64 tiles
+    assert not sp(Q4, 64, 4096, 4096) and sp(Q6, 64, 4096, 4096) and sp(P6, 128, 4096, 4096)
+    assert not sp(Q6, 192, 4096, 4096)                # 96 tiles
+    assert not sp(qmm.QMM_TYPE_Q4_0, 512, 4096, 12288)
+    assert not sp(qmm.QMM_TYPE_Q5_K, 512, 4096, 12288)
     n = qmm.qmm_act_bytes(384, 12288)
     assert qmm.qmm_matmul_ws_bytes(Q4, 384, 4096, 12288) == n + qmm.qmm_streamk_ws_bytes()
-    assert qmm.qmm_matmul_ws_bytes(Q6, 384, 4096, 12288) == n
+    assert qmm.qmm_matmul_ws_bytes(Q6, 384, 4096, 12288) == n + qmm.qmm_streamk_ws_bytes()
+    assert qmm.qmm_matmul_ws_bytes(Q4, 512, 4096, 12288) == qmm.qmm_act_bytes(512, 12288)
     with pytest.raises(qmm.QmmError):
         qmm.qmm_streamk_preferred(Q4, 512, 4096, 4000)
     with pytest.raises(qmm.QmmError):
@@ -179,7 +187,12 @@ def test_streamk_validation():
     n = qmm.qmm_streamk_ws_bytes()
     assert n == 256 * 2 * 128 * 64 * 4
     assert L.qmm_matmul_q8_streamk(1, p, p, p, p, 9, 4, 256, p, None, n, None) == qmm.QMM_ERR_ARG
-    assert L.qmm_matmul_q8_streamk(2, p, p, p, p, 9, 4, 256, p, p, n, None) == qmm.QMM_ERR_TYPE
+    # Q4_K and Q6_K (both layouts) pass validation (the device check answers here);
+    # the 32-block types and Q5_K have no stream-K kernel
+    for t in (1, 2, 3):
+        assert L.qmm_matmul_q8_streamk(t, p, p, p, p, 9, 4, 256, p, p, n, None) == qmm.QMM_ERR_DEVICE
+    for t in (4, 5, 6):
+        assert L.qmm_matmul_q8_streamk(t, p, p, p, p, 9, 4, 256, p, p, n, None) == qmm.QMM_ERR_TYPE
     assert L.qmm_matmul_q8_streamk(1, p, p, p, p, 9, 4, 256, p, p, n - 1, None) == qmm.QMM_ERR_WORKSPACE
     assert L.qmm_matmul_q8_streamk(1, p, p, p, p, 9, 4, 256, p, ctypes.c_void_p((1 << 20) + 4), n, None) == \
         qmm.QMM_ERR_ALIGN

@@ -1,4 +1,4 @@
-"""GPU parity of the stream-K matrix kernel (Q4_K), through the C ABI.
+"""GPU parity of the stream-K matrix kernel (Q4_K, Q6_K in both layouts), through the C ABI.
 
 The (tile, super-block) units of a launch are cut into equal ranges, one per
 workgroup; tiles split between workgroups are added by a fixup kernel in a fixed
@@ -24,7 +24,7 @@ from tests._parity import assert_close
 pytestmark = pytest.mark.gpu
 
 qmm = pytest.importorskip("quantized_matmul_amd")
-Q4 = qmm.QMM_TYPE_Q4_K
+Q4, Q6, P6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K, qmm.QMM_TYPE_Q6_K_P224
 DEV = "cuda:0"
 
 
@@ -32,77 +32,98 @@ def _up(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
+def _weights(qtype, od, idim, seed):
+    """Host weight bytes of the type (the padded layout: each 210-byte Q6_K block
+    followed by 14 zero bytes), as the oracle and the kernels take them."""
+    W = synth.weights(Q6 if qtype == P6 else qtype, od, idim, seed=seed)
+    if qtype != P6:
+        return W
+    b = np.ascontiguousarray(W, dtype=np.uint8).reshape(-1, 210)
+    out = np.zeros((b.shape[0], 224), np.uint8)
+    out[:, :210] = b
+    return out.reshape(-1)
+
+
 CASES = [(1, 1, 256), (9, 100, 768), (64, 128, 1024), (17, 40, 65536), (300, 1000, 2304), (130, 96, 4096),
          (256, 4096, 4096), (256, 12288, 4096), (512, 12288, 4096), (512, 4096, 12288)]
 
 
-@pytest.mark.parametrize("nt,od,idim", CASES, ids=[f"{a}x{b}x{c}" for a, b, c in CASES])
-def test_streamk(nt, od, idim):
-    print(f"stream-K nt={nt} od={od} id={idim}", flush=True)
-    W = synth.weights(Q4, od, idim, seed=4000 + od)
+CASES6 = [(1, 1, 256), (9, 100, 768), (17, 40, 65536), (300, 1000, 2304), (130, 96, 4096), (64, 4096, 4096),
+          (192, 12288, 4096), (17, 4096, 12288)]
+TYPED = [(Q4,) + c for c in CASES] + [(qt,) + c for qt in (Q6, P6) for c in CASES6]
+
+
+@pytest.mark.parametrize("qtype,nt,od,idim", TYPED, ids=[f"t{q}-{a}x{b}x{c}" for q, a, b, c in TYPED])
+def test_streamk(qtype, nt, od, idim):
+    print(f"stream-K type={qtype} nt={nt} od={od} id={idim}", flush=True)
+    W = _weights(qtype, od, idim, seed=4000 + od)
     x = synth.activations(nt, idim, seed=4100 + nt, outlier_frac=0.01)
     Wt = _up(W)
     q, d, s = qmm.qmm_quantize_act(_up(x))
     ws = torch.full((qmm.qmm_streamk_ws_bytes(),), 0xFF, dtype=torch.uint8, device=DEV)
-    a = qmm.qmm_matmul_q8_streamk(Q4, Wt, q, d, s, od, ws)
-    b = qmm.qmm_matmul_q8_streamk(Q4, Wt, q, d, s, od, ws)
+    a = qmm.qmm_matmul_q8_streamk(qtype, Wt, q, d, s, od, ws)
+    b = qmm.qmm_matmul_q8_streamk(qtype, Wt, q, d, s, od, ws)
     torch.cuda.synchronize()
     an = a.cpu().numpy()
     assert np.array_equal(an.view(np.uint32), b.cpu().numpy().view(np.uint32)), "not deterministic"
     assert np.all(np.isfinite(an))
     qn, dn, sn = q.cpu().numpy(), d.cpu().numpy(), s.cpu().numpy()
     if nt * od <= 300 * 1000:
-        ref, mag = oracle.matmul_q8(Q4, W, qn, dn, sn, od)
-        assert_close(an, ref, mag, Q4, idim, "stream-K vs oracle")
+        ref, mag = oracle.matmul_q8(qtype, W, qn, dn, sn, od)
+        assert_close(an, ref, mag, qtype, idim, "stream-K vs oracle")
     else:
         rng = np.random.default_rng(od + nt)
         ts = np.unique(np.concatenate([rng.choice(nt, 24, replace=False), [0, nt - 1]]))
         rs = np.unique(np.concatenate([rng.choice(od, 160, replace=False), [0, od - 1]]))
         tt, rr = np.meshgrid(ts, rs, indexing="ij")
         tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
-        ref, mag = oracle.matmul_q8_points(Q4, W, qn, dn, sn, od, tt, rr)
-        assert_close(an[tt, rr], ref, mag, Q4, idim, "stream-K vs oracle (sampled)")
+        ref, mag = oracle.matmul_q8_points(qtype, W, qn, dn, sn, od, tt, rr)
+        assert_close(an[tt, rr], ref, mag, qtype, idim, "stream-K vs oracle (sampled)")
 
 
-PATH_CASES = [(20, 96, 8192), (9, 40, 65536), (300, 1000, 2304), (384, 4096, 12288), (512, 4096, 12288),
-              (384, 12288, 4096), (512, 12288, 4096), (128, 12288, 4096)]
+PATH_CASES = [(Q4, 20, 96, 8192), (Q4, 9, 40, 65536), (Q4, 300, 1000, 2304), (Q4, 384, 4096, 12288),
+              (Q4, 512, 4096, 12288), (Q4, 384, 12288, 4096), (Q4, 512, 12288, 4096), (Q4, 128, 12288, 4096),
+              (Q6, 64, 4096, 4096), (Q6, 192, 4096, 4096), (Q6, 20, 96, 8192), (P6, 192, 12288, 4096),
+              (P6, 128, 12288, 4096)]
 
 
-@pytest.mark.parametrize("nt,od,idim", PATH_CASES, ids=[f"{a}x{b}x{c}" for a, b, c in PATH_CASES])
-def test_qmm_matmul_takes_streamk_where_preferred(nt, od, idim):
+@pytest.mark.parametrize("qtype,nt,od,idim", PATH_CASES, ids=[f"t{q}-{a}x{b}x{c}" for q, a, b, c in PATH_CASES])
+def test_qmm_matmul_takes_streamk_where_preferred(qtype, nt, od, idim):
     """qmm_matmul with a workspace of qmm_matmul_ws_bytes runs the stream-K kernel
     exactly where qmm_streamk_preferred says so (same bits as the stream-K entry
     point on the same quantized input), the per-tile kernel elsewhere and with a
     workspace of only the q8 plane (same bits as qmm_matmul_q8); outputs within the
     tolerance of the oracle."""
-    pref = qmm.qmm_streamk_preferred(Q4, nt, od, idim)
-    print(f"qmm_matmul path nt={nt} od={od} id={idim} stream-K preferred={pref}", flush=True)
-    mmq = qmm.qmm_dispatch_kind(Q4, nt, od, idim) == qmm.QMM_KIND_MMQ
+    pref = qmm.qmm_streamk_preferred(qtype, nt, od, idim)
+    print(f"qmm_matmul path type={qtype} nt={nt} od={od} id={idim} stream-K preferred={pref}", flush=True)
+    mmq = qmm.qmm_dispatch_kind(qtype, nt, od, idim) == qmm.QMM_KIND_MMQ
     tiles = -(-nt // 64) * -(-od // 128)
-    assert pref == (mmq and tiles % 256 != 0 and (idim // 256 >= 32 or tiles > 256))
-    W = synth.weights(Q4, od, idim, seed=4200 + od)
+    slots = 256 * -(-tiles // 256)
+    rule = (slots - tiles) * 10 >= slots if tiles > 256 else (idim // 256 >= 32 or (qtype != Q4 and tiles <= 64))
+    assert pref == (mmq and tiles % 256 != 0 and rule)
+    W = _weights(qtype, od, idim, seed=4200 + od)
     x = synth.activations(nt, idim, seed=4300 + nt, outlier_frac=0.01)
     Wt, xt = _up(W), _up(x)
-    full = qmm.qmm_matmul(Q4, Wt, xt, od)   # workspace of qmm_matmul_ws_bytes
-    small = qmm.qmm_matmul(Q4, Wt, xt, od,
+    full = qmm.qmm_matmul(qtype, Wt, xt, od)   # workspace of qmm_matmul_ws_bytes
+    small = qmm.qmm_matmul(qtype, Wt, xt, od,
                            workspace=torch.empty(qmm.qmm_act_bytes(nt, idim), dtype=torch.uint8, device=DEV))
     q, d, s = qmm.qmm_quantize_act(xt)
     ws = torch.empty(qmm.qmm_streamk_ws_bytes(), dtype=torch.uint8, device=DEV)
-    sk = qmm.qmm_matmul_q8_streamk(Q4, Wt, q, d, s, od, ws)
-    pt = qmm.qmm_matmul_q8(Q4, Wt, q, d, s, od)
+    sk = qmm.qmm_matmul_q8_streamk(qtype, Wt, q, d, s, od, ws)
+    pt = qmm.qmm_matmul_q8(qtype, Wt, q, d, s, od)
     torch.cuda.synchronize()
     bits = lambda t: t.view(torch.int32)
     assert torch.equal(bits(full), bits(sk if pref else pt))
     assert torch.equal(bits(small), bits(pt))
     qn, dn, sn = q.cpu().numpy(), d.cpu().numpy(), s.cpu().numpy()
     if nt * od <= 300 * 1000:
-        ref, mag = oracle.matmul_q8(Q4, W, qn, dn, sn, od)
-        assert_close(full.cpu().numpy(), ref, mag, Q4, idim, "qmm_matmul vs oracle")
+        ref, mag = oracle.matmul_q8(qtype, W, qn, dn, sn, od)
+        assert_close(full.cpu().numpy(), ref, mag, qtype, idim, "qmm_matmul vs oracle")
     else:
         rng = np.random.default_rng(od + nt + 1)
         ts = np.unique(np.concatenate([rng.choice(nt, 16, replace=False), [0, nt - 1]]))
         rs = np.unique(np.concatenate([rng.choice(od, 128, replace=False), [0, od - 1]]))
         tt, rr = np.meshgrid(ts, rs, indexing="ij")
         tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
-        ref, mag = oracle.matmul_q8_points(Q4, W, qn, dn, sn, od, tt, rr)
-        assert_close(full.cpu().numpy()[tt, rr], ref, mag, Q4, idim, "qmm_matmul vs oracle (sampled)")
+        ref, mag = oracle.matmul_q8_points(qtype, W, qn, dn, sn, od, tt, rr)
+        assert_close(full.cpu().numpy()[tt, rr], ref, mag, qtype, idim, "qmm_matmul vs oracle (sampled)")
