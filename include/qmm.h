@@ -189,8 +189,9 @@ int qmm_dispatch_kind(int type, int nt, int od, int id);
  * call, else 0; a negative status for invalid arguments.  Q4_K and Q6_K (both
  * layouts), MMQ calls only.  With T tiles of 128 x 64: never when T is a multiple
  * of 256; for T > 256 when the last round of 256 workgroups leaves at least 10 %
- * of all workgroup slots idle; for T < 256 when K has at least 32 super-blocks, or
- * for Q6_K when T <= 64.  Measured on Q4_K and Q6_K matrices of 1024..32000 rows
+ * of all workgroup slots idle; for T < 256 when K has at least 32 super-blocks
+ * (except T = 128: the per-tile 64 x 64 split is one full round then), or for Q6_K
+ * when T <= 64.  Measured on Q4_K and Q6_K matrices of 1024..32000 rows
  * and 4096..14336 columns at 17..512 tokens.  qmm_matmul follows it when its
  * workspace is large enough. */
 int qmm_streamk_preferred(int type, int nt, int od, int id);

@@ -134,8 +134,11 @@ int dispatch_kind(int nt, int od)
 //  * T > 256: stream-K when the last round leaves at least 10 % of the R * 256
 //    workgroup slots idle (6-22 % faster there; equal below);
 //  * T < 256: stream-K for a long K (>= 32 super-blocks: the few tiles each walk a
-//    long chain; up to 2x faster for Q4_K, 2.5x for Q6_K), and for Q6_K grids of at
-//    most 64 tiles (1.2-1.4x); otherwise per tile (stream-K up to 25 % slower).
+//    long chain; up to 2x faster for Q4_K, 2.5x for Q6_K), except at T = 128, where
+//    the per-tile dispatch's 64 x 64 split over K is exactly 256 workgroups (one
+//    full round; stream-K equal or up to 5 % slower, also in a whole-model graph);
+//    and for Q6_K grids of at most 64 tiles (1.2-1.4x); otherwise per tile
+//    (stream-K up to 25 % slower).
 bool streamk_preferred(int type, int nt, int od, int id)
 {
     const bool q6 = type == QMM_TYPE_Q6_K || type == QMM_TYPE_Q6_K_P224;
@@ -148,7 +151,7 @@ bool streamk_preferred(int type, int nt, int od, int id)
         const long slots = 256 * ((tiles + 255) / 256);
         return (slots - tiles) * 10 >= slots;
     }
-    return id / 256 >= 32 || (q6 && tiles <= 64);
+    return (id / 256 >= 32 && tiles != 128) || (q6 && tiles <= 64);
 }
 
 int matmul_q8_checked(int kind, int type, const void* W, const int8_t* q, const float* d,

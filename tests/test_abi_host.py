@@ -77,13 +77,15 @@ def test_dispatch_kind_host():
 def test_streamk_preferred_host():
     """Stream-K for Q4_K and Q6_K MMQ calls: never for a whole number of rounds of 256
     tiles (128 x 64); above 256 tiles when the last round leaves >= 10 % of the
-    workgroup slots idle; within one round for K of >= 32 super-blocks, or Q6_K grids
-    of at most 64 tiles.  Never for vector-kernel calls or other types."""
+    workgroup slots idle; within one round for K of >= 32 super-blocks (not at 128
+    tiles), or Q6_K grids of at most 64 tiles.  Never for vector-kernel calls or other
+    types."""
     Q4, Q6, P6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K, qmm.QMM_TYPE_Q6_K_P224
     sp = qmm.qmm_streamk_preferred
     for qt in (Q4, Q6, P6):
         assert sp(qt, 17, 4096, 12288)               # 48 super-blocks, 32 tiles
         assert sp(qt, 448, 4096, 8192)                # 32 super-blocks, 224 tiles
+        assert not sp(qt, 256, 4096, 12288)           # 128 tiles: the per-tile split fills one round
         assert not sp(qt, 512, 4096, 12288)           # 256 tiles: one whole round
         assert not sp(qt, 512, 12288, 4096)           # 768 tiles: three rounds
         assert sp(qt, 192, 12288, 4096)               # 288 tiles: 44 % of 512 slots idle

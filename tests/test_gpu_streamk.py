@@ -84,7 +84,7 @@ def test_streamk(qtype, nt, od, idim):
 PATH_CASES = [(Q4, 20, 96, 8192), (Q4, 9, 40, 65536), (Q4, 300, 1000, 2304), (Q4, 384, 4096, 12288),
               (Q4, 512, 4096, 12288), (Q4, 384, 12288, 4096), (Q4, 512, 12288, 4096), (Q4, 128, 12288, 4096),
               (Q6, 64, 4096, 4096), (Q6, 192, 4096, 4096), (Q6, 20, 96, 8192), (P6, 192, 12288, 4096),
-              (P6, 128, 12288, 4096)]
+              (P6, 128, 12288, 4096), (P6, 256, 4096, 12288), (P6, 128, 4096, 12288)]
 
 
 @pytest.mark.parametrize("qtype,nt,od,idim", PATH_CASES, ids=[f"t{q}-{a}x{b}x{c}" for q, a, b, c in PATH_CASES])
@@ -99,7 +99,8 @@ def test_qmm_matmul_takes_streamk_where_preferred(qtype, nt, od, idim):
     mmq = qmm.qmm_dispatch_kind(qtype, nt, od, idim) == qmm.QMM_KIND_MMQ
     tiles = -(-nt // 64) * -(-od // 128)
     slots = 256 * -(-tiles // 256)
-    rule = (slots - tiles) * 10 >= slots if tiles > 256 else (idim // 256 >= 32 or (qtype != Q4 and tiles <= 64))
+    rule = ((slots - tiles) * 10 >= slots if tiles > 256 else
+            ((idim // 256 >= 32 and tiles != 128) or (qtype != Q4 and tiles <= 64)))
     assert pref == (mmq and tiles % 256 != 0 and rule)
     W = _weights(qtype, od, idim, seed=4200 + od)
     x = synth.activations(nt, idim, seed=4300 + nt, outlier_frac=0.01)
