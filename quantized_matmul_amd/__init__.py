@@ -202,7 +202,8 @@ def qmm_streamk_ws_bytes() -> int:
 
 def qmm_matmul_q8_streamk(qtype: int, W: torch.Tensor, q: torch.Tensor, d: torch.Tensor, s: torch.Tensor, od: int,
                           workspace: torch.Tensor, out=None, stream=None) -> torch.Tensor:
-    """Stream-K matrix kernel (Q4_K): out f32 [nt, od]; workspace uint8 >= qmm_streamk_ws_bytes()."""
+    """Stream-K matrix kernel (Q4_K, Q6_K, Q6_K padded): out f32 [nt, od]; workspace uint8 >=
+    qmm_streamk_ws_bytes(), any content."""
     nt, idim = q.shape
     if out is None:
         out = torch.empty((nt, od), dtype=torch.float32, device=q.device)

@@ -653,42 +653,66 @@ __global__ __launch_bounds__(64 * WR * WC, 2) void mmq_q4k_streamk_kernel(const 
     }
 }
 
-// One workgroup per range boundary g = 1 .. G-1: a boundary inside a tile splits it;
-// the first boundary inside a tile adds the partials of the workgroups covering the
-// tile, in workgroup order, and stores the sum (a tile one workgroup covered whole
-// was stored by that workgroup).
-template <int WR, int WC>
-__global__ __launch_bounds__(64 * WR * WC) void mmq_streamk_fixup_kernel(const float* __restrict__ ws,
-                                                                        float* __restrict__ out, int nt, int od,
-                                                                        int nsb, int G)
+// One single-wave workgroup per (range boundary b = 1 .. G-1, 32 x 32 block of the
+// tile): a boundary inside a tile splits it; the first boundary inside a tile adds,
+// block by block, the partials of the workgroups covering the tile in workgroup
+// order and stores the sum (a tile one workgroup covered whole was stored by that
+// workgroup).  Single waves spread the sums over all CUs; up to four partials per
+// wave are in flight at once.  G is a compile-time constant, so the range
+// boundaries cost a shift, not a 64-bit division.
+template <int WR, int WC, int G>
+__global__ __launch_bounds__(64) void mmq_streamk_fixup_kernel(const float* __restrict__ ws, float* __restrict__ out,
+                                                               int nt, int od, int nsb)
 {
-    constexpr int BM = 32 * WR, BN = 32 * WC, NW = WR * WC;
+    constexpr int BM = 32 * WR, BN = 32 * WC, NW = WR * WC, PF = 4;
     const int ntb = (nt + BN - 1) / BN;
     const int ntiles = ntb * ((od + BM - 1) / BM);
     const long units = (long)ntiles * nsb;
-    const int b = blockIdx.x + 1;
+    const int b = (int)(blockIdx.x / NW) + 1, wave = (int)(blockIdx.x % NW);
     const long ub = sk_first_unit(b, units, G);
     if (b >= G || ub >= units || ub % nsb == 0)
         return;  // not a boundary inside a tile
     const int tile = (int)(ub / nsb);
     const long t0 = (long)tile * nsb, t1 = t0 + nsb;
-    if (sk_first_unit(b - 1, units, G) > t0)
+    long f = sk_first_unit(b - 1, units, G);
+    if (f > t0)
         return;  // an earlier boundary inside this tile does the sum
-    // workgroups b-1, b, ... cover the tile (b-1 holds its first unit)
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int wr = wave / WC, wc = wave % WC, li = lane & 31, lh = lane >> 5;
+    // workgroups b-1, b, ... cover the tile (b-1 holds its first unit); a covering
+    // workgroup keeps the tile in slot 0 when its range starts inside the tile (its
+    // first tile), else in slot 1 (its last)
+    const int lane = threadIdx.x;
     v16f v = {};
-    for (int gg = b - 1; gg < G && sk_first_unit(gg, units, G) < t1; ++gg) {
-        if (sk_first_unit(gg + 1, units, G) <= sk_first_unit(gg, units, G))
-            continue;  // an empty range
-        const int slot = (int)(sk_first_unit(gg, units, G) / nsb) == tile ? 0 : 1;
-        const float* src = ws + ((size_t)(2 * gg + slot) * NW + wave) * 1024;
+    for (int gg = b - 1; gg < G && f < t1; gg += PF) {
+        long fs[PF + 1];
+        fs[0] = f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            v[i] += src[i * 64 + lane];
+        for (int k = 1; k <= PF; ++k)
+            fs[k] = gg + k <= G ? sk_first_unit(gg + k, units, G) : units;
+        float a[PF][16];
+        bool used[PF];
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            // gg + k covers part of the tile with a non-empty range; an unused read
+            // takes workgroup b-1's slot (inside the workspace) and is not added
+            used[k] = gg + k < G && fs[k] < t1 && fs[k + 1] > fs[k];
+            const float* src =
+                ws + ((size_t)(2 * (used[k] ? gg + k : b - 1) + (used[k] && fs[k] < t0 ? 1 : 0)) * NW + wave) * 1024;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                a[k][i] = src[i * 64 + lane];
+        }
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            if (used[k]) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    v[i] += a[k][i];
+            }
+        }
+        f = fs[PF];
     }
-    const int row0 = (tile / ntb) * BM, tok0 = (tile % ntb) * BN;
-    store_tile(v, out, nt, od, tok0 + wc * 32 + li, row0 + wr * 32, lh);
+    const int wr = wave / WC, wc = wave % WC;
+    store_tile(v, out, nt, od, (tile % ntb) * BN + wc * 32 + (lane & 31), (tile / ntb) * BM + wr * 32, lane >> 5);
 }
 
 // ------------------------------------------------------------------ Q6_K
@@ -1378,7 +1402,8 @@ hipError_t launch_mmq_streamk(int type, const uint8_t* W, const int8_t* q, const
     }
     if (!split)
         return hipSuccess;
-    hipLaunchKernelGGL((mmq_streamk_fixup_kernel<4, 2>), dim3(G - 1), dim3(512), 0, st, ws, out, nt, od, (int)nsb, G);
+    hipLaunchKernelGGL((mmq_streamk_fixup_kernel<4, 2, kStreamKGroups>), dim3((G - 1) * 8), dim3(64), 0, st, ws, out, nt,
+                       od, (int)nsb);
     return hipGetLastError();
 }
 

@@ -4,10 +4,11 @@ The library's calls only enqueue kernels on the caller's stream (no allocation, 
 memset, no synchronisation), so a caller can capture a whole step -- quantize, the
 producer-fused quantize, the vector kernel, its 8-token slices and the matrix
 kernel with and without the split over K -- into one HIP graph and replay it.
-Checked here: the graph is replayed several times, with other GPU work and host
-synchronisation between replays and the outputs cleared before each, and every
-output of every replay equals the eagerly computed one (the kernels are
-deterministic: no atomics, fixed reduction orders).
+The stream-K kernel and its fixup (three launches sharing one workspace) are in
+the step too.  Checked here: the graph is replayed several times, with other GPU
+work and host synchronisation between replays and the outputs cleared before
+each, and every output of every replay equals the eagerly computed one (the
+kernels are deterministic: no atomics, fixed reduction orders).
 """
 from __future__ import annotations
 
@@ -52,6 +53,13 @@ class Step:
         self.fs = torch.empty_like(self.fd)
         self.fW = _up(synth.weights(qmm.QMM_TYPE_Q4_K, 4096, 4096, seed=82))
         self.fout = torch.empty(16, 4096, dtype=torch.float32, device=DEV)
+        # stream-K launches (tiles split over up to 8 workgroups; a padded Q6_K one)
+        # sharing one workspace, on the first and the third item's quantized input
+        self.ws = torch.full((qmm.qmm_streamk_ws_bytes(),), 0xFF, dtype=torch.uint8, device=DEV)
+        self.skW6 = qmm.qmm_pad_q6k(_up(synth.weights(qmm.QMM_TYPE_Q6_K, 1000, 4096, seed=83)))
+        self.skout = [torch.empty(4, 4096, dtype=torch.float32, device=DEV),
+                      torch.empty(64, 4096, dtype=torch.float32, device=DEV),
+                      torch.empty(64, 1000, dtype=torch.float32, device=DEV)]
 
     def issue(self):
         for qt, od, W, x, q, d, s, out in self.items:
@@ -59,24 +67,30 @@ class Step:
             qmm.qmm_matmul_q8(qt, W, q, d, s, od, out=out)
         qmm.qmm_rmsnorm_quantize(self.h, self.w, 1e-5, self.fq, self.fd, self.fs)
         qmm.qmm_matmul_q8(qmm.QMM_TYPE_Q4_K, self.fW, self.fq, self.fd, self.fs, 4096, out=self.fout)
+        for (qt, W, q, d, s), out in zip((self.items[0][:1] + self.items[0][2:3] + self.items[0][4:7],
+                                          self.items[2][:1] + self.items[2][2:3] + self.items[2][4:7],
+                                          (qmm.QMM_TYPE_Q6_K_P224, self.skW6) + self.items[2][4:7]),
+                                         self.skout):
+            qmm.qmm_matmul_q8_streamk(qt, W, q, d, s, out.shape[1], self.ws, out=out)
 
     def outputs(self):
         res = []
         for item in self.items:
             res += [t.clone() for t in item[4:]]
-        return res + [self.fq.clone(), self.fd.clone(), self.fs.clone(), self.fout.clone()]
+        return res + [self.fq.clone(), self.fd.clone(), self.fs.clone(), self.fout.clone()] + \
+            [t.clone() for t in self.skout]
 
     def clear(self):
         # eager fill kernels (not recorded in the graph)
         for item in self.items:
             for t in item[4:]:
                 t.zero_()
-        for t in (self.fq, self.fd, self.fs, self.fout):
+        for t in (self.fq, self.fd, self.fs, self.fout, *self.skout):
             t.zero_()
 
 
 def test_graph_replays_match_eager():
-    print("graph replay: capture a step of 5 quantize and 5 matmul calls", flush=True)
+    print("graph replay: capture a step of 5 quantize, 5 matmul and 3 stream-K calls", flush=True)
     assert qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q6_K, 12, 4096, 4096) == qmm.QMM_KIND_MMVQ
     assert qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q4_K, 64, 4096, 4096) == qmm.QMM_KIND_MMQ
     step = Step()

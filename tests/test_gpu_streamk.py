@@ -9,7 +9,10 @@ pages warn that split reductions must not make results depend on timing).
   with fewer units than workgroups, tiles split over several workgroups, ranges
   spanning several tiles, ragged edges, and the benchmark's shapes;
 * determinism: repeated launches are bit-identical;
-* the workspace is filled with NaN bytes first: every partial read was written.
+* the workspace is filled with NaN bytes before each launch: every partial read
+  was written in that launch;
+* a launch after one of another shape on the same workspace gives the same bits as
+  one on a fresh workspace.
 """
 from __future__ import annotations
 
@@ -62,6 +65,7 @@ def test_streamk(qtype, nt, od, idim):
     q, d, s = qmm.qmm_quantize_act(_up(x))
     ws = torch.full((qmm.qmm_streamk_ws_bytes(),), 0xFF, dtype=torch.uint8, device=DEV)
     a = qmm.qmm_matmul_q8_streamk(qtype, Wt, q, d, s, od, ws)
+    ws.fill_(0xFF)  # a partial read before it is written in this launch shows as NaN
     b = qmm.qmm_matmul_q8_streamk(qtype, Wt, q, d, s, od, ws)
     torch.cuda.synchronize()
     an = a.cpu().numpy()
@@ -128,3 +132,22 @@ def test_qmm_matmul_takes_streamk_where_preferred(qtype, nt, od, idim):
         tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
         ref, mag = oracle.matmul_q8_points(qtype, W, qn, dn, sn, od, tt, rr)
         assert_close(full.cpu().numpy()[tt, rr], ref, mag, qtype, idim, "qmm_matmul vs oracle (sampled)")
+
+
+def test_streamk_workspace_reuse_across_shapes():
+    """Partials left by launches of other shapes (and other types) on the same
+    workspace change nothing: each launch equals, bit for bit, a launch on a
+    workspace of NaN bytes."""
+    print("stream-K workspace reuse across shapes", flush=True)
+    shapes = [(Q4, 64, 4096, 4096), (Q6, 130, 96, 4096), (Q4, 256, 12288, 4096), (P6, 17, 4096, 12288),
+              (Q4, 64, 4096, 4096)]
+    ws = torch.full((qmm.qmm_streamk_ws_bytes(),), 0xFF, dtype=torch.uint8, device=DEV)
+    for i, (qtype, nt, od, idim) in enumerate(shapes):
+        Wt = _up(_weights(qtype, od, idim, seed=4400 + i))
+        q, d, s = qmm.qmm_quantize_act(_up(synth.activations(nt, idim, seed=4500 + i)))
+        shared = qmm.qmm_matmul_q8_streamk(qtype, Wt, q, d, s, od, ws)
+        fresh = qmm.qmm_matmul_q8_streamk(qtype, Wt, q, d, s, od,
+                                          torch.full_like(ws, 0xFF))
+        torch.cuda.synchronize()
+        assert torch.equal(shared.view(torch.int32), fresh.view(torch.int32)), (qtype, nt, od, idim)
+        assert bool(torch.isfinite(shared).all())
