@@ -45,7 +45,10 @@ per32_same_shapes gives the per-32 kernel's rate from the same process.
 Workload "dllm_step": the 224 matmuls of one diffusion-LM step at L = 256 (32 layers x
 q, k, v, o, gate, up Q4_K and down Q6_K in the padded layout; distinct weights per
 layer).  value = int8 ops over the summed kernel times; graph = the whole step
-(quantize + matmul per call) captured into one HIP graph and replayed.
+(quantize + matmul per call) captured into one HIP graph and replayed;
+graph_layers = the same matmuls fed as a model's layers feed them (fused RMS-norm,
+residual-add and silu * up producers; one quantized input shared by q, k, v and one
+by gate, up: 4 producer launches per layer), also one graph.
 
 Workload "formats": Q4_0, Q8_0 and Q5_K (and Q4_K for comparison) at 12288 x 4096, nt = 1
 and nt = 512.  value = HBM GB/s of the Q4_0 vector kernel at nt = 1.
@@ -218,6 +221,78 @@ def graph_replay_ms(torch, calls, replays=5):
     side.wait_stream(torch.cuda.current_stream())
     issue()  # warm-up on the capture stream
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side, capture_error_mode="relaxed"):
+        issue()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        g.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(side)
+        for _ in range(replays):
+            g.replay()
+        e1.record(side)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / replays
+
+
+def layer_graph_ms(torch, qmm, calls, replays=5):
+    """The step's 224 matmuls with the data flow of a model's layers, captured as one
+    HIP graph like graph_replay_ms.  Per layer: q, k and v read one fused RMS-norm
+    quantize of the residual stream; o reads the quantized v output (standing in
+    for the attention output); gate and up read one fused residual-add + RMS-norm
+    quantize; down reads the fused silu(gate) * up quantize of their outputs; the
+    next layer's first producer adds the down output into the residual stream.  So
+    4 producer launches and 7 matmuls per layer (the plain step: 7 quantize
+    launches, one per matmul), the same matmul kernels and weights."""
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L = qmm.lib()
+    dev = torch.device("cuda:0")
+    nt, hid, ffn = calls[0].nt, 4096, 12288
+    h = torch.from_numpy(synth.activations(nt, hid, seed=300)).to(dev)
+    w_attn = torch.from_numpy(1.0 + 0.25 * synth.activations(1, hid, seed=301)[0]).to(dev)
+    w_ffn = torch.from_numpy(1.0 + 0.25 * synth.activations(1, hid, seed=302)[0]).to(dev)
+
+    def q8(n):
+        return (torch.empty((nt, n), dtype=torch.int8, device=dev), torch.empty((nt, n // 32), device=dev),
+                torch.empty((nt, n // 32), device=dev))
+
+    qa, qo, qf, qd = q8(hid), q8(hid), q8(hid), q8(ffn)
+    ptr = lambda t: P(t.data_ptr())  # noqa: E731
+    side = torch.cuda.Stream()
+    sp = P(side.cuda_stream)
+    eps = F(1e-5)
+
+    def mm(c, src):
+        a = c.margs[0]
+        return c.mfn(*(a[:2] + (ptr(src[0]), ptr(src[1]), ptr(src[2])) + a[5:-1] + (sp,)))
+
+    def issue():
+        rc = []
+        for layer in range(len(calls) // 7):
+            cq, ck, cv, co, cg, cu, cd = calls[7 * layer:7 * layer + 7]
+            if layer == 0:
+                rc.append(L.qmm_rmsnorm_quantize(ptr(h), ptr(w_attn), eps, I(nt), I(hid), *map(ptr, qa), sp))
+            else:
+                prev = calls[7 * layer - 1].out
+                rc.append(L.qmm_add_rmsnorm_quantize(ptr(h), ptr(prev), ptr(w_attn), eps, I(nt), I(hid),
+                                                     *map(ptr, qa), sp))
+            rc += [mm(cq, qa), mm(ck, qa), mm(cv, qa)]
+            rc.append(L.qmm_quantize_act(ptr(cv.out), I(nt), I(hid), *map(ptr, qo), sp))
+            rc.append(mm(co, qo))
+            rc.append(L.qmm_add_rmsnorm_quantize(ptr(h), ptr(co.out), ptr(w_ffn), eps, I(nt), I(hid),
+                                                 *map(ptr, qf), sp))
+            rc += [mm(cg, qf), mm(cu, qf)]
+            rc.append(L.qmm_silu_mul_quantize(ptr(cg.out), ptr(cu.out), I(nt), I(ffn), *map(ptr, qd), sp))
+            rc.append(mm(cd, qd))
+        if any(rc):
+            raise RuntimeError(f"layer data flow: a launch failed ({[r for r in rc if r]})")
+
+    side.wait_stream(torch.cuda.current_stream())
+    issue()  # warm-up on the capture stream
+    torch.cuda.synchronize()
+    if not bool(torch.isfinite(h).all()):
+        raise RuntimeError("layer data flow: the residual stream is not finite")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side, capture_error_mode="relaxed"):
         issue()
@@ -744,6 +819,11 @@ def main():
         gms = graph_replay_ms(torch, calls)
         line["graph"] = {"ms_per_step": round(gms, 4), "replays": 5,
                          "TOP_s_incl_quantize": round(ops / (gms * 1e-3) / 1e12, 2)}
+        # the same matmuls fed as a model's layers feed them (fused producers, one
+        # quantized input for q, k, v and one for gate, up)
+        lms = layer_graph_ms(torch, qmm, calls)
+        line["graph_layers"] = {"ms_per_step": round(lms, 4), "replays": 5, "producer_launches_per_layer": 4,
+                                "TOP_s_incl_producers": round(ops / (lms * 1e-3) / 1e12, 2)}
         line["config"] = {"workload": "dllm_step", "layers": 32, "canvas": 256, "hidden": 4096, "ffn": 12288,
                           "matmuls_per_step": len(calls), "down_projection": "Q6_K padded to 224-byte blocks"}
         detail = detail[:7]
