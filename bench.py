@@ -39,8 +39,10 @@ bytes over their summed launch times); roofline on silu_mul_quantize 512 x 12288
 
 Workload "q8k_prefill": the two prefill shapes above on Q8_K activations (one scale
 per 256 values, 16-value code sums; its own numerics) and, on the same weights and
-inputs, on the per-32 activations.  value = int8 TOP/s of the Q8_K matmul kernel;
-per32_same_shapes gives the per-32 kernel's rate from the same process.
+inputs, on the per-32 activations.  value = int8 TOP/s of the Q4_K Q8_K matmul
+kernel; per32_same_shapes gives the per-32 kernel's rate from the same process;
+q6k_padded_4096x12288 the same comparison for the down projection's shape in the
+padded Q6_K layout.
 
 Workload "dllm_step": the 224 matmuls of one diffusion-LM step at L = 256 (32 layers x
 q, k, v, o, gate, up Q4_K and down Q6_K in the padded layout; distinct weights per
@@ -341,6 +343,15 @@ def build_calls(torch, qmm, workload):
             calls.append(per32)
             calls.append(Call(torch, qmm, Q4, od, idim, 512, seed=seed, outliers=True, copies=per32.W, x=per32.x,
                               q8k=True))
+        # and the down projection's shape in the padded Q6_K layout
+        P6 = qmm.QMM_TYPE_Q6_K_P224
+        w = qmm.qmm_pad_q6k(torch.from_numpy(synth.weights(Q6, 4096, 12288, seed=9)).to("cuda:0"))
+        copies = [w] + [w.clone() for _ in range(max(1, -(-COPY_BYTES // w.numel())) - 1)]
+        per32 = Call(torch, qmm, P6, 4096, 12288, 512, seed=9, outliers=True, copies=copies,
+                     label="Q6_K padded 4096x12288 nt=512")
+        calls.append(per32)
+        calls.append(Call(torch, qmm, P6, 4096, 12288, 512, seed=9, outliers=True, copies=copies, x=per32.x,
+                          q8k=True, label="Q6_K padded 4096x12288 nt=512 Q8_K"))
     elif workload == "streamk":
         # the Q4_K matrix shapes of the diffusion-LM step (L = 256) and of prefill
         # (nt = 512), per-tile dispatch and stream-K on the same weights and inputs
@@ -744,8 +755,9 @@ def main():
                           "mmq": "Q4_K 12288x4096 and 4096x12288, nt=512, 1% outliers x20",
                           "weight_copies_bytes_per_shape": COPY_BYTES}
     elif args.workload == "q8k_prefill":
-        q8 = [c for c in calls if c.q8k]
-        p32 = [c for c in calls if not c.q8k]
+        q8 = [c for c in calls if c.q8k and c.qtype == qmm.QMM_TYPE_Q4_K]
+        p32 = [c for c in calls if not c.q8k and c.qtype == qmm.QMM_TYPE_Q4_K]
+        k6 = {c.q8k: float(np.mean(c.k_ms)) * 1e3 for c in calls if c.qtype != qmm.QMM_TYPE_Q4_K}
         ops = sum(c.ops for c in q8)
         t8 = sum(float(np.mean(c.k_ms)) * 1e-3 for c in q8)
         t32 = sum(float(np.mean(c.k_ms)) * 1e-3 for c in p32)
@@ -763,6 +775,10 @@ def main():
                             "ops_per_launch": int(m.ops)}
         line["per32_same_shapes"] = {"value": round(sum(c.ops for c in p32) / t32 / 1e12, 2), "unit": "TOP/s",
                                      "speedup_q8k": round(t32 / t8, 3)}
+        ops6 = 2.0 * 512 * 4096 * 12288
+        line["q6k_padded_4096x12288"] = {"per32_us": round(k6[False], 2), "q8k_us": round(k6[True], 2),
+                                         "q8k_TOP_s": round(ops6 / k6[True] / 1e6, 2),
+                                         "speedup_q8k": round(k6[False] / k6[True], 3)}
         line["config"] = {"workload": "q8k_prefill", "shapes": "Q4_K 12288x4096 and 4096x12288, nt=512, "
                           "1% outliers x20", "activations": "Q8_K (one scale per 256) vs per-32"}
     elif args.workload == "streamk":

@@ -739,7 +739,10 @@ __device__ __forceinline__ void q6_prefetch(uint32_t (&pl)[WC8][5], uint32_t (&p
                                             const float* __restrict__ dx, int sb, int tid, int row0, int tok0, int nt,
                                             int od, int id, int nblk, size_t row_bytes)
 {
-    // unconditional loads, as for Q4_K: clamped task, row and token indices
+    // unconditional loads, as for Q4_K: clamped task, row and token indices.  The
+    // weight part is q6_prefetch_task (and q6_stage's code part q6_stage_codes)
+    // written out: calling the shared helpers here moves these kernels' register
+    // allocation into spills at 256 VGPRs.
 #pragma unroll
     for (int k = 0; k < WC8; ++k) {
         const int e = task<BM * 8, NTH, WC8>(tid + k * NTH);

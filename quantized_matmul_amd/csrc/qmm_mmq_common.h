@@ -44,6 +44,71 @@ __device__ __forceinline__ v16f mfma_k2(float a, float b, v16f acc)
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
 }
 
+// Q6_K staging task e = (row r = e / 8, piece c = e % 8) of super-block sb: the
+// 16-byte chunks of low fields and high 2-bit fields piece c covers (h = c / 4,
+// jq = c / 2 % 2, half = c % 2: low bytes 64h + 32jq + 16half, high bytes
+// 128 + 32h + 16half of the block), its two group scales 2c, 2c+1 and d.  The
+// unpadded 210-byte block is only 2-byte aligned: each chunk is read as the five
+// dwords around it plus a byte shift; the padded 224-byte block (PAD) has both
+// chunks 16-byte aligned.  psd: low half the two int8 scales, high half the f16 d.
+template <bool PAD>
+__device__ __forceinline__ void q6_prefetch_task(uint32_t (&pl)[5], uint32_t (&phh)[5], uint32_t& pshift,
+                                                 uint32_t& psd, const uint8_t* __restrict__ W, int e, int sb,
+                                                 int row0, int od, size_t row_bytes)
+{
+    const int r = e >> 3, c = e & 7;
+    const int h = c >> 2, jq = (c >> 1) & 1, half = c & 1;
+    const uint8_t* blk = W + (size_t)min(row0 + r, od - 1) * row_bytes + (size_t)sb * (PAD ? kQ6KP224Bytes : kQ6KBytes);
+    const uintptr_t al = reinterpret_cast<uintptr_t>(blk + 64 * h + 32 * jq + 16 * half);
+    const uintptr_t ah = reinterpret_cast<uintptr_t>(blk + 128 + 32 * h + 16 * half);
+    if constexpr (PAD) {
+        const uint4 l4 = *reinterpret_cast<const uint4*>(al), h4 = *reinterpret_cast<const uint4*>(ah);
+        pl[0] = l4.x, pl[1] = l4.y, pl[2] = l4.z, pl[3] = l4.w, pl[4] = 0;
+        phh[0] = h4.x, phh[1] = h4.y, phh[2] = h4.z, phh[3] = h4.w, phh[4] = 0;
+        pshift = 0;
+    } else {
+        const uint32_t* wl = reinterpret_cast<const uint32_t*>(al & ~(uintptr_t)3);
+        const uint32_t* wh = reinterpret_cast<const uint32_t*>(ah & ~(uintptr_t)3);
+        pshift = (uint32_t)(al & 3);  // same for both chunks
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            pl[i] = wl[i];
+            phh[i] = wh[i];
+        }
+    }
+    const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(blk + 192 + 2 * c);
+    const uint32_t d16 = *reinterpret_cast<const uint16_t*>(blk + 208);
+    psd = sc2 | (d16 << 16);
+}
+
+// The 32 centred codes (q6 - 32, int8) of piece c, from its prefetched chunks, into
+// the staged row wrow: elements 128h + 32jq + 16half .. + 15 (low nibbles with high
+// bits 2jq) and the same + 64 (high nibbles with high bits 2jq + 4).
+__device__ __forceinline__ void q6_stage_codes(int8_t* wrow, const uint32_t (&pl)[5], const uint32_t (&phh)[5],
+                                               uint32_t sh, int c)
+{
+    const int h = c >> 2, jq = (c >> 1) & 1, half = c & 1;
+    uint32_t L[4], H[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        L[i] = __builtin_amdgcn_alignbyte(pl[i + 1], pl[i], sh);
+        H[i] = __builtin_amdgcn_alignbyte(phh[i + 1], phh[i], sh);
+    }
+    const int hs1 = 2 * jq, hs2 = 2 * jq + 4;
+    int4 ca, cb;
+    ca.x = q6_center4(L[0] & 0x0F0F0F0Fu, (H[0] >> hs1) & 0x03030303u);
+    ca.y = q6_center4(L[1] & 0x0F0F0F0Fu, (H[1] >> hs1) & 0x03030303u);
+    ca.z = q6_center4(L[2] & 0x0F0F0F0Fu, (H[2] >> hs1) & 0x03030303u);
+    ca.w = q6_center4(L[3] & 0x0F0F0F0Fu, (H[3] >> hs1) & 0x03030303u);
+    cb.x = q6_center4((L[0] >> 4) & 0x0F0F0F0Fu, (H[0] >> hs2) & 0x03030303u);
+    cb.y = q6_center4((L[1] >> 4) & 0x0F0F0F0Fu, (H[1] >> hs2) & 0x03030303u);
+    cb.z = q6_center4((L[2] >> 4) & 0x0F0F0F0Fu, (H[2] >> hs2) & 0x03030303u);
+    cb.w = q6_center4((L[3] >> 4) & 0x0F0F0F0Fu, (H[3] >> hs2) & 0x03030303u);
+    const int e1 = 128 * h + 32 * jq + 16 * half;
+    *reinterpret_cast<int4*>(wrow + e1) = ca;
+    *reinterpret_cast<int4*>(wrow + e1 + 64) = cb;
+}
+
 // Tile index of this workgroup: consecutive tiles (same row block, successive
 // token blocks) go to the same XCD.  Returns -1 for a padding workgroup.
 __device__ __forceinline__ int xcd_tile(int ntiles)

@@ -321,6 +321,181 @@ __global__ __launch_bounds__(64 * WR * WC) void mmq_q4k_q8k_kernel(const uint8_t
         store_tile_rowmajor(acc, out, nt, od, tok0 + wc * 32, row0 + brow, lh);
 }
 
+// ------------------------------------------------------------------ Q6_K on Q8_K
+// [GEMM, "Activations: int8 with a scale per 256"] with Q6_K weights: the sixteen
+// 16-weight groups of a super-block share one activation scale, so its contribution
+// to out[t][r] is d[r] * dx[t] * S, S = sum_g sc_g[r] * sum((q6 - 32) * qx) an exact
+// integer (|sum((q6 - 32) * qx)| <= 16 * 32 * 127, |sc_g| <= 128, |S| < 2^28).  No
+// min term (the codes are centred).  Same swapped MFMA roles as the Q4_K kernel
+// (A = activation codes, B = weight codes, a result lane holds one weight row and
+// 16 tokens), so sc_g is one register per lane and the combine is one
+// v_mad_i32_i24 per value and group on v_mfma_i32_32x32x16_i8 results (the per-32
+// path: a conversion and an FMA per value and group).  Codes are centred at
+// staging as in the per-32 Q6_K kernel; PAD reads the 224-byte layout.
+template <int BM, int BN>
+struct __attribute__((aligned(16))) Q6Q8KSmem {
+    static constexpr int W_STRIDE = 272;    // 256 centred codes + 16 pad
+    static constexpr int X_STRIDE = 272;    // 256 activation codes + 16 pad
+    int8_t wq[BM * W_STRIDE];
+    int32_t sc[BM * 16];                    // [row][g]
+    float dd[BM];                           // [row] d
+    uint8_t xq[BN * X_STRIDE];
+    float dx[BN];                           // [token] activation scale
+};
+
+// Groups 2m and 2m + 1 of the staged super-block: the two int8 products,
+// token-major (A = activation codes of token atok, B = weight codes of row brow).
+template <int BM, int BN>
+__device__ __forceinline__ void q6q8k_step(const Q6Q8KSmem<BM, BN>& sm, int m, int atok, int brow, int lh, v16i& C0,
+                                           v16i& C1)
+{
+    using SM = Q6Q8KSmem<BM, BN>;
+    const long x0 = *reinterpret_cast<const long*>(&sm.xq[atok * SM::X_STRIDE + 32 * m + 8 * lh]);
+    const long x1 = *reinterpret_cast<const long*>(&sm.xq[atok * SM::X_STRIDE + 32 * m + 16 + 8 * lh]);
+    const long w0 = *reinterpret_cast<const long*>(&sm.wq[brow * SM::W_STRIDE + 32 * m + 8 * lh]);
+    const long w1 = *reinterpret_cast<const long*>(&sm.wq[brow * SM::W_STRIDE + 32 * m + 16 + 8 * lh]);
+    C0 = mfma_i8_k16(x0, w0);
+    C1 = mfma_i8_k16(x1, w1);
+}
+
+template <int WR, int WC, bool DUMP, bool PAD>
+__global__ __launch_bounds__(64 * WR * WC) void mmq_q6k_q8k_kernel(const uint8_t* __restrict__ W,
+                                                                   const int8_t* __restrict__ q,
+                                                                   const float* __restrict__ dx,
+                                                                   float* __restrict__ out, int nt, int od, int id,
+                                                                   int32_t* __restrict__ S)
+{
+    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;
+    constexpr int WC8 = (BM * 8 + NTH - 1) / NTH;  // (row, 32-code piece) tasks per thread
+    constexpr int XC = (BN * 16 + NTH - 1) / NTH;
+    constexpr int DC = (BN + NTH - 1) / NTH;
+    using SM = Q6Q8KSmem<BM, BN>;
+    __shared__ SM smb[2];
+
+    const int ntb = (nt + BN - 1) / BN;
+    const int tile = xcd_tile(ntb * ((od + BM - 1) / BM));
+    if (tile < 0)
+        return;  // whole workgroup
+    const int row0 = (tile / ntb) * BM, tok0 = (tile % ntb) * BN;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wr = wave / WC, wc = wave % WC;
+    const int li = lane & 31, lh = lane >> 5;
+    const int nsb = id >> 8;
+    const size_t row_bytes = (size_t)nsb * (PAD ? kQ6KP224Bytes : kQ6KBytes);
+
+    uint32_t pl[WC8][5], phh[WC8][5], pshift[WC8], psd[WC8];
+    v4i px[XC];
+    uint32_t pdx[DC];
+    // unconditional loads with clamped task, row and token indices
+    const auto prefetch = [&](int sb) {
+#pragma unroll
+        for (int k = 0; k < WC8; ++k)
+            q6_prefetch_task<PAD>(pl[k], phh[k], pshift[k], psd[k], W, task<BM * 8, NTH, WC8>(tid + k * NTH), sb,
+                                  row0, od, row_bytes);
+#pragma unroll
+        for (int k = 0; k < XC; ++k) {
+            const int e = task<BN * 16, NTH, XC>(tid + k * NTH);
+            const int t = min(tok0 + (e >> 4), nt - 1);
+            px[k] = *reinterpret_cast<const v4i*>(q + (size_t)t * id + 256 * sb + 16 * (e & 15));
+        }
+#pragma unroll
+        for (int k = 0; k < DC; ++k) {
+            const int t = min(tok0 + task<BN, NTH, DC>(tid + k * NTH), nt - 1);
+            pdx[k] = __float_as_uint(dx[(size_t)t * nsb + sb]);
+        }
+    };
+    // valid == false (a super-block past the end) stages d = 0: it adds nothing
+    const auto stage = [&](SM& sm, bool valid) {
+#pragma unroll
+        for (int k = 0; k < WC8; ++k) {
+            const int e = task<BM * 8, NTH, WC8>(tid + k * NTH);
+            const int r = e >> 3, c = e & 7;
+            q6_stage_codes(&sm.wq[r * SM::W_STRIDE], pl[k], phh[k], pshift[k], c);
+            sm.sc[r * 16 + 2 * c] = (int)(int8_t)(psd[k] & 0xFF);
+            sm.sc[r * 16 + 2 * c + 1] = (int)(int8_t)((psd[k] >> 8) & 0xFF);
+            sm.dd[r] = valid ? f16_bits_to_f32(psd[k] >> 16) : 0.f;  // every task of a row writes the same d
+        }
+#pragma unroll
+        for (int k = 0; k < XC; ++k) {
+            const int e = task<BN * 16, NTH, XC>(tid + k * NTH);
+            *reinterpret_cast<v4i*>(&sm.xq[(e >> 4) * SM::X_STRIDE + 16 * (e & 15)]) = px[k];
+        }
+#pragma unroll
+        for (int k = 0; k < DC; ++k)
+            sm.dx[task<BN, NTH, DC>(tid + k * NTH)] = __uint_as_float(pdx[k]);
+    };
+
+    v16f acc = {};
+    const int atok = wc * 32 + li;   // this lane's token as an A operand
+    const int brow = wr * 32 + li;   // this lane's weight row as a B operand
+
+    prefetch(0);
+    stage(smb[0], true);
+    prefetch(min(1, nsb - 1));
+    __syncthreads();
+    for (int sb = 0; sb < nsb; ++sb) {
+        const SM& sm = smb[sb & 1];
+        // the scale product d[r] * dx[t] in the result layout (one outer product on
+        // the k = 0 lanes), and this row's sixteen group scales
+        const float oa = lh == 0 ? sm.dx[atok] : 0.f, ob = lh == 0 ? sm.dd[brow] : 0.f;
+        const v16f pp = mfma_k2(oa, ob, v16f{});
+        const v4i s0 = *reinterpret_cast<const v4i*>(&sm.sc[brow * 16]);
+        const v4i s1 = *reinterpret_cast<const v4i*>(&sm.sc[brow * 16 + 4]);
+        const v4i s2 = *reinterpret_cast<const v4i*>(&sm.sc[brow * 16 + 8]);
+        const v4i s3 = *reinterpret_cast<const v4i*>(&sm.sc[brow * 16 + 12]);
+        const int scv[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
+                             s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+
+        // step m: groups 2m, 2m + 1; the MFMAs of step m + 1 are issued before the
+        // combine of step m
+        v16i acci = {}, acco = {};
+        v16i Ca0, Ca1;
+        q6q8k_step<BM, BN>(sm, 0, atok, brow, lh, Ca0, Ca1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            v16i Cb0, Cb1;
+            if (m < 7)
+                q6q8k_step<BM, BN>(sm, m + 1, atok, brow, lh, Cb0, Cb1);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                // even and odd groups in separate sums, one v_mad_i32_i24 each
+                acci[i] = __mul24(Ca0[i], scv[2 * m]) + acci[i];
+                acco[i] = __mul24(Ca1[i], scv[2 * m + 1]) + acco[i];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < 7) {
+                Ca0 = Cb0;
+                Ca1 = Cb1;
+            }
+        }
+        acci += acco;
+        if constexpr (DUMP) {
+            const int r = row0 + brow;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int t = tok0 + wc * 32 + 8 * (i >> 2) + 4 * lh + (i & 3);
+                if (t < nt && r < od) {
+                    int32_t* dst = S + (((size_t)t * od + r) * nsb + sb) * 2;
+                    dst[0] = acci[i];
+                    dst[1] = 0;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                acc[i] = fmaf(pp[i], (float)acci[i], acc[i]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        stage(smb[(sb + 1) & 1], sb + 1 < nsb);
+        prefetch(min(sb + 2, nsb - 1));
+        __syncthreads();
+    }
+    if constexpr (!DUMP)
+        store_tile_rowmajor(acc, out, nt, od, tok0 + wc * 32, row0 + brow, lh);
+}
+
 // The shape with the fewer (rounds of workgroups over the 256 CUs) x super-blocks:
 // 128 x 64 (8 waves) or 64 x 64 (4 waves); ties go to the larger tile.
 int q8k_tile_choice(int nt, int od)
@@ -330,26 +505,33 @@ int q8k_tile_choice(int nt, int od)
     return (t42 + 255) / 256 <= (t22 + 511) / 512 ? 1 : 2;
 }
 
+// type 1: Q4_K, 2: Q6_K, 3: Q6_K padded (checked by the caller)
 template <int WR, int WC, bool DUMP>
-static hipError_t launch_q8k_tile(const uint8_t* W, const int8_t* q, const float* d, const float* bsum, int nt,
-                                  int od, int id, float* out, int32_t* S, hipStream_t st)
+static hipError_t launch_q8k_tile(int type, const uint8_t* W, const int8_t* q, const float* d, const float* bsum,
+                                  int nt, int od, int id, float* out, int32_t* S, hipStream_t st)
 {
     const long tiles = (long)((nt + 32 * WC - 1) / (32 * WC)) * ((od + 32 * WR - 1) / (32 * WR));
     const long grid = (tiles + 7) / 8 * 8;  // a multiple of the 8 XCDs (xcd_tile drops the padding)
-    hipLaunchKernelGGL((mmq_q4k_q8k_kernel<WR, WC, DUMP>), dim3((unsigned)grid), dim3(64 * WR * WC), 0, st, W, q,
-                       d, bsum, out, nt, od, id, S);
+    const dim3 g((unsigned)grid), b(64 * WR * WC);
+    if (type == 1)
+        hipLaunchKernelGGL((mmq_q4k_q8k_kernel<WR, WC, DUMP>), g, b, 0, st, W, q, d, bsum, out, nt, od, id, S);
+    else if (type == 2)
+        hipLaunchKernelGGL((mmq_q6k_q8k_kernel<WR, WC, DUMP, false>), g, b, 0, st, W, q, d, out, nt, od, id, S);
+    else if (type == 3)
+        hipLaunchKernelGGL((mmq_q6k_q8k_kernel<WR, WC, DUMP, true>), g, b, 0, st, W, q, d, out, nt, od, id, S);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 hipError_t launch_mmq_q8k(int type, const uint8_t* W, const int8_t* q, const float* d, const float* bsum, int nt,
                           int od, int id, float* out, int32_t* S, hipStream_t st)
 {
-    (void)type;  // Q4_K only (checked by the caller)
     if (S)
-        return launch_q8k_tile<2, 2, true>(W, q, d, bsum, nt, od, id, out, S, st);
+        return launch_q8k_tile<2, 2, true>(type, W, q, d, bsum, nt, od, id, out, S, st);
     if (q8k_tile_choice(nt, od) == 1)
-        return launch_q8k_tile<4, 2, false>(W, q, d, bsum, nt, od, id, out, nullptr, st);
-    return launch_q8k_tile<2, 2, false>(W, q, d, bsum, nt, od, id, out, nullptr, st);
+        return launch_q8k_tile<4, 2, false>(type, W, q, d, bsum, nt, od, id, out, nullptr, st);
+    return launch_q8k_tile<2, 2, false>(type, W, q, d, bsum, nt, od, id, out, nullptr, st);
 }
 
 }  // namespace qmm

@@ -7,12 +7,13 @@ scale per 256" and "The zero points do not touch the inner loop".
 * qmm_quantize_act_q8k: q, d and the 16-value group sums bit-exact against the
   oracle (crafted blocks, ragged token counts, zero / subnormal / huge blocks, the
   full prefill plane);
-* qmm_q8k_superblock_sums: the integer stage (sum_j sc_j * sum(q*qx) and
-  sum_j m_j * (bsum_2j + bsum_2j+1)) bit-exact against the oracle;
+* qmm_q8k_superblock_sums: the integer stage bit-exact against the oracle -- Q4_K:
+  sum_j sc_j * sum(q*qx) and sum_j m_j * (bsum_2j + bsum_2j+1); Q6_K (both
+  layouts): sum_g sc_g * sum((q6 - 32) * qx) and 0;
 * qmm_matmul_q8k: f32 outputs within |g - o| <= 1e-5 * max(|o|, A / sqrt(n))
-  of the oracle's f64 combine, over several tiles and ragged tails in every
-  dimension, one token, one super-block, long rows, and the benchmark's prefill
-  shapes on a sampled set of outputs.
+  of the oracle's f64 combine, for Q4_K and Q6_K in both layouts, over several
+  tiles and ragged tails in every dimension, one token, one super-block, long
+  rows, and the benchmark's prefill shapes on a sampled set of outputs.
 """
 from __future__ import annotations
 
@@ -27,8 +28,21 @@ from tests._parity import assert_close
 pytestmark = pytest.mark.gpu
 
 qmm = pytest.importorskip("quantized_matmul_amd")
-Q4 = qmm.QMM_TYPE_Q4_K
+Q4, Q6, P6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K, qmm.QMM_TYPE_Q6_K_P224
 DEV = "cuda:0"
+
+
+def _weights(qtype, od, idim, seed):
+    """(device bytes, host bytes for the oracle, oracle type): the padded layout
+    puts 14 zero bytes after each 210-byte Q6_K block; the oracle reads the
+    unpadded blocks."""
+    W = synth.weights(Q6 if qtype == P6 else qtype, od, idim, seed=seed)
+    if qtype != P6:
+        return _up(W), W, qtype
+    b = np.ascontiguousarray(W, dtype=np.uint8).reshape(-1, 210)
+    pad = np.zeros((b.shape[0], 224), np.uint8)
+    pad[:, :210] = b
+    return _up(pad.reshape(-1)), W, Q6
 
 
 def _say(*a):
@@ -88,58 +102,78 @@ def test_quantize_q8k_edge_blocks():
 
 SHAPES = [(1, 1, 256), (5, 7, 512), (9, 100, 768), (64, 128, 1024), (70, 257, 2304), (130, 96, 4096),
           (3, 4096, 4096), (200, 300, 256)]
+SHAPES6 = [(1, 1, 256), (9, 100, 768), (64, 128, 1024), (70, 257, 2304), (130, 96, 4096), (200, 300, 256)]
+TYPED = [(Q4,) + c for c in SHAPES] + [(qt,) + c for qt in (Q6, P6) for c in SHAPES6]
+TYPED_IDS = [f"t{q}-{a}x{b}x{c}" for q, a, b, c in TYPED]
 
 
-@pytest.mark.parametrize("nt,od,idim", SHAPES, ids=[f"{a}x{b}x{c}" for a, b, c in SHAPES])
-def test_q8k_superblock_sums_bit_exact(nt, od, idim):
-    _say(f"q8k integer stage nt={nt} od={od} id={idim}")
-    W = synth.weights(Q4, od, idim, seed=1200 + od)
+@pytest.mark.parametrize("qtype,nt,od,idim", TYPED, ids=TYPED_IDS)
+def test_q8k_superblock_sums_bit_exact(qtype, nt, od, idim):
+    _say(f"q8k integer stage type={qtype} nt={nt} od={od} id={idim}")
+    Wd, W, ot = _weights(qtype, od, idim, seed=1200 + od)
     x = synth.activations(nt, idim, seed=1300 + nt, outlier_frac=0.01)
     q, d, bs = _quant(x)
-    S = qmm.qmm_q8k_superblock_sums(Q4, _up(W), q, d, bs, od)
+    S = qmm.qmm_q8k_superblock_sums(qtype, Wd, q, d, bs, od)
     torch.cuda.synchronize()
-    ref = oracle.q8k_superblock_sums(Q4, W, q.cpu().numpy(), bs.cpu().numpy(), od)
+    ref = oracle.q8k_superblock_sums(ot, W, q.cpu().numpy(), bs.cpu().numpy(), od)
     _same(S.cpu().numpy(), ref, "integer stage")
 
 
-@pytest.mark.parametrize("nt,od,idim", SHAPES, ids=[f"{a}x{b}x{c}" for a, b, c in SHAPES])
-def test_matmul_q8k_against_oracle(nt, od, idim):
-    _say(f"matmul_q8k nt={nt} od={od} id={idim}")
-    W = synth.weights(Q4, od, idim, seed=1400 + od)
+@pytest.mark.parametrize("qtype,nt,od,idim", TYPED, ids=TYPED_IDS)
+def test_matmul_q8k_against_oracle(qtype, nt, od, idim):
+    _say(f"matmul_q8k type={qtype} nt={nt} od={od} id={idim}")
+    Wd, W, ot = _weights(qtype, od, idim, seed=1400 + od)
     x = synth.activations(nt, idim, seed=1500 + nt, outlier_frac=0.01)
     q, d, bs = _quant(x)
-    out = qmm.qmm_matmul_q8k(Q4, _up(W), q, d, bs, od)
+    out = qmm.qmm_matmul_q8k(qtype, Wd, q, d, bs, od)
     torch.cuda.synchronize()
-    ref, mag = oracle.matmul_q8k(Q4, W, q.cpu().numpy(), d.cpu().numpy(), bs.cpu().numpy(), od)
-    worst, rel = assert_close(out.cpu().numpy(), ref, mag, Q4, idim, f"{nt}x{od}x{idim}")
+    ref, mag = oracle.matmul_q8k(ot, W, q.cpu().numpy(), d.cpu().numpy(), bs.cpu().numpy(), od)
+    worst, rel = assert_close(out.cpu().numpy(), ref, mag, ot, idim, f"{nt}x{od}x{idim}")
     _say(f"  worst err/tol {worst:.3f}, max rel {rel:.2e}")
 
 
-@pytest.mark.parametrize("od,idim,nt", [(12288, 4096, 512), (4096, 12288, 512), (12288, 4096, 256),
-                                        (40, 65536, 17)])
-def test_matmul_q8k_full_size_sampled(od, idim, nt):
-    _say(f"matmul_q8k full size od={od} id={idim} nt={nt}")
-    W = synth.weights(Q4, od, idim, seed=1600 + od)
+FULL = [(Q4, 12288, 4096, 512), (Q4, 4096, 12288, 512), (Q4, 12288, 4096, 256), (Q4, 40, 65536, 17),
+        (Q6, 4096, 12288, 512), (P6, 4096, 12288, 256), (P6, 32000, 4096, 64), (Q6, 40, 65536, 17)]
+
+
+@pytest.mark.parametrize("qtype,od,idim,nt", FULL, ids=[f"t{q}-{a}x{b}-{c}" for q, a, b, c in FULL])
+def test_matmul_q8k_full_size_sampled(qtype, od, idim, nt):
+    _say(f"matmul_q8k full size type={qtype} od={od} id={idim} nt={nt}")
+    Wd, W, ot = _weights(qtype, od, idim, seed=1600 + od)
     x = synth.activations(nt, idim, seed=1700 + nt, outlier_frac=0.01)
     q, d, bs = _quant(x)
     qn, dn, bn = q.cpu().numpy(), d.cpu().numpy(), bs.cpu().numpy()
     ref_q = oracle.quantize_q8k(x)
     for name, g, r in zip(("q", "d", "bsum"), (qn, dn, bn), ref_q):
         _same(g, r, f"full-size quantize {name}")
-    out = qmm.qmm_matmul_q8k(Q4, _up(W), q, d, bs, od).cpu().numpy()
+    out = qmm.qmm_matmul_q8k(qtype, Wd, q, d, bs, od).cpu().numpy()
     rng = np.random.default_rng(od + nt)
     ts = np.unique(np.concatenate([rng.choice(nt, size=min(nt, 24), replace=False), [0, nt - 1]]))
     rs = np.unique(np.concatenate([rng.choice(od, size=min(od, 160), replace=False), [0, od - 1]]))
     tt, rr = np.meshgrid(ts, rs, indexing="ij")
     tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
-    ref, mag = oracle.matmul_q8k_points(Q4, W, qn, dn, bn, od, tt, rr)
-    worst, rel = assert_close(out[tt, rr], ref, mag, Q4, idim, f"full size {od}x{idim} nt={nt}")
+    ref, mag = oracle.matmul_q8k_points(ot, W, qn, dn, bn, od, tt, rr)
+    worst, rel = assert_close(out[tt, rr], ref, mag, ot, idim, f"full size {od}x{idim} nt={nt}")
     _say(f"  worst err/tol {worst:.3f}, max rel {rel:.2e}")
 
 
-def test_q8k_rejects_q6k():
-    W = torch.zeros(210, dtype=torch.uint8, device=DEV)
+def test_q8k_padded_equals_unpadded():
+    """The padded Q6_K layout gives the unpadded one's outputs bit for bit (same
+    arithmetic in the same order), on both tile shapes."""
+    for nt, od, idim in ((64, 4096, 4096), (512, 4096, 4096), (17, 300, 2304)):
+        _say(f"matmul_q8k padded vs unpadded nt={nt} od={od} id={idim}")
+        W = synth.weights(Q6, od, idim, seed=1900 + nt)
+        q, d, bs = _quant(synth.activations(nt, idim, seed=1910 + nt))
+        a = qmm.qmm_matmul_q8k(Q6, _up(W), q, d, bs, od)
+        b = qmm.qmm_matmul_q8k(P6, qmm.qmm_pad_q6k(_up(W)), q, d, bs, od)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_q8k_rejects_other_types():
     q, d, bs = _quant(synth.activations(1, 256, seed=1800))
-    with pytest.raises(qmm.QmmError) as e:
-        qmm.qmm_matmul_q8k(qmm.QMM_TYPE_Q6_K, W, q, d, bs, 1)
-    assert e.value.status == qmm.QMM_ERR_TYPE
+    for qt, nbytes in ((qmm.QMM_TYPE_Q4_0, 144), (qmm.QMM_TYPE_Q8_0, 272), (qmm.QMM_TYPE_Q5_K, 176)):
+        W = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+        with pytest.raises(qmm.QmmError) as e:
+            qmm.qmm_matmul_q8k(qt, W, q, d, bs, 1)
+        assert e.value.status == qmm.QMM_ERR_TYPE
