@@ -228,6 +228,20 @@ int qmm_quantize_act_q8k(const float* x, int nt, int id, int8_t* q, float* d, fl
 int qmm_matmul_q8k(int type, const void* W, const int8_t* q, const float* d, const float* bsum, int nt,
                    int od, int id, float* out, void* stream);
 
+/* qmm_matmul_q8k with the tile shape chosen by the caller: kind = QMM_KIND_MMQ
+ * (the rule of qmm_q8k_tile), QMM_KIND_MMQ_128X64, QMM_KIND_MMQ_64X64 or
+ * QMM_KIND_MMQ_64X64_SPLITK (two groups of waves take alternate super-blocks and
+ * add their partial tiles in group order at the end).  For tests and measurement.
+ * Other kinds: QMM_ERR_ARG; other rules as qmm_matmul_q8k. */
+int qmm_matmul_q8k_kind(int kind, int type, const void* W, const int8_t* q, const float* d, const float* bsum,
+                        int nt, int od, int id, float* out, void* stream);
+
+/* The tile shape (QMM_KIND_MMQ_128X64, _64X64 or _64X64_SPLITK) qmm_matmul_q8k uses
+ * for this shape: the one with the fewest (rounds of workgroups over the 256 CUs)
+ * x (super-blocks per wave), ties to the larger tile, as qmm_mmq_tile.  Negative
+ * status for invalid shapes. */
+int qmm_q8k_tile(int nt, int od, int id);
+
 /* Diagnostic: the integer stage of qmm_matmul_q8k alone.  S [nt][od][id/256][2]
  * int32: S[..][0] = sum_j sc_j * sum(q * qx), S[..][1] = sum_j m_j * (bsum_2j +
  * bsum_2j+1) (Q4_K); S[..][0] = sum_g sc_g * sum((q6 - 32) * qx), S[..][1] = 0

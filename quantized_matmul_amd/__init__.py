@@ -47,7 +47,7 @@ EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul"
            "qmm_matmul_q8_kind", "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots",
            "qmm_mfma_tile_check", "qmm_strerror", "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize",
            "qmm_silu_mul_quantize", "qmm_residual_add", "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k",
-           "qmm_matmul_q8k", "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_streamk_ws_bytes",
+           "qmm_matmul_q8k", "qmm_matmul_q8k_kind", "qmm_q8k_tile", "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_streamk_ws_bytes",
            "qmm_matmul_q8_streamk", "qmm_streamk_preferred")
 
 
@@ -92,6 +92,8 @@ def lib():
         L.qmm_silu_mul.argtypes = [P, P, I, I, P, P]
         L.qmm_quantize_act_q8k.argtypes = [P, I, I, P, P, P, P]
         L.qmm_matmul_q8k.argtypes = [I, P, P, P, P, I, I, I, P, P]
+        L.qmm_matmul_q8k_kind.argtypes = [I, I, P, P, P, P, I, I, I, P, P]
+        L.qmm_q8k_tile.argtypes = [I, I, I]
         L.qmm_q8k_superblock_sums.argtypes = [I, P, P, P, P, I, I, I, P, P]
         L.qmm_pad_q6k.argtypes = [P, P, ctypes.c_longlong, P]
         L.qmm_streamk_ws_bytes.argtypes = []
@@ -102,8 +104,8 @@ def lib():
         for f in ("qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8", "qmm_matmul_q8_kind",
                   "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots", "qmm_mfma_tile_check",
                   "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize", "qmm_silu_mul_quantize", "qmm_residual_add",
-                  "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k", "qmm_matmul_q8k",
-                  "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_matmul_q8_streamk", "qmm_streamk_preferred"):
+                  "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k", "qmm_matmul_q8k", "qmm_matmul_q8k_kind",
+                  "qmm_q8k_tile", "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_matmul_q8_streamk", "qmm_streamk_preferred"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -252,6 +254,26 @@ def qmm_matmul_q8k(qtype: int, W: torch.Tensor, q: torch.Tensor, d: torch.Tensor
                                 _dev(d, torch.float32, "d"), _dev(bsum, torch.float32, "bsum"), nt, od, idim,
                                 _dev(out, torch.float32, "out"), _stream(stream)), "qmm_matmul_q8k")
     return out
+
+
+def qmm_matmul_q8k_kind(kind: int, qtype: int, W: torch.Tensor, q: torch.Tensor, d: torch.Tensor,
+                        bsum: torch.Tensor, od: int, out=None, stream=None) -> torch.Tensor:
+    """qmm_matmul_q8k with the tile shape forced (QMM_KIND_MMQ or one of QMM_KIND_MMQ_*)."""
+    nt, idim = q.shape
+    if out is None:
+        out = torch.empty((nt, od), dtype=torch.float32, device=q.device)
+    _check(lib().qmm_matmul_q8k_kind(kind, qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"),
+                                     _dev(d, torch.float32, "d"), _dev(bsum, torch.float32, "bsum"), nt, od, idim,
+                                     _dev(out, torch.float32, "out"), _stream(stream)), "qmm_matmul_q8k_kind")
+    return out
+
+
+def qmm_q8k_tile(nt: int, od: int, idim: int) -> int:
+    """The tile shape (a QMM_KIND_MMQ_* value) qmm_matmul_q8k uses for this shape."""
+    k = int(lib().qmm_q8k_tile(nt, od, idim))
+    if k < 0:
+        raise QmmError(k, "qmm_q8k_tile")
+    return k
 
 
 def qmm_q8k_superblock_sums(qtype: int, W: torch.Tensor, q: torch.Tensor, d: torch.Tensor, bsum: torch.Tensor,

@@ -355,7 +355,7 @@ int qmm_quantize_act_q8k(const float* x, int nt, int id, int8_t* q, float* d, fl
 }
 
 static int q8k_checked(int type, const void* W, const int8_t* q, const float* d, const float* bsum, int nt, int od,
-                       int id, float* out, int32_t* S, void* stream)
+                       int id, float* out, int32_t* S, void* stream, int tile = 0)
 {
     if (!W || !q || !d || !bsum || (!out && !S))
         return QMM_ERR_ARG;
@@ -373,7 +373,7 @@ static int q8k_checked(int type, const void* W, const int8_t* q, const float* d,
     if ((rc = check_device()))
         return rc;
     return launched(qmm::launch_mmq_q8k(type, reinterpret_cast<const uint8_t*>(W), q, d, bsum, nt, od, id, out, S,
-                                        reinterpret_cast<hipStream_t>(stream)));
+                                        reinterpret_cast<hipStream_t>(stream), tile));
 }
 
 int qmm_matmul_q8k(int type, const void* W, const int8_t* q, const float* d, const float* bsum, int nt, int od,
@@ -382,6 +382,25 @@ int qmm_matmul_q8k(int type, const void* W, const int8_t* q, const float* d, con
     if (!out)
         return QMM_ERR_ARG;
     return q8k_checked(type, W, q, d, bsum, nt, od, id, out, nullptr, stream);
+}
+
+int qmm_matmul_q8k_kind(int kind, int type, const void* W, const int8_t* q, const float* d, const float* bsum,
+                        int nt, int od, int id, float* out, void* stream)
+{
+    if (kind != QMM_KIND_MMQ && (kind < QMM_KIND_MMQ_128X64 || kind > QMM_KIND_MMQ_64X64_SPLITK))
+        return QMM_ERR_ARG;
+    if (!out)
+        return QMM_ERR_ARG;
+    const int tile = kind == QMM_KIND_MMQ ? 0 : kind - QMM_KIND_MMQ_128X64 + 1;
+    return q8k_checked(type, W, q, d, bsum, nt, od, id, out, nullptr, stream, tile);
+}
+
+int qmm_q8k_tile(int nt, int od, int id)
+{
+    const int rc = check_shape(nt, od, id);
+    if (rc)
+        return rc;
+    return QMM_KIND_MMQ_128X64 - 1 + qmm::q8k_tile_choice(nt, od, id);
 }
 
 int qmm_q8k_superblock_sums(int type, const void* W, const int8_t* q, const float* d, const float* bsum, int nt,

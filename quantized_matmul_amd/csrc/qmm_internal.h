@@ -37,11 +37,14 @@ hipError_t launch_mmq_streamk(int type, const uint8_t* W, const int8_t* q, const
                               int od, int id, float* out, float* ws, hipStream_t st);
 
 // Q8_K activations: q [nt][id] int8, d [nt][id/256] f32, bsum [nt][id/16] f32
-// (id % 256 == 0), and the Q4_K matmul on them (qmm_mmq_q8k.hip).  S != null: the
-// integer stage only, S [nt][od][id/256][2] int32.
+// (id % 256 == 0), and the Q4_K / Q6_K matmul on them (qmm_mmq_q8k.hip; type 1
+// Q4_K, 2 Q6_K, 3 Q6_K padded).  S != null: the integer stage only, S
+// [nt][od][id/256][2] int32.  tile: 0 = q8k_tile_choice, else 1 = 128 x 64, 2 =
+// 64 x 64, 3 = 64 x 64 split over K.
 hipError_t launch_quantize_q8k(const float* x, int nt, int id, int8_t* q, float* d, float* bsum, hipStream_t st);
+int q8k_tile_choice(int nt, int od, int id);
 hipError_t launch_mmq_q8k(int type, const uint8_t* W, const int8_t* q, const float* d, const float* bsum, int nt,
-                          int od, int id, float* out, int32_t* S, hipStream_t st);
+                          int od, int id, float* out, int32_t* S, hipStream_t st, int tile);
 
 // Producer-side steps that feed the quantizer (qmm_fused.hip).  Rows are [nt][id]
 // f32, id % 32 == 0; q/d/s as for launch_quantize.  With q == null the kernels

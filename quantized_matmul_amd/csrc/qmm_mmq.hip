@@ -220,33 +220,6 @@ __device__ __forceinline__ void q4_stage(Q4Smem<BM, BN, Q5>& sm, const v4i (&pq)
 
 }
 
-// Split over K: groups 1 .. KS-1 write their partial 32 x 32 tile (v, the
-// lane's 16 values) to LDS; group 0 adds them in group order.  Returns false for
-// the waves that are done (groups past 0).  Called by every wave after the last
-// barrier of the K loop; red is the workgroup's tile memory, free by then.
-template <int NW, int KS>
-__device__ __forceinline__ bool combine_k_groups(v16f& v, float* red, int kg, int gw, int lane)
-{
-    if constexpr (KS == 1) {
-        return true;
-    } else {
-        if (kg > 0) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                red[((kg - 1) * NW + gw) * 1024 + i * 64 + lane] = v[i];
-        }
-        __syncthreads();
-        if (kg > 0)
-            return false;
-#pragma unroll
-        for (int g = 1; g < KS; ++g)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                v[i] += red[((g - 1) * NW + gw) * 1024 + i * 64 + lane];
-        return true;
-    }
-}
-
 // Store one wave's 32 x 32 result tile (lane: token tg, rows r0 + 8k + 4 lh + 0..3
 // from v[4k .. 4k+3]) into out [nt][od], masked at the edges.
 __device__ __forceinline__ void store_tile(const v16f& v, float* __restrict__ out, int nt, int od, int tg, int r0,

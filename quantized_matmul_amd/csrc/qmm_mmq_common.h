@@ -44,6 +44,33 @@ __device__ __forceinline__ v16f mfma_k2(float a, float b, v16f acc)
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
 }
 
+// Split over K: groups 1 .. KS-1 write their partial 32 x 32 tile (v, the
+// lane's 16 values) to LDS; group 0 adds them in group order.  Returns false for
+// the waves that are done (groups past 0).  Called by every wave after the last
+// barrier of the K loop; red is the workgroup's tile memory, free by then.
+template <int NW, int KS>
+__device__ __forceinline__ bool combine_k_groups(v16f& v, float* red, int kg, int gw, int lane)
+{
+    if constexpr (KS == 1) {
+        return true;
+    } else {
+        if (kg > 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                red[((kg - 1) * NW + gw) * 1024 + i * 64 + lane] = v[i];
+        }
+        __syncthreads();
+        if (kg > 0)
+            return false;
+#pragma unroll
+        for (int g = 1; g < KS; ++g)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] += red[((g - 1) * NW + gw) * 1024 + i * 64 + lane];
+        return true;
+    }
+}
+
 // Q6_K staging task e = (row r = e / 8, piece c = e % 8) of super-block sb: the
 // 16-byte chunks of low fields and high 2-bit fields piece c covers (h = c / 4,
 // jq = c / 2 % 2, half = c % 2: low bytes 64h + 32jq + 16half, high bytes

@@ -210,32 +210,40 @@ __device__ __forceinline__ void store_tile_rowmajor(const v16f& v, float* __rest
     }
 }
 
-template <int WR, int WC, bool DUMP>
-__global__ __launch_bounds__(64 * WR * WC) void mmq_q4k_q8k_kernel(const uint8_t* __restrict__ W,
-                                                                   const int8_t* __restrict__ q,
-                                                                   const float* __restrict__ dx,
-                                                                   const float* __restrict__ bsum,
-                                                                   float* __restrict__ out, int nt, int od, int id,
-                                                                   int32_t* __restrict__ S)
+// KS = 2: two groups of WR x WC waves in one workgroup split K (alternate
+// super-blocks, each group with its own LDS buffers), their 32 x 32 partial sums
+// added at the end in group order (combine_k_groups), as in the per-32 kernels.
+template <int WR, int WC, int KS, bool DUMP>
+__global__ __launch_bounds__(64 * WR * WC * KS) void mmq_q4k_q8k_kernel(const uint8_t* __restrict__ W,
+                                                                        const int8_t* __restrict__ q,
+                                                                        const float* __restrict__ dx,
+                                                                        const float* __restrict__ bsum,
+                                                                        float* __restrict__ out, int nt, int od,
+                                                                        int id, int32_t* __restrict__ S)
 {
-    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;
+    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;   // NTH: threads of one K group
     constexpr int QC = (BM * 8 + NTH - 1) / NTH;
     constexpr int HC = (BM * 4 + NTH - 1) / NTH;
     constexpr int XC = (BN * 16 + NTH - 1) / NTH;
     constexpr int BC = (BN * 4 + NTH - 1) / NTH;
     constexpr int DC = (BN + NTH - 1) / NTH;
     using SM = Q8KSmem<BM, BN>;
-    __shared__ SM smb[2];
+    __shared__ SM smb[KS][2];
+    static_assert(!DUMP || KS == 1, "the integer-stage dump runs unsplit");
+    static_assert((KS - 1) * WR * WC * 1024 * sizeof(float) <= sizeof(smb), "reduction scratch fits the tiles");
 
     const int ntb = (nt + BN - 1) / BN;
     const int tile = xcd_tile(ntb * ((od + BM - 1) / BM));
     if (tile < 0)
         return;  // whole workgroup
     const int row0 = (tile / ntb) * BM, tok0 = (tile % ntb) * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wr = wave / WC, wc = wave % WC;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kg = KS > 1 ? wave / (WR * WC) : 0, gw = wave - kg * (WR * WC);
+    const int tid = threadIdx.x - kg * NTH;
+    const int wr = gw / WC, wc = gw % WC;
     const int li = lane & 31, lh = lane >> 5;
     const int nsb = id >> 8;
+    const int niter = (nsb + KS - 1) / KS;
     const uint32_t row_bytes = (uint32_t)nsb * kQ4KBytes;
 
     Q8KRegs<QC, HC, XC, BC, DC> pr;
@@ -253,12 +261,13 @@ __global__ __launch_bounds__(64 * WR * WC) void mmq_q4k_q8k_kernel(const uint8_t
     // double-buffered LDS as in the per-32 kernel: compute from smb[it & 1] while
     // the next super-block (in registers) goes to the other buffer and the loads
     // of the one after are issued; unconditional prefetches with clamped indices
-    q8k_prefetch(pr, offs, rs, 0);
-    q8k_stage<BM, BN, NTH, QC, HC, XC, BC, DC>(smb[0], pr, tid, true);
-    q8k_prefetch(pr, offs, rs, min(1, nsb - 1));
+    q8k_prefetch(pr, offs, rs, min(kg, nsb - 1));
+    q8k_stage<BM, BN, NTH, QC, HC, XC, BC, DC>(smb[kg][0], pr, tid, kg < nsb);
+    q8k_prefetch(pr, offs, rs, min(KS + kg, nsb - 1));
     __syncthreads();
-    for (int sb = 0; sb < nsb; ++sb) {
-        const SM& sm = smb[sb & 1];
+    for (int it = 0; it < niter; ++it) {
+        const SM& sm = smb[kg][it & 1];
+        const int sb = it * KS + kg;
         // operands that do not depend on the codes first: the exact min sums and
         // the scale products d*dx (registers 0..15) and -dmin*dx (16..31)
         const v8h bsv = *reinterpret_cast<const v8h*>(&sm.bs[atok * 16 + 8 * lh]);
@@ -313,12 +322,15 @@ __global__ __launch_bounds__(64 * WR * WC) void mmq_q4k_q8k_kernel(const uint8_t
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        q8k_stage<BM, BN, NTH, QC, HC, XC, BC, DC>(smb[(sb + 1) & 1], pr, tid, sb + 1 < nsb);
-        q8k_prefetch(pr, offs, rs, min(sb + 2, nsb - 1));
+        q8k_stage<BM, BN, NTH, QC, HC, XC, BC, DC>(smb[kg][(it + 1) & 1], pr, tid, sb + KS < nsb);
+        q8k_prefetch(pr, offs, rs, min(sb + 2 * KS, nsb - 1));
         __syncthreads();
     }
-    if constexpr (!DUMP)
+    if constexpr (!DUMP) {
+        if (!combine_k_groups<WR * WC, KS>(acc, reinterpret_cast<float*>(&smb[0][0]), kg, gw, lane))
+            return;
         store_tile_rowmajor(acc, out, nt, od, tok0 + wc * 32, row0 + brow, lh);
+    }
 }
 
 // ------------------------------------------------------------------ Q6_K on Q8_K
@@ -358,29 +370,34 @@ __device__ __forceinline__ void q6q8k_step(const Q6Q8KSmem<BM, BN>& sm, int m, i
     C1 = mfma_i8_k16(x1, w1);
 }
 
-template <int WR, int WC, bool DUMP, bool PAD>
-__global__ __launch_bounds__(64 * WR * WC) void mmq_q6k_q8k_kernel(const uint8_t* __restrict__ W,
-                                                                   const int8_t* __restrict__ q,
-                                                                   const float* __restrict__ dx,
-                                                                   float* __restrict__ out, int nt, int od, int id,
-                                                                   int32_t* __restrict__ S)
+template <int WR, int WC, int KS, bool DUMP, bool PAD>
+__global__ __launch_bounds__(64 * WR * WC * KS) void mmq_q6k_q8k_kernel(const uint8_t* __restrict__ W,
+                                                                        const int8_t* __restrict__ q,
+                                                                        const float* __restrict__ dx,
+                                                                        float* __restrict__ out, int nt, int od,
+                                                                        int id, int32_t* __restrict__ S)
 {
-    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;
+    constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;   // NTH: threads of one K group
     constexpr int WC8 = (BM * 8 + NTH - 1) / NTH;  // (row, 32-code piece) tasks per thread
     constexpr int XC = (BN * 16 + NTH - 1) / NTH;
     constexpr int DC = (BN + NTH - 1) / NTH;
     using SM = Q6Q8KSmem<BM, BN>;
-    __shared__ SM smb[2];
+    __shared__ SM smb[KS][2];
+    static_assert(!DUMP || KS == 1, "the integer-stage dump runs unsplit");
+    static_assert((KS - 1) * WR * WC * 1024 * sizeof(float) <= sizeof(smb), "reduction scratch fits the tiles");
 
     const int ntb = (nt + BN - 1) / BN;
     const int tile = xcd_tile(ntb * ((od + BM - 1) / BM));
     if (tile < 0)
         return;  // whole workgroup
     const int row0 = (tile / ntb) * BM, tok0 = (tile % ntb) * BN;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wr = wave / WC, wc = wave % WC;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int kg = KS > 1 ? wave / (WR * WC) : 0, gw = wave - kg * (WR * WC);
+    const int tid = threadIdx.x - kg * NTH;
+    const int wr = gw / WC, wc = gw % WC;
     const int li = lane & 31, lh = lane >> 5;
     const int nsb = id >> 8;
+    const int niter = (nsb + KS - 1) / KS;
     const size_t row_bytes = (size_t)nsb * (PAD ? kQ6KP224Bytes : kQ6KBytes);
 
     uint32_t pl[WC8][5], phh[WC8][5], pshift[WC8], psd[WC8];
@@ -429,12 +446,13 @@ __global__ __launch_bounds__(64 * WR * WC) void mmq_q6k_q8k_kernel(const uint8_t
     const int atok = wc * 32 + li;   // this lane's token as an A operand
     const int brow = wr * 32 + li;   // this lane's weight row as a B operand
 
-    prefetch(0);
-    stage(smb[0], true);
-    prefetch(min(1, nsb - 1));
+    prefetch(min(kg, nsb - 1));
+    stage(smb[kg][0], kg < nsb);
+    prefetch(min(KS + kg, nsb - 1));
     __syncthreads();
-    for (int sb = 0; sb < nsb; ++sb) {
-        const SM& sm = smb[sb & 1];
+    for (int it = 0; it < niter; ++it) {
+        const SM& sm = smb[kg][it & 1];
+        const int sb = it * KS + kg;
         // the scale product d[r] * dx[t] in the result layout (one outer product on
         // the k = 0 lanes), and this row's sixteen group scales
         const float oa = lh == 0 ? sm.dx[atok] : 0.f, ob = lh == 0 ? sm.dd[brow] : 0.f;
@@ -488,50 +506,64 @@ __global__ __launch_bounds__(64 * WR * WC) void mmq_q6k_q8k_kernel(const uint8_t
                 acc[i] = fmaf(pp[i], (float)acci[i], acc[i]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        stage(smb[(sb + 1) & 1], sb + 1 < nsb);
-        prefetch(min(sb + 2, nsb - 1));
+        stage(smb[kg][(it + 1) & 1], sb + KS < nsb);
+        prefetch(min(sb + 2 * KS, nsb - 1));
         __syncthreads();
     }
-    if constexpr (!DUMP)
+    if constexpr (!DUMP) {
+        if (!combine_k_groups<WR * WC, KS>(acc, reinterpret_cast<float*>(&smb[0][0]), kg, gw, lane))
+            return;
         store_tile_rowmajor(acc, out, nt, od, tok0 + wc * 32, row0 + brow, lh);
+    }
 }
 
-// The shape with the fewer (rounds of workgroups over the 256 CUs) x super-blocks:
-// 128 x 64 (8 waves) or 64 x 64 (4 waves); ties go to the larger tile.
-int q8k_tile_choice(int nt, int od)
+// The shape with the fewest (rounds of workgroups over the 256 CUs) x (super-blocks
+// each wave walks): 1 = 128 x 64 (8 waves, one workgroup per CU), 2 = 64 x 64 (4
+// waves, two per CU), 3 = 64 x 64 split over K (8 waves in two groups, one
+// workgroup per CU by LDS); ties go to the lower number.  The per-32 kernels'
+// rule.
+int q8k_tile_choice(int nt, int od, int id)
 {
+    const long nsb = id / 256;
     const long t42 = (long)((nt + 63) / 64) * ((od + 127) / 128);
     const long t22 = (long)((nt + 63) / 64) * ((od + 63) / 64);
-    return (t42 + 255) / 256 <= (t22 + 511) / 512 ? 1 : 2;
+    const long c1 = ((t42 + 255) / 256) * nsb;
+    const long c2 = ((t22 + 511) / 512) * nsb;
+    const long c3 = ((t22 + 255) / 256) * ((nsb + 1) / 2);
+    if (c1 <= c2 && c1 <= c3)
+        return 1;
+    return c2 <= c3 ? 2 : 3;
 }
 
 // type 1: Q4_K, 2: Q6_K, 3: Q6_K padded (checked by the caller)
-template <int WR, int WC, bool DUMP>
+template <int WR, int WC, int KS, bool DUMP>
 static hipError_t launch_q8k_tile(int type, const uint8_t* W, const int8_t* q, const float* d, const float* bsum,
                                   int nt, int od, int id, float* out, int32_t* S, hipStream_t st)
 {
     const long tiles = (long)((nt + 32 * WC - 1) / (32 * WC)) * ((od + 32 * WR - 1) / (32 * WR));
     const long grid = (tiles + 7) / 8 * 8;  // a multiple of the 8 XCDs (xcd_tile drops the padding)
-    const dim3 g((unsigned)grid), b(64 * WR * WC);
+    const dim3 g((unsigned)grid), b(64 * WR * WC * KS);
     if (type == 1)
-        hipLaunchKernelGGL((mmq_q4k_q8k_kernel<WR, WC, DUMP>), g, b, 0, st, W, q, d, bsum, out, nt, od, id, S);
+        hipLaunchKernelGGL((mmq_q4k_q8k_kernel<WR, WC, KS, DUMP>), g, b, 0, st, W, q, d, bsum, out, nt, od, id, S);
     else if (type == 2)
-        hipLaunchKernelGGL((mmq_q6k_q8k_kernel<WR, WC, DUMP, false>), g, b, 0, st, W, q, d, out, nt, od, id, S);
+        hipLaunchKernelGGL((mmq_q6k_q8k_kernel<WR, WC, KS, DUMP, false>), g, b, 0, st, W, q, d, out, nt, od, id, S);
     else if (type == 3)
-        hipLaunchKernelGGL((mmq_q6k_q8k_kernel<WR, WC, DUMP, true>), g, b, 0, st, W, q, d, out, nt, od, id, S);
+        hipLaunchKernelGGL((mmq_q6k_q8k_kernel<WR, WC, KS, DUMP, true>), g, b, 0, st, W, q, d, out, nt, od, id, S);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 hipError_t launch_mmq_q8k(int type, const uint8_t* W, const int8_t* q, const float* d, const float* bsum, int nt,
-                          int od, int id, float* out, int32_t* S, hipStream_t st)
+                          int od, int id, float* out, int32_t* S, hipStream_t st, int tile)
 {
     if (S)
-        return launch_q8k_tile<2, 2, true>(type, W, q, d, bsum, nt, od, id, out, S, st);
-    if (q8k_tile_choice(nt, od) == 1)
-        return launch_q8k_tile<4, 2, false>(type, W, q, d, bsum, nt, od, id, out, nullptr, st);
-    return launch_q8k_tile<2, 2, false>(type, W, q, d, bsum, nt, od, id, out, nullptr, st);
+        return launch_q8k_tile<2, 2, 1, true>(type, W, q, d, bsum, nt, od, id, out, S, st);
+    switch (tile ? tile : q8k_tile_choice(nt, od, id)) {
+    case 1: return launch_q8k_tile<4, 2, 1, false>(type, W, q, d, bsum, nt, od, id, out, nullptr, st);
+    case 2: return launch_q8k_tile<2, 2, 1, false>(type, W, q, d, bsum, nt, od, id, out, nullptr, st);
+    default: return launch_q8k_tile<2, 2, 2, false>(type, W, q, d, bsum, nt, od, id, out, nullptr, st);
+    }
 }
 
 }  // namespace qmm

@@ -197,6 +197,18 @@ def test_q8k_validation():
     assert L.qmm_matmul_q8k(2, p, p, p, None, 9, 4, 256, p, None) == qmm.QMM_ERR_ARG
     assert L.qmm_matmul_q8k(2, p, p, p, p, 9, 4, 320, p, None) == qmm.QMM_ERR_SHAPE
     assert L.qmm_matmul_q8k(3, ctypes.c_void_p((1 << 20) + 2), p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_ALIGN
+    for kind in (qmm.QMM_KIND_MMQ, qmm.QMM_KIND_MMQ_128X64, qmm.QMM_KIND_MMQ_64X64, qmm.QMM_KIND_MMQ_64X64_SPLITK):
+        assert L.qmm_matmul_q8k_kind(kind, 2, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_DEVICE
+    for kind in (0, qmm.QMM_KIND_MMVQ, 6):
+        assert L.qmm_matmul_q8k_kind(kind, 2, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    # the tile rule: fewest rounds x super-blocks per wave, ties to the larger tile
+    assert qmm.qmm_q8k_tile(512, 12288, 4096) == qmm.QMM_KIND_MMQ_128X64
+    assert qmm.qmm_q8k_tile(512, 4096, 12288) == qmm.QMM_KIND_MMQ_128X64
+    assert qmm.qmm_q8k_tile(256, 4096, 12288) == qmm.QMM_KIND_MMQ_64X64_SPLITK
+    assert qmm.qmm_q8k_tile(256, 4096, 4096) == qmm.QMM_KIND_MMQ_64X64_SPLITK
+    assert qmm.qmm_q8k_tile(64, 32000, 4096) == qmm.QMM_KIND_MMQ_128X64
+    with pytest.raises(qmm.QmmError):
+        qmm.qmm_q8k_tile(4, 4, 300)
 
 
 def test_streamk_validation():

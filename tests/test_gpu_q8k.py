@@ -13,7 +13,9 @@ scale per 256" and "The zero points do not touch the inner loop".
 * qmm_matmul_q8k: f32 outputs within |g - o| <= 1e-5 * max(|o|, A / sqrt(n))
   of the oracle's f64 combine, for Q4_K and Q6_K in both layouts, over several
   tiles and ragged tails in every dimension, one token, one super-block, long
-  rows, and the benchmark's prefill shapes on a sampled set of outputs.
+  rows, and the benchmark's prefill shapes on a sampled set of outputs;
+* qmm_matmul_q8k_kind: every tile shape, the split over K included, against the
+  oracle; the default call equals its chosen tile's call bit for bit.
 """
 from __future__ import annotations
 
@@ -155,6 +157,49 @@ def test_matmul_q8k_full_size_sampled(qtype, od, idim, nt):
     ref, mag = oracle.matmul_q8k_points(ot, W, qn, dn, bn, od, tt, rr)
     worst, rel = assert_close(out[tt, rr], ref, mag, ot, idim, f"full size {od}x{idim} nt={nt}")
     _say(f"  worst err/tol {worst:.3f}, max rel {rel:.2e}")
+
+
+KIND_SHAPES = [(1, 1, 256), (9, 100, 768), (64, 128, 1024), (70, 257, 2304), (130, 96, 4096), (65, 200, 1280)]
+KINDS = [(qt, kind) + c for qt in (Q4, Q6, P6)
+         for kind in (qmm.QMM_KIND_MMQ_128X64, qmm.QMM_KIND_MMQ_64X64, qmm.QMM_KIND_MMQ_64X64_SPLITK)
+         for c in KIND_SHAPES]
+
+
+@pytest.mark.parametrize("qtype,kind,nt,od,idim", KINDS, ids=[f"t{q}-k{k}-{a}x{b}x{c}" for q, k, a, b, c in KINDS])
+def test_matmul_q8k_every_tile(qtype, kind, nt, od, idim):
+    """Each tile shape, the split over K included (odd super-block counts leave the
+    second group a super-block past the end; one super-block leaves it nothing),
+    against the oracle; the default call equals its own tile's call bit for bit."""
+    _say(f"matmul_q8k kind={kind} type={qtype} nt={nt} od={od} id={idim}")
+    Wd, W, ot = _weights(qtype, od, idim, seed=2000 + od + kind)
+    x = synth.activations(nt, idim, seed=2100 + nt, outlier_frac=0.01)
+    q, d, bs = _quant(x)
+    out = qmm.qmm_matmul_q8k_kind(kind, qtype, Wd, q, d, bs, od)
+    auto = qmm.qmm_matmul_q8k(qtype, Wd, q, d, bs, od)
+    same = qmm.qmm_matmul_q8k_kind(qmm.qmm_q8k_tile(nt, od, idim), qtype, Wd, q, d, bs, od)
+    torch.cuda.synchronize()
+    assert torch.equal(auto.view(torch.int32), same.view(torch.int32))
+    ref, mag = oracle.matmul_q8k(ot, W, q.cpu().numpy(), d.cpu().numpy(), bs.cpu().numpy(), od)
+    worst, rel = assert_close(out.cpu().numpy(), ref, mag, ot, idim, f"kind {kind} {nt}x{od}x{idim}")
+    _say(f"  worst err/tol {worst:.3f}, max rel {rel:.2e}")
+
+
+def test_matmul_q8k_split_full_size_sampled():
+    """The split tile on the long-K shape it is chosen for (padded Q6_K 4096 x 12288
+    at 256 tokens; Q4_K 4096 x 4096 at 256), sampled against the oracle."""
+    for qtype, od, idim, nt in ((P6, 4096, 12288, 256), (Q4, 4096, 4096, 256)):
+        assert qmm.qmm_q8k_tile(nt, od, idim) == qmm.QMM_KIND_MMQ_64X64_SPLITK
+        _say(f"matmul_q8k split full size type={qtype} od={od} id={idim} nt={nt}")
+        Wd, W, ot = _weights(qtype, od, idim, seed=2200 + od)
+        q, d, bs = _quant(synth.activations(nt, idim, seed=2300 + nt, outlier_frac=0.01))
+        out = qmm.qmm_matmul_q8k(qtype, Wd, q, d, bs, od).cpu().numpy()
+        rng = np.random.default_rng(od + nt + 7)
+        ts = np.unique(np.concatenate([rng.choice(nt, size=24, replace=False), [0, nt - 1]]))
+        rs = np.unique(np.concatenate([rng.choice(od, size=160, replace=False), [0, od - 1]]))
+        tt, rr = np.meshgrid(ts, rs, indexing="ij")
+        tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
+        ref, mag = oracle.matmul_q8k_points(ot, W, q.cpu().numpy(), d.cpu().numpy(), bs.cpu().numpy(), od, tt, rr)
+        assert_close(out[tt, rr], ref, mag, ot, idim, f"split full size {od}x{idim} nt={nt}")
 
 
 def test_q8k_padded_equals_unpadded():
