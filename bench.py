@@ -121,13 +121,6 @@ def copy_calibration(torch, mib):
 MMQ_TILES = {3: (4, 2, 1), 4: (2, 2, 1), 5: (2, 2, 2)}   # tile kind -> (row waves, token waves, K groups)
 
 
-def q8k_tile(nt, od):
-    """1 for the 128 x 64 tile of the Q8_K kernel, 2 for 64 x 64 (the library's rule)."""
-    t42 = -(-nt // 64) * -(-od // 128)
-    t22 = -(-nt // 64) * -(-od // 64)
-    return 1 if -(-t42 // 256) <= -(-t22 // 512) else 2
-
-
 def mmq_kernel(qmm, nt, od, idim):
     """(kernel name, launch threads) of the Q4_K matrix kernel qmm_matmul runs for this
     shape with a full workspace: stream-K (256 workgroups of 8 waves) where
@@ -765,12 +758,12 @@ def main():
                     value=round(ops / t8 / 1e12, 2), unit="TOP/s")
         m = max(q8, key=lambda c: float(np.mean(c.k_ms)))
         km = float(np.mean(m.k_ms)) * 1e-3
-        wr, wc = (4, 2) if q8k_tile(m.nt, m.od) == 1 else (2, 2)
-        kname = f"qmm::mmq_q4k_q8k_kernel<{wr}, {wc}, false>"
+        wr, wc, ks = MMQ_TILES[qmm.qmm_q8k_tile(m.nt, m.od, m.idim)]
+        kname = f"qmm::mmq_q4k_q8k_kernel<{wr}, {wc}, {ks}, false>"
         tiles = -(-m.nt // (32 * wc)) * -(-m.od // (32 * wr))
         line["roofline"] = {"bound": "mfma", "achieved": round(m.ops / km / 1e12, 2), "peak": INT8_PEAK_TOPS,
                             "unit": "TFLOP/s", "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4),
-                            "traffic": read_traffic(Q8K_COUNTERS, kname, 8 * -(-tiles // 8) * 64 * wr * wc),
+                            "traffic": read_traffic(Q8K_COUNTERS, kname, 8 * -(-tiles // 8) * 64 * wr * wc * ks),
                             "kernel": kname.replace("qmm::", "").replace(" ", ""), "call": m.label,
                             "ops_per_launch": int(m.ops)}
         line["per32_same_shapes"] = {"value": round(sum(c.ops for c in p32) / t32 / 1e12, 2), "unit": "TOP/s",
