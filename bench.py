@@ -759,7 +759,7 @@ def main():
         m = max(q8, key=lambda c: float(np.mean(c.k_ms)))
         km = float(np.mean(m.k_ms)) * 1e-3
         wr, wc, ks = MMQ_TILES[qmm.qmm_q8k_tile(m.nt, m.od, m.idim)]
-        kname = f"qmm::mmq_q4k_q8k_kernel<{wr}, {wc}, {ks}, false>"
+        kname = f"qmm::mmq_k4_q8k_kernel<{wr}, {wc}, {ks}, false, false>"
         tiles = -(-m.nt // (32 * wc)) * -(-m.od // (32 * wr))
         line["roofline"] = {"bound": "mfma", "achieved": round(m.ops / km / 1e12, 2), "peak": INT8_PEAK_TOPS,
                             "unit": "TFLOP/s", "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4),

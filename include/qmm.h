@@ -217,14 +217,14 @@ int qmm_nt_switch(void);
 int qmm_quantize_act_q8k(const float* x, int nt, int id, int8_t* q, float* d, float* bsum, void* stream);
 
 /* out [nt][od] = W x on Q8_K activations (q, d, bsum from qmm_quantize_act_q8k).
- * Per super-block b of row r and token t, Q4_K:
+ * Per super-block b of row r and token t, Q4_K and Q5_K (codes 0..15 or 0..31):
  *   d_r * dx_tb * sum_j sc_j * sum(q * qx) - dmin_r * dx_tb * sum_j m_j * (bsum_2j + bsum_2j+1);
  * Q6_K (either layout; bsum is not read but must be a valid aligned pointer):
  *   d_r * dx_tb * sum_g sc_g * sum((q6 - 32) * qx)  over its sixteen 16-weight groups;
  * the inner sums exact integers, the f32 terms accumulated in f32.  Runs the
  * int8-MFMA matrix kernel for every nt (no vector kernel on this path).  Weight
- * types Q4_K, Q6_K, Q6_K_P224 (QMM_ERR_TYPE otherwise); shapes and alignment as
- * qmm_matmul_q8. */
+ * types Q4_K, Q5_K, Q6_K, Q6_K_P224 (QMM_ERR_TYPE otherwise); shapes and alignment
+ * as qmm_matmul_q8. */
 int qmm_matmul_q8k(int type, const void* W, const int8_t* q, const float* d, const float* bsum, int nt,
                    int od, int id, float* out, void* stream);
 
@@ -244,8 +244,8 @@ int qmm_q8k_tile(int nt, int od, int id);
 
 /* Diagnostic: the integer stage of qmm_matmul_q8k alone.  S [nt][od][id/256][2]
  * int32: S[..][0] = sum_j sc_j * sum(q * qx), S[..][1] = sum_j m_j * (bsum_2j +
- * bsum_2j+1) (Q4_K); S[..][0] = sum_g sc_g * sum((q6 - 32) * qx), S[..][1] = 0
- * (Q6_K), computed by the kernel's code.  Arguments as qmm_matmul_q8k. */
+ * bsum_2j+1) (Q4_K, Q5_K); S[..][0] = sum_g sc_g * sum((q6 - 32) * qx), S[..][1] =
+ * 0 (Q6_K), computed by the kernel's code.  Arguments as qmm_matmul_q8k. */
 int qmm_q8k_superblock_sums(int type, const void* W, const int8_t* q, const float* d, const float* bsum,
                             int nt, int od, int id, int32_t* S, void* stream);
 

@@ -246,7 +246,7 @@ def qmm_quantize_act_q8k(x: torch.Tensor, q=None, d=None, bsum=None, stream=None
 
 def qmm_matmul_q8k(qtype: int, W: torch.Tensor, q: torch.Tensor, d: torch.Tensor, bsum: torch.Tensor, od: int,
                    out=None, stream=None):
-    """out f32 [nt, od] from Q8_K activations (Q4_K or Q6_K weights, either Q6_K layout)."""
+    """out f32 [nt, od] from Q8_K activations (Q4_K, Q5_K or Q6_K weights, either Q6_K layout)."""
     nt, idim = q.shape
     if out is None:
         out = torch.empty((nt, od), dtype=torch.float32, device=q.device)

@@ -362,7 +362,7 @@ static int q8k_checked(int type, const void* W, const int8_t* q, const float* d,
     int rc = check_type(type);
     if (rc)
         return rc;
-    if (type != QMM_TYPE_Q4_K && type != QMM_TYPE_Q6_K && type != QMM_TYPE_Q6_K_P224)
+    if (type != QMM_TYPE_Q4_K && type != QMM_TYPE_Q5_K && type != QMM_TYPE_Q6_K && type != QMM_TYPE_Q6_K_P224)
         return QMM_ERR_TYPE;
     if ((rc = check_shape(nt, od, id)))
         return rc;

@@ -1,5 +1,5 @@
-// MMQ on Q8_K activations (one scale per 256 values): Q4_K weights, int8 MFMA, the
-// eight sub-block products combined in integer inside each super-block.
+// MMQ on Q8_K activations (one scale per 256 values): Q4_K / Q5_K and Q6_K weights,
+// int8 MFMA, the group products combined in integer inside each super-block.
 //
 // [GEMM, "Activations: int8 with a scale per 256"]: the activations carry one f32
 // scale per 256 values and the code sum of every 16-value group.  [GEMM, "The zero
@@ -47,7 +47,7 @@ __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t vo
 }
 
 template <int BM, int BN>
-struct __attribute__((aligned(16))) Q8KSmem {
+struct __attribute__((aligned(16))) Q8KSmemK4 {
     static constexpr int QS_STRIDE = 144;   // 128 code bytes + 16 pad
     static constexpr int X_STRIDE = 272;    // 256 activation codes + 16 pad
     uint8_t qs[BM * QS_STRIDE];
@@ -59,31 +59,49 @@ struct __attribute__((aligned(16))) Q8KSmem {
     float dx[BN];                           // [token] activation scale
 };
 
+template <int BM, int BN, bool Q5>
+struct __attribute__((aligned(16))) Q8KSmem : Q8KSmemK4<BM, BN> {};
+
+// Q5_K: also the 32 high-bit bytes of each row
+template <int BM, int BN>
+struct __attribute__((aligned(16))) Q8KSmem<BM, BN, true> : Q8KSmemK4<BM, BN> {
+    uint8_t qh[BM * 32];
+};
+
 // Per-thread prefetch slots: code chunks, row headers, activation chunks, group
 // sum chunks (four per token), activation scales.
-template <int QC, int HC, int XC, int BC, int DC>
+template <int QC, int HC, int XC, int BC, int DC, int HBC>
 struct Q8KRegs {
-    v4i q[QC], h[HC], x[XC], b[BC];
+    v4i q[QC], h[HC], x[XC], b[BC], hb[HBC];
     uint32_t d[DC];
 };
 
-template <int QC, int HC, int XC, int BC, int DC>
+template <int QC, int HC, int XC, int BC, int DC, int HBC>
 struct Q8KOffs {
-    uint32_t q[QC], h[HC], x[XC], b[BC], d[DC];
+    uint32_t q[QC], h[HC], x[XC], b[BC], d[DC], hb[HBC];
 };
 
 struct Q8KRsrc {
     __amdgpu_buffer_rsrc_t w, x, d, b;
 };
 
-template <int BM, int BN, int NTH, int QC, int HC, int XC, int BC, int DC>
-__device__ __forceinline__ void q8k_offsets(Q8KOffs<QC, HC, XC, BC, DC>& o, int tid, int row0, int tok0, int nt,
-                                            int od, int id, int nsb, uint32_t row_bytes)
+// Q5 (Q5_K, 176-byte blocks): the codes start at byte 48, after the 32 high-bit
+// bytes at 16 (task HBC: one 16-byte half of a row's high-bit bytes).
+template <int BM, int BN, int NTH, int QC, int HC, int XC, int BC, int DC, int HBC, bool Q5>
+__device__ __forceinline__ void q8k_offsets(Q8KOffs<QC, HC, XC, BC, DC, HBC>& o, int tid, int row0, int tok0,
+                                            int nt, int od, int id, int nsb, uint32_t row_bytes)
 {
 #pragma unroll
     for (int k = 0; k < QC; ++k) {
         const int e = task<BM * 8, NTH, QC>(tid + k * NTH);
-        o.q[k] = (uint32_t)(min(row0 + (e >> 3), od - 1) - row0) * row_bytes + 16 + 16 * (e & 7);
+        o.q[k] = (uint32_t)(min(row0 + (e >> 3), od - 1) - row0) * row_bytes + (Q5 ? 48 : 16) + 16 * (e & 7);
+    }
+    if constexpr (Q5) {
+#pragma unroll
+        for (int k = 0; k < HBC; ++k) {
+            const int e = task<BM * 2, NTH, HBC>(tid + k * NTH);
+            o.hb[k] = (uint32_t)(min(row0 + (e >> 1), od - 1) - row0) * row_bytes + 16 + 16 * (e & 1);
+        }
     }
 #pragma unroll
     for (int k = 0; k < HC; ++k) {
@@ -107,15 +125,20 @@ __device__ __forceinline__ void q8k_offsets(Q8KOffs<QC, HC, XC, BC, DC>& o, int 
     }
 }
 
-template <int QC, int HC, int XC, int BC, int DC>
-__device__ __forceinline__ void q8k_prefetch(Q8KRegs<QC, HC, XC, BC, DC>& r, const Q8KOffs<QC, HC, XC, BC, DC>& o,
-                                             const Q8KRsrc& rs, int sb)
+template <int QC, int HC, int XC, int BC, int DC, int HBC, bool Q5>
+__device__ __forceinline__ void q8k_prefetch(Q8KRegs<QC, HC, XC, BC, DC, HBC>& r,
+                                             const Q8KOffs<QC, HC, XC, BC, DC, HBC>& o, const Q8KRsrc& rs, int sb)
 {
-    const uint32_t ow = (uint32_t)sb * kQ4KBytes, ox = 256u * (uint32_t)sb, ob = 64u * (uint32_t)sb,
-                   odx = 4u * (uint32_t)sb;
+    const uint32_t ow = (uint32_t)sb * (Q5 ? kQ5KBytes : kQ4KBytes), ox = 256u * (uint32_t)sb,
+                   ob = 64u * (uint32_t)sb, odx = 4u * (uint32_t)sb;
 #pragma unroll
     for (int k = 0; k < QC; ++k)
         r.q[k] = bload16(rs.w, o.q[k], ow);
+    if constexpr (Q5) {
+#pragma unroll
+        for (int k = 0; k < HBC; ++k)
+            r.hb[k] = bload16(rs.w, o.hb[k], ow);
+    }
 #pragma unroll
     for (int k = 0; k < HC; ++k)
         r.h[k] = bload16(rs.w, o.h[k], ow);
@@ -132,15 +155,22 @@ __device__ __forceinline__ void q8k_prefetch(Q8KRegs<QC, HC, XC, BC, DC>& r, con
 
 // valid == false (a super-block index past the end) stages d = dmin = 0: that
 // super-block then adds nothing.
-template <int BM, int BN, int NTH, int QC, int HC, int XC, int BC, int DC>
-__device__ __forceinline__ void q8k_stage(Q8KSmem<BM, BN>& sm, const Q8KRegs<QC, HC, XC, BC, DC>& r, int tid,
-                                          bool valid)
+template <int BM, int BN, int NTH, int QC, int HC, int XC, int BC, int DC, int HBC, bool Q5>
+__device__ __forceinline__ void q8k_stage(Q8KSmem<BM, BN, Q5>& sm, const Q8KRegs<QC, HC, XC, BC, DC, HBC>& r,
+                                          int tid, bool valid)
 {
-    using SM = Q8KSmem<BM, BN>;
+    using SM = Q8KSmem<BM, BN, Q5>;
 #pragma unroll
     for (int k = 0; k < QC; ++k) {
         const int e = task<BM * 8, NTH, QC>(tid + k * NTH);
         *reinterpret_cast<v4i*>(&sm.qs[(e >> 3) * SM::QS_STRIDE + 16 * (e & 7)]) = r.q[k];
+    }
+    if constexpr (Q5) {
+#pragma unroll
+        for (int k = 0; k < HBC; ++k) {
+            const int e = task<BM * 2, NTH, HBC>(tid + k * NTH);
+            *reinterpret_cast<v4i*>(&sm.qh[(e >> 1) * 32 + 16 * (e & 1)]) = r.hb[k];
+        }
     }
 #pragma unroll
     for (int k = 0; k < HC; ++k) {
@@ -182,13 +212,20 @@ __device__ __forceinline__ void q8k_stage(Q8KSmem<BM, BN>& sm, const Q8KRegs<QC,
 
 // Sub-blocks 2p and 2p + 1 of the staged super-block: the two int8 products,
 // token-major (A = activation codes of token atok, B = weight codes of row brow).
-template <int BM, int BN>
-__device__ __forceinline__ void q8k_step(const Q8KSmem<BM, BN>& sm, int p, int atok, int brow, int lh, v16i& C0,
+// Q5: bits 2p and 2p + 1 of the row's high-bit bytes 16 lh .. + 15 are the fifth
+// code bits of the two sub-blocks at those positions (codes 0..31).
+template <int BM, int BN, bool Q5>
+__device__ __forceinline__ void q8k_step(const Q8KSmem<BM, BN, Q5>& sm, int p, int atok, int brow, int lh, v16i& C0,
                                          v16i& C1)
 {
-    using SM = Q8KSmem<BM, BN>;
+    using SM = Q8KSmem<BM, BN, Q5>;
     const v4i w16 = *reinterpret_cast<const v4i*>(&sm.qs[brow * SM::QS_STRIDE + 32 * p + 16 * lh]);
-    const v4i b0 = w16 & 0x0F0F0F0F, b1 = (w16 >> 4) & 0x0F0F0F0F;
+    v4i b0 = w16 & 0x0F0F0F0F, b1 = (w16 >> 4) & 0x0F0F0F0F;
+    if constexpr (Q5) {
+        const v4i hb = *reinterpret_cast<const v4i*>(&sm.qh[brow * 32 + 16 * lh]);
+        b0 |= ((hb >> (2 * p)) & 0x01010101) << 4;
+        b1 |= ((hb >> (2 * p + 1)) & 0x01010101) << 4;
+    }
     const v4i x0 = *reinterpret_cast<const v4i*>(&sm.xq[atok * SM::X_STRIDE + 64 * p + 16 * lh]);
     const v4i x1 = *reinterpret_cast<const v4i*>(&sm.xq[atok * SM::X_STRIDE + 64 * p + 32 + 16 * lh]);
     C0 = mfma_i8_k32(x0, b0);
@@ -210,16 +247,20 @@ __device__ __forceinline__ void store_tile_rowmajor(const v16f& v, float* __rest
     }
 }
 
+// Q4_K (Q5 false) and Q5_K (Q5 true, 176-byte blocks: the fifth code bit from the
+// staged high-bit bytes; |sum(q * qx)| <= 32 * 31 * 127 per sub-block, sc <= 63,
+// so the integer combine stays in range).  One kernel rather than a shared body
+// under two wrappers: the wrapped body took 15 more VGPRs.
 // KS = 2: two groups of WR x WC waves in one workgroup split K (alternate
 // super-blocks, each group with its own LDS buffers), their 32 x 32 partial sums
 // added at the end in group order (combine_k_groups), as in the per-32 kernels.
-template <int WR, int WC, int KS, bool DUMP>
-__global__ __launch_bounds__(64 * WR * WC * KS) void mmq_q4k_q8k_kernel(const uint8_t* __restrict__ W,
-                                                                        const int8_t* __restrict__ q,
-                                                                        const float* __restrict__ dx,
-                                                                        const float* __restrict__ bsum,
-                                                                        float* __restrict__ out, int nt, int od,
-                                                                        int id, int32_t* __restrict__ S)
+template <int WR, int WC, int KS, bool DUMP, bool Q5>
+__global__ __launch_bounds__(64 * WR * WC * KS) void mmq_k4_q8k_kernel(const uint8_t* __restrict__ W,
+                                                                       const int8_t* __restrict__ q,
+                                                                       const float* __restrict__ dx,
+                                                                       const float* __restrict__ bsum,
+                                                                       float* __restrict__ out, int nt, int od,
+                                                                       int id, int32_t* __restrict__ S)
 {
     constexpr int BM = 32 * WR, BN = 32 * WC, NTH = 64 * WR * WC;   // NTH: threads of one K group
     constexpr int QC = (BM * 8 + NTH - 1) / NTH;
@@ -227,7 +268,8 @@ __global__ __launch_bounds__(64 * WR * WC * KS) void mmq_q4k_q8k_kernel(const ui
     constexpr int XC = (BN * 16 + NTH - 1) / NTH;
     constexpr int BC = (BN * 4 + NTH - 1) / NTH;
     constexpr int DC = (BN + NTH - 1) / NTH;
-    using SM = Q8KSmem<BM, BN>;
+    constexpr int HBC = Q5 ? (BM * 2 + NTH - 1) / NTH : 1;
+    using SM = Q8KSmem<BM, BN, Q5>;
     __shared__ SM smb[KS][2];
     static_assert(!DUMP || KS == 1, "the integer-stage dump runs unsplit");
     static_assert((KS - 1) * WR * WC * 1024 * sizeof(float) <= sizeof(smb), "reduction scratch fits the tiles");
@@ -244,11 +286,11 @@ __global__ __launch_bounds__(64 * WR * WC * KS) void mmq_q4k_q8k_kernel(const ui
     const int li = lane & 31, lh = lane >> 5;
     const int nsb = id >> 8;
     const int niter = (nsb + KS - 1) / KS;
-    const uint32_t row_bytes = (uint32_t)nsb * kQ4KBytes;
+    const uint32_t row_bytes = (uint32_t)nsb * (Q5 ? kQ5KBytes : kQ4KBytes);
 
-    Q8KRegs<QC, HC, XC, BC, DC> pr;
-    Q8KOffs<QC, HC, XC, BC, DC> offs;
-    q8k_offsets<BM, BN, NTH, QC, HC, XC, BC, DC>(offs, tid, row0, tok0, nt, od, id, nsb, row_bytes);
+    Q8KRegs<QC, HC, XC, BC, DC, HBC> pr;
+    Q8KOffs<QC, HC, XC, BC, DC, HBC> offs;
+    q8k_offsets<BM, BN, NTH, QC, HC, XC, BC, DC, HBC, Q5>(offs, tid, row0, tok0, nt, od, id, nsb, row_bytes);
     Q8KRsrc rs;
     rs.w = buffer_rsrc(W + (size_t)row0 * row_bytes, (size_t)(od - row0) * row_bytes);
     rs.x = buffer_rsrc(q + (size_t)tok0 * id, (size_t)(nt - tok0) * id);
@@ -261,9 +303,9 @@ __global__ __launch_bounds__(64 * WR * WC * KS) void mmq_q4k_q8k_kernel(const ui
     // double-buffered LDS as in the per-32 kernel: compute from smb[it & 1] while
     // the next super-block (in registers) goes to the other buffer and the loads
     // of the one after are issued; unconditional prefetches with clamped indices
-    q8k_prefetch(pr, offs, rs, min(kg, nsb - 1));
-    q8k_stage<BM, BN, NTH, QC, HC, XC, BC, DC>(smb[kg][0], pr, tid, kg < nsb);
-    q8k_prefetch(pr, offs, rs, min(KS + kg, nsb - 1));
+    q8k_prefetch<QC, HC, XC, BC, DC, HBC, Q5>(pr, offs, rs, min(kg, nsb - 1));
+    q8k_stage<BM, BN, NTH, QC, HC, XC, BC, DC, HBC, Q5>(smb[kg][0], pr, tid, kg < nsb);
+    q8k_prefetch<QC, HC, XC, BC, DC, HBC, Q5>(pr, offs, rs, min(KS + kg, nsb - 1));
     __syncthreads();
     for (int it = 0; it < niter; ++it) {
         const SM& sm = smb[kg][it & 1];
@@ -280,13 +322,13 @@ __global__ __launch_bounds__(64 * WR * WC * KS) void mmq_q4k_q8k_kernel(const ui
 
         v16i acci = {}, acco = {};
         v16i Ca0, Ca1;
-        q8k_step<BM, BN>(sm, 0, atok, brow, lh, Ca0, Ca1);
+        q8k_step<BM, BN, Q5>(sm, 0, atok, brow, lh, Ca0, Ca1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             v16i Cb0, Cb1;
             if (p < 3)
-                q8k_step<BM, BN>(sm, p + 1, atok, brow, lh, Cb0, Cb1);
+                q8k_step<BM, BN, Q5>(sm, p + 1, atok, brow, lh, Cb0, Cb1);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
@@ -322,8 +364,8 @@ __global__ __launch_bounds__(64 * WR * WC * KS) void mmq_q4k_q8k_kernel(const ui
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        q8k_stage<BM, BN, NTH, QC, HC, XC, BC, DC>(smb[kg][(it + 1) & 1], pr, tid, sb + KS < nsb);
-        q8k_prefetch(pr, offs, rs, min(sb + 2 * KS, nsb - 1));
+        q8k_stage<BM, BN, NTH, QC, HC, XC, BC, DC, HBC, Q5>(smb[kg][(it + 1) & 1], pr, tid, sb + KS < nsb);
+        q8k_prefetch<QC, HC, XC, BC, DC, HBC, Q5>(pr, offs, rs, min(sb + 2 * KS, nsb - 1));
         __syncthreads();
     }
     if constexpr (!DUMP) {
@@ -535,7 +577,7 @@ int q8k_tile_choice(int nt, int od, int id)
     return c2 <= c3 ? 2 : 3;
 }
 
-// type 1: Q4_K, 2: Q6_K, 3: Q6_K padded (checked by the caller)
+// type 1: Q4_K, 2: Q6_K, 3: Q6_K padded, 6: Q5_K (checked by the caller)
 template <int WR, int WC, int KS, bool DUMP>
 static hipError_t launch_q8k_tile(int type, const uint8_t* W, const int8_t* q, const float* d, const float* bsum,
                                   int nt, int od, int id, float* out, int32_t* S, hipStream_t st)
@@ -544,7 +586,11 @@ static hipError_t launch_q8k_tile(int type, const uint8_t* W, const int8_t* q, c
     const long grid = (tiles + 7) / 8 * 8;  // a multiple of the 8 XCDs (xcd_tile drops the padding)
     const dim3 g((unsigned)grid), b(64 * WR * WC * KS);
     if (type == 1)
-        hipLaunchKernelGGL((mmq_q4k_q8k_kernel<WR, WC, KS, DUMP>), g, b, 0, st, W, q, d, bsum, out, nt, od, id, S);
+        hipLaunchKernelGGL((mmq_k4_q8k_kernel<WR, WC, KS, DUMP, false>), g, b, 0, st, W, q, d, bsum, out, nt, od, id,
+                           S);
+    else if (type == 6)
+        hipLaunchKernelGGL((mmq_k4_q8k_kernel<WR, WC, KS, DUMP, true>), g, b, 0, st, W, q, d, bsum, out, nt, od, id,
+                           S);
     else if (type == 2)
         hipLaunchKernelGGL((mmq_q6k_q8k_kernel<WR, WC, KS, DUMP, false>), g, b, 0, st, W, q, d, out, nt, od, id, S);
     else if (type == 3)

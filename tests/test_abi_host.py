@@ -184,15 +184,15 @@ def test_pad_q6k_validation():
 
 
 def test_q8k_validation():
-    """qmm_matmul_q8k and its integer-stage diagnostic take Q4_K and Q6_K in both
-    layouts (validation passes; the device check answers here) and refuse the
-    32-block types and Q5_K; shape, null and alignment errors come first."""
+    """qmm_matmul_q8k and its integer-stage diagnostic take Q4_K, Q5_K and Q6_K in
+    both layouts (validation passes; the device check answers here) and refuse the
+    32-block types and unknown types; shape, null and alignment errors come first."""
     L = qmm.lib()
     p = ctypes.c_void_p(1 << 20)
-    for t in (1, 2, 3):
+    for t in (1, 2, 3, 6):
         assert L.qmm_matmul_q8k(t, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_DEVICE
         assert L.qmm_q8k_superblock_sums(t, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_DEVICE
-    for t in (4, 5, 6):
+    for t in (4, 5, 7):
         assert L.qmm_matmul_q8k(t, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_TYPE
     assert L.qmm_matmul_q8k(2, p, p, p, None, 9, 4, 256, p, None) == qmm.QMM_ERR_ARG
     assert L.qmm_matmul_q8k(2, p, p, p, p, 9, 4, 320, p, None) == qmm.QMM_ERR_SHAPE

@@ -7,13 +7,13 @@ scale per 256" and "The zero points do not touch the inner loop".
 * qmm_quantize_act_q8k: q, d and the 16-value group sums bit-exact against the
   oracle (crafted blocks, ragged token counts, zero / subnormal / huge blocks, the
   full prefill plane);
-* qmm_q8k_superblock_sums: the integer stage bit-exact against the oracle -- Q4_K:
-  sum_j sc_j * sum(q*qx) and sum_j m_j * (bsum_2j + bsum_2j+1); Q6_K (both
-  layouts): sum_g sc_g * sum((q6 - 32) * qx) and 0;
+* qmm_q8k_superblock_sums: the integer stage bit-exact against the oracle -- Q4_K
+  and Q5_K: sum_j sc_j * sum(q*qx) and sum_j m_j * (bsum_2j + bsum_2j+1); Q6_K
+  (both layouts): sum_g sc_g * sum((q6 - 32) * qx) and 0;
 * qmm_matmul_q8k: f32 outputs within |g - o| <= 1e-5 * max(|o|, A / sqrt(n))
-  of the oracle's f64 combine, for Q4_K and Q6_K in both layouts, over several
-  tiles and ragged tails in every dimension, one token, one super-block, long
-  rows, and the benchmark's prefill shapes on a sampled set of outputs;
+  of the oracle's f64 combine, for Q4_K, Q5_K and Q6_K in both layouts, over
+  several tiles and ragged tails in every dimension, one token, one super-block,
+  long rows, and the benchmark's prefill shapes on a sampled set of outputs;
 * qmm_matmul_q8k_kind: every tile shape, the split over K included, against the
   oracle; the default call equals its chosen tile's call bit for bit.
 """
@@ -30,7 +30,7 @@ from tests._parity import assert_close
 pytestmark = pytest.mark.gpu
 
 qmm = pytest.importorskip("quantized_matmul_amd")
-Q4, Q6, P6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K, qmm.QMM_TYPE_Q6_K_P224
+Q4, Q6, P6, Q5 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K, qmm.QMM_TYPE_Q6_K_P224, qmm.QMM_TYPE_Q5_K
 DEV = "cuda:0"
 
 
@@ -105,7 +105,7 @@ def test_quantize_q8k_edge_blocks():
 SHAPES = [(1, 1, 256), (5, 7, 512), (9, 100, 768), (64, 128, 1024), (70, 257, 2304), (130, 96, 4096),
           (3, 4096, 4096), (200, 300, 256)]
 SHAPES6 = [(1, 1, 256), (9, 100, 768), (64, 128, 1024), (70, 257, 2304), (130, 96, 4096), (200, 300, 256)]
-TYPED = [(Q4,) + c for c in SHAPES] + [(qt,) + c for qt in (Q6, P6) for c in SHAPES6]
+TYPED = [(Q4,) + c for c in SHAPES] + [(qt,) + c for qt in (Q6, P6, Q5) for c in SHAPES6]
 TYPED_IDS = [f"t{q}-{a}x{b}x{c}" for q, a, b, c in TYPED]
 
 
@@ -135,7 +135,8 @@ def test_matmul_q8k_against_oracle(qtype, nt, od, idim):
 
 
 FULL = [(Q4, 12288, 4096, 512), (Q4, 4096, 12288, 512), (Q4, 12288, 4096, 256), (Q4, 40, 65536, 17),
-        (Q6, 4096, 12288, 512), (P6, 4096, 12288, 256), (P6, 32000, 4096, 64), (Q6, 40, 65536, 17)]
+        (Q6, 4096, 12288, 512), (P6, 4096, 12288, 256), (P6, 32000, 4096, 64), (Q6, 40, 65536, 17),
+        (Q5, 12288, 4096, 512), (Q5, 4096, 12288, 256)]
 
 
 @pytest.mark.parametrize("qtype,od,idim,nt", FULL, ids=[f"t{q}-{a}x{b}-{c}" for q, a, b, c in FULL])
@@ -160,7 +161,7 @@ def test_matmul_q8k_full_size_sampled(qtype, od, idim, nt):
 
 
 KIND_SHAPES = [(1, 1, 256), (9, 100, 768), (64, 128, 1024), (70, 257, 2304), (130, 96, 4096), (65, 200, 1280)]
-KINDS = [(qt, kind) + c for qt in (Q4, Q6, P6)
+KINDS = [(qt, kind) + c for qt in (Q4, Q6, P6, Q5)
          for kind in (qmm.QMM_KIND_MMQ_128X64, qmm.QMM_KIND_MMQ_64X64, qmm.QMM_KIND_MMQ_64X64_SPLITK)
          for c in KIND_SHAPES]
 
@@ -217,7 +218,7 @@ def test_q8k_padded_equals_unpadded():
 
 def test_q8k_rejects_other_types():
     q, d, bs = _quant(synth.activations(1, 256, seed=1800))
-    for qt, nbytes in ((qmm.QMM_TYPE_Q4_0, 144), (qmm.QMM_TYPE_Q8_0, 272), (qmm.QMM_TYPE_Q5_K, 176)):
+    for qt, nbytes in ((qmm.QMM_TYPE_Q4_0, 144), (qmm.QMM_TYPE_Q8_0, 272)):
         W = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
         with pytest.raises(qmm.QmmError) as e:
             qmm.qmm_matmul_q8k(qt, W, q, d, bs, 1)

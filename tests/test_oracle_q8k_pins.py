@@ -28,7 +28,7 @@ import synth
 from tests import bruteforce as bf
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-Q4, Q6 = oracle.TYPE_Q4_K, oracle.TYPE_Q6_K
+Q4, Q6, Q5 = oracle.TYPE_Q4_K, oracle.TYPE_Q6_K, oracle.TYPE_Q5_K
 
 
 def _golden():
@@ -74,7 +74,7 @@ def _fold_case(qtype, od, idim, nt, seed):
 
 
 def pin_q8k_fold_identity():
-    for qtype in (Q4, Q6):
+    for qtype in (Q4, Q6, Q5):
         for seed in (1, 2):
             _, _, _, out, mag, Wd, xd = _fold_case(qtype, 6, 768, 3, 20 + seed)
             ref = xd @ Wd.T
@@ -85,7 +85,7 @@ def pin_q8k_fold_identity():
 
 
 def pin_q8k_quantization_bound():
-    for qtype in (Q4, Q6):
+    for qtype in (Q4, Q6, Q5):
         _, x, (q, d, bs), out, mag, Wd, _ = _fold_case(qtype, 5, 1024, 4, 30)
         exact = x.astype(np.float64) @ Wd.T
         absW = np.abs(Wd).reshape(Wd.shape[0], -1, 256).sum(axis=2)
@@ -127,7 +127,7 @@ def test_q8k_invariants(seed, scale):
 
 def test_q8k_points_match_full():
     od, idim, nt = 7, 512, 3
-    for qtype in (Q4, Q6):
+    for qtype in (Q4, Q6, Q5):
         W, _, (q, d, bs), out, mag, _, _ = _fold_case(qtype, od, idim, nt, 40)
         t = np.array([0, 2, 1], np.int32)
         r = np.array([6, 0, 3], np.int32)
@@ -135,21 +135,22 @@ def test_q8k_points_match_full():
         assert np.array_equal(po, out[t, r]) and np.array_equal(pm, mag[t, r])
 
 
-@pytest.mark.parametrize("qtype", [Q4, Q6])
+@pytest.mark.parametrize("qtype", [Q4, Q6, Q5])
 def test_q8k_superblock_sums_brute_force(qtype):
     """The integer stage from the element-indexed decoder and plain Python sums."""
     od, idim, nt = 3, 512, 2
     W, _, (q, d, bs), *_ = _fold_case(qtype, od, idim, nt, 50)
     S = oracle.q8k_superblock_sums(qtype, W, q, bs, od)
-    bb = 144 if qtype == Q4 else 210
+    bb = {Q4: 144, Q6: 210, Q5: 176}[qtype]
     Wb = W.reshape(od, idim // 256, bb)
     for t in range(nt):
         for r in range(od):
             for b in range(idim // 256):
                 blk = Wb[r, b]
                 qx = q[t, 256 * b: 256 * b + 256].astype(np.int64)
-                if qtype == Q4:
-                    codes = np.array([bf.q4k_code(blk, e) for e in range(256)], np.int64)
+                if qtype in (Q4, Q5):
+                    code = bf.q4k_code if qtype == Q4 else bf.q5k_code
+                    codes = np.array([code(blk, e) for e in range(256)], np.int64)
                     scm = [bf.q4k_field(blk, j) for j in range(8)]
                     s1 = sum(scm[j][0] * int(np.dot(codes[32 * j: 32 * j + 32], qx[32 * j: 32 * j + 32]))
                              for j in range(8))
