@@ -50,7 +50,8 @@ layer).  value = int8 ops over the summed kernel times; graph = the whole step
 (quantize + matmul per call) captured into one HIP graph and replayed;
 graph_layers = the same matmuls fed as a model's layers feed them (fused RMS-norm,
 residual-add and silu * up producers; one quantized input shared by q, k, v and one
-by gate, up: 4 producer launches per layer), also one graph.
+by gate, up: 4 producer launches per layer), also one graph; graph_q8k = "graph"
+on Q8_K activations (quantize_q8k + the Q8_K matrix kernels; other numerics).
 
 Workload "formats": Q4_0, Q8_0 and Q5_K (and Q4_K for comparison) at 12288 x 4096, nt = 1
 and nt = 512.  value = HBM GB/s of the Q4_0 vector kernel at nt = 1.
@@ -833,6 +834,15 @@ def main():
         lms = layer_graph_ms(torch, qmm, calls)
         line["graph_layers"] = {"ms_per_step": round(lms, 4), "replays": 5, "producer_launches_per_layer": 4,
                                 "TOP_s_incl_producers": round(ops / (lms * 1e-3) / 1e12, 2)}
+        # the same step on Q8_K activations (one scale per 256 values: other numerics),
+        # one Q8_K quantize per matmul as in "graph"
+        q8k_calls = [Call(torch, qmm, c.qtype, c.od, c.idim, c.nt, seed=0, outliers=False, copies=c.W[:1], x=c.x,
+                          q8k=True, label=c.label + " Q8_K") for c in calls]
+        kms = graph_replay_ms(torch, q8k_calls)
+        line["graph_q8k"] = {"ms_per_step": round(kms, 4), "replays": 5,
+                             "TOP_s_incl_quantize": round(ops / (kms * 1e-3) / 1e12, 2),
+                             "activations": "Q8_K (one scale per 256 values, its own numerics)"}
+        del q8k_calls
         line["config"] = {"workload": "dllm_step", "layers": 32, "canvas": 256, "hidden": 4096, "ffn": 12288,
                           "matmuls_per_step": len(calls), "down_projection": "Q6_K padded to 224-byte blocks"}
         detail = detail[:7]
