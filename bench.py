@@ -51,7 +51,9 @@ layer).  value = int8 ops over the summed kernel times; graph = the whole step
 graph_layers = the same matmuls fed as a model's layers feed them (fused RMS-norm,
 residual-add and silu * up producers; one quantized input shared by q, k, v and one
 by gate, up: 4 producer launches per layer), also one graph; graph_q8k = "graph"
-on Q8_K activations (quantize_q8k + the Q8_K matrix kernels; other numerics).
+on Q8_K activations (quantize_q8k + the Q8_K matrix kernels; other numerics);
+graph_layers_q8k = graph_layers with the producers' Q8_K variants and the Q8_K
+matrix kernels.
 
 Workload "formats": Q4_0, Q8_0 and Q5_K (and Q4_K for comparison) at 12288 x 4096, nt = 1
 and nt = 512.  value = HBM GB/s of the Q4_0 vector kernel at nt = 1.
@@ -232,7 +234,7 @@ def graph_replay_ms(torch, calls, replays=5):
     return e0.elapsed_time(e1) / replays
 
 
-def layer_graph_ms(torch, qmm, calls, replays=5):
+def layer_graph_ms(torch, qmm, calls, replays=5, q8k=False):
     """The step's 224 matmuls with the data flow of a model's layers, captured as one
     HIP graph like graph_replay_ms.  Per layer: q, k and v read one fused RMS-norm
     quantize of the residual stream; o reads the quantized v output (standing in
@@ -240,7 +242,8 @@ def layer_graph_ms(torch, qmm, calls, replays=5):
     quantize; down reads the fused silu(gate) * up quantize of their outputs; the
     next layer's first producer adds the down output into the residual stream.  So
     4 producer launches and 7 matmuls per layer (the plain step: 7 quantize
-    launches, one per matmul), the same matmul kernels and weights."""
+    launches, one per matmul), the same matmul kernels and weights.  q8k: the
+    producers' Q8_K variants and calls on the Q8_K matrix path."""
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     L = qmm.lib()
     dev = torch.device("cuda:0")
@@ -250,8 +253,16 @@ def layer_graph_ms(torch, qmm, calls, replays=5):
     w_ffn = torch.from_numpy(1.0 + 0.25 * synth.activations(1, hid, seed=302)[0]).to(dev)
 
     def q8(n):
+        if q8k:  # codes, d per 256 values, 16-value group sums
+            return (torch.empty((nt, n), dtype=torch.int8, device=dev), torch.empty((nt, n // 256), device=dev),
+                    torch.empty((nt, n // 16), device=dev))
         return (torch.empty((nt, n), dtype=torch.int8, device=dev), torch.empty((nt, n // 32), device=dev),
                 torch.empty((nt, n // 32), device=dev))
+
+    sfx = "_q8k" if q8k else ""
+    rms_q, add_rms_q, silu_q = (getattr(L, f"qmm_rmsnorm_quantize{sfx}"), getattr(L, f"qmm_add_rmsnorm_quantize{sfx}"),
+                                getattr(L, f"qmm_silu_mul_quantize{sfx}"))
+    quant = L.qmm_quantize_act_q8k if q8k else L.qmm_quantize_act
 
     qa, qo, qf, qd = q8(hid), q8(hid), q8(hid), q8(ffn)
     ptr = lambda t: P(t.data_ptr())  # noqa: E731
@@ -268,18 +279,16 @@ def layer_graph_ms(torch, qmm, calls, replays=5):
         for layer in range(len(calls) // 7):
             cq, ck, cv, co, cg, cu, cd = calls[7 * layer:7 * layer + 7]
             if layer == 0:
-                rc.append(L.qmm_rmsnorm_quantize(ptr(h), ptr(w_attn), eps, I(nt), I(hid), *map(ptr, qa), sp))
+                rc.append(rms_q(ptr(h), ptr(w_attn), eps, I(nt), I(hid), *map(ptr, qa), sp))
             else:
                 prev = calls[7 * layer - 1].out
-                rc.append(L.qmm_add_rmsnorm_quantize(ptr(h), ptr(prev), ptr(w_attn), eps, I(nt), I(hid),
-                                                     *map(ptr, qa), sp))
+                rc.append(add_rms_q(ptr(h), ptr(prev), ptr(w_attn), eps, I(nt), I(hid), *map(ptr, qa), sp))
             rc += [mm(cq, qa), mm(ck, qa), mm(cv, qa)]
-            rc.append(L.qmm_quantize_act(ptr(cv.out), I(nt), I(hid), *map(ptr, qo), sp))
+            rc.append(quant(ptr(cv.out), I(nt), I(hid), *map(ptr, qo), sp))
             rc.append(mm(co, qo))
-            rc.append(L.qmm_add_rmsnorm_quantize(ptr(h), ptr(co.out), ptr(w_ffn), eps, I(nt), I(hid),
-                                                 *map(ptr, qf), sp))
+            rc.append(add_rms_q(ptr(h), ptr(co.out), ptr(w_ffn), eps, I(nt), I(hid), *map(ptr, qf), sp))
             rc += [mm(cg, qf), mm(cu, qf)]
-            rc.append(L.qmm_silu_mul_quantize(ptr(cg.out), ptr(cu.out), I(nt), I(ffn), *map(ptr, qd), sp))
+            rc.append(silu_q(ptr(cg.out), ptr(cu.out), I(nt), I(ffn), *map(ptr, qd), sp))
             rc.append(mm(cd, qd))
         if any(rc):
             raise RuntimeError(f"layer data flow: a launch failed ({[r for r in rc if r]})")
@@ -471,11 +480,11 @@ class FusedCall:
 def fused_kernel_name(op, idim):
     """(trace name, launch threads per row or per element group) of a fused kernel."""
     if op == "silu_mul_quantize":
-        return "qmm::{anonymous}::silu_mul_kernel<true>"
+        return "qmm::{anonymous}::silu_mul_kernel<1>"
     nch = (idim // 4 + 255) // 256
     ch = next((c for c in (1, 2, 4, 8, 16) if nch <= c), 0)
     add = "true" if op == "add_rmsnorm_quantize" else "false"
-    return f"qmm::{{anonymous}}::rmsnorm_kernel<{ch}, {add}, true>"
+    return f"qmm::{{anonymous}}::rmsnorm_kernel<{ch}, {add}, 1>"
 
 
 def fused_cpu_baseline(calls):
@@ -842,6 +851,9 @@ def main():
         line["graph_q8k"] = {"ms_per_step": round(kms, 4), "replays": 5,
                              "TOP_s_incl_quantize": round(ops / (kms * 1e-3) / 1e12, 2),
                              "activations": "Q8_K (one scale per 256 values, its own numerics)"}
+        lkms = layer_graph_ms(torch, qmm, q8k_calls, q8k=True)
+        line["graph_layers_q8k"] = {"ms_per_step": round(lkms, 4), "replays": 5, "producer_launches_per_layer": 4,
+                                    "TOP_s_incl_producers": round(ops / (lkms * 1e-3) / 1e12, 2)}
         del q8k_calls
         line["config"] = {"workload": "dllm_step", "layers": 32, "canvas": 256, "hidden": 4096, "ffn": 12288,
                           "matmuls_per_step": len(calls), "down_projection": "Q6_K padded to 224-byte blocks"}

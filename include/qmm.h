@@ -289,6 +289,17 @@ int qmm_rmsnorm_quantize(const float* x, const float* w, float eps, int nt, int 
 int qmm_silu_mul_quantize(const float* g, const float* u, int nt, int id, int8_t* q, float* d,
                           float* s, void* stream);
 
+/* The same three steps ending in the Q8_K quantizer (qmm_quantize_act_q8k's rules;
+ * id a multiple of 256, else QMM_ERR_SHAPE): q [nt][id] int8, d [nt][id/256],
+ * bsum [nt][id/16] f32, bit for bit the unfused step followed by
+ * qmm_quantize_act_q8k.  For the Q8_K matrix path (qmm_matmul_q8k). */
+int qmm_add_rmsnorm_quantize_q8k(float* h, const float* o, const float* w, float eps, int nt, int id, int8_t* q,
+                                 float* d, float* bsum, void* stream);
+int qmm_rmsnorm_quantize_q8k(const float* x, const float* w, float eps, int nt, int id, int8_t* q, float* d,
+                             float* bsum, void* stream);
+int qmm_silu_mul_quantize_q8k(const float* g, const float* u, int nt, int id, int8_t* q, float* d, float* bsum,
+                              void* stream);
+
 /* Unfused steps (f32 out), the chain the fused calls are equal to. */
 /* h <- h + o over [nt][id] (id % 32 == 0 as above). */
 int qmm_residual_add(float* h, const float* o, int nt, int id, void* stream);

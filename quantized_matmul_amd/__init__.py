@@ -46,7 +46,8 @@ BLOCK_BYTES = {QMM_TYPE_Q4_K: 144, QMM_TYPE_Q6_K: 210, QMM_TYPE_Q6_K_P224: 224, 
 EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8",
            "qmm_matmul_q8_kind", "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots",
            "qmm_mfma_tile_check", "qmm_strerror", "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize",
-           "qmm_silu_mul_quantize", "qmm_residual_add", "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k",
+           "qmm_silu_mul_quantize", "qmm_add_rmsnorm_quantize_q8k", "qmm_rmsnorm_quantize_q8k",
+           "qmm_silu_mul_quantize_q8k", "qmm_residual_add", "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k",
            "qmm_matmul_q8k", "qmm_matmul_q8k_kind", "qmm_q8k_tile", "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_streamk_ws_bytes",
            "qmm_matmul_q8_streamk", "qmm_streamk_preferred")
 
@@ -87,6 +88,9 @@ def lib():
         L.qmm_add_rmsnorm_quantize.argtypes = [P, P, P, F, I, I, P, P, P, P]
         L.qmm_rmsnorm_quantize.argtypes = [P, P, F, I, I, P, P, P, P]
         L.qmm_silu_mul_quantize.argtypes = [P, P, I, I, P, P, P, P]
+        L.qmm_add_rmsnorm_quantize_q8k.argtypes = [P, P, P, F, I, I, P, P, P, P]
+        L.qmm_rmsnorm_quantize_q8k.argtypes = [P, P, F, I, I, P, P, P, P]
+        L.qmm_silu_mul_quantize_q8k.argtypes = [P, P, I, I, P, P, P, P]
         L.qmm_residual_add.argtypes = [P, P, I, I, P]
         L.qmm_rmsnorm.argtypes = [P, P, F, I, I, P, P]
         L.qmm_silu_mul.argtypes = [P, P, I, I, P, P]
@@ -103,7 +107,9 @@ def lib():
         L.qmm_strerror.restype = ctypes.c_char_p
         for f in ("qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8", "qmm_matmul_q8_kind",
                   "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots", "qmm_mfma_tile_check",
-                  "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize", "qmm_silu_mul_quantize", "qmm_residual_add",
+                  "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize", "qmm_silu_mul_quantize",
+                  "qmm_add_rmsnorm_quantize_q8k", "qmm_rmsnorm_quantize_q8k", "qmm_silu_mul_quantize_q8k",
+                  "qmm_residual_add",
                   "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k", "qmm_matmul_q8k", "qmm_matmul_q8k_kind",
                   "qmm_q8k_tile", "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_matmul_q8_streamk", "qmm_streamk_preferred"):
             getattr(L, f).restype = I
@@ -340,6 +346,58 @@ def qmm_silu_mul_quantize(g: torch.Tensor, u: torch.Tensor, q=None, d=None, s=No
                                        _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
                                        _dev(s, torch.float32, "s"), _stream(stream)), "qmm_silu_mul_quantize")
     return q, d, s
+
+
+def _q8k_out(x: torch.Tensor, q, d, bsum):
+    nt, idim = x.shape
+    if q is None:
+        q = torch.empty((nt, idim), dtype=torch.int8, device=x.device)
+    if d is None:
+        d = torch.empty((nt, idim // 256), dtype=torch.float32, device=x.device)
+    if bsum is None:
+        bsum = torch.empty((nt, idim // 16), dtype=torch.float32, device=x.device)
+    return q, d, bsum
+
+
+def qmm_add_rmsnorm_quantize_q8k(h: torch.Tensor, o: torch.Tensor, w: torch.Tensor, eps: float, q=None, d=None,
+                                 bsum=None, stream=None):
+    """h <- h + o in place, then rmsnorm(h) * w quantized to Q8_K: returns (q, d, bsum)."""
+    nt, idim = h.shape
+    if o.shape != h.shape:
+        raise ValueError("o must have the shape of h")
+    _weight_vec(w, idim)
+    q, d, bsum = _q8k_out(h, q, d, bsum)
+    _check(lib().qmm_add_rmsnorm_quantize_q8k(_dev(h, torch.float32, "h"), _dev(o, torch.float32, "o"),
+                                              _dev(w, torch.float32, "w"), float(eps), nt, idim,
+                                              _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
+                                              _dev(bsum, torch.float32, "bsum"), _stream(stream)),
+           "qmm_add_rmsnorm_quantize_q8k")
+    return q, d, bsum
+
+
+def qmm_rmsnorm_quantize_q8k(x: torch.Tensor, w: torch.Tensor, eps: float, q=None, d=None, bsum=None, stream=None):
+    """rmsnorm(x) * w quantized to Q8_K: returns (q, d, bsum)."""
+    nt, idim = x.shape
+    _weight_vec(w, idim)
+    q, d, bsum = _q8k_out(x, q, d, bsum)
+    _check(lib().qmm_rmsnorm_quantize_q8k(_dev(x, torch.float32, "x"), _dev(w, torch.float32, "w"), float(eps),
+                                          nt, idim, _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
+                                          _dev(bsum, torch.float32, "bsum"), _stream(stream)),
+           "qmm_rmsnorm_quantize_q8k")
+    return q, d, bsum
+
+
+def qmm_silu_mul_quantize_q8k(g: torch.Tensor, u: torch.Tensor, q=None, d=None, bsum=None, stream=None):
+    """silu(g) * u quantized to Q8_K: returns (q, d, bsum)."""
+    nt, idim = g.shape
+    if u.shape != g.shape:
+        raise ValueError("u must have the shape of g")
+    q, d, bsum = _q8k_out(g, q, d, bsum)
+    _check(lib().qmm_silu_mul_quantize_q8k(_dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), nt, idim,
+                                           _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
+                                           _dev(bsum, torch.float32, "bsum"), _stream(stream)),
+           "qmm_silu_mul_quantize_q8k")
+    return q, d, bsum
 
 
 def qmm_residual_add(h: torch.Tensor, o: torch.Tensor, stream=None) -> torch.Tensor:

@@ -249,51 +249,96 @@ int qmm_quantize_act(const float* x, int nt, int id, int8_t* q, float* d, float*
     return launched(qmm::launch_quantize(x, nt, id, q, d, s, reinterpret_cast<hipStream_t>(stream)));
 }
 
-int qmm_add_rmsnorm_quantize(float* h, const float* o, const float* w, float eps, int nt, int id, int8_t* q,
-                             float* d, float* s, void* stream)
+// The fused producers, per-32 (q8k false) or Q8_K (q8k true: whole 256-value
+// blocks, d [nt][id/256], s = the group sums [nt][id/16]).
+static int add_rmsnorm_quantize(float* h, const float* o, const float* w, float eps, int nt, int id, int8_t* q,
+                                float* d, float* s, void* stream, bool q8k)
 {
     if (!h || !o || !w || !q || !d || !s || !eps_ok(eps))
         return QMM_ERR_ARG;
     int rc = check_rows(nt, id);
     if (rc)
         return rc;
+    if (q8k && id % 256)
+        return QMM_ERR_SHAPE;
     if (!all_aligned({h, o, w, q, d, s}))
         return QMM_ERR_ALIGN;
     if ((rc = check_device()))
         return rc;
     return launched(qmm::launch_rmsnorm(h, o, h, w, eps, nt, id, q, d, s, nullptr,
-                                        reinterpret_cast<hipStream_t>(stream)));
+                                        reinterpret_cast<hipStream_t>(stream), q8k));
 }
 
-int qmm_rmsnorm_quantize(const float* x, const float* w, float eps, int nt, int id, int8_t* q, float* d, float* s,
-                         void* stream)
+static int rmsnorm_quantize(const float* x, const float* w, float eps, int nt, int id, int8_t* q, float* d,
+                            float* s, void* stream, bool q8k)
 {
     if (!x || !w || !q || !d || !s || !eps_ok(eps))
         return QMM_ERR_ARG;
     int rc = check_rows(nt, id);
     if (rc)
         return rc;
+    if (q8k && id % 256)
+        return QMM_ERR_SHAPE;
     if (!all_aligned({x, w, q, d, s}))
         return QMM_ERR_ALIGN;
     if ((rc = check_device()))
         return rc;
     return launched(qmm::launch_rmsnorm(x, nullptr, nullptr, w, eps, nt, id, q, d, s, nullptr,
-                                        reinterpret_cast<hipStream_t>(stream)));
+                                        reinterpret_cast<hipStream_t>(stream), q8k));
 }
 
-int qmm_silu_mul_quantize(const float* g, const float* u, int nt, int id, int8_t* q, float* d, float* s,
-                          void* stream)
+static int silu_mul_quantize(const float* g, const float* u, int nt, int id, int8_t* q, float* d, float* s,
+                             void* stream, bool q8k)
 {
     if (!g || !u || !q || !d || !s)
         return QMM_ERR_ARG;
     int rc = check_rows(nt, id);
     if (rc)
         return rc;
+    if (q8k && id % 256)
+        return QMM_ERR_SHAPE;
     if (!all_aligned({g, u, q, d, s}))
         return QMM_ERR_ALIGN;
     if ((rc = check_device()))
         return rc;
-    return launched(qmm::launch_silu_mul(g, u, nt, id, q, d, s, nullptr, reinterpret_cast<hipStream_t>(stream)));
+    return launched(qmm::launch_silu_mul(g, u, nt, id, q, d, s, nullptr, reinterpret_cast<hipStream_t>(stream),
+                                         q8k));
+}
+
+int qmm_add_rmsnorm_quantize(float* h, const float* o, const float* w, float eps, int nt, int id, int8_t* q,
+                             float* d, float* s, void* stream)
+{
+    return add_rmsnorm_quantize(h, o, w, eps, nt, id, q, d, s, stream, false);
+}
+
+int qmm_rmsnorm_quantize(const float* x, const float* w, float eps, int nt, int id, int8_t* q, float* d, float* s,
+                         void* stream)
+{
+    return rmsnorm_quantize(x, w, eps, nt, id, q, d, s, stream, false);
+}
+
+int qmm_silu_mul_quantize(const float* g, const float* u, int nt, int id, int8_t* q, float* d, float* s,
+                          void* stream)
+{
+    return silu_mul_quantize(g, u, nt, id, q, d, s, stream, false);
+}
+
+int qmm_add_rmsnorm_quantize_q8k(float* h, const float* o, const float* w, float eps, int nt, int id, int8_t* q,
+                                 float* d, float* bsum, void* stream)
+{
+    return add_rmsnorm_quantize(h, o, w, eps, nt, id, q, d, bsum, stream, true);
+}
+
+int qmm_rmsnorm_quantize_q8k(const float* x, const float* w, float eps, int nt, int id, int8_t* q, float* d,
+                             float* bsum, void* stream)
+{
+    return rmsnorm_quantize(x, w, eps, nt, id, q, d, bsum, stream, true);
+}
+
+int qmm_silu_mul_quantize_q8k(const float* g, const float* u, int nt, int id, int8_t* q, float* d, float* bsum,
+                              void* stream)
+{
+    return silu_mul_quantize(g, u, nt, id, q, d, bsum, stream, true);
 }
 
 int qmm_residual_add(float* h, const float* o, int nt, int id, void* stream)

@@ -5,13 +5,15 @@
 // quantizer.  Run as separate kernels, a layer writes the normalized rows (or the
 // product silu(g) * u) to HBM and reads them back; the fused kernels quantize
 // from registers instead:
-//   rmsnorm_kernel<CH, true,  true>   residual add + RMS norm + quantize
-//   rmsnorm_kernel<CH, false, true>   RMS norm + quantize (first layer: no add)
-//   silu_mul_kernel<true>             silu(g) * u + quantize
-// The same templates with QUANT = false (plus residual_add_kernel) are the
-// unfused chain's steps: they store the f32 values, which the plain quantizer
-// then reads.  Fused and unfused evaluate the same float expressions in the same
-// order and quantize through the same quantize_lane4, so they agree bit for bit.
+//   rmsnorm_kernel<CH, true,  1>   residual add + RMS norm + quantize
+//   rmsnorm_kernel<CH, false, 1>   RMS norm + quantize (first layer: no add)
+//   silu_mul_kernel<1>             silu(g) * u + quantize
+// and with 2 in place of 1 the same steps ending in the Q8_K quantizer ([GEMM,
+// "Activations: int8 with a scale per 256"]; rows of whole 256-value blocks).
+// The same templates with 0 (plus residual_add_kernel) are the unfused chain's
+// steps: they store the f32 values, which the plain quantizer then reads.  Fused
+// and unfused evaluate the same float expressions in the same order and quantize
+// through the same quantize_lane4 / quantize_lane4_q8k, so they agree bit for bit.
 //
 // Arithmetic (the pages fix only the fused = unfused property):
 // * RMS norm, f32: 256 lane partials; lane t accumulates fma(x_i, x_i, p_t) in
@@ -25,7 +27,8 @@
 // float4 groups t, t + 256, ... (a row of up to 16384 values stays in registers,
 // longer rows are read twice, the second time from cache).  A wave's 64 lanes
 // hold 256 consecutive values = eight quantization blocks at each step, so the
-// quantizer's eight-lane groups line up with the blocks.  The cross-lane sum goes
+// quantizer's eight-lane groups line up with the blocks (for Q8_K the wave is one
+// block: rows start on a 256-value boundary).  The cross-lane sum goes
 // through LDS once (strides 128 and 64, every wave reading all 256 partials) and
 // then a butterfly inside the wave, which leaves the same total in every lane.
 // silu: one float4 per lane, the plain quantizer's layout.
@@ -76,13 +79,15 @@ __device__ __forceinline__ float rms_scale(float ss, int n, float eps)
     return 1.0f / sqrtf(ss / (float)n + eps);
 }
 
-// Store one lane's four normalized values: quantized (codes + the block's d and
-// s from the first lane of each eight) or as f32.
-template <bool QUANT>
+// Store one lane's four normalized values (float4 group gi): QM = 1 quantized per
+// 32 (codes + the block's d and s from the first lane of each eight), QM = 2 Q8_K
+// (the wave's 64 lanes are one 256-value block: codes, d from lane 0 and each
+// 16-value group's code sum into s from its quad's first lane), QM = 0 as f32.
+template <int QM>
 __device__ __forceinline__ void emit4(float4 yv, long gi, bool valid, uint32_t* __restrict__ q,
                                       float* __restrict__ d, float* __restrict__ s, float4* y)
 {
-    if constexpr (QUANT) {
+    if constexpr (QM == 1) {
         float dk, sk;
         const uint32_t codes = quantize_lane4(yv, dk, sk);
         if (valid) {
@@ -91,6 +96,17 @@ __device__ __forceinline__ void emit4(float4 yv, long gi, bool valid, uint32_t* 
                 d[gi >> 3] = dk;
                 s[gi >> 3] = sk;
             }
+        }
+    } else if constexpr (QM == 2) {
+        float dk;
+        int gsum;
+        const uint32_t codes = quantize_lane4_q8k(yv, dk, gsum);
+        if (valid) {
+            q[gi] = codes;
+            if ((threadIdx.x & 63) == 0)
+                d[gi >> 6] = dk;
+            if ((threadIdx.x & 3) == 0)
+                s[gi >> 2] = (float)gsum;
         }
     } else {
         if (valid)
@@ -102,7 +118,7 @@ __device__ __forceinline__ void emit4(float4 yv, long gi, bool valid, uint32_t* 
 // y may equal x (each lane reads its values before it writes them).
 // CH > 0: the row is held in registers, CH float4 per lane (id <= 1024 CH);
 // CH == 0: any length, the row is read a second time for the output pass.
-template <int CH, bool ADD, bool QUANT>
+template <int CH, bool ADD, int QM>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(float4* xh, const float4* __restrict__ o,
                                                       const float4* __restrict__ w, float eps, int id,
                                                       uint32_t* __restrict__ q, float* __restrict__ d,
@@ -141,7 +157,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float4* xh, const float4* 
         for (int c = 0; c < CH; ++c) {
             const int g = c * 256 + t;
             const float4 wv = w[min(g, n4 - 1)];
-            emit4<QUANT>(scale4(v[c], r, wv), rb + g, g < n4, q, d, s, y);
+            emit4<QM>(scale4(v[c], r, wv), rb + g, g < n4, q, d, s, y);
         }
     } else {
         const int nch = (n4 + 255) >> 8;
@@ -163,7 +179,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float4* xh, const float4* 
             const int gc = min(g, n4 - 1);
             const float4 a = xh[rb + gc];
             const float4 wv = w[gc];
-            emit4<QUANT>(scale4(g < n4 ? a : zero, r, wv), rb + g, g < n4, q, d, s, y);
+            emit4<QM>(scale4(g < n4 ? a : zero, r, wv), rb + g, g < n4, q, d, s, y);
         }
     }
 }
@@ -184,7 +200,7 @@ __device__ __forceinline__ float silu_mul1(float g, float u)
 }
 
 // n4 = nt * id / 4 float4 groups; a multiple of eight (id % 32 == 0).
-template <bool QUANT>
+template <int QM>
 __global__ __launch_bounds__(256) void silu_mul_kernel(const float4* __restrict__ g, const float4* __restrict__ u,
                                                        long n4, uint32_t* __restrict__ q, float* __restrict__ d,
                                                        float* __restrict__ s, float4* __restrict__ y)
@@ -196,10 +212,10 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const float4* __restrict_
     const float4 b = u[ic];
     const float4 v = make_float4(silu_mul1(a.x, b.x), silu_mul1(a.y, b.y), silu_mul1(a.z, b.z),
                                  silu_mul1(a.w, b.w));
-    emit4<QUANT>(v, i, valid, q, d, s, y);
+    emit4<QM>(v, i, valid, q, d, s, y);
 }
 
-template <bool ADD, bool QUANT>
+template <bool ADD, int QM>
 hipError_t launch_rms(int ch, float* xh, const float* o, const float* w, float eps, int nt, int id, int8_t* q,
                       float* d, float* s, float* y, hipStream_t st)
 {
@@ -210,12 +226,12 @@ hipError_t launch_rms(int ch, float* xh, const float* o, const float* w, float e
     auto Y = reinterpret_cast<float4*>(y);
     const dim3 grid(nt), block(256);
     switch (ch) {
-    case 1: hipLaunchKernelGGL((rmsnorm_kernel<1, ADD, QUANT>), grid, block, 0, st, X, O, Wv, eps, id, Q, d, s, Y); break;
-    case 2: hipLaunchKernelGGL((rmsnorm_kernel<2, ADD, QUANT>), grid, block, 0, st, X, O, Wv, eps, id, Q, d, s, Y); break;
-    case 4: hipLaunchKernelGGL((rmsnorm_kernel<4, ADD, QUANT>), grid, block, 0, st, X, O, Wv, eps, id, Q, d, s, Y); break;
-    case 8: hipLaunchKernelGGL((rmsnorm_kernel<8, ADD, QUANT>), grid, block, 0, st, X, O, Wv, eps, id, Q, d, s, Y); break;
-    case 16: hipLaunchKernelGGL((rmsnorm_kernel<16, ADD, QUANT>), grid, block, 0, st, X, O, Wv, eps, id, Q, d, s, Y); break;
-    default: hipLaunchKernelGGL((rmsnorm_kernel<0, ADD, QUANT>), grid, block, 0, st, X, O, Wv, eps, id, Q, d, s, Y); break;
+    case 1: hipLaunchKernelGGL((rmsnorm_kernel<1, ADD, QM>), grid, block, 0, st, X, O, Wv, eps, id, Q, d, s, Y); break;
+    case 2: hipLaunchKernelGGL((rmsnorm_kernel<2, ADD, QM>), grid, block, 0, st, X, O, Wv, eps, id, Q, d, s, Y); break;
+    case 4: hipLaunchKernelGGL((rmsnorm_kernel<4, ADD, QM>), grid, block, 0, st, X, O, Wv, eps, id, Q, d, s, Y); break;
+    case 8: hipLaunchKernelGGL((rmsnorm_kernel<8, ADD, QM>), grid, block, 0, st, X, O, Wv, eps, id, Q, d, s, Y); break;
+    case 16: hipLaunchKernelGGL((rmsnorm_kernel<16, ADD, QM>), grid, block, 0, st, X, O, Wv, eps, id, Q, d, s, Y); break;
+    default: hipLaunchKernelGGL((rmsnorm_kernel<0, ADD, QM>), grid, block, 0, st, X, O, Wv, eps, id, Q, d, s, Y); break;
     }
     return hipGetLastError();
 }
@@ -225,18 +241,20 @@ hipError_t launch_rms(int ch, float* xh, const float* o, const float* w, float e
 // o != null: residual add (h = x updated in place).  q != null: quantize, else
 // store y.  The unfused chain never combines the add with an f32 output.
 hipError_t launch_rmsnorm(const float* x, const float* o, float* h, const float* w, float eps, int nt, int id,
-                          int8_t* q, float* d, float* s, float* y, hipStream_t st)
+                          int8_t* q, float* d, float* s, float* y, hipStream_t st, bool q8k)
 {
     if (nt == 0)
         return hipSuccess;
     const int nch = (id / 4 + 255) / 256;
     const int ch = nch <= 1 ? 1 : nch <= 2 ? 2 : nch <= 4 ? 4 : nch <= 8 ? 8 : nch <= 16 ? 16 : 0;
     if (o)
-        return launch_rms<true, true>(ch, h, o, w, eps, nt, id, q, d, s, nullptr, st);
+        return q8k ? launch_rms<true, 2>(ch, h, o, w, eps, nt, id, q, d, s, nullptr, st)
+                   : launch_rms<true, 1>(ch, h, o, w, eps, nt, id, q, d, s, nullptr, st);
     float* xh = const_cast<float*>(x);  // read only when there is no add
     if (q)
-        return launch_rms<false, true>(ch, xh, nullptr, w, eps, nt, id, q, d, s, nullptr, st);
-    return launch_rms<false, false>(ch, xh, nullptr, w, eps, nt, id, nullptr, nullptr, nullptr, y, st);
+        return q8k ? launch_rms<false, 2>(ch, xh, nullptr, w, eps, nt, id, q, d, s, nullptr, st)
+                   : launch_rms<false, 1>(ch, xh, nullptr, w, eps, nt, id, q, d, s, nullptr, st);
+    return launch_rms<false, 0>(ch, xh, nullptr, w, eps, nt, id, nullptr, nullptr, nullptr, y, st);
 }
 
 hipError_t launch_residual_add(float* h, const float* o, long n, hipStream_t st)
@@ -251,7 +269,7 @@ hipError_t launch_residual_add(float* h, const float* o, long n, hipStream_t st)
 }
 
 hipError_t launch_silu_mul(const float* g, const float* u, int nt, int id, int8_t* q, float* d, float* s, float* y,
-                           hipStream_t st)
+                           hipStream_t st, bool q8k)
 {
     const long n4 = (long)nt * id / 4;
     const long grid = (n4 + 255) / 256;
@@ -259,11 +277,14 @@ hipError_t launch_silu_mul(const float* g, const float* u, int nt, int id, int8_
         return hipSuccess;
     auto G = reinterpret_cast<const float4*>(g);
     auto U = reinterpret_cast<const float4*>(u);
-    if (q)
-        hipLaunchKernelGGL(silu_mul_kernel<true>, dim3((unsigned)grid), dim3(256), 0, st, G, U, n4,
+    if (q && q8k)
+        hipLaunchKernelGGL(silu_mul_kernel<2>, dim3((unsigned)grid), dim3(256), 0, st, G, U, n4,
+                           reinterpret_cast<uint32_t*>(q), d, s, nullptr);
+    else if (q)
+        hipLaunchKernelGGL(silu_mul_kernel<1>, dim3((unsigned)grid), dim3(256), 0, st, G, U, n4,
                            reinterpret_cast<uint32_t*>(q), d, s, nullptr);
     else
-        hipLaunchKernelGGL(silu_mul_kernel<false>, dim3((unsigned)grid), dim3(256), 0, st, G, U, n4, nullptr,
+        hipLaunchKernelGGL(silu_mul_kernel<0>, dim3((unsigned)grid), dim3(256), 0, st, G, U, n4, nullptr,
                            nullptr, nullptr, reinterpret_cast<float4*>(y));
     return hipGetLastError();
 }

@@ -49,11 +49,13 @@ hipError_t launch_mmq_q8k(int type, const uint8_t* W, const int8_t* q, const flo
 // Producer-side steps that feed the quantizer (qmm_fused.hip).  Rows are [nt][id]
 // f32, id % 32 == 0; q/d/s as for launch_quantize.  With q == null the kernels
 // store the f32 values y instead of quantizing them (the unfused chain's steps).
+// q8k: quantize to Q8_K instead (id % 256 == 0; d [nt][id/256], s = the group
+// sums bsum [nt][id/16], as launch_quantize_q8k).
 hipError_t launch_rmsnorm(const float* x, const float* o, float* h, const float* w, float eps, int nt,
-                          int id, int8_t* q, float* d, float* s, float* y, hipStream_t st);
+                          int id, int8_t* q, float* d, float* s, float* y, hipStream_t st, bool q8k = false);
 hipError_t launch_residual_add(float* h, const float* o, long n, hipStream_t st);
 hipError_t launch_silu_mul(const float* g, const float* u, int nt, int id, int8_t* q, float* d, float* s,
-                           float* y, hipStream_t st);
+                           float* y, hipStream_t st, bool q8k = false);
 hipError_t launch_mfma_tile_probe(int kind, const void* A, const void* B, void* C, hipStream_t st);
 
 // ---------------------------------------------------------------- device helpers
@@ -106,6 +108,39 @@ __device__ __forceinline__ uint32_t quantize_lane4(float4 v, float& dk, float& s
     sum += dpp_quad_xor2(sum);
     sum += dpp_half_mirror(sum);
     sk = dk * (float)sum;
+    return (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
+           ((uint32_t)(q3 & 0xFF) << 24);
+}
+
+// One lane's share of the Q8_K activation quantizer ([GEMM, "Activations: int8
+// with a scale per 256"]): the 64 lanes of a wave hold one 256-value block, four
+// consecutive values each, and all make the call together.  Same rules as
+// quantize_lane4 over 256 values: d = amax / 127, codes round(v / d) half away
+// from zero, a zero block gives d = q = 0.  gsum: the sum of the codes of this
+// lane's 16-value group (its quad).  The plain Q8_K quantizer and the
+// producer-fused kernels both quantize through this function.
+__device__ __forceinline__ uint32_t quantize_lane4_q8k(float4 v, float& dk, int& gsum)
+{
+    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+    int ai = __builtin_bit_cast(int, a);  // non-negative floats order like their bits
+    ai = max(ai, dpp_quad_xor1(ai));
+    ai = max(ai, dpp_quad_xor2(ai));
+    ai = max(ai, dpp_half_mirror(ai));
+    ai = max(ai, dpp_row_mirror(ai));
+    ai = max(ai, __shfl_xor(ai, 16));
+    ai = max(ai, __shfl_xor(ai, 32));
+    dk = __builtin_bit_cast(float, ai) / 127.0f;
+    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
+    if (dk != 0.0f) {
+        q0 = (int)roundf(v.x / dk);
+        q1 = (int)roundf(v.y / dk);
+        q2 = (int)roundf(v.z / dk);
+        q3 = (int)roundf(v.w / dk);
+    }
+    int sum = q0 + q1 + q2 + q3;
+    sum += dpp_quad_xor1(sum);
+    sum += dpp_quad_xor2(sum);
+    gsum = sum;
     return (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
            ((uint32_t)(q3 & 0xFF) << 24);
 }

@@ -58,28 +58,11 @@ __global__ __launch_bounds__(256) void quantize_q8k_kernel(const float4* __restr
     if (!valid)
         v = make_float4(0.f, 0.f, 0.f, 0.f);
 
-    float a = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    int ai = __builtin_bit_cast(int, a);
-    ai = max(ai, dpp_quad_xor1(ai));
-    ai = max(ai, dpp_quad_xor2(ai));
-    ai = max(ai, dpp_half_mirror(ai));
-    ai = max(ai, dpp_row_mirror(ai));
-    ai = max(ai, __shfl_xor(ai, 16));
-    ai = max(ai, __shfl_xor(ai, 32));
-    const float dk = __builtin_bit_cast(float, ai) / 127.0f;
-    int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
-    if (dk != 0.0f) {
-        q0 = (int)roundf(v.x / dk);
-        q1 = (int)roundf(v.y / dk);
-        q2 = (int)roundf(v.z / dk);
-        q3 = (int)roundf(v.w / dk);
-    }
-    int sum = q0 + q1 + q2 + q3;
-    sum += dpp_quad_xor1(sum);
-    sum += dpp_quad_xor2(sum);
+    float dk;
+    int sum;
+    const uint32_t codes = quantize_lane4_q8k(v, dk, sum);
     if (valid) {
-        q[g] = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
-               ((uint32_t)(q3 & 0xFF) << 24);
+        q[g] = codes;
         if (lane == 0)
             d[blk] = dk;
         if ((lane & 3) == 0)

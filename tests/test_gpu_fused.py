@@ -10,7 +10,10 @@ gives.  Checked here, every comparison bit for bit:
 * the chain's f32 values == the oracle's (fixed f32 sum order for the norm; f64
   silu * u rounded once);
 * fused q, d, s == the oracle quantizer applied to the oracle's f32 values;
-* the updated residual h == the oracle's h + o.
+* the updated residual h == the oracle's h + o;
+* the Q8_K variants (the same steps ending in the Q8_K quantizer): q, d and the
+  16-value group sums == the chain ending in qmm_quantize_act_q8k and == the
+  oracle's Q8_K quantizer on the oracle's f32 values.
 
 Shapes cover every register-resident row length class (up to 16384 values), the
 two-pass path for longer rows, ragged row lengths (not a multiple of 1024), one
@@ -218,3 +221,80 @@ def test_fused_feeds_matmul():
         b = qmm.qmm_matmul_q8(qtype, W, q2, d2, s2, od)
         torch.cuda.synchronize()
         _same(_host(a), _host(b), f"type {qtype} matmul on fused vs chain activations")
+
+
+# ---- the same steps ending in the Q8_K quantizer (one scale per 256 values):
+# fused q, d, bsum == the unfused chain (step, then qmm_quantize_act_q8k) on the
+# GPU and == the oracle's Q8_K quantizer applied to the oracle's f32 values; rows
+# of whole 256-value blocks (register-resident and two-pass lengths).
+Q8K_NORM_SHAPES = [(1, 256), (3, 1024), (7, 4096), (2, 12288), (1, 16384), (2, 20480), (64, 4096), (512, 4096),
+                   (5, 2304)]
+Q8K_SILU_SHAPES = [(1, 256), (3, 768), (8, 12288), (13, 4352), (512, 12288)]
+
+
+@pytest.mark.parametrize("nt,idim", Q8K_NORM_SHAPES, ids=[f"{a}x{b}" for a, b in Q8K_NORM_SHAPES])
+def test_add_rmsnorm_quantize_q8k(nt, idim):
+    _say(f"add_rmsnorm_quantize_q8k nt={nt} id={idim}")
+    eps = 1e-5
+    h = _rows(nt, idim, 1100 + idim + nt)
+    o = _rows(nt, idim, 1200 + idim + nt, scale=0.5)
+    w = _weight(idim, 1300 + idim)
+    ref_h, ref_y = oracle.add_rmsnorm(h, o, w, eps)
+    ref = oracle.quantize_q8k(ref_y)
+    hf, ot, wt = _up(h), _up(o), _up(w)
+    got = qmm.qmm_add_rmsnorm_quantize_q8k(hf, ot, wt, eps)
+    hc = _up(h)
+    qmm.qmm_residual_add(hc, ot)
+    chain = qmm.qmm_quantize_act_q8k(qmm.qmm_rmsnorm(hc, wt, eps))
+    torch.cuda.synchronize()
+    _same(_host(hf), ref_h, "fused residual h + o")
+    for name, g, c, r in zip(("q", "d", "bsum"), got, chain, ref):
+        _same(_host(g), _host(c), f"fused vs chain {name}")
+        _same(_host(g), r, f"fused vs oracle {name}")
+
+
+@pytest.mark.parametrize("nt,idim", Q8K_NORM_SHAPES, ids=[f"{a}x{b}" for a, b in Q8K_NORM_SHAPES])
+def test_rmsnorm_quantize_q8k(nt, idim):
+    _say(f"rmsnorm_quantize_q8k nt={nt} id={idim}")
+    eps = 1e-6
+    x = _rows(nt, idim, 1400 + idim + nt, scale=3.0)
+    w = _weight(idim, 1500 + idim)
+    ref = oracle.quantize_q8k(oracle.rmsnorm(x, w, eps))
+    xt, wt = _up(x), _up(w)
+    got = qmm.qmm_rmsnorm_quantize_q8k(xt, wt, eps)
+    chain = qmm.qmm_quantize_act_q8k(qmm.qmm_rmsnorm(xt, wt, eps))
+    torch.cuda.synchronize()
+    _same(_host(xt), x, "input unchanged")
+    for name, g, c, r in zip(("q", "d", "bsum"), got, chain, ref):
+        _same(_host(g), _host(c), f"fused vs chain {name}")
+        _same(_host(g), r, f"fused vs oracle {name}")
+
+
+@pytest.mark.parametrize("nt,idim", Q8K_SILU_SHAPES, ids=[f"{a}x{b}" for a, b in Q8K_SILU_SHAPES])
+def test_silu_mul_quantize_q8k(nt, idim):
+    _say(f"silu_mul_quantize_q8k nt={nt} id={idim}")
+    g = _rows(nt, idim, 1600 + idim + nt, scale=2.0)
+    u = _rows(nt, idim, 1700 + idim + nt)
+    ref = oracle.quantize_q8k(oracle.silu_mul(g, u))
+    gt, ut = _up(g), _up(u)
+    got = qmm.qmm_silu_mul_quantize_q8k(gt, ut)
+    chain = qmm.qmm_quantize_act_q8k(qmm.qmm_silu_mul(gt, ut))
+    torch.cuda.synchronize()
+    for name, gg, c, r in zip(("q", "d", "bsum"), got, chain, ref):
+        _same(_host(gg), _host(c), f"fused vs chain {name}")
+        _same(_host(gg), r, f"fused vs oracle {name}")
+
+
+def test_q8k_fused_zero_rows_and_shape_errors():
+    """A zero row gives d = q = bsum = 0; rows that are not whole 256-value blocks
+    are refused."""
+    x = _rows(2, 512, 1800)
+    x[1] = 0.0
+    q, d, bs = qmm.qmm_rmsnorm_quantize_q8k(_up(x), _up(_weight(512, 1801)), 1e-5)
+    torch.cuda.synchronize()
+    assert not _host(q)[1].any() and not _host(d)[1].any() and not _host(bs)[1].any()
+    for fn, args in ((qmm.qmm_rmsnorm_quantize_q8k, (_up(_rows(1, 288, 1802)), _up(_weight(288, 1803)), 1e-5)),
+                     (qmm.qmm_silu_mul_quantize_q8k, (_up(_rows(1, 288, 1804)), _up(_rows(1, 288, 1805))))):
+        with pytest.raises(qmm.QmmError) as e:
+            fn(*args)
+        assert e.value.status == qmm.QMM_ERR_SHAPE

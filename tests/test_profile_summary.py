@@ -19,8 +19,8 @@ def test_sources_hash_only_for_library_kernels():
     assert ps.sources_sha256("qmm::mmq_k4_q8k_kernel<4, 2, 1, false, false>") != ps.sources_sha256("qmm::mmq_q4k_kernel<4, 2, 1, false>")
     assert ps.sources_sha256("qmm::mmq_q6k_q8k_kernel<4, 2, false, true>") == \
         ps.sources_sha256("qmm::mmq_k4_q8k_kernel<4, 2, 1, false, false>")
-    fused = ps.sources_sha256("qmm::{anonymous}::silu_mul_kernel<true>")
-    assert fused is not None and fused == ps.sources_sha256("qmm::{anonymous}::rmsnorm_kernel<4, true, true>")
+    fused = ps.sources_sha256("qmm::{anonymous}::silu_mul_kernel<1>")
+    assert fused is not None and fused == ps.sources_sha256("qmm::{anonymous}::rmsnorm_kernel<4, true, 1>")
     assert ps.short_name("void qmm::(anonymous namespace)::silu_mul_kernel<true>(HIP_vector_type<float, 4u> const*)") \
         == "qmm::{anonymous}::silu_mul_kernel<true>"
 
