@@ -5,10 +5,11 @@ memset, no synchronisation), so a caller can capture a whole step -- quantize, t
 producer-fused quantize, the vector kernel, its 8-token slices and the matrix
 kernel with and without the split over K -- into one HIP graph and replay it.
 The stream-K kernel and its fixup (three launches sharing one workspace) are in
-the step too.  Checked here: the graph is replayed several times, with other GPU
-work and host synchronisation between replays and the outputs cleared before
-each, and every output of every replay equals the eagerly computed one (the
-kernels are deterministic: no atomics, fixed reduction orders).
+the step too, and the Q8_K path (a fused RMS-norm Q8_K quantize, a Q4_K matmul
+split over K, a padded Q6_K matmul).  Checked here: the graph is replayed several
+times, with other GPU work and host synchronisation between replays and the
+outputs cleared before each, and every output of every replay equals the eagerly
+computed one (the kernels are deterministic: no atomics, fixed reduction orders).
 """
 from __future__ import annotations
 
@@ -60,6 +61,13 @@ class Step:
         self.skout = [torch.empty(4, 4096, dtype=torch.float32, device=DEV),
                       torch.empty(64, 4096, dtype=torch.float32, device=DEV),
                       torch.empty(64, 1000, dtype=torch.float32, device=DEV)]
+        # the Q8_K path: a fused RMS-norm Q8_K quantize feeding a Q4_K matmul split
+        # over K (4096 x 4096 at 16 tokens) and a padded Q6_K matmul
+        self.kq = torch.empty(16, 4096, dtype=torch.int8, device=DEV)
+        self.kd = torch.empty(16, 16, dtype=torch.float32, device=DEV)
+        self.kb = torch.empty(16, 256, dtype=torch.float32, device=DEV)
+        self.kout = [torch.empty(16, 4096, dtype=torch.float32, device=DEV),
+                     torch.empty(16, 1000, dtype=torch.float32, device=DEV)]
 
     def issue(self):
         for qt, od, W, x, q, d, s, out in self.items:
@@ -72,25 +80,29 @@ class Step:
                                           (qmm.QMM_TYPE_Q6_K_P224, self.skW6) + self.items[2][4:7]),
                                          self.skout):
             qmm.qmm_matmul_q8_streamk(qt, W, q, d, s, out.shape[1], self.ws, out=out)
+        qmm.qmm_rmsnorm_quantize_q8k(self.h, self.w, 1e-5, self.kq, self.kd, self.kb)
+        qmm.qmm_matmul_q8k(qmm.QMM_TYPE_Q4_K, self.fW, self.kq, self.kd, self.kb, 4096, out=self.kout[0])
+        qmm.qmm_matmul_q8k(qmm.QMM_TYPE_Q6_K_P224, self.skW6, self.kq, self.kd, self.kb, 1000, out=self.kout[1])
 
     def outputs(self):
         res = []
         for item in self.items:
             res += [t.clone() for t in item[4:]]
         return res + [self.fq.clone(), self.fd.clone(), self.fs.clone(), self.fout.clone()] + \
-            [t.clone() for t in self.skout]
+            [t.clone() for t in self.skout] + [t.clone() for t in (self.kq, self.kd, self.kb, *self.kout)]
 
     def clear(self):
         # eager fill kernels (not recorded in the graph)
         for item in self.items:
             for t in item[4:]:
                 t.zero_()
-        for t in (self.fq, self.fd, self.fs, self.fout, *self.skout):
+        for t in (self.fq, self.fd, self.fs, self.fout, *self.skout, self.kq, self.kd, self.kb, *self.kout):
             t.zero_()
 
 
 def test_graph_replays_match_eager():
-    print("graph replay: capture a step of 5 quantize, 5 matmul and 3 stream-K calls", flush=True)
+    print("graph replay: capture a step of 5 quantize, 5 matmul, 3 stream-K and 3 Q8_K calls", flush=True)
+    assert qmm.qmm_q8k_tile(16, 4096, 4096) == qmm.QMM_KIND_MMQ_64X64_SPLITK
     assert qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q6_K, 12, 4096, 4096) == qmm.QMM_KIND_MMVQ
     assert qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q4_K, 64, 4096, 4096) == qmm.QMM_KIND_MMQ
     step = Step()
