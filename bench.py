@@ -731,6 +731,9 @@ def main():
         tb = sum(c.kbytes for c in dec)
         tt = sum(float(np.mean(c.k_ms)) * 1e-3 for c in dec)
         line.update(value=round(tb / tt / 1e9, 1), unit="GB/s")
+        # the same bytes over quantize + MMVQ time: the whole decode call
+        tq = sum(float(np.mean(c.q_ms)) * 1e-3 for c in dec)
+        line["decode_with_quantize_GB_s"] = round(tb / (tt + tq) / 1e9, 1)
         head = max(dec, key=lambda c: c.od)
         kh = float(np.mean(head.k_ms)) * 1e-3
         line["roofline"] = {"bound": "hbm", "achieved": round(head.kbytes / kh / 1e9, 1), "peak": HBM_PEAK_GBS,
