@@ -638,8 +638,9 @@ def cpu_baseline(calls):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(a row-sharded design is described in DESIGN.md)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path; across "
+              "GPUs each one would hold a slice of the weight rows and run these same kernels "
+              "on it, with the outputs gathered afterwards", file=sys.stderr)
         sys.exit(2)
     import torch
     import quantized_matmul_amd as qmm
