@@ -100,8 +100,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="q4k_decode_prefill",
                     choices=["q4k_decode_prefill", "q6k_head", "dllm_step", "fused_quantize", "q8k_prefill",
-                             "formats", "streamk"])
+                             "formats", "streamk", "peaks"])
+    ap.add_argument("--chunk", type=int, default=CHUNK, help="launches per event-timed chunk")
+    ap.add_argument("--spread-chunks", type=int, default=8,
+                    help="event-timed chunks per call after the timed region, for the median and p10/p90")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dllm", action="store_true", help="default workload: skip the diffusion-LM step graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB")
     return ap.parse_args()
 
@@ -145,8 +149,10 @@ class Call:
         self.qtype, self.od, self.idim, self.nt, self.q8k = qtype, od, idim, nt, q8k
         self.label = label or f"{'Q4_K' if qtype == 1 else 'Q6_K'} {od}x{idim} nt={nt}" + (" Q8_K" if q8k else "")
         dev = torch.device("cuda:0")
+        self.w_host = None   # host bytes of the weights when generated here (for the CPU baseline)
         if copies is None:
-            w = torch.from_numpy(synth.weights(qtype, od, idim, seed=seed)).to(dev)
+            self.w_host = synth.weights(qtype, od, idim, seed=seed)
+            w = torch.from_numpy(self.w_host).to(dev)
             n = max(1, -(-COPY_BYTES // w.numel()))
             copies = [w] + [w.clone() for _ in range(n - 1)]
         self.W = copies
@@ -328,17 +334,31 @@ def build_calls(torch, qmm, workload):
         return sk_ws[0]
 
     if workload == "q4k_decode_prefill":
+        # the decode GEMV of one 1024 x 4096 matrix
+        calls.append(Call(torch, qmm, Q4, 1024, 4096, 1, seed=0, outliers=False))
         shared = {}
         for od, idim in ((4096, 4096), (12288, 4096)):
             for nt in (1, 4, 8):
                 c = Call(torch, qmm, Q4, od, idim, nt, seed=10 * nt + od, outliers=False,
                          copies=shared.get((od, idim)))
-                shared[(od, idim)] = c.W
+                if (od, idim) not in shared:
+                    shared[(od, idim)] = c.W
+                    shared[("host", od, idim)] = c.w_host
+                c.w_host = shared[("host", od, idim)]
                 calls.append(c)
-        calls.append(Call(torch, qmm, Q4, 12288, 4096, 512, seed=7, outliers=True, copies=shared[(12288, 4096)],
-                          streamk=path_ws(Q4, 512, 12288, 4096)))
-        calls.append(Call(torch, qmm, Q4, 4096, 12288, 512, seed=8, outliers=True,
-                          streamk=path_ws(Q4, 512, 4096, 12288)))
+        # the Q6_K output projection, as stored (210-byte blocks) and padded to 224 bytes
+        c6 = Call(torch, qmm, Q6, 32000, 4096, 1, seed=3, outliers=False)
+        calls.append(c6)
+        calls.append(Call(torch, qmm, qmm.QMM_TYPE_Q6_K_P224, 32000, 4096, 1, seed=3, outliers=False,
+                          copies=[qmm.qmm_pad_q6k(w) for w in c6.W], x=c6.x, label="Q6_K padded 32000x4096 nt=1"))
+        # prefill: per-32 activations (the path), then the same weights and inputs on Q8_K activations
+        pa = Call(torch, qmm, Q4, 12288, 4096, 512, seed=7, outliers=True, copies=shared[(12288, 4096)],
+                  streamk=path_ws(Q4, 512, 12288, 4096))
+        pa.w_host = shared[("host", 12288, 4096)]
+        pb = Call(torch, qmm, Q4, 4096, 12288, 512, seed=8, outliers=True, streamk=path_ws(Q4, 512, 4096, 12288))
+        calls += [pa, pb]
+        for c in (pa, pb):
+            calls.append(Call(torch, qmm, Q4, c.od, c.idim, 512, seed=0, outliers=True, copies=c.W, x=c.x, q8k=True))
     elif workload == "q8k_prefill":
         # the prefill shapes on both activation schemes, same weights and inputs
         for od, idim, seed in ((12288, 4096, 7), (4096, 12288, 8)):
@@ -390,17 +410,19 @@ def build_calls(torch, qmm, workload):
         # per projection
         per_proj = []
         for p, (qt, od, idim) in enumerate(shapes):
-            w = torch.from_numpy(synth.weights(Q6 if qt == P6 else qt, od, idim, seed=100 + p)).to("cuda:0")
+            host = synth.weights(Q6 if qt == P6 else qt, od, idim, seed=100 + p)
+            w = torch.from_numpy(host).to("cuda:0")
             if qt == P6:
                 w = qmm.qmm_pad_q6k(w)
             x = torch.from_numpy(synth.activations(256, idim, seed=200 + p)).to("cuda:0")
-            per_proj.append(([w] + [w.clone() for _ in range(31)], x))
+            per_proj.append(([w] + [w.clone() for _ in range(31)], x, host if qt == Q4 else None))
         for layer in range(32):
             for p, (qt, od, idim) in enumerate(shapes):
-                copies, x = per_proj[p]
-                calls.append(Call(torch, qmm, qt, od, idim, 256, seed=0, outliers=False, copies=[copies[layer]],
-                                  label=f"layer{layer} proj{p} {od}x{idim}", x=x,
-                                  streamk=path_ws(qt, 256, od, idim)))
+                copies, x, host = per_proj[p]
+                c = Call(torch, qmm, qt, od, idim, 256, seed=0, outliers=False, copies=[copies[layer]],
+                         label=f"layer{layer} proj{p} {od}x{idim}", x=x, streamk=path_ws(qt, 256, od, idim))
+                c.w_host = host if layer == 0 else None   # the CPU baseline times layer 0's Q4_K projections
+                calls.append(c)
     return calls
 
 
@@ -518,7 +540,7 @@ def fused_cpu_baseline(calls):
 
 
 def run_fused(args, torch, qmm):
-    from quantized_matmul_amd.profile_summary import read_traffic
+    from profile_summary import read_traffic
 
     calls = []
     for op, idim in (("add_rmsnorm_quantize", 4096), ("rmsnorm_quantize", 4096), ("silu_mul_quantize", 12288)):
@@ -590,49 +612,244 @@ def run_fused(args, torch, qmm):
     print(json.dumps(line), flush=True)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _median_rate(fn, units, min_s):
+    """Median over 3 timing loops (each at least min_s seconds of calls to fn) of units per
+    second, and the three rates."""
+    rates = []
+    for _ in range(3):
+        t, u = 0.0, 0.0
+        while t < min_s:
+            t0 = time.perf_counter()
+            fn()
+            t += time.perf_counter() - t0
+            u += units
+        rates.append(u / t)
+    return float(np.median(rates)), rates
+
+
 def cpu_baseline(calls):
-    """The CPU oracle as it stands, on a bounded sample of the same workload."""
+    """The CPU oracle as it stands (plain C, -O2, OpenMP over output rows) on a bounded
+    sample of the same workload, on one thread and on every thread OpenMP starts;
+    each figure the median of 3 timing loops.  Decode: quantize + matmul of every nt = 1
+    call (GB/s of the same algorithmic bytes as the GPU line).  Prefill: quantize +
+    matmul of the first rows of the largest nt >= 9 per-32 call (int8 TOP/s)."""
     import oracle
     oracle.build(force=False)
-    res = {"kind": "oracle", "cores": oracle.num_threads()}
-    dec = [c for c in calls if c.nt == 1 and c.qtype != 3]  # the padded copy of a matrix is not re-timed
-    big = [c for c in calls if c.nt >= 9]
-    if dec:
-        nbytes, t_total, reps = 0.0, 0.0, 0
-        data = [(c, synth.weights(c.qtype, c.od, c.idim, seed=10 * c.nt + c.od if c.qtype == 1 else 3),
-                 c.x.cpu().numpy()) for c in dec]
-        while t_total < 5.0:
-            for c, W, x in data:
-                t0 = time.perf_counter()
-                oracle.matmul(c.qtype, W, x, c.od)
-                t_total += time.perf_counter() - t0
-                nbytes += c.kbytes
-            reps += 1
-        res.update(value=nbytes / t_total / 1e9, unit="GB/s",
-                   sample=f"quantize + matmul of every nt=1 call ({', '.join(c.label for c in dec)}), "
-                          f"repeated {reps}x, {t_total:.1f} s")
+    allc = oracle.num_threads()
+    dec = [c for c in calls if c.nt == 1 and c.w_host is not None]
+    big = [c for c in calls if c.nt >= 9 and not c.q8k and c.w_host is not None]
+    res = {"kind": "oracle", "cores": allc, "cpu_model": _cpu_model(), "nproc": os.cpu_count(),
+           "timing": "median of 3 loops per figure, compute only (inputs on the host)"}
+    data = [(c, c.x.cpu().numpy()) for c in dec]
+    if not dec and not big:
+        return {"kind": "oracle", "cores": allc, "cpu_model": _cpu_model(), "value": None, "unit": None,
+                "sample": "none: no call of this workload keeps host weights"}
+    pre = None
     if big:
-        c = next((b for b in big if b.q8k), big[0])  # the Q8_K oracle where the workload runs Q8_K
-        rows = 1024 if c.nt >= 512 else 2048
-        bpr = c.wbytes // c.od
-        W = synth.weights(c.qtype, c.od, c.idim, seed=7)[: rows * bpr]
-        x = c.x.cpu().numpy()
-        ops, t_total, reps = 0.0, 0.0, 0
-        while t_total < 5.0:
-            t0 = time.perf_counter()
-            if c.q8k:
-                oracle.matmul_q8k(c.qtype, W, *oracle.quantize_q8k(x), rows)
-            else:
-                oracle.matmul(c.qtype, W, x, rows)
-            t_total += time.perf_counter() - t0
-            ops += 2.0 * c.nt * rows * c.idim
-            reps += 1
-        res["mmq_value"] = ops / t_total / 1e12
-        res["mmq_unit"] = "TOP/s"
-        res["mmq_sample"] = f"quantize + matmul of {c.label} on its first {rows} rows, repeated {reps}x, {t_total:.1f} s"
-        if "value" not in res:
-            res.update(value=res["mmq_value"], unit="TOP/s", sample=res["mmq_sample"])
+        c = max(big, key=lambda b: b.ops)
+        pre = (c, c.x.cpu().numpy(), c.wbytes // c.od)
+    try:
+        for threads, key in ((1, "single_thread"), (allc, "all_cores")):
+            oracle.set_num_threads(threads)
+            row = {"threads": threads}
+            if data:
+                nbytes = sum(c.kbytes for c, _ in data)
+                v, runs = _median_rate(lambda: [oracle.matmul(c.qtype, c.w_host, x, c.od) for c, x in data],
+                                       nbytes, 1.5)
+                row.update(GB_s=round(v / 1e9, 3), GB_s_runs=[round(r / 1e9, 3) for r in runs])
+            if pre is not None:
+                c, x, bpr = pre
+                rows = 64 if threads == 1 else 64 * threads
+                W = c.w_host[: rows * bpr]
+                v, runs = _median_rate(lambda: oracle.matmul(c.qtype, W, x, rows), 2.0 * c.nt * rows * c.idim, 1.0)
+                row.update(TOP_s=round(v / 1e12, 5), TOP_s_runs=[round(r / 1e12, 5) for r in runs],
+                           prefill_rows=rows)
+            res[key] = row
+    finally:
+        oracle.set_num_threads(allc)
+    a = res["all_cores"]
+    if "GB_s" in a:
+        res.update(value=a["GB_s"], unit="GB/s")
+    else:
+        res.update(value=a["TOP_s"], unit="TOP/s")
+    parts = []
+    if data:
+        parts.append(f"decode: quantize + matmul of every nt=1 call ({', '.join(c.label for c, _ in data)})")
+    if pre is not None:
+        parts.append(f"prefill: quantize + matmul of {pre[0].label} on its first 64 rows per thread")
+    res["sample"] = "; ".join(parts)
+    if pre is not None:
+        res["mmq_value"], res["mmq_unit"] = a["TOP_s"], "TOP/s"
     return res
+
+
+def kms(c):
+    """Mean per-launch matmul kernel time of a call over the timed region, in seconds."""
+    return float(np.mean(c.k_ms)) * 1e-3
+
+
+def report_default(line, calls, qmm, torch, read_traffic):
+    """The default workload's line: value = Q4_K MMVQ GB/s at nt = 1 over the 4096 x 4096
+    and 12288 x 4096 calls; roofline = the 12288 x 4096 one; mmq = the per-32 matrix
+    kernel at nt = 512 (int8 TOP/s); mmq_q8k = the Q8_K matrix kernel on the same
+    weights and inputs; q6k_head and gemv_1024x4096 the Q6_K output projection and
+    the small decode GEMV; measured = the GPU's measured limits (bench_peaks), each
+    roofline also given as a fraction of them."""
+    import bench_peaks
+
+    Q4 = qmm.QMM_TYPE_Q4_K
+    dec = [c for c in calls if c.nt == 1 and c.qtype == Q4 and c.od in (4096, 12288)]
+    tb = sum(c.kbytes for c in dec)
+    tt = sum(kms(c) for c in dec)
+    line.update(value=round(tb / tt / 1e9, 1), unit="GB/s")
+    # the same bytes over quantize + MMVQ time: the whole decode call
+    tq = sum(float(np.mean(c.q_ms)) * 1e-3 for c in dec)
+    line["decode_with_quantize_GB_s"] = round(tb / (tt + tq) / 1e9, 1)
+
+    # measured limits: streaming reads of the weight byte counts, int8 MFMA issue rate
+    rd = {r["bytes"]: r for r in bench_peaks.stream_read(torch, [9437184, 28311552, 107520000])}
+    mf = bench_peaks.mfma_rate(torch, reps=3, waves=(4,))["int8"][0]
+    line["measured"] = {"stream_read": list(rd.values()), "int8_mfma_TOP_s": mf["T_s"],
+                        "int8_mfma_clock_GHz": mf["clock_GHz"],
+                        "note": "plain kernels of bench_peaks.hip run in this process"}
+
+    head = max(dec, key=lambda c: c.od)
+    kh = kms(head)
+    ach = head.kbytes / kh / 1e9
+    line["roofline"] = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                        "frac_of_measured": round(ach / rd[28311552]["GB_s"], 4),
+                        "measured_peak": rd[28311552]["GB_s"],
+                        "traffic": read_traffic(COUNTERS, "qmm::mmvq_q4k_kernel<1, 4, false>", None),
+                        "kernel": "mmvq_q4k_kernel<1,4,false>", "call": head.label,
+                        "bytes_per_launch": int(head.kbytes)}
+
+    big = [c for c in calls if c.nt >= 9 and not c.q8k]
+    ops = sum(c.ops for c in big)
+    m = max(big, key=kms)
+    ta = m.ops / kms(m) / 1e12
+    mk, mg = mmq_kernel(qmm, m.nt, m.od, m.idim)
+    line["mmq"] = {"value": round(ops / sum(kms(c) for c in big) / 1e12, 2), "unit": "TOP/s",
+                   "roofline": {"bound": "mfma", "achieved": round(ta, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                                "frac": round(ta / INT8_PEAK_TOPS, 4),
+                                "frac_of_measured": round(ta / mf["T_s"], 4), "measured_peak": mf["T_s"],
+                                "traffic": read_traffic(COUNTERS, mk, mg),
+                                "kernel": mk.replace("qmm::", "").replace(" ", ""), "call": m.label,
+                                "ops_per_launch": int(m.ops)},
+                   "per_call": {c.label: {"us": round(kms(c) * 1e6, 2), "TOP_s": round(c.ops / kms(c) / 1e12, 2),
+                                          "int8_frac": round(c.ops / kms(c) / 1e12 / INT8_PEAK_TOPS, 4)}
+                                for c in big}}
+    if "streamk" in mk:
+        # one kernel and one grid for both prefill shapes: the counters give their mean
+        line["mmq"]["roofline"]["traffic_note"] = "HBM bytes per launch, mean over both nt=512 shapes"
+
+    k8 = [c for c in calls if c.q8k]
+    if k8:
+        m8 = max(k8, key=kms)
+        t8 = m8.ops / kms(m8) / 1e12
+        line["mmq_q8k"] = {"value": round(sum(c.ops for c in k8) / sum(kms(c) for c in k8) / 1e12, 2),
+                           "unit": "TOP/s", "activations": "Q8_K: one scale per 256 values (its own numerics)",
+                           "roofline": {"bound": "mfma", "achieved": round(t8, 2), "peak": INT8_PEAK_TOPS,
+                                        "unit": "TOP/s", "frac": round(t8 / INT8_PEAK_TOPS, 4),
+                                        "frac_of_measured": round(t8 / mf["T_s"], 4), "call": m8.label},
+                           "per_call": {c.label: {"us": round(kms(c) * 1e6, 2),
+                                                  "TOP_s": round(c.ops / kms(c) / 1e12, 2)} for c in k8}}
+
+    q6 = [c for c in calls if c.nt == 1 and c.od == 32000]
+    if q6:
+        alg = q6[0].kbytes   # 210-byte blocks: the algorithmic bytes of either layout
+        line["q6k_head"] = {c.label: {"us": round(kms(c) * 1e6, 2), "GB_s": round(alg / kms(c) / 1e9, 1),
+                                      "hbm_frac": round(alg / kms(c) / 1e9 / HBM_PEAK_GBS, 4),
+                                      "frac_of_measured": round(alg / kms(c) / 1e9 / rd[107520000]["GB_s"], 4)}
+                            for c in q6}
+        line["q6k_head"]["bytes"] = "algorithmic: 210-byte blocks + q8 activations + f32 output, both layouts"
+    c1 = [c for c in calls if c.nt == 1 and c.od == 1024]
+    if c1:
+        c = c1[0]
+        line["gemv_1024x4096"] = {"us": round(kms(c) * 1e6, 2), "GB_s": round(c.kbytes / kms(c) / 1e9, 1),
+                                  "note": "2.4 MB of weights: launch-latency bound, no roofline claim"}
+    line["config"] = {"workload": "q4k_decode_prefill",
+                      "mmvq": "Q4_K 4096x4096 and 12288x4096, nt=1,4,8; Q4_K 1024x4096 nt=1; "
+                              "Q6_K 32000x4096 nt=1 (210- and 224-byte blocks)",
+                      "mmq": "Q4_K 12288x4096 and 4096x12288, nt=512, 1% outliers x20 (per-32 and Q8_K activations)",
+                      "weight_copies_bytes_per_shape": COPY_BYTES}
+
+
+def dllm_graph(torch, qmm):
+    """One diffusion-LM step (32 layers x q, k, v, o, gate, up Q4_K and down Q6_K padded
+    at L = 256, distinct weights per layer) as one HIP graph of 224 quantize and 224
+    matmul launches: ms per replay and int8 TOP/s including the quantize launches."""
+    calls = build_calls(torch, qmm, "dllm_step")
+    ops = sum(c.ops for c in calls)
+    gms = graph_replay_ms(torch, calls)
+    del calls
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(gms, 4), "replays": 5, "TOP_s_incl_quantize": round(ops / (gms * 1e-3) / 1e12, 2),
+            "int8_frac": round(ops / (gms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+            "shape": "32 layers x 7 projections at L=256; 4.46 GB of distinct weights per step"}
+
+
+def spread_pass(torch, calls, chunk, nchunks, gate_cycles):
+    """Per call, `nchunks` more event-timed chunks of `chunk` matmul launches after the
+    timed region (the same launches and weight rotation): the per-launch time of each
+    chunk, for the median and p10 / p90.  The timed region itself holds one chunk per
+    call at the default 20 steps, and chunks shorter than 20 launches would let the
+    fixed cost of an event (a few microseconds) into the per-launch time."""
+    st = torch.cuda.current_stream()
+    out = {c: [] for c in calls}
+    if nchunks < 1:
+        return {c: c.k_ms for c in calls}
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in calls]
+           for _ in range(nchunks)]
+    torch.cuda.synchronize()
+    for ch in range(nchunks):
+        torch.cuda._sleep(gate_cycles)
+        for c, (e0, e1) in zip(calls, evs[ch]):
+            c.quantize()
+            e0.record(st)
+            for _ in range(chunk):
+                c.matmul()
+            e1.record(st)
+    torch.cuda.synchronize()
+    for ch in range(nchunks):
+        for c, (e0, e1) in zip(calls, evs[ch]):
+            out[c].append(e0.elapsed_time(e1) / chunk)
+    return out
+
+
+def run_peaks(args, torch):
+    """The measured limits of the GPU (bench_peaks): streaming read at the weight
+    byte counts of the decode shapes, MFMA and VALU issue rates, MFMA/VALU overlap."""
+    import bench_peaks
+
+    sizes = [9437184, 28311552, 107520000, 112896000]   # Q4_K 4096^2, 12288x4096; Q6_K 32000x4096 (210 / 224 B)
+    t0 = time.perf_counter()
+    res = bench_peaks.run_all(torch, sizes)
+    wall = time.perf_counter() - t0
+    i8 = max(res["mfma"]["int8"], key=lambda r: r["T_s"])
+    rd = {r["bytes"]: r for r in res["stream_read"]}
+    line = {"metric": "measured limits: HBM streaming read (GB/s) and int8 MFMA rate (TOP/s)",
+            "value": rd[28311552]["GB_s"], "unit": "GB/s", "n_gpus": 1, "steps": 1, "warmup": 1,
+            "ms_per_step": round(wall * 1e3, 1), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "int8", "data": "synthetic (register-only loops; a plain read of device buffers)",
+            "roofline": {"bound": "hbm", "achieved": rd[28311552]["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(rd[28311552]["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                         "kernel": "stream_read_kernel", "bytes_per_launch": 28311552},
+            "int8_mfma": {"T_s": i8["T_s"], "unit": "TOP/s", "frac": round(i8["T_s"] / INT8_PEAK_TOPS, 4),
+                          "waves_per_simd": i8["waves_per_simd"]},
+            "config": {"workload": "peaks", "stream_read_bytes": sizes}, "detail": res}
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -645,15 +862,17 @@ def main():
     import torch
     import quantized_matmul_amd as qmm
 
-    from quantized_matmul_amd.profile_summary import read_traffic
+    from profile_summary import read_traffic
 
     torch.cuda.set_device(0)
     if args.workload == "fused_quantize":
         return run_fused(args, torch, qmm)
+    if args.workload == "peaks":
+        return run_peaks(args, torch)
     calls = build_calls(torch, qmm, args.workload)
     cal = copy_calibration(torch, args.copy_calibration) if args.copy_calibration > 0 else None
     st = torch.cuda.current_stream()
-    chunk = min(CHUNK, args.steps)
+    chunk = min(args.chunk, args.steps)
     nchunks = max(1, args.steps // chunk)
     steps = chunk * nchunks
     evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in calls] for _ in range(nchunks)]
@@ -703,15 +922,18 @@ def main():
         for c, (e0, e1, e2) in zip(calls, evs[ch]):
             c.q_ms.append(e0.elapsed_time(e1) / chunk)
             c.k_ms.append(e1.elapsed_time(e2) / chunk)
+    spread = spread_pass(torch, calls, chunk, args.spread_chunks, gate_cycles)
 
     detail = []
     for c in calls:
         k = float(np.mean(c.k_ms))
         qm = float(np.mean(c.q_ms))
+        sp = spread[c]
         row = {"call": c.label, "kernel": "mmvq" if c.kind == qmm.QMM_KIND_MMVQ else "mmq",
                "kernel_us": round(k * 1e3, 2), "quantize_us": round(qm * 1e3, 2),
-               "kernel_us_p10_p90": [round(float(np.percentile(c.k_ms, 10)) * 1e3, 2),
-                                     round(float(np.percentile(c.k_ms, 90)) * 1e3, 2)],
+               "kernel_us_median": round(float(np.median(sp)) * 1e3, 2),
+               "kernel_us_p10_p90": [round(float(np.percentile(sp, 10)) * 1e3, 2),
+                                     round(float(np.percentile(sp, 90)) * 1e3, 2)],
                "GB_s": round(c.kbytes / (k * 1e-3) / 1e9, 1),
                "TOP_s": round(c.ops / (k * 1e-3) / 1e12, 2)}
         row["hbm_frac"] = round(row["GB_s"] / HBM_PEAK_GBS, 4)
@@ -729,38 +951,7 @@ def main():
     dec = [c for c in calls if c.nt == 1]
     big = [c for c in calls if c.nt >= 9]
     if args.workload == "q4k_decode_prefill":
-        tb = sum(c.kbytes for c in dec)
-        tt = sum(float(np.mean(c.k_ms)) * 1e-3 for c in dec)
-        line.update(value=round(tb / tt / 1e9, 1), unit="GB/s")
-        # the same bytes over quantize + MMVQ time: the whole decode call
-        tq = sum(float(np.mean(c.q_ms)) * 1e-3 for c in dec)
-        line["decode_with_quantize_GB_s"] = round(tb / (tt + tq) / 1e9, 1)
-        head = max(dec, key=lambda c: c.od)
-        kh = float(np.mean(head.k_ms)) * 1e-3
-        line["roofline"] = {"bound": "hbm", "achieved": round(head.kbytes / kh / 1e9, 1), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(head.kbytes / kh / 1e9 / HBM_PEAK_GBS, 4),
-                            "traffic": read_traffic(COUNTERS, "qmm::mmvq_q4k_kernel<1, 4, false>", None),
-                            "kernel": "mmvq_q4k_kernel<1,4,false>", "call": head.label,
-                            "bytes_per_launch": int(head.kbytes)}
-        ops = sum(c.ops for c in big)
-        tb2 = sum(float(np.mean(c.k_ms)) * 1e-3 for c in big)
-        m = max(big, key=lambda c: float(np.mean(c.k_ms)))
-        km = float(np.mean(m.k_ms)) * 1e-3
-        mk, mg = mmq_kernel(qmm, m.nt, m.od, m.idim)
-        line["mmq"] = {"value": round(ops / tb2 / 1e12, 2), "unit": "TOP/s",
-                       "roofline": {"bound": "mfma", "achieved": round(m.ops / km / 1e12, 2),
-                                    "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
-                                    "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4),
-                                    "traffic": read_traffic(COUNTERS, mk, mg),
-                                    "kernel": mk.replace("qmm::", "").replace(" ", ""), "call": m.label,
-                                    "ops_per_launch": int(m.ops)}}
-        if "streamk" in mk:
-            # one kernel and one grid for both prefill shapes: the counters give their mean
-            line["mmq"]["roofline"]["traffic_note"] = "HBM bytes per launch, mean over both nt=512 shapes"
-        line["config"] = {"workload": "q4k_decode_prefill",
-                          "mmvq": "Q4_K 4096x4096 and 12288x4096, nt=1,4,8",
-                          "mmq": "Q4_K 12288x4096 and 4096x12288, nt=512, 1% outliers x20",
-                          "weight_copies_bytes_per_shape": COPY_BYTES}
+        report_default(line, calls, qmm, torch, read_traffic)
     elif args.workload == "q8k_prefill":
         q8 = [c for c in calls if c.q8k and c.qtype == qmm.QMM_TYPE_Q4_K]
         p32 = [c for c in calls if not c.q8k and c.qtype == qmm.QMM_TYPE_Q4_K]
@@ -865,6 +1056,8 @@ def main():
     line["detail"] = detail
     if cal:
         line["copy_calibration"] = cal
+    if args.workload == "q4k_decode_prefill" and not args.no_dllm:
+        line["dllm_step"] = dllm_graph(torch, qmm)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(calls)
     print(json.dumps(line), flush=True)

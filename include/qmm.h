@@ -107,7 +107,10 @@ enum {
 
 /* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K, Q4_0), *176
  * (Q5_K), *210 (Q6_K), *224 (Q6_K padded) or *272 (Q8_0).  0 for an unknown type or
- * a bad shape. */
+ * a bad shape.  [GEMM, "The GPU path", "Weights stay in GGUF blocks"]: a matrix is
+ * uploaded as its blocks (144 bytes per Q4_K super-block, Q6_K's 210 bytes padded to
+ * 224); [CH04, section 3.4]: the weight bytes a matmul streams are rows x blocks per
+ * row x bytes per block, the decode budget.  Host function, no device work. */
 size_t qmm_weight_bytes(int type, int od, int id);
 
 /* Upload-time repack: nblocks Q6_K blocks of 210 bytes (src, any alignment) to
@@ -118,7 +121,10 @@ int qmm_pad_q6k(const void* src, void* dst, long long nblocks, void* stream);
 
 /* Workspace bytes qmm_matmul needs for nt tokens of id values: the q8 plane
  * (nt*id int8, rounded up to 256 B) then d and s (nt*id/32 f32 each, each rounded
- * up to 256 B).  0 for a bad shape. */
+ * up to 256 B).  0 for a bad shape.  [GEMM, "The GPU path", "Activations get one
+ * scale per 32"]: int8 codes with one f32 scale per 32 values and scale x sum(q)
+ * kept beside them; [CH04, section 3.3]: the matmul call produces that q8
+ * activation plane itself before the kernel runs.  Host function, no device work. */
 size_t qmm_act_bytes(int nt, int id);
 
 /* Quantize activations to int8 blocks of 32.
@@ -146,7 +152,13 @@ int qmm_matmul(int type, const void* W, const float* x, int nt, int od, int id, 
                void* workspace, size_t ws_bytes, void* stream);
 
 /* The matmul on already quantized activations (reuse one quantized input for
- * several weight matrices).  q, d, s as produced by qmm_quantize_act. */
+ * several weight matrices).  q, d, s as produced by qmm_quantize_act.
+ * [CH04, section 3.3]: the decode and prefill kernels read a q8 activation plane
+ * that a quantize step produced or kept from an earlier call (memoized), so one
+ * quantized input can serve several matmuls; [GEMM, "The GPU path", "Fused
+ * elementwise kernels"]: the norm or activation feeding the matmuls ends in that
+ * quantize.  Dispatch, layouts, validation and errors as qmm_matmul (no workspace:
+ * the per-tile matrix kernel, never stream-K). */
 int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, const float* s, int nt,
                   int od, int id, float* out, void* stream);
 
@@ -182,7 +194,11 @@ int qmm_mmq_tile(int nt, int od, int id);
  * switch, and with the default switch (8) also for 9..16 tokens on od <= 4096
  * rows, as launches on slices of 8 tokens (the MMQ tile grid of such a matrix
  * fills at most a quarter of the GPU); QMM_KIND_MMQ otherwise.  A negative status
- * for invalid arguments. */
+ * for invalid arguments.  [MMQ, section 12.1]: every batch size has a dedicated
+ * kernel, 1..8 tokens the quantized vector kernel and 9 and more the tiled matrix
+ * kernel, with the threshold tuned per chip; [CH04, section 3.3]: the dispatch is a
+ * function of nt with shape gates, and an unsupported shape is an error, not a
+ * fallback.  Host function, no device work. */
 int qmm_dispatch_kind(int type, int nt, int od, int id);
 
 /* 1 if the stream-K kernel is expected to be faster than the per-tile MMQ for this

@@ -1,13 +1,13 @@
 """Short text summaries of rocprofv3 results (rocpd SQLite databases).
 
-  python -m quantized_matmul_amd.profile_summary trace DB --cmd "..." [--bench JSON] --out FILE
+  python profile_summary.py trace DB --cmd "..." [--bench JSON] --out FILE
       Per (kernel, grid): dispatch count, mean / median / min / max duration.  With
       --bench, the bench line's per-call kernel times are listed beside the trace.
 
-  python -m quantized_matmul_amd.profile_summary counters DB... --cmd "..." [--cmd "..."] --out FILE
+  python profile_summary.py counters DB... --cmd "..." [--cmd "..."] --out FILE
       Every counter of every library kernel in the databases (mean per dispatch).
 
-  python -m quantized_matmul_amd.profile_summary pmc FETCH_DB WRITE_DB --cmd-fetch "..."
+  python profile_summary.py pmc FETCH_DB WRITE_DB --cmd-fetch "..."
       --cmd-write "..." --copy-bytes N --out FILE
       Per (kernel, grid): mean FETCH_SIZE and WRITE_SIZE (KiB per dispatch).  The two
       counters are scaled to bytes by a plain device copy of N bytes that the profiled
@@ -28,7 +28,7 @@ import sqlite3
 import statistics
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_CSRC = os.path.join(_HERE, "csrc")
+_CSRC = os.path.join(_HERE, "quantized_matmul_amd", "csrc")
 
 # library kernel (name prefix) -> sources it is compiled from
 KERNEL_SOURCES = {

@@ -134,7 +134,10 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
-def _dev(t: torch.Tensor, dtype, name: str) -> ctypes.c_void_p:
+def _dev(t: torch.Tensor, dtype, name: str, need: int = 0) -> ctypes.c_void_p:
+    """The device pointer of t, after checking its type, placement, layout and that it
+    holds at least `need` elements: the library sees only pointers and sizes, so an
+    undersized tensor must be refused here, before any launch."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
     if not t.is_cuda:
@@ -143,7 +146,15 @@ def _dev(t: torch.Tensor, dtype, name: str) -> ctypes.c_void_p:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if t.numel() < need:
+        raise ValueError(f"{name} holds {t.numel()} elements; this call needs at least {need}")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _wbytes(qtype: int, od: int, idim: int) -> int:
+    """Bytes W must hold (0 for an unknown type or a bad shape: the library then
+    returns an error status before any launch)."""
+    return qmm_weight_bytes(qtype, od, idim) if od > 0 and idim > 0 else 0
 
 
 def qmm_weight_bytes(qtype: int, od: int, idim: int) -> int:
@@ -198,8 +209,9 @@ def qmm_quantize_act(x: torch.Tensor, q=None, d=None, s=None, stream=None):
         d = torch.empty((nt, idim // 32), dtype=torch.float32, device=x.device)
     if s is None:
         s = torch.empty((nt, idim // 32), dtype=torch.float32, device=x.device)
-    _check(lib().qmm_quantize_act(_dev(x, torch.float32, "x"), nt, idim, _dev(q, torch.int8, "q"),
-                                  _dev(d, torch.float32, "d"), _dev(s, torch.float32, "s"), _stream(stream)),
+    nb = nt * (idim // 32)
+    _check(lib().qmm_quantize_act(_dev(x, torch.float32, "x"), nt, idim, _dev(q, torch.int8, "q", nt * idim),
+                                  _dev(d, torch.float32, "d", nb), _dev(s, torch.float32, "s", nb), _stream(stream)),
            "qmm_quantize_act")
     return q, d, s
 
@@ -215,10 +227,13 @@ def qmm_matmul_q8_streamk(qtype: int, W: torch.Tensor, q: torch.Tensor, d: torch
     nt, idim = q.shape
     if out is None:
         out = torch.empty((nt, od), dtype=torch.float32, device=q.device)
-    _check(lib().qmm_matmul_q8_streamk(qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"),
-                                       _dev(d, torch.float32, "d"), _dev(s, torch.float32, "s"), nt, od, idim,
-                                       _dev(out, torch.float32, "out"), _dev(workspace, torch.uint8, "workspace"),
-                                       workspace.numel(), _stream(stream)), "qmm_matmul_q8_streamk")
+    nb = nt * (idim // 32)
+    _check(lib().qmm_matmul_q8_streamk(qtype, _dev(W, torch.uint8, "W", _wbytes(qtype, od, idim)),
+                                       _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d", nb),
+                                       _dev(s, torch.float32, "s", nb), nt, od, idim,
+                                       _dev(out, torch.float32, "out", nt * od),
+                                       _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                       _stream(stream)), "qmm_matmul_q8_streamk")
     return out
 
 
@@ -230,8 +245,8 @@ def qmm_pad_q6k(W: torch.Tensor, out=None, stream=None) -> torch.Tensor:
     nb = W.numel() // 210
     if out is None:
         out = torch.empty(nb * 224, dtype=torch.uint8, device=W.device)
-    _check(lib().qmm_pad_q6k(_dev(W, torch.uint8, "W"), _dev(out, torch.uint8, "out"), nb, _stream(stream)),
-           "qmm_pad_q6k")
+    _check(lib().qmm_pad_q6k(_dev(W, torch.uint8, "W"), _dev(out, torch.uint8, "out", nb * 224), nb,
+                             _stream(stream)), "qmm_pad_q6k")
     return out
 
 
@@ -244,9 +259,10 @@ def qmm_quantize_act_q8k(x: torch.Tensor, q=None, d=None, bsum=None, stream=None
         d = torch.empty((nt, idim // 256), dtype=torch.float32, device=x.device)
     if bsum is None:
         bsum = torch.empty((nt, idim // 16), dtype=torch.float32, device=x.device)
-    _check(lib().qmm_quantize_act_q8k(_dev(x, torch.float32, "x"), nt, idim, _dev(q, torch.int8, "q"),
-                                      _dev(d, torch.float32, "d"), _dev(bsum, torch.float32, "bsum"),
-                                      _stream(stream)), "qmm_quantize_act_q8k")
+    _check(lib().qmm_quantize_act_q8k(_dev(x, torch.float32, "x"), nt, idim, _dev(q, torch.int8, "q", nt * idim),
+                                      _dev(d, torch.float32, "d", nt * (idim // 256)),
+                                      _dev(bsum, torch.float32, "bsum", nt * (idim // 16)), _stream(stream)),
+           "qmm_quantize_act_q8k")
     return q, d, bsum
 
 
@@ -256,9 +272,10 @@ def qmm_matmul_q8k(qtype: int, W: torch.Tensor, q: torch.Tensor, d: torch.Tensor
     nt, idim = q.shape
     if out is None:
         out = torch.empty((nt, od), dtype=torch.float32, device=q.device)
-    _check(lib().qmm_matmul_q8k(qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"),
-                                _dev(d, torch.float32, "d"), _dev(bsum, torch.float32, "bsum"), nt, od, idim,
-                                _dev(out, torch.float32, "out"), _stream(stream)), "qmm_matmul_q8k")
+    _check(lib().qmm_matmul_q8k(qtype, _dev(W, torch.uint8, "W", _wbytes(qtype, od, idim)), _dev(q, torch.int8, "q"),
+                                _dev(d, torch.float32, "d", nt * (idim // 256)),
+                                _dev(bsum, torch.float32, "bsum", nt * (idim // 16)), nt, od, idim,
+                                _dev(out, torch.float32, "out", nt * od), _stream(stream)), "qmm_matmul_q8k")
     return out
 
 
@@ -268,9 +285,11 @@ def qmm_matmul_q8k_kind(kind: int, qtype: int, W: torch.Tensor, q: torch.Tensor,
     nt, idim = q.shape
     if out is None:
         out = torch.empty((nt, od), dtype=torch.float32, device=q.device)
-    _check(lib().qmm_matmul_q8k_kind(kind, qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"),
-                                     _dev(d, torch.float32, "d"), _dev(bsum, torch.float32, "bsum"), nt, od, idim,
-                                     _dev(out, torch.float32, "out"), _stream(stream)), "qmm_matmul_q8k_kind")
+    _check(lib().qmm_matmul_q8k_kind(kind, qtype, _dev(W, torch.uint8, "W", _wbytes(qtype, od, idim)),
+                                     _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d", nt * (idim // 256)),
+                                     _dev(bsum, torch.float32, "bsum", nt * (idim // 16)), nt, od, idim,
+                                     _dev(out, torch.float32, "out", nt * od), _stream(stream)),
+           "qmm_matmul_q8k_kind")
     return out
 
 
@@ -288,9 +307,11 @@ def qmm_q8k_superblock_sums(qtype: int, W: torch.Tensor, q: torch.Tensor, d: tor
     nt, idim = q.shape
     if S is None:
         S = torch.empty((nt, od, idim // 256, 2), dtype=torch.int32, device=q.device)
-    _check(lib().qmm_q8k_superblock_sums(qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"),
-                                         _dev(d, torch.float32, "d"), _dev(bsum, torch.float32, "bsum"), nt, od,
-                                         idim, _dev(S, torch.int32, "S"), _stream(stream)), "qmm_q8k_superblock_sums")
+    _check(lib().qmm_q8k_superblock_sums(qtype, _dev(W, torch.uint8, "W", _wbytes(qtype, od, idim)),
+                                         _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d", nt * (idim // 256)),
+                                         _dev(bsum, torch.float32, "bsum", nt * (idim // 16)), nt, od, idim,
+                                         _dev(S, torch.int32, "S", nt * od * (idim // 256) * 2), _stream(stream)),
+           "qmm_q8k_superblock_sums")
     return S
 
 
@@ -303,6 +324,16 @@ def _q8_out(x: torch.Tensor, q, d, s):
     if s is None:
         s = torch.empty((nt, idim // 32), dtype=torch.float32, device=x.device)
     return q, d, s
+
+
+def _q8_ptrs(q, d, s, nt: int, idim: int):
+    nb = nt * (idim // 32)
+    return (_dev(q, torch.int8, "q", nt * idim), _dev(d, torch.float32, "d", nb), _dev(s, torch.float32, "s", nb))
+
+
+def _q8k_ptrs(q, d, bsum, nt: int, idim: int):
+    return (_dev(q, torch.int8, "q", nt * idim), _dev(d, torch.float32, "d", nt * (idim // 256)),
+            _dev(bsum, torch.float32, "bsum", nt * (idim // 16)))
 
 
 def _weight_vec(w: torch.Tensor, idim: int):
@@ -320,8 +351,7 @@ def qmm_add_rmsnorm_quantize(h: torch.Tensor, o: torch.Tensor, w: torch.Tensor, 
     q, d, s = _q8_out(h, q, d, s)
     _check(lib().qmm_add_rmsnorm_quantize(_dev(h, torch.float32, "h"), _dev(o, torch.float32, "o"),
                                           _dev(w, torch.float32, "w"), float(eps), nt, idim,
-                                          _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
-                                          _dev(s, torch.float32, "s"), _stream(stream)), "qmm_add_rmsnorm_quantize")
+                                          *_q8_ptrs(q, d, s, nt, idim), _stream(stream)), "qmm_add_rmsnorm_quantize")
     return q, d, s
 
 
@@ -331,8 +361,7 @@ def qmm_rmsnorm_quantize(x: torch.Tensor, w: torch.Tensor, eps: float, q=None, d
     _weight_vec(w, idim)
     q, d, s = _q8_out(x, q, d, s)
     _check(lib().qmm_rmsnorm_quantize(_dev(x, torch.float32, "x"), _dev(w, torch.float32, "w"), float(eps), nt,
-                                      idim, _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
-                                      _dev(s, torch.float32, "s"), _stream(stream)), "qmm_rmsnorm_quantize")
+                                      idim, *_q8_ptrs(q, d, s, nt, idim), _stream(stream)), "qmm_rmsnorm_quantize")
     return q, d, s
 
 
@@ -343,8 +372,7 @@ def qmm_silu_mul_quantize(g: torch.Tensor, u: torch.Tensor, q=None, d=None, s=No
         raise ValueError("u must have the shape of g")
     q, d, s = _q8_out(g, q, d, s)
     _check(lib().qmm_silu_mul_quantize(_dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), nt, idim,
-                                       _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
-                                       _dev(s, torch.float32, "s"), _stream(stream)), "qmm_silu_mul_quantize")
+                                       *_q8_ptrs(q, d, s, nt, idim), _stream(stream)), "qmm_silu_mul_quantize")
     return q, d, s
 
 
@@ -369,8 +397,7 @@ def qmm_add_rmsnorm_quantize_q8k(h: torch.Tensor, o: torch.Tensor, w: torch.Tens
     q, d, bsum = _q8k_out(h, q, d, bsum)
     _check(lib().qmm_add_rmsnorm_quantize_q8k(_dev(h, torch.float32, "h"), _dev(o, torch.float32, "o"),
                                               _dev(w, torch.float32, "w"), float(eps), nt, idim,
-                                              _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
-                                              _dev(bsum, torch.float32, "bsum"), _stream(stream)),
+                                              *_q8k_ptrs(q, d, bsum, nt, idim), _stream(stream)),
            "qmm_add_rmsnorm_quantize_q8k")
     return q, d, bsum
 
@@ -381,8 +408,7 @@ def qmm_rmsnorm_quantize_q8k(x: torch.Tensor, w: torch.Tensor, eps: float, q=Non
     _weight_vec(w, idim)
     q, d, bsum = _q8k_out(x, q, d, bsum)
     _check(lib().qmm_rmsnorm_quantize_q8k(_dev(x, torch.float32, "x"), _dev(w, torch.float32, "w"), float(eps),
-                                          nt, idim, _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
-                                          _dev(bsum, torch.float32, "bsum"), _stream(stream)),
+                                          nt, idim, *_q8k_ptrs(q, d, bsum, nt, idim), _stream(stream)),
            "qmm_rmsnorm_quantize_q8k")
     return q, d, bsum
 
@@ -394,8 +420,7 @@ def qmm_silu_mul_quantize_q8k(g: torch.Tensor, u: torch.Tensor, q=None, d=None, 
         raise ValueError("u must have the shape of g")
     q, d, bsum = _q8k_out(g, q, d, bsum)
     _check(lib().qmm_silu_mul_quantize_q8k(_dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), nt, idim,
-                                           _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d"),
-                                           _dev(bsum, torch.float32, "bsum"), _stream(stream)),
+                                           *_q8k_ptrs(q, d, bsum, nt, idim), _stream(stream)),
            "qmm_silu_mul_quantize_q8k")
     return q, d, bsum
 
@@ -417,7 +442,7 @@ def qmm_rmsnorm(x: torch.Tensor, w: torch.Tensor, eps: float, y=None, stream=Non
     if y is None:
         y = torch.empty_like(x)
     _check(lib().qmm_rmsnorm(_dev(x, torch.float32, "x"), _dev(w, torch.float32, "w"), float(eps), nt, idim,
-                             _dev(y, torch.float32, "y"), _stream(stream)), "qmm_rmsnorm")
+                             _dev(y, torch.float32, "y", nt * idim), _stream(stream)), "qmm_rmsnorm")
     return y
 
 
@@ -429,7 +454,7 @@ def qmm_silu_mul(g: torch.Tensor, u: torch.Tensor, y=None, stream=None) -> torch
     if y is None:
         y = torch.empty_like(g)
     _check(lib().qmm_silu_mul(_dev(g, torch.float32, "g"), _dev(u, torch.float32, "u"), nt, idim,
-                              _dev(y, torch.float32, "y"), _stream(stream)), "qmm_silu_mul")
+                              _dev(y, torch.float32, "y", nt * idim), _stream(stream)), "qmm_silu_mul")
     return y
 
 
@@ -441,9 +466,10 @@ def qmm_matmul(qtype: int, W: torch.Tensor, x: torch.Tensor, od: int, out=None, 
     if workspace is None:
         workspace = torch.empty(max(qmm_matmul_ws_bytes(qtype, nt, od, idim), 1), dtype=torch.uint8,
                                 device=x.device)
-    _check(lib().qmm_matmul(qtype, _dev(W, torch.uint8, "W"), _dev(x, torch.float32, "x"), nt, od, idim,
-                            _dev(out, torch.float32, "out"), _dev(workspace, torch.uint8, "workspace"),
-                            workspace.numel(), _stream(stream)), "qmm_matmul")
+    _check(lib().qmm_matmul(qtype, _dev(W, torch.uint8, "W", _wbytes(qtype, od, idim)), _dev(x, torch.float32, "x"),
+                            nt, od, idim, _dev(out, torch.float32, "out", nt * od),
+                            _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
+           "qmm_matmul")
     return out
 
 
@@ -452,9 +478,10 @@ def qmm_matmul_q8(qtype: int, W: torch.Tensor, q: torch.Tensor, d: torch.Tensor,
     nt, idim = q.shape
     if out is None:
         out = torch.empty((nt, od), dtype=torch.float32, device=q.device)
-    _check(lib().qmm_matmul_q8(qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"),
-                               _dev(d, torch.float32, "d"), _dev(s, torch.float32, "s"), nt, od, idim,
-                               _dev(out, torch.float32, "out"), _stream(stream)), "qmm_matmul_q8")
+    nb = nt * (idim // 32)
+    _check(lib().qmm_matmul_q8(qtype, _dev(W, torch.uint8, "W", _wbytes(qtype, od, idim)), _dev(q, torch.int8, "q"),
+                               _dev(d, torch.float32, "d", nb), _dev(s, torch.float32, "s", nb), nt, od, idim,
+                               _dev(out, torch.float32, "out", nt * od), _stream(stream)), "qmm_matmul_q8")
     return out
 
 
@@ -462,9 +489,11 @@ def qmm_matmul_q8_kind(kind: int, qtype: int, W, q, d, s, od: int, out=None, str
     nt, idim = q.shape
     if out is None:
         out = torch.empty((nt, od), dtype=torch.float32, device=q.device)
-    _check(lib().qmm_matmul_q8_kind(kind, qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"),
-                                    _dev(d, torch.float32, "d"), _dev(s, torch.float32, "s"), nt, od, idim,
-                                    _dev(out, torch.float32, "out"), _stream(stream)), "qmm_matmul_q8_kind")
+    nb = nt * (idim // 32)
+    _check(lib().qmm_matmul_q8_kind(kind, qtype, _dev(W, torch.uint8, "W", _wbytes(qtype, od, idim)),
+                                    _dev(q, torch.int8, "q"), _dev(d, torch.float32, "d", nb),
+                                    _dev(s, torch.float32, "s", nb), nt, od, idim,
+                                    _dev(out, torch.float32, "out", nt * od), _stream(stream)), "qmm_matmul_q8_kind")
     return out
 
 
@@ -474,8 +503,10 @@ def qmm_group_dots(kind: int, qtype: int, W: torch.Tensor, q: torch.Tensor, od: 
     ng = 16 if qtype in (QMM_TYPE_Q6_K, QMM_TYPE_Q6_K_P224) else 8
     if S is None:
         S = torch.empty((nt, od, idim // 256, ng), dtype=torch.int32, device=q.device)
-    _check(lib().qmm_group_dots(kind, qtype, _dev(W, torch.uint8, "W"), _dev(q, torch.int8, "q"), nt, od,
-                                idim, _dev(S, torch.int32, "S"), _stream(stream)), "qmm_group_dots")
+    _check(lib().qmm_group_dots(kind, qtype, _dev(W, torch.uint8, "W", _wbytes(qtype, od, idim)),
+                                _dev(q, torch.int8, "q"), nt, od, idim,
+                                _dev(S, torch.int32, "S", nt * od * (idim // 256) * ng), _stream(stream)),
+           "qmm_group_dots")
     return S
 
 
@@ -490,6 +521,7 @@ def qmm_mfma_tile_check(kind: int, A: torch.Tensor, B: torch.Tensor, C=None, str
             C = torch.empty((32, 32), dtype=torch.float32, device=A.device)
     dt = torch.int8 if kind == 1 else torch.float32
     ct = torch.int32 if kind == 1 else torch.float32
-    _check(lib().qmm_mfma_tile_check(int(kind), _dev(A, dt, "A"), _dev(B, dt, "B"), _dev(C, ct, "C"),
+    na, nc = {1: (1024, 1024), 2: (64, 2048), 3: (64, 1024)}.get(int(kind), (0, 0))
+    _check(lib().qmm_mfma_tile_check(int(kind), _dev(A, dt, "A", na), _dev(B, dt, "B", na), _dev(C, ct, "C", nc),
                                      _stream(stream)), "qmm_mfma_tile_check")
     return C

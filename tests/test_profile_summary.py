@@ -1,7 +1,7 @@
 """Host-side checks of the rocprofv3 summary helper used for roofline.traffic."""
 import os
 
-from quantized_matmul_amd import profile_summary as ps
+import profile_summary as ps
 
 
 def test_short_name_strips_arguments_keeps_templates():
