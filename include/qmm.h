@@ -91,7 +91,8 @@ enum {
     QMM_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned */
     QMM_ERR_WORKSPACE = -5, /* workspace smaller than qmm_act_bytes(nt, id) */
     QMM_ERR_DEVICE = -6,    /* current device is not gfx950, or no device */
-    QMM_ERR_LAUNCH = -7     /* a kernel launch reported an error */
+    QMM_ERR_LAUNCH = -7,    /* a kernel launch reported an error */
+    QMM_ERR_SCRATCH = -8    /* qmm_matmul_noalloc: the call needs more than its fixed scratch */
 };
 
 /* Dispatch kinds. */
@@ -150,6 +151,25 @@ int qmm_quantize_act(const float* x, int nt, int id, int8_t* q, float* d, float*
  * only, and calls sharing a workspace must not overlap in time. */
 int qmm_matmul(int type, const void* W, const float* x, int nt, int od, int id, float* out,
                void* workspace, size_t ws_bytes, void* stream);
+
+/* qmm_matmul for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * quantize, dispatch and kernels as qmm_matmul with a workspace of
+ * QMM_NOALLOC_SCRATCH_BYTES, but the workspace is the library's own fixed device
+ * scratch, a file-scope array of QMM_NOALLOC_SCRATCH_BYTES (32 MiB) that every device
+ * the library runs on holds until the process ends.  The call allocates and frees
+ * nothing.  The quantized activations take the first qmm_act_bytes(nt, id) bytes,
+ * at most QMM_NOALLOC_ACT_BYTES (16 MiB; e.g. 512 tokens of 12288 values need 7.9
+ * MiB), else QMM_ERR_SCRATCH before any device work; the stream-K partial tiles
+ * (qmm_streamk_ws_bytes(), 16 MiB) follow them.  Nothing in the scratch needs to
+ * start at zero (each call writes before it reads).  Every call on one device
+ * shares that device's scratch: calls that overlap in time on one device (other
+ * streams, other host threads) race and give wrong results; calls on one stream are
+ * ordered and safe.  Other arguments, validation and errors as qmm_matmul. */
+#define QMM_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define QMM_NOALLOC_ACT_BYTES (16u << 20)
+int qmm_matmul_noalloc(int type, const void* W, const float* x, int nt, int od, int id, float* out,
+                       void* stream);
 
 /* The matmul on already quantized activations (reuse one quantized input for
  * several weight matrices).  q, d, s as produced by qmm_quantize_act.

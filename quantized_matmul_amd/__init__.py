@@ -39,6 +39,9 @@ QMM_ERR_ALIGN = -4
 QMM_ERR_WORKSPACE = -5
 QMM_ERR_DEVICE = -6
 QMM_ERR_LAUNCH = -7
+QMM_ERR_SCRATCH = -8
+QMM_NOALLOC_SCRATCH_BYTES = 32 << 20
+QMM_NOALLOC_ACT_BYTES = 16 << 20
 
 BLOCK_BYTES = {QMM_TYPE_Q4_K: 144, QMM_TYPE_Q6_K: 210, QMM_TYPE_Q6_K_P224: 224,  # bytes per 256 weights
                QMM_TYPE_Q4_0: 144, QMM_TYPE_Q8_0: 272, QMM_TYPE_Q5_K: 176}
@@ -49,7 +52,7 @@ EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul"
            "qmm_silu_mul_quantize", "qmm_add_rmsnorm_quantize_q8k", "qmm_rmsnorm_quantize_q8k",
            "qmm_silu_mul_quantize_q8k", "qmm_residual_add", "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k",
            "qmm_matmul_q8k", "qmm_matmul_q8k_kind", "qmm_q8k_tile", "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_streamk_ws_bytes",
-           "qmm_matmul_q8_streamk", "qmm_streamk_preferred")
+           "qmm_matmul_q8_streamk", "qmm_streamk_preferred", "qmm_matmul_noalloc")
 
 
 class QmmError(RuntimeError):
@@ -76,6 +79,7 @@ def lib():
         L.qmm_act_bytes.restype = Z
         L.qmm_quantize_act.argtypes = [P, I, I, P, P, P, P]
         L.qmm_matmul.argtypes = [I, P, P, I, I, I, P, P, Z, P]
+        L.qmm_matmul_noalloc.argtypes = [I, P, P, I, I, I, P, P]
         L.qmm_matmul_q8.argtypes = [I, P, P, P, P, I, I, I, P, P]
         L.qmm_matmul_q8_kind.argtypes = [I, I, P, P, P, P, I, I, I, P, P]
         L.qmm_dispatch_kind.argtypes = [I, I, I, I]
@@ -105,7 +109,7 @@ def lib():
         L.qmm_matmul_q8_streamk.argtypes = [I, P, P, P, P, I, I, I, P, P, Z, P]
         L.qmm_strerror.argtypes = [I]
         L.qmm_strerror.restype = ctypes.c_char_p
-        for f in ("qmm_quantize_act", "qmm_matmul", "qmm_matmul_q8", "qmm_matmul_q8_kind",
+        for f in ("qmm_quantize_act", "qmm_matmul", "qmm_matmul_noalloc", "qmm_matmul_q8", "qmm_matmul_q8_kind",
                   "qmm_dispatch_kind", "qmm_mmq_tile", "qmm_nt_switch", "qmm_group_dots", "qmm_mfma_tile_check",
                   "qmm_add_rmsnorm_quantize", "qmm_rmsnorm_quantize", "qmm_silu_mul_quantize",
                   "qmm_add_rmsnorm_quantize_q8k", "qmm_rmsnorm_quantize_q8k", "qmm_silu_mul_quantize_q8k",
@@ -470,6 +474,19 @@ def qmm_matmul(qtype: int, W: torch.Tensor, x: torch.Tensor, od: int, out=None, 
                             nt, od, idim, _dev(out, torch.float32, "out", nt * od),
                             _dev(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)),
            "qmm_matmul")
+    return out
+
+
+def qmm_matmul_noalloc(qtype: int, W: torch.Tensor, x: torch.Tensor, od: int, out=None, stream=None):
+    """out f32 [nt, od] = quantize(x) then the nt-dispatched kernel, with the library's
+    fixed device scratch as the workspace (the call itself allocates nothing; pass
+    `out` to allocate nothing here either).  Calls overlapping on one device race."""
+    nt, idim = x.shape
+    if out is None:
+        out = torch.empty((nt, od), dtype=torch.float32, device=x.device)
+    _check(lib().qmm_matmul_noalloc(qtype, _dev(W, torch.uint8, "W", _wbytes(qtype, od, idim)),
+                                    _dev(x, torch.float32, "x"), nt, od, idim,
+                                    _dev(out, torch.float32, "out", nt * od), _stream(stream)), "qmm_matmul_noalloc")
     return out
 
 

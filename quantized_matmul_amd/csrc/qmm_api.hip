@@ -9,11 +9,21 @@
 #include <string.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "qmm.h"
 #include "qmm_internal.h"
 
 namespace {
+
+// Fixed device scratch of qmm_matmul_noalloc: the quantized activations (at most
+// QMM_NOALLOC_ACT_BYTES) followed by the stream-K partial tiles.  A file-scope
+// device array: every device the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, never the
+// device memory: host code uses only the address that hipGetSymbolAddress returns
+// for the current device (noalloc_scratch below).
+constexpr size_t kNoallocBytes = (size_t)QMM_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoallocBytes];
 
 constexpr int kMaxDevices = 64;
 int g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
@@ -37,6 +47,27 @@ int check_device()
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// The device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int noalloc_scratch(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return QMM_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return QMM_ERR_DEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QMM_OK;
+}
 
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
@@ -596,6 +627,33 @@ int qmm_matmul(int type, const void* W, const float* x, int nt, int od, int id, 
     return matmul_q8_checked(kind, type, W, q, d, s, nt, od, id, out, nullptr, stream);
 }
 
+int qmm_matmul_noalloc(int type, const void* W, const float* x, int nt, int od, int id, float* out, void* stream)
+{
+    if (!W || !x || !out)
+        return QMM_ERR_ARG;
+    int rc = check_type(type);
+    if (rc)
+        return rc;
+    rc = check_shape(nt, od, id);
+    if (rc)
+        return rc;
+    if (!aligned16(W) || !aligned16(x) || !aligned16(out))
+        return QMM_ERR_ALIGN;
+    if (qmm_act_bytes(nt, id) > (size_t)QMM_NOALLOC_ACT_BYTES)
+        return QMM_ERR_SCRATCH;
+    rc = check_device();
+    if (rc)
+        return rc;
+    void* ws = nullptr;
+    rc = noalloc_scratch(&ws);
+    if (rc)
+        return rc;
+    static_assert(QMM_NOALLOC_SCRATCH_BYTES >= QMM_NOALLOC_ACT_BYTES, "the scratch holds the activation region");
+    // the same launches as qmm_matmul with a workspace of the whole scratch: the q8
+    // plane at its start, the stream-K partial tiles after it where they fit
+    return qmm_matmul(type, W, x, nt, od, id, out, ws, kNoallocBytes, stream);
+}
+
 int qmm_group_dots(int kind, int type, const void* W, const int8_t* q, int nt, int od, int id,
                    int32_t* S, void* stream)
 {
@@ -645,6 +703,9 @@ const char* qmm_strerror(int status)
     case QMM_ERR_WORKSPACE: return "workspace too small (see qmm_act_bytes)";
     case QMM_ERR_DEVICE: return "current device is not gfx950";
     case QMM_ERR_LAUNCH: return "kernel launch failed";
+    case QMM_ERR_SCRATCH:
+        return "call too large for the fixed scratch of qmm_matmul_noalloc (qmm_act_bytes(nt, id) > "
+               "QMM_NOALLOC_ACT_BYTES)";
     default: return "unknown status";
     }
 }

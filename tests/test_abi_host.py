@@ -272,3 +272,22 @@ def test_mmq_tile_choice():
     assert qmm.qmm_mmq_tile(33, 131072, 256) == T128
     with pytest.raises(qmm.QmmError):
         qmm.qmm_mmq_tile(9, 65, 300)
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch():
+    """qmm_matmul_noalloc refuses, before any device work, a call whose quantized
+    activations exceed QMM_NOALLOC_ACT_BYTES; a call that fits gets past that check
+    (and, with no gfx950 device here, stops at the device check)."""
+    L = qmm.lib()
+    P = ctypes.c_void_p
+    fake = P(0x10000)   # non-null, aligned; never dereferenced on these paths
+    nt, idim = 2048, 12288
+    assert qmm.qmm_act_bytes(nt, idim) > qmm.QMM_NOALLOC_ACT_BYTES
+    assert L.qmm_matmul_noalloc(1, fake, fake, nt, 64, idim, fake, None) == qmm.QMM_ERR_SCRATCH
+    assert "scratch" in qmm.strerror(qmm.QMM_ERR_SCRATCH)
+    assert qmm.qmm_act_bytes(512, 12288) <= qmm.QMM_NOALLOC_ACT_BYTES
+    rc = L.qmm_matmul_noalloc(1, fake, fake, 512, 64, 12288, fake, None)
+    assert rc != qmm.QMM_ERR_SCRATCH and rc < 0
+    assert L.qmm_matmul_noalloc(1, None, fake, 1, 64, 256, fake, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_matmul_noalloc(1, fake, fake, 1, 64, 300, fake, None) == qmm.QMM_ERR_SHAPE
+    assert L.qmm_matmul_noalloc(1, P(0x10004), fake, 1, 64, 256, fake, None) == qmm.QMM_ERR_ALIGN
