@@ -136,7 +136,11 @@ def mmq_kernel(qmm, nt, od, idim):
     8 XCDs."""
     if qmm.qmm_streamk_preferred(qmm.QMM_TYPE_Q4_K, nt, od, idim):
         return "qmm::mmq_q4k_streamk_kernel<4, 2>", 256 * 512
-    wr, wc, ks = MMQ_TILES[qmm.qmm_mmq_tile(nt, od, idim)]
+    tile = qmm.qmm_mmq_tile(nt, od, idim)
+    tiles = -(-nt // 64) * -(-od // 128)
+    if tile == qmm.QMM_KIND_MMQ_128X64 and tiles > 256:   # the 4-wave kernel of 32 x 64 per wave
+        return "qmm::{anonymous}::mmq_q4k_v2_kernel<false>", 8 * -(-tiles // 8) * 256
+    wr, wc, ks = MMQ_TILES[tile]
     tiles = -(-nt // (32 * wc)) * -(-od // (32 * wr))
     return f"qmm::mmq_q4k_kernel<{wr}, {wc}, {ks}, false>", 8 * -(-tiles // 8) * 64 * wr * wc * ks
 

@@ -220,6 +220,95 @@ __global__ __launch_bounds__(256) void valu_instr_kernel(int iters, float f, uin
         sink[blockIdx.x] = 1;
 }
 
+// Shadow of an MFMA: per step one v_mfma_i32_32x32x32_i8 (accumulator input a fixed
+// register block, result to fresh registers, as in the matrix kernels) followed by
+// NV independent v_fmac_f32 (VOP2, VGPR operands) that do not read it; one element
+// of every result is folded in one step later.  Time against the MFMA-only and the
+// VALU-only forms gives how much VALU work a wave hides behind its own MFMAs.
+template <int NV, bool DO_M, bool DO_V>
+__global__ __launch_bounds__(256) void shadow_kernel(int iters, float f, uint32_t* __restrict__ sink)
+{
+    const int lane = threadIdx.x & 63;
+    v4i a = {lane, lane + 1, lane + 2, lane + 3};
+    const v4i b = {3 - lane, 2, 1, lane};
+    v16i k;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        k[i] = 0x4B400000 + lane + i;
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        acc[i] = f * (float)(lane + i);
+    const float pv = f * 0.5f + (float)lane, qv = f - (float)lane;
+    uint32_t x = 0;
+    v16i prev = k;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if (DO_M) {
+                const v16i C = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, k, 0, 0, 0);
+                x ^= (uint32_t)prev[r];
+                prev = C;
+            }
+            if (DO_V) {
+#pragma unroll
+                for (int v = 0; v < NV; ++v)
+                    asm volatile("v_fmac_f32 %0, %1, %2" : "+v"(acc[(r * NV + v) & 31]) : "v"(pv), "v"(qv));
+            }
+            a.x += 1;
+        }
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        t += acc[i];
+    if (x == kNever || __float_as_uint(t) == kNever)
+        sink[blockIdx.x] = 1;
+}
+
+// The MFMA mix of a per-32 matrix step, MFMAs only: per round MODE 0: two
+// v_mfma_i32_32x32x32_i8 whose accumulator input is a fixed register block
+// (results to fresh registers) and one v_mfma_f32_32x32x1_2b_f32; MODE 1: the two
+// int8 MFMAs alone; MODE 2: the outer product alone; MODE 3: two int8 MFMAs
+// accumulating in place.  One element of every result is folded into a running
+// xor (one VALU op per MFMA) so no MFMA is dead.
+template <int MODE>
+__global__ __launch_bounds__(256) void mfma_mix_kernel(int iters, float f, uint32_t* __restrict__ sink)
+{
+    const int lane = threadIdx.x & 63;
+    v4i a = {lane, lane + 1, lane + 2, lane + 3}, b = {3 - lane, 2, 1, lane};
+    v16i k;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        k[i] = 0x4B400000 + lane + i;
+    v16i acc0 = k, acc1 = k;
+    uint32_t x = 0;
+    const float fa = f * (float)lane, fb = f - (float)lane;
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if constexpr (MODE == 0 || MODE == 2) {
+                const v32f P = __builtin_amdgcn_mfma_f32_32x32x1f32(fa + (float)r, fb, (v32f){}, 0, 0, 0);
+                x ^= __float_as_uint(P[r]);
+            }
+            if constexpr (MODE == 0 || MODE == 1) {
+                const v16i C0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, k, 0, 0, 0);
+                const v16i C1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, k, 0, 0, 0);
+                x ^= (uint32_t)(C0[r] + C1[15 - r]);
+            }
+            if constexpr (MODE == 3) {
+                acc0 = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, acc1, 0, 0, 0);
+            }
+            a.x += 1;
+        }
+    }
+    if constexpr (MODE == 3)
+        x ^= (uint32_t)(acc0[lane & 15] + acc1[3]);
+    if (x == kNever)
+        sink[blockIdx.x] = x;
+}
+
 // LDS read bandwidth: every wave reads 16 bytes per lane per ds_read_b128 from
 // addresses spread over a 64 KiB LDS buffer (consecutive lanes, consecutive 16-byte
 // words: no bank conflicts), 16 reads in flight per round.
@@ -376,6 +465,52 @@ int peaks_valu_instr(int op, int blocks, int iters, uint32_t* sink, hipStream_t 
     case N: hipLaunchKernelGGL(valu_instr_kernel<N>, grid, block, 0, stream, iters, 0.5f, sink); break;
     QMM_VI(0) QMM_VI(1) QMM_VI(2) QMM_VI(3) QMM_VI(4) QMM_VI(5) QMM_VI(6) QMM_VI(7) QMM_VI(8) QMM_VI(9)
 #undef QMM_VI
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+// MFMA shadow: nv in {0, 4, 8, 12, 16, 24, 32} VALU per MFMA; parts 3 both, 1 MFMA
+// only, 2 VALU only.  blocks workgroups of 256 threads, iters rounds of 8 steps.
+int peaks_shadow(int nv, int parts, int blocks, int iters, uint32_t* sink, hipStream_t stream)
+{
+    if (!sink || blocks < 1 || iters < 1 || parts < 1 || parts > 3)
+        return hipErrorInvalidValue;
+    const dim3 grid(blocks), block(256);
+#define QMM_SH(N)                                                                                            \
+    do {                                                                                                     \
+        if (parts == 3)                                                                                      \
+            hipLaunchKernelGGL((shadow_kernel<N, true, true>), grid, block, 0, stream, iters, 0.5f, sink);   \
+        else if (parts == 1)                                                                                 \
+            hipLaunchKernelGGL((shadow_kernel<N, true, false>), grid, block, 0, stream, iters, 0.5f, sink);  \
+        else                                                                                                 \
+            hipLaunchKernelGGL((shadow_kernel<N, false, true>), grid, block, 0, stream, iters, 0.5f, sink);  \
+    } while (0)
+    switch (nv) {
+    case 4: QMM_SH(4); break;
+    case 8: QMM_SH(8); break;
+    case 12: QMM_SH(12); break;
+    case 16: QMM_SH(16); break;
+    case 24: QMM_SH(24); break;
+    case 32: QMM_SH(32); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef QMM_SH
+    return hipGetLastError();
+}
+
+// MFMA mix (mode 0..3 of mfma_mix_kernel), blocks workgroups of 256 threads, iters
+// rounds of 8 steps.
+int peaks_mfma_mix(int mode, int blocks, int iters, uint32_t* sink, hipStream_t stream)
+{
+    if (!sink || blocks < 1 || iters < 1)
+        return hipErrorInvalidValue;
+    const dim3 grid(blocks), block(256);
+    switch (mode) {
+    case 0: hipLaunchKernelGGL(mfma_mix_kernel<0>, grid, block, 0, stream, iters, 0.5f, sink); break;
+    case 1: hipLaunchKernelGGL(mfma_mix_kernel<1>, grid, block, 0, stream, iters, 0.5f, sink); break;
+    case 2: hipLaunchKernelGGL(mfma_mix_kernel<2>, grid, block, 0, stream, iters, 0.5f, sink); break;
+    case 3: hipLaunchKernelGGL(mfma_mix_kernel<3>, grid, block, 0, stream, iters, 0.5f, sink); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

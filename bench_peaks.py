@@ -52,7 +52,10 @@ def lib():
         L.peaks_overlap.argtypes = [I, I, I, I, I, P, P]
         L.peaks_valu_instr.argtypes = [I, I, I, P, P]
         L.peaks_lds_read.argtypes = [I, I, P, P]
-        for f in ("peaks_stream_read", "peaks_rate", "peaks_overlap", "peaks_valu_instr", "peaks_lds_read"):
+        L.peaks_mfma_mix.argtypes = [I, I, I, P, P]
+        L.peaks_shadow.argtypes = [I, I, I, I, P, P]
+        for f in ("peaks_stream_read", "peaks_rate", "peaks_overlap", "peaks_valu_instr", "peaks_lds_read",
+                  "peaks_mfma_mix", "peaks_shadow"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -240,10 +243,60 @@ def overlap(torch, reps=3):
     return res
 
 
+MIX_MODES = ["2 int8 (fixed accumulator input) + 1 f32 outer pair", "2 int8 (fixed accumulator input)",
+             "1 f32 outer pair", "2 int8 (accumulating)"]
+
+
+def mfma_mix(torch, clock_ghz, reps=3):
+    """SIMD clocks per step of each MFMA mix (mfma_mix_kernel), 1 and 2 waves per SIMD."""
+    L = lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = []
+    for mode, name in enumerate(MIX_MODES):
+        row = {"mix": name}
+        for w in (1, 2):
+            blocks, iters = CUS * w, 1024 // w
+            sink = torch.empty(blocks, dtype=torch.int32, device="cuda:0")
+
+            def launch(i, mode=mode):
+                _check(L.peaks_mfma_mix(mode, blocks, iters, ctypes.c_void_p(sink.data_ptr()), st), "mfma_mix")
+
+            ms = statistics.median(_timed(torch, launch, 1, reps))
+            row[f"clocks_per_step_w{w}"] = round(ms * 1e-3 * clock_ghz * 1e9 / (8 * iters * w), 1)
+        out.append(row)
+    return out
+
+
+def shadow(torch, clock_ghz, reps=3):
+    """SIMD clocks per step (one int8 MFMA + nv VOP2 fmacs in one wave) at 1 and 2
+    waves per SIMD, with the MFMA-only and VALU-only times: hidden = the share of
+    the shorter part that does not add to the time."""
+    L = lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = []
+    for nv in (4, 8, 12, 16, 24, 32):
+        row = {"valu_per_mfma": nv}
+        for w in (1, 2):
+            blocks, iters = CUS * w, 1024 // w
+            sink = torch.empty(blocks, dtype=torch.int32, device="cuda:0")
+            t = {}
+            for parts in (1, 2, 3):
+                def launch(i, parts=parts):
+                    _check(L.peaks_shadow(nv, parts, blocks, iters, ctypes.c_void_p(sink.data_ptr()), st), "shadow")
+
+                t[parts] = statistics.median(_timed(torch, launch, 1, reps)) * 1e-3 * clock_ghz * 1e9 / (8 * iters * w)
+            row[f"w{w}"] = {"mfma": round(t[1], 1), "valu": round(t[2], 1), "both": round(t[3], 1),
+                            "hidden": round((t[1] + t[2] - t[3]) / min(t[1], t[2]), 3)}
+        out.append(row)
+    return out
+
+
 def run_all(torch, sizes):
     res = {"stream_read": stream_read(torch, sizes), "mfma": mfma_rate(torch), "valu": valu_rate(torch)}
     ghz = res["valu"]["fma"][-1]["clock_GHz"] or 2.4
     res["valu_instr"] = valu_instr(torch, ghz)
     res["lds_read"] = lds_read(torch, ghz)
+    res["mfma_mix"] = mfma_mix(torch, res["mfma"]["int8"][-1]["clock_GHz"] or ghz)
+    res["shadow"] = shadow(torch, res["mfma"]["int8"][-1]["clock_GHz"] or ghz)
     res["overlap"] = overlap(torch)
     return res

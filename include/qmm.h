@@ -103,7 +103,10 @@ enum {
     /* MMQ with a given tile shape (qmm_matmul_q8_kind and qmm_mmq_tile only): */
     QMM_KIND_MMQ_128X64 = 3,        /* 128 rows x 64 tokens, 8 waves */
     QMM_KIND_MMQ_64X64 = 4,         /* 64 rows x 64 tokens, 4 waves */
-    QMM_KIND_MMQ_64X64_SPLITK = 5   /* 64 x 64, 8 waves in two groups splitting K */
+    QMM_KIND_MMQ_64X64_SPLITK = 5,  /* 64 x 64, 8 waves in two groups splitting K */
+    QMM_KIND_MMQ_WAVE32X64 = 6      /* Q4_K only: 128 x 64, 4 waves of 32 rows x 64 tokens,
+                                       weights straight into registers (the default Q4_K
+                                       matrix kernel) */
 };
 
 /* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K, Q4_0), *176
@@ -183,7 +186,8 @@ int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, cons
                   int od, int id, float* out, void* stream);
 
 /* Same as qmm_matmul_q8 but with the kernel chosen by the caller (kind =
- * QMM_KIND_MMVQ, QMM_KIND_MMQ, or one of the QMM_KIND_MMQ_* tile shapes; any nt:
+ * QMM_KIND_MMVQ, QMM_KIND_MMQ, or one of the QMM_KIND_MMQ_* tile shapes, the last
+ * for Q4_K only, else QMM_ERR_TYPE; any nt:
  * above 8 tokens MMVQ runs one launch per slice of 8 tokens, each slice giving
  * the same bits as that slice alone).  For tests and measurement of every kernel
  * variant on one shape.  Unknown kind: QMM_ERR_ARG. */

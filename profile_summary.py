@@ -34,6 +34,7 @@ _CSRC = os.path.join(_HERE, "quantized_matmul_amd", "csrc")
 KERNEL_SOURCES = {
     "qmm::mmvq_": ("qmm_mmvq.hip", "qmm_internal.h"),
     "qmm::mmq_": ("qmm_mmq.hip", "qmm_mmq_common.h", "qmm_internal.h"),
+    "qmm::{anonymous}::mmq_q4k_v2_": ("qmm_mmq2.hip", "qmm_mmq_common.h", "qmm_internal.h"),
     "qmm::mmq_k4_q8k_": ("qmm_mmq_q8k.hip", "qmm_mmq_common.h", "qmm_internal.h"),
     "qmm::mmq_q6k_q8k_": ("qmm_mmq_q8k.hip", "qmm_mmq_common.h", "qmm_internal.h"),
     "qmm::quantize_": ("qmm_quantize.hip", "qmm_internal.h"),

@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqmm.so")
-SOURCES = ["qmm_api.hip", "qmm_quantize.hip", "qmm_fused.hip", "qmm_mmvq.hip", "qmm_mmq.hip",
+SOURCES = ["qmm_api.hip", "qmm_quantize.hip", "qmm_fused.hip", "qmm_mmvq.hip", "qmm_mmq.hip", "qmm_mmq2.hip",
            "qmm_mmq_q8k.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

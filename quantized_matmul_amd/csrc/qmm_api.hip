@@ -579,8 +579,10 @@ int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, cons
 int qmm_matmul_q8_kind(int kind, int type, const void* W, const int8_t* q, const float* d,
                        const float* s, int nt, int od, int id, float* out, void* stream)
 {
-    if (kind < QMM_KIND_MMVQ || kind > QMM_KIND_MMQ_64X64_SPLITK)
+    if (kind < QMM_KIND_MMVQ || kind > QMM_KIND_MMQ_WAVE32X64)
         return QMM_ERR_ARG;
+    if (kind == QMM_KIND_MMQ_WAVE32X64 && type != QMM_TYPE_Q4_K)
+        return QMM_ERR_TYPE;
     int rc = validate_q8(type, W, q, d, s, nt, od, id, out);
     if (rc)
         return rc;

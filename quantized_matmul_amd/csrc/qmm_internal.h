@@ -31,6 +31,10 @@ hipError_t launch_mmvq(int type, const uint8_t* W, const int8_t* q, const float*
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
                       int nt, int od, int id, float* out, int32_t* S, hipStream_t st, int tile = 0);
 int mmq_tile_choice(int nt, int od, int id);
+// Q4_K matrix kernel of 4 waves x (32 rows x 64 tokens) per workgroup (qmm_mmq2.hip);
+// S != null writes the integer dots instead (S [nt][od][nsb][8]).
+hipError_t launch_mmq_q4k_v2(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od,
+                             int id, float* out, int32_t* S, hipStream_t st);
 // Stream-K (Q4_K and Q6_K in both layouts): workspace of mmq_streamk_ws_bytes() bytes, 16-byte aligned.
 size_t mmq_streamk_ws_bytes();
 hipError_t launch_mmq_streamk(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt,

@@ -220,28 +220,6 @@ __device__ __forceinline__ void q4_stage(Q4Smem<BM, BN, Q5>& sm, const v4i (&pq)
 
 }
 
-// Store one wave's 32 x 32 result tile (lane: token tg, rows r0 + 8k + 4 lh + 0..3
-// from v[4k .. 4k+3]) into out [nt][od], masked at the edges.
-__device__ __forceinline__ void store_tile(const v16f& v, float* __restrict__ out, int nt, int od, int tg, int r0,
-                                           int lh)
-{
-    if (tg >= nt)
-        return;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int rg = r0 + 8 * k + 4 * lh;
-        float* o = out + (size_t)tg * od + rg;
-        if (rg + 3 < od && (od & 3) == 0) {
-            *reinterpret_cast<float4*>(o) = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
-        } else {
-            if (rg < od) o[0] = v[4 * k];
-            if (rg + 1 < od) o[1] = v[4 * k + 1];
-            if (rg + 2 < od) o[2] = v[4 * k + 2];
-            if (rg + 3 < od) o[3] = v[4 * k + 3];
-        }
-    }
-}
-
 // The LDS operands of one compute step (sub-blocks 2p and 2p + 1): this lane's 16
 // code bytes (row arow), its two 16-byte activation pieces (token btok), and the
 // scale factors of sub-block 2p + lh for the outer products.
@@ -1386,6 +1364,15 @@ hipError_t launch_mmq_streamk(int type, const uint8_t* W, const int8_t* q, const
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
                       int nt, int od, int id, float* out, int32_t* S, hipStream_t st, int tile)
 {
+    // Q4_K: the kernel of 4 waves of 32 rows x 64 tokens (qmm_mmq2.hip) where the
+    // cost model picks 128 x 64 tiles and there are more tiles than CUs (two of its
+    // workgroups share a CU; 3-10 % faster than this file's 8-wave tiles there; on
+    // fewer tiles, or the split-K shapes, this file's kernels win), or when asked for
+    const long t128 = (long)((nt + 63) / 64) * ((od + 127) / 128);
+    if (type == 1 && (tile == 4 || (tile == 0 && (S || (t128 > 256 && mmq_tile_choice(nt, od, id) == 1)))))
+        return launch_mmq_q4k_v2(W, q, d, s, nt, od, id, out, S, st);
+    if (tile == 4)
+        return hipErrorInvalidValue;
     if (S)
         return launch_tile<2, 2, 1, true>(type, W, q, d, s, nt, od, id, out, S, st);
     switch (tile ? tile : mmq_tile_choice(nt, od, id)) {

@@ -136,6 +136,28 @@ __device__ __forceinline__ void q6_stage_codes(int8_t* wrow, const uint32_t (&pl
     *reinterpret_cast<int4*>(wrow + e1 + 64) = cb;
 }
 
+// Store one wave's 32 x 32 result tile (lane: token tg, rows r0 + 8k + 4 lh + 0..3
+// from v[4k .. 4k+3]) into out [nt][od], masked at the edges.
+__device__ __forceinline__ void store_tile(const v16f& v, float* __restrict__ out, int nt, int od, int tg, int r0,
+                                           int lh)
+{
+    if (tg >= nt)
+        return;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int rg = r0 + 8 * k + 4 * lh;
+        float* o = out + (size_t)tg * od + rg;
+        if (rg + 3 < od && (od & 3) == 0) {
+            *reinterpret_cast<float4*>(o) = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+        } else {
+            if (rg < od) o[0] = v[4 * k];
+            if (rg + 1 < od) o[1] = v[4 * k + 1];
+            if (rg + 2 < od) o[2] = v[4 * k + 2];
+            if (rg + 3 < od) o[3] = v[4 * k + 3];
+        }
+    }
+}
+
 // Tile index of this workgroup: consecutive tiles (same row block, successive
 // token blocks) go to the same XCD.  Returns -1 for a padding workgroup.
 __device__ __forceinline__ int xcd_tile(int ntiles)

@@ -149,7 +149,10 @@ def test_mmq_every_tile_shape(qtype, nt, od, idim):
     rq, rd, rs = oracle.quantize(x)
     ref, mag = oracle.matmul_q8(qtype, W, rq, rd, rs, od)
     args = (_up(W), _up(rq), _up(rd), _up(rs), od)
-    for kind in (qmm.QMM_KIND_MMQ_128X64, qmm.QMM_KIND_MMQ_64X64, qmm.QMM_KIND_MMQ_64X64_SPLITK):
+    kinds = [qmm.QMM_KIND_MMQ_128X64, qmm.QMM_KIND_MMQ_64X64, qmm.QMM_KIND_MMQ_64X64_SPLITK]
+    if qtype == Q4:
+        kinds.append(qmm.QMM_KIND_MMQ_WAVE32X64)
+    for kind in kinds:
         o = qmm.qmm_matmul_q8_kind(kind, qtype, *args)
         torch.cuda.synchronize()
         assert_close(o.cpu().numpy(), ref, mag, qtype, idim, f"kind {kind}")
