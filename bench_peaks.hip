@@ -22,6 +22,7 @@
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v32f __attribute__((ext_vector_type(32)));
 
 namespace {
@@ -266,6 +267,162 @@ __global__ __launch_bounds__(256) void shadow_kernel(int iters, float f, uint32_
         sink[blockIdx.x] = 1;
 }
 
+// Ping-pong of MFMA and VALU phases between the two waves of each SIMD, the step
+// of a per-32 matrix kernel: per phase a wave either issues the MFMAs of two
+// sub-blocks (2 x two int8 MFMAs with a fixed accumulator input, 2 f32 outer-product
+// pairs: 128 result registers) or runs the epilogue of the results it issued in its
+// previous MFMA phase (128 v_sub_f32 + 128 v_fma: acc += (C - bias) * P).  PP 1:
+// 512-thread workgroups, waves 0-3 in one phase and 4-7 in the other, an s_barrier
+// between phases; PP 0: every wave does its MFMA phase then its epilogue, no
+// barriers (the same work per wave).
+template <int PP>
+__global__ __launch_bounds__(512) void pingpong_kernel(int iters, float f, uint32_t* __restrict__ sink)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v4i a = {lane, lane + 1, lane + 2, lane + 3};
+    const v4i b = {3 - lane, 2, 1, lane};
+    v16i k;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        k[i] = 0x4B400000 + lane + i;
+    const float fk = __int_as_float(k[0]);
+    float acc[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        acc[i] = f * (float)(lane + i);
+    v16i C[4];
+    v32f P[2];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        C[m] = k;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+        P[m] = (v32f){};
+    const float fa = f * (float)lane, fb = f - (float)lane;
+    const bool second = PP && wave >= 4;
+    auto mfma_phase = [&](int r) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            P[m] = __builtin_amdgcn_mfma_f32_32x32x1f32(fa + (float)(r + m), fb, (v32f){}, 0, 0, 0);
+            C[2 * m] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, k, 0, 0, 0);
+            C[2 * m + 1] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b, a, k, 0, 0, 0);
+        }
+        a.x += 1;
+    };
+    auto valu_phase = [&]() {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const v16f S0 = __builtin_bit_cast(v16f, C[2 * m]) - fk;
+            const v16f S1 = __builtin_bit_cast(v16f, C[2 * m + 1]) - fk;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                acc[i] = fmaf(S0[i], P[m][i], acc[i]);
+                acc[16 + i] = fmaf(S1[i], P[m][16 + i], acc[16 + i]);
+            }
+        }
+    };
+    for (int r = 0; r < iters; ++r) {
+        if (PP) {
+            if (second)
+                valu_phase();
+            else
+                mfma_phase(r);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if (second)
+                mfma_phase(r);
+            else
+                valu_phase();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            mfma_phase(r);
+            __builtin_amdgcn_sched_barrier(0);
+            valu_phase();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+        t += acc[i];
+    if (__float_as_uint(t) == kNever)
+        sink[blockIdx.x] = 1;
+}
+
+// Burst length of the per-32 step: per burst, NB sub-blocks over NN 32-token blocks
+// (NN int8 MFMAs per sub-block with a fixed accumulator input; f32 outer-product
+// pairs: one per sub-block for NN = 2, one per two sub-blocks for NN = 1), then the
+// epilogue of all of them (acc += (C - bias) * P).  One wave does both in turn; 2
+// waves per SIMD.
+template <int NB, int NN>
+__global__ __launch_bounds__(256) void burst_kernel(int iters, float f, uint32_t* __restrict__ sink)
+{
+    const int lane = threadIdx.x & 63;
+    v4i a = {lane, lane + 1, lane + 2, lane + 3};
+    const v4i b = {3 - lane, 2, 1, lane};
+    v16i k;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        k[i] = 0x4B400000 + lane + i;
+    const float fk = __int_as_float(k[0]);
+    float acc[16 * NN];
+#pragma unroll
+    for (int i = 0; i < 16 * NN; ++i)
+        acc[i] = f * (float)(lane + i);
+    const float fb = f - (float)lane;
+    constexpr int NP = NN == 2 ? NB : NB / 2;   // outer-product pairs per burst
+    // distinct operands per MFMA (identical MFMAs would be computed once)
+    v4i av[NB];
+    float fav[NP];
+#pragma unroll
+    for (int m = 0; m < NB; ++m)
+        av[m] = (v4i){lane + m, lane + 1, lane + 2 * m, lane + 3};
+#pragma unroll
+    for (int m = 0; m < NP; ++m)
+        fav[m] = f * (float)(lane + m);
+    v4i bv[NN];
+#pragma unroll
+    for (int n = 0; n < NN; ++n)
+        bv[n] = (v4i){3 - lane, 2 + n, 1, lane};
+    for (int r = 0; r < iters; ++r) {
+        v16i C[NB * NN];
+        v32f P[NP];
+#pragma unroll
+        for (int m = 0; m < NP; ++m)
+            P[m] = __builtin_amdgcn_mfma_f32_32x32x1f32(fav[m], fb, (v32f){}, 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < NB * NN; ++m)
+            C[m] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av[m / NN], bv[m % NN], k, 0, 0, 0);
+#pragma unroll
+        for (int n = 0; n < NN; ++n)
+            bv[n].x += 1;
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int sbk = 0; sbk < NB; ++sbk) {
+#pragma unroll
+            for (int n = 0; n < NN; ++n) {
+                const v16f S = __builtin_bit_cast(v16f, C[sbk * NN + n]) - fk;
+                // the scale products of (sub-block sbk, block n): pair NN == 2: P[sbk] half n;
+                // NN == 1: P[sbk / 2] half sbk % 2
+                const int pm = NN == 2 ? sbk : sbk / 2, ph = NN == 2 ? n : sbk % 2;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    acc[16 * n + i] = fmaf(S[i], P[pm][16 * ph + i], acc[16 * n + i]);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16 * NN; ++i)
+        t += acc[i];
+    if (__float_as_uint(t) == kNever)
+        sink[blockIdx.x] = 1;
+}
+
 // The MFMA mix of a per-32 matrix step, MFMAs only: per round MODE 0: two
 // v_mfma_i32_32x32x32_i8 whose accumulator input is a fixed register block
 // (results to fresh registers) and one v_mfma_f32_32x32x1_2b_f32; MODE 1: the two
@@ -496,6 +653,39 @@ int peaks_shadow(int nv, int parts, int blocks, int iters, uint32_t* sink, hipSt
     default: return hipErrorInvalidValue;
     }
 #undef QMM_SH
+    return hipGetLastError();
+}
+
+// Ping-pong probe: pp 1 (phases alternate between the wave halves) or 0 (serial).
+// blocks workgroups of 512 threads, iters rounds (each: one MFMA phase and one
+// epilogue phase per wave).
+int peaks_pingpong(int pp, int blocks, int iters, uint32_t* sink, hipStream_t stream)
+{
+    if (!sink || blocks < 1 || iters < 1 || pp < 0 || pp > 1)
+        return hipErrorInvalidValue;
+    if (pp)
+        hipLaunchKernelGGL(pingpong_kernel<1>, dim3(blocks), dim3(512), 0, stream, iters, 0.5f, sink);
+    else
+        hipLaunchKernelGGL(pingpong_kernel<0>, dim3(blocks), dim3(512), 0, stream, iters, 0.5f, sink);
+    return hipGetLastError();
+}
+
+// Burst probe: mode 0..5 = (NB, NN) of (1,2) (2,2) (2,1) (4,1) (8,1) (1,1)... see
+// peaks_burst_modes; blocks workgroups of 256 threads, iters bursts.
+int peaks_burst(int mode, int blocks, int iters, uint32_t* sink, hipStream_t stream)
+{
+    if (!sink || blocks < 1 || iters < 1)
+        return hipErrorInvalidValue;
+    const dim3 grid(blocks), block(256);
+    switch (mode) {
+    case 0: hipLaunchKernelGGL((burst_kernel<1, 2>), grid, block, 0, stream, iters, 0.5f, sink); break;
+    case 1: hipLaunchKernelGGL((burst_kernel<2, 2>), grid, block, 0, stream, iters, 0.5f, sink); break;
+    case 2: hipLaunchKernelGGL((burst_kernel<2, 1>), grid, block, 0, stream, iters, 0.5f, sink); break;
+    case 3: hipLaunchKernelGGL((burst_kernel<4, 1>), grid, block, 0, stream, iters, 0.5f, sink); break;
+    case 4: hipLaunchKernelGGL((burst_kernel<8, 1>), grid, block, 0, stream, iters, 0.5f, sink); break;
+    case 5: hipLaunchKernelGGL((burst_kernel<4, 2>), grid, block, 0, stream, iters, 0.5f, sink); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -35,7 +35,9 @@ def build(out: str = LIB) -> str:
     from quantized_matmul_amd import _build
 
     tmp = out + ".tmp"
-    subprocess.run([_build.HIPCC, *_build.FLAGS, SRC, "-o", tmp], check=True)
+    # MFMA results in VGPRs, where the library's matrix kernels get them (the compiler
+    # otherwise moves the results of these small kernels to AGPRs and reads them back)
+    subprocess.run([_build.HIPCC, *_build.FLAGS, "-mllvm", "-amdgpu-mfma-vgpr-form=1", SRC, "-o", tmp], check=True)
     os.replace(tmp, out)
     return out
 
@@ -54,8 +56,10 @@ def lib():
         L.peaks_lds_read.argtypes = [I, I, P, P]
         L.peaks_mfma_mix.argtypes = [I, I, I, P, P]
         L.peaks_shadow.argtypes = [I, I, I, I, P, P]
+        L.peaks_pingpong.argtypes = [I, I, I, P, P]
+        L.peaks_burst.argtypes = [I, I, I, P, P]
         for f in ("peaks_stream_read", "peaks_rate", "peaks_overlap", "peaks_valu_instr", "peaks_lds_read",
-                  "peaks_mfma_mix", "peaks_shadow"):
+                  "peaks_mfma_mix", "peaks_shadow", "peaks_pingpong", "peaks_burst"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -291,6 +295,48 @@ def shadow(torch, clock_ghz, reps=3):
     return out
 
 
+def pingpong(torch, clock_ghz, reps=3):
+    """SIMD clocks per round (per wave: the MFMAs of two per-32 sub-blocks over two
+    token blocks and their epilogue) with the phases alternating between the two
+    waves of a SIMD (barrier between phases) and with each wave doing both in turn."""
+    L = lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    blocks, iters = CUS, 512
+    sink = torch.empty(blocks, dtype=torch.int32, device="cuda:0")
+    out = {}
+    for pp, key in ((0, "serial"), (1, "pingpong")):
+        def launch(i, pp=pp):
+            _check(L.peaks_pingpong(pp, blocks, iters, ctypes.c_void_p(sink.data_ptr()), st), "pingpong")
+
+        ms = statistics.median(_timed(torch, launch, 1, reps))
+        out[key] = round(ms * 1e-3 * clock_ghz * 1e9 / iters, 1)   # SIMD clocks per round (2 waves)
+    return out
+
+
+BURST_MODES = [(1, 2), (2, 2), (2, 1), (4, 1), (8, 1), (4, 2)]   # (sub-blocks per burst, token blocks)
+
+
+def burst(torch, clock_ghz, reps=3):
+    """SIMD clocks per 32 x 32 x 32 block (one int8 MFMA, its share of the outer
+    products and its 32-instruction epilogue) by burst length, 2 waves per SIMD."""
+    L = lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = []
+    for mode, (nb, nn) in enumerate(BURST_MODES):
+        blocks = CUS * 2
+        iters = 2048 // (nb * nn)
+        sink = torch.empty(blocks, dtype=torch.int32, device="cuda:0")
+
+        def launch(i, mode=mode):
+            _check(L.peaks_burst(mode, blocks, iters, ctypes.c_void_p(sink.data_ptr()), st), "burst")
+
+        ms = statistics.median(_timed(torch, launch, 1, reps))
+        per_block = ms * 1e-3 * clock_ghz * 1e9 / (iters * nb * nn * 2)   # 2 waves per SIMD
+        out.append({"subblocks_per_burst": nb, "token_blocks": nn, "clocks_per_block": round(per_block, 1),
+                    "int8_frac_of_mfma": round(32.8 / per_block, 3)})
+    return out
+
+
 def run_all(torch, sizes):
     res = {"stream_read": stream_read(torch, sizes), "mfma": mfma_rate(torch), "valu": valu_rate(torch)}
     ghz = res["valu"]["fma"][-1]["clock_GHz"] or 2.4
@@ -298,5 +344,7 @@ def run_all(torch, sizes):
     res["lds_read"] = lds_read(torch, ghz)
     res["mfma_mix"] = mfma_mix(torch, res["mfma"]["int8"][-1]["clock_GHz"] or ghz)
     res["shadow"] = shadow(torch, res["mfma"]["int8"][-1]["clock_GHz"] or ghz)
+    res["pingpong"] = pingpong(torch, res["mfma"]["int8"][-1]["clock_GHz"] or ghz)
+    res["burst"] = burst(torch, res["mfma"]["int8"][-1]["clock_GHz"] or ghz)
     res["overlap"] = overlap(torch)
     return res
