@@ -698,6 +698,9 @@ def cpu_baseline(calls):
     return res
 
 
+KIND_LABEL = {1: "mmvq", 7: "small_batch"}   # QMM_KIND_MMVQ, QMM_KIND_SKINNY; the rest are MMQ kernels
+
+
 def kms(c):
     """Mean per-launch matmul kernel time of a call over the timed region, in seconds."""
     return float(np.mean(c.k_ms)) * 1e-3
@@ -738,6 +741,16 @@ def report_default(line, calls, qmm, torch, read_traffic):
                         "traffic": read_traffic(COUNTERS, "qmm::mmvq_q4k_kernel<1, 4, false>", None),
                         "kernel": "mmvq_q4k_kernel<1,4,false>", "call": head.label,
                         "bytes_per_launch": int(head.kbytes)}
+
+    # decode with a few tokens (the weights streamed once for all of them)
+    few = [c for c in calls if c.qtype == Q4 and 2 <= c.nt <= 16 and not c.q8k]
+    if few:
+        line["small_batch"] = {
+            c.label: {"kernel": KIND_LABEL.get(c.kind, "mmq"), "us": round(kms(c) * 1e6, 2),
+                      "GB_s": round(c.kbytes / kms(c) / 1e9, 1),
+                      "frac_of_measured": round(c.kbytes / kms(c) / 1e9 / rd[min(rd, key=lambda b: abs(b - c.kbytes))]
+                                                ["GB_s"], 4)}
+            for c in few}
 
     big = [c for c in calls if c.nt >= 9 and not c.q8k]
     ops = sum(c.ops for c in big)
@@ -933,7 +946,7 @@ def main():
         k = float(np.mean(c.k_ms))
         qm = float(np.mean(c.q_ms))
         sp = spread[c]
-        row = {"call": c.label, "kernel": "mmvq" if c.kind == qmm.QMM_KIND_MMVQ else "mmq",
+        row = {"call": c.label, "kernel": KIND_LABEL.get(c.kind, "mmq"),
                "kernel_us": round(k * 1e3, 2), "quantize_us": round(qm * 1e3, 2),
                "kernel_us_median": round(float(np.median(sp)) * 1e3, 2),
                "kernel_us_p10_p90": [round(float(np.percentile(sp, 10)) * 1e3, 2),

@@ -104,9 +104,14 @@ enum {
     QMM_KIND_MMQ_128X64 = 3,        /* 128 rows x 64 tokens, 8 waves */
     QMM_KIND_MMQ_64X64 = 4,         /* 64 rows x 64 tokens, 4 waves */
     QMM_KIND_MMQ_64X64_SPLITK = 5,  /* 64 x 64, 8 waves in two groups splitting K */
-    QMM_KIND_MMQ_WAVE32X64 = 6      /* Q4_K only: 128 x 64, 4 waves of 32 rows x 64 tokens,
+    QMM_KIND_MMQ_WAVE32X64 = 6,     /* Q4_K only: 128 x 64, 4 waves of 32 rows x 64 tokens,
                                        weights straight into registers (the default Q4_K
                                        matrix kernel) */
+    QMM_KIND_SKINNY = 7             /* Q4_K only, nt <= 16 (else QMM_ERR_ARG): 16 x 16 x 32
+                                       int8 MFMA tiles of 16 weight rows x 16 tokens, the
+                                       weights streamed once for all tokens ([MMQ, section
+                                       12.2]: token count in registers; per-32 rescale as
+                                       MMQ); qmm_matmul's kernel for Q4_K at 4..16 tokens */
 };
 
 /* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K, Q4_0), *176
@@ -214,11 +219,15 @@ int qmm_matmul_q8_streamk(int type, const void* W, const int8_t* q, const float*
  * QMM_MMQ_TILE = 1, 2 or 3 (read once) forces one, for tuning. */
 int qmm_mmq_tile(int nt, int od, int id);
 
-/* Which kernel qmm_matmul would run for this call: QMM_KIND_MMVQ for nt <= the
- * switch, and with the default switch (8) also for 9..16 tokens on od <= 4096
- * rows, as launches on slices of 8 tokens (the MMQ tile grid of such a matrix
- * fills at most a quarter of the GPU); QMM_KIND_MMQ otherwise.  A negative status
- * for invalid arguments.  [MMQ, section 12.1]: every batch size has a dedicated
+/* Which kernel qmm_matmul would run for this call.  With the default switch (8):
+ * QMM_KIND_SKINNY for Q4_K on 4..16 tokens of a matrix of at least 2048 rows and
+ * on 9..16 tokens of any matrix; otherwise QMM_KIND_MMVQ for nt <= 8 and for 9..16
+ * tokens on od <= 4096 rows (as launches on slices of 8 tokens: the MMQ tile grid
+ * of such a matrix fills at most a quarter of the GPU); QMM_KIND_MMQ beyond.  With
+ * another switch: QMM_KIND_MMVQ for nt <= the switch, QMM_KIND_MMQ above.  A
+ * token's outputs are the same bits for every nt that runs the same kernel; the
+ * kernels differ from each other by f32 rounding.  A negative status for invalid
+ * arguments.  [MMQ, section 12.1]: every batch size has a dedicated
  * kernel, 1..8 tokens the quantized vector kernel and 9 and more the tiled matrix
  * kernel, with the threshold tuned per chip; [CH04, section 3.3]: the dispatch is a
  * function of nt with shape gates, and an unsupported shape is an error, not a
@@ -236,9 +245,10 @@ int qmm_dispatch_kind(int type, int nt, int od, int id);
  * workspace is large enough. */
 int qmm_streamk_preferred(int type, int nt, int od, int id);
 
-/* The nt at or below which MMVQ runs on every shape (default 8; environment
- * QMM_NT_SWITCH, clamped to 0..8, read once; a value other than 8 also turns off
- * the 9..16-token rule of qmm_dispatch_kind). */
+/* The nt at or below which MMVQ (or, for Q4_K, the small-batch kernel) runs on
+ * every shape (default 8; environment QMM_NT_SWITCH, clamped to 0..8, read once; a
+ * value other than 8 runs MMVQ up to it and turns off the small-batch and
+ * 9..16-token rules of qmm_dispatch_kind). */
 int qmm_nt_switch(void);
 
 /* ---- Q8_K activations: one scale per 256 values ------------------------------

@@ -37,6 +37,7 @@ KERNEL_SOURCES = {
     "qmm::{anonymous}::mmq_q4k_v2_": ("qmm_mmq2.hip", "qmm_mmq_common.h", "qmm_internal.h"),
     "qmm::mmq_k4_q8k_": ("qmm_mmq_q8k.hip", "qmm_mmq_common.h", "qmm_internal.h"),
     "qmm::mmq_q6k_q8k_": ("qmm_mmq_q8k.hip", "qmm_mmq_common.h", "qmm_internal.h"),
+    "qmm::{anonymous}::mmq_skinny_": ("qmm_skinny.hip", "qmm_mmq_common.h", "qmm_internal.h"),
     "qmm::quantize_": ("qmm_quantize.hip", "qmm_internal.h"),
     "qmm::{anonymous}::rmsnorm_": ("qmm_fused.hip", "qmm_internal.h"),
     "qmm::{anonymous}::silu_mul_": ("qmm_fused.hip", "qmm_internal.h"),

@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqmm.so")
 SOURCES = ["qmm_api.hip", "qmm_quantize.hip", "qmm_fused.hip", "qmm_mmvq.hip", "qmm_mmq.hip", "qmm_mmq2.hip",
-           "qmm_mmq_q8k.hip"]
+           "qmm_mmq_q8k.hip", "qmm_skinny.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -21,11 +21,29 @@ FLAGS = [
 ]
 
 
+# Per-file code generation options.  The small-batch kernel keeps its MFMA
+# operands and results in ordinary VGPRs (its epilogue reads every result; the
+# accumulator-register form would add one copy per value).
+FILE_FLAGS = {"qmm_skinny.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def build(out: str = LIB, extra=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
-    subprocess.run(cmd, check=True)
+    """Compile every source to an object of its own (in parallel), then link."""
+    import concurrent.futures
+    import tempfile
+
+    with tempfile.TemporaryDirectory(prefix="qmm_build_") as tmpdir:
+        def compile_one(src):
+            obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
+            cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *extra, "-I", INCLUDE, "-I", CSRC, "-c",
+                   os.path.join(CSRC, src), "-o", obj]
+            subprocess.run(cmd, check=True)
+            return obj
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+            objs = list(ex.map(compile_one, SOURCES))
+        tmp = out + ".tmp"
+        subprocess.run([HIPCC, *FLAGS, *extra, *objs, "-o", tmp], check=True)
     os.replace(tmp, out)
     return out
 

@@ -142,15 +142,37 @@ int nt_switch_value()
 
 int launched(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH; }
 
-// The kernel a call runs: MMVQ up to the switch; with the default switch also for
-// 9..16 tokens on matrices of at most 4096 rows, as launches on token slices of 8.
-// Such a matrix gives MMQ at most 64 tiles of 64 rows, a quarter of the 256 CUs,
-// and MMQ then costs about the same for any nt up to 128 (4096 x 4096: 22 us; two
-// MMVQ launches: 13.7-14.7 us; 4096 x 12288: 57 us against 32-47 us).  On 12288
-// rows the MMQ grid is large enough and two MMVQ launches lose from nt = 12.
-int dispatch_kind(int nt, int od)
+// QMM_SKINNY_CFG (RT * 100 + KS: 16*RT rows per wave, RT 1 or 2, and KS <= 8 waves
+// per workgroup of the small-batch kernel) forces its configuration, read once, for
+// tuning sweeps; 0 = by shape.
+int skinny_cfg_override()
+{
+    static int v = -1;
+    int cur = __atomic_load_n(&v, __ATOMIC_ACQUIRE);
+    if (cur >= 0)
+        return cur;
+    const char* e = getenv("QMM_SKINNY_CFG");
+    int val = e ? atoi(e) : 0;
+    if (val < 101 || val > 208 || val % 100 > 8 || val % 100 == 0)
+        val = 0;
+    __atomic_store_n(&v, val, __ATOMIC_RELEASE);
+    return val;
+}
+
+// The kernel a call runs.  With the default switch (8): Q4_K on 4..16 tokens of a
+// matrix of at least 2048 rows, and on 9..16 tokens of any matrix, runs the
+// small-batch MFMA kernel (measured on 1024..12288-row Q4_K: 4096 x 4096 nt = 4:
+// 5.1 us against MMVQ's 5.6, nt = 8: 5.5 against 7.8; 12288 x 4096 nt = 4: 9.0
+// against 10.3, nt = 8: 10.7 against 16.6; 9..16 tokens: 6-15 us against 21-58 for
+// MMQ); MMVQ up to the switch otherwise (and on 1..3 tokens, where it wins); other
+// types also on 9..16 tokens of a matrix of at most 4096 rows, as launches on token
+// slices of 8 (such a matrix gives MMQ at most 64 tiles of 64 rows, a quarter of
+// the 256 CUs; 4096 x 4096: MMQ 22 us, two MMVQ launches 13.7-14.7 us); MMQ beyond.
+int dispatch_kind(int type, int nt, int od)
 {
     const int sw = nt_switch_value();
+    if (sw == 8 && type == QMM_TYPE_Q4_K && nt <= 16 && (nt >= 9 || (nt >= 4 && od >= 2048)))
+        return QMM_KIND_SKINNY;
     if (nt <= sw || (sw == 8 && nt <= 16 && od <= 4096))
         return QMM_KIND_MMVQ;
     return QMM_KIND_MMQ;
@@ -173,7 +195,7 @@ int dispatch_kind(int nt, int od)
 bool streamk_preferred(int type, int nt, int od, int id)
 {
     const bool q6 = type == QMM_TYPE_Q6_K || type == QMM_TYPE_Q6_K_P224;
-    if ((type != QMM_TYPE_Q4_K && !q6) || dispatch_kind(nt, od) != QMM_KIND_MMQ)
+    if ((type != QMM_TYPE_Q4_K && !q6) || dispatch_kind(type, nt, od) != QMM_KIND_MMQ)
         return false;
     const long tiles = (long)((nt + 63) / 64) * ((od + 127) / 128);
     if (tiles % 256 == 0)
@@ -190,6 +212,13 @@ int matmul_q8_checked(int kind, int type, const void* W, const int8_t* q, const 
 {
     const auto st = reinterpret_cast<hipStream_t>(stream);
     const auto w = reinterpret_cast<const uint8_t*>(W);
+    if (kind == QMM_KIND_SKINNY) {
+        if (type != QMM_TYPE_Q4_K)
+            return QMM_ERR_TYPE;
+        if (nt > 16 || S)
+            return QMM_ERR_ARG;
+        return launched(qmm::launch_skinny(w, q, d, s, nt, od, id, out, st, skinny_cfg_override()));
+    }
     if (kind == QMM_KIND_MMVQ) {
         if (nt <= 8)
             return launched(qmm::launch_mmvq(type, w, q, d, s, nt, od, id, out, S, st));
@@ -552,7 +581,7 @@ int qmm_dispatch_kind(int type, int nt, int od, int id)
     rc = check_shape(nt, od, id);
     if (rc)
         return rc;
-    return dispatch_kind(nt, od);
+    return dispatch_kind(type, nt, od);
 }
 
 int qmm_mmq_tile(int nt, int od, int id)
@@ -572,17 +601,19 @@ int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, cons
     rc = check_device();
     if (rc)
         return rc;
-    const int kind = dispatch_kind(nt, od);
+    const int kind = dispatch_kind(type, nt, od);
     return matmul_q8_checked(kind, type, W, q, d, s, nt, od, id, out, nullptr, stream);
 }
 
 int qmm_matmul_q8_kind(int kind, int type, const void* W, const int8_t* q, const float* d,
                        const float* s, int nt, int od, int id, float* out, void* stream)
 {
-    if (kind < QMM_KIND_MMVQ || kind > QMM_KIND_MMQ_WAVE32X64)
+    if (kind < QMM_KIND_MMVQ || kind > QMM_KIND_SKINNY)
         return QMM_ERR_ARG;
-    if (kind == QMM_KIND_MMQ_WAVE32X64 && type != QMM_TYPE_Q4_K)
+    if ((kind == QMM_KIND_MMQ_WAVE32X64 || kind == QMM_KIND_SKINNY) && type != QMM_TYPE_Q4_K)
         return QMM_ERR_TYPE;
+    if (kind == QMM_KIND_SKINNY && nt > 16)
+        return QMM_ERR_ARG;
     int rc = validate_q8(type, W, q, d, s, nt, od, id, out);
     if (rc)
         return rc;
@@ -625,7 +656,7 @@ int qmm_matmul(int type, const void* W, const float* x, int nt, int od, int id, 
     if (streamk_preferred(type, nt, od, id) && ws_bytes >= act + qmm::mmq_streamk_ws_bytes())
         return launched(qmm::launch_mmq_streamk(type, static_cast<const uint8_t*>(W), q, d, s, nt, od, id, out,
                                                 reinterpret_cast<float*>(base + act), st));
-    const int kind = dispatch_kind(nt, od);
+    const int kind = dispatch_kind(type, nt, od);
     return matmul_q8_checked(kind, type, W, q, d, s, nt, od, id, out, nullptr, stream);
 }
 

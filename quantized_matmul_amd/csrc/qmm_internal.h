@@ -35,6 +35,11 @@ int mmq_tile_choice(int nt, int od, int id);
 // S != null writes the integer dots instead (S [nt][od][nsb][8]).
 hipError_t launch_mmq_q4k_v2(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od,
                              int id, float* out, int32_t* S, hipStream_t st);
+// Small-batch Q4_K kernel on 16 x 16 x 32 int8 MFMA tiles, 1..16 tokens
+// (qmm_skinny.hip).  cfg 0: rows per wave and waves per workgroup by the shape;
+// else RT * 100 + KS (RT 1 or 2 tiles of 16 rows per wave, KS <= 8 waves).
+hipError_t launch_skinny(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od, int id,
+                         float* out, hipStream_t st, int cfg = 0);
 // Stream-K (Q4_K and Q6_K in both layouts): workspace of mmq_streamk_ws_bytes() bytes, 16-byte aligned.
 size_t mmq_streamk_ws_bytes();
 hipError_t launch_mmq_streamk(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt,

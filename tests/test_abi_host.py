@@ -61,25 +61,35 @@ def test_act_bytes():
 
 def test_dispatch_kind_host():
     assert qmm.qmm_nt_switch() == 8
+    Q4, Q6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K
+    # Q4_K: the small-batch kernel on 4..16 tokens from 2048 rows, on 9..16 below;
+    # MMVQ on 1..3 tokens and on 4..8 tokens of fewer than 2048 rows
+    for nt in range(1, 17):
+        for od in (2048, 4096, 12288):
+            want = qmm.QMM_KIND_SKINNY if nt >= 4 else qmm.QMM_KIND_MMVQ
+            assert qmm.qmm_dispatch_kind(Q4, nt, od, 4096) == want
+        want = qmm.QMM_KIND_SKINNY if nt >= 9 else qmm.QMM_KIND_MMVQ
+        assert qmm.qmm_dispatch_kind(Q4, nt, 2047, 4096) == want
+        assert qmm.qmm_dispatch_kind(Q4, nt, 64, 12288) == want
+    assert qmm.qmm_dispatch_kind(Q4, 17, 4096, 4096) == qmm.QMM_KIND_MMQ
+    # other types: MMVQ up to 8 tokens; 9..16 tokens on token slices of 8 up to 4096
+    # rows, MMQ above
     for nt in range(1, 9):
-        for od in (4096, 12288):
-            assert qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q4_K, nt, od, 4096) == qmm.QMM_KIND_MMVQ
-    # 9..16 tokens: MMVQ on token slices of 8 up to 4096 rows, MMQ above
+        assert qmm.qmm_dispatch_kind(Q6, nt, 12288, 4096) == qmm.QMM_KIND_MMVQ
     for nt in (9, 12, 16):
-        for qt in (qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K):
-            assert qmm.qmm_dispatch_kind(qt, nt, 4096, 4096) == qmm.QMM_KIND_MMVQ
-            assert qmm.qmm_dispatch_kind(qt, nt, 64, 12288) == qmm.QMM_KIND_MMVQ
-            assert qmm.qmm_dispatch_kind(qt, nt, 4097, 4096) == qmm.QMM_KIND_MMQ
+        assert qmm.qmm_dispatch_kind(Q6, nt, 4096, 4096) == qmm.QMM_KIND_MMVQ
+        assert qmm.qmm_dispatch_kind(Q6, nt, 64, 12288) == qmm.QMM_KIND_MMVQ
+        assert qmm.qmm_dispatch_kind(Q6, nt, 4097, 4096) == qmm.QMM_KIND_MMQ
     for nt in (17, 256, 512):
-        assert qmm.qmm_dispatch_kind(qmm.QMM_TYPE_Q6_K, nt, 4096, 4096) == qmm.QMM_KIND_MMQ
+        assert qmm.qmm_dispatch_kind(Q6, nt, 4096, 4096) == qmm.QMM_KIND_MMQ
 
 
 def test_streamk_preferred_host():
     """Stream-K for Q4_K and Q6_K MMQ calls: never for a whole number of rounds of 256
     tiles (128 x 64); above 256 tiles when the last round leaves >= 10 % of the
     workgroup slots idle; within one round for K of >= 32 super-blocks (not at 128
-    tiles), or Q6_K grids of at most 64 tiles.  Never for vector-kernel calls or other
-    types."""
+    tiles), or Q6_K grids of at most 64 tiles.  Never for vector-kernel or small-batch
+    calls or other types."""
     Q4, Q6, P6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K, qmm.QMM_TYPE_Q6_K_P224
     sp = qmm.qmm_streamk_preferred
     for qt in (Q4, Q6, P6):
@@ -94,7 +104,7 @@ def test_streamk_preferred_host():
         assert not sp(qt, 128, 12288, 4096)           # 192 tiles, short K
         assert not sp(qt, 8, 4096, 65536)             # vector kernel
         assert not sp(qt, 12, 4096, 65536)            # vector kernel on slices
-        assert sp(qt, 12, 4097, 65536)                # MMQ above 4096 rows
+        assert sp(qt, 12, 4097, 65536) == (qt != Q4)  # MMQ above 4096 rows (Q4_K: the small-batch kernel)
     assert not sp(Q4, 448, 4096, 7936)                # 31 super-blocks, 224 tiles
     # short K within one round: only Q6_K grids of at most 64 tiles
     assert not sp(Q4, 64, 4096, 4096) and sp(Q6, 64, 4096, 4096) and sp(P6, 128, 4096, 4096)
@@ -126,9 +136,13 @@ def test_validation_before_device_work():
     assert L.qmm_matmul(1, p, p, 1, 4, 256, p, p, 10, None) == qmm.QMM_ERR_WORKSPACE
     assert L.qmm_matmul_q8(2, p, p, p, mis, 1, 4, 256, p, None) == qmm.QMM_ERR_ALIGN
     assert L.qmm_matmul_q8_kind(0, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_ARG
-    assert L.qmm_matmul_q8_kind(7, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_ARG
-    # the 32 x 64 per-wave kernel exists for Q4_K only
+    assert L.qmm_matmul_q8_kind(8, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    # the 32 x 64 per-wave kernel and the small-batch kernel exist for Q4_K only; the
+    # small-batch kernel takes at most 16 tokens
     assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_WAVE32X64, 2, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_TYPE
+    assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_SKINNY, 2, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_TYPE
+    assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_SKINNY, 1, p, p, p, p, 17, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_SKINNY, 1, p, p, p, p, 16, 4, 256, p, None) == qmm.QMM_ERR_DEVICE
     # the MMQ tile kinds pass validation; without a GPU the device check answers
     assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_64X64_SPLITK, 1, p, p, p, p, 1, 4, 256, p, None) == \
         qmm.QMM_ERR_DEVICE

@@ -120,11 +120,19 @@ def test_mmvq_rows_equal_single_token_calls(qtype, od, idim):
         torch.cuda.synchronize()
         assert np.array_equal(o.cpu().numpy().view(np.uint32), ref[:nt].view(np.uint32)), f"MMVQ nt={nt}"
         kind = qmm.qmm_dispatch_kind(qtype, nt, od, idim)
-        assert kind == (qmm.QMM_KIND_MMVQ if nt <= 8 or od <= 4096 else qmm.QMM_KIND_MMQ)
         if kind == qmm.QMM_KIND_MMVQ:
             o = qmm.qmm_matmul_q8(qtype, W, *args)
             torch.cuda.synchronize()
             assert np.array_equal(o.cpu().numpy().view(np.uint32), ref[:nt].view(np.uint32)), f"nt={nt}"
+        elif kind == qmm.QMM_KIND_SKINNY:
+            # the small-batch kernel is batch invariant too: against its own single-token calls
+            o = qmm.qmm_matmul_q8(qtype, W, *args)
+            ones = [qmm.qmm_matmul_q8_kind(kind, qtype, W, q[t:t + 1].contiguous(), d[t:t + 1].contiguous(),
+                                           s[t:t + 1].contiguous(), od) for t in range(nt)]
+            torch.cuda.synchronize()
+            assert torch.equal(o.view(torch.int32), torch.cat(ones).view(torch.int32)), f"small-batch nt={nt}"
+        else:
+            assert kind == qmm.QMM_KIND_MMQ and nt > 8 and od > 4096
 
 
 EDGE = [

@@ -164,13 +164,16 @@ def test_mmq_every_tile_shape(qtype, nt, od, idim):
 
 
 def test_dispatch_boundary():
-    """nt = 8 runs MMVQ; on a matrix of at most 4096 rows nt = 9..16 run MMVQ on
-    token slices of 8 and nt = 17 runs MMQ; every call matches the oracle, and the
-    sliced call gives the same bits as its slices called alone."""
+    """On a small matrix: nt = 8 runs MMVQ; nt = 9..16 run the small-batch kernel
+    (Q4_K) or MMVQ on token slices of 8 (Q6_K); nt = 17 runs MMQ.  Every call
+    matches the oracle; the Q6_K sliced call gives the same bits as its slices
+    called alone, and a Q4_K small-batch call the same bits as the small-batch
+    kernel on its tokens alone."""
     assert qmm.qmm_dispatch_kind(Q4, 8, 64, 512) == qmm.QMM_KIND_MMVQ
-    assert qmm.qmm_dispatch_kind(Q4, 9, 64, 512) == qmm.QMM_KIND_MMVQ
-    assert qmm.qmm_dispatch_kind(Q4, 16, 64, 512) == qmm.QMM_KIND_MMVQ
+    assert qmm.qmm_dispatch_kind(Q4, 9, 64, 512) == qmm.QMM_KIND_SKINNY
+    assert qmm.qmm_dispatch_kind(Q4, 16, 64, 512) == qmm.QMM_KIND_SKINNY
     assert qmm.qmm_dispatch_kind(Q4, 17, 64, 512) == qmm.QMM_KIND_MMQ
+    assert qmm.qmm_dispatch_kind(Q6, 9, 64, 512) == qmm.QMM_KIND_MMVQ
     od, idim = 96, 1024
     for qtype in (Q4, Q6):
         W = synth.weights(qtype, od, idim, seed=5)
@@ -183,8 +186,13 @@ def test_dispatch_boundary():
             assert_close(o.cpu().numpy(), ref[:nt], mag[:nt], qtype, idim, f"nt={nt}")
         q, d, s = qmm.qmm_quantize_act(_up(x[:13]))
         whole = qmm.qmm_matmul_q8(qtype, Wt, q, d, s, od)
-        a = qmm.qmm_matmul_q8(qtype, Wt, q[:8].contiguous(), d[:8].contiguous(), s[:8].contiguous(), od)
-        b = qmm.qmm_matmul_q8(qtype, Wt, q[8:].contiguous(), d[8:].contiguous(), s[8:].contiguous(), od)
+        if qtype == Q4:
+            k7 = qmm.QMM_KIND_SKINNY
+            a = qmm.qmm_matmul_q8_kind(k7, qtype, Wt, q[:8].contiguous(), d[:8].contiguous(), s[:8].contiguous(), od)
+            b = qmm.qmm_matmul_q8_kind(k7, qtype, Wt, q[8:].contiguous(), d[8:].contiguous(), s[8:].contiguous(), od)
+        else:
+            a = qmm.qmm_matmul_q8(qtype, Wt, q[:8].contiguous(), d[:8].contiguous(), s[:8].contiguous(), od)
+            b = qmm.qmm_matmul_q8(qtype, Wt, q[8:].contiguous(), d[8:].contiguous(), s[8:].contiguous(), od)
         torch.cuda.synchronize()
         assert torch.equal(whole.view(torch.int32), torch.cat([a, b]).view(torch.int32))
 

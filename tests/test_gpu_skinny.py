@@ -1,0 +1,90 @@
+"""GPU parity of the small-batch Q4_K kernel (QMM_KIND_SKINNY: 16 x 16 x 32 int8
+MFMA tiles, 1..16 tokens) against the CPU oracle through the C ABI.
+
+Outputs within the f32 tolerance of tests/_parity.py, elementwise: every output on
+shapes with ragged row tiles (od not a multiple of 16 or 32), odd super-block
+counts (1, 3, 9, 18: the waves splitting K then get unequal shares or none) and
+every token count 1..16 (padding lanes of the 16-token tile); sampled outputs at
+the decode layer shapes; and the refusals (more than 16 tokens, other weight types).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests._parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+qmm = pytest.importorskip("quantized_matmul_amd")
+Q4, Q6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K
+DEV = "cuda:0"
+K7 = qmm.QMM_KIND_SKINNY
+
+
+def _up(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+CASES = [(nt, od, idim) for nt in (1, 2, 3, 4, 5, 7, 8, 9, 12, 13, 16)
+         for od, idim in ((1, 256), (7, 768), (33, 4608), (100, 2304), (257, 1024))]
+
+
+@pytest.mark.parametrize("nt,od,idim", CASES)
+def test_skinny_parity(nt, od, idim):
+    _say(f"skinny nt={nt} od={od} id={idim}")
+    W = synth.weights(Q4, od, idim, seed=5000 + nt)
+    x = synth.activations(nt, idim, seed=6000 + od, outlier_frac=0.01)
+    rq, rd, rs = oracle.quantize(x)
+    ref, mag = oracle.matmul_q8(Q4, W, rq, rd, rs, od)
+    out = qmm.qmm_matmul_q8_kind(K7, Q4, _up(W), _up(rq), _up(rd), _up(rs), od)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, mag, Q4, idim, f"skinny nt={nt} od={od} id={idim}")
+
+
+def _sample(n, k, rng):
+    idx = rng.choice(n, size=min(n, k), replace=False)
+    return np.unique(np.concatenate([idx, [0, n - 1]]))
+
+
+@pytest.mark.parametrize("od,idim,nt", [(12288, 4096, 8), (12288, 4096, 1), (4096, 4096, 16), (4096, 12288, 4),
+                                        (1024, 4096, 3)])
+def test_skinny_full_size_sampled(od, idim, nt):
+    _say(f"skinny full size {od}x{idim} nt={nt}")
+    W = synth.weights(Q4, od, idim, seed=7000 + nt)
+    x = synth.activations(nt, idim, seed=7100 + od, outlier_frac=0.01)
+    rq, rd, rs = oracle.quantize(x)
+    out = qmm.qmm_matmul_q8_kind(K7, Q4, _up(W), _up(rq), _up(rd), _up(rs), od).cpu().numpy()
+    rng = np.random.default_rng(nt)
+    ts, rs_ = _sample(nt, 16, rng), _sample(od, 160, rng)
+    tt, rr = np.meshgrid(ts, rs_, indexing="ij")
+    tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
+    ref, mag = oracle.matmul_q8_points(Q4, W, rq, rd, rs, od, tt, rr)
+    assert_close(out[tt, rr], ref, mag, Q4, idim, f"skinny {od}x{idim} nt={nt}")
+
+
+def test_skinny_deterministic():
+    """The waves splitting K add their partial sums in a fixed order."""
+    W = _up(synth.weights(Q4, 4096, 4096, seed=1))
+    q, d, s = qmm.qmm_quantize_act(_up(synth.activations(8, 4096, seed=2)))
+    o1 = qmm.qmm_matmul_q8_kind(K7, Q4, W, q, d, s, 4096)
+    o2 = qmm.qmm_matmul_q8_kind(K7, Q4, W, q, d, s, 4096)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+
+
+def test_skinny_refusals():
+    W = _up(synth.weights(Q4, 16, 256, seed=3))
+    q, d, s = qmm.qmm_quantize_act(_up(synth.activations(17, 256, seed=4)))
+    with pytest.raises(qmm.QmmError):
+        qmm.qmm_matmul_q8_kind(K7, Q4, W, q, d, s, 16)
+    W6 = _up(synth.weights(Q6, 16, 256, seed=5))
+    with pytest.raises(qmm.QmmError):
+        qmm.qmm_matmul_q8_kind(K7, Q6, W6, q[:4], d[:32], s[:32], 16)
