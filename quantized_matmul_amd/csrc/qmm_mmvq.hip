@@ -36,8 +36,31 @@ struct pow2_ceil {
 
 constexpr int kMaxWaves = 8;   // waves per workgroup
 
+// The value of lane (lane ^ m).  Inside a 16-lane row the exchange is a DPP move
+// on the VALU (quad permutes for m = 1, 2; the row shifts by 4 selected by lane
+// bit 2 for m = 4; the row rotation by 8 for m = 8); across rows it goes through
+// the LDS crossbar (ds_bpermute), whose round trip is the long part of a reduction.
+__device__ __forceinline__ float lane_xor(float v, int m, int lane)
+{
+    const int x = __float_as_int(v);
+    if (m == 1)
+        return __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+    if (m == 2)
+        return __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+    if (m == 4) {
+        const int up = __builtin_amdgcn_update_dpp(x, x, 0x104, 0xF, 0xF, false);   // row_shl:4: lane + 4
+        const int dn = __builtin_amdgcn_update_dpp(x, x, 0x114, 0xF, 0xF, false);   // row_shr:4: lane - 4
+        return __int_as_float((lane & 4) ? dn : up);
+    }
+    if (m == 8)
+        return __int_as_float(__builtin_amdgcn_update_dpp(x, x, 0x128, 0xF, 0xF, false));  // row_ror:8
+    return __shfl_xor(v, m, 64);
+}
+
 // Reduce V values per lane across the wave.  Afterwards lane l (l < V) holds the
-// wave total of value index l.  V must be a power of two <= 64.
+// wave total of value index l.  V must be a power of two <= 64.  Every step adds
+// the same pair of partial sums whatever the exchange path, so the result does not
+// depend on it.
 template <int V>
 __device__ __forceinline__ float wave_reduce_spread(float (&a)[V], int lane)
 {
@@ -49,13 +72,13 @@ __device__ __forceinline__ float wave_reduce_spread(float (&a)[V], int lane)
         for (int i = 0; i < cnt / 2; ++i) {
             const float keep = upper ? a[2 * i + 1] : a[2 * i];
             const float send = upper ? a[2 * i] : a[2 * i + 1];
-            a[i] = keep + __shfl_xor(send, m, 64);
+            a[i] = keep + lane_xor(send, m, lane);
         }
         cnt >>= 1;
     }
 #pragma unroll
     for (int m = V; m < 64; m <<= 1)
-        a[0] += __shfl_xor(a[0], m, 64);
+        a[0] += lane_xor(a[0], m, lane);
     return a[0];
 }
 
@@ -111,27 +134,41 @@ __device__ __forceinline__ uint32_t q4k_scale_bytes(uint32_t h1, uint32_t h2, ui
 // 32 bytes of high bits after the header (bit j of byte l: element l of sub-block
 // j), then the 128 code bytes; the lane's 16 high-bit bytes (positions 16 half ..)
 // supply bits 2p and 2p + 1.
-// Tokens T0 .. T0 + TN - 1 of one window: the activation loads, then the products
-// with each of the R rows' blocks (hdr, qs, qh already loaded), added into acc.
-template <int TN, int T0, int NTP, int R, bool DUMP, bool Q5>
-__device__ __forceinline__ void k4_tokens(
-    const int8_t* __restrict__ q, const float* __restrict__ dx, const float* __restrict__ sx, int id, int nblk,
-    uint32_t ox, uint32_t od2, bool bv, int half, int p, uint32_t selx, uint32_t selz, bool plt2,
-    const uint4 (&hdr)[R], const uint4 (&qs)[R], const uint4 (&qh)[Q5 ? R : 1], float (&acc)[R * NTP],
-    int32_t* __restrict__ S, int row0, int od, int nsb, int b)
-{
+// The activation loads of tokens T0 .. T0 + TN - 1 of one window: this lane's two
+// 16-byte code pieces and its two blocks' d and s.
+template <int TN>
+struct K4Act {
     int4 xa[TN], xb[TN];
     float2 dd[TN], ss[TN];
+};
+
+template <int TN, int T0>
+__device__ __forceinline__ void k4_act_load(K4Act<TN>& A, const int8_t* __restrict__ q, const float* __restrict__ dx,
+                                            const float* __restrict__ sx, int id, int nblk, uint32_t ox, uint32_t od2)
+{
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
         const int8_t* qt = q + (size_t)(T0 + t) * id;
-        xa[t] = *reinterpret_cast<const int4*>(qt + ox);
-        xb[t] = *reinterpret_cast<const int4*>(qt + ox + 32);
-        dd[t] = *reinterpret_cast<const float2*>(dx + (size_t)(T0 + t) * nblk + od2);
-        ss[t] = *reinterpret_cast<const float2*>(sx + (size_t)(T0 + t) * nblk + od2);
+        A.xa[t] = *reinterpret_cast<const int4*>(qt + ox);
+        A.xb[t] = *reinterpret_cast<const int4*>(qt + ox + 32);
+        A.dd[t] = *reinterpret_cast<const float2*>(dx + (size_t)(T0 + t) * nblk + od2);
+        A.ss[t] = *reinterpret_cast<const float2*>(sx + (size_t)(T0 + t) * nblk + od2);
     }
-    // keep every load above this point: the wave waits once for all of them
-    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Tokens T0 .. T0 + TN - 1 of one window (activations in A): the products with
+// each of the R rows' blocks (hdr, qs, qh), added into acc, row by row in the
+// order the rows' loads were issued.
+template <int TN, int T0, int NTP, int R, bool DUMP, bool Q5>
+__device__ __forceinline__ void k4_tokens(
+    const K4Act<TN>& A, bool bv, int half, int p, uint32_t selx, uint32_t selz, bool plt2,
+    const uint4 (&hdr)[R], const uint4 (&qs)[R], const uint4 (&qh)[Q5 ? R : 1], float (&acc)[R * NTP],
+    int32_t* __restrict__ S, int row0, int od, int nsb, int b)
+{
+    const int4 (&xa)[TN] = A.xa;
+    const int4 (&xb)[TN] = A.xb;
+    const float2 (&dd)[TN] = A.dd;
+    const float2 (&ss)[TN] = A.ss;
     // a lane past the row end adds nothing; the min term of a sub-block is
     // added by its half-0 lane only
     float da[TN], db[TN], sa[TN], sb[TN];
@@ -236,6 +273,13 @@ __device__ __forceinline__ void mmvq_k4_body(
         const uint32_t bc = (uint32_t)(bv ? b : nsb - 1);
         // ---- loads: uniform row / token bases plus a 32-bit lane offset
         const uint32_t oh = bc * BB, oq = oh + (Q5 ? 48 : 16) + 32 * p + 16 * half, o5 = oh + 16 + 16 * half;
+        const uint32_t ox = 256 * bc + 64 * p + 16 * half, od2 = 8 * bc + 2 * p;
+        // all tokens at once: the activations (cache hits) first, then the rows'
+        // blocks in row order, so the compute of row r waits only for rows <= r
+        K4Act<TB> A;
+        if constexpr (TB == NT)
+            k4_act_load<TB, 0>(A, q, dx, sx, id, nblk, ox, od2);
+        __builtin_amdgcn_sched_barrier(0);
         uint4 hdr[R], qs[R], qh[Q5 ? R : 1];
 #pragma unroll
         for (int r = 0; r < R; ++r) {
@@ -244,13 +288,20 @@ __device__ __forceinline__ void mmvq_k4_body(
             qs[r] = *reinterpret_cast<const uint4*>(rp + oq);
             if constexpr (Q5)
                 qh[r] = *reinterpret_cast<const uint4*>(rp + o5);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        const uint32_t ox = 256 * bc + 64 * p + 16 * half, od2 = 8 * bc + 2 * p;
-        k4_tokens<TB, 0, NTP, R, DUMP, Q5>(q, dx, sx, id, nblk, ox, od2, bv, half, p, selx, selz, plt2, hdr, qs,
-                                            qh, acc, S, row0, od, nsb, b);
         if constexpr (TB < NT)
-            k4_tokens<NT - TB, TB, NTP, R, DUMP, Q5>(q, dx, sx, id, nblk, ox, od2, bv, half, p, selx, selz, plt2,
-                                                     hdr, qs, qh, acc, S, row0, od, nsb, b);
+            k4_act_load<TB, 0>(A, q, dx, sx, id, nblk, ox, od2);
+        // keep every load above this point
+        __builtin_amdgcn_sched_barrier(0);
+        k4_tokens<TB, 0, NTP, R, DUMP, Q5>(A, bv, half, p, selx, selz, plt2, hdr, qs, qh, acc, S, row0, od, nsb, b);
+        if constexpr (TB < NT) {
+            K4Act<NT - TB> B;
+            k4_act_load<NT - TB, TB>(B, q, dx, sx, id, nblk, ox, od2);
+            __builtin_amdgcn_sched_barrier(0);
+            k4_tokens<NT - TB, TB, NTP, R, DUMP, Q5>(B, bv, half, p, selx, selz, plt2, hdr, qs, qh, acc, S, row0, od,
+                                                     nsb, b);
+        }
     }
     if constexpr (!DUMP) {
         const float v = wave_reduce_spread<V>(acc, lane);

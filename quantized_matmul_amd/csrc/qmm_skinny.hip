@@ -18,15 +18,19 @@
 //    sub-blocks 2c (low nibbles) and 2c+1 (high nibbles) at the same byte
 //    positions: lane group p reads bytes 8p .. 8p+7 of each chunk, which feed two
 //    MFMAs.
-//  * Per output and sub-block the VALU does three operations: the exact
-//    subtraction below, the product with the token's dx and the fma with d*sc_j.
-//    The int8 accumulator starts at the bit pattern of 1.5 * 2^23, so the result
-//    read as f32 is 12582912 + S exactly (|S| <= 60960).
+//  * Per output and sub-block the VALU does two operations: the exact subtraction
+//    below and one fma with the scale product (d*sc_j)[row] * dx_j[token].  The int8
+//    accumulator starts at the bit pattern of 1.5 * 2^23, so the result read as f32
+//    is 12582912 + S exactly (|S| <= 60960).  The scale products of four sub-blocks
+//    come from one four-block v_mfma_f32_16x16x1_f32 (block b: the outer product of
+//    lanes 16b .. 16b+15's dx and d*sc_j), already in the result layout; a lane
+//    loads dx and s of its own token for two sub-blocks and decodes d*sc_j and
+//    dmin*m_j of its own row for the same two.
 //  * The min term sum_j (-dmin*m_j)[row] * s_j[token] is a product over the 8
 //    sub-blocks: two v_mfma_f32_16x16x4_f32 per super-block add it into the same
 //    accumulators (same result layout).
-//  * Every global load is a 16-byte piece of a contiguous run -- a row's 144-byte
-//    block, a token's 256 codes, 4 of a token's scales -- so a load instruction
+//  * Every weight and code load is a 16-byte piece of a contiguous run -- a row's
+//    144-byte block, a token's 256 codes -- so a load instruction
 //    touches few cache lines; the pieces go through a wave-private LDS area into
 //    the MFMA operand layout (no barrier: one wave's LDS operations complete in
 //    order).  The next super-block's loads are issued before the current one is
