@@ -370,24 +370,42 @@ __global__ __launch_bounds__(64 * kMaxWaves) void mmvq_q5k_kernel(
 // Tokens T0 .. T0 + TN - 1 of one Q6_K window: the activation loads and sums, then
 // the products with each of the R rows' chunks (ql, qh, scales and d loaded),
 // added into acc.
-template <int TN, int T0, int NTP, int R, bool DUMP>
-__device__ __forceinline__ void q6k_tokens(
-    const int8_t* __restrict__ q, const float* __restrict__ dx, int id, int nblk, uint32_t ox, uint32_t od2, bool bv,
-    uint32_t hs, int g1, int g2, const uint4 (&ql)[R], const uint4 (&qh)[R], const int (&sc1)[R],
-    const int (&sc2)[R], const uint32_t (&dbits)[R], float (&acc)[R * NTP], int32_t* __restrict__ S, int row0, int od,
-    int nsb, int b)
-{
+// The activation loads of tokens T0 .. T0 + TN - 1 of one window for the Q6_K
+// body: the lane's two 16-byte code pieces and the d of their two 32-blocks.
+template <int TN>
+struct Q6Act {
     int4 xa[TN], xb[TN];
     float da[TN], db[TN];
+};
+
+template <int TN, int T0>
+__device__ __forceinline__ void q6k_act_load(Q6Act<TN>& A, const int8_t* __restrict__ q, const float* __restrict__ dx,
+                                             int id, int nblk, uint32_t ox, uint32_t od2)
+{
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
         const int8_t* qt = q + (size_t)(T0 + t) * id;
-        xa[t] = *reinterpret_cast<const int4*>(qt + ox);
-        xb[t] = *reinterpret_cast<const int4*>(qt + ox + 64);
-        da[t] = dx[(size_t)(T0 + t) * nblk + od2];
-        db[t] = dx[(size_t)(T0 + t) * nblk + od2 + 2];
+        A.xa[t] = *reinterpret_cast<const int4*>(qt + ox);
+        A.xb[t] = *reinterpret_cast<const int4*>(qt + ox + 64);
+        A.da[t] = dx[(size_t)(T0 + t) * nblk + od2];
+        A.db[t] = dx[(size_t)(T0 + t) * nblk + od2 + 2];
     }
-    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int TN, int T0, int NTP, int R, bool DUMP>
+__device__ __forceinline__ void q6k_tokens(
+    const Q6Act<TN>& A, bool bv, uint32_t hs, int g1, int g2, const uint4 (&ql)[R], const uint4 (&qh)[R],
+    const int (&sc1)[R], const int (&sc2)[R], const uint32_t (&dbits)[R], float (&acc)[R * NTP],
+    int32_t* __restrict__ S, int row0, int od, int nsb, int b)
+{
+    const int4 (&xa)[TN] = A.xa;
+    const int4 (&xb)[TN] = A.xb;
+    float da[TN], db[TN];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+        da[t] = A.da[t];
+        db[t] = A.db[t];
+    }
     // 32 * sum of the activation codes of each of the lane's two groups
     int ca[TN], cb[TN];
 #pragma unroll
@@ -478,6 +496,13 @@ __device__ __forceinline__ void mmvq_q6k_body(
         const bool bv = b < nsb;
         const uint32_t bc = (uint32_t)(bv ? b : nsb - 1);
         const uint32_t ob = bc * BB;
+        const uint32_t ox = 256 * bc + 128 * h + 32 * jq + 16 * half, od2 = 8 * bc + 4 * h + jq;
+        // all tokens at once: the activations (cache hits) first, then the rows'
+        // blocks in row order, so the compute of row r waits only for rows <= r
+        Q6Act<TB> A;
+        if constexpr (TB == NT)
+            q6k_act_load<TB, 0>(A, q, dx, id, nblk, ox, od2);
+        __builtin_amdgcn_sched_barrier(0);
         uint4 ql[R], qh[R];
         int sc1[R], sc2[R];
         uint32_t dbits[R];
@@ -504,13 +529,20 @@ __device__ __forceinline__ void mmvq_q6k_body(
             sc1[r] = (int)reinterpret_cast<const int8_t*>(rp)[ob + 192 + g1];
             sc2[r] = (int)reinterpret_cast<const int8_t*>(rp)[ob + 192 + g2];
             dbits[r] = *reinterpret_cast<const uint16_t*>(rp + ob + 208);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        const uint32_t ox = 256 * bc + 128 * h + 32 * jq + 16 * half, od2 = 8 * bc + 4 * h + jq;
-        q6k_tokens<TB, 0, NTP, R, DUMP>(q, dx, id, nblk, ox, od2, bv, hs, g1, g2, ql, qh, sc1, sc2, dbits, acc, S,
-                                         row0, od, nsb, b);
         if constexpr (TB < NT)
-            q6k_tokens<NT - TB, TB, NTP, R, DUMP>(q, dx, id, nblk, ox, od2, bv, hs, g1, g2, ql, qh, sc1, sc2, dbits,
-                                                  acc, S, row0, od, nsb, b);
+            q6k_act_load<TB, 0>(A, q, dx, id, nblk, ox, od2);
+        // keep every load above this point
+        __builtin_amdgcn_sched_barrier(0);
+        q6k_tokens<TB, 0, NTP, R, DUMP>(A, bv, hs, g1, g2, ql, qh, sc1, sc2, dbits, acc, S, row0, od, nsb, b);
+        if constexpr (TB < NT) {
+            Q6Act<NT - TB> B;
+            q6k_act_load<NT - TB, TB>(B, q, dx, id, nblk, ox, od2);
+            __builtin_amdgcn_sched_barrier(0);
+            q6k_tokens<NT - TB, TB, NTP, R, DUMP>(B, bv, hs, g1, g2, ql, qh, sc1, sc2, dbits, acc, S, row0, od, nsb,
+                                                  b);
+        }
     }
     if constexpr (!DUMP) {
         const float v = wave_reduce_spread<V>(acc, lane);
