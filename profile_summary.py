@@ -96,12 +96,22 @@ def cmd_trace(a):
              "Durations are rocprofv3 kernel-trace timestamps (end - start) per dispatch.", "",
              "| kernel | grid (threads) | calls | mean us | median us | min us | max us | total ms | share |",
              "|---|---|---|---|---|---|---|---|---|"]
+    if a.kernel_filter:
+        rows = [r for r in rows if a.kernel_filter in r["kernel"]]
+        lines.insert(9, f"Kernels whose name contains `{a.kernel_filter}` only.")
+        lines.insert(10, "")
     for r in rows:
         lines.append(f"| `{r['kernel']}` | {r['grid']} | {r['calls']} | {r['mean_us']:.2f} | {r['median_us']:.2f} "
                      f"| {r['min_us']:.2f} | {r['max_us']:.2f} | {r['total_ms']:.3f} | {100 * r['share']:.1f} % |")
     if a.bench:
         with open(a.bench) as fh:
             line = json.loads([ln for ln in fh if ln.startswith("{")][-1])
+        if isinstance(line.get("detail"), dict):   # the measured-limits workload
+            lines += peaks_lines(line["detail"])
+            with open(a.out, "w") as fh:
+                fh.write("\n".join(lines) + "\n")
+            print("\n".join(lines))
+            return
         lines += ["", "Bench line of the same command run without the profiler (HIP events over back-to-back "
                   "launches, per launch; under kernel tracing the launches no longer run back to back):", "",
                   "| call | kernel | event us |", "|---|---|---|"]
@@ -118,6 +128,41 @@ def cmd_trace(a):
     with open(a.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def peaks_lines(det):
+    """The measured limits of bench.py --workload peaks (run without the profiler)."""
+    out = ["", "Figures of the same command run without the profiler (HIP events; clocks from the shader and "
+           "100 MHz reference counters the probes read):", "",
+           "| streaming read | bytes | us | GB/s | % of 8 TB/s |", "|---|---|---|---|---|"]
+    for r in det["stream_read"]:
+        out.append(f"| {r['loads_per_lane']} x 16 B per lane | {r['bytes_read']} | {r['us']} | {r['GB_s']} "
+                   f"| {100 * r['GB_s'] / 8000:.1f} % |")
+    out += ["", "| MFMA issue rate | waves per SIMD | TOP/s (int8) or TFLOP/s (f32) | clock GHz | clocks per "
+            "instruction |", "|---|---|---|---|---|"]
+    for r in det["mfma"]["int8"]:
+        out.append(f"| v_mfma_i32_32x32x32_i8 | {r['waves_per_simd']} | {r['T_s']} | {r['clock_GHz']} "
+                   f"| {r['clocks_per_instr']} |")
+    for r in det["mfma"]["f32_outer"]:
+        out.append(f"| v_mfma_f32_32x32x1_2b_f32 | {r['waves_per_simd']} | {r['T_s']} | | |")
+    out += ["", "| VALU instruction | clocks per wave instruction, 1 / 2 / 4 waves per SIMD |", "|---|---|"]
+    for r in det["valu_instr"]:
+        out.append(f"| {r['instr']} | {r['clocks_w1']} / {r['clocks_w2']} / {r['clocks_w4']} |")
+    out += ["", f"LDS read: {det['lds_read']['bytes_per_cu_per_clock']} bytes per CU per clock.", "",
+            "| MFMA and VALU together | VALU per MFMA | MFMA alone ms | VALU alone ms | both ms | overlap |",
+            "|---|---|---|---|---|---|"]
+    for r in det["overlap"]:
+        out.append(f"| {r['mode']} | {r['valu_per_mfma']} | {r['mfma_ms']} | {r['valu_ms']} | {r['both_ms']} "
+                   f"| {r['overlap']} |")
+    out += ["", "| per-32 step (MFMAs then their epilogue, 2 waves per SIMD) | clocks per 32x32x32 block "
+            "| share of int8 MFMA peak |", "|---|---|---|"]
+    for r in det["burst"]:
+        out.append(f"| {r['subblocks_per_burst']} sub-blocks x {r['token_blocks']} token blocks per burst "
+                   f"| {r['clocks_per_block']} | {r['int8_frac_of_mfma']} |")
+    pp = det["pingpong"]
+    out += ["", f"Ping-pong of MFMA and epilogue phases between the two waves of a SIMD (s_barrier between "
+            f"phases): {pp['pingpong']} clocks against {pp['serial']} for the same work without barriers."]
+    return out
 
 
 def pmc_rows(db: str, counter: str):
@@ -243,6 +288,7 @@ def main():
     t.add_argument("--cmd", required=True)
     t.add_argument("--title", default="")
     t.add_argument("--bench")
+    t.add_argument("--kernel-filter", default="", help="list only kernels whose name contains this")
     t.add_argument("--out", required=True)
     p = sub.add_parser("pmc")
     p.add_argument("fetch_db")
