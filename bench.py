@@ -2,18 +2,25 @@
 
 Default workload ("q4k_decode_prefill"): one step is the whole hot path --
 activation quantize, nt dispatch, and the selected kernel -- over
-  * Q4_K decode MMVQ: W 4096x4096 and 12288x4096 at nt = 1, 4 and 8 (six calls),
-  * Q4_K prefill MMQ: W 12288x4096 and 4096x12288 at nt = 512, activations
-    N(0,1) with 1 % of elements x20 (two calls).
+  * Q4_K decode: W 1024x4096 at nt = 1, and W 4096x4096 and 12288x4096 at nt = 1, 4
+    and 8 (the vector kernel at nt = 1, the small-batch MFMA kernel at 4 and 8),
+  * the Q6_K output projection W 32000x4096 at nt = 1, as stored (210-byte blocks)
+    and padded to 224 bytes,
+  * Q4_K prefill: W 12288x4096 and 4096x12288 at nt = 512, activations N(0,1) with
+    1 % of elements x20, on per-32 activations (the path) and, on the same weights
+    and inputs, on Q8_K activations (one scale per 256 values; its own numerics).
 Inputs are seeded synthetic data (see synth/), resident in HBM before timing.
 Weight copies rotate so every weight read of the timed region comes from HBM
 (more than 1 GB of copies per shape, above the 256 MB last-level cache).
 
-Reported (one JSON line): value = HBM GB/s of the MMVQ kernel at nt = 1
+Reported (one JSON line): value = HBM GB/s of the vector kernel at nt = 1
 (algorithmic bytes: weights + q8 activations + f32 output, over the kernel's
-average launch time, both nt = 1 shapes together), the int8 TOP/s of the MMQ
-kernel at nt = 512 (2*nt*od*id over its average launch time), each with its
-roofline fraction, and the CPU oracle timed on a bounded sample.
+average launch time, the 4096x4096 and 12288x4096 calls together), its roofline on
+the 12288x4096 call against 8 TB/s and against the streaming read of the same bytes
+measured in the same process (bench_peaks: frac_of_measured); small_batch (nt = 4
+and 8), q6k_head, mmq (int8 TOP/s at nt = 512 against 5.0 POP/s and the measured
+int8 MFMA rate), mmq_q8k, the diffusion-LM step as one HIP graph (dllm_step; skip
+with --no-dllm), and the CPU oracle timed on a bounded sample (cpu_baseline).
 
 Kernel times come from HIP events on the launch stream inside the timed region.
 The K steps are issued call by call: for each call, a chunk of 20 quantize
@@ -62,9 +69,13 @@ Workload "streamk": the Q4_K matrix shapes of the diffusion-LM step (4096x4096 a
 12288x4096 at nt = 256) and of prefill (nt = 512), on the per-tile dispatch and on
 the stream-K kernel (two launches: the kernel and its fixup), same inputs.
 
+Workload "peaks": the measured limits of this GPU (bench_peaks.hip): a plain
+streaming read at the decode weight sizes, int8 and f32 MFMA issue rates, VALU issue
+rates, LDS read rate, MFMA/VALU overlap and the per-32 step on its own.
+
 Options: --gpus N (1 only), --steps K, --warmup W, --workload
-{q4k_decode_prefill, q6k_head, dllm_step, fused_quantize, q8k_prefill, formats, streamk}, --no-cpu-baseline,
---copy-calibration
+{q4k_decode_prefill, q6k_head, dllm_step, fused_quantize, q8k_prefill, formats, streamk, peaks},
+--no-cpu-baseline, --no-dllm, --chunk, --spread-chunks, --copy-calibration
 MIB (before warm-up, run five plain device copies of MIB MiB between two spin-kernel
 markers, for scaling the HBM counters of a profiled run).
 """
