@@ -13,6 +13,8 @@
 //    row group sit in one workgroup and add their partial sums through LDS.  So a
 //    wave issues all of its loads at once -- R rows x two 16-byte weight loads plus
 //    the activation loads of its window -- and there is no serial chain of loads.
+//    One token on a K of two windows with at most 2 rows per group: one wave takes
+//    both windows (all loads first), with no LDS step and no barrier.
 //  * Inside a window, lane L takes super-block slot g = L/8 and 16-byte code chunk
 //    c = L%8 (32 weights).  A weight load instruction covers eight consecutive
 //    super-blocks of a row (1152 contiguous bytes for Q4_K).
@@ -307,6 +309,71 @@ __device__ __forceinline__ void mmvq_k4_body(
         const float v = wave_reduce_spread<V>(acc, lane);
         group_store<NT, R, NTP>(v, lane, wave, grp, wk, wpr, row0, od, out);
     }
+}
+
+// One token over a K of two windows (9..16 super-blocks): one wave takes both windows
+// of its row group, with every load issued first (the activations, then window 0's
+// rows, then window 1's), so the row group needs no second wave, no LDS round trip
+// and no barrier.  The two windows' sums are reduced across the lanes apart and
+// added in window order: the operations and their order are those of the
+// two-wave form, so the outputs are the same bits.
+template <int R>
+__global__ __launch_bounds__(256) void mmvq_q4k_w2_kernel(const uint8_t* __restrict__ W,
+                                                          const int8_t* __restrict__ q,
+                                                          const float* __restrict__ dx,
+                                                          const float* __restrict__ sx, float* __restrict__ out,
+                                                          int od, int id)
+{
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row0 = (blockIdx.x * 4 + wave) * R;
+    if (row0 >= od)
+        return;  // whole wave; the kernel has no barrier
+    const int g = lane >> 3, c = lane & 7;
+    const int p = c >> 1, half = c & 1;
+    const uint32_t k = 2u * (uint32_t)(p & 1);
+    const uint32_t selx = k | ((k + 1) << 8) | ((k + 4) << 16) | ((k + 5) << 24);
+    const uint32_t selz = k | ((k + 1) << 8) | (k << 16) | ((k + 1) << 24);
+    const bool plt2 = p < 2;
+    const int nsb = id >> 8, nblk = id >> 5;
+    const size_t row_bytes = (size_t)nsb * kQ4KBytes;
+    const int b0 = g, b1 = 8 + g;
+    const bool bv0 = b0 < nsb, bv1 = b1 < nsb;
+    const uint32_t c0 = (uint32_t)(bv0 ? b0 : nsb - 1), c1 = (uint32_t)(bv1 ? b1 : nsb - 1);
+    const uint32_t oh0 = c0 * kQ4KBytes, oq0 = oh0 + 16 + 32 * p + 16 * half;
+    const uint32_t oh1 = c1 * kQ4KBytes, oq1 = oh1 + 16 + 32 * p + 16 * half;
+    K4Act<1> A0, A1;
+    k4_act_load<1, 0>(A0, q, dx, sx, id, nblk, 256 * c0 + 64 * p + 16 * half, 8 * c0 + 2 * p);
+    k4_act_load<1, 0>(A1, q, dx, sx, id, nblk, 256 * c1 + 64 * p + 16 * half, 8 * c1 + 2 * p);
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 hdr0[R], qs0[R], hdr1[R], qs1[R], qh[1];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint8_t* rp = W + (size_t)min(row0 + r, od - 1) * row_bytes;
+        hdr0[r] = *reinterpret_cast<const uint4*>(rp + oh0);
+        qs0[r] = *reinterpret_cast<const uint4*>(rp + oq0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint8_t* rp = W + (size_t)min(row0 + r, od - 1) * row_bytes;
+        hdr1[r] = *reinterpret_cast<const uint4*>(rp + oh1);
+        qs1[r] = *reinterpret_cast<const uint4*>(rp + oq1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float acc0[R], acc1[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+        acc0[i] = acc1[i] = 0.f;
+    k4_tokens<1, 0, 1, R, false, false>(A0, bv0, half, p, selx, selz, plt2, hdr0, qs0, qh, acc0, nullptr, row0, od,
+                                        nsb, b0);
+    k4_tokens<1, 0, 1, R, false, false>(A1, bv1, half, p, selx, selz, plt2, hdr1, qs1, qh, acc1, nullptr, row0, od,
+                                        nsb, b1);
+    const float v0 = wave_reduce_spread<R>(acc0, lane);
+    const float v1 = wave_reduce_spread<R>(acc1, lane);
+    if (lane < R && row0 + lane < od)
+        out[row0 + lane] = v0 + v1;
 }
 
 template <int NT, int R, bool DUMP>
@@ -714,6 +781,17 @@ static hipError_t launch_one(int type, const uint8_t* W, const int8_t* q, const 
     const int groups = (od + R - 1) / R;
     const int grid = (groups + gpw - 1) / gpw;
     const dim3 block(64 * wpr * gpw);
+    // one token, two K windows, at most 2 rows per group (matrices under 8192 rows):
+    // the single-wave form (4096 x 4096: 4.40 -> 4.05 us in one process); from 4
+    // rows on, the two-wave form's doubled wave count is worth more (12288 x 4096:
+    // 6.93 against 7.23 us)
+    if constexpr (!DUMP && NT == 1 && R <= 2) {
+        if (type == 1 && nwin == 2) {
+            hipLaunchKernelGGL((mmvq_q4k_w2_kernel<R>), dim3((groups + 3) / 4), dim3(256), 0, st, W, q, d, s, out, od,
+                               id);
+            return hipGetLastError();
+        }
+    }
     if constexpr (!DUMP && R == 4) {
         const bool many = (int64_t)grid * wpr * gpw >= 4096;
         if constexpr (k4_batch(NT, false) < NT) {

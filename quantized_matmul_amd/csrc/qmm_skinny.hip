@@ -199,7 +199,7 @@ __device__ __forceinline__ uint32_t sk_vgpr(uint32_t bits)
 // ...; all over the same RT*16 rows.  N > 0: every wave has exactly N super-blocks
 // (ks * N == nsb); N = 0: any share.  NTB >= nt tokens are
 // staged (the 16-token tile's other lanes repeat token NTB-1 or nt-1; their results
-// are not stored).  Dynamic LDS: ks stage areas, then (ks-1) partial tiles.
+// are not stored).  Dynamic LDS: ks stage areas, then ks partial tiles.
 constexpr int kSkMaxWaves = 8;
 
 template <int RT, int NTB, int N>
@@ -294,22 +294,24 @@ __global__ __launch_bounds__(64 * kSkMaxWaves) void mmq_skinny_q4k_kernel(const 
         }
     }
     if (ks > 1) {
-        if (w > 0) {
+        // every wave's partial tile to LDS; then wave w adds value v = w, w + ks, ...
+        // (value v: tile v / 4, token slot 4p + v % 4) over the waves in the order
+        // 0, 1, .., ks-1 and stores it
 #pragma unroll
-            for (int r = 0; r < RT; ++r)
+        for (int r = 0; r < RT; ++r)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    red[(((w - 1) * RT + r) * 4 + i) * 64 + lane] = acc[r][i];
-        }
+            for (int i = 0; i < 4; ++i)
+                red[((w * RT + r) * 4 + i) * 64 + lane] = acc[r][i];
         __syncthreads();
-        if (w > 0)
-            return;
-        for (int k = 0; k < ks - 1; ++k)
-#pragma unroll
-            for (int r = 0; r < RT; ++r)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[r][i] += red[((k * RT + r) * 4 + i) * 64 + lane];
+        for (int v = w; v < RT * 4; v += ks) {
+            float sum = red[v * 64 + lane];
+            for (int k = 1; k < ks; ++k)
+                sum += red[(k * RT * 4 + v) * 64 + lane];
+            const int row = row0 + 16 * (v >> 2) + (lane & 15), t = 4 * p + (v & 3);
+            if (row < od && t < nt)
+                out[(size_t)t * od + row] = sum;
+        }
+        return;
     }
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
@@ -330,7 +332,7 @@ hipError_t launch_rk(const uint8_t* W, const int8_t* q, const float* d, const fl
                      float* out, int ks, hipStream_t st)
 {
     const int grid = (od + 16 * RT - 1) / (16 * RT);
-    const size_t lds = (size_t)ks * sizeof(SkStage<RT, NTB>) + (size_t)(ks - 1) * RT * 4 * 64 * sizeof(float);
+    const size_t lds = (size_t)ks * (sizeof(SkStage<RT, NTB>) + (size_t)RT * 4 * 64 * sizeof(float));
     hipLaunchKernelGGL((mmq_skinny_q4k_kernel<RT, NTB, N>), dim3(grid), dim3(64 * ks), lds, st, W, q, d, s, out, nt,
                        od, id);
     return hipGetLastError();
