@@ -164,14 +164,18 @@ int skinny_cfg_override()
 // small-batch MFMA kernel (measured on 1024..12288-row Q4_K: 4096 x 4096 nt = 4:
 // 5.1 us against MMVQ's 5.6, nt = 8: 5.5 against 7.8; 12288 x 4096 nt = 4: 9.0
 // against 10.3, nt = 8: 10.7 against 16.6; 9..16 tokens: 6-15 us against 21-58 for
-// MMQ); MMVQ up to the switch otherwise (and on 1..3 tokens, where it wins); other
-// types also on 9..16 tokens of a matrix of at most 4096 rows, as launches on token
-// slices of 8 (such a matrix gives MMQ at most 64 tiles of 64 rows, a quarter of
-// the 256 CUs; 4096 x 4096: MMQ 22 us, two MMVQ launches 13.7-14.7 us); MMQ beyond.
-int dispatch_kind(int type, int nt, int od)
+// MMQ), and on 3 tokens of a matrix of at least 2048 rows and at least 8192 rows or
+// columns (12288 x 4096: 8.9 against 9.6 us; 4096 x 12288: 9.6 against 13.5; at
+// 4096 x 4096 the two are equal and MMVQ keeps it); MMVQ up to the switch otherwise
+// (1..2 tokens, where it wins); other types also on 9..16 tokens of a matrix of at most
+// 4096 rows, as launches on token slices of 8 (such a matrix gives MMQ at most 64
+// tiles of 64 rows, a quarter of the 256 CUs; 4096 x 4096: MMQ 22 us, two MMVQ
+// launches 13.7-14.7 us); MMQ beyond.
+int dispatch_kind(int type, int nt, int od, int id)
 {
     const int sw = nt_switch_value();
-    if (sw == 8 && type == QMM_TYPE_Q4_K && nt <= 16 && (nt >= 9 || (nt >= 4 && od >= 2048)))
+    if (sw == 8 && type == QMM_TYPE_Q4_K && nt <= 16 &&
+        (nt >= 9 || (nt >= 4 && od >= 2048) || (nt == 3 && od >= 2048 && (od >= 8192 || id >= 8192))))
         return QMM_KIND_SKINNY;
     if (nt <= sw || (sw == 8 && nt <= 16 && od <= 4096))
         return QMM_KIND_MMVQ;
@@ -195,7 +199,7 @@ int dispatch_kind(int type, int nt, int od)
 bool streamk_preferred(int type, int nt, int od, int id)
 {
     const bool q6 = type == QMM_TYPE_Q6_K || type == QMM_TYPE_Q6_K_P224;
-    if ((type != QMM_TYPE_Q4_K && !q6) || dispatch_kind(type, nt, od) != QMM_KIND_MMQ)
+    if ((type != QMM_TYPE_Q4_K && !q6) || dispatch_kind(type, nt, od, id) != QMM_KIND_MMQ)
         return false;
     const long tiles = (long)((nt + 63) / 64) * ((od + 127) / 128);
     if (tiles % 256 == 0)
@@ -581,7 +585,7 @@ int qmm_dispatch_kind(int type, int nt, int od, int id)
     rc = check_shape(nt, od, id);
     if (rc)
         return rc;
-    return dispatch_kind(type, nt, od);
+    return dispatch_kind(type, nt, od, id);
 }
 
 int qmm_mmq_tile(int nt, int od, int id)
@@ -601,7 +605,7 @@ int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, cons
     rc = check_device();
     if (rc)
         return rc;
-    const int kind = dispatch_kind(type, nt, od);
+    const int kind = dispatch_kind(type, nt, od, id);
     return matmul_q8_checked(kind, type, W, q, d, s, nt, od, id, out, nullptr, stream);
 }
 
@@ -656,7 +660,7 @@ int qmm_matmul(int type, const void* W, const float* x, int nt, int od, int id, 
     if (streamk_preferred(type, nt, od, id) && ws_bytes >= act + qmm::mmq_streamk_ws_bytes())
         return launched(qmm::launch_mmq_streamk(type, static_cast<const uint8_t*>(W), q, d, s, nt, od, id, out,
                                                 reinterpret_cast<float*>(base + act), st));
-    const int kind = dispatch_kind(type, nt, od);
+    const int kind = dispatch_kind(type, nt, od, id);
     return matmul_q8_checked(kind, type, W, q, d, s, nt, od, id, out, nullptr, stream);
 }
 

@@ -62,12 +62,18 @@ def test_act_bytes():
 def test_dispatch_kind_host():
     assert qmm.qmm_nt_switch() == 8
     Q4, Q6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K
-    # Q4_K: the small-batch kernel on 4..16 tokens from 2048 rows, on 9..16 below;
-    # MMVQ on 1..3 tokens and on 4..8 tokens of fewer than 2048 rows
+    # Q4_K: the small-batch kernel on 4..16 tokens from 2048 rows, on 3 tokens from
+    # 8192 rows or 8192 columns, on 9..16 below; MMVQ on 1..2 tokens, on 3 tokens of
+    # smaller matrices and on 4..8 tokens of fewer than 2048 rows
     for nt in range(1, 17):
         for od in (2048, 4096, 12288):
-            want = qmm.QMM_KIND_SKINNY if nt >= 4 else qmm.QMM_KIND_MMVQ
+            big = od >= 8192
+            want = qmm.QMM_KIND_SKINNY if nt >= 4 or (nt == 3 and big) else qmm.QMM_KIND_MMVQ
             assert qmm.qmm_dispatch_kind(Q4, nt, od, 4096) == want
+            want = qmm.QMM_KIND_SKINNY if nt >= 3 else qmm.QMM_KIND_MMVQ
+            assert qmm.qmm_dispatch_kind(Q4, nt, od, 12288) == want
+        assert qmm.qmm_dispatch_kind(Q4, 3, 8191, 8191 // 256 * 256) == qmm.QMM_KIND_MMVQ
+        assert qmm.qmm_dispatch_kind(Q4, 3, 8192, 4096) == qmm.QMM_KIND_SKINNY
         want = qmm.QMM_KIND_SKINNY if nt >= 9 else qmm.QMM_KIND_MMVQ
         assert qmm.qmm_dispatch_kind(Q4, nt, 2047, 4096) == want
         assert qmm.qmm_dispatch_kind(Q4, nt, 64, 12288) == want
