@@ -1,4 +1,4 @@
-"""Shared helpers for the GPU parity tests (comparison rule and device upload)."""
+"""Shared helpers for the GPU parity tests (comparison rule, the oracle's own activations)."""
 from __future__ import annotations
 
 import numpy as np
@@ -28,3 +28,16 @@ def assert_close(got, ref, mag, qtype: int, idim: int, what: str = ""):
                              f"got {got.flat[k]!r} ref {ref.flat[k]!r} err {err.flat[k]:.3e} tol {tol.flat[k]:.3e}")
     rel = err / np.maximum(np.abs(ref), 1e-300)
     return float(np.max(err / np.maximum(tol, 1e-300))), float(np.max(rel))
+
+
+def oracle_activations(quantize, x, gpu, what: str = ""):
+    """The oracle's own quantization of x (quantize: the oracle's per-32 or Q8_K
+    quantizer), checked bit-equal to the GPU's activation tensors `gpu`.  The
+    reference computations take the oracle's arrays, so no oracle input comes from
+    the GPU path."""
+    ref = quantize(x)
+    for name, g, r in zip(("q", "d", "s"), gpu, ref):
+        g = g.cpu().numpy() if hasattr(g, "cpu") else np.asarray(g)
+        same = g.dtype == r.dtype and g.shape == r.shape and np.array_equal(g.view(np.uint8), r.view(np.uint8))
+        assert same, f"{what}: activation {name} differs from the oracle's"
+    return ref

@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import synth
-from tests._parity import assert_close
+from tests._parity import assert_close, oracle_activations
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +49,7 @@ def test_b32_parity(qtype, nt, od, idim):
     x = synth.activations(nt, idim, seed=3100 + nt, outlier_frac=0.01)
     Wt = _up(W)
     q, d, s = qmm.qmm_quantize_act(_up(x))
-    qn, dn, sn = q.cpu().numpy(), d.cpu().numpy(), s.cpu().numpy()
+    qn, dn, sn = oracle_activations(oracle.quantize, x, (q, d, s), "quantize")
     ref, mag = oracle.matmul_q8(qtype, W, qn, dn, sn, od)
     ref_S = oracle.subblock_dots(qtype, W, qn, od)
     kinds = ([qmm.QMM_KIND_MMVQ] if nt <= 8 else []) + [qmm.QMM_KIND_MMQ]
@@ -81,5 +81,6 @@ def test_b32_full_size(qtype, nt):
     rs = np.unique(np.concatenate([rng.choice(od, 160, replace=False), [0, od - 1]]))
     tt, rr = np.meshgrid(ts, rs, indexing="ij")
     tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
-    ref, mag = oracle.matmul_q8_points(qtype, W, q.cpu().numpy(), d.cpu().numpy(), s.cpu().numpy(), od, tt, rr)
+    qn, dn, sn = oracle_activations(oracle.quantize, x, (q, d, s), "quantize")
+    ref, mag = oracle.matmul_q8_points(qtype, W, qn, dn, sn, od, tt, rr)
     assert_close(out[tt, rr], ref, mag, qtype, idim, f"full size nt={nt}")

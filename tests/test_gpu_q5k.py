@@ -19,7 +19,7 @@ import torch
 
 import oracle
 import synth
-from tests._parity import assert_close
+from tests._parity import assert_close, oracle_activations
 
 pytestmark = pytest.mark.gpu
 
@@ -43,7 +43,7 @@ def test_q5k_parity(nt, od, idim):
     x = synth.activations(nt, idim, seed=5100 + nt, outlier_frac=0.01)
     Wt = _up(W)
     q, d, s = qmm.qmm_quantize_act(_up(x))
-    qn, dn, sn = q.cpu().numpy(), d.cpu().numpy(), s.cpu().numpy()
+    qn, dn, sn = oracle_activations(oracle.quantize, x, (q, d, s), "quantize")
     ref, mag = oracle.matmul_q8(Q5, W, qn, dn, sn, od)
     ref_S = oracle.subblock_dots(Q5, W, qn, od)
     kinds = ([qmm.QMM_KIND_MMVQ] if nt <= 8 else []) + [qmm.QMM_KIND_MMQ]
@@ -80,5 +80,6 @@ def test_q5k_full_size(nt):
     rs = np.unique(np.concatenate([rng.choice(od, 160, replace=False), [0, od - 1]]))
     tt, rr = np.meshgrid(ts, rs, indexing="ij")
     tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
-    ref, mag = oracle.matmul_q8_points(Q5, W, q.cpu().numpy(), d.cpu().numpy(), s.cpu().numpy(), od, tt, rr)
+    qn, dn, sn = oracle_activations(oracle.quantize, x, (q, d, s), "quantize")
+    ref, mag = oracle.matmul_q8_points(Q5, W, qn, dn, sn, od, tt, rr)
     assert_close(out[tt, rr], ref, mag, Q5, idim, f"full size nt={nt}")

@@ -21,7 +21,7 @@ import torch
 
 import oracle
 import synth
-from tests._parity import assert_close
+from tests._parity import assert_close, oracle_activations
 
 pytestmark = pytest.mark.gpu
 
@@ -69,8 +69,8 @@ def test_padded_equals_unpadded(nt, od, idim):
     kinds = [qmm.QMM_KIND_MMQ, qmm.QMM_KIND_MMQ_128X64, qmm.QMM_KIND_MMQ_64X64, qmm.QMM_KIND_MMQ_64X64_SPLITK]
     if nt <= 8:
         kinds = [qmm.QMM_KIND_MMVQ] + kinds
-    ref, mag = oracle.matmul_q8(oracle.TYPE_Q6_K_P224, _np_pad(W), q.cpu().numpy(), d.cpu().numpy(),
-                                s.cpu().numpy(), od)
+    qn, dn, sn = oracle_activations(oracle.quantize, x, (q, d, s), "quantize")
+    ref, mag = oracle.matmul_q8(oracle.TYPE_Q6_K_P224, _np_pad(W), qn, dn, sn, od)
     for kind in kinds:
         a = qmm.qmm_matmul_q8_kind(kind, Q6, Wt, q, d, s, od)
         b = qmm.qmm_matmul_q8_kind(kind, P6, Wp, q, d, s, od)
@@ -81,7 +81,7 @@ def test_padded_equals_unpadded(nt, od, idim):
     for kind in ([qmm.QMM_KIND_MMVQ] if nt <= 8 else []) + [qmm.QMM_KIND_MMQ]:
         S = qmm.qmm_group_dots(kind, P6, Wp, q, od)
         torch.cuda.synchronize()
-        ref_S = oracle.subblock_dots(oracle.TYPE_Q6_K_P224, _np_pad(W), q.cpu().numpy(), od)
+        ref_S = oracle.subblock_dots(oracle.TYPE_Q6_K_P224, _np_pad(W), qn, od)
         assert np.array_equal(S.cpu().numpy(), ref_S), f"kind {kind}: group dots"
 
 
@@ -103,6 +103,6 @@ def test_padded_full_size(od, idim, nt):
     ts = np.arange(nt, dtype=np.int32) if nt <= 8 else np.array([0, 7, 100, nt - 1], np.int32)
     tt, rr = np.meshgrid(ts, rs, indexing="ij")
     tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
-    ref, mag = oracle.matmul_q8_points(oracle.TYPE_Q6_K_P224, _np_pad(W), q.cpu().numpy(), d.cpu().numpy(),
-                                       s.cpu().numpy(), od, tt, rr)
+    qn, dn, sn = oracle_activations(oracle.quantize, x, (q, d, s), "quantize")
+    ref, mag = oracle.matmul_q8_points(oracle.TYPE_Q6_K_P224, _np_pad(W), qn, dn, sn, od, tt, rr)
     assert_close(b.cpu().numpy()[tt, rr], ref, mag, P6, idim, "padded full size")

@@ -25,7 +25,7 @@ import torch
 
 import oracle
 import synth
-from tests._parity import assert_close
+from tests._parity import assert_close, oracle_activations
 
 pytestmark = pytest.mark.gpu
 
@@ -117,7 +117,10 @@ def test_q8k_superblock_sums_bit_exact(qtype, nt, od, idim):
     q, d, bs = _quant(x)
     S = qmm.qmm_q8k_superblock_sums(qtype, Wd, q, d, bs, od)
     torch.cuda.synchronize()
-    ref = oracle.q8k_superblock_sums(ot, W, q.cpu().numpy(), bs.cpu().numpy(), od)
+    # the oracle's reference runs on the oracle's own quantization of x, which the
+    # GPU's must equal bit for bit
+    oq, od_, obs = oracle_activations(oracle.quantize_q8k, x, (q, d, bs), "quantize_q8k")
+    ref = oracle.q8k_superblock_sums(ot, W, oq, obs, od)
     _same(S.cpu().numpy(), ref, "integer stage")
 
 
@@ -129,7 +132,8 @@ def test_matmul_q8k_against_oracle(qtype, nt, od, idim):
     q, d, bs = _quant(x)
     out = qmm.qmm_matmul_q8k(qtype, Wd, q, d, bs, od)
     torch.cuda.synchronize()
-    ref, mag = oracle.matmul_q8k(ot, W, q.cpu().numpy(), d.cpu().numpy(), bs.cpu().numpy(), od)
+    oq, od_, obs = oracle_activations(oracle.quantize_q8k, x, (q, d, bs), "quantize_q8k")
+    ref, mag = oracle.matmul_q8k(ot, W, oq, od_, obs, od)
     worst, rel = assert_close(out.cpu().numpy(), ref, mag, ot, idim, f"{nt}x{od}x{idim}")
     _say(f"  worst err/tol {worst:.3f}, max rel {rel:.2e}")
 
@@ -155,7 +159,7 @@ def test_matmul_q8k_full_size_sampled(qtype, od, idim, nt):
     rs = np.unique(np.concatenate([rng.choice(od, size=min(od, 160), replace=False), [0, od - 1]]))
     tt, rr = np.meshgrid(ts, rs, indexing="ij")
     tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
-    ref, mag = oracle.matmul_q8k_points(ot, W, qn, dn, bn, od, tt, rr)
+    ref, mag = oracle.matmul_q8k_points(ot, W, ref_q[0], ref_q[1], ref_q[2], od, tt, rr)
     worst, rel = assert_close(out[tt, rr], ref, mag, ot, idim, f"full size {od}x{idim} nt={nt}")
     _say(f"  worst err/tol {worst:.3f}, max rel {rel:.2e}")
 
@@ -180,7 +184,8 @@ def test_matmul_q8k_every_tile(qtype, kind, nt, od, idim):
     same = qmm.qmm_matmul_q8k_kind(qmm.qmm_q8k_tile(nt, od, idim), qtype, Wd, q, d, bs, od)
     torch.cuda.synchronize()
     assert torch.equal(auto.view(torch.int32), same.view(torch.int32))
-    ref, mag = oracle.matmul_q8k(ot, W, q.cpu().numpy(), d.cpu().numpy(), bs.cpu().numpy(), od)
+    oq, od_, obs = oracle_activations(oracle.quantize_q8k, x, (q, d, bs), "quantize_q8k")
+    ref, mag = oracle.matmul_q8k(ot, W, oq, od_, obs, od)
     worst, rel = assert_close(out.cpu().numpy(), ref, mag, ot, idim, f"kind {kind} {nt}x{od}x{idim}")
     _say(f"  worst err/tol {worst:.3f}, max rel {rel:.2e}")
 
@@ -192,14 +197,16 @@ def test_matmul_q8k_split_full_size_sampled():
         assert qmm.qmm_q8k_tile(nt, od, idim) == qmm.QMM_KIND_MMQ_64X64_SPLITK
         _say(f"matmul_q8k split full size type={qtype} od={od} id={idim} nt={nt}")
         Wd, W, ot = _weights(qtype, od, idim, seed=2200 + od)
-        q, d, bs = _quant(synth.activations(nt, idim, seed=2300 + nt, outlier_frac=0.01))
+        x = synth.activations(nt, idim, seed=2300 + nt, outlier_frac=0.01)
+        q, d, bs = _quant(x)
         out = qmm.qmm_matmul_q8k(qtype, Wd, q, d, bs, od).cpu().numpy()
         rng = np.random.default_rng(od + nt + 7)
         ts = np.unique(np.concatenate([rng.choice(nt, size=24, replace=False), [0, nt - 1]]))
         rs = np.unique(np.concatenate([rng.choice(od, size=160, replace=False), [0, od - 1]]))
         tt, rr = np.meshgrid(ts, rs, indexing="ij")
         tt, rr = tt.reshape(-1).astype(np.int32), rr.reshape(-1).astype(np.int32)
-        ref, mag = oracle.matmul_q8k_points(ot, W, q.cpu().numpy(), d.cpu().numpy(), bs.cpu().numpy(), od, tt, rr)
+        oq, od_, obs = oracle_activations(oracle.quantize_q8k, x, (q, d, bs), "quantize_q8k")
+        ref, mag = oracle.matmul_q8k_points(ot, W, oq, od_, obs, od, tt, rr)
         assert_close(out[tt, rr], ref, mag, ot, idim, f"split full size {od}x{idim} nt={nt}")
 
 

@@ -22,7 +22,7 @@ import torch
 
 import oracle
 import synth
-from tests._parity import assert_close
+from tests._parity import assert_close, oracle_activations
 
 pytestmark = pytest.mark.gpu
 
@@ -71,7 +71,7 @@ def test_streamk(qtype, nt, od, idim):
     an = a.cpu().numpy()
     assert np.array_equal(an.view(np.uint32), b.cpu().numpy().view(np.uint32)), "not deterministic"
     assert np.all(np.isfinite(an))
-    qn, dn, sn = q.cpu().numpy(), d.cpu().numpy(), s.cpu().numpy()
+    qn, dn, sn = oracle_activations(oracle.quantize, x, (q, d, s), "quantize")
     if nt * od <= 300 * 1000:
         ref, mag = oracle.matmul_q8(qtype, W, qn, dn, sn, od)
         assert_close(an, ref, mag, qtype, idim, "stream-K vs oracle")
@@ -120,7 +120,7 @@ def test_qmm_matmul_takes_streamk_where_preferred(qtype, nt, od, idim):
     bits = lambda t: t.view(torch.int32)
     assert torch.equal(bits(full), bits(sk if pref else pt))
     assert torch.equal(bits(small), bits(pt))
-    qn, dn, sn = q.cpu().numpy(), d.cpu().numpy(), s.cpu().numpy()
+    qn, dn, sn = oracle_activations(oracle.quantize, x, (q, d, s), "quantize")
     if nt * od <= 300 * 1000:
         ref, mag = oracle.matmul_q8(qtype, W, qn, dn, sn, od)
         assert_close(full.cpu().numpy(), ref, mag, qtype, idim, "qmm_matmul vs oracle")
