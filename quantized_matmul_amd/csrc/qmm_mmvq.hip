@@ -847,10 +847,11 @@ static hipError_t launch_one(int type, const uint8_t* W, const int8_t* q, const 
     return hipGetLastError();
 }
 
-// Rows per row group R.  One token: the largest of 4, 2, 1 that leaves at least
-// 2048 row groups (eight per CU on 256 CUs).  Several tokens: every lane's
-// activation loads (NT tokens) are shared by R rows, so 4 rows from od = 4096 up
-// (measured on 4096- and 12288-row Q4_K at nt = 4 and 8: 7-9 % faster than 2).
+// Rows per row group R.  K of up to two windows (id <= 4096): one token, the
+// largest of 4, 2, 1 that leaves at least 2048 row groups (eight per CU on 256
+// CUs); several tokens: every lane's activation loads (NT tokens) are shared by R
+// rows, so 4 rows from od = 4096 up (measured on 4096- and 12288-row Q4_K at nt = 4
+// and 8: 7-9 % faster than 2).  Longer K: by the wave count (below).
 // QMM_MMVQ_ROWS (1, 2, 4, or 8 for nt <= 2) overrides it, read once, for tuning
 // sweeps.
 static int rows_override()
@@ -875,10 +876,23 @@ static hipError_t launch_nt(int type, const uint8_t* W, const int8_t* q, const f
         return launch_one<NT, 1, true>(type, W, q, d, s, od, id, out, S, st);
     int R = rows_override();
     if (R == 0) {
-        if constexpr (NT >= 2)
+        const int nwin = (id / 256 + 7) / 8;
+        const bool q6_one = NT == 1 && (type == 2 || type == 3);
+        if (nwin >= 3 && !q6_one) {
+            // a K of three or more windows multiplies the waves of a row group, so
+            // fewer row groups keep the chip busy and each wave's activation loads
+            // serve more rows: 4 rows while there are at least 2048 waves (1024 for
+            // several tokens), else 2 (Q4_K 4096 x 12288 nt = 1: 7.98 -> 7.15 us;
+            // 2048 x 12288: 6.48 -> 5.47; 1024 x 12288 nt = 8: 13.5 -> 7.4; Q4_0, Q5_K
+            // alike).  Q6_K at one token keeps the rule below (more rows per wave
+            // were 4-6 % slower on 1024 and 2048 rows: its rows take more registers)
+            const long need = NT >= 2 ? 1024 : 2048;
+            R = (long)((od + 3) / 4) * nwin >= need ? 4 : (long)((od + 1) / 2) * nwin >= need ? 2 : 1;
+        } else if constexpr (NT >= 2) {
             R = od >= 4096 ? 4 : od >= 2048 ? 2 : 1;
-        else
+        } else {
             R = od >= 4 * 2048 ? 4 : od >= 2 * 2048 ? 2 : 1;
+        }
     }
     if constexpr (NT <= 2) {
         if (R == 8)

@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import synth
-from tests._parity import assert_close
+from tests._parity import assert_close, oracle_activations
 
 pytestmark = pytest.mark.gpu
 
@@ -174,3 +174,22 @@ def test_zero_blocks_and_extreme_scales(qtype, nt):
     assert np.all(d[:, 0::5] == 0.0) and np.all(q.reshape(nt, -1, 32)[:, 0::5] == 0)
     assert np.any((d[:, 1::5] > 0) & (d[:, 1::5] < np.finfo(np.float32).tiny))
     _check_out(qtype, W, od, idim, *ref_q8, out, f"type {qtype} nt {nt}", full=True)
+
+LONG_K = [(qt, od, idim) for qt in (1, 2, 4, 6) for od, idim in ((1024, 12288), (2048, 12288), (300, 14336))]
+
+
+@pytest.mark.parametrize("qtype,od,idim", LONG_K, ids=[f"t{q}-{a}x{b}" for q, a, b in LONG_K])
+def test_mmvq_long_k_against_oracle(qtype, od, idim):
+    """MMVQ on a K of six or seven windows and few rows, where the row-group size
+    follows the wave count (2 or 4 rows per wave), at 1..8 tokens: every output
+    against the oracle, which quantizes the activations itself."""
+    _say(f"MMVQ long K type={qtype} od={od} id={idim}")
+    W = synth.weights(qtype, od, idim, seed=51 + qtype)
+    Wt = _up(W)
+    for nt in (1, 2, 3, 5, 8):
+        x = synth.activations(nt, idim, seed=52 + nt, outlier_frac=0.01)
+        q, d, s = qmm.qmm_quantize_act(_up(x))
+        out = qmm.qmm_matmul_q8_kind(qmm.QMM_KIND_MMVQ, qtype, Wt, q, d, s, od)
+        torch.cuda.synchronize()
+        rq, rd, rs = oracle_activations(oracle.quantize, x, (q, d, s), f"nt={nt}")
+        _check_out(qtype, W, od, idim, rq, rd, rs, out.cpu().numpy(), f"type {qtype} {od}x{idim} nt={nt}", full=True)
