@@ -159,15 +159,15 @@ int skinny_cfg_override()
     return val;
 }
 
-// The kernel a call runs.  With the default switch (8): Q4_K on 4..16 tokens of a
-// matrix of at least 2048 rows, and on 9..16 tokens of any matrix, runs the
-// small-batch MFMA kernel (measured on 1024..12288-row Q4_K: 4096 x 4096 nt = 4:
-// 5.1 us against MMVQ's 5.6, nt = 8: 5.5 against 7.8; 12288 x 4096 nt = 4: 9.0
-// against 10.3, nt = 8: 10.7 against 16.6; 9..16 tokens: 6-15 us against 21-58 for
-// MMQ), and on 3 tokens of a matrix of at least 2048 rows and at least 8192 rows or
-// columns (12288 x 4096: 8.9 against 9.6 us; 4096 x 12288: 9.6 against 13.5; at
-// 4096 x 4096 the two are equal and MMVQ keeps it); MMVQ up to the switch otherwise
-// (1..2 tokens, where it wins); other types also on 9..16 tokens of a matrix of at most
+// The kernel a call runs.  With the default switch (8): Q4_K runs the small-batch
+// MFMA kernel on 9..16 tokens of any matrix, on 5..8 tokens of a matrix of at least
+// 2048 rows, on 4 tokens of at least 3072 rows, and on 3 tokens of at least 3072
+// rows with at least 8192 rows or columns (measured, us, small-batch against MMVQ:
+// 4096 x 4096 nt = 4: 5.1 / 5.6, nt = 8: 5.5 / 7.8; 12288 x 4096 nt = 3: 8.9 / 9.6,
+// nt = 4: 9.0 / 10.3, nt = 8: 10.7 / 16.6; 3072 x 12288 nt = 3: 9.0 / 9.7, nt = 4:
+// 9.4 / 10.4; 2048 x 12288 nt = 4: 9.0 / 7.7, nt = 6: 9.9 / 11.9; 2048 x 4096
+// nt = 4: 4.5 / 4.1, nt = 8: 5.0 / 5.5; 4096 x 4096 nt = 3: equal; 9..16 tokens:
+// 6-15 us against 21-58 for MMQ); MMVQ up to the switch otherwise; other types also on 9..16 tokens of a matrix of at most
 // 4096 rows, as launches on token slices of 8 (such a matrix gives MMQ at most 64
 // tiles of 64 rows, a quarter of the 256 CUs; 4096 x 4096: MMQ 22 us, two MMVQ
 // launches 13.7-14.7 us); MMQ beyond.
@@ -175,7 +175,8 @@ int dispatch_kind(int type, int nt, int od, int id)
 {
     const int sw = nt_switch_value();
     if (sw == 8 && type == QMM_TYPE_Q4_K && nt <= 16 &&
-        (nt >= 9 || (nt >= 4 && od >= 2048) || (nt == 3 && od >= 2048 && (od >= 8192 || id >= 8192))))
+        (nt >= 9 || (nt >= 5 && od >= 2048) || (nt == 4 && od >= 3072) ||
+         (nt == 3 && od >= 3072 && (od >= 8192 || id >= 8192))))
         return QMM_KIND_SKINNY;
     if (nt <= sw || (sw == 8 && nt <= 16 && od <= 4096))
         return QMM_KIND_MMVQ;

@@ -62,18 +62,20 @@ def test_act_bytes():
 def test_dispatch_kind_host():
     assert qmm.qmm_nt_switch() == 8
     Q4, Q6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K
-    # Q4_K: the small-batch kernel on 4..16 tokens from 2048 rows, on 3 tokens from
-    # 8192 rows or 8192 columns, on 9..16 below; MMVQ on 1..2 tokens, on 3 tokens of
-    # smaller matrices and on 4..8 tokens of fewer than 2048 rows
+    # Q4_K: the small-batch kernel on 9..16 tokens of any matrix, on 5..8 tokens from
+    # 2048 rows, on 4 tokens from 3072 rows, on 3 tokens from 3072 rows with 8192 rows
+    # or columns; MMVQ otherwise
     for nt in range(1, 17):
-        for od in (2048, 4096, 12288):
-            big = od >= 8192
-            want = qmm.QMM_KIND_SKINNY if nt >= 4 or (nt == 3 and big) else qmm.QMM_KIND_MMVQ
-            assert qmm.qmm_dispatch_kind(Q4, nt, od, 4096) == want
-            want = qmm.QMM_KIND_SKINNY if nt >= 3 else qmm.QMM_KIND_MMVQ
-            assert qmm.qmm_dispatch_kind(Q4, nt, od, 12288) == want
+        for od in (2048, 3072, 4096, 12288):
+            for idim in (4096, 12288):
+                big = od >= 8192 or idim >= 8192
+                sk = (nt >= 9 or (nt >= 5 and od >= 2048) or (nt == 4 and od >= 3072) or
+                      (nt == 3 and od >= 3072 and big))
+                want = qmm.QMM_KIND_SKINNY if sk else qmm.QMM_KIND_MMVQ
+                assert qmm.qmm_dispatch_kind(Q4, nt, od, idim) == want, (nt, od, idim)
         assert qmm.qmm_dispatch_kind(Q4, 3, 8191, 8191 // 256 * 256) == qmm.QMM_KIND_MMVQ
         assert qmm.qmm_dispatch_kind(Q4, 3, 8192, 4096) == qmm.QMM_KIND_SKINNY
+        assert qmm.qmm_dispatch_kind(Q4, 4, 3071, 4096) == qmm.QMM_KIND_MMVQ
         want = qmm.QMM_KIND_SKINNY if nt >= 9 else qmm.QMM_KIND_MMVQ
         assert qmm.qmm_dispatch_kind(Q4, nt, 2047, 4096) == want
         assert qmm.qmm_dispatch_kind(Q4, nt, 64, 12288) == want
