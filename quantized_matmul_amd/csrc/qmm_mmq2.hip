@@ -32,10 +32,7 @@
 //  * The min term sum_j (-dmin*m_j)[row] * s_j[token] goes straight into the
 //    accumulators once per super-block on three bf16 MFMAs over exact three-part
 //    splits of both factors (the six part products above 2^-24 of the product).
-//  * One kernel body walks a contiguous range of (tile, super-block) units: the
-//    per-tile launch gives each workgroup one tile; the stream-K launch cuts all
-//    units into equal ranges (tile counts that do not fill the chip) and leaves
-//    partial tiles to the fixup kernel, which adds them in a fixed order.
+//  * One workgroup per tile, tiles of one row block numbered onto one XCD.
 #include "qmm_mmq_common.h"
 
 namespace qmm {
@@ -238,15 +235,13 @@ __device__ __forceinline__ void k4_superblock(const K4Stage& st, const v4i (&a16
     }
 }
 
-// The kernel body over units [u0, u1) of (tile, super-block), tile-major; a tile the
-// range covers whole is stored, a partial one goes to workspace slot `slot0` (the
-// range's first tile) or slot0 + 1 (its last), 8 blocks of 32 x 32 per slot in the
-// fixup's order (block 2w + n: rows 32w.., tokens 32n..).
+// The kernel body for one whole tile: rows row0 .. row0 + 127 and tokens tok0 ..
+// tok0 + 63 over all super-blocks.
 template <bool DUMP>
-__device__ __forceinline__ void k4_range(const uint8_t* __restrict__ W, const int8_t* __restrict__ q,
-                                         const float* __restrict__ dx, const float* __restrict__ sx,
-                                         float* __restrict__ out, int nt, int od, int id, long u0, long u1,
-                                         float* __restrict__ ws, int slot0, int32_t* __restrict__ S)
+__device__ __forceinline__ void k4_tile(const uint8_t* __restrict__ W, const int8_t* __restrict__ q,
+                                        const float* __restrict__ dx, const float* __restrict__ sx,
+                                        float* __restrict__ out, int nt, int od, int id, int tile,
+                                        int32_t* __restrict__ S)
 {
     __shared__ K4Stage stg[2];
     const int ntb = (nt + kK4BN - 1) / kK4BN;
@@ -254,83 +249,66 @@ __device__ __forceinline__ void k4_range(const uint8_t* __restrict__ W, const in
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int li = lane & 31, lh = lane >> 5;
     const uint32_t row_bytes = (uint32_t)nsb * kQ4KBytes;
-    const int first_tile = (int)(u0 / nsb);
     const float Mv = vgpr_f32(kMagicBits);
     const uint32_t mask = vgpr_u32(0x0F0F0F0Fu);
     v16i magic;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
         magic[i] = (int)__float_as_uint(Mv);
+    const int row0 = (tile / ntb) * kK4BM, tok0 = (tile % ntb) * kK4BN;
 
-    for (long u = u0; u < u1;) {
-        const int tile = (int)(u / nsb);
-        const int k0 = (int)(u - (long)tile * nsb);
-        const int k1 = (int)min((long)nsb, k0 + (u1 - u));
-        const int row0 = (tile / ntb) * kK4BM, tok0 = (tile % ntb) * kK4BN;
-
-        // per-thread offsets (rows past od / tokens past nt read the last valid one)
-        K4Offs o;
+    // per-thread offsets (rows past od / tokens past nt read the last valid one)
+    K4Offs o;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int e = tid + 256 * k;
-            o.x[k] = (uint32_t)(min(tok0 + (e >> 4), nt - 1) - tok0) * (uint32_t)id + 16u * (uint32_t)(e & 15);
-        }
-        const int tds = (tid & 127) >> 1;
-        o.ds = ((uint32_t)(min(tok0 + tds, nt - 1) - tok0) * (uint32_t)nblk + 4u * (uint32_t)(tid & 1)) * 4u;
-        o.h = (uint32_t)(min(row0 + (tid >> 1), od - 1) - row0) * row_bytes;
-        K4Rsrc rs;
-        rs.w = buffer_rsrc(W + (size_t)row0 * row_bytes, (size_t)(od - row0) * row_bytes);
-        rs.x = buffer_rsrc(q + (size_t)tok0 * id, (size_t)(nt - tok0) * id);
-        // waves 0-1 stage d, waves 2-3 stage s: a wave-uniform choice, made scalar so
-        // the buffer resource stays in scalar registers
-        const uintptr_t pds = reinterpret_cast<uintptr_t>(tid < 128 ? dx : sx);
-        const uintptr_t pdsu = ((uintptr_t)__builtin_amdgcn_readfirstlane((uint32_t)(pds >> 32)) << 32) |
-                               (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)pds);
-        rs.ds = buffer_rsrc(reinterpret_cast<const float*>(pdsu) + (size_t)tok0 * nblk, (size_t)(nt - tok0) * nblk * 4);
-        const uint32_t oa = (uint32_t)(min(row0 + 32 * w + li, od - 1) - row0) * row_bytes + 16u + 16u * (uint32_t)lh;
+    for (int k = 0; k < 4; ++k) {
+        const int e = tid + 256 * k;
+        o.x[k] = (uint32_t)(min(tok0 + (e >> 4), nt - 1) - tok0) * (uint32_t)id + 16u * (uint32_t)(e & 15);
+    }
+    const int tds = (tid & 127) >> 1;
+    o.ds = ((uint32_t)(min(tok0 + tds, nt - 1) - tok0) * (uint32_t)nblk + 4u * (uint32_t)(tid & 1)) * 4u;
+    o.h = (uint32_t)(min(row0 + (tid >> 1), od - 1) - row0) * row_bytes;
+    K4Rsrc rs;
+    rs.w = buffer_rsrc(W + (size_t)row0 * row_bytes, (size_t)(od - row0) * row_bytes);
+    rs.x = buffer_rsrc(q + (size_t)tok0 * id, (size_t)(nt - tok0) * id);
+    // waves 0-1 stage d, waves 2-3 stage s: a wave-uniform choice, made scalar so
+    // the buffer resource stays in scalar registers
+    const uintptr_t pds = reinterpret_cast<uintptr_t>(tid < 128 ? dx : sx);
+    const uintptr_t pdsu = ((uintptr_t)__builtin_amdgcn_readfirstlane((uint32_t)(pds >> 32)) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)pds);
+    rs.ds = buffer_rsrc(reinterpret_cast<const float*>(pdsu) + (size_t)tok0 * nblk, (size_t)(nt - tok0) * nblk * 4);
+    const uint32_t oa = (uint32_t)(min(row0 + 32 * w + li, od - 1) - row0) * row_bytes + 16u + 16u * (uint32_t)lh;
 
-        K4Pref pf;
-        v4i aA[4], aB[4];
-        v16f acc0 = {}, acc1 = {};
-        k4_prefetch(pf, o, rs, k0, nblk);
-        k4_load_a(aA, rs.w, oa, k0);
-        k4_stage(stg[0], pf, tid);
-        k4_prefetch(pf, o, rs, min(k0 + 1, k1 - 1), nblk);
-        k4_load_a(aB, rs.w, oa, min(k0 + 1, k1 - 1));
+    K4Pref pf;
+    v4i aA[4], aB[4];
+    v16f acc0 = {}, acc1 = {};
+    k4_prefetch(pf, o, rs, 0, nblk);
+    k4_load_a(aA, rs.w, oa, 0);
+    k4_stage(stg[0], pf, tid);
+    k4_prefetch(pf, o, rs, min(1, nsb - 1), nblk);
+    k4_load_a(aB, rs.w, oa, min(1, nsb - 1));
+    __syncthreads();
+    // two super-blocks per trip so the A registers alternate without copies; the
+    // prefetch indices are clamped to the last super-block (no load under a branch)
+    for (int sb = 0; sb < nsb; sb += 2) {
+        k4_superblock<DUMP>(stg[sb & 1], aA, magic, Mv, mask, w, li, lh, acc0, acc1, S, nt, od, nsb, sb, row0, tok0);
+        __builtin_amdgcn_sched_barrier(0);
+        k4_stage(stg[(sb + 1) & 1], pf, tid);
+        k4_prefetch(pf, o, rs, min(sb + 2, nsb - 1), nblk);
+        k4_load_a(aA, rs.w, oa, min(sb + 2, nsb - 1));
         __syncthreads();
-        // two super-blocks per trip so the A registers alternate without copies
-        for (int sb = k0; sb < k1; sb += 2) {
-            k4_superblock<DUMP>(stg[(sb - k0) & 1], aA, magic, Mv, mask, w, li, lh, acc0, acc1, S, nt, od, nsb, sb,
-                                row0, tok0);
-            __builtin_amdgcn_sched_barrier(0);
-            k4_stage(stg[(sb - k0 + 1) & 1], pf, tid);
-            k4_prefetch(pf, o, rs, min(sb + 2, k1 - 1), nblk);
-            k4_load_a(aA, rs.w, oa, min(sb + 2, k1 - 1));
-            __syncthreads();
-            if (sb + 1 >= k1)
-                break;
-            k4_superblock<DUMP>(stg[(sb - k0 + 1) & 1], aB, magic, Mv, mask, w, li, lh, acc0, acc1, S, nt, od, nsb,
-                                sb + 1, row0, tok0);
-            __builtin_amdgcn_sched_barrier(0);
-            k4_stage(stg[(sb - k0) & 1], pf, tid);
-            k4_prefetch(pf, o, rs, min(sb + 3, k1 - 1), nblk);
-            k4_load_a(aB, rs.w, oa, min(sb + 3, k1 - 1));
-            __syncthreads();
-        }
-        if constexpr (!DUMP) {
-            if (k0 == 0 && k1 == nsb) {
-                store_tile(acc0, out, nt, od, tok0 + li, row0 + 32 * w, lh);
-                store_tile(acc1, out, nt, od, tok0 + 32 + li, row0 + 32 * w, lh);
-            } else {
-                float* slot = ws + ((size_t)(slot0 + (tile == first_tile ? 0 : 1)) * 8 + 2 * w) * 1024;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    slot[i * 64 + lane] = acc0[i];
-                    slot[1024 + i * 64 + lane] = acc1[i];
-                }
-            }
-        }
-        u += k1 - k0;
+        if (sb + 1 >= nsb)
+            break;
+        k4_superblock<DUMP>(stg[(sb + 1) & 1], aB, magic, Mv, mask, w, li, lh, acc0, acc1, S, nt, od, nsb, sb + 1,
+                            row0, tok0);
+        __builtin_amdgcn_sched_barrier(0);
+        k4_stage(stg[sb & 1], pf, tid);
+        k4_prefetch(pf, o, rs, min(sb + 3, nsb - 1), nblk);
+        k4_load_a(aB, rs.w, oa, min(sb + 3, nsb - 1));
+        __syncthreads();
+    }
+    if constexpr (!DUMP) {
+        store_tile(acc0, out, nt, od, tok0 + li, row0 + 32 * w, lh);
+        store_tile(acc1, out, nt, od, tok0 + 32 + li, row0 + 32 * w, lh);
     }
 }
 
@@ -346,29 +324,10 @@ __global__ __launch_bounds__(kK4NTH, 2) void mmq_q4k_v2_kernel(const uint8_t* __
     const int tile = xcd_tile(ntiles);
     if (tile < 0)
         return;  // whole workgroup
-    const long nsb = id >> 8;
-    k4_range<DUMP>(W, q, dx, sx, out, nt, od, id, tile * nsb, (tile + 1) * nsb, nullptr, 0, S);
+    k4_tile<DUMP>(W, q, dx, sx, out, nt, od, id, tile, S);
 }
 
 }  // namespace
-
-// Stream-K: all ntiles * nsb units cut into G equal ranges (workgroups numbered so
-// that those of one XCD take consecutive ranges).  Workspace: 2 partial tiles per
-// workgroup.
-template <int G>
-__global__ __launch_bounds__(kK4NTH, 2) void mmq_q4k_v2_streamk_kernel(const uint8_t* __restrict__ W,
-                                                                       const int8_t* __restrict__ q,
-                                                                       const float* __restrict__ dx,
-                                                                       const float* __restrict__ sx,
-                                                                       float* __restrict__ out, int nt, int od, int id,
-                                                                       float* __restrict__ ws)
-{
-    const int ntiles = ((nt + kK4BN - 1) / kK4BN) * ((od + kK4BM - 1) / kK4BM);
-    const long units = (long)ntiles * (id >> 8);
-    const int g = (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
-    const long u0 = (long)g * units / G, u1 = (long)(g + 1) * units / G;
-    k4_range<false>(W, q, dx, sx, out, nt, od, id, u0, u1, ws, 2 * g, nullptr);
-}
 
 hipError_t launch_mmq_q4k_v2(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od,
                              int id, float* out, int32_t* S, hipStream_t st)
