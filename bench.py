@@ -11,7 +11,9 @@ activation quantize, nt dispatch, and the selected kernel -- over
     and inputs, on Q8_K activations (one scale per 256 values; its own numerics).
 Inputs are seeded synthetic data (see synth/), resident in HBM before timing.
 Weight copies rotate so every weight read of the timed region comes from HBM
-(more than 1 GB of copies per shape, above the 256 MB last-level cache).
+(more than 1 GB of copies per shape, above the 256 MB last-level cache); calls on
+the same matrix start at evenly spaced points of its rotation, so no call reads
+copies another call has just read.
 
 Reported (one JSON line): value = HBM GB/s of the vector kernel at nt = 1
 (algorithmic bytes: weights + q8 activations + f32 output, over the kernel's
@@ -187,6 +189,7 @@ class Call:
         self.ops = 2.0 * nt * od * idim
         self.k_ms = []   # matmul kernel time per launch, one entry per timed chunk
         self.q_ms = []   # quantize kernel time per launch, one entry per timed chunk
+        self.i0 = 0      # first copy of the rotation (calls sharing copies start apart)
         self.i = 0
         # raw C-ABI arguments, built once so the timed loop only makes the calls
         P, I = ctypes.c_void_p, ctypes.c_int
@@ -438,6 +441,16 @@ def build_calls(torch, qmm, workload):
                          label=f"layer{layer} proj{p} {od}x{idim}", x=x, streamk=path_ws(qt, 256, od, idim))
                 c.w_host = host if layer == 0 else None   # the CPU baseline times layer 0's Q4_K projections
                 calls.append(c)
+    # calls that share a matrix's weight copies start at evenly spaced points of the
+    # rotation: one call's chunk of launches then never reads copies another call
+    # has just read (20 copies of a 4096 x 4096 matrix, 188 MB, would still sit in
+    # the 256 MB last-level cache)
+    groups = {}
+    for c in calls:
+        groups.setdefault(id(c.W), []).append(c)
+    for g in groups.values():
+        for k, c in enumerate(g):
+            c.i0 = c.i = k * (len(c.W) // len(g))
     return calls
 
 
@@ -926,7 +939,7 @@ def main():
     torch.cuda.synchronize()
     gate_cycles = int(max(1.5 * host_s, 100e-6) * 1e9 / ns_per_cycle)
     for c in calls:
-        c.i = 0
+        c.i = c.i0
 
     # timed region: K steps, i.e. K launches of every call of the step; launches of
     # one call are issued back to back in chunks bracketed by HIP events on the

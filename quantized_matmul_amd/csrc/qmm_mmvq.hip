@@ -316,18 +316,7 @@ __device__ __forceinline__ void mmvq_k4_body(
 // rows, then window 1's), so the row group needs no second wave, no LDS round trip
 // and no barrier.  The two windows' sums are reduced across the lanes apart and
 // added in window order: the operations and their order are those of the
-// two-wave form, so the outputs are the same bits.  Its weight loads are
-// non-temporal (2048 x 4096: 3.42 -> 3.03 us, 3072 x 3072: 3.91 -> 3.31; equal at
-// 4096 x 4096; on the two-wave form they were slower at 12288 rows).
-// A 16-byte load marked non-temporal: the weights are streamed once, nothing
-// re-reads them within the launch.
-__device__ __forceinline__ uint4 nt_load16(const uint8_t* p)
-{
-    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-    const u4 v = __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
-
+// two-wave form, so the outputs are the same bits.
 template <int R>
 __global__ __launch_bounds__(256) void mmvq_q4k_w2_kernel(const uint8_t* __restrict__ W,
                                                           const int8_t* __restrict__ q,
@@ -361,15 +350,15 @@ __global__ __launch_bounds__(256) void mmvq_q4k_w2_kernel(const uint8_t* __restr
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint8_t* rp = W + (size_t)min(row0 + r, od - 1) * row_bytes;
-        hdr0[r] = nt_load16(rp + oh0);
-        qs0[r] = nt_load16(rp + oq0);
+        hdr0[r] = *reinterpret_cast<const uint4*>(rp + oh0);
+        qs0[r] = *reinterpret_cast<const uint4*>(rp + oq0);
         __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint8_t* rp = W + (size_t)min(row0 + r, od - 1) * row_bytes;
-        hdr1[r] = nt_load16(rp + oh1);
-        qs1[r] = nt_load16(rp + oq1);
+        hdr1[r] = *reinterpret_cast<const uint4*>(rp + oh1);
+        qs1[r] = *reinterpret_cast<const uint4*>(rp + oq1);
         __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_sched_barrier(0);
