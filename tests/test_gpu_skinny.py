@@ -4,8 +4,10 @@ MFMA tiles, 1..16 tokens) against the CPU oracle through the C ABI.
 Outputs within the f32 tolerance of tests/_parity.py, elementwise: every output on
 shapes with ragged row tiles (od not a multiple of 16 or 32), odd super-block
 counts (1, 3, 9, 18: the waves splitting K then get unequal shares or none) and
-every token count 1..16 (padding lanes of the 16-token tile); sampled outputs at
-the decode layer shapes; and the refusals (more than 16 tokens, other weight types).
+every token count 1..16 (padding lanes of the 16-token tile); matrices of more than
+256 row tiles with K split over 1 to 6 waves (straight-line and loop forms, 4, 8
+and 16 token slots, a last row tile of 8 rows); sampled outputs at the decode layer
+shapes; and the refusals (more than 16 tokens, other weight types).
 """
 from __future__ import annotations
 
@@ -35,6 +37,12 @@ def _say(*a):
 
 CASES = [(nt, od, idim) for nt in (1, 2, 3, 4, 5, 7, 8, 9, 12, 13, 16)
          for od, idim in ((1, 256), (7, 768), (33, 4608), (100, 2304), (257, 1024))]
+# larger matrices (with the waves splitting K that the launch rule gives): 5480 x 256
+# (1, the last row tile holds 8 rows), 5480 x 512 (2), 6000 x 1024 (4), 9000 x 768
+# (3), 8200 x 2304 (4, 9 super-blocks: the loop form), 7000 x 12288 (6, 8
+# super-blocks per wave: the loop form)
+CASES += [(1, 5480, 256), (4, 5480, 512), (8, 6000, 1024), (16, 9000, 768), (5, 8200, 2304),
+          (3, 7000, 12288), (12, 5480, 512), (7, 9000, 768)]
 
 
 @pytest.mark.parametrize("nt,od,idim", CASES)
