@@ -48,6 +48,51 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restric
         sink[blockIdx.x] = x;
 }
 
+// Load shapes of a Q4_K matrix (rows of 16 blocks of 144 bytes), every byte read
+// once, no arithmetic.  SHAPE 0, the vector kernel's: a workgroup of two waves (K
+// windows 0 and 1) over 4 rows, lane l taking block 8w + l/8 of the window and per
+// row one load of its 16-byte header and one of its 16-byte code chunk l%8.  SHAPE
+// 1: one wave per 2 rows, each row read as its 144 consecutive 16-byte pieces (lane
+// l: pieces l, 64 + l and 128 + l, the last clamped to piece 143).
+template <int SHAPE>
+__global__ __launch_bounds__(128) void load_shape_kernel(const uint8_t* __restrict__ w, uint32_t* __restrict__ sink)
+{
+    constexpr int kRow = 16 * 144;
+    uint32_t x = 0;
+    if constexpr (SHAPE == 0) {
+        const int lane = threadIdx.x & 63, win = threadIdx.x >> 6;
+        const int blk = 8 * win + (lane >> 3), c = lane & 7;
+        uint4 h[4], q[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const uint8_t* rp = w + ((size_t)blockIdx.x * 4 + r) * kRow + blk * 144;
+            h[r] = *reinterpret_cast<const uint4*>(rp);
+            q[r] = *reinterpret_cast<const uint4*>(rp + 16 + 16 * c);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            x ^= h[r].x ^ h[r].y ^ h[r].z ^ h[r].w ^ q[r].x ^ q[r].y ^ q[r].z ^ q[r].w;
+    } else {
+        const int lane = threadIdx.x & 63;
+        const size_t row0 = ((size_t)blockIdx.x * 2 + (threadIdx.x >> 6)) * 2;
+        uint4 v[2][3];
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const uint8_t* rp = w + (row0 + r) * kRow;
+            v[r][0] = *reinterpret_cast<const uint4*>(rp + 16 * lane);
+            v[r][1] = *reinterpret_cast<const uint4*>(rp + 16 * (64 + lane));
+            v[r][2] = *reinterpret_cast<const uint4*>(rp + 16 * min(128 + lane, 143));
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int k = 0; k < 3; ++k)
+                x ^= v[r][k].x ^ v[r][k].y ^ v[r][k].z ^ v[r][k].w;
+    }
+    if (x == kNever)
+        sink[blockIdx.x] = x;
+}
+
 // Thread 0 of workgroup 0 records the shader-clock and 100 MHz reference-clock
 // ticks its loop took into clk[0], clk[1] (clk may be null): the ratio gives the
 // clock the chip ran at under this load.
@@ -587,6 +632,22 @@ int peaks_stream_read(const void* p, size_t bytes, int u, uint32_t* sink, hipStr
     case 4: hipLaunchKernelGGL(stream_read_kernel<4>, grid, block, 0, stream, q, sink); break;
     default: hipLaunchKernelGGL(stream_read_kernel<8>, grid, block, 0, stream, q, sink); break;
     }
+    return hipGetLastError();
+}
+
+// Load shape `shape` (0 or 1, see load_shape_kernel) over `rows` rows of a Q4_K
+// matrix of 4096 columns at `w` (device, 16-byte aligned; rows a multiple of 4).
+// sink: rows / 4 dwords.  Returns hipErrorInvalidValue on a bad argument.
+int peaks_load_shape(const void* w, int rows, int shape, uint32_t* sink, hipStream_t stream)
+{
+    if (!w || !sink || (reinterpret_cast<uintptr_t>(w) & 15) || rows < 4 || rows % 4 || (shape != 0 && shape != 1))
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(rows / 4)), block(128);
+    const uint8_t* p = static_cast<const uint8_t*>(w);
+    if (shape == 0)
+        hipLaunchKernelGGL(load_shape_kernel<0>, grid, block, 0, stream, p, sink);
+    else
+        hipLaunchKernelGGL(load_shape_kernel<1>, grid, block, 0, stream, p, sink);
     return hipGetLastError();
 }
 

@@ -12,7 +12,10 @@ beside the documented peak; these functions give the measured side:
                 clock the chip ran at;
   valu_rate     issue rate of v_fma_f32 and of the epilogue pair cvt + fma;
   overlap       time of MFMA work and VALU work together against each alone, in
-                one wave (interleaved) and split over the two waves of a SIMD.
+                one wave (interleaved) and split over the two waves of a SIMD;
+  load_shape    loads without arithmetic of a Q4_K 12288 x 4096 matrix in the vector
+                kernel's shape (a 16-byte header and a 16-byte code chunk per lane and
+                row) and as each row's consecutive 16-byte pieces, same rotation.
 
 All times come from HIP events on the launch stream.
 """
@@ -50,6 +53,7 @@ def lib():
         L = ctypes.CDLL(LIB)
         P, I = ctypes.c_void_p, ctypes.c_int
         L.peaks_stream_read.argtypes = [P, ctypes.c_size_t, I, P, P]
+        L.peaks_load_shape.argtypes = [P, I, I, P, P]
         L.peaks_rate.argtypes = [I, I, I, P, P, P]
         L.peaks_overlap.argtypes = [I, I, I, I, I, P, P]
         L.peaks_valu_instr.argtypes = [I, I, I, P, P]
@@ -59,7 +63,7 @@ def lib():
         L.peaks_pingpong.argtypes = [I, I, I, P, P]
         L.peaks_burst.argtypes = [I, I, I, P, P]
         for f in ("peaks_stream_read", "peaks_rate", "peaks_overlap", "peaks_valu_instr", "peaks_lds_read",
-                  "peaks_mfma_mix", "peaks_shadow", "peaks_pingpong", "peaks_burst"):
+                  "peaks_mfma_mix", "peaks_shadow", "peaks_pingpong", "peaks_burst", "peaks_load_shape"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -117,6 +121,30 @@ def stream_read(torch, sizes, copy_bytes=1 << 30, per_chunk=20, chunks=5):
         ms, u, n = best
         res.append({"bytes": size, "bytes_read": n, "us": round(ms * 1e3, 3),
                     "GB_s": round(n / (ms * 1e-3) / 1e9, 1), "loads_per_lane": u})
+    return res
+
+
+def load_shape(torch, rows=12288, copy_bytes=1 << 30, per_chunk=20, chunks=5):
+    """Median per-launch time of both load shapes over a Q4_K rows x 4096 matrix
+    (144-byte blocks, 16 per row), launches rotating over > copy_bytes of copies."""
+    L = lib()
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    n = rows * 16 * 144
+    stride = -(-n // 65536) * 65536
+    copies = max(2, -(-copy_bytes // stride))
+    buf = torch.empty(stride * copies, dtype=torch.uint8, device="cuda:0")
+    sink = torch.empty(rows // 4, dtype=torch.int32, device="cuda:0")
+    base, sp = buf.data_ptr(), ctypes.c_void_p(sink.data_ptr())
+    res = []
+    for shape, name in ((0, "header + code chunk per lane and row"), (1, "consecutive 16-byte pieces per row")):
+        def launch(i, shape=shape):
+            _check(L.peaks_load_shape(ctypes.c_void_p(base + (i % copies) * stride), rows, shape, sp, st),
+                   "load_shape")
+
+        ms = statistics.median(_timed(torch, launch, per_chunk, chunks))
+        res.append({"shape": name, "rows": rows, "bytes": n, "us": round(ms * 1e3, 3),
+                    "GB_s": round(n / (ms * 1e-3) / 1e9, 1)})
+    del buf, sink
     return res
 
 
@@ -347,4 +375,5 @@ def run_all(torch, sizes):
     res["pingpong"] = pingpong(torch, res["mfma"]["int8"][-1]["clock_GHz"] or ghz)
     res["burst"] = burst(torch, res["mfma"]["int8"][-1]["clock_GHz"] or ghz)
     res["overlap"] = overlap(torch)
+    res["load_shape"] = load_shape(torch)
     return res

@@ -162,6 +162,10 @@ def peaks_lines(det):
     pp = det["pingpong"]
     out += ["", f"Ping-pong of MFMA and epilogue phases between the two waves of a SIMD (s_barrier between "
             f"phases): {pp['pingpong']} clocks against {pp['serial']} for the same work without barriers."]
+    if det.get("load_shape"):
+        out += ["", "| loads only, Q4_K 12288 x 4096 (no arithmetic) | bytes | us | GB/s |", "|---|---|---|---|"]
+        for r in det["load_shape"]:
+            out.append(f"| {r['shape']} | {r['bytes']} | {r['us']} | {r['GB_s']} |")
     return out
 
 
