@@ -111,7 +111,8 @@ enum {
                                        int8 MFMA tiles of 16 weight rows x 16 tokens, the
                                        weights streamed once for all tokens ([MMQ, section
                                        12.2]: token count in registers; per-32 rescale as
-                                       MMQ); qmm_matmul's kernel for Q4_K at 4..16 tokens */
+                                       MMQ); qmm_matmul's kernel for Q4_K at 3..16 tokens
+                                       (by shape) */
 };
 
 /* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K, Q4_0), *176
@@ -220,9 +221,9 @@ int qmm_matmul_q8_streamk(int type, const void* W, const int8_t* q, const float*
 int qmm_mmq_tile(int nt, int od, int id);
 
 /* Which kernel qmm_matmul would run for this call.  With the default switch (8):
- * QMM_KIND_SKINNY for Q4_K on 9..16 tokens of any matrix, on 5..8 tokens of a matrix
- * of at least 2048 rows, on 4 tokens of at least 3072 rows, and on 3 tokens of at
- * least 3072 rows with at least 8192 rows or columns; otherwise QMM_KIND_MMVQ for nt <= 8 and for 9..16
+ * QMM_KIND_SKINNY for Q4_K on 9..16 tokens of any matrix, on 3..8 tokens of a matrix
+ * of at least 3072 rows, on 5..8 tokens of at least 2048 rows, and on 6..8 tokens of
+ * at least 1024 rows of at most 4096 columns; otherwise QMM_KIND_MMVQ for nt <= 8 and for 9..16
  * tokens on od <= 4096 rows (as launches on slices of 8 tokens: the MMQ tile grid
  * of such a matrix fills at most a quarter of the GPU); QMM_KIND_MMQ beyond.  With
  * another switch: QMM_KIND_MMVQ for nt <= the switch, QMM_KIND_MMQ above.  A

@@ -142,9 +142,9 @@ int nt_switch_value()
 
 int launched(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH; }
 
-// QMM_SKINNY_CFG (RT * 100 + KS: 16*RT rows per wave, RT 1 or 2, and KS <= 8 waves
-// per workgroup of the small-batch kernel) forces its configuration, read once, for
-// tuning sweeps; 0 = by shape.
+// QMM_SKINNY_CFG (100 + KS: KS = 1, 2, 4 or 8 waves per workgroup of the
+// small-batch kernel, splitting K) forces its configuration, read once, for tuning
+// sweeps (the results do not depend on it); 0 = by shape and token count.
 int skinny_cfg_override()
 {
     static int v = -1;
@@ -153,30 +153,30 @@ int skinny_cfg_override()
         return cur;
     const char* e = getenv("QMM_SKINNY_CFG");
     int val = e ? atoi(e) : 0;
-    if (val < 101 || val > 208 || val % 100 > 8 || val % 100 == 0)
+    if (val != 101 && val != 102 && val != 104 && val != 108)
         val = 0;
     __atomic_store_n(&v, val, __ATOMIC_RELEASE);
     return val;
 }
 
 // The kernel a call runs.  With the default switch (8): Q4_K runs the small-batch
-// MFMA kernel on 9..16 tokens of any matrix, on 5..8 tokens of a matrix of at least
-// 2048 rows, on 4 tokens of at least 3072 rows, and on 3 tokens of at least 3072
-// rows with at least 8192 rows or columns (measured, us, small-batch against MMVQ:
-// 4096 x 4096 nt = 4: 5.1 / 5.6, nt = 8: 5.5 / 7.8; 12288 x 4096 nt = 3: 8.9 / 9.6,
-// nt = 4: 9.0 / 10.3, nt = 8: 10.7 / 16.6; 3072 x 12288 nt = 3: 9.0 / 9.7, nt = 4:
-// 9.4 / 10.4; 2048 x 12288 nt = 4: 9.0 / 7.7, nt = 6: 9.9 / 11.9; 2048 x 4096
-// nt = 4: 4.5 / 4.1, nt = 8: 5.0 / 5.5; 4096 x 4096 nt = 3: equal; 9..16 tokens:
-// 6-15 us against 21-58 for MMQ); MMVQ up to the switch otherwise; other types also on 9..16 tokens of a matrix of at most
-// 4096 rows, as launches on token slices of 8 (such a matrix gives MMQ at most 64
-// tiles of 64 rows, a quarter of the 256 CUs; 4096 x 4096: MMQ 22 us, two MMVQ
-// launches 13.7-14.7 us); MMQ beyond.
+// MFMA kernel on 9..16 tokens of any matrix, on 3..8 tokens of a matrix of at least
+// 3072 rows, on 5..8 tokens of at least 2048 rows, and on 6..8 tokens of at least
+// 1024 rows of at most 4096 columns (measured, us, small-batch against MMVQ, one
+// process: nt = 3: 3072 x 3072 4.0 / 4.6, 4096 x 4096 4.8 / 5.2, 12288 x 4096 8.3 /
+// 9.8, 3072 x 12288 8.5 / 9.5; 2048 x 4096 nt = 3: 4.0 / 3.8; 2048 x 12288 nt = 4:
+// 8.5 / 7.6, nt = 5: 9.0 / 10.4; 1024 x 4096 nt = 5: 4.1 / 4.0, nt = 6: 4.1 / 4.3,
+// nt = 8: 4.3 / 4.9; 1024 x 12288 nt = 8: 10.1 / 7.6; 12288 x 4096 nt = 8: 10.0 /
+// 16.8; at 2 tokens within a few per cent either way, so MMVQ; 9..16 tokens: 6-15 us
+// against 21-58 for MMQ); MMVQ up to the switch otherwise; other types also on
+// 9..16 tokens of a matrix of at most 4096 rows, as launches on token slices of 8
+// (such a matrix gives MMQ at most 64 tiles of 64 rows, a quarter of the 256 CUs;
+// 4096 x 4096: MMQ 22 us, two MMVQ launches 13.7-14.7 us); MMQ beyond.
 int dispatch_kind(int type, int nt, int od, int id)
 {
     const int sw = nt_switch_value();
     if (sw == 8 && type == QMM_TYPE_Q4_K && nt <= 16 &&
-        (nt >= 9 || (nt >= 5 && od >= 2048) || (nt == 4 && od >= 3072) ||
-         (nt == 3 && od >= 3072 && (od >= 8192 || id >= 8192))))
+        (nt >= 9 || (nt >= 3 && od >= 3072) || (nt >= 5 && od >= 2048) || (nt >= 6 && od >= 1024 && id <= 4096)))
         return QMM_KIND_SKINNY;
     if (nt <= sw || (sw == 8 && nt <= 16 && od <= 4096))
         return QMM_KIND_MMVQ;

@@ -35,9 +35,10 @@
 //    the MFMA operand layout (no barrier: one wave's LDS operations complete in
 //    order).  The next super-block's loads are issued before the current one is
 //    staged and computed.
-//  * A wave takes RT tiles of 16 rows; their MFMAs share the activation operand.
-//    The KS waves of a workgroup split K (super-blocks w, w + KS, ...) and add
-//    their partial sums through LDS in wave order at the end (a fixed order).
+//  * A wave takes RT tiles of 16 rows (RT = 1 is launched); their MFMAs share the
+//    activation operand.  The KS waves of a workgroup split K (super-blocks w,
+//    w + KS, ...); the partial sums are kept per virtual wave of an 8-way split and
+//    added through LDS in a fixed order, so the result does not depend on KS.
 //  * Tokens past nt read the last token (their results are not stored); rows past
 //    od read the last row.
 #include "qmm_mmq_common.h"
@@ -195,25 +196,32 @@ __device__ __forceinline__ uint32_t sk_vgpr(uint32_t bits)
     return v;
 }
 
-// Workgroup: ks waves (ks <= 8) splitting K, wave w taking super-blocks w, w + ks,
-// ...; all over the same RT*16 rows.  N > 0: every wave has exactly N super-blocks
-// (ks * N == nsb); N = 0: any share.  NTB >= nt tokens are
-// staged (the 16-token tile's other lanes repeat token NTB-1 or nt-1; their results
-// are not stored).  Dynamic LDS: ks stage areas, then ks partial tiles.
-constexpr int kSkMaxWaves = 8;
+// Workgroup: KS waves (KS = 1, 2, 4 or 8) splitting K, wave w taking super-blocks
+// w, w + KS, ...; all over the same RT*16 rows.  N > 0: every wave has exactly N
+// super-blocks (KS * N == nsb); N = 0: any share.  NTB >= nt tokens are staged
+// (the 16-token tile's other lanes repeat token NTB-1 or nt-1; their results are
+// not stored).
+//
+// The sum does not depend on KS: super-block sb belongs to virtual wave sb % 8 of
+// an 8-way split, each wave keeps one accumulator per virtual wave it covers (8 / KS
+// of them: super-blocks v, v + 8, v + 16, ... in order), and the 8 virtual partial
+// tiles are added in the order 0, 1, .., 7.  So every KS gives the same bits, a
+// token's result does not depend on the other tokens of the call, and KS is chosen
+// per shape and token count for speed alone.  Dynamic LDS: KS stage areas, then the
+// 8 partial tiles.
+constexpr int kSkMaxWaves = 8, kSkVirt = 8;
 
-template <int RT, int NTB, int N>
-__global__ __launch_bounds__(64 * kSkMaxWaves) void mmq_skinny_q4k_kernel(const uint8_t* __restrict__ W,
-                                                                         const int8_t* __restrict__ q,
-                                                                         const float* __restrict__ dx,
-                                                                         const float* __restrict__ sx,
-                                                                         float* __restrict__ out, int nt, int od,
-                                                                         int id)
+template <int RT, int NTB, int N, int KS>
+__global__ __launch_bounds__(64 * KS) void mmq_skinny_q4k_kernel(const uint8_t* __restrict__ W,
+                                                                 const int8_t* __restrict__ q,
+                                                                 const float* __restrict__ dx,
+                                                                 const float* __restrict__ sx,
+                                                                 float* __restrict__ out, int nt, int od, int id)
 {
+    constexpr int NV = kSkVirt / KS;   // virtual waves per wave
     extern __shared__ __attribute__((aligned(16))) uint8_t sk_lds[];
-    const int ks = (int)(blockDim.x >> 6);
     auto* stage = reinterpret_cast<SkStage<RT, NTB>*>(sk_lds);
-    auto* red = reinterpret_cast<float*>(sk_lds + (size_t)ks * sizeof(SkStage<RT, NTB>));
+    auto* red = reinterpret_cast<float*>(sk_lds + (size_t)KS * sizeof(SkStage<RT, NTB>));
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int p = lane >> 4;
@@ -242,19 +250,24 @@ __global__ __launch_bounds__(64 * kSkMaxWaves) void mmq_skinny_q4k_kernel(const 
     const v4i magic = {mg, mg, mg, mg};
     SkStage<RT, NTB>& my = stage[w];
 
-    v4f acc[RT];
+    // acc[j]: virtual wave w + j * KS (super-blocks w + j * KS, + 8, + 16, ...)
+    v4f acc[NV][RT];
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
-        acc[r] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+            acc[j][r] = (v4f){0.f, 0.f, 0.f, 0.f};
+    int rot = 0;   // the loop form rotates acc: acc[j] then holds virtual wave w + ((rot + j) % NV) * KS
 
     if constexpr (N > 0) {
-        // exactly N super-blocks per wave (ks * N == nsb): every load first, then
+        // exactly N super-blocks per wave (KS * N == nsb): every load first, then
         // stage and compute in order -- straight-line code, so the compiler waits
-        // for one set at a time (one memory latency per wave)
+        // for one set at a time (one memory latency per wave); the k-th
+        // super-block (w + k * KS) belongs to virtual wave w + (k % NV) * KS
         SkLoad<RT, NTB> L[N];
 #pragma unroll
         for (int k = 0; k < N; ++k) {
-            sk_load<RT, NTB>(L[k], ad, w + k * ks);
+            sk_load<RT, NTB>(L[k], ad, w + k * KS);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -262,142 +275,153 @@ __global__ __launch_bounds__(64 * kSkMaxWaves) void mmq_skinny_q4k_kernel(const 
             sk_handover();
             sk_stage<RT, NTB>(my, L[k], lane);
             sk_handover();
-            sk_superblock<RT, NTB>(my, L[k], acc, lane, mask, Mv, magic);
+            sk_superblock<RT, NTB>(my, L[k], acc[k % NV], lane, mask, Mv, magic);
         }
     } else {
-        // super-blocks w, w + ks, ...: two per trip so the load sets alternate, the
+        // super-blocks w, w + KS, ...: two per trip so the load sets alternate, the
         // odd last one after the loop (no exit between a prefetch and its use: the
-        // compiler keeps the loads where they are issued)
-        const int n = (nsb - w + ks - 1) / ks;  // >= 1: the launch has ks <= nsb
+        // compiler keeps the loads where they are issued).  Each super-block adds
+        // into acc[0], then the accumulators rotate by one, so acc[0] always holds
+        // the virtual wave of the next super-block.
+        const int n = (nsb - w + KS - 1) / KS;  // >= 1: the launch has KS <= nsb
+        auto rotate = [&]() {
+            if constexpr (NV > 1) {
+#pragma unroll
+                for (int r = 0; r < RT; ++r) {
+                    const v4f t = acc[0][r];
+#pragma unroll
+                    for (int j = 0; j + 1 < NV; ++j)
+                        acc[j][r] = acc[j + 1][r];
+                    acc[NV - 1][r] = t;
+                }
+            }
+        };
         SkLoad<RT, NTB> A, B;
         sk_load<RT, NTB>(A, ad, w);
         for (int i = 0; i + 1 < n; i += 2) {
-            const int sb = w + i * ks;
-            sk_load<RT, NTB>(B, ad, sb + ks);
+            const int sb = w + i * KS;
+            sk_load<RT, NTB>(B, ad, sb + KS);
             __builtin_amdgcn_sched_barrier(0);
             sk_handover();
             sk_stage<RT, NTB>(my, A, lane);
             sk_handover();
-            sk_superblock<RT, NTB>(my, A, acc, lane, mask, Mv, magic);
-            sk_load<RT, NTB>(A, ad, min(sb + 2 * ks, nsb - 1));
+            sk_superblock<RT, NTB>(my, A, acc[0], lane, mask, Mv, magic);
+            rotate();
+            sk_load<RT, NTB>(A, ad, min(sb + 2 * KS, nsb - 1));
             __builtin_amdgcn_sched_barrier(0);
             sk_handover();
             sk_stage<RT, NTB>(my, B, lane);
             sk_handover();
-            sk_superblock<RT, NTB>(my, B, acc, lane, mask, Mv, magic);
+            sk_superblock<RT, NTB>(my, B, acc[0], lane, mask, Mv, magic);
+            rotate();
         }
         if (n & 1) {
             sk_handover();
             sk_stage<RT, NTB>(my, A, lane);
             sk_handover();
-            sk_superblock<RT, NTB>(my, A, acc, lane, mask, Mv, magic);
+            sk_superblock<RT, NTB>(my, A, acc[0], lane, mask, Mv, magic);
+            rotate();
         }
+        rot = n % NV;
     }
-    if (ks > 1) {
-        // every wave's partial tile to LDS; then wave w adds value v = w, w + ks, ...
-        // (value v: tile v / 4, token slot 4p + v % 4) over the waves in the order
-        // 0, 1, .., ks-1 and stores it
+    // every wave's virtual partial tiles to LDS (tile v at red[v][r][i][lane]); then
+    // wave w adds value e = w, w + KS, ... (value e: row tile e / 4, token slot
+    // 4p + e % 4) over the virtual waves in the order 0, 1, .., 7 and stores it
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int v = w + ((rot + j) % NV) * KS;
 #pragma unroll
         for (int r = 0; r < RT; ++r)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                red[((w * RT + r) * 4 + i) * 64 + lane] = acc[r][i];
-        __syncthreads();
-        for (int v = w; v < RT * 4; v += ks) {
-            float sum = red[v * 64 + lane];
-            for (int k = 1; k < ks; ++k)
-                sum += red[(k * RT * 4 + v) * 64 + lane];
-            const int row = row0 + 16 * (v >> 2) + (lane & 15), t = 4 * p + (v & 3);
-            if (row < od && t < nt)
-                out[(size_t)t * od + row] = sum;
-        }
-        return;
+                red[((v * RT + r) * 4 + i) * 64 + lane] = acc[j][r][i];
     }
+    __syncthreads();
+    for (int e = w; e < RT * 4; e += KS) {
+        float sum = red[e * 64 + lane];
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-        const int row = row0 + 16 * r + (lane & 15);
-        if (row < od) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 4 * p + i;
-                if (t < nt)
-                    out[(size_t)t * od + row] = acc[r][i];
-            }
-        }
+        for (int v = 1; v < kSkVirt; ++v)
+            sum += red[(v * RT * 4 + e) * 64 + lane];
+        const int row = row0 + 16 * (e >> 2) + (lane & 15), t = 4 * p + (e & 3);
+        if (row < od && t < nt)
+            out[(size_t)t * od + row] = sum;
     }
 }
 
-template <int RT, int NTB, int N>
+template <int NTB, int N, int KS>
 hipError_t launch_rk(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od, int id,
-                     float* out, int ks, hipStream_t st)
+                     float* out, hipStream_t st)
 {
+    constexpr int RT = 1;
     const int grid = (od + 16 * RT - 1) / (16 * RT);
-    const size_t lds = (size_t)ks * (sizeof(SkStage<RT, NTB>) + (size_t)RT * 4 * 64 * sizeof(float));
-    hipLaunchKernelGGL((mmq_skinny_q4k_kernel<RT, NTB, N>), dim3(grid), dim3(64 * ks), lds, st, W, q, d, s, out, nt,
-                       od, id);
+    const size_t lds = (size_t)KS * sizeof(SkStage<RT, NTB>) + (size_t)kSkVirt * RT * 4 * 64 * sizeof(float);
+    hipLaunchKernelGGL((mmq_skinny_q4k_kernel<RT, NTB, N, KS>), dim3(grid), dim3(64 * KS), lds, st, W, q, d, s, out,
+                       nt, od, id);
     return hipGetLastError();
 }
 
 // Straight-line form when the waves share K evenly in at most 4 super-blocks each.
-template <int RT, int NTB>
+template <int NTB, int KS>
 hipError_t launch_rkk(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od, int id,
-                      float* out, int ks, hipStream_t st)
+                      float* out, hipStream_t st)
 {
     const int nsb = id / 256;
-    switch (nsb % ks ? 0 : nsb / ks) {
-    case 1: return launch_rk<RT, NTB, 1>(W, q, d, s, nt, od, id, out, ks, st);
-    case 2: return launch_rk<RT, NTB, 2>(W, q, d, s, nt, od, id, out, ks, st);
-    case 3: return launch_rk<RT, NTB, 3>(W, q, d, s, nt, od, id, out, ks, st);
-    case 4: return launch_rk<RT, NTB, 4>(W, q, d, s, nt, od, id, out, ks, st);
-    default: return launch_rk<RT, NTB, 0>(W, q, d, s, nt, od, id, out, ks, st);
+    switch (nsb % KS ? 0 : nsb / KS) {
+    case 1: return launch_rk<NTB, 1, KS>(W, q, d, s, nt, od, id, out, st);
+    case 2: return launch_rk<NTB, 2, KS>(W, q, d, s, nt, od, id, out, st);
+    case 3: return launch_rk<NTB, 3, KS>(W, q, d, s, nt, od, id, out, st);
+    case 4: return launch_rk<NTB, 4, KS>(W, q, d, s, nt, od, id, out, st);
+    default: return launch_rk<NTB, 0, KS>(W, q, d, s, nt, od, id, out, st);
     }
 }
 
-template <int RT>
+template <int NTB>
 hipError_t launch_rkn(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od, int id,
                       float* out, int ks, hipStream_t st)
 {
-    if (nt <= 4)
-        return launch_rkk<RT, 4>(W, q, d, s, nt, od, id, out, ks, st);
-    if (nt <= 8)
-        return launch_rkk<RT, 8>(W, q, d, s, nt, od, id, out, ks, st);
-    return launch_rkk<RT, 16>(W, q, d, s, nt, od, id, out, ks, st);
+    switch (ks) {
+    case 1: return launch_rkk<NTB, 1>(W, q, d, s, nt, od, id, out, st);
+    case 2: return launch_rkk<NTB, 2>(W, q, d, s, nt, od, id, out, st);
+    case 4: return launch_rkk<NTB, 4>(W, q, d, s, nt, od, id, out, st);
+    default: return launch_rkk<NTB, 8>(W, q, d, s, nt, od, id, out, st);
+    }
 }
 
 }  // namespace
 
-// Rows per wave (16 * RT) and waves per workgroup (ks, splitting K): enough waves
-// in flight for the weight stream (about 2048 over the chip), up to 8, preferring
-// a ks that divides the super-block count (every wave then runs the straight-line
-// form when its share is at most 4).
-// cfg != 0 forces RT * 100 + ks (RT 1 or 2, ks 1..8) for tuning sweeps.
+// Waves per workgroup (ks, splitting K; 1, 2, 4 or 8, never more than the
+// super-blocks): enough waves in flight for the weight stream and a short compute
+// after the last bytes land.  ks does not change the results (see the kernel), so
+// the choice is by speed alone, measured over 8192..14336 x 4096 (us, 4 / 8 waves
+// splitting K, same process): at 1..4 tokens 8 waves everywhere (12288: 9.2 ->
+// 8.6, 14336: 10.7 -> 10.0, 8192: 7.4 -> 6.7); at 5..8 tokens about 3072 waves in
+// flight (8192 x 4096 nt = 8: 8.2 -> 7.7 with 8; 12288: 10.3 against 10.7 with 4);
+// at 9..16 tokens about 2048 waves.
+// cfg != 0 forces 100 + ks (ks 1, 2, 4 or 8) for tuning sweeps.
 hipError_t launch_skinny(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od, int id,
                          float* out, hipStream_t st, int cfg)
 {
     if (nt < 1 || nt > 16)
         return hipErrorInvalidValue;
     const int nsb = id / 256;
-    int rt = 1, ks;
+    int ks;
     if (cfg) {
-        rt = cfg / 100;
-        ks = cfg % 100;
-        if ((rt != 1 && rt != 2) || ks < 1 || ks > kSkMaxWaves)
+        ks = cfg - 100;
+        if (ks != 1 && ks != 2 && ks != 4 && ks != 8)
             return hipErrorInvalidValue;
     } else {
-        // the smallest divisor of nsb (up to 8) that gives about 2048 waves in flight
         const int grid = (od + 15) / 16;
-        const int want = min(max((2048 + grid - 1) / grid, 1), kSkMaxWaves);
-        ks = 0;
-        for (int k = want; k <= kSkMaxWaves && !ks; ++k)
-            if (nsb % k == 0)
-                ks = k;
-        if (!ks)
-            ks = min(want, nsb);
-        ks = min(ks, nsb);
+        const int target = nt <= 4 ? 1 << 30 : nt <= 8 ? 3072 : 2048;   // waves in flight
+        const long want = (target + (long)grid - 1) / grid;
+        ks = want <= 1 ? 1 : want <= 2 ? 2 : want <= 4 ? 4 : 8;
     }
-    if (rt == 2)
-        return launch_rkn<2>(W, q, d, s, nt, od, id, out, ks, st);
-    return launch_rkn<1>(W, q, d, s, nt, od, id, out, ks, st);
+    while (ks > nsb)
+        ks >>= 1;
+    if (nt <= 4)
+        return launch_rkn<4>(W, q, d, s, nt, od, id, out, ks, st);
+    if (nt <= 8)
+        return launch_rkn<8>(W, q, d, s, nt, od, id, out, ks, st);
+    return launch_rkn<16>(W, q, d, s, nt, od, id, out, ks, st);
 }
 
 }  // namespace qmm

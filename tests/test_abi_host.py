@@ -62,22 +62,22 @@ def test_act_bytes():
 def test_dispatch_kind_host():
     assert qmm.qmm_nt_switch() == 8
     Q4, Q6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K
-    # Q4_K: the small-batch kernel on 9..16 tokens of any matrix, on 5..8 tokens from
-    # 2048 rows, on 4 tokens from 3072 rows, on 3 tokens from 3072 rows with 8192 rows
-    # or columns; MMVQ otherwise
+    # Q4_K: the small-batch kernel on 9..16 tokens of any matrix, on 3..8 tokens from
+    # 3072 rows, on 5..8 tokens from 2048 rows, on 6..8 tokens from 1024 rows of at
+    # most 4096 columns; MMVQ otherwise
     for nt in range(1, 17):
-        for od in (2048, 3072, 4096, 12288):
+        for od in (1024, 2048, 3072, 4096, 12288):
             for idim in (4096, 12288):
-                big = od >= 8192 or idim >= 8192
-                sk = (nt >= 9 or (nt >= 5 and od >= 2048) or (nt == 4 and od >= 3072) or
-                      (nt == 3 and od >= 3072 and big))
+                sk = (nt >= 9 or (nt >= 3 and od >= 3072) or (nt >= 5 and od >= 2048) or
+                      (nt >= 6 and od >= 1024 and idim <= 4096))
                 want = qmm.QMM_KIND_SKINNY if sk else qmm.QMM_KIND_MMVQ
                 assert qmm.qmm_dispatch_kind(Q4, nt, od, idim) == want, (nt, od, idim)
-        assert qmm.qmm_dispatch_kind(Q4, 3, 8191, 8191 // 256 * 256) == qmm.QMM_KIND_MMVQ
-        assert qmm.qmm_dispatch_kind(Q4, 3, 8192, 4096) == qmm.QMM_KIND_SKINNY
-        assert qmm.qmm_dispatch_kind(Q4, 4, 3071, 4096) == qmm.QMM_KIND_MMVQ
+        assert qmm.qmm_dispatch_kind(Q4, 3, 3072, 3072) == qmm.QMM_KIND_SKINNY
+        assert qmm.qmm_dispatch_kind(Q4, 3, 3071, 4096) == qmm.QMM_KIND_MMVQ
+        assert qmm.qmm_dispatch_kind(Q4, 6, 1023, 4096) == qmm.QMM_KIND_MMVQ
+        assert qmm.qmm_dispatch_kind(Q4, 6, 1024, 4352) == qmm.QMM_KIND_MMVQ
         want = qmm.QMM_KIND_SKINNY if nt >= 9 else qmm.QMM_KIND_MMVQ
-        assert qmm.qmm_dispatch_kind(Q4, nt, 2047, 4096) == want
+        assert qmm.qmm_dispatch_kind(Q4, nt, 1023, 4096) == want
         assert qmm.qmm_dispatch_kind(Q4, nt, 64, 12288) == want
     assert qmm.qmm_dispatch_kind(Q4, 17, 4096, 4096) == qmm.QMM_KIND_MMQ
     # other types: MMVQ up to 8 tokens; 9..16 tokens on token slices of 8 up to 4096

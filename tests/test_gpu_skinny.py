@@ -88,6 +88,25 @@ def test_skinny_deterministic():
     assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
 
 
+@pytest.mark.parametrize("od,idim,nts", [(12288, 4096, (6, 12)), (20000, 1024, (12,)), (40000, 512, (16,)),
+                                         (8192, 4096, (3, 7, 16))])
+def test_skinny_split_independent(od, idim, nts):
+    """The K split (1, 2, 4 or 8 waves, chosen by shape and token count) does not
+    change the bits: every token row of an nt-token call equals that token alone
+    (single-token calls run an 8-way split, capped by the super-block count; these
+    calls run 4 (12288 x 4096), 2 (20000 x 1024), 1 (40000 x 512) and 8 / 8 / 4
+    (8192 x 4096) waves)."""
+    _say(f"skinny split independence {od}x{idim} nt={nts}")
+    W = _up(synth.weights(Q4, od, idim, seed=41))
+    q, d, s = qmm.qmm_quantize_act(_up(synth.activations(max(nts), idim, seed=42)))
+    ones = [qmm.qmm_matmul_q8_kind(K7, Q4, W, q[t:t + 1].contiguous(), d[t:t + 1].contiguous(),
+                                   s[t:t + 1].contiguous(), od) for t in range(max(nts))]
+    for nt in nts:
+        o = qmm.qmm_matmul_q8_kind(K7, Q4, W, q[:nt].contiguous(), d[:nt].contiguous(), s[:nt].contiguous(), od)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int32), torch.cat(ones[:nt]).view(torch.int32)), f"{od}x{idim} nt={nt}"
+
+
 def test_skinny_refusals():
     W = _up(synth.weights(Q4, 16, 256, seed=3))
     q, d, s = qmm.qmm_quantize_act(_up(synth.activations(17, 256, seed=4)))
