@@ -253,6 +253,14 @@ int qmm_streamk_preferred(int type, int nt, int od, int id);
  * 9..16-token rules of qmm_dispatch_kind). */
 int qmm_nt_switch(void);
 
+/* For tests and tuning: force the K split of the small-batch kernel (QMM_KIND_SKINNY)
+ * to ks = 1, 2, 4 or 8 waves per workgroup (never more than the super-blocks of a
+ * row), or 0 for the default (8).  The kernel sums over a fixed 8-way split, so its
+ * results are the same bits for every ks; only its speed changes.  Process-wide, for
+ * all devices and later calls; not synchronised with calls already enqueued.
+ * Returns QMM_OK, or QMM_ERR_ARG for another value.  Host function, no device work. */
+int qmm_set_skinny_split(int ks);
+
 /* ---- Q8_K activations: one scale per 256 values ------------------------------
  * [GEMM, "Activations: int8 with a scale per 256"]: each activation row quantized
  * to int8 with one f32 scale per 256 values and the sum of every 16-value group of

@@ -54,7 +54,7 @@ EXPORTS = ("qmm_weight_bytes", "qmm_act_bytes", "qmm_quantize_act", "qmm_matmul"
            "qmm_silu_mul_quantize", "qmm_add_rmsnorm_quantize_q8k", "qmm_rmsnorm_quantize_q8k",
            "qmm_silu_mul_quantize_q8k", "qmm_residual_add", "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k",
            "qmm_matmul_q8k", "qmm_matmul_q8k_kind", "qmm_q8k_tile", "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_streamk_ws_bytes",
-           "qmm_matmul_q8_streamk", "qmm_streamk_preferred", "qmm_matmul_noalloc")
+           "qmm_matmul_q8_streamk", "qmm_streamk_preferred", "qmm_matmul_noalloc", "qmm_set_skinny_split")
 
 
 class QmmError(RuntimeError):
@@ -88,6 +88,7 @@ def lib():
         L.qmm_streamk_preferred.argtypes = [I, I, I, I]
         L.qmm_mmq_tile.argtypes = [I, I, I]
         L.qmm_nt_switch.argtypes = []
+        L.qmm_set_skinny_split.argtypes = [I]
         L.qmm_group_dots.argtypes = [I, I, P, P, I, I, I, P, P]
         L.qmm_mfma_tile_check.argtypes = [I, P, P, P, P]
         F = ctypes.c_float
@@ -117,7 +118,8 @@ def lib():
                   "qmm_add_rmsnorm_quantize_q8k", "qmm_rmsnorm_quantize_q8k", "qmm_silu_mul_quantize_q8k",
                   "qmm_residual_add",
                   "qmm_rmsnorm", "qmm_silu_mul", "qmm_quantize_act_q8k", "qmm_matmul_q8k", "qmm_matmul_q8k_kind",
-                  "qmm_q8k_tile", "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_matmul_q8_streamk", "qmm_streamk_preferred"):
+                  "qmm_q8k_tile", "qmm_q8k_superblock_sums", "qmm_pad_q6k", "qmm_matmul_q8_streamk", "qmm_streamk_preferred",
+                  "qmm_set_skinny_split"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -173,6 +175,12 @@ def qmm_act_bytes(nt: int, idim: int) -> int:
 
 def qmm_nt_switch() -> int:
     return int(lib().qmm_nt_switch())
+
+
+def qmm_set_skinny_split(ks: int) -> None:
+    """Force the small-batch kernel's K split (1, 2, 4 or 8 waves; 0 = default).
+    Process-wide; the results do not depend on it (tests and tuning)."""
+    _check(int(lib().qmm_set_skinny_split(ks)), "qmm_set_skinny_split")
 
 
 def qmm_dispatch_kind(qtype: int, nt: int, od: int, idim: int) -> int:

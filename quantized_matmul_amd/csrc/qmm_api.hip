@@ -142,21 +142,24 @@ int nt_switch_value()
 
 int launched(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH; }
 
-// QMM_SKINNY_CFG (100 + KS: KS = 1, 2, 4 or 8 waves per workgroup of the
-// small-batch kernel, splitting K) forces its configuration, read once, for tuning
-// sweeps (the results do not depend on it); 0 = by shape and token count.
+// The small-batch kernel's K split: 100 + KS (KS = 1, 2, 4 or 8 waves per workgroup)
+// forced, 0 = by shape; set by qmm_set_skinny_split, else read once from
+// QMM_SKINNY_CFG (the same encoding), for tests and tuning sweeps (the results do
+// not depend on it).
+int g_skinny_cfg = -1;
+
 int skinny_cfg_override()
 {
-    static int v = -1;
-    int cur = __atomic_load_n(&v, __ATOMIC_ACQUIRE);
+    int cur = __atomic_load_n(&g_skinny_cfg, __ATOMIC_ACQUIRE);
     if (cur >= 0)
         return cur;
     const char* e = getenv("QMM_SKINNY_CFG");
     int val = e ? atoi(e) : 0;
     if (val != 101 && val != 102 && val != 104 && val != 108)
         val = 0;
-    __atomic_store_n(&v, val, __ATOMIC_RELEASE);
-    return val;
+    int expect = -1;
+    __atomic_compare_exchange_n(&g_skinny_cfg, &expect, val, false, __ATOMIC_ACQ_REL, __ATOMIC_ACQUIRE);
+    return __atomic_load_n(&g_skinny_cfg, __ATOMIC_ACQUIRE);
 }
 
 // The kernel a call runs.  With the default switch (8): Q4_K runs the small-batch
@@ -566,6 +569,14 @@ int qmm_matmul_q8_streamk(int type, const void* W, const int8_t* q, const float*
 }
 
 int qmm_nt_switch(void) { return nt_switch_value(); }
+
+int qmm_set_skinny_split(int ks)
+{
+    if (ks != 0 && ks != 1 && ks != 2 && ks != 4 && ks != 8)
+        return QMM_ERR_ARG;
+    __atomic_store_n(&g_skinny_cfg, ks ? 100 + ks : 0, __ATOMIC_RELEASE);
+    return QMM_OK;
+}
 
 int qmm_streamk_preferred(int type, int nt, int od, int id)
 {

@@ -390,14 +390,12 @@ hipError_t launch_rkn(const uint8_t* W, const int8_t* q, const float* d, const f
 }  // namespace
 
 // Waves per workgroup (ks, splitting K; 1, 2, 4 or 8, never more than the
-// super-blocks): enough waves in flight for the weight stream and a short compute
-// after the last bytes land.  ks does not change the results (see the kernel), so
-// the choice is by speed alone, measured over 8192..14336 x 4096 (us, 4 / 8 waves
-// splitting K, same process): at 1..4 tokens 8 waves everywhere (12288: 9.2 ->
-// 8.6, 14336: 10.7 -> 10.0, 8192: 7.4 -> 6.7); at 5..8 tokens about 3072 waves in
-// flight (8192 x 4096 nt = 8: 8.2 -> 7.7 with 8; 12288: 10.3 against 10.7 with 4);
-// at 9..16 tokens about 2048 waves.
-// cfg != 0 forces 100 + ks (ks 1, 2, 4 or 8) for tuning sweeps.
+// super-blocks): 8.  ks does not change the results (see the kernel), so the choice
+// is by speed alone; 8 waves were as fast as 4 or faster at every token count
+// measured on 8192..16384 x 4096 (us, alternating processes: 12288 x 4096 nt = 4
+// 9.2 -> 8.6, nt = 8 10.3 -> 10.0, nt = 16 13.0 -> 12.1; 8192 x 4096 nt = 8 8.1 ->
+// 7.2; 16384 x 4096 nt = 8 12.5 either way).
+// cfg != 0 forces 100 + ks (ks 1, 2, 4 or 8) for tests and tuning.
 hipError_t launch_skinny(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od, int id,
                          float* out, hipStream_t st, int cfg)
 {
@@ -410,10 +408,7 @@ hipError_t launch_skinny(const uint8_t* W, const int8_t* q, const float* d, cons
         if (ks != 1 && ks != 2 && ks != 4 && ks != 8)
             return hipErrorInvalidValue;
     } else {
-        const int grid = (od + 15) / 16;
-        const int target = nt <= 4 ? 1 << 30 : nt <= 8 ? 3072 : 2048;   // waves in flight
-        const long want = (target + (long)grid - 1) / grid;
-        ks = want <= 1 ? 1 : want <= 2 ? 2 : want <= 4 ? 4 : 8;
+        ks = kSkMaxWaves;
     }
     while (ks > nsb)
         ks >>= 1;

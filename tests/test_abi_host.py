@@ -59,6 +59,19 @@ def test_act_bytes():
     assert qmm.qmm_act_bytes(0, 256) == 0 and qmm.qmm_act_bytes(1, 33) == 0
 
 
+def test_set_skinny_split_host():
+    """The small-batch split setting takes 0, 1, 2, 4 and 8 and refuses anything else
+    before touching any state (host only)."""
+    try:
+        for ks in (1, 2, 4, 8, 0):
+            qmm.qmm_set_skinny_split(ks)
+        for bad in (3, 5, 16, -1):
+            with pytest.raises(qmm.QmmError):
+                qmm.qmm_set_skinny_split(bad)
+    finally:
+        qmm.qmm_set_skinny_split(0)
+
+
 def test_dispatch_kind_host():
     assert qmm.qmm_nt_switch() == 8
     Q4, Q6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K

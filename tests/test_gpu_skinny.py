@@ -88,23 +88,34 @@ def test_skinny_deterministic():
     assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
 
 
-@pytest.mark.parametrize("od,idim,nts", [(12288, 4096, (6, 12)), (20000, 1024, (12,)), (40000, 512, (16,)),
-                                         (8192, 4096, (3, 7, 16))])
-def test_skinny_split_independent(od, idim, nts):
-    """The K split (1, 2, 4 or 8 waves, chosen by shape and token count) does not
-    change the bits: every token row of an nt-token call equals that token alone
-    (single-token calls run an 8-way split, capped by the super-block count; these
-    calls run 4 (12288 x 4096), 2 (20000 x 1024), 1 (40000 x 512) and 8 / 8 / 4
-    (8192 x 4096) waves)."""
-    _say(f"skinny split independence {od}x{idim} nt={nts}")
-    W = _up(synth.weights(Q4, od, idim, seed=41))
-    q, d, s = qmm.qmm_quantize_act(_up(synth.activations(max(nts), idim, seed=42)))
-    ones = [qmm.qmm_matmul_q8_kind(K7, Q4, W, q[t:t + 1].contiguous(), d[t:t + 1].contiguous(),
-                                   s[t:t + 1].contiguous(), od) for t in range(max(nts))]
-    for nt in nts:
-        o = qmm.qmm_matmul_q8_kind(K7, Q4, W, q[:nt].contiguous(), d[:nt].contiguous(), s[:nt].contiguous(), od)
+@pytest.mark.parametrize("od,idim,nt", [(12288, 4096, 4), (12288, 4096, 8), (12288, 4096, 16), (1000, 2304, 5),
+                                        (500, 768, 3), (4096, 12288, 8), (257, 1024, 12)])
+def test_skinny_split_independent(od, idim, nt):
+    """The K split (1, 2, 4 or 8 waves per workgroup, forced through
+    qmm_set_skinny_split; capped by the super-blocks of a row) does not change the
+    bits: 16 super-blocks (straight-line at 8 and 4 waves, the loop at 2 and 1), 9
+    and 3 super-blocks (loop forms, unequal shares), 48 super-blocks (loops with 1,
+    2, 4 and 8 accumulators per wave), 4 super-blocks; and every token row equals
+    that token alone."""
+    _say(f"skinny split independence {od}x{idim} nt={nt}")
+    W = _up(synth.weights(Q4, od, idim, seed=41 + nt))
+    q, d, s = qmm.qmm_quantize_act(_up(synth.activations(nt, idim, seed=42 + od)))
+    outs = {}
+    try:
+        for ks in (8, 4, 2, 1):
+            qmm.qmm_set_skinny_split(ks)
+            outs[ks] = qmm.qmm_matmul_q8_kind(K7, Q4, W, q, d, s, od)
+            torch.cuda.synchronize()
+        qmm.qmm_set_skinny_split(0)
+        ones = [qmm.qmm_matmul_q8_kind(K7, Q4, W, q[t:t + 1].contiguous(), d[t:t + 1].contiguous(),
+                                       s[t:t + 1].contiguous(), od) for t in range(nt)]
         torch.cuda.synchronize()
-        assert torch.equal(o.view(torch.int32), torch.cat(ones[:nt]).view(torch.int32)), f"{od}x{idim} nt={nt}"
+    finally:
+        qmm.qmm_set_skinny_split(0)
+    ref = outs[8].view(torch.int32)
+    for ks in (4, 2, 1):
+        assert torch.equal(outs[ks].view(torch.int32), ref), f"{od}x{idim} nt={nt}: split {ks} against 8"
+    assert torch.equal(torch.cat(ones).view(torch.int32), ref), f"{od}x{idim} nt={nt}: single tokens"
 
 
 def test_skinny_refusals():
