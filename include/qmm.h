@@ -254,8 +254,9 @@ int qmm_streamk_preferred(int type, int nt, int od, int id);
 int qmm_nt_switch(void);
 
 /* For tests and tuning: force the K split of the small-batch kernel (QMM_KIND_SKINNY)
- * to ks = 1, 2, 4 or 8 waves per workgroup (never more than the super-blocks of a
- * row), or 0 for the default (8).  The kernel sums over a fixed 8-way split, so its
+ * to ks = 1, 2, 4, 8 or 16 waves per workgroup (never more than the super-blocks of
+ * a row), or 0 for the default (8, or 16 on matrices of at most 4096 rows with 32 or
+ * 48 super-blocks per row).  The kernel sums over a fixed 16-way split, so its
  * results are the same bits for every ks; only its speed changes.  Process-wide, for
  * all devices and later calls; not synchronised with calls already enqueued.
  * Returns QMM_OK, or QMM_ERR_ARG for another value.  Host function, no device work. */

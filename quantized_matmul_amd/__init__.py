@@ -178,7 +178,7 @@ def qmm_nt_switch() -> int:
 
 
 def qmm_set_skinny_split(ks: int) -> None:
-    """Force the small-batch kernel's K split (1, 2, 4 or 8 waves; 0 = default).
+    """Force the small-batch kernel's K split (1, 2, 4, 8 or 16 waves; 0 = default).
     Process-wide; the results do not depend on it (tests and tuning)."""
     _check(int(lib().qmm_set_skinny_split(ks)), "qmm_set_skinny_split")
 

@@ -142,7 +142,7 @@ int nt_switch_value()
 
 int launched(hipError_t e) { return e == hipSuccess ? QMM_OK : QMM_ERR_LAUNCH; }
 
-// The small-batch kernel's K split: 100 + KS (KS = 1, 2, 4 or 8 waves per workgroup)
+// The small-batch kernel's K split: 100 + KS (KS = 1, 2, 4, 8 or 16 waves per workgroup)
 // forced, 0 = by shape; set by qmm_set_skinny_split, else read once from
 // QMM_SKINNY_CFG (the same encoding), for tests and tuning sweeps (the results do
 // not depend on it).
@@ -155,7 +155,7 @@ int skinny_cfg_override()
         return cur;
     const char* e = getenv("QMM_SKINNY_CFG");
     int val = e ? atoi(e) : 0;
-    if (val != 101 && val != 102 && val != 104 && val != 108)
+    if (val != 101 && val != 102 && val != 104 && val != 108 && val != 116)
         val = 0;
     int expect = -1;
     __atomic_compare_exchange_n(&g_skinny_cfg, &expect, val, false, __ATOMIC_ACQ_REL, __ATOMIC_ACQUIRE);
@@ -572,7 +572,7 @@ int qmm_nt_switch(void) { return nt_switch_value(); }
 
 int qmm_set_skinny_split(int ks)
 {
-    if (ks != 0 && ks != 1 && ks != 2 && ks != 4 && ks != 8)
+    if (ks != 0 && ks != 1 && ks != 2 && ks != 4 && ks != 8 && ks != 16)
         return QMM_ERR_ARG;
     __atomic_store_n(&g_skinny_cfg, ks ? 100 + ks : 0, __ATOMIC_RELEASE);
     return QMM_OK;

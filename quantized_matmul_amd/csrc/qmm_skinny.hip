@@ -37,7 +37,7 @@
 //    staged and computed.
 //  * A wave takes RT tiles of 16 rows (RT = 1 is launched); their MFMAs share the
 //    activation operand.  The KS waves of a workgroup split K (super-blocks w,
-//    w + KS, ...); the partial sums are kept per virtual wave of an 8-way split and
+//    w + KS, ...); the partial sums are kept per virtual wave of a 16-way split and
 //    added through LDS in a fixed order, so the result does not depend on KS.
 //  * Tokens past nt read the last token (their results are not stored); rows past
 //    od read the last row.
@@ -196,20 +196,20 @@ __device__ __forceinline__ uint32_t sk_vgpr(uint32_t bits)
     return v;
 }
 
-// Workgroup: KS waves (KS = 1, 2, 4 or 8) splitting K, wave w taking super-blocks
+// Workgroup: KS waves (KS = 1, 2, 4, 8 or 16) splitting K, wave w taking super-blocks
 // w, w + KS, ...; all over the same RT*16 rows.  N > 0: every wave has exactly N
 // super-blocks (KS * N == nsb); N = 0: any share.  NTB >= nt tokens are staged
 // (the 16-token tile's other lanes repeat token NTB-1 or nt-1; their results are
 // not stored).
 //
-// The sum does not depend on KS: super-block sb belongs to virtual wave sb % 8 of
-// an 8-way split, each wave keeps one accumulator per virtual wave it covers (8 / KS
-// of them: super-blocks v, v + 8, v + 16, ... in order), and the 8 virtual partial
-// tiles are added in the order 0, 1, .., 7.  So every KS gives the same bits, a
-// token's result does not depend on the other tokens of the call, and KS is chosen
-// per shape and token count for speed alone.  Dynamic LDS: KS stage areas, then the
-// 8 partial tiles.
-constexpr int kSkMaxWaves = 8, kSkVirt = 8;
+// The sum does not depend on KS: super-block sb belongs to virtual wave sb % 16 of
+// a 16-way split, each wave keeps one accumulator per virtual wave it covers (16 /
+// KS of them: super-blocks v, v + 16, v + 32, ... in order), and the 16 virtual
+// partial tiles are added in the order 0, 1, .., 15.  So every KS gives the same
+// bits, a token's result does not depend on the other tokens of the call, and KS is
+// chosen per shape for speed alone.  Dynamic LDS: KS stage areas, then the 16
+// partial tiles.
+constexpr int kSkMaxWaves = 16, kSkVirt = 16;
 
 template <int RT, int NTB, int N, int KS>
 __global__ __launch_bounds__(64 * KS) void mmq_skinny_q4k_kernel(const uint8_t* __restrict__ W,
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(64 * KS) void mmq_skinny_q4k_kernel(const uint8_t* 
     }
     // every wave's virtual partial tiles to LDS (tile v at red[v][r][i][lane]); then
     // wave w adds value e = w, w + KS, ... (value e: row tile e / 4, token slot
-    // 4p + e % 4) over the virtual waves in the order 0, 1, .., 7 and stores it
+    // 4p + e % 4) over the virtual waves in the order 0, 1, .., 15 and stores it
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
         const int v = w + ((rot + j) % NV) * KS;
@@ -383,19 +383,23 @@ hipError_t launch_rkn(const uint8_t* W, const int8_t* q, const float* d, const f
     case 1: return launch_rkk<NTB, 1>(W, q, d, s, nt, od, id, out, st);
     case 2: return launch_rkk<NTB, 2>(W, q, d, s, nt, od, id, out, st);
     case 4: return launch_rkk<NTB, 4>(W, q, d, s, nt, od, id, out, st);
-    default: return launch_rkk<NTB, 8>(W, q, d, s, nt, od, id, out, st);
+    case 8: return launch_rkk<NTB, 8>(W, q, d, s, nt, od, id, out, st);
+    default: return launch_rkk<NTB, 16>(W, q, d, s, nt, od, id, out, st);
     }
 }
 
 }  // namespace
 
-// Waves per workgroup (ks, splitting K; 1, 2, 4 or 8, never more than the
-// super-blocks): 8.  ks does not change the results (see the kernel), so the choice
-// is by speed alone; 8 waves were as fast as 4 or faster at every token count
-// measured on 8192..16384 x 4096 (us, alternating processes: 12288 x 4096 nt = 4
-// 9.2 -> 8.6, nt = 8 10.3 -> 10.0, nt = 16 13.0 -> 12.1; 8192 x 4096 nt = 8 8.1 ->
-// 7.2; 16384 x 4096 nt = 8 12.5 either way).
-// cfg != 0 forces 100 + ks (ks 1, 2, 4 or 8) for tests and tuning.
+// Waves per workgroup (ks, splitting K; 1, 2, 4, 8 or 16, never more than the
+// super-blocks): 8, or 16 on a matrix of at most 256 row tiles with 32 or 48
+// super-blocks per row (2 or 3 per wave; 16 waves of 4 or more would spill).  ks
+// does not change the results (see the kernel), so the choice is by speed alone.
+// Measured (us): 8 waves as fast as 4 or faster at every token count on 8192..16384
+// x 4096 (alternating processes: 12288 x 4096 nt = 4 9.2 -> 8.6, nt = 8 10.3 ->
+// 10.0, nt = 16 13.0 -> 12.1; 8192 x 4096 nt = 8 8.1 -> 7.2); 16 against 8 in one
+// process: 4096 x 12288 nt = 4 9.4 -> 8.7, nt = 8 10.9 -> 9.9, but 12288 x 4096 nt = 4
+// 8.2 -> 9.0, nt = 8 9.6 -> 12.6 (many row tiles) and 4096 x 4096 within 2 %.
+// cfg != 0 forces 100 + ks (ks 1, 2, 4, 8 or 16) for tests and tuning.
 hipError_t launch_skinny(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od, int id,
                          float* out, hipStream_t st, int cfg)
 {
@@ -405,10 +409,11 @@ hipError_t launch_skinny(const uint8_t* W, const int8_t* q, const float* d, cons
     int ks;
     if (cfg) {
         ks = cfg - 100;
-        if (ks != 1 && ks != 2 && ks != 4 && ks != 8)
+        if (ks != 1 && ks != 2 && ks != 4 && ks != 8 && ks != 16)
             return hipErrorInvalidValue;
     } else {
-        ks = kSkMaxWaves;
+        const int grid = (od + 15) / 16;
+        ks = grid <= 256 && (nsb == 32 || nsb == 48) ? 16 : 8;
     }
     while (ks > nsb)
         ks >>= 1;

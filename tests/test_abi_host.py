@@ -60,12 +60,12 @@ def test_act_bytes():
 
 
 def test_set_skinny_split_host():
-    """The small-batch split setting takes 0, 1, 2, 4 and 8 and refuses anything else
-    before touching any state (host only)."""
+    """The small-batch split setting takes 0, 1, 2, 4, 8 and 16 and refuses anything
+    else before touching any state (host only)."""
     try:
-        for ks in (1, 2, 4, 8, 0):
+        for ks in (1, 2, 4, 8, 16, 0):
             qmm.qmm_set_skinny_split(ks)
-        for bad in (3, 5, 16, -1):
+        for bad in (3, 5, 32, -1):
             with pytest.raises(qmm.QmmError):
                 qmm.qmm_set_skinny_split(bad)
     finally:

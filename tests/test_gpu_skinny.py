@@ -89,20 +89,20 @@ def test_skinny_deterministic():
 
 
 @pytest.mark.parametrize("od,idim,nt", [(12288, 4096, 4), (12288, 4096, 8), (12288, 4096, 16), (1000, 2304, 5),
-                                        (500, 768, 3), (4096, 12288, 8), (257, 1024, 12)])
+                                        (500, 768, 3), (4096, 12288, 8), (257, 1024, 12), (4096, 8192, 4)])
 def test_skinny_split_independent(od, idim, nt):
-    """The K split (1, 2, 4 or 8 waves per workgroup, forced through
+    """The K split (1, 2, 4, 8 or 16 waves per workgroup, forced through
     qmm_set_skinny_split; capped by the super-blocks of a row) does not change the
-    bits: 16 super-blocks (straight-line at 8 and 4 waves, the loop at 2 and 1), 9
-    and 3 super-blocks (loop forms, unequal shares), 48 super-blocks (loops with 1,
-    2, 4 and 8 accumulators per wave), 4 super-blocks; and every token row equals
-    that token alone."""
+    bits: 16 super-blocks (straight-line at 16, 8 and 4 waves, the loop at 2 and 1),
+    9 and 3 super-blocks (loop forms, unequal shares), 48 and 32 super-blocks (16
+    waves by default; loops with 2 to 16 accumulators per wave), 4 super-blocks; and
+    every token row equals that token alone."""
     _say(f"skinny split independence {od}x{idim} nt={nt}")
     W = _up(synth.weights(Q4, od, idim, seed=41 + nt))
     q, d, s = qmm.qmm_quantize_act(_up(synth.activations(nt, idim, seed=42 + od)))
     outs = {}
     try:
-        for ks in (8, 4, 2, 1):
+        for ks in (8, 16, 4, 2, 1):
             qmm.qmm_set_skinny_split(ks)
             outs[ks] = qmm.qmm_matmul_q8_kind(K7, Q4, W, q, d, s, od)
             torch.cuda.synchronize()
@@ -113,7 +113,7 @@ def test_skinny_split_independent(od, idim, nt):
     finally:
         qmm.qmm_set_skinny_split(0)
     ref = outs[8].view(torch.int32)
-    for ks in (4, 2, 1):
+    for ks in (16, 4, 2, 1):
         assert torch.equal(outs[ks].view(torch.int32), ref), f"{od}x{idim} nt={nt}: split {ks} against 8"
     assert torch.equal(torch.cat(ones).view(torch.int32), ref), f"{od}x{idim} nt={nt}: single tokens"
 
