@@ -209,7 +209,7 @@ __device__ __forceinline__ uint32_t sk_vgpr(uint32_t bits)
 // bits, a token's result does not depend on the other tokens of the call, and KS is
 // chosen per shape for speed alone.  Dynamic LDS: KS stage areas, then the 16
 // partial tiles.
-constexpr int kSkVirt = 16;   // the virtual split; KS divides it
+constexpr int kSkMaxWaves = 16, kSkVirt = 16;
 
 template <int RT, int NTB, int N, int KS>
 __global__ __launch_bounds__(64 * KS) void mmq_skinny_q4k_kernel(const uint8_t* __restrict__ W,
