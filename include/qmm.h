@@ -107,11 +107,12 @@ enum {
     QMM_KIND_MMQ_WAVE32X64 = 6,     /* Q4_K only: 128 x 64, 4 waves of 32 rows x 64 tokens,
                                        weights straight into registers (the default Q4_K
                                        matrix kernel) */
-    QMM_KIND_SKINNY = 7             /* Q4_K only, nt <= 16 (else QMM_ERR_ARG): 16 x 16 x 32
+    QMM_KIND_SKINNY = 7             /* Q4_K only; up to 16 tokens per launch, more as
+                                       launches on token slices of 16: 16 x 16 x 32
                                        int8 MFMA tiles of 16 weight rows x 16 tokens, the
                                        weights streamed once for all tokens ([MMQ, section
                                        12.2]: token count in registers; per-32 rescale as
-                                       MMQ); qmm_matmul's kernel for Q4_K at 3..16 tokens
+                                       MMQ); qmm_matmul's kernel for Q4_K at 3..48 tokens
                                        (by shape) */
 };
 
@@ -222,8 +223,10 @@ int qmm_mmq_tile(int nt, int od, int id);
 
 /* Which kernel qmm_matmul would run for this call.  With the default switch (8):
  * QMM_KIND_SKINNY for Q4_K on 9..16 tokens of any matrix, on 3..8 tokens of a matrix
- * of at least 3072 rows, on 5..8 tokens of at least 2048 rows, and on 6..8 tokens of
- * at least 1024 rows of at most 4096 columns; otherwise QMM_KIND_MMVQ for nt <= 8 and for 9..16
+ * of at least 3072 rows, on 5..8 tokens of at least 2048 rows, on 6..8 tokens of at
+ * least 1024 rows of at most 4096 columns, on 17..32 tokens of at most 12288 rows and
+ * on 33..48 tokens of at most 8192 rows and 4096 columns (token slices of 16);
+ * otherwise QMM_KIND_MMVQ for nt <= 8 and for 9..16
  * tokens on od <= 4096 rows (as launches on slices of 8 tokens: the MMQ tile grid
  * of such a matrix fills at most a quarter of the GPU); QMM_KIND_MMQ beyond.  With
  * another switch: QMM_KIND_MMVQ for nt <= the switch, QMM_KIND_MMQ above.  A

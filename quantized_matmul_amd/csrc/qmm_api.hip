@@ -171,15 +171,23 @@ int skinny_cfg_override()
 // 8.5 / 7.6, nt = 5: 9.0 / 10.4; 1024 x 4096 nt = 5: 4.1 / 4.0, nt = 6: 4.1 / 4.3,
 // nt = 8: 4.3 / 4.9; 1024 x 12288 nt = 8: 10.1 / 7.6; 12288 x 4096 nt = 8: 10.0 /
 // 16.8; at 2 tokens within a few per cent either way, so MMVQ; 9..16 tokens: 6-15 us
-// against 21-58 for MMQ); MMVQ up to the switch otherwise; other types also on
+// against 21-58 for MMQ); on 17..32 tokens of at most 12288 rows and on 33..48
+// tokens of at most 8192 rows and 4096 columns, as launches on token slices of 16
+// (the MMQ tile grids of these calls fill a fraction of the GPU; us, slices against
+// per-tile MMQ and stream-K: 4096 x 4096 nt = 32 10.4 / 22.0 / 20.6, 12288 x 4096
+// nt = 32 22.0 / 24.7 / 29.1, 4096 x 12288 nt = 32 25.3 / 59.6 / 28.4, 8192 x 4096
+// nt = 48 24.1 / 24.3 / 24.0; 14336 x 4096 nt = 32 27.1 / 24.6, 4096 x 12288 nt = 40
+// 34.4 / 28.7 (stream-K)); MMVQ up to the switch otherwise; other types also on
 // 9..16 tokens of a matrix of at most 4096 rows, as launches on token slices of 8
 // (such a matrix gives MMQ at most 64 tiles of 64 rows, a quarter of the 256 CUs;
 // 4096 x 4096: MMQ 22 us, two MMVQ launches 13.7-14.7 us); MMQ beyond.
 int dispatch_kind(int type, int nt, int od, int id)
 {
     const int sw = nt_switch_value();
-    if (sw == 8 && type == QMM_TYPE_Q4_K && nt <= 16 &&
-        (nt >= 9 || (nt >= 3 && od >= 3072) || (nt >= 5 && od >= 2048) || (nt >= 6 && od >= 1024 && id <= 4096)))
+    if (sw == 8 && type == QMM_TYPE_Q4_K &&
+        ((nt <= 16 &&
+          (nt >= 9 || (nt >= 3 && od >= 3072) || (nt >= 5 && od >= 2048) || (nt >= 6 && od >= 1024 && id <= 4096))) ||
+         (nt >= 17 && nt <= 32 && od <= 12288) || (nt >= 33 && nt <= 48 && od <= 8192 && id <= 4096)))
         return QMM_KIND_SKINNY;
     if (nt <= sw || (sw == 8 && nt <= 16 && od <= 4096))
         return QMM_KIND_MMVQ;
@@ -223,9 +231,19 @@ int matmul_q8_checked(int kind, int type, const void* W, const int8_t* q, const 
     if (kind == QMM_KIND_SKINNY) {
         if (type != QMM_TYPE_Q4_K)
             return QMM_ERR_TYPE;
-        if (nt > 16 || S)
-            return QMM_ERR_ARG;
-        return launched(qmm::launch_skinny(w, q, d, s, nt, od, id, out, st, skinny_cfg_override()));
+        if (S)
+            return QMM_ERR_ARG;  // no integer dump from this kernel
+        // up to 16 tokens per launch; more as token slices of 16 (rows t0.. of q, d,
+        // s and out), each a complete call on its own
+        const size_t nblk = (size_t)id / 32;
+        for (int t0 = 0; t0 < nt; t0 += 16) {
+            const int rc = launched(qmm::launch_skinny(w, q + (size_t)t0 * id, d + (size_t)t0 * nblk,
+                                                       s + (size_t)t0 * nblk, min(16, nt - t0), od, id,
+                                                       out + (size_t)t0 * od, st, skinny_cfg_override()));
+            if (rc)
+                return rc;
+        }
+        return QMM_OK;
     }
     if (kind == QMM_KIND_MMVQ) {
         if (nt <= 8)
@@ -628,8 +646,6 @@ int qmm_matmul_q8_kind(int kind, int type, const void* W, const int8_t* q, const
         return QMM_ERR_ARG;
     if ((kind == QMM_KIND_MMQ_WAVE32X64 || kind == QMM_KIND_SKINNY) && type != QMM_TYPE_Q4_K)
         return QMM_ERR_TYPE;
-    if (kind == QMM_KIND_SKINNY && nt > 16)
-        return QMM_ERR_ARG;
     int rc = validate_q8(type, W, q, d, s, nt, od, id, out);
     if (rc)
         return rc;

@@ -77,22 +77,26 @@ def test_dispatch_kind_host():
     Q4, Q6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K
     # Q4_K: the small-batch kernel on 9..16 tokens of any matrix, on 3..8 tokens from
     # 3072 rows, on 5..8 tokens from 2048 rows, on 6..8 tokens from 1024 rows of at
-    # most 4096 columns; MMVQ otherwise
-    for nt in range(1, 17):
-        for od in (1024, 2048, 3072, 4096, 12288):
+    # most 4096 columns, on 17..32 tokens up to 12288 rows, on 33..48 tokens up to
+    # 8192 rows of at most 4096 columns; MMVQ otherwise up to 8 tokens (and 9..16 when
+    # the switch is moved), MMQ beyond
+    def want(nt, od, idim):
+        sk = ((nt <= 16 and (nt >= 9 or (nt >= 3 and od >= 3072) or (nt >= 5 and od >= 2048) or
+                             (nt >= 6 and od >= 1024 and idim <= 4096))) or
+              (17 <= nt <= 32 and od <= 12288) or (33 <= nt <= 48 and od <= 8192 and idim <= 4096))
+        return qmm.QMM_KIND_SKINNY if sk else qmm.QMM_KIND_MMVQ if nt <= 8 else qmm.QMM_KIND_MMQ
+
+    for nt in range(1, 65):
+        for od in (64, 1023, 1024, 2048, 3072, 4096, 8192, 12288, 12544, 14336):
             for idim in (4096, 12288):
-                sk = (nt >= 9 or (nt >= 3 and od >= 3072) or (nt >= 5 and od >= 2048) or
-                      (nt >= 6 and od >= 1024 and idim <= 4096))
-                want = qmm.QMM_KIND_SKINNY if sk else qmm.QMM_KIND_MMVQ
-                assert qmm.qmm_dispatch_kind(Q4, nt, od, idim) == want, (nt, od, idim)
+                assert qmm.qmm_dispatch_kind(Q4, nt, od, idim) == want(nt, od, idim), (nt, od, idim)
         assert qmm.qmm_dispatch_kind(Q4, 3, 3072, 3072) == qmm.QMM_KIND_SKINNY
         assert qmm.qmm_dispatch_kind(Q4, 3, 3071, 4096) == qmm.QMM_KIND_MMVQ
         assert qmm.qmm_dispatch_kind(Q4, 6, 1023, 4096) == qmm.QMM_KIND_MMVQ
         assert qmm.qmm_dispatch_kind(Q4, 6, 1024, 4352) == qmm.QMM_KIND_MMVQ
-        want = qmm.QMM_KIND_SKINNY if nt >= 9 else qmm.QMM_KIND_MMVQ
-        assert qmm.qmm_dispatch_kind(Q4, nt, 1023, 4096) == want
-        assert qmm.qmm_dispatch_kind(Q4, nt, 64, 12288) == want
-    assert qmm.qmm_dispatch_kind(Q4, 17, 4096, 4096) == qmm.QMM_KIND_MMQ
+    assert qmm.qmm_dispatch_kind(Q4, 17, 4096, 4096) == qmm.QMM_KIND_SKINNY
+    assert qmm.qmm_dispatch_kind(Q4, 33, 4096, 12288) == qmm.QMM_KIND_MMQ
+    assert qmm.qmm_dispatch_kind(Q4, 49, 4096, 4096) == qmm.QMM_KIND_MMQ
     # other types: MMVQ up to 8 tokens; 9..16 tokens on token slices of 8 up to 4096
     # rows, MMQ above
     for nt in range(1, 9):
@@ -114,7 +118,8 @@ def test_streamk_preferred_host():
     Q4, Q6, P6 = qmm.QMM_TYPE_Q4_K, qmm.QMM_TYPE_Q6_K, qmm.QMM_TYPE_Q6_K_P224
     sp = qmm.qmm_streamk_preferred
     for qt in (Q4, Q6, P6):
-        assert sp(qt, 17, 4096, 12288)               # 48 super-blocks, 32 tiles
+        assert sp(qt, 33, 4096, 12288)               # 48 super-blocks, 32 tiles
+        assert sp(qt, 17, 4096, 12288) == (qt != Q4)  # the same (Q4_K: small-batch slices)
         assert sp(qt, 448, 4096, 8192)                # 32 super-blocks, 224 tiles
         assert not sp(qt, 256, 4096, 12288)           # 128 tiles: the per-tile split fills one round
         assert not sp(qt, 512, 4096, 12288)           # 256 tiles: one whole round
@@ -159,10 +164,10 @@ def test_validation_before_device_work():
     assert L.qmm_matmul_q8_kind(0, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_ARG
     assert L.qmm_matmul_q8_kind(8, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_ARG
     # the 32 x 64 per-wave kernel and the small-batch kernel exist for Q4_K only; the
-    # small-batch kernel takes at most 16 tokens
+    # small-batch kernel takes any nt (slices of 16 tokens above 16): validation passes
     assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_WAVE32X64, 2, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_TYPE
     assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_SKINNY, 2, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_TYPE
-    assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_SKINNY, 1, p, p, p, p, 17, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_SKINNY, 1, p, p, p, p, 17, 4, 256, p, None) == qmm.QMM_ERR_DEVICE
     assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_SKINNY, 1, p, p, p, p, 16, 4, 256, p, None) == qmm.QMM_ERR_DEVICE
     # the MMQ tile kinds pass validation; without a GPU the device check answers
     assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_64X64_SPLITK, 1, p, p, p, p, 1, 4, 256, p, None) == \

@@ -165,22 +165,26 @@ def test_mmq_every_tile_shape(qtype, nt, od, idim):
 
 def test_dispatch_boundary():
     """On a small matrix: nt = 8 runs MMVQ; nt = 9..16 run the small-batch kernel
-    (Q4_K) or MMVQ on token slices of 8 (Q6_K); nt = 17 runs MMQ.  Every call
-    matches the oracle; the Q6_K sliced call gives the same bits as its slices
-    called alone, and a Q4_K small-batch call the same bits as the small-batch
-    kernel on its tokens alone."""
+    (Q4_K) or MMVQ on token slices of 8 (Q6_K); Q4_K at 17..48 tokens the
+    small-batch kernel on token slices of 16; nt = 49 (Q4_K) and 17 (Q6_K) run MMQ.
+    Every call matches the oracle; the Q6_K sliced call gives the same bits as its
+    slices called alone, and a Q4_K small-batch call the same bits as the
+    small-batch kernel on its tokens alone."""
     assert qmm.qmm_dispatch_kind(Q4, 8, 64, 512) == qmm.QMM_KIND_MMVQ
     assert qmm.qmm_dispatch_kind(Q4, 9, 64, 512) == qmm.QMM_KIND_SKINNY
     assert qmm.qmm_dispatch_kind(Q4, 16, 64, 512) == qmm.QMM_KIND_SKINNY
-    assert qmm.qmm_dispatch_kind(Q4, 17, 64, 512) == qmm.QMM_KIND_MMQ
+    assert qmm.qmm_dispatch_kind(Q4, 17, 64, 512) == qmm.QMM_KIND_SKINNY
+    assert qmm.qmm_dispatch_kind(Q4, 48, 64, 512) == qmm.QMM_KIND_SKINNY
+    assert qmm.qmm_dispatch_kind(Q4, 49, 64, 512) == qmm.QMM_KIND_MMQ
     assert qmm.qmm_dispatch_kind(Q6, 9, 64, 512) == qmm.QMM_KIND_MMVQ
+    assert qmm.qmm_dispatch_kind(Q6, 17, 64, 512) == qmm.QMM_KIND_MMQ
     od, idim = 96, 1024
     for qtype in (Q4, Q6):
         W = synth.weights(qtype, od, idim, seed=5)
-        x = synth.activations(17, idim, seed=5)
+        x = synth.activations(49, idim, seed=5)
         ref, mag, _ = oracle.matmul(qtype, W, x, od)
         Wt = _up(W)
-        for nt in (8, 9, 13, 16, 17):
+        for nt in (8, 9, 13, 16, 17, 33, 48, 49):
             o = qmm.qmm_matmul(qtype, Wt, _up(x[:nt]), od)
             torch.cuda.synchronize()
             assert_close(o.cpu().numpy(), ref[:nt], mag[:nt], qtype, idim, f"nt={nt}")

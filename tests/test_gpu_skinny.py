@@ -1,13 +1,14 @@
 """GPU parity of the small-batch Q4_K kernel (QMM_KIND_SKINNY: 16 x 16 x 32 int8
-MFMA tiles, 1..16 tokens) against the CPU oracle through the C ABI.
+MFMA tiles, 1..16 tokens per launch) against the CPU oracle through the C ABI.
 
 Outputs within the f32 tolerance of tests/_parity.py, elementwise: every output on
 shapes with ragged row tiles (od not a multiple of 16 or 32), odd super-block
 counts (1, 3, 9, 18: the waves splitting K then get unequal shares or none) and
 every token count 1..16 (padding lanes of the 16-token tile); matrices of more than
-256 row tiles with K split over 1 to 6 waves (straight-line and loop forms, 4, 8
+256 row tiles with K split over 1 to 8 waves (straight-line and loop forms, 4, 8
 and 16 token slots, a last row tile of 8 rows); sampled outputs at the decode layer
-shapes; and the refusals (more than 16 tokens, other weight types).
+shapes; more than 16 tokens as token slices of 16; and the refusal of other weight
+types.
 """
 from __future__ import annotations
 
@@ -39,10 +40,13 @@ CASES = [(nt, od, idim) for nt in (1, 2, 3, 4, 5, 7, 8, 9, 12, 13, 16)
          for od, idim in ((1, 256), (7, 768), (33, 4608), (100, 2304), (257, 1024))]
 # larger matrices (with the waves splitting K that the launch rule gives): 5480 x 256
 # (1, the last row tile holds 8 rows), 5480 x 512 (2), 6000 x 1024 (4), 9000 x 768
-# (3), 8200 x 2304 (4, 9 super-blocks: the loop form), 7000 x 12288 (6, 8
-# super-blocks per wave: the loop form)
+# (2, 3 super-blocks: the loop form, unequal shares), 8200 x 2304 (8, 9
+# super-blocks: the loop form), 7000 x 12288 (8, 6 super-blocks per wave: the loop
+# form)
 CASES += [(1, 5480, 256), (4, 5480, 512), (8, 6000, 1024), (16, 9000, 768), (5, 8200, 2304),
           (3, 7000, 12288), (12, 5480, 512), (7, 9000, 768)]
+# more than 16 tokens: launches on token slices of 16 (ragged last slice)
+CASES += [(17, 33, 4608), (24, 257, 1024), (33, 100, 2304), (48, 7, 768), (40, 5480, 512)]
 
 
 @pytest.mark.parametrize("nt,od,idim", CASES)
@@ -118,11 +122,23 @@ def test_skinny_split_independent(od, idim, nt):
     assert torch.equal(torch.cat(ones).view(torch.int32), ref), f"{od}x{idim} nt={nt}: single tokens"
 
 
+@pytest.mark.parametrize("od,idim,nt", [(4096, 4096, 40), (12288, 4096, 32), (4096, 12288, 24)])
+def test_skinny_slices_match_single_tokens(od, idim, nt):
+    """qmm_matmul_q8 on 17..48 tokens takes the small-batch kernel on token slices of
+    16 (the dispatcher's choice here); every token row equals that token alone."""
+    _say(f"skinny slices {od}x{idim} nt={nt}")
+    assert qmm.qmm_dispatch_kind(Q4, nt, od, idim) == K7
+    W = _up(synth.weights(Q4, od, idim, seed=51))
+    q, d, s = qmm.qmm_quantize_act(_up(synth.activations(nt, idim, seed=52)))
+    whole = qmm.qmm_matmul_q8(Q4, W, q, d, s, od)
+    ones = [qmm.qmm_matmul_q8_kind(K7, Q4, W, q[t:t + 1].contiguous(), d[t:t + 1].contiguous(),
+                                   s[t:t + 1].contiguous(), od) for t in range(nt)]
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(torch.int32), torch.cat(ones).view(torch.int32))
+
+
 def test_skinny_refusals():
-    W = _up(synth.weights(Q4, 16, 256, seed=3))
-    q, d, s = qmm.qmm_quantize_act(_up(synth.activations(17, 256, seed=4)))
-    with pytest.raises(qmm.QmmError):
-        qmm.qmm_matmul_q8_kind(K7, Q4, W, q, d, s, 16)
     W6 = _up(synth.weights(Q6, 16, 256, seed=5))
+    q, d, s = qmm.qmm_quantize_act(_up(synth.activations(17, 256, seed=4)))
     with pytest.raises(qmm.QmmError):
         qmm.qmm_matmul_q8_kind(K7, Q6, W6, q[:4], d[:32], s[:32], 16)
