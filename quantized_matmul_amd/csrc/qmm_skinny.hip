@@ -209,7 +209,7 @@ __device__ __forceinline__ uint32_t sk_vgpr(uint32_t bits)
 // bits, a token's result does not depend on the other tokens of the call, and KS is
 // chosen per shape for speed alone.  Dynamic LDS: KS stage areas, then the 16
 // partial tiles.
-constexpr int kSkMaxWaves = 16, kSkVirt = 16;
+constexpr int kSkVirt = 16;   // the virtual split (KS divides it)
 
 template <int RT, int NTB, int N, int KS>
 __global__ __launch_bounds__(64 * KS) void mmq_skinny_q4k_kernel(const uint8_t* __restrict__ W,
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(64 * KS) void mmq_skinny_q4k_kernel(const uint8_t* 
     const v4i magic = {mg, mg, mg, mg};
     SkStage<RT, NTB>& my = stage[w];
 
-    // acc[j]: virtual wave w + j * KS (super-blocks w + j * KS, + 8, + 16, ...)
+    // acc[j]: virtual wave w + j * KS (super-blocks w + j * KS, + 16, + 32, ...)
     v4f acc[NV][RT];
 #pragma unroll
     for (int j = 0; j < NV; ++j)
