@@ -107,13 +107,18 @@ enum {
     QMM_KIND_MMQ_WAVE32X64 = 6,     /* Q4_K only: 128 x 64, 4 waves of 32 rows x 64 tokens,
                                        weights straight into registers (the default Q4_K
                                        matrix kernel) */
-    QMM_KIND_SKINNY = 7             /* Q4_K only; up to 16 tokens per launch, more as
+    QMM_KIND_SKINNY = 7,            /* Q4_K only; up to 16 tokens per launch, more as
                                        launches on token slices of 16: 16 x 16 x 32
                                        int8 MFMA tiles of 16 weight rows x 16 tokens, the
                                        weights streamed once for all tokens ([MMQ, section
                                        12.2]: token count in registers; per-32 rescale as
                                        MMQ); qmm_matmul's kernel for Q4_K at 3..48 tokens
                                        (by shape) */
+    QMM_KIND_MMQ_WAVE32X64_SPLITK = 8 /* Q4_K on Q8_K activations only
+                                         (qmm_matmul_q8k_kind): 128 x 64, 8 waves in two
+                                         groups of 4 (32 rows x 64 tokens each) taking
+                                         alternate super-blocks, partial tiles added in
+                                         group order */
 };
 
 /* Bytes of a [od][id] weight matrix of `type`: od*(id/256)*144 (Q4_K, Q4_0), *176
@@ -295,8 +300,18 @@ int qmm_matmul_q8k(int type, const void* W, const int8_t* q, const float* d, con
 /* qmm_matmul_q8k with the tile shape chosen by the caller: kind = QMM_KIND_MMQ
  * (the rule of qmm_q8k_tile), QMM_KIND_MMQ_128X64, QMM_KIND_MMQ_64X64 or
  * QMM_KIND_MMQ_64X64_SPLITK (two groups of waves take alternate super-blocks and
- * add their partial tiles in group order at the end).  For tests and measurement.
- * Other kinds: QMM_ERR_ARG; other rules as qmm_matmul_q8k. */
+ * add their partial tiles in group order at the end), and for Q4_K only
+ * (QMM_ERR_TYPE otherwise) QMM_KIND_MMQ_WAVE32X64 or QMM_KIND_MMQ_WAVE32X64_SPLITK:
+ * 4 waves of 32 rows x 64 tokens per 128 x 64 tile, each sub-block scale split as
+ * sc = 8a + b with a, b <= 7 and carried inside the int8 weight operand (a q and
+ * b q are at most 105), so two int32 accumulators chained over the super-block
+ * give sum_j sc_j * sum(q * qx) = 8 Ca + Cb exactly ([GEMM, "Activations: int8
+ * with a scale per 256"]: one activation scale per super-block makes that sum a
+ * single integer).  Same results bit for bit as QMM_KIND_MMQ_128X64 and
+ * QMM_KIND_MMQ_64X64_SPLITK respectively.  qmm_matmul_q8k runs the unsplit one for
+ * Q4_K where the rule picks 128 x 64 tiles and there are more than 256 of them.
+ * For tests and measurement.  Other kinds: QMM_ERR_ARG; other rules as
+ * qmm_matmul_q8k. */
 int qmm_matmul_q8k_kind(int kind, int type, const void* W, const int8_t* q, const float* d, const float* bsum,
                         int nt, int od, int id, float* out, void* stream);
 
@@ -309,7 +324,9 @@ int qmm_q8k_tile(int nt, int od, int id);
 /* Diagnostic: the integer stage of qmm_matmul_q8k alone.  S [nt][od][id/256][2]
  * int32: S[..][0] = sum_j sc_j * sum(q * qx), S[..][1] = sum_j m_j * (bsum_2j +
  * bsum_2j+1) (Q4_K, Q5_K); S[..][0] = sum_g sc_g * sum((q6 - 32) * qx), S[..][1] =
- * 0 (Q6_K), computed by the kernel's code.  Arguments as qmm_matmul_q8k. */
+ * 0 (Q6_K), computed by the code of the kernel qmm_matmul_q8k takes for the shape
+ * (for Q4_K with more than 256 tiles of 128 x 64: the wave kernel's 8 Ca + Cb).
+ * Arguments as qmm_matmul_q8k. */
 int qmm_q8k_superblock_sums(int type, const void* W, const int8_t* q, const float* d, const float* bsum,
                             int nt, int od, int id, int32_t* S, void* stream);
 

@@ -32,6 +32,7 @@ QMM_KIND_MMQ_128X64 = 3
 QMM_KIND_MMQ_64X64 = 4
 QMM_KIND_MMQ_64X64_SPLITK = 5
 QMM_KIND_MMQ_WAVE32X64 = 6
+QMM_KIND_MMQ_WAVE32X64_SPLITK = 8
 QMM_KIND_SKINNY = 7
 QMM_OK = 0
 QMM_ERR_ARG = -1

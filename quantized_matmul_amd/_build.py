@@ -10,7 +10,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqmm.so")
 SOURCES = ["qmm_api.hip", "qmm_quantize.hip", "qmm_fused.hip", "qmm_mmvq.hip", "qmm_mmq.hip", "qmm_mmq2.hip",
-           "qmm_mmq_q8k.hip", "qmm_skinny.hip"]
+           "qmm_mmq_q8k.hip", "qmm_mmq_q8k2.hip", "qmm_skinny.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

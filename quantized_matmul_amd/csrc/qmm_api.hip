@@ -518,11 +518,14 @@ int qmm_matmul_q8k(int type, const void* W, const int8_t* q, const float* d, con
 int qmm_matmul_q8k_kind(int kind, int type, const void* W, const int8_t* q, const float* d, const float* bsum,
                         int nt, int od, int id, float* out, void* stream)
 {
-    if (kind != QMM_KIND_MMQ && (kind < QMM_KIND_MMQ_128X64 || kind > QMM_KIND_MMQ_64X64_SPLITK))
+    const bool wave = kind == QMM_KIND_MMQ_WAVE32X64 || kind == QMM_KIND_MMQ_WAVE32X64_SPLITK;
+    if (kind != QMM_KIND_MMQ && !wave && (kind < QMM_KIND_MMQ_128X64 || kind > QMM_KIND_MMQ_64X64_SPLITK))
         return QMM_ERR_ARG;
     if (!out)
         return QMM_ERR_ARG;
-    const int tile = kind == QMM_KIND_MMQ ? 0 : kind - QMM_KIND_MMQ_128X64 + 1;
+    if (wave && type != QMM_TYPE_Q4_K)
+        return QMM_ERR_TYPE;
+    const int tile = kind == QMM_KIND_MMQ ? 0 : kind == QMM_KIND_MMQ_WAVE32X64_SPLITK ? 5 : kind - QMM_KIND_MMQ_128X64 + 1;
     return q8k_checked(type, W, q, d, bsum, nt, od, id, out, nullptr, stream, tile);
 }
 

@@ -49,11 +49,17 @@ hipError_t launch_mmq_streamk(int type, const uint8_t* W, const int8_t* q, const
 // (id % 256 == 0), and the Q4_K / Q6_K matmul on them (qmm_mmq_q8k.hip; type 1
 // Q4_K, 2 Q6_K, 3 Q6_K padded).  S != null: the integer stage only, S
 // [nt][od][id/256][2] int32.  tile: 0 = q8k_tile_choice, else 1 = 128 x 64, 2 =
-// 64 x 64, 3 = 64 x 64 split over K.
+// 64 x 64, 3 = 64 x 64 split over K, 4 = Q4_K on launch_mmq_k4_q8k_v2.
 hipError_t launch_quantize_q8k(const float* x, int nt, int id, int8_t* q, float* d, float* bsum, hipStream_t st);
 int q8k_tile_choice(int nt, int od, int id);
 hipError_t launch_mmq_q8k(int type, const uint8_t* W, const int8_t* q, const float* d, const float* bsum, int nt,
                           int od, int id, float* out, int32_t* S, hipStream_t st, int tile);
+// Q4_K on Q8_K activations, 4 waves x (32 rows x 64 tokens) per workgroup, the
+// sub-block scales inside the int8 operands (qmm_mmq_q8k2.hip); S != null writes
+// the integer stage instead (S [nt][od][nsb][2]).  ks = 2: 8 waves in two groups
+// splitting K.
+hipError_t launch_mmq_k4_q8k_v2(const uint8_t* W, const int8_t* q, const float* d, const float* bsum, int nt, int od,
+                                int id, float* out, int32_t* S, hipStream_t st, int ks);
 
 // Producer-side steps that feed the quantizer (qmm_fused.hip).  Rows are [nt][id]
 // f32, id % 32 == 0; q/d/s as for launch_quantize.  With q == null the kernels

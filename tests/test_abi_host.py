@@ -241,8 +241,13 @@ def test_q8k_validation():
     assert L.qmm_matmul_q8k(3, ctypes.c_void_p((1 << 20) + 2), p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_ALIGN
     for kind in (qmm.QMM_KIND_MMQ, qmm.QMM_KIND_MMQ_128X64, qmm.QMM_KIND_MMQ_64X64, qmm.QMM_KIND_MMQ_64X64_SPLITK):
         assert L.qmm_matmul_q8k_kind(kind, 2, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_DEVICE
-    for kind in (0, qmm.QMM_KIND_MMVQ, 6):
+    for kind in (0, qmm.QMM_KIND_MMVQ, qmm.QMM_KIND_SKINNY, 9):
         assert L.qmm_matmul_q8k_kind(kind, 2, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    # the wave kernels with the scales in the int8 operand exist for Q4_K only
+    for kind in (qmm.QMM_KIND_MMQ_WAVE32X64, qmm.QMM_KIND_MMQ_WAVE32X64_SPLITK):
+        assert L.qmm_matmul_q8k_kind(kind, 1, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_DEVICE
+        for t in (2, 3, 6):
+            assert L.qmm_matmul_q8k_kind(kind, t, p, p, p, p, 9, 4, 256, p, None) == qmm.QMM_ERR_TYPE
     # the tile rule: fewest rounds x super-blocks per wave, ties to the larger tile
     assert qmm.qmm_q8k_tile(512, 12288, 4096) == qmm.QMM_KIND_MMQ_128X64
     assert qmm.qmm_q8k_tile(512, 4096, 12288) == qmm.QMM_KIND_MMQ_128X64

@@ -190,6 +190,48 @@ def test_matmul_q8k_every_tile(qtype, kind, nt, od, idim):
     _say(f"  worst err/tol {worst:.3f}, max rel {rel:.2e}")
 
 
+WKINDS = [(kind, base) + c
+          for kind, base in ((qmm.QMM_KIND_MMQ_WAVE32X64, qmm.QMM_KIND_MMQ_128X64),
+                             (qmm.QMM_KIND_MMQ_WAVE32X64_SPLITK, qmm.QMM_KIND_MMQ_64X64_SPLITK))
+          for c in KIND_SHAPES + [(64, 384, 3328), (130, 1000, 512)]]
+
+
+@pytest.mark.parametrize("kind,base,nt,od,idim", WKINDS, ids=[f"k{k}-{a}x{b}x{c}" for k, _, a, b, c in WKINDS])
+def test_matmul_q8k_wave_kernels(kind, base, nt, od, idim):
+    """Q4_K on the wave kernels with the sub-block scales in the int8 operand (and
+    their split over K): against the oracle, and bit for bit against the staged
+    kernel of the same summation order (128 x 64, or the 64 x 64 split)."""
+    _say(f"matmul_q8k wave kind={kind} nt={nt} od={od} id={idim}")
+    Wd, W, ot = _weights(Q4, od, idim, seed=2400 + od + kind)
+    x = synth.activations(nt, idim, seed=2500 + nt, outlier_frac=0.01)
+    q, d, bs = _quant(x)
+    out = qmm.qmm_matmul_q8k_kind(kind, Q4, Wd, q, d, bs, od)
+    ref_same = qmm.qmm_matmul_q8k_kind(base, Q4, Wd, q, d, bs, od)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), ref_same.view(torch.int32))
+    oq, od_, obs = oracle_activations(oracle.quantize_q8k, x, (q, d, bs), "quantize_q8k")
+    ref, mag = oracle.matmul_q8k(ot, W, oq, od_, obs, od)
+    worst, rel = assert_close(out.cpu().numpy(), ref, mag, ot, idim, f"wave kind {kind} {nt}x{od}x{idim}")
+    _say(f"  worst err/tol {worst:.3f}, max rel {rel:.2e}")
+
+
+def test_q8k_wave_integer_stage_bit_exact():
+    """The integer stage of the wave kernel (S1 = 8 Ca + Cb from the two chained
+    accumulators, and S2): qmm_q8k_superblock_sums takes it where qmm_matmul_q8k
+    does (Q4_K, more than 256 tiles of 128 x 64); ragged rows and tokens, three
+    super-blocks (the two-per-trip loop with an odd count)."""
+    nt, od, idim = 50, 33243, 768
+    _say(f"q8k wave integer stage nt={nt} od={od} id={idim}")
+    Wd, W, ot = _weights(Q4, od, idim, seed=2600)
+    x = synth.activations(nt, idim, seed=2700, outlier_frac=0.01)
+    q, d, bs = _quant(x)
+    S = qmm.qmm_q8k_superblock_sums(Q4, Wd, q, d, bs, od)
+    torch.cuda.synchronize()
+    oq, od_, obs = oracle_activations(oracle.quantize_q8k, x, (q, d, bs), "quantize_q8k")
+    ref = oracle.q8k_superblock_sums(ot, W, oq, obs, od)
+    _same(S.cpu().numpy(), ref, "wave integer stage")
+
+
 def test_matmul_q8k_split_full_size_sampled():
     """The split tile on the long-K shape it is chosen for (padded Q6_K 4096 x 12288
     at 256 tokens; Q4_K 4096 x 4096 at 256), sampled against the oracle."""
