@@ -1004,12 +1004,18 @@ def main():
                     value=round(ops / t8 / 1e12, 2), unit="TOP/s")
         m = max(q8, key=lambda c: float(np.mean(c.k_ms)))
         km = float(np.mean(m.k_ms)) * 1e-3
-        wr, wc, ks = MMQ_TILES[qmm.qmm_q8k_tile(m.nt, m.od, m.idim)]
-        kname = f"qmm::mmq_k4_q8k_kernel<{wr}, {wc}, {ks}, false, false>"
-        tiles = -(-m.nt // (32 * wc)) * -(-m.od // (32 * wr))
+        t128 = -(-m.nt // 64) * -(-m.od // 128)
+        if m.qtype == qmm.QMM_TYPE_Q4_K and t128 > 256:
+            # the wave kernel with the scales in the int8 operand (4 waves per 128 x 64 tile)
+            kname, threads = "qmm::{anonymous}::mmq_k4_q8k_v2_kernel<1, false>", 8 * -(-t128 // 8) * 256
+        else:
+            wr, wc, ks = MMQ_TILES[qmm.qmm_q8k_tile(m.nt, m.od, m.idim)]
+            kname = f"qmm::mmq_k4_q8k_kernel<{wr}, {wc}, {ks}, false, false>"
+            tiles = -(-m.nt // (32 * wc)) * -(-m.od // (32 * wr))
+            threads = 8 * -(-tiles // 8) * 64 * wr * wc * ks
         line["roofline"] = {"bound": "mfma", "achieved": round(m.ops / km / 1e12, 2), "peak": INT8_PEAK_TOPS,
-                            "unit": "TFLOP/s", "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4),
-                            "traffic": read_traffic(Q8K_COUNTERS, kname, 8 * -(-tiles // 8) * 64 * wr * wc * ks),
+                            "unit": "TOP/s", "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4),
+                            "traffic": read_traffic(Q8K_COUNTERS, kname, threads),
                             "kernel": kname.replace("qmm::", "").replace(" ", ""), "call": m.label,
                             "ops_per_launch": int(m.ops)}
         line["per32_same_shapes"] = {"value": round(sum(c.ops for c in p32) / t32 / 1e12, 2), "unit": "TOP/s",
@@ -1029,7 +1035,7 @@ def main():
         m = max(sk, key=lambda c: c.ops / float(np.mean(c.k_ms)))
         km = float(np.mean(m.k_ms)) * 1e-3
         line["roofline"] = {"bound": "mfma", "achieved": round(m.ops / km / 1e12, 2), "peak": INT8_PEAK_TOPS,
-                            "unit": "TFLOP/s", "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4), "traffic": None,
+                            "unit": "TOP/s", "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4), "traffic": None,
                             "kernel": "mmq_q4k_streamk_kernel<4,2> + fixup", "call": m.label,
                             "ops_per_launch": int(m.ops)}
         line["per_tile_dispatch"] = {"value": round(sum(c.ops for c in tiles) / ksum(tiles) / 1e12, 2),

@@ -309,7 +309,7 @@ int qmm_matmul_q8k(int type, const void* W, const int8_t* q, const float* d, con
  * with a scale per 256"]: one activation scale per super-block makes that sum a
  * single integer).  Same results bit for bit as QMM_KIND_MMQ_128X64 and
  * QMM_KIND_MMQ_64X64_SPLITK respectively.  qmm_matmul_q8k runs the unsplit one for
- * Q4_K where the rule picks 128 x 64 tiles and there are more than 256 of them.
+ * Q4_K wherever there are more than 256 tiles of 128 x 64.
  * For tests and measurement.  Other kinds: QMM_ERR_ARG; other rules as
  * qmm_matmul_q8k. */
 int qmm_matmul_q8k_kind(int kind, int type, const void* W, const int8_t* q, const float* d, const float* bsum,

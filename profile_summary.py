@@ -35,6 +35,7 @@ KERNEL_SOURCES = {
     "qmm::mmvq_": ("qmm_mmvq.hip", "qmm_internal.h"),
     "qmm::mmq_": ("qmm_mmq.hip", "qmm_mmq_common.h", "qmm_internal.h"),
     "qmm::{anonymous}::mmq_q4k_v2_": ("qmm_mmq2.hip", "qmm_mmq_common.h", "qmm_internal.h"),
+    "qmm::{anonymous}::mmq_k4_q8k_v2_": ("qmm_mmq_q8k2.hip", "qmm_mmq_common.h", "qmm_internal.h"),
     "qmm::mmq_k4_q8k_": ("qmm_mmq_q8k.hip", "qmm_mmq_common.h", "qmm_internal.h"),
     "qmm::mmq_q6k_q8k_": ("qmm_mmq_q8k.hip", "qmm_mmq_common.h", "qmm_internal.h"),
     "qmm::{anonymous}::mmq_skinny_": ("qmm_skinny.hip", "qmm_mmq_common.h", "qmm_internal.h"),

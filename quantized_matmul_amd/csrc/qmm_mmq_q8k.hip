@@ -603,11 +603,12 @@ static hipError_t launch_q8k_tile(int type, const uint8_t* W, const int8_t* q, c
 hipError_t launch_mmq_q8k(int type, const uint8_t* W, const int8_t* q, const float* d, const float* bsum, int nt,
                           int od, int id, float* out, int32_t* S, hipStream_t st, int tile)
 {
-    // Q4_K on the wave kernel with the scales in the int8 operand where the cost
-    // model picks 128 x 64 tiles and there are more than 256 of them (measured
-    // 6-9 % faster there; on fewer tiles it holds one wave per SIMD)
+    // Q4_K on the wave kernel with the scales in the int8 operand wherever there
+    // are more than 256 of its 128 x 64 tiles (measured 6-9 % faster than the tile
+    // the cost model picks there, the 64 x 64 split included; on fewer tiles it
+    // holds one wave per SIMD and the staged kernels win)
     const long t128 = (long)((nt + 63) / 64) * ((od + 127) / 128);
-    if (type == 1 && (tile == 4 || tile == 5 || (tile == 0 && t128 > 256 && q8k_tile_choice(nt, od, id) == 1)))
+    if (type == 1 && (tile == 4 || tile == 5 || (tile == 0 && t128 > 256)))
         return launch_mmq_k4_q8k_v2(W, q, d, bsum, nt, od, id, out, S, st, tile == 5 ? 2 : 1);
     if (S)
         return launch_q8k_tile<2, 2, 1, true>(type, W, q, d, bsum, nt, od, id, out, S, st);

@@ -218,7 +218,8 @@ def test_matmul_q8k_wave_kernels(kind, base, nt, od, idim):
 def test_q8k_wave_integer_stage_bit_exact():
     """The integer stage of the wave kernel (S1 = 8 Ca + Cb from the two chained
     accumulators, and S2): qmm_q8k_superblock_sums takes it where qmm_matmul_q8k
-    does (Q4_K, more than 256 tiles of 128 x 64); ragged rows and tokens, three
+    does (Q4_K, more than 256 tiles of 128 x 64, whichever tile the cost model
+    names); ragged rows and tokens, three
     super-blocks (the two-per-trip loop with an odd count)."""
     nt, od, idim = 50, 33243, 768
     _say(f"q8k wave integer stage nt={nt} od={od} id={idim}")
