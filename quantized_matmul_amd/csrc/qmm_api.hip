@@ -208,12 +208,17 @@ int dispatch_kind(int type, int nt, int od, int id)
 //    full round; stream-K equal or up to 5 % slower, also in a whole-model graph);
 //    and for Q6_K grids of at most 64 tiles (1.2-1.4x); otherwise per tile
 //    (stream-K up to 25 % slower).
+// Where Q4_K runs the 4-wave kernel within one of its rounds (qmm::mmq_q4k_wave_tile
+// on 257-512 tiles: two of its workgroups per CU, so a round holds 512 tiles) the
+// per-tile launch stays: stream-K was 5-31 % slower at every such shape measured.
 bool streamk_preferred(int type, int nt, int od, int id)
 {
     const bool q6 = type == QMM_TYPE_Q6_K || type == QMM_TYPE_Q6_K_P224;
     if ((type != QMM_TYPE_Q4_K && !q6) || dispatch_kind(type, nt, od, id) != QMM_KIND_MMQ)
         return false;
     const long tiles = (long)((nt + 63) / 64) * ((od + 127) / 128);
+    if (type == QMM_TYPE_Q4_K && tiles <= 512 && qmm::mmq_q4k_wave_tile(nt, od, id))
+        return false;
     if (tiles % 256 == 0)
         return false;
     if (tiles > 256) {

@@ -31,6 +31,10 @@ hipError_t launch_mmvq(int type, const uint8_t* W, const int8_t* q, const float*
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
                       int nt, int od, int id, float* out, int32_t* S, hipStream_t st, int tile = 0);
 int mmq_tile_choice(int nt, int od, int id);
+// Whether a Q4_K matrix call runs the 4-wave kernel (launch_mmq_q4k_v2): more than
+// 256 of its 128 x 64 tiles, and either the cost model names 128 x 64 or the tiles
+// fill three quarters or more of one round of 512 workgroup slots (two per CU).
+bool mmq_q4k_wave_tile(int nt, int od, int id);
 // Q4_K matrix kernel of 4 waves x (32 rows x 64 tokens) per workgroup (qmm_mmq2.hip);
 // S != null writes the integer dots instead (S [nt][od][nsb][8]).
 hipError_t launch_mmq_q4k_v2(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od,

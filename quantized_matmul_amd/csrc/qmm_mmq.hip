@@ -1361,15 +1361,27 @@ hipError_t launch_mmq_streamk(int type, const uint8_t* W, const int8_t* q, const
     return hipGetLastError();
 }
 
+// Two of the 4-wave kernel's workgroups share a CU, so one round holds 512 tiles.
+// Measured (Q4_K, 4096 and 8192 columns, same process): where the cost model names
+// 128 x 64 tiles and there are more than 256, it is 3-10 % faster than this file's
+// 8-wave tiles and 12-31 % faster than stream-K (448-768 tiles); where it names the
+// 64 x 64 split, it wins from 384 tiles up to one full round (12288 x 4096 at 256
+// tokens: 62.1 against 67.1 us stream-K and 73.4 us split; 12288 x 8192: 113.0
+// against 119.5 and 128.8), and loses to stream-K at 288-320 tiles (by 3-4 %) and
+// past one round (576 tiles: 100.8 against 95.6 us).  On at most 256 tiles it holds
+// one wave per SIMD and the 8-wave tiles win.
+bool mmq_q4k_wave_tile(int nt, int od, int id)
+{
+    const long t128 = (long)((nt + 63) / 64) * ((od + 127) / 128);
+    return t128 > 256 && (mmq_tile_choice(nt, od, id) == 1 || (t128 >= 384 && t128 <= 512));
+}
+
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
                       int nt, int od, int id, float* out, int32_t* S, hipStream_t st, int tile)
 {
-    // Q4_K: the kernel of 4 waves of 32 rows x 64 tokens (qmm_mmq2.hip) where the
-    // cost model picks 128 x 64 tiles and there are more tiles than CUs (two of its
-    // workgroups share a CU; 3-10 % faster than this file's 8-wave tiles there; on
-    // fewer tiles, or the split-K shapes, this file's kernels win), or when asked for
-    const long t128 = (long)((nt + 63) / 64) * ((od + 127) / 128);
-    if (type == 1 && (tile == 4 || (tile == 0 && (S || (t128 > 256 && mmq_tile_choice(nt, od, id) == 1)))))
+    // Q4_K: the kernel of 4 waves of 32 rows x 64 tokens (qmm_mmq2.hip) by
+    // mmq_q4k_wave_tile, or when asked for
+    if (type == 1 && (tile == 4 || (tile == 0 && (S || mmq_q4k_wave_tile(nt, od, id)))))
         return launch_mmq_q4k_v2(W, q, d, s, nt, od, id, out, S, st);
     if (tile == 4)
         return hipErrorInvalidValue;

@@ -135,6 +135,10 @@ def test_streamk_preferred_host():
     # short K within one round: only Q6_K grids of at most 64 tiles
     assert not sp(Q4, 64, 4096, 4096) and sp(Q6, 64, 4096, 4096) and sp(P6, 128, 4096, 4096)
     assert not sp(Q6, 192, 4096, 4096)                # 96 tiles
+    # Q4_K within one round of the 4-wave kernel (257-512 tiles where it runs): per tile
+    assert not sp(Q4, 256, 12288, 4096) and sp(Q6, 256, 12288, 4096)   # 384 tiles, the split named
+    assert not sp(Q4, 448, 8192, 4096) and sp(Q6, 448, 8192, 4096)     # 448 tiles, 128 x 64 named
+    assert sp(Q4, 320, 8192, 4096)                                     # 320 tiles, the split: stream-K
     assert not sp(qmm.QMM_TYPE_Q4_0, 512, 4096, 12288)
     assert not sp(qmm.QMM_TYPE_Q5_K, 512, 4096, 12288)
     n = qmm.qmm_act_bytes(384, 12288)
