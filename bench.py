@@ -730,6 +730,18 @@ def kms(c):
     return float(np.mean(c.k_ms)) * 1e-3
 
 
+def q8k_kernel(qmm, c):
+    """Name and launch size (threads) of the Q4_K Q8_K matrix kernel qmm_matmul_q8k runs
+    for call c: the wave kernel with the scales in the int8 operand above 256 tiles of
+    128 x 64, else the staged kernel of the cost model's tile."""
+    t128 = -(-c.nt // 64) * -(-c.od // 128)
+    if c.qtype == qmm.QMM_TYPE_Q4_K and t128 > 256:
+        return "qmm::{anonymous}::mmq_k4_q8k_v2_kernel<1, false>", 8 * -(-t128 // 8) * 256
+    wr, wc, ks = MMQ_TILES[qmm.qmm_q8k_tile(c.nt, c.od, c.idim)]
+    tiles = -(-c.nt // (32 * wc)) * -(-c.od // (32 * wr))
+    return f"qmm::mmq_k4_q8k_kernel<{wr}, {wc}, {ks}, false, false>", 8 * -(-tiles // 8) * 64 * wr * wc * ks
+
+
 def report_default(line, calls, qmm, torch, read_traffic):
     """The default workload's line: value = Q4_K MMVQ GB/s at nt = 1 over the 4096 x 4096
     and 12288 x 4096 calls; roofline = the 12288 x 4096 one; mmq = the per-32 matrix
@@ -799,11 +811,14 @@ def report_default(line, calls, qmm, torch, read_traffic):
     if k8:
         m8 = max(k8, key=kms)
         t8 = m8.ops / kms(m8) / 1e12
+        k8name, k8threads = q8k_kernel(qmm, m8)
         line["mmq_q8k"] = {"value": round(sum(c.ops for c in k8) / sum(kms(c) for c in k8) / 1e12, 2),
                            "unit": "TOP/s", "activations": "Q8_K: one scale per 256 values (its own numerics)",
                            "roofline": {"bound": "mfma", "achieved": round(t8, 2), "peak": INT8_PEAK_TOPS,
                                         "unit": "TOP/s", "frac": round(t8 / INT8_PEAK_TOPS, 4),
-                                        "frac_of_measured": round(t8 / mf["T_s"], 4), "call": m8.label},
+                                        "frac_of_measured": round(t8 / mf["T_s"], 4),
+                                        "traffic": read_traffic(COUNTERS, k8name, k8threads),
+                                        "kernel": k8name.replace("qmm::", "").replace(" ", ""), "call": m8.label},
                            "per_call": {c.label: {"us": round(kms(c) * 1e6, 2),
                                                   "TOP_s": round(c.ops / kms(c) / 1e12, 2)} for c in k8}}
 
@@ -1004,15 +1019,7 @@ def main():
                     value=round(ops / t8 / 1e12, 2), unit="TOP/s")
         m = max(q8, key=lambda c: float(np.mean(c.k_ms)))
         km = float(np.mean(m.k_ms)) * 1e-3
-        t128 = -(-m.nt // 64) * -(-m.od // 128)
-        if m.qtype == qmm.QMM_TYPE_Q4_K and t128 > 256:
-            # the wave kernel with the scales in the int8 operand (4 waves per 128 x 64 tile)
-            kname, threads = "qmm::{anonymous}::mmq_k4_q8k_v2_kernel<1, false>", 8 * -(-t128 // 8) * 256
-        else:
-            wr, wc, ks = MMQ_TILES[qmm.qmm_q8k_tile(m.nt, m.od, m.idim)]
-            kname = f"qmm::mmq_k4_q8k_kernel<{wr}, {wc}, {ks}, false, false>"
-            tiles = -(-m.nt // (32 * wc)) * -(-m.od // (32 * wr))
-            threads = 8 * -(-tiles // 8) * 64 * wr * wc * ks
+        kname, threads = q8k_kernel(qmm, m)
         line["roofline"] = {"bound": "mfma", "achieved": round(m.ops / km / 1e12, 2), "peak": INT8_PEAK_TOPS,
                             "unit": "TOP/s", "frac": round(m.ops / km / 1e12 / INT8_PEAK_TOPS, 4),
                             "traffic": read_traffic(Q8K_COUNTERS, kname, threads),
