@@ -151,8 +151,12 @@ def mmq_kernel(qmm, nt, od, idim):
         return "qmm::mmq_q4k_streamk_kernel<4, 2>", 256 * 512
     tile = qmm.qmm_mmq_tile(nt, od, idim)
     tiles = -(-nt // 64) * -(-od // 128)
-    if tile == qmm.QMM_KIND_MMQ_128X64 and tiles > 256:   # the 4-wave kernel of 32 x 64 per wave
-        return "qmm::{anonymous}::mmq_q4k_v2_kernel<false>", 8 * -(-tiles // 8) * 256
+    # the 4-wave kernel of 32 x 64 per wave (the library's mmq_q4k_wave_form), and its
+    # split over K in 8 waves
+    if tiles > 256 and (tile == qmm.QMM_KIND_MMQ_128X64 or 384 <= tiles <= 512):
+        return "qmm::{anonymous}::mmq_q4k_v2_kernel<1, false>", 8 * -(-tiles // 8) * 256
+    if tile == qmm.QMM_KIND_MMQ_128X64 and tiles >= 192:
+        return "qmm::{anonymous}::mmq_q4k_v2_kernel<2, false>", 8 * -(-tiles // 8) * 512
     wr, wc, ks = MMQ_TILES[tile]
     tiles = -(-nt // (32 * wc)) * -(-od // (32 * wr))
     return f"qmm::mmq_q4k_kernel<{wr}, {wc}, {ks}, false>", 8 * -(-tiles // 8) * 64 * wr * wc * ks

@@ -114,8 +114,8 @@ enum {
                                        12.2]: token count in registers; per-32 rescale as
                                        MMQ); qmm_matmul's kernel for Q4_K at 3..48 tokens
                                        (by shape) */
-    QMM_KIND_MMQ_WAVE32X64_SPLITK = 8 /* Q4_K on Q8_K activations only
-                                         (qmm_matmul_q8k_kind): 128 x 64, 8 waves in two
+    QMM_KIND_MMQ_WAVE32X64_SPLITK = 8 /* Q4_K only (qmm_matmul_q8_kind,
+                                         qmm_matmul_q8k_kind): 128 x 64, 8 waves in two
                                          groups of 4 (32 rows x 64 tokens each) taking
                                          alternate super-blocks, partial tiles added in
                                          group order */

@@ -208,8 +208,8 @@ int dispatch_kind(int type, int nt, int od, int id)
 //    full round; stream-K equal or up to 5 % slower, also in a whole-model graph);
 //    and for Q6_K grids of at most 64 tiles (1.2-1.4x); otherwise per tile
 //    (stream-K up to 25 % slower).
-// Where Q4_K runs the 4-wave kernel within one of its rounds (qmm::mmq_q4k_wave_tile
-// on 257-512 tiles: two of its workgroups per CU, so a round holds 512 tiles) the
+// Where Q4_K runs the 4-wave kernel within one of its rounds (qmm::mmq_q4k_wave_form
+// 1 on 257-512 tiles: two of its workgroups per CU, so a round holds 512 tiles) the
 // per-tile launch stays: stream-K was 5-31 % slower at every such shape measured.
 bool streamk_preferred(int type, int nt, int od, int id)
 {
@@ -217,7 +217,7 @@ bool streamk_preferred(int type, int nt, int od, int id)
     if ((type != QMM_TYPE_Q4_K && !q6) || dispatch_kind(type, nt, od, id) != QMM_KIND_MMQ)
         return false;
     const long tiles = (long)((nt + 63) / 64) * ((od + 127) / 128);
-    if (type == QMM_TYPE_Q4_K && tiles <= 512 && qmm::mmq_q4k_wave_tile(nt, od, id))
+    if (type == QMM_TYPE_Q4_K && tiles <= 512 && qmm::mmq_q4k_wave_form(nt, od, id) == 1)
         return false;
     if (tiles % 256 == 0)
         return false;
@@ -267,7 +267,9 @@ int matmul_q8_checked(int kind, int type, const void* W, const int8_t* q, const 
         }
         return QMM_OK;
     }
-    const int tile = kind >= QMM_KIND_MMQ_128X64 ? kind - QMM_KIND_MMQ_128X64 + 1 : 0;
+    const int tile = kind == QMM_KIND_MMQ_WAVE32X64_SPLITK ? 5
+                     : kind >= QMM_KIND_MMQ_128X64     ? kind - QMM_KIND_MMQ_128X64 + 1
+                                                       : 0;
     return launched(qmm::launch_mmq(type, w, q, d, s, nt, od, id, out, S, st, tile));
 }
 
@@ -650,9 +652,10 @@ int qmm_matmul_q8(int type, const void* W, const int8_t* q, const float* d, cons
 int qmm_matmul_q8_kind(int kind, int type, const void* W, const int8_t* q, const float* d,
                        const float* s, int nt, int od, int id, float* out, void* stream)
 {
-    if (kind < QMM_KIND_MMVQ || kind > QMM_KIND_SKINNY)
+    if (kind < QMM_KIND_MMVQ || (kind > QMM_KIND_SKINNY && kind != QMM_KIND_MMQ_WAVE32X64_SPLITK))
         return QMM_ERR_ARG;
-    if ((kind == QMM_KIND_MMQ_WAVE32X64 || kind == QMM_KIND_SKINNY) && type != QMM_TYPE_Q4_K)
+    if ((kind == QMM_KIND_MMQ_WAVE32X64 || kind == QMM_KIND_MMQ_WAVE32X64_SPLITK || kind == QMM_KIND_SKINNY) &&
+        type != QMM_TYPE_Q4_K)
         return QMM_ERR_TYPE;
     int rc = validate_q8(type, W, q, d, s, nt, od, id, out);
     if (rc)

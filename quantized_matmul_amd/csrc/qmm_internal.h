@@ -31,14 +31,17 @@ hipError_t launch_mmvq(int type, const uint8_t* W, const int8_t* q, const float*
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
                       int nt, int od, int id, float* out, int32_t* S, hipStream_t st, int tile = 0);
 int mmq_tile_choice(int nt, int od, int id);
-// Whether a Q4_K matrix call runs the 4-wave kernel (launch_mmq_q4k_v2): more than
-// 256 of its 128 x 64 tiles, and either the cost model names 128 x 64 or the tiles
-// fill three quarters or more of one round of 512 workgroup slots (two per CU).
-bool mmq_q4k_wave_tile(int nt, int od, int id);
+// Which form of the 4-wave kernel (launch_mmq_q4k_v2) a Q4_K matrix call runs:
+// 1 (4 waves) on more than 256 of its 128 x 64 tiles where the cost model names
+// 128 x 64 or the tiles fill 384..512 of one round of 512 workgroup slots (two per
+// CU); 2 (8 waves in two groups splitting K, one workgroup per CU) on 192..256
+// tiles where the cost model names 128 x 64; 0 otherwise (the 8-wave tiles).
+int mmq_q4k_wave_form(int nt, int od, int id);
 // Q4_K matrix kernel of 4 waves x (32 rows x 64 tokens) per workgroup (qmm_mmq2.hip);
-// S != null writes the integer dots instead (S [nt][od][nsb][8]).
+// S != null writes the integer dots instead (S [nt][od][nsb][8]); ks = 2: 8 waves in
+// two groups splitting K.
 hipError_t launch_mmq_q4k_v2(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od,
-                             int id, float* out, int32_t* S, hipStream_t st);
+                             int id, float* out, int32_t* S, hipStream_t st, int ks = 1);
 // Small-batch Q4_K kernel on 16 x 16 x 32 int8 MFMA tiles, 1..16 tokens
 // (qmm_skinny.hip).  cfg 0: rows per wave and waves per workgroup by the shape;
 // else RT * 100 + KS (RT 1 or 2 tiles of 16 rows per wave, KS <= 8 waves).

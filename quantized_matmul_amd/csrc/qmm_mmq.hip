@@ -1369,21 +1369,31 @@ hipError_t launch_mmq_streamk(int type, const uint8_t* W, const int8_t* q, const
 // tokens: 62.1 against 67.1 us stream-K and 73.4 us split; 12288 x 8192: 113.0
 // against 119.5 and 128.8), and loses to stream-K at 288-320 tiles (by 3-4 %) and
 // past one round (576 tiles: 100.8 against 95.6 us).  On at most 256 tiles it holds
-// one wave per SIMD and the 8-wave tiles win.
-bool mmq_q4k_wave_tile(int nt, int od, int id)
+// one wave per SIMD; there its split over K (8 waves, one workgroup per CU, two
+// waves per SIMD) beats the 8-wave 128 x 64 tiles by 1-4 % where the cost model
+// names them (4096 x 8192 at 512 tokens: 70.7 against 72.4 us; 4096 x 12288 at 384,
+// 448 and 512 tokens: 100.6 / 101.0 / 101.7-103.1 against 103.0 / 103.0 /
+// 104.1-106.2 us).
+int mmq_q4k_wave_form(int nt, int od, int id)
 {
     const long t128 = (long)((nt + 63) / 64) * ((od + 127) / 128);
-    return t128 > 256 && (mmq_tile_choice(nt, od, id) == 1 || (t128 >= 384 && t128 <= 512));
+    const int choice = mmq_tile_choice(nt, od, id);
+    if (t128 > 256 && (choice == 1 || (t128 >= 384 && t128 <= 512)))
+        return 1;
+    return (choice == 1 && t128 >= 192) ? 2 : 0;
 }
 
 hipError_t launch_mmq(int type, const uint8_t* W, const int8_t* q, const float* d, const float* s,
                       int nt, int od, int id, float* out, int32_t* S, hipStream_t st, int tile)
 {
-    // Q4_K: the kernel of 4 waves of 32 rows x 64 tokens (qmm_mmq2.hip) by
-    // mmq_q4k_wave_tile, or when asked for
-    if (type == 1 && (tile == 4 || (tile == 0 && (S || mmq_q4k_wave_tile(nt, od, id)))))
+    // Q4_K: the kernel of 4 waves of 32 rows x 64 tokens (qmm_mmq2.hip) and its
+    // split over K by mmq_q4k_wave_form, or when asked for
+    const int wf = (type == 1 && tile == 0 && !S) ? mmq_q4k_wave_form(nt, od, id) : 0;
+    if (type == 1 && (tile == 4 || (tile == 0 && S) || wf == 1))
         return launch_mmq_q4k_v2(W, q, d, s, nt, od, id, out, S, st);
-    if (tile == 4)
+    if (type == 1 && !S && (tile == 5 || wf == 2))
+        return launch_mmq_q4k_v2(W, q, d, s, nt, od, id, out, nullptr, st, 2);
+    if (tile == 4 || tile == 5)
         return hipErrorInvalidValue;
     if (S)
         return launch_tile<2, 2, 1, true>(type, W, q, d, s, nt, od, id, out, S, st);

@@ -97,7 +97,7 @@ __device__ __forceinline__ void k4_prefetch(K4Pref& pf, const K4Offs& o, const K
 // Store one super-block's prefetched data into a stage: codes as they are, d as it
 // is, s split in three bf16 parts, and the header decoded to the per-row factors.
 // Thread (row r = tid/2, half h = tid%2) decodes sub-blocks 2h, 2h+1, 2h+4, 2h+5.
-__device__ __forceinline__ void k4_stage(K4Stage& st, const K4Pref& pf, int tid)
+__device__ __forceinline__ void k4_stage(K4Stage& st, const K4Pref& pf, int tid, bool valid)
 {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -119,8 +119,10 @@ __device__ __forceinline__ void k4_stage(K4Stage& st, const K4Pref& pf, int tid)
                 make_uint2(s0.p[pt] | (s1.p[pt] << 16), s2.p[pt] | (s3.p[pt] << 16));
     }
     const int r = tid >> 1;
-    const float dw = f16_bits_to_f32((uint32_t)pf.h.x & 0xFFFF);
-    const float dm = f16_bits_to_f32((uint32_t)pf.h.x >> 16);
+    // valid == false (a super-block past the end in the split over K): zero row
+    // factors, so that super-block adds nothing
+    const float dw = valid ? f16_bits_to_f32((uint32_t)pf.h.x & 0xFFFF) : 0.f;
+    const float dm = valid ? f16_bits_to_f32((uint32_t)pf.h.x >> 16) : 0.f;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int jj = 2 * hf + u;  // sub-blocks jj and jj + 4
@@ -236,18 +238,23 @@ __device__ __forceinline__ void k4_superblock(const K4Stage& st, const v4i (&a16
 }
 
 // The kernel body for one whole tile: rows row0 .. row0 + 127 and tokens tok0 ..
-// tok0 + 63 over all super-blocks.
-template <bool DUMP>
+// tok0 + 63 over all super-blocks.  KS = 2: two groups of 4 waves split K (group g
+// takes super-blocks g, g + 2, ..., each group with its own stages); the second
+// group's partial tiles are added to the first's in a fixed order at the end.
+template <int KS, bool DUMP>
 __device__ __forceinline__ void k4_tile(const uint8_t* __restrict__ W, const int8_t* __restrict__ q,
                                         const float* __restrict__ dx, const float* __restrict__ sx,
                                         float* __restrict__ out, int nt, int od, int id, int tile,
                                         int32_t* __restrict__ S)
 {
-    __shared__ K4Stage stg[2];
+    __shared__ K4Stage stg[KS][2];
+    static_assert(KS == 1 || sizeof(stg) >= 4 * 2 * 1024 * sizeof(float), "the combine fits the stages");
     const int ntb = (nt + kK4BN - 1) / kK4BN;
     const int nsb = id >> 8, nblk = id >> 5;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int kg = KS > 1 ? (int)(threadIdx.x >> 8) : 0;
+    const int tid = threadIdx.x & 255, lane = tid & 63, w = tid >> 6;
     const int li = lane & 31, lh = lane >> 5;
+    const int niter = (nsb + KS - 1) / KS;   // the same count for every group (barriers)
     const uint32_t row_bytes = (uint32_t)nsb * kQ4KBytes;
     const float Mv = vgpr_f32(kMagicBits);
     const uint32_t mask = vgpr_u32(0x0F0F0F0Fu);
@@ -270,74 +277,99 @@ __device__ __forceinline__ void k4_tile(const uint8_t* __restrict__ W, const int
     K4Rsrc rs;
     rs.w = buffer_rsrc(W + (size_t)row0 * row_bytes, (size_t)(od - row0) * row_bytes);
     rs.x = buffer_rsrc(q + (size_t)tok0 * id, (size_t)(nt - tok0) * id);
-    // waves 0-1 stage d, waves 2-3 stage s: a wave-uniform choice, made scalar so
-    // the buffer resource stays in scalar registers
+    // waves 0-1 of a group stage d, waves 2-3 stage s: a wave-uniform choice, made
+    // scalar so the buffer resource stays in scalar registers
     const uintptr_t pds = reinterpret_cast<uintptr_t>(tid < 128 ? dx : sx);
     const uintptr_t pdsu = ((uintptr_t)__builtin_amdgcn_readfirstlane((uint32_t)(pds >> 32)) << 32) |
                            (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)pds);
     rs.ds = buffer_rsrc(reinterpret_cast<const float*>(pdsu) + (size_t)tok0 * nblk, (size_t)(nt - tok0) * nblk * 4);
     const uint32_t oa = (uint32_t)(min(row0 + 32 * w + li, od - 1) - row0) * row_bytes + 16u + 16u * (uint32_t)lh;
+    K4Stage* sg = stg[kg];
+    // this group's super-block of local iteration it, and its clamped load index
+    auto sbi = [&](int it) { return it * KS + kg; };
+    auto ld = [&](int it) { return min(sbi(it), nsb - 1); };
 
     K4Pref pf;
     v4i aA[4], aB[4];
     v16f acc0 = {}, acc1 = {};
-    k4_prefetch(pf, o, rs, 0, nblk);
-    k4_load_a(aA, rs.w, oa, 0);
-    k4_stage(stg[0], pf, tid);
-    k4_prefetch(pf, o, rs, min(1, nsb - 1), nblk);
-    k4_load_a(aB, rs.w, oa, min(1, nsb - 1));
+    k4_prefetch(pf, o, rs, ld(0), nblk);
+    k4_load_a(aA, rs.w, oa, ld(0));
+    k4_stage(sg[0], pf, tid, sbi(0) < nsb);
+    k4_prefetch(pf, o, rs, ld(1), nblk);
+    k4_load_a(aB, rs.w, oa, ld(1));
     __syncthreads();
-    // two super-blocks per trip so the A registers alternate without copies; the
+    // two iterations per trip so the A registers alternate without copies; the
     // prefetch indices are clamped to the last super-block (no load under a branch)
-    for (int sb = 0; sb < nsb; sb += 2) {
-        k4_superblock<DUMP>(stg[sb & 1], aA, magic, Mv, mask, w, li, lh, acc0, acc1, S, nt, od, nsb, sb, row0, tok0);
+    for (int it = 0; it < niter; it += 2) {
+        k4_superblock<DUMP>(sg[0], aA, magic, Mv, mask, w, li, lh, acc0, acc1, S, nt, od, nsb, sbi(it), row0, tok0);
         __builtin_amdgcn_sched_barrier(0);
-        k4_stage(stg[(sb + 1) & 1], pf, tid);
-        k4_prefetch(pf, o, rs, min(sb + 2, nsb - 1), nblk);
-        k4_load_a(aA, rs.w, oa, min(sb + 2, nsb - 1));
+        k4_stage(sg[1], pf, tid, sbi(it + 1) < nsb);
+        k4_prefetch(pf, o, rs, ld(it + 2), nblk);
+        k4_load_a(aA, rs.w, oa, ld(it + 2));
         __syncthreads();
-        if (sb + 1 >= nsb)
+        if (it + 1 >= niter)
             break;
-        k4_superblock<DUMP>(stg[(sb + 1) & 1], aB, magic, Mv, mask, w, li, lh, acc0, acc1, S, nt, od, nsb, sb + 1,
-                            row0, tok0);
+        k4_superblock<DUMP>(sg[1], aB, magic, Mv, mask, w, li, lh, acc0, acc1, S, nt, od, nsb, sbi(it + 1), row0,
+                            tok0);
         __builtin_amdgcn_sched_barrier(0);
-        k4_stage(stg[sb & 1], pf, tid);
-        k4_prefetch(pf, o, rs, min(sb + 3, nsb - 1), nblk);
-        k4_load_a(aB, rs.w, oa, min(sb + 3, nsb - 1));
+        k4_stage(sg[0], pf, tid, sbi(it + 2) < nsb);
+        k4_prefetch(pf, o, rs, ld(it + 3), nblk);
+        k4_load_a(aB, rs.w, oa, ld(it + 3));
         __syncthreads();
     }
     if constexpr (!DUMP) {
+        if constexpr (KS == 2) {
+            // every wave is past the last barrier of the loop: the stages are free
+            float* red = reinterpret_cast<float*>(&stg[0][0]);
+            if (kg == 1) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    red[((w * 2 + 0) * 16 + i) * 64 + lane] = acc0[i];
+                    red[((w * 2 + 1) * 16 + i) * 64 + lane] = acc1[i];
+                }
+            }
+            __syncthreads();
+            if (kg == 1)
+                return;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                acc0[i] += red[((w * 2 + 0) * 16 + i) * 64 + lane];
+                acc1[i] += red[((w * 2 + 1) * 16 + i) * 64 + lane];
+            }
+        }
         store_tile(acc0, out, nt, od, tok0 + li, row0 + 32 * w, lh);
         store_tile(acc1, out, nt, od, tok0 + 32 + li, row0 + 32 * w, lh);
     }
 }
 
 // One tile per workgroup (tiles of one row block on one XCD).
-template <bool DUMP>
-__global__ __launch_bounds__(kK4NTH, 2) void mmq_q4k_v2_kernel(const uint8_t* __restrict__ W,
-                                                               const int8_t* __restrict__ q,
-                                                               const float* __restrict__ dx,
-                                                               const float* __restrict__ sx, float* __restrict__ out,
-                                                               int nt, int od, int id, int32_t* __restrict__ S)
+template <int KS, bool DUMP>
+__global__ __launch_bounds__(kK4NTH * KS, KS == 1 ? 2 : 1) void mmq_q4k_v2_kernel(
+    const uint8_t* __restrict__ W, const int8_t* __restrict__ q, const float* __restrict__ dx,
+    const float* __restrict__ sx, float* __restrict__ out, int nt, int od, int id, int32_t* __restrict__ S)
 {
+    static_assert(!DUMP || KS == 1, "the integer dump runs unsplit");
     const int ntiles = ((nt + kK4BN - 1) / kK4BN) * ((od + kK4BM - 1) / kK4BM);
     const int tile = xcd_tile(ntiles);
     if (tile < 0)
         return;  // whole workgroup
-    k4_tile<DUMP>(W, q, dx, sx, out, nt, od, id, tile, S);
+    k4_tile<KS, DUMP>(W, q, dx, sx, out, nt, od, id, tile, S);
 }
 
 }  // namespace
 
 hipError_t launch_mmq_q4k_v2(const uint8_t* W, const int8_t* q, const float* d, const float* s, int nt, int od,
-                             int id, float* out, int32_t* S, hipStream_t st)
+                             int id, float* out, int32_t* S, hipStream_t st, int ks)
 {
     const int ntiles = ((nt + kK4BN - 1) / kK4BN) * ((od + kK4BM - 1) / kK4BM);
-    const dim3 grid((unsigned)(8 * ((ntiles + 7) / 8))), block(kK4NTH);
+    const dim3 grid((unsigned)(8 * ((ntiles + 7) / 8)));
     if (S)
-        hipLaunchKernelGGL(mmq_q4k_v2_kernel<true>, grid, block, 0, st, W, q, d, s, out, nt, od, id, S);
+        hipLaunchKernelGGL((mmq_q4k_v2_kernel<1, true>), grid, dim3(kK4NTH), 0, st, W, q, d, s, out, nt, od, id, S);
+    else if (ks == 2)
+        hipLaunchKernelGGL((mmq_q4k_v2_kernel<2, false>), grid, dim3(2 * kK4NTH), 0, st, W, q, d, s, out, nt, od, id,
+                           S);
     else
-        hipLaunchKernelGGL(mmq_q4k_v2_kernel<false>, grid, block, 0, st, W, q, d, s, out, nt, od, id, S);
+        hipLaunchKernelGGL((mmq_q4k_v2_kernel<1, false>), grid, dim3(kK4NTH), 0, st, W, q, d, s, out, nt, od, id, S);
     return hipGetLastError();
 }
 

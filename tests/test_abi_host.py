@@ -166,7 +166,9 @@ def test_validation_before_device_work():
     assert L.qmm_matmul(1, p, p, 1, 4, 256, p, p, 10, None) == qmm.QMM_ERR_WORKSPACE
     assert L.qmm_matmul_q8(2, p, p, p, mis, 1, 4, 256, p, None) == qmm.QMM_ERR_ALIGN
     assert L.qmm_matmul_q8_kind(0, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_ARG
-    assert L.qmm_matmul_q8_kind(8, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_matmul_q8_kind(9, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_ARG
+    assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_WAVE32X64_SPLITK, 1, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_DEVICE
+    assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_WAVE32X64_SPLITK, 2, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_TYPE
     # the 32 x 64 per-wave kernel and the small-batch kernel exist for Q4_K only; the
     # small-batch kernel takes any nt (slices of 16 tokens above 16): validation passes
     assert L.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_WAVE32X64, 2, p, p, p, p, 1, 4, 256, p, None) == qmm.QMM_ERR_TYPE

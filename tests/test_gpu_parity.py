@@ -151,7 +151,7 @@ def test_mmq_every_tile_shape(qtype, nt, od, idim):
     args = (_up(W), _up(rq), _up(rd), _up(rs), od)
     kinds = [qmm.QMM_KIND_MMQ_128X64, qmm.QMM_KIND_MMQ_64X64, qmm.QMM_KIND_MMQ_64X64_SPLITK]
     if qtype == Q4:
-        kinds.append(qmm.QMM_KIND_MMQ_WAVE32X64)
+        kinds += [qmm.QMM_KIND_MMQ_WAVE32X64, qmm.QMM_KIND_MMQ_WAVE32X64_SPLITK]
     for kind in kinds:
         o = qmm.qmm_matmul_q8_kind(kind, qtype, *args)
         torch.cuda.synchronize()

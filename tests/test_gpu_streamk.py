@@ -90,7 +90,9 @@ PATH_CASES = [(Q4, 20, 96, 8192), (Q4, 9, 40, 65536), (Q4, 300, 1000, 2304), (Q4
               (Q6, 64, 4096, 4096), (Q6, 192, 4096, 4096), (Q6, 20, 96, 8192), (P6, 192, 12288, 4096),
               (P6, 128, 12288, 4096), (P6, 256, 4096, 12288), (P6, 128, 4096, 12288),
               # Q4_K within one round of the 4-wave kernel (per tile there), and beside it
-              (Q4, 256, 12288, 4096), (Q4, 448, 8192, 4096), (Q4, 320, 8192, 4096), (P6, 256, 12288, 4096)]
+              (Q4, 256, 12288, 4096), (Q4, 448, 8192, 4096), (Q4, 320, 8192, 4096), (P6, 256, 12288, 4096),
+              # Q4_K on 192..256 tiles of 128 x 64: the 4-wave kernel split over K per tile
+              (Q4, 512, 4096, 8192), (Q4, 448, 4096, 12288)]
 
 
 @pytest.mark.parametrize("qtype,nt,od,idim", PATH_CASES, ids=[f"t{q}-{a}x{b}x{c}" for q, a, b, c in PATH_CASES])
@@ -113,6 +115,8 @@ def test_qmm_matmul_takes_streamk_where_preferred(qtype, nt, od, idim):
     wave = (qtype == Q4 and mmq and tiles > 256 and
             (qmm.qmm_mmq_tile(nt, od, idim) == qmm.QMM_KIND_MMQ_128X64 or 384 <= tiles <= 512))
     assert pref == (mmq and tiles % 256 != 0 and rule and not (wave and tiles <= 512))
+    split = (qtype == Q4 and mmq and not wave and 192 <= tiles <= 256 and
+             qmm.qmm_mmq_tile(nt, od, idim) == qmm.QMM_KIND_MMQ_128X64)
     W = _weights(qtype, od, idim, seed=4200 + od)
     x = synth.activations(nt, idim, seed=4300 + nt, outlier_frac=0.01)
     Wt, xt = _up(W), _up(x)
@@ -123,12 +127,13 @@ def test_qmm_matmul_takes_streamk_where_preferred(qtype, nt, od, idim):
     ws = torch.empty(qmm.qmm_streamk_ws_bytes(), dtype=torch.uint8, device=DEV)
     sk = qmm.qmm_matmul_q8_streamk(qtype, Wt, q, d, s, od, ws)
     pt = qmm.qmm_matmul_q8(qtype, Wt, q, d, s, od)
-    wv = qmm.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_WAVE32X64, qtype, Wt, q, d, s, od) if wave else None
+    wv = (qmm.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_WAVE32X64, qtype, Wt, q, d, s, od) if wave else
+          qmm.qmm_matmul_q8_kind(qmm.QMM_KIND_MMQ_WAVE32X64_SPLITK, qtype, Wt, q, d, s, od) if split else None)
     torch.cuda.synchronize()
     bits = lambda t: t.view(torch.int32)
     assert torch.equal(bits(full), bits(sk if pref else pt))
     assert torch.equal(bits(small), bits(pt))
-    if wave:
+    if wave or split:
         assert torch.equal(bits(pt), bits(wv))
     qn, dn, sn = oracle_activations(oracle.quantize, x, (q, d, s), "quantize")
     if nt * od <= 300 * 1000:
